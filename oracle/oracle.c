@@ -1,0 +1,537 @@
+/*
+ * fp64 CPU oracle for Newton (DEER) / quasi-Newton (quasi-DEER) evaluation of
+ * nonlinear RNNs over the sequence length.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or run
+ * this file: only the test suite, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code, header, table or constant with the HIP
+ * library; both sides see the same seeded inputs and nothing else.
+ *
+ * What it computes, and where the pages state it:
+ *  - orc_rollout: the plain sequential evaluation h_t = f(h_{t-1}, x_t) that
+ *    DEER is measured against ("Parallelizing non-linear sequential models
+ *    over the sequence length", Key results and Measured effects: sequential
+ *    GRU evaluation; ParaRNN abstract: "naive sequential application").
+ *  - orc_deer: Newton on the residual system F(h)_t = h_t - f(h_{t-1}, x_t) = 0
+ *    (ParaRNN abstract: the recurrences cast as one system of equations solved
+ *    with Newton's iterations; Gonzalez et al. abstract: the states as the
+ *    solution of a fixed-point problem; Para-Seq README, Background: linearise
+ *    and solve the resulting linear recurrence).  Each sweep evaluates the cell
+ *    and its Jacobian at every step, solves dh_t = J_t dh_{t-1} + r_t, and
+ *    updates.  The linear recurrence is solved here by its plain sequential
+ *    definition, not by a scan.  Stopping uses the single tolerance
+ *    hyperparameter of DEER (DEER summary, Limitations) on max |dh|.
+ *  - orc_adjoint: the gradient of L = sum_t <g_t, h_t> by reverse-mode
+ *    differentiation through the recurrence at a given trajectory (textbook
+ *    backpropagation through time).  At a converged trajectory this equals
+ *    the single reverse linear solve lambda_t = g_t + J_{t+1}^T lambda_{t+1}
+ *    that the DEER summary describes (Surprising findings: the backward pass
+ *    needs one inverse linear operator evaluation; Para-Seq README, Main
+ *    features: reverse adjoint scans).
+ *  - orc_affine_solve: y_t = A_t y_{t-1} + b_t (or the reverse-time recurrence)
+ *    by its definition, for the dense, diagonal and 2x2-block operators that
+ *    the Para-Seq README lists (Main features: src.utils scans).
+ *
+ * The pages never print the cell equations.  The cells follow the PyTorch
+ * conventions that Para-Seq keeps (README intro: the familiar RNN/GRU/LSTM
+ * interface); the CIFG/peephole ParaLSTM (README, Main features) is read as:
+ *   f = sigm(U_f + w_f h + p_f c + b_f),  g = tanh(U_g + w_g h + b_g),
+ *   c' = f c + (1-f) g,  o = sigm(U_o + w_o h + p_o c' + b_o),  h' = o tanh(c').
+ * Every operation runs in double precision, built without contraction of
+ * multiplies and adds into fused operations.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_TANH_RNN = 0, ORC_GRU = 1, ORC_GRU_DIAG = 2, ORC_LSTM = 3, ORC_LINEAR = 4 };
+enum { ORC_DENSE = 0, ORC_DIAG = 1, ORC_BLOCK2 = 2 };
+enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENOMEM = -4, ORC_NOT_CONVERGED = 1, ORC_NONFINITE = 2 };
+
+typedef struct {
+  int cell, B, T, d, n;
+  const double *Wx;   /* [G*n, d] */
+  const double *bx;   /* [G*n] or NULL */
+  const double *Wh;   /* dense cells [G*n, n]; diagonal cells [G*n] */
+  const double *bh;   /* [G*n] or NULL */
+  const double *peep; /* LSTM [2n] = p_f | p_o, else NULL */
+} orc_model;
+
+static int n_gates(int cell) { return (cell == ORC_GRU || cell == ORC_GRU_DIAG || cell == ORC_LSTM) ? 3 : 1; }
+static int swidth(const orc_model *m) { return m->cell == ORC_LSTM ? 2 * m->n : m->n; }
+static int jkind(int cell) {
+  if (cell == ORC_GRU_DIAG) return ORC_DIAG;
+  if (cell == ORC_LSTM) return ORC_BLOCK2;
+  return ORC_DENSE;
+}
+/* number of doubles one step's Jacobian occupies in its own structure */
+static size_t jsize(const orc_model *m) {
+  int k = jkind(m->cell), S = swidth(m);
+  if (k == ORC_DENSE) return (size_t)S * S;
+  if (k == ORC_DIAG) return (size_t)S;
+  return (size_t)m->n * 4;
+}
+static double sigm(double a) { return 1.0 / (1.0 + exp(-a)); }
+static double bias(const double *b, int i) { return b ? b[i] : 0.0; }
+
+/* U = W_x x_t + b_x : the input transform of a standard RNN layer. */
+static void input_proj(const orc_model *m, const double *xt, double *U) {
+  int Gn = n_gates(m->cell) * m->n;
+  for (int j = 0; j < Gn; j++) {
+    double a = bias(m->bx, j);
+    for (int k = 0; k < m->d; k++) a += m->Wx[(size_t)j * m->d + k] * xt[k];
+    U[j] = a;
+  }
+}
+
+/* Dense row-vector product (W s)_i for the rows [row0, row0+n) of W [*, n]. */
+static double rowdot(const double *W, int row, int n, const double *s) {
+  double a = 0.0;
+  for (int k = 0; k < n; k++) a += W[(size_t)row * n + k] * s[k];
+  return a;
+}
+
+/*
+ * One cell step: f = f(s, U) and, when J != NULL, J = df/ds in the cell's own
+ * structure (dense S x S row-major; diagonal S; 2x2 blocks [n][2][2] with rows
+ * (c', h') and columns (c, h)).
+ */
+static void cell_fwd(const orc_model *m, const double *s, const double *U, double *f, double *J) {
+  int n = m->n;
+  switch (m->cell) {
+  case ORC_TANH_RNN:
+  case ORC_LINEAR:
+    for (int i = 0; i < n; i++) {
+      double a = U[i] + rowdot(m->Wh, i, n, s) + bias(m->bh, i);
+      double fi = m->cell == ORC_TANH_RNN ? tanh(a) : a;
+      f[i] = fi;
+      if (J) {
+        double da = m->cell == ORC_TANH_RNN ? 1.0 - fi * fi : 1.0;
+        for (int k = 0; k < n; k++) J[(size_t)i * n + k] = da * m->Wh[(size_t)i * n + k];
+      }
+    }
+    break;
+  case ORC_GRU:
+    for (int i = 0; i < n; i++) {
+      double r = sigm(U[i] + rowdot(m->Wh, i, n, s) + bias(m->bh, i));
+      double z = sigm(U[n + i] + rowdot(m->Wh, n + i, n, s) + bias(m->bh, n + i));
+      double q = rowdot(m->Wh, 2 * n + i, n, s) + bias(m->bh, 2 * n + i);
+      double c = tanh(U[2 * n + i] + r * q);
+      f[i] = (1.0 - z) * c + z * s[i];
+      if (J) {
+        double al = (s[i] - c) * z * (1.0 - z);            /* through z          */
+        double be = (1.0 - z) * (1.0 - c * c);             /* through c          */
+        for (int k = 0; k < n; k++) {
+          double whr = m->Wh[(size_t)i * n + k];
+          double whz = m->Wh[(size_t)(n + i) * n + k];
+          double whn = m->Wh[(size_t)(2 * n + i) * n + k];
+          double v = al * whz + be * (r * whn + q * r * (1.0 - r) * whr);
+          if (k == i) v += z;
+          J[(size_t)i * n + k] = v;
+        }
+      }
+    }
+    break;
+  case ORC_GRU_DIAG:
+    for (int i = 0; i < n; i++) {
+      double ar = m->Wh[i], az = m->Wh[n + i], an = m->Wh[2 * n + i];
+      double r = sigm(U[i] + ar * s[i] + bias(m->bh, i));
+      double z = sigm(U[n + i] + az * s[i] + bias(m->bh, n + i));
+      double q = an * s[i] + bias(m->bh, 2 * n + i);
+      double c = tanh(U[2 * n + i] + r * q);
+      f[i] = (1.0 - z) * c + z * s[i];
+      if (J) J[i] = z + (s[i] - c) * z * (1.0 - z) * az + (1.0 - z) * (1.0 - c * c) * (r * an + q * r * (1.0 - r) * ar);
+    }
+    break;
+  case ORC_LSTM:
+    for (int i = 0; i < n; i++) {
+      double c = s[2 * i], h = s[2 * i + 1];
+      double wf = m->Wh[i], wg = m->Wh[n + i], wo = m->Wh[2 * n + i];
+      double pf = m->peep[i], po = m->peep[n + i];
+      double fg = sigm(U[i] + wf * h + pf * c + bias(m->bh, i));
+      double g = tanh(U[n + i] + wg * h + bias(m->bh, n + i));
+      double cn = fg * c + (1.0 - fg) * g;
+      double o = sigm(U[2 * n + i] + wo * h + po * cn + bias(m->bh, 2 * n + i));
+      double tc = tanh(cn);
+      f[2 * i] = cn;
+      f[2 * i + 1] = o * tc;
+      if (J) {
+        double dcc = fg + (c - g) * fg * (1.0 - fg) * pf;
+        double dch = (c - g) * fg * (1.0 - fg) * wf + (1.0 - fg) * (1.0 - g * g) * wg;
+        double dhdcn = o * (1.0 - tc * tc) + tc * o * (1.0 - o) * po;
+        double *Jb = J + (size_t)4 * i;
+        Jb[0] = dcc;
+        Jb[1] = dch;
+        Jb[2] = dhdcn * dcc;
+        Jb[3] = tc * o * (1.0 - o) * wo + dhdcn * dch;
+      }
+    }
+    break;
+  }
+}
+
+/* Size of the gradient of W_h (dense cells [G n, n], diagonal cells [G n]). */
+static size_t wh_size(const orc_model *m) {
+  int Gn = n_gates(m->cell) * m->n;
+  return (m->cell == ORC_GRU_DIAG || m->cell == ORC_LSTM) ? (size_t)Gn : (size_t)Gn * m->n;
+}
+
+/*
+ * Reverse-mode step through one cell by the chain rule: given the output
+ * gradient lam (S) at (s, U), return ds = (df/ds)^T lam, dU = (df/dU)^T lam, and
+ * add the parameter gradients of W_h, b_h and the peepholes.
+ */
+static void cell_vjp(const orc_model *m, const double *s, const double *U, const double *lam,
+                     double *ds, double *dU, double *dWh, double *dbh, double *dpeep) {
+  int n = m->n;
+  switch (m->cell) {
+  case ORC_TANH_RNN:
+  case ORC_LINEAR: {
+    for (int k = 0; k < n; k++) ds[k] = 0.0;
+    for (int i = 0; i < n; i++) {
+      double a = U[i] + rowdot(m->Wh, i, n, s) + bias(m->bh, i);
+      double da = lam[i];
+      if (m->cell == ORC_TANH_RNN) { double fi = tanh(a); da *= 1.0 - fi * fi; }
+      dU[i] = da;
+      dbh[i] += da;
+      for (int k = 0; k < n; k++) {
+        dWh[(size_t)i * n + k] += da * s[k];
+        ds[k] += da * m->Wh[(size_t)i * n + k];
+      }
+    }
+    break;
+  }
+  case ORC_GRU: {
+    for (int k = 0; k < n; k++) ds[k] = 0.0;
+    for (int i = 0; i < n; i++) {
+      double r = sigm(U[i] + rowdot(m->Wh, i, n, s) + bias(m->bh, i));
+      double z = sigm(U[n + i] + rowdot(m->Wh, n + i, n, s) + bias(m->bh, n + i));
+      double q = rowdot(m->Wh, 2 * n + i, n, s) + bias(m->bh, 2 * n + i);
+      double c = tanh(U[2 * n + i] + r * q);
+      double dc = lam[i] * (1.0 - z);
+      double dz = lam[i] * (s[i] - c);
+      double daz = dz * z * (1.0 - z);
+      double dan = dc * (1.0 - c * c);
+      double dq = dan * r;
+      double dar = dan * q * r * (1.0 - r);
+      ds[i] += lam[i] * z;
+      dU[i] = dar; dU[n + i] = daz; dU[2 * n + i] = dan;
+      dbh[i] += dar; dbh[n + i] += daz; dbh[2 * n + i] += dq;
+      for (int k = 0; k < n; k++) {
+        dWh[(size_t)i * n + k] += dar * s[k];
+        dWh[(size_t)(n + i) * n + k] += daz * s[k];
+        dWh[(size_t)(2 * n + i) * n + k] += dq * s[k];
+        ds[k] += dar * m->Wh[(size_t)i * n + k] + daz * m->Wh[(size_t)(n + i) * n + k] +
+                 dq * m->Wh[(size_t)(2 * n + i) * n + k];
+      }
+    }
+    break;
+  }
+  case ORC_GRU_DIAG:
+    for (int i = 0; i < n; i++) {
+      double ar = m->Wh[i], az = m->Wh[n + i], an = m->Wh[2 * n + i];
+      double r = sigm(U[i] + ar * s[i] + bias(m->bh, i));
+      double z = sigm(U[n + i] + az * s[i] + bias(m->bh, n + i));
+      double q = an * s[i] + bias(m->bh, 2 * n + i);
+      double c = tanh(U[2 * n + i] + r * q);
+      double dc = lam[i] * (1.0 - z);
+      double dz = lam[i] * (s[i] - c);
+      double daz = dz * z * (1.0 - z);
+      double dan = dc * (1.0 - c * c);
+      double dq = dan * r;
+      double dar = dan * q * r * (1.0 - r);
+      ds[i] = lam[i] * z + dar * ar + daz * az + dq * an;
+      dU[i] = dar; dU[n + i] = daz; dU[2 * n + i] = dan;
+      dbh[i] += dar; dbh[n + i] += daz; dbh[2 * n + i] += dq;
+      dWh[i] += dar * s[i]; dWh[n + i] += daz * s[i]; dWh[2 * n + i] += dq * s[i];
+    }
+    break;
+  case ORC_LSTM:
+    for (int i = 0; i < n; i++) {
+      double c = s[2 * i], h = s[2 * i + 1];
+      double wf = m->Wh[i], wg = m->Wh[n + i], wo = m->Wh[2 * n + i];
+      double pf = m->peep[i], po = m->peep[n + i];
+      double fg = sigm(U[i] + wf * h + pf * c + bias(m->bh, i));
+      double g = tanh(U[n + i] + wg * h + bias(m->bh, n + i));
+      double cn = fg * c + (1.0 - fg) * g;
+      double o = sigm(U[2 * n + i] + wo * h + po * cn + bias(m->bh, 2 * n + i));
+      double tc = tanh(cn);
+      double lc = lam[2 * i], lh = lam[2 * i + 1];
+      double dao = lh * tc * o * (1.0 - o);
+      double dcn = lc + lh * o * (1.0 - tc * tc) + dao * po;
+      double daf = dcn * (c - g) * fg * (1.0 - fg);
+      double dag = dcn * (1.0 - fg) * (1.0 - g * g);
+      ds[2 * i] = dcn * fg + daf * pf;
+      ds[2 * i + 1] = daf * wf + dag * wg + dao * wo;
+      dU[i] = daf; dU[n + i] = dag; dU[2 * n + i] = dao;
+      dbh[i] += daf; dbh[n + i] += dag; dbh[2 * n + i] += dao;
+      dWh[i] += daf * h; dWh[n + i] += dag * h; dWh[2 * n + i] += dao * h;
+      dpeep[i] += daf * c; dpeep[n + i] += dao * cn;
+    }
+    break;
+  }
+}
+
+static int model_ok(const orc_model *m) {
+  if (m->cell < 0 || m->cell > 4) return 0;
+  if (m->B < 0 || m->T < 0 || m->d < 1 || m->n < 1) return 0;
+  if (!m->Wx || !m->Wh) return 0;
+  if (m->cell == ORC_LSTM && !m->peep) return 0;
+  return 1;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Exported API                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* One cell step (f and its structured Jacobian) at s_prev, x_t. */
+int orc_cell(const orc_model *m, const double *s_prev, const double *xt, double *f, double *J) {
+  if (!model_ok(m)) return ORC_EINVAL;
+  int Gn = n_gates(m->cell) * m->n;
+  double *U = (double *)malloc(sizeof(double) * Gn);
+  if (!U) return ORC_ENOMEM;
+  input_proj(m, xt, U);
+  cell_fwd(m, s_prev, U, f, J);
+  free(U);
+  return ORC_OK;
+}
+
+/* One reverse-mode cell step: ds = J^T lam and dU = (df/dU)^T lam. */
+int orc_cell_vjp(const orc_model *m, const double *s_prev, const double *xt, const double *lam,
+                 double *ds, double *dU) {
+  if (!model_ok(m)) return ORC_EINVAL;
+  int Gn = n_gates(m->cell) * m->n;
+  double *U = (double *)malloc(sizeof(double) * Gn);
+  double *dWh = (double *)calloc(wh_size(m), sizeof(double));
+  double *dbh = (double *)calloc(Gn, sizeof(double));
+  double *dp = (double *)calloc(2 * m->n, sizeof(double));
+  if (!U || !dWh || !dbh || !dp) { free(U); free(dWh); free(dbh); free(dp); return ORC_ENOMEM; }
+  input_proj(m, xt, U);
+  cell_vjp(m, s_prev, U, lam, ds, dU, dWh, dbh, dp);
+  free(U); free(dWh); free(dbh); free(dp);
+  return ORC_OK;
+}
+
+/* Sequential rollout h_t = f(h_{t-1}, x_t), h_{-1} = h0 (NULL = 0).  h: [B,T,S]. */
+int orc_rollout(const orc_model *m, const double *x, const double *h0, double *h) {
+  if (!model_ok(m)) return ORC_EINVAL;
+  int S = swidth(m), Gn = n_gates(m->cell) * m->n, err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int b = 0; b < m->B; b++) {
+    double *U = (double *)malloc(sizeof(double) * Gn);
+    double *s = (double *)malloc(sizeof(double) * S);
+    if (!U || !s) { err |= 1; free(U); free(s); continue; }
+    for (int i = 0; i < S; i++) s[i] = h0 ? h0[(size_t)b * S + i] : 0.0;
+    for (int t = 0; t < m->T; t++) {
+      const double *xt = x + ((size_t)b * m->T + t) * m->d;
+      double *ht = h + ((size_t)b * m->T + t) * S;
+      input_proj(m, xt, U);
+      cell_fwd(m, s, U, ht, NULL);
+      memcpy(s, ht, sizeof(double) * S);
+    }
+    free(U); free(s);
+  }
+  return err ? ORC_ENOMEM : ORC_OK;
+}
+
+/* y = A y_prev + b for one step of an operator of the given structure. */
+static void affine_step(int kind, int n, const double *A, const double *yprev, const double *b, double *y) {
+  if (kind == ORC_DENSE) {
+    for (int i = 0; i < n; i++) {
+      double a = b[i];
+      for (int k = 0; k < n; k++) a += A[(size_t)i * n + k] * yprev[k];
+      y[i] = a;
+    }
+  } else if (kind == ORC_DIAG) {
+    for (int i = 0; i < n; i++) y[i] = A[i] * yprev[i] + b[i];
+  } else { /* n channels, 2x2 blocks, state interleaved */
+    for (int i = 0; i < n; i++) {
+      const double *Ab = A + (size_t)4 * i;
+      double y0 = yprev[2 * i], y1 = yprev[2 * i + 1];
+      y[2 * i] = Ab[0] * y0 + Ab[1] * y1 + b[2 * i];
+      y[2 * i + 1] = Ab[2] * y0 + Ab[3] * y1 + b[2 * i + 1];
+    }
+  }
+}
+
+/*
+ * The linear recurrence by its definition, per sequence b:
+ *   forward:  y_t = A_t y_{t-1} + b_t,  y_{-1} = 0;
+ *   reverse:  y_t = A_t y_{t+1} + b_t,  y_T = 0.
+ * kind DENSE: A [B,T,n,n], b,y [B,T,n]; DIAG: A,b,y [B,T,n];
+ * BLOCK2: A [B,T,n,2,2], b,y [B,T,n,2].
+ */
+int orc_affine_solve(int kind, int B, int T, int n, int reverse, const double *A, const double *bv, double *y) {
+  if (kind < 0 || kind > 2 || B < 0 || T < 0 || n < 1) return ORC_EINVAL;
+  int S = kind == ORC_BLOCK2 ? 2 * n : n;
+  size_t js = kind == ORC_DENSE ? (size_t)n * n : (kind == ORC_DIAG ? (size_t)n : (size_t)4 * n);
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int b = 0; b < B; b++) {
+    double *zero = (double *)calloc(S, sizeof(double));
+    if (!zero) { err |= 1; continue; }
+    for (int s = 0; s < T; s++) {
+      int t = reverse ? T - 1 - s : s;
+      const double *yp = s == 0 ? zero : y + ((size_t)b * T + (reverse ? t + 1 : t - 1)) * S;
+      affine_step(kind, n, A + ((size_t)b * T + t) * js, yp, bv + ((size_t)b * T + t) * S,
+                  y + ((size_t)b * T + t) * S);
+    }
+    free(zero);
+  }
+  return err ? ORC_ENOMEM : ORC_OK;
+}
+
+/*
+ * CPU DEER.  h: [B,T,S] output (the last iterate); iters, status out;
+ * deltas: [hist_cap] history of delta_k = max |dh| (entry k-1 for sweep k).
+ *
+ * Sweep k, for every sequence:
+ *   1. for every t: s_prev = (t == 0 ? h0 : h_{t-1}) of the current iterate;
+ *      f_t, J_t = cell(s_prev, U_t);  r_t = f_t - h_t;
+ *   2. dh_0-1 = 0;  for t = 0..T-1: dh_t = J_t dh_{t-1} + r_t  (sequential);
+ *   3. h_t += dh_t.
+ * delta_k is the max over the whole batch.  Stop rule: non-finite delta ->
+ * NONFINITE; tol > 0 and delta < tol -> OK; k == T -> OK (Newton is exact
+ * after T sweeps); k == max_iters -> NOT_CONVERGED (OK when tol <= 0).
+ */
+int orc_deer(const orc_model *m, const double *x, const double *h0, double tol, int max_iters,
+             double *h, int *iters, int *status, double *deltas, int hist_cap) {
+  if (!model_ok(m) || max_iters < 1) return ORC_EINVAL;
+  int S = swidth(m), Gn = n_gates(m->cell) * m->n, T = m->T;
+  size_t js = jsize(m);
+  int kind = jkind(m->cell);
+  memset(h, 0, sizeof(double) * (size_t)m->B * T * S); /* initial guess: zeros */
+  *iters = 0;
+  *status = ORC_OK;
+  if (T == 0 || m->B == 0) return ORC_OK;
+  for (int k = 1; k <= max_iters; k++) {
+    double delta = 0.0;
+    int err = 0, nonfin = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : delta) reduction(| : err, nonfin)
+    for (int b = 0; b < m->B; b++) {
+      double *U = (double *)malloc(sizeof(double) * Gn);
+      double *F = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *R = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *D = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *Jb = (double *)malloc(sizeof(double) * (size_t)T * js);
+      double *zero = (double *)calloc(S, sizeof(double));
+      if (!U || !F || !R || !D || !Jb || !zero) {
+        err |= 1;
+      } else {
+        double *hb = h + (size_t)b * T * S;
+        /* 1. cell, Jacobian and residual at every step (the parallel part). */
+        for (int t = 0; t < T; t++) {
+          const double *sp = t == 0 ? (h0 ? h0 + (size_t)b * S : zero) : hb + (size_t)(t - 1) * S;
+          input_proj(m, x + ((size_t)b * T + t) * m->d, U);
+          cell_fwd(m, sp, U, F + (size_t)t * S, Jb + (size_t)t * js);
+          for (int i = 0; i < S; i++) R[(size_t)t * S + i] = F[(size_t)t * S + i] - hb[(size_t)t * S + i];
+        }
+        /* 2. the linear recurrence, sequentially. */
+        for (int t = 0; t < T; t++)
+          affine_step(kind, m->n, Jb + (size_t)t * js, t == 0 ? zero : D + (size_t)(t - 1) * S,
+                      R + (size_t)t * S, D + (size_t)t * S);
+        /* 3. update and convergence measure. */
+        for (size_t e = 0; e < (size_t)T * S; e++) {
+          hb[e] += D[e];
+          double a = fabs(D[e]);
+          if (!isfinite(a)) nonfin = 1;
+          else if (a > delta) delta = a;
+        }
+      }
+      free(U); free(F); free(R); free(D); free(Jb); free(zero);
+    }
+    if (err) return ORC_ENOMEM;
+    if (nonfin) delta = NAN;
+    if (deltas && k <= hist_cap) deltas[k - 1] = delta;
+    *iters = k;
+    if (!isfinite(delta)) { *status = ORC_NONFINITE; return ORC_OK; }
+    if (tol > 0.0 && delta < tol) { *status = ORC_OK; return ORC_OK; }
+    if (k == T) { *status = ORC_OK; return ORC_OK; }
+  }
+  *status = tol > 0.0 ? ORC_NOT_CONVERGED : ORC_OK;
+  return ORC_OK;
+}
+
+/*
+ * Gradient of L = sum_{b,t} <g_t, h_t> through the recurrence at the given
+ * trajectory h (reverse-mode, t = T-1 .. 0):
+ *   lam_t = g_t + carry;  (carry, dU_t, dtheta) = cell_vjp at (h_{t-1}, U_t, lam_t).
+ * Outputs (each may be NULL): lam [B,T,S]; dx [B,T,d]; dh0 [B,S]; dWx [Gn,d];
+ * dbx [Gn]; dWh (dense [Gn,n] / diag [Gn]); dbh [Gn]; dpeep [2n].
+ * Parameter gradients are summed per sequence and then over b in order.
+ */
+int orc_adjoint(const orc_model *m, const double *x, const double *h0, const double *h, const double *g,
+                double *lam, double *dx, double *dh0, double *dWx, double *dbx, double *dWh, double *dbh,
+                double *dpeep) {
+  if (!model_ok(m)) return ORC_EINVAL;
+  int S = swidth(m), Gn = n_gates(m->cell) * m->n, T = m->T, B = m->B, d = m->d, n = m->n;
+  size_t nwx = (size_t)Gn * d, nwh = wh_size(m);
+  size_t per = nwx + Gn + nwh + Gn + 2 * (size_t)n;
+  double *acc = (double *)calloc((size_t)(B > 0 ? B : 1) * per, sizeof(double));
+  if (!acc) return ORC_ENOMEM;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int b = 0; b < B; b++) {
+    double *A = acc + (size_t)b * per;
+    double *aWx = A, *abx = A + nwx, *aWh = abx + Gn, *abh = aWh + nwh, *ap = abh + Gn;
+    double *U = (double *)malloc(sizeof(double) * Gn);
+    double *dU = (double *)malloc(sizeof(double) * Gn);
+    double *carry = (double *)calloc(S, sizeof(double));
+    double *ds = (double *)malloc(sizeof(double) * S);
+    double *lt = (double *)malloc(sizeof(double) * S);
+    double *zero = (double *)calloc(S, sizeof(double));
+    if (!U || !dU || !carry || !ds || !lt || !zero) {
+      err |= 1;
+    } else {
+      for (int t = T - 1; t >= 0; t--) {
+        const double *xt = x + ((size_t)b * T + t) * d;
+        const double *sp = t == 0 ? (h0 ? h0 + (size_t)b * S : zero) : h + ((size_t)b * T + t - 1) * S;
+        for (int i = 0; i < S; i++) lt[i] = g[((size_t)b * T + t) * S + i] + carry[i];
+        if (lam) memcpy(lam + ((size_t)b * T + t) * S, lt, sizeof(double) * S);
+        input_proj(m, xt, U);
+        cell_vjp(m, sp, U, lt, ds, dU, aWh, abh, ap);
+        for (int j = 0; j < Gn; j++) {
+          abx[j] += dU[j];
+          for (int k = 0; k < d; k++) aWx[(size_t)j * d + k] += dU[j] * xt[k];
+        }
+        if (dx)
+          for (int k = 0; k < d; k++) {
+            double a = 0.0;
+            for (int j = 0; j < Gn; j++) a += m->Wx[(size_t)j * d + k] * dU[j];
+            dx[((size_t)b * T + t) * d + k] = a;
+          }
+        memcpy(carry, ds, sizeof(double) * S);
+      }
+      if (dh0) memcpy(dh0 + (size_t)b * S, carry, sizeof(double) * S);
+    }
+    free(U); free(dU); free(carry); free(ds); free(lt); free(zero);
+  }
+  if (!err) {
+    double *outs[5] = {dWx, dbx, dWh, dbh, dpeep};
+    size_t off[5] = {0, nwx, nwx + Gn, nwx + Gn + nwh, nwx + Gn + nwh + Gn};
+    size_t cnt[5] = {nwx, (size_t)Gn, nwh, (size_t)Gn, 2 * (size_t)n};
+    for (int o = 0; o < 5; o++) {
+      if (!outs[o]) continue;
+      if (o == 4 && m->cell != ORC_LSTM) continue;
+      for (size_t e = 0; e < cnt[o]; e++) {
+        double a = 0.0;
+        for (int b = 0; b < B; b++) a += acc[(size_t)b * per + off[o] + e];
+        outs[o][e] = a;
+      }
+    }
+  }
+  free(acc);
+  return err ? ORC_ENOMEM : ORC_OK;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
