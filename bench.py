@@ -1,0 +1,197 @@
+"""Benchmark of the DEER / quasi-DEER hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the Newton solve to
+convergence (input projection, every sweep, the on-device stop rule and its
+polls) followed by the adjoint (reverse scan, chain rule, weight-gradient
+reductions).  Inputs are seeded synthetic data already resident in HBM.
+
+Default workload: the scalar-state GRU at batch 16 and length 2^20 that the
+DEER paper times on a V100 ("Parallelizing non-linear sequential models over
+the sequence length", Key results: 15 ms DEER vs 8.7 s sequential).
+
+Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFS = 157.3
+# DEER on a V100, GRU n=1, batch 16, length 2^20: 15 ms forward (pages' figure)
+V100_DEER_TSB_PER_S = 16 * (1 << 20) / 15e-3
+
+
+def sweep_bytes_per_unit(p: dict, k: int) -> float:
+    """Algorithmic HBM bytes per (b, t) unit of one fused Newton sweep.
+
+    Sweep 1 starts from h = 0, so it reads x and writes h; later sweeps also
+    read the current iterate h.  (fp32: x, h in, h out = 4 + 4 + 4 bytes for
+    the scalar GRU.)
+    """
+    es = 2 if p["dtype"] == 1 else 4
+    xin = p["d"] * 4 if p["cfg"] in (1, 2) else 0
+    hb = p["S"] * es
+    return xin + hb + (hb if k >= 2 else 0)
+
+
+def adjoint_bytes_per_unit(p: dict) -> float:
+    """Reads x, h, g; writes lambda and dx (fp32, fused projection)."""
+    es = 2 if p["dtype"] == 1 else 4
+    return p["d"] * 4 + 2 * p["S"] * es + p["S"] * es + p["d"] * 4
+
+
+def cpu_baseline(p: dict) -> dict:
+    import numpy as np
+    import oracle
+    threads = min(oracle.num_threads(), p["B"])
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    t0 = time.perf_counter()
+    oracle.rollout(p)
+    dt = time.perf_counter() - t0
+    units = p["B"] * p["T"]
+    return {"value": units / dt, "unit": "timesteps*batch/s", "cores": threads, "kind": "oracle",
+            "sample": f"full workload: fp64 sequential rollout of all {p['B']} sequences x {p['T']} steps, "
+                      f"OpenMP over sequences; {dt:.2f} s wall", "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GRU n=1, B=16, T=2^20)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="do not bracket kernels with events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 launches), to scale HBM counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    from nonlinear_rnn_evaluation_newton_amd import binding as bd
+    from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
+        return 0
+    p = sy.make_problem(args.config)
+    dp = bd.DeviceProblem(p)
+    B, T = p["B"], p["T"]
+    units = B * T
+
+    f32 = dict(dtype=torch.float32, device="cuda")
+    lam = torch.empty_like(dp.h)
+    dx = torch.empty_like(dp.x)
+    dh0 = torch.empty((B, p["S"]), dtype=dp.tdtype, device="cuda")
+    grads = dict(W_x=torch.empty(tuple(dp.W_x.shape), **f32), b_x=torch.empty(tuple(dp.b_x.shape), **f32),
+                 W_h=torch.empty(tuple(dp.W_h.shape), **f32), b_h=torch.empty(tuple(dp.b_h.shape), **f32))
+    if dp.peep is not None:
+        grads["peep"] = torch.empty(tuple(dp.peep.shape), **f32)
+
+    iters_seen = []
+
+    def step():
+        st, it, dl = dp.solve()
+        if st < 0 or st == bd.PR_NONFINITE:
+            raise RuntimeError(f"solve failed: {st}")
+        iters_seen.append(it)
+        bd.adjoint(dp.prob, dp.w, dp.x, dp.h0, dp.h, dp.g, dp.ws, lam, dx, dh0, grads)
+        return it, dl
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    if not args.no_trace:
+        bd.trace(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        it, dl = step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = bd.trace_read() if not args.no_trace else None
+    bd.trace(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # solve alone (context; same inputs)
+    torch.cuda.synchronize()
+    s0 = time.perf_counter()
+    for _ in range(args.steps):
+        dp.solve()
+    torch.cuda.synchronize()
+    ms_solve = (time.perf_counter() - s0) * 1e3 / args.steps
+
+    iters = iters_seen[-1]
+    roofline = None
+    extra = {}
+    if tr is not None and tr["sweep_launches"] > 0:
+        per_step_bytes = sum(sweep_bytes_per_unit(p, k) for k in range(1, iters + 1)) * units
+        nsteps = tr["sweep_launches"] / iters
+        avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
+        achieved = per_step_bytes * nsteps / (tr["sweep_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_time_sweep (fused cell + Jacobian + scan + update)",
+                    "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "bytes_per_launch": per_step_bytes / iters}
+        if tr["adjoint_launches"] > 0:
+            adj_ms = tr["adjoint_ms"] / tr["adjoint_launches"]
+            extra["adjoint_kernel"] = {"avg_launch_us": round(adj_ms * 1e3, 2),
+                                       "achieved_GBs": round(adjoint_bytes_per_unit(p) * units / (adj_ms * 1e-3) / 1e9, 1)}
+
+    value = units / (ms_step * 1e-3)
+    line = {
+        "metric": "timesteps*batch/sec per converged Newton solve; scan HBM GB/s; speedup vs seq",
+        "value": value,
+        "unit": "timesteps*batch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (value / V100_DEER_TSB_PER_S) if args.config == 2 else None,
+        "dtype": "bf16" if p["dtype"] == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": p["name"], "cell": sy.CELL_NAMES[p["cell"]], "B": B, "T": T, "d": p["d"],
+                   "n": p["n"], "tol": p["tol"], "max_iters": p["max_iters"], "step": "solve + adjoint"},
+        "iters": iters,
+        "final_delta": float(dl[-1]) if len(dl) else None,
+        "solve_ms": ms_solve,
+        "solve_value": units / (ms_solve * 1e-3),
+        "roofline": roofline,
+        **extra,
+    }
+    if args.config == 2:
+        line["vs_baseline_basis"] = "V100 DEER forward-only 15 ms (pages); value here includes the adjoint"
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(p)
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["speedup_vs_seq"] = cb["seconds"] / (ms_solve * 1e-3)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

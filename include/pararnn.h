@@ -1,0 +1,176 @@
+/*
+ * pararnn.h -- C ABI of the MI355X (gfx950) library for Newton (DEER) and
+ * quasi-Newton (quasi-DEER) evaluation of nonlinear RNNs over the sequence
+ * length, and for the adjoint gradient of that evaluation.
+ *
+ * The method: the T recurrences h_t = f(h_{t-1}, x_t) are one nonlinear system
+ * of equations (ParaRNN abstract; Gonzalez et al. abstract: the states are the
+ * solution of a fixed-point problem).  Each Newton sweep evaluates the cell
+ * and its Jacobian J_t = df/dh at every step, forms r_t = f_t - h_t, solves the
+ * linear recurrence dh_t = J_t dh_{t-1} + r_t with a parallel associative
+ * prefix scan, and updates h += dh ("Parallelizing non-linear sequential models
+ * over the sequence length", Approach).  Jacobians are dense (full DEER),
+ * diagonal (quasi-DEER / ParaGRU) or 2x2 block-diagonal (ParaLSTM) (Para-Seq
+ * README, Main features).  The gradient needs one reverse linear solve with the
+ * transposed Jacobians (DEER summary, Surprising findings).
+ *
+ * Conventions for every entry point
+ *  - All array arguments are device pointers to caller-owned memory, row-major,
+ *    batch-first ([B, T, ...]).  The library never allocates device memory;
+ *    all scratch lives in the caller's workspace.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is ordered
+ *    on it.  pararnn_solve returns after it has read the iteration count back
+ *    (host-synchronous on `stream`); the other calls are asynchronous.
+ *  - Negative return values are errors (outputs undefined); positive values
+ *    are soft failures whose outputs are valid.  Arguments are validated before
+ *    any HIP call, so PR_EINVAL / PR_EWORKSPACE / PR_EUNSUPPORTED never touch
+ *    the device.  pararnn_last_error() gives a message for the calling thread.
+ *  - Calls on the same workspace must not overlap; distinct workspaces may be
+ *    used concurrently.
+ */
+#ifndef PARARNN_H
+#define PARARNN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- cells (the standard RNN cells Para-Seq keeps, README intro) --------- */
+/* f = tanh(W_x x + b_x + W_h h + b_h)                              G = 1, S = n */
+#define PR_CELL_TANH_RNN 0
+/* PyTorch GRU, gate order r|z|n, b_hn inside r*(.), h' = (1-z) c + z h.  G = 3 */
+#define PR_CELL_GRU 1
+/* The same GRU with diagonal recurrent weights W_h = [a_r | a_z | a_n] (each [n])
+ * (ParaGRU, Para-Seq README Main features).                        G = 3, S = n */
+#define PR_CELL_GRU_DIAG 2
+/* CIFG ParaLSTM with peepholes, per channel state (c, h) stored interleaved:
+ *   f = sigm(U_f + w_f h + p_f c + b_f), g = tanh(U_g + w_g h + b_g),
+ *   c' = f c + (1-f) g, o = sigm(U_o + w_o h + p_o c' + b_o), h' = o tanh(c').
+ * W_h = [w_f | w_g | w_o] (each [n]); peep = [p_f | p_o].       G = 3, S = 2n */
+#define PR_CELL_LSTM_CIFG_DIAG 3
+/* f = W_x x + b_x + W_h h + b_h: a linear state-space recurrence; Newton is
+ * exact after one update.                                          G = 1, S = n */
+#define PR_CELL_LINEAR 4
+
+/* ---- Jacobian structure used by the Newton linear solve ------------------ */
+#define PR_JAC_DENSE 0   /* n x n per step: TANH_RNN, GRU, LINEAR                */
+#define PR_JAC_DIAG 1    /* n per step: GRU_DIAG (exact); GRU with n == 1         */
+#define PR_JAC_BLOCK2 2  /* 2x2 per channel: LSTM_CIFG_DIAG                       */
+
+/* ---- storage dtype of x, weights, h0, h, g, lambda, dx, dh0 -------------- */
+/* Arithmetic, scan carries and the convergence measure are always fp32.
+ * Gradients of the weights (pr_grads) are always fp32.                       */
+#define PR_F32 0
+#define PR_BF16 1
+
+/* ---- status codes -------------------------------------------------------- */
+#define PR_OK 0
+#define PR_EINVAL (-1)        /* bad enum, size <= 0, NULL required pointer, max_iters < 1 */
+#define PR_EWORKSPACE (-2)    /* workspace NULL or smaller than pararnn_*workspace_bytes   */
+#define PR_EHIP (-3)          /* a HIP runtime call failed                                */
+#define PR_EUNSUPPORTED (-5)  /* valid problem this build has no kernel for               */
+#define PR_NOT_CONVERGED 1    /* max_iters sweeps, delta never < tol; h = last iterate   */
+#define PR_NONFINITE 2        /* delta became NaN/Inf; h = that iterate                   */
+
+typedef struct {
+  int cell;   /* PR_CELL_*                              */
+  int jac;    /* PR_JAC_*, must suit the cell (above)   */
+  int dtype;  /* PR_F32 or PR_BF16                      */
+  int B;      /* batch (independent sequences), >= 1    */
+  int T;      /* sequence length, >= 1                  */
+  int d;      /* input width, >= 1                      */
+  int n;      /* hidden channels, >= 1 (state S = n or 2n) */
+} pr_problem;
+
+/* Weights, device pointers in the problem's storage dtype.  G = gate count. */
+typedef struct {
+  const void *W_x;  /* [G*n, d], required                                   */
+  const void *b_x;  /* [G*n] or NULL (= 0)                                  */
+  const void *W_h;  /* dense cells [G*n, n]; diagonal cells [G*n]; required */
+  const void *b_h;  /* [G*n] or NULL (= 0)                                  */
+  const void *peep; /* LSTM: [2n] = p_f | p_o, required; others: ignored    */
+} pr_weights;
+
+/* Weight gradients, fp32 device pointers with the shapes of pr_weights; any
+ * field may be NULL to skip it.  They are overwritten, not accumulated.      */
+typedef struct {
+  float *W_x;
+  float *b_x;
+  float *W_h;
+  float *b_h;
+  float *peep;
+} pr_grads;
+
+/* Bytes of workspace pararnn_solve (with_adjoint = 0) or both pararnn_solve
+ * and pararnn_adjoint (with_adjoint = 1) need; 0 for an invalid problem. */
+size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint);
+
+/*
+ * Newton solve of the recurrence from the initial guess h = 0 everywhere.
+ *   x     [B, T, d]                input sequence
+ *   h0    [B, S] or NULL (= 0)     state before the first step
+ *   tol   stop when delta_k = max over (b, t, i) of |dh| is < tol; tol <= 0
+ *         runs exactly max_iters sweeps (fixed-iteration mode)
+ *   max_iters >= 1; a solve also stops after sweep T, where Newton is exact
+ *   h     [B, T, S] output: the final iterate (it is used as the iterate in
+ *         place, so it must not alias x or h0)
+ *   iters (host, may be NULL) number of sweeps run, including the one that met tol
+ *   delta_hist (host, may be NULL) delta_k for k = 1 .. min(iters, hist_cap, 1024)
+ * Returns PR_OK, PR_NOT_CONVERGED (tol > 0 and max_iters sweeps done),
+ * PR_NONFINITE, or an error.
+ */
+int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                  int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
+                  size_t ws_bytes, void *stream);
+
+/*
+ * Gradient of L = sum_{b,t} <g_t, h_t> at the trajectory h (normally the
+ * output of pararnn_solve), by one reverse linear solve
+ *   lambda_t = g_t + J_{t+1}^T lambda_{t+1},  lambda_T-1 = g_T-1,
+ * with J re-evaluated at h, followed by the chain rule through each cell.
+ *   g      [B, T, S]               upstream gradient dL/dh
+ *   lambda [B, T, S] or NULL       output: the adjoint state
+ *   dx     [B, T, d] or NULL       output: dL/dx
+ *   dh0    [B, S] or NULL          output: dL/dh0
+ *   dW     NULL or the fp32 weight-gradient outputs (fields may be NULL)
+ * The workspace must be at least pararnn_workspace_bytes(p, 1).
+ */
+int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0,
+                    const void *h, const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The linear recurrence alone (the Newton inner solve), fp32, per sequence:
+ *   reverse = 0:  y_t = A_t y_{t-1} + b_t,  y_{-1} = 0
+ *   reverse = 1:  y_t = A_t y_{t+1} + b_t,  y_T = 0
+ * PR_JAC_DIAG:   A, b, y [B, T, n]
+ * PR_JAC_BLOCK2: A [B, T, n, 2, 2], b, y [B, T, n, 2]
+ * PR_JAC_DENSE:  A [B, T, n, n], b, y [B, T, n]   (n <= 8)
+ */
+size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n);
+int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *A, const float *b,
+                        float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Kernel timing for profiling and benchmarks (per calling thread).
+ * pararnn_trace(1) clears the counters and starts bracketing, with HIP events
+ * on the call's stream, every Newton-sweep launch that does work (launches
+ * after the stop rule has fired are not counted) and the main kernel of each
+ * adjoint; pararnn_trace(0) stops.  pararnn_trace_read waits for pending
+ * events and returns the totals (any pointer may be NULL).
+ */
+int pararnn_trace(int enable);
+int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches);
+
+/* Static text for a status code. */
+const char *pararnn_strerror(int status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *pararnn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARARNN_H */

@@ -1,0 +1,57 @@
+// Host-side interface between the ABI layer (pararnn.cpp) and the kernel
+// files.  Every launch_* returns a hipError_t and validates nothing: the ABI
+// layer checks shapes, pointers and workspace sizes before it calls them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace pr {
+
+constexpr int DX_FUSED = 8;  // largest input width folded into the time-parallel kernels
+
+// ---------------- time-parallel path (dense state, n <= 8) -----------------
+struct TimeArgs {
+  const float *x;   // [B,T,d]
+  float *h;         // [B,T,n] iterate, updated in place (read-only in the adjoint)
+  const float *h0;  // [B,n] or null
+  const float *Wx, *bx, *Wh, *bh;
+  const float *g;   // adjoint: [B,T,n]
+  float *lam, *dx, *dh0;  // adjoint outputs (may be null)
+  float *part;            // adjoint: per-tile parameter-gradient partials
+  int B, T, d, n;
+  int k;
+  float tol;
+  int max_iters;
+  SolveState *st;
+  unsigned long long *agg, *incl;  // look-back descriptors
+  float *bnd;                      // [2][ntiles][N] boundary states
+  int tiles_per_seq, ntiles, vec_ok;
+  int nparts;  // adjoint: blocks that wrote weight partials (set by the launcher)
+};
+
+int time_tile(int N);               // elements per tile for padded width N
+int time_padded_n(int n);           // N for a given n (0 if unsupported)
+int time_part_count(int cell, int N);  // floats per tile of gradient partials
+hipError_t launch_time_sweep(int cell, int N, const TimeArgs &a, hipStream_t s);
+hipError_t launch_time_adjoint(int cell, int N, TimeArgs &a, hipStream_t s);
+hipError_t launch_time_reduce(int cell, int N, const TimeArgs &a, const float *part, float *dWx, float *dbx,
+                              float *dWh, float *dbh, hipStream_t s);
+
+struct ScanArgs {
+  const float *A, *b;
+  float *y;
+  int B, T, n, reverse;
+  unsigned long long *agg, *incl;
+  SolveState *st;
+  int tiles_per_seq, ntiles;
+};
+hipError_t launch_time_scan(int N, const ScanArgs &a, hipStream_t s);
+
+// ---------------- utilities ------------------------------------------------
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace pr

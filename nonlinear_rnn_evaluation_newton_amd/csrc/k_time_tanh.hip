@@ -1,0 +1,14 @@
+// Time-parallel kernels instantiated for one cell (one translation unit per
+// cell keeps compile times short).
+#include "k_time_impl.h"
+
+namespace pr {
+
+hipError_t time_sweep_tanh(int Nv, const TimeArgs &a, hipStream_t s) { return time_sweep_cell<C_TANH>(Nv, a, s); }
+hipError_t time_adjoint_tanh(int Nv, TimeArgs &a, hipStream_t s) { return time_adjoint_cell<C_TANH>(Nv, a, s); }
+hipError_t time_reduce_tanh(int Nv, const TimeArgs &a, const float *part, float *dWx, float *dbx, float *dWh,
+                             float *dbh, hipStream_t s) {
+  return time_reduce_cell<C_TANH>(Nv, a, part, dWx, dbx, dWh, dbh, s);
+}
+
+}  // namespace pr

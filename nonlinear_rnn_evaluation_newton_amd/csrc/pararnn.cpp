@@ -1,0 +1,399 @@
+// C ABI of libpararnn: argument validation, workspace planning, the host side
+// of the Newton loop (asynchronous sweeps, on-device stop rule, rare polls of
+// a 4 KB state record) and dispatch to the kernel families.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.h"
+#include "pararnn.h"
+
+using namespace pr;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(PR_EHIP, "%s: %s", #expr, hipGetErrorString(e_));       \
+  } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+enum { PATH_NONE = 0, PATH_TIME = 1 };
+
+struct Plan {
+  int path = PATH_NONE;
+  int G = 1, S = 1, N = 1;
+  int tile = 0, tps = 0, ntiles = 0;
+  size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
+  size_t zero_bytes = 0;     // bytes cleared at the start of each call
+  size_t solve_bytes = 0, adjoint_bytes = 0;
+};
+
+int gates_of(int cell) { return (cell == PR_CELL_GRU || cell == PR_CELL_GRU_DIAG || cell == PR_CELL_LSTM_CIFG_DIAG) ? 3 : 1; }
+
+// Validates the problem and picks the kernel family.  Returns PR_OK,
+// PR_EINVAL or PR_EUNSUPPORTED.
+int make_plan(const pr_problem *p, Plan *pl) {
+  if (!p) return fail(PR_EINVAL, "problem is NULL");
+  if (p->cell < 0 || p->cell > 4) return fail(PR_EINVAL, "unknown cell %d", p->cell);
+  if (p->jac < 0 || p->jac > 2) return fail(PR_EINVAL, "unknown jac %d", p->jac);
+  if (p->dtype != PR_F32 && p->dtype != PR_BF16) return fail(PR_EINVAL, "unknown dtype %d", p->dtype);
+  if (p->B < 1 || p->T < 1 || p->d < 1 || p->n < 1)
+    return fail(PR_EINVAL, "sizes must be >= 1 (B=%d T=%d d=%d n=%d)", p->B, p->T, p->d, p->n);
+  const bool dense_cell = p->cell == PR_CELL_TANH_RNN || p->cell == PR_CELL_GRU || p->cell == PR_CELL_LINEAR;
+  bool jac_ok = false;
+  if (dense_cell) jac_ok = p->jac == PR_JAC_DENSE || (p->jac == PR_JAC_DIAG && p->n == 1);
+  if (p->cell == PR_CELL_GRU_DIAG) jac_ok = p->jac == PR_JAC_DIAG;
+  if (p->cell == PR_CELL_LSTM_CIFG_DIAG) jac_ok = p->jac == PR_JAC_BLOCK2;
+  if (!jac_ok) return fail(PR_EINVAL, "jac %d does not suit cell %d", p->jac, p->cell);
+  if ((double)p->B * p->T * p->n * 2 > 2147483647.0 * 64) return fail(PR_EUNSUPPORTED, "problem too large");
+
+  pl->G = gates_of(p->cell);
+  pl->S = p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 * p->n : p->n;
+  if (dense_cell && p->n <= 8 && p->d <= DX_FUSED) {
+    if (p->dtype != PR_F32) return fail(PR_EUNSUPPORTED, "dense cells with n <= 8 run in fp32 storage only");
+    pl->path = PATH_TIME;
+    pl->N = time_padded_n(p->n);
+    pl->tile = time_tile(pl->N);
+    pl->tps = (p->T + pl->tile - 1) / pl->tile;
+    if ((long long)pl->tps * p->B > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
+    pl->ntiles = pl->tps * p->B;
+    const int N = pl->N;
+    size_t o = 0;
+    pl->off_state = o; o = align256(o + sizeof(SolveState));
+    pl->off_agg = o; o = align256(o + (size_t)pl->ntiles * (N * N + N) * 8);
+    pl->off_incl = o; o = align256(o + (size_t)pl->ntiles * N * 8);
+    pl->zero_bytes = o;
+    pl->off_bnd = o; o = align256(o + (size_t)2 * pl->ntiles * N * 4);
+    pl->solve_bytes = o;
+    pl->off_part = o; o = align256(o + (size_t)pl->ntiles * time_part_count(p->cell, N) * 4);
+    pl->adjoint_bytes = o;
+    return PR_OK;
+  }
+  return fail(PR_EUNSUPPORTED, "no kernel for cell %d jac %d dtype %d n %d d %d", p->cell, p->jac, p->dtype, p->n,
+              p->d);
+}
+
+int kcell(int cell) { return cell == PR_CELL_TANH_RNN ? C_TANH : cell == PR_CELL_LINEAR ? C_LINEAR : C_GRU; }
+
+bool al16(const void *q) { return q == nullptr || ((uintptr_t)q & 15) == 0; }
+
+// Pinned host copy of the solve state, one per thread.
+SolveState *host_state() {
+  thread_local SolveState *hs = nullptr;
+  if (!hs) {
+    if (hipHostMalloc((void **)&hs, sizeof(SolveState), hipHostMallocDefault) != hipSuccess) hs = nullptr;
+  }
+  return hs;
+}
+
+// Event timing of the main kernels (pararnn_trace).
+struct Trace {
+  bool on = false;
+  double sweep_ms = 0, adj_ms = 0;
+  long long sweeps = 0, adjs = 0;
+  static constexpr int CAP = 256;
+  hipEvent_t sw[2 * CAP] = {};
+  hipEvent_t ad[2 * CAP] = {};
+  int ad_pending = 0;
+  bool made = false;
+  hipError_t make() {
+    if (made) return hipSuccess;
+    for (int i = 0; i < 2 * CAP; i++) {
+      hipError_t e = hipEventCreate(&sw[i]);
+      if (e != hipSuccess) return e;
+      e = hipEventCreate(&ad[i]);
+      if (e != hipSuccess) return e;
+    }
+    made = true;
+    return hipSuccess;
+  }
+  hipError_t drain_adjoint() {
+    for (int i = 0; i < ad_pending; i++) {
+      hipError_t e = hipEventSynchronize(ad[2 * i + 1]);
+      if (e != hipSuccess) return e;
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ad[2 * i], ad[2 * i + 1]);
+      if (e != hipSuccess) return e;
+      adj_ms += ms;
+      adjs++;
+    }
+    ad_pending = 0;
+    return hipSuccess;
+  }
+};
+Trace &trace() {
+  thread_local Trace t;
+  return t;
+}
+
+void poll_schedule(int *first, int *next) {
+  *first = 4;
+  *next = 2;
+  const char *e = getenv("PARARNN_POLL");
+  if (e) {
+    int a = 0, b = 0;
+    if (sscanf(e, "%d,%d", &a, &b) == 2 && a > 0 && b > 0) {
+      *first = a;
+      *next = b;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pararnn_strerror(int status) {
+  switch (status) {
+    case PR_OK: return "ok";
+    case PR_EINVAL: return "invalid argument";
+    case PR_EWORKSPACE: return "workspace too small";
+    case PR_EHIP: return "HIP runtime error";
+    case PR_EUNSUPPORTED: return "unsupported problem";
+    case PR_NOT_CONVERGED: return "not converged within max_iters";
+    case PR_NONFINITE: return "non-finite Newton update";
+  }
+  return "unknown status";
+}
+
+const char *pararnn_last_error(void) { return g_err.c_str(); }
+
+int pararnn_trace(int enable) {
+  Trace &t = trace();
+  if (t.on) {
+    hipError_t e = t.drain_adjoint();
+    if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
+  }
+  t.on = enable != 0;
+  t.sweep_ms = t.adj_ms = 0;
+  t.sweeps = t.adjs = 0;
+  if (t.on) {
+    hipError_t e = t.make();
+    if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
+  }
+  return PR_OK;
+}
+
+int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches) {
+  Trace &t = trace();
+  hipError_t e = t.drain_adjoint();
+  if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
+  if (sweep_ms) *sweep_ms = t.sweep_ms;
+  if (sweep_launches) *sweep_launches = t.sweeps;
+  if (adjoint_ms) *adjoint_ms = t.adj_ms;
+  if (adjoint_launches) *adjoint_launches = t.adjs;
+  return PR_OK;
+}
+
+size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
+  Plan pl;
+  if (make_plan(p, &pl) != PR_OK) return 0;
+  return with_adjoint ? pl.adjoint_bytes : pl.solve_bytes;
+}
+
+int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol, int max_iters,
+                  void *h, int *iters, float *delta_hist, int hist_cap, void *workspace, size_t ws_bytes,
+                  void *stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != PR_OK) return rc;
+  if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
+  if (p->cell == PR_CELL_LSTM_CIFG_DIAG && !w->peep) return fail(PR_EINVAL, "the LSTM cell needs peepholes");
+  if (!x || !h) return fail(PR_EINVAL, "x and h are required");
+  if (max_iters < 1) return fail(PR_EINVAL, "max_iters must be >= 1");
+  if (tol != tol) return fail(PR_EINVAL, "tol is NaN");
+  if (!workspace || ws_bytes < pl.solve_bytes)
+    return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, pl.solve_bytes);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  SolveState *hs = host_state();
+  if (!hs) return fail(PR_EHIP, "pinned host buffer allocation failed");
+
+  Trace &tr = trace();
+  if (tr.on) HIPCHK(tr.make());
+  HIPCHK(launch_zero(ws, pl.zero_bytes, s));
+  const int kmax = max_iters < p->T ? max_iters : p->T;
+
+  TimeArgs a{};
+  if (pl.path == PATH_TIME) {
+    a.x = (const float *)x;
+    a.h = (float *)h;
+    a.h0 = (const float *)h0;
+    a.Wx = (const float *)w->W_x;
+    a.bx = (const float *)w->b_x;
+    a.Wh = (const float *)w->W_h;
+    a.bh = (const float *)w->b_h;
+    a.B = p->B; a.T = p->T; a.d = p->d; a.n = p->n;
+    a.tol = tol;
+    a.max_iters = max_iters;
+    a.st = (SolveState *)(ws + pl.off_state);
+    a.agg = (unsigned long long *)(ws + pl.off_agg);
+    a.incl = (unsigned long long *)(ws + pl.off_incl);
+    a.bnd = (float *)(ws + pl.off_bnd);
+    a.tiles_per_seq = pl.tps;
+    a.ntiles = pl.ntiles;
+    a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0);
+  }
+
+  int first, next;
+  poll_schedule(&first, &next);
+  if (tol <= 0.f) first = kmax;
+  int k = 1, out_iters = 0, out_status = PR_OK;
+  while (true) {
+    const int batch = k == 1 ? first : next;
+    int k_last = k + batch - 1;
+    if (k_last > kmax) k_last = kmax;
+    for (int kk = k; kk <= k_last; kk++) {
+      a.k = kk;
+      const bool ev = tr.on && kk <= Trace::CAP;
+      if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
+      HIPCHK(launch_time_sweep(kcell(p->cell), pl.N, a, s));
+      if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
+    }
+    HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    if (hs->stopped) {
+      out_iters = hs->iters;
+      out_status = hs->status;
+      break;
+    }
+    int status;
+    unsigned dbits = 0;
+    for (int i = 0; i < PR_DSHARDS; i++) dbits = hs->dslot[k_last & 3][i] > dbits ? hs->dslot[k_last & 3][i] : dbits;
+    hs->hist[k_last % PR_HIST] = dbits;
+    const float dl = __builtin_bit_cast(float, dbits);
+    if (stop_rule(dl, k_last, tol, p->T, max_iters, &status)) {
+      out_iters = k_last;
+      out_status = status;
+      break;
+    }
+    k = k_last + 1;
+  }
+  if (tr.on) {
+    const int m = out_iters < Trace::CAP ? out_iters : Trace::CAP;
+    for (int kk = 1; kk <= m; kk++) {
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (kk - 1)], tr.sw[2 * (kk - 1) + 1]));
+      tr.sweep_ms += ms;
+      tr.sweeps++;
+    }
+  }
+  if (iters) *iters = out_iters;
+  if (delta_hist) {
+    int m = out_iters < hist_cap ? out_iters : hist_cap;
+    if (m > PR_HIST) m = PR_HIST;
+    for (int kk = 1; kk <= m; kk++) delta_hist[kk - 1] = __builtin_bit_cast(float, hs->hist[kk % PR_HIST]);
+  }
+  return out_status == ST_NONFINITE ? PR_NONFINITE : out_status == ST_NOT_CONVERGED ? PR_NOT_CONVERGED : PR_OK;
+}
+
+int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
+                    const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
+                    size_t ws_bytes, void *stream) {
+  g_err.clear();
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != PR_OK) return rc;
+  if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
+  if (p->cell == PR_CELL_LSTM_CIFG_DIAG && !w->peep) return fail(PR_EINVAL, "the LSTM cell needs peepholes");
+  if (!x || !h || !g) return fail(PR_EINVAL, "x, h and g are required");
+  if (!workspace || ws_bytes < pl.adjoint_bytes)
+    return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, pl.adjoint_bytes);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  HIPCHK(launch_zero(ws, pl.zero_bytes, s));
+  if (pl.path == PATH_TIME) {
+    TimeArgs a{};
+    a.x = (const float *)x;
+    a.h = (float *)h;
+    a.h0 = (const float *)h0;
+    a.Wx = (const float *)w->W_x;
+    a.bx = (const float *)w->b_x;
+    a.Wh = (const float *)w->W_h;
+    a.bh = (const float *)w->b_h;
+    a.g = (const float *)g;
+    a.lam = (float *)lambda;
+    a.dx = (float *)dx;
+    a.dh0 = (float *)dh0;
+    a.part = (float *)(ws + pl.off_part);
+    a.B = p->B; a.T = p->T; a.d = p->d; a.n = p->n;
+    a.k = 1;
+    a.st = (SolveState *)(ws + pl.off_state);
+    a.agg = (unsigned long long *)(ws + pl.off_agg);
+    a.incl = (unsigned long long *)(ws + pl.off_incl);
+    a.tiles_per_seq = pl.tps;
+    a.ntiles = pl.ntiles;
+    a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0) | (al16(g) ? 4 : 0) | (al16(lambda) ? 8 : 0);
+    Trace &tr = trace();
+    const bool ev = tr.on && tr.made;
+    if (ev && tr.ad_pending == Trace::CAP) HIPCHK(tr.drain_adjoint());
+    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending], s));
+    HIPCHK(launch_time_adjoint(kcell(p->cell), pl.N, a, s));
+    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending++ + 1], s));
+    if (dW && (dW->W_x || dW->b_x || dW->W_h || dW->b_h))
+      HIPCHK(launch_time_reduce(kcell(p->cell), pl.N, a, a.part, dW->W_x, dW->b_x, dW->W_h, dW->b_h, s));
+    return PR_OK;
+  }
+  return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
+}
+
+size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n) {
+  if (B < 1 || T < 1 || n < 1) return 0;
+  if (jac == PR_JAC_DENSE) {
+    const int N = time_padded_n(n);
+    if (!N) return 0;
+    const size_t nt = (size_t)B * ((T + time_tile(N) - 1) / time_tile(N));
+    return align256(sizeof(SolveState)) + align256(nt * (N * N + N) * 8) + align256(nt * N * 8);
+  }
+  return 0;
+}
+
+int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *A, const float *b, float *y,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  if (jac < 0 || jac > 2) return fail(PR_EINVAL, "unknown jac %d", jac);
+  if (B < 1 || T < 1 || n < 1) return fail(PR_EINVAL, "sizes must be >= 1");
+  if (!A || !b || !y) return fail(PR_EINVAL, "A, b and y are required");
+  const size_t need = pararnn_scan_workspace_bytes(jac, B, T, n);
+  if (need == 0) return fail(PR_EUNSUPPORTED, "no scan kernel for jac %d n %d", jac, n);
+  if (!workspace || ws_bytes < need) return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  HIPCHK(launch_zero(ws, need, s));
+  const int N = time_padded_n(n);
+  ScanArgs a{};
+  a.A = A; a.b = b; a.y = y;
+  a.B = B; a.T = T; a.n = n; a.reverse = reverse ? 1 : 0;
+  a.tiles_per_seq = (T + time_tile(N) - 1) / time_tile(N);
+  a.ntiles = a.tiles_per_seq * B;
+  a.st = (SolveState *)ws;
+  a.agg = (unsigned long long *)(ws + align256(sizeof(SolveState)));
+  a.incl = (unsigned long long *)(ws + align256(sizeof(SolveState)) + align256((size_t)a.ntiles * (N * N + N) * 8));
+  HIPCHK(launch_time_scan(N, a, s));
+  return PR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/pararnn.h declares, and rejects bad arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pararnn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pararnn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = bd.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_covers_all_codes():
+    for code in (0, -1, -2, -3, -5, 1, 2):
+        assert bd.strerror(code) != "unknown status"
+
+
+def _prob(**kw):
+    base = dict(cell=sy.CELL_GRU, jac=sy.JAC_DENSE, dtype=bd.PR_F32, B=2, T=64, d=1, n=1)
+    base.update(kw)
+    return bd.Problem(**base)
+
+
+def test_workspace_bytes_for_supported_problems():
+    for cfg in (1, 2, 3, 4, 5):
+        w = sy.WORKLOADS[cfg]
+        pb = bd.Problem(w["cell"], sy.natural_jac(w["cell"]), w["dtype"], w["B"], w["T"], w["d"], w["n"])
+        if cfg in (1, 2):
+            assert bd.workspace_bytes(pb, False) > 0
+            assert bd.workspace_bytes(pb, True) >= bd.workspace_bytes(pb, False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cell=9), bd.PR_EINVAL), (dict(jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL), (dict(dtype=7), bd.PR_EINVAL),
+    (dict(B=0), bd.PR_EINVAL), (dict(T=0), bd.PR_EINVAL), (dict(d=0), bd.PR_EINVAL), (dict(n=-3), bd.PR_EINVAL),
+    (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
+    (dict(cell=sy.CELL_TANH_RNN, n=13), bd.PR_EUNSUPPORTED),
+])
+def test_invalid_problems_rejected_without_device(kw, code):
+    L = bd.lib()
+    pb = _prob(**kw)
+    assert L.pararnn_workspace_bytes(C.byref(pb), 1) == 0
+    w = bd.Weights(1, None, 1, None, None)     # never dereferenced
+    rc = L.pararnn_solve(C.byref(pb), C.byref(w), C.c_void_p(16), None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                         C.c_void_p(256), 1 << 30, None)
+    assert rc == code, bd.last_error()
+    assert bd.last_error() != ""
+
+
+def test_missing_pointers_and_workspace_rejected():
+    L = bd.lib()
+    pb = _prob()
+    w = bd.Weights(1, None, 1, None, None)
+    ok_ws = bd.workspace_bytes(pb, False)
+    assert L.pararnn_solve(C.byref(pb), None, C.c_void_p(16), None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                           C.c_void_p(256), ok_ws, None) == bd.PR_EINVAL
+    assert L.pararnn_solve(C.byref(pb), C.byref(w), None, None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                           C.c_void_p(256), ok_ws, None) == bd.PR_EINVAL
+    assert L.pararnn_solve(C.byref(pb), C.byref(w), C.c_void_p(16), None, 1e-6, 0, C.c_void_p(16), None, None, 0,
+                           C.c_void_p(256), ok_ws, None) == bd.PR_EINVAL
+    assert L.pararnn_solve(C.byref(pb), C.byref(w), C.c_void_p(16), None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                           C.c_void_p(256), ok_ws - 1, None) == bd.PR_EWORKSPACE
+    assert L.pararnn_solve(C.byref(pb), C.byref(w), C.c_void_p(16), None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                           None, ok_ws, None) == bd.PR_EWORKSPACE
+    assert L.pararnn_adjoint(C.byref(pb), C.byref(w), C.c_void_p(16), None, C.c_void_p(16), None, None, None, None,
+                             None, C.c_void_p(256), 1 << 30, None) == bd.PR_EINVAL
+    assert L.pararnn_affine_scan(5, 1, 8, 1, 0, C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(256),
+                                 1 << 20, None) == bd.PR_EINVAL

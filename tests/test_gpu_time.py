@@ -1,0 +1,171 @@
+"""GPU parity of the time-parallel path (dense state n <= 8, fp32) against the
+fp64 oracle: Newton solves, iteration counts, status codes, the adjoint and
+the standalone affine scan."""
+import numpy as np
+import pytest
+
+import oracle
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ATOL = 1e-4  # fp32 storage and arithmetic: max-abs bound on h, lambda, dx, dh0
+RTOL_W = 1e-4  # weight gradients (sums over B*T terms): norm-wise relative bound
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_solve(p, tol=None, max_iters=None):
+    dp = bd.DeviceProblem(p)
+    st, it, dl = dp.solve(tol=tol, max_iters=max_iters)
+    torch.cuda.synchronize()
+    return dp, st, it, dl, dp.h.float().cpu().numpy().astype(np.float64)
+
+
+def check_solve(p, tol=None, max_iters=None, atol=ATOL):
+    tol = p["tol"] if tol is None else tol
+    max_iters = p["max_iters"] if max_iters is None else max_iters
+    say("case", p["name"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"], "tol", tol, "max_iters", max_iters)
+    dp, st, it, dl, h = gpu_solve(p, tol, max_iters)
+    ho, ito, sto, dlo = oracle.deer(p, tol=tol, max_iters=max_iters)
+    say("  gpu iters", it, "status", st, "deltas", dl, "| oracle", ito, sto, dlo)
+    assert st == sto
+    assert it == ito
+    err = np.abs(h - ho).max()
+    say("  max |h_gpu - h_oracle| =", err)
+    assert err <= atol
+    return dp, h, ho
+
+
+def test_cfg1_dense_tanh_rnn():
+    p = sy.make_problem(1)
+    dp, h, ho = check_solve(p)
+    assert np.abs(h - oracle.rollout(p)).max() <= ATOL
+
+
+@pytest.mark.parametrize("T", [65536, 1 << 20])
+def test_cfg2_scalar_gru(T):
+    p = sy.make_problem(2, T=T)
+    check_solve(p)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 64, 65, 4095, 4096, 4097, 10001])
+def test_scalar_gru_lengths_and_ragged_tiles(T):
+    p = sy.custom_problem(sy.CELL_GRU, B=3, T=T, d=2, n=1, seed=T, w_scale=1.0, h0=True)
+    check_solve(p, tol=1e-6, max_iters=T)
+
+
+@pytest.mark.parametrize("cell,n,d", [(sy.CELL_TANH_RNN, 3, 5), (sy.CELL_TANH_RNN, 8, 2), (sy.CELL_GRU, 2, 3),
+                                      (sy.CELL_GRU, 4, 8), (sy.CELL_GRU, 7, 1), (sy.CELL_LINEAR, 4, 2)])
+@pytest.mark.parametrize("T", [77, 1000, 2049])
+def test_dense_small_cells(cell, n, d, T):
+    p = sy.custom_problem(cell, B=2, T=T, d=d, n=n, seed=T + n, w_scale=0.7, h0=True)
+    # the linear cell's state is unbounded (|h| ~ 10 here), so its fp32 noise
+    # floor on delta is ~1e-6; Newton is exact after one update regardless
+    check_solve(p, tol=1e-4 if cell == sy.CELL_LINEAR else 1e-6, max_iters=T)
+
+
+def test_status_codes():
+    p = sy.make_problem(1, T=200)
+    dp = bd.DeviceProblem(p)
+    st, it, _ = dp.solve(tol=1e-6, max_iters=1)
+    assert (st, it) == (bd.PR_NOT_CONVERGED, 1)
+    st, it, dl = dp.solve(tol=0.0, max_iters=3)
+    assert (st, it) == (bd.PR_OK, 3) and len(dl) == 3
+    h3 = dp.h.float().cpu().numpy()
+    ho, *_ = oracle.deer(p, tol=0.0, max_iters=3)
+    assert np.abs(h3 - ho).max() <= ATOL
+    q = dict(p, x=p["x"].copy())
+    q["x"][1, 17, 0] = np.nan
+    dq = bd.DeviceProblem(q)
+    st, it, dl = dq.solve(tol=1e-6, max_iters=50)
+    assert (st, it) == (bd.PR_NONFINITE, 1) and np.isnan(dl[0])
+
+
+def test_solve_is_repeatable_on_one_workspace():
+    p = sy.make_problem(2, T=50000)
+    dp = bd.DeviceProblem(p)
+    r1 = dp.solve()
+    h1 = dp.h.clone()
+    r2 = dp.solve()
+    assert r1[0] == r2[0] and r1[1] == r2[1]
+    assert torch.equal(h1, dp.h) or (h1 - dp.h).abs().max().item() < 1e-6
+
+
+def adjoint_check(p, h_traj, a_gpu, atol=ATOL):
+    """lambda, dx, dh0: max-abs error <= atol * max(1, max|ref|) (the scale
+    factor only matters for unbounded cells); weight gradients: relative."""
+    ref = oracle.adjoint(p, h_traj)
+    for key, gkey in (("lam", "lam"), ("dx", "dx"), ("dh0", "dh0")):
+        err = np.abs(a_gpu[gkey].float().cpu().numpy() - ref[key]).max()
+        scale = max(1.0, float(np.abs(ref[key]).max()))
+        say("  ", key, "max abs err", err, "scale", scale)
+        assert err <= atol * scale, key
+    for key in ("dW_x", "db_x", "dW_h", "db_h"):
+        g = a_gpu[key].float().cpu().numpy()
+        r = ref[key]
+        rel = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+        say("  ", key, "rel err", rel)
+        assert rel <= RTOL_W, key
+
+
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(T=65536)), (2, {})])
+def test_adjoint_configs(cfg, kw):
+    p = sy.make_problem(cfg, **kw)
+    say("adjoint case", p["name"], p["B"], p["T"])
+    dp, st, it, dl, h = gpu_solve(p)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_check(p, h, a)
+
+
+@pytest.mark.parametrize("cell,n,d,T", [(sy.CELL_GRU, 1, 2, 4097), (sy.CELL_TANH_RNN, 3, 5, 777),
+                                        (sy.CELL_GRU, 5, 3, 1500), (sy.CELL_LINEAR, 2, 1, 64),
+                                        (sy.CELL_GRU, 2, 3, 4095), (sy.CELL_TANH_RNN, 4, 2, 9),
+                                        (sy.CELL_GRU, 1, 1, 1), (sy.CELL_TANH_RNN, 8, 8, 300)])
+def test_adjoint_small_cells(cell, n, d, T):
+    p = sy.custom_problem(cell, B=2, T=T, d=d, n=n, seed=5 + T, w_scale=0.5 if cell == sy.CELL_LINEAR else 0.7,
+                          h0=True)
+    say("adjoint case", p["name"], n, d, T)
+    dp, st, it, dl, h = gpu_solve(p, tol=1e-6, max_iters=T)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    adjoint_check(p, h, a)
+
+
+def _int_ops(rng, B, T, n):
+    A = np.zeros((B, T, n, n))
+    col = rng.integers(0, n, size=(B, T, n))
+    val = rng.integers(-1, 2, size=(B, T, n)).astype(float)
+    np.put_along_axis(A, col[..., None], val[..., None], axis=-1)
+    b = rng.integers(-4, 5, size=(B, T, n)).astype(float)
+    return A, b
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("T", [1, 7, 64, 4095, 4097, 20000])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_dense_affine_scan_bit_exact(n, T, reverse):
+    say("scan case n", n, "T", T, "reverse", reverse)
+    rng = np.random.default_rng(n * 100000 + T)
+    A, b = _int_ops(rng, 3, T, n)
+    y_ref = oracle.affine_solve(oracle.DENSE, A, b, reverse=reverse)
+    At = torch.tensor(A, dtype=torch.float32, device="cuda")
+    bt = torch.tensor(b, dtype=torch.float32, device="cuda")
+    yt = torch.empty_like(bt)
+    ws = torch.empty(bd.scan_workspace_bytes(bd.PR_JAC_DENSE, 3, T, n), dtype=torch.uint8, device="cuda")
+    bd.affine_scan(bd.PR_JAC_DENSE, At, bt, yt, ws, reverse=reverse)
+    torch.cuda.synchronize()
+    assert np.array_equal(yt.cpu().numpy().astype(np.float64), y_ref)
