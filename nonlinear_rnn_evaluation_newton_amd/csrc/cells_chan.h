@@ -1,0 +1,113 @@
+// Per-channel cells whose Jacobian is diagonal (ParaGRU) or 2x2 block-diagonal
+// (CIFG/peephole ParaLSTM), as the Para-Seq README's feature table lists them.
+// Channels are independent given the input projection U = W_x x + b_x, so a
+// thread evaluates one channel at a time.
+//
+// GRU, diagonal recurrence (PyTorch gate order r|z|n, b_hn inside r*(.)):
+//   r = sigm(U_r + a_r h + b_r), z = sigm(U_z + a_z h + b_z), q = a_n h + b_n,
+//   c = tanh(U_n + r q), f = (1 - z) c + z h,
+//   J = z + (h - c) z(1-z) a_z + (1-z)(1-c^2)(r a_n + q r(1-r) a_r).
+// LSTM, coupled input/forget gate with peepholes, state (c, h):
+//   f = sigm(U_f + w_f h + p_f c + b_f), g = tanh(U_g + w_g h + b_g),
+//   c' = f c + (1-f) g, o = sigm(U_o + w_o h + p_o c' + b_o), h' = o tanh(c'),
+//   J rows (c', h'), columns (c, h).
+#pragma once
+
+#include "common.h"
+
+namespace pr {
+
+struct ChanW {  // per-channel weights (fp32)
+  float a0, a1, a2;  // GRU: a_r, a_z, a_n   LSTM: w_f, w_g, w_o
+  float b0, b1, b2;  // recurrent biases of the three gates
+  float p0, p1;      // LSTM peepholes p_f, p_o
+};
+
+// f and J at state s (SW values) with projection U (3 gates).
+template <int CELL>
+__device__ inline void chan_cell(const float *s, const float *U, const ChanW &w, float *f, float *J) {
+  if constexpr (CELL == C_GRU_DIAG) {
+    const float h = s[0];
+    const float r = fsigm(fmaf(w.a0, h, U[0] + w.b0));
+    const float z = fsigm(fmaf(w.a1, h, U[1] + w.b1));
+    const float q = fmaf(w.a2, h, w.b2);
+    const float c = ftanh(fmaf(r, q, U[2]));
+    f[0] = fmaf(z, h - c, c);
+    const float be = (1.f - z) * (1.f - c * c);
+    J[0] = z + (h - c) * z * (1.f - z) * w.a1 + be * r * (w.a2 + q * (1.f - r) * w.a0);
+  } else {  // C_LSTM
+    const float c = s[0], h = s[1];
+    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0] + w.b0)));
+    const float g = ftanh(fmaf(w.a1, h, U[1] + w.b1));
+    const float cn = fmaf(fg, c - g, g);
+    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2] + w.b2)));
+    const float tc = ftanh(cn);
+    f[0] = cn;
+    f[1] = o * tc;
+    const float dfg = fg * (1.f - fg);
+    const float dcc = fmaf((c - g) * dfg, w.p0, fg);
+    const float dch = (c - g) * dfg * w.a0 + (1.f - fg) * (1.f - g * g) * w.a1;
+    const float oo = o * (1.f - o) * tc;
+    const float dhdcn = fmaf(oo, w.p1, o * (1.f - tc * tc));
+    J[0] = dcc;
+    J[1] = dch;
+    J[2] = dhdcn * dcc;
+    J[3] = fmaf(oo, w.a2, dhdcn * dch);
+  }
+}
+
+// Reverse-mode step: lam = dL/df; returns ds = J^T lam, dU (3 gates) and
+// adds the per-channel weight gradients into acc[8] (a0 a1 a2 b0 b1 b2 p0 p1).
+template <int CELL>
+__device__ inline void chan_cell_vjp(const float *s, const float *U, const float *lam, const ChanW &w, float *ds,
+                                     float *dU, float *acc) {
+  if constexpr (CELL == C_GRU_DIAG) {
+    const float h = s[0];
+    const float r = fsigm(fmaf(w.a0, h, U[0] + w.b0));
+    const float z = fsigm(fmaf(w.a1, h, U[1] + w.b1));
+    const float q = fmaf(w.a2, h, w.b2);
+    const float c = ftanh(fmaf(r, q, U[2]));
+    const float l = lam[0];
+    const float daz = l * (h - c) * z * (1.f - z);
+    const float dan = l * (1.f - z) * (1.f - c * c);
+    const float dq = dan * r;
+    const float dar = dan * q * r * (1.f - r);
+    ds[0] = l * z + dar * w.a0 + daz * w.a1 + dq * w.a2;
+    dU[0] = dar;
+    dU[1] = daz;
+    dU[2] = dan;
+    acc[0] = fmaf(dar, h, acc[0]);
+    acc[1] = fmaf(daz, h, acc[1]);
+    acc[2] = fmaf(dq, h, acc[2]);
+    acc[3] += dar;
+    acc[4] += daz;
+    acc[5] += dq;
+  } else {
+    const float c = s[0], h = s[1];
+    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0] + w.b0)));
+    const float g = ftanh(fmaf(w.a1, h, U[1] + w.b1));
+    const float cn = fmaf(fg, c - g, g);
+    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2] + w.b2)));
+    const float tc = ftanh(cn);
+    const float lc = lam[0], lh = lam[1];
+    const float dao = lh * tc * o * (1.f - o);
+    const float dcn = lc + lh * o * (1.f - tc * tc) + dao * w.p1;
+    const float daf = dcn * (c - g) * fg * (1.f - fg);
+    const float dag = dcn * (1.f - fg) * (1.f - g * g);
+    ds[0] = dcn * fg + daf * w.p0;
+    ds[1] = daf * w.a0 + dag * w.a1 + dao * w.a2;
+    dU[0] = daf;
+    dU[1] = dag;
+    dU[2] = dao;
+    acc[0] = fmaf(daf, h, acc[0]);
+    acc[1] = fmaf(dag, h, acc[1]);
+    acc[2] = fmaf(dao, h, acc[2]);
+    acc[3] += daf;
+    acc[4] += dag;
+    acc[5] += dao;
+    acc[6] = fmaf(daf, c, acc[6]);
+    acc[7] = fmaf(dao, cn, acc[7]);
+  }
+}
+
+}  // namespace pr

@@ -51,6 +51,51 @@ struct ScanArgs {
 };
 hipError_t launch_time_scan(int N, const ScanArgs &a, hipStream_t s);
 
+// ---------------- channel-parallel path (diagonal / 2x2-block Jacobian) ----
+struct ChanArgs {
+  const void *U;        // [B,T,3n] input projection (storage dtype)
+  void *h;              // [B,T,S] iterate, updated in place
+  const void *h0;       // [B,S] or null
+  const void *Wh, *bh, *peep;
+  const void *g;        // adjoint: [B,T,S]
+  void *lam, *dh0;      // adjoint outputs (may be null)
+  void *dU;             // adjoint: [B,T,3n] gate gradients (storage dtype)
+  float *part;          // adjoint: weight-gradient partials
+  const float *A, *b;   // standalone scan
+  float *y;
+  int B, T, n, SW;
+  int k;
+  float tol;
+  int max_iters;
+  SolveState *st;
+  unsigned long long *agg, *incl;
+  float *bnd;           // [2][ntiles][CH*SW]
+  int stripes, tps, ntiles;
+  int reverse;
+  int part_per_block, nparts;
+};
+struct ChanGeomInfo {
+  int CPL, TW, CH, TT;
+};
+ChanGeomInfo chan_geom(int cell, int n, bool adjoint);
+hipError_t launch_chan_sweep(int cell, bool bf16, ChanArgs &a, hipStream_t s);
+hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s);
+hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
+                              hipStream_t s);
+hipError_t launch_chan_scan(int SW, ChanArgs &a, hipStream_t s);
+
+// ---------------- MFMA GEMM ------------------------------------------------
+struct GemmArgs {
+  const void *A, *B;    // A: [M,K] (a_kc) or [K,M]; B: [N,K] (b_kc) or [K,N]
+  void *C;              // [M,N] row stride ldc
+  const void *bias;     // [N] or null (input dtype)
+  float *ws;            // split-K workspace [splits][M][N]
+  int M, N, K, lda, ldb, ldc, splits;
+  bool a_kc, b_kc, bf16, out_f32, vec_a, vec_b;
+};
+int gemm_splits(int M, int N, int K);
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+
 // ---------------- utilities ------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 

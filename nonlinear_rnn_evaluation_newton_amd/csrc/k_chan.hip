@@ -1,0 +1,97 @@
+// Instantiations and launchers of the channel-parallel kernel family.
+#include "k_chan_impl.h"
+#include "k_time_impl.h"  // resident_blocks / persistent_grid
+
+namespace pr {
+
+// Tile geometry per cell: lanes own CPL adjacent channels, wavefronts TW steps.
+ChanGeomInfo chan_geom(int cell, int n, bool adjoint) {
+  ChanGeomInfo g;
+  if (cell == C_GRU_DIAG) {
+    g.CPL = (n % 2 == 0) ? 2 : 1;
+    g.TW = adjoint ? 8 : 16;
+  } else {
+    g.CPL = 1;
+    g.TW = 8;
+  }
+  g.CH = 64 * g.CPL;
+  g.TT = 4 * g.TW;
+  return g;
+}
+
+template <auto KERN>
+static int chan_grid(const ChanArgs &a, bool stripe_aligned) {
+  const int r = resident_blocks<KERN>();
+  if (r <= 0) return 0;
+  int grid = a.ntiles < r ? a.ntiles : r;
+  if (stripe_aligned && a.stripes <= grid) grid = grid / a.stripes * a.stripes;
+  return grid;
+}
+
+#define PR_CHAN_CFG(cell, n, adj, ...)                                                    \
+  {                                                                                       \
+    const ChanGeomInfo gi = chan_geom(cell, n, adj);                                      \
+    if (cell == C_GRU_DIAG && gi.CPL == 2 && gi.TW == 16) { constexpr int CELL = C_GRU_DIAG, CPL = 2, TW = 16; __VA_ARGS__; } \
+    else if (cell == C_GRU_DIAG && gi.CPL == 2 && gi.TW == 8) { constexpr int CELL = C_GRU_DIAG, CPL = 2, TW = 8; __VA_ARGS__; } \
+    else if (cell == C_GRU_DIAG && gi.CPL == 1 && gi.TW == 16) { constexpr int CELL = C_GRU_DIAG, CPL = 1, TW = 16; __VA_ARGS__; } \
+    else if (cell == C_GRU_DIAG && gi.CPL == 1 && gi.TW == 8) { constexpr int CELL = C_GRU_DIAG, CPL = 1, TW = 8; __VA_ARGS__; } \
+    else if (cell == C_LSTM && gi.CPL == 1 && gi.TW == 8) { constexpr int CELL = C_LSTM, CPL = 1, TW = 8; __VA_ARGS__; } \
+    else return hipErrorInvalidValue;                                                     \
+  }
+
+hipError_t launch_chan_sweep(int cell, bool bf16, ChanArgs &a, hipStream_t s) {
+  PR_CHAN_CFG(cell, a.n, false, {
+    if (bf16) {
+      const int grid = chan_grid<k_chan_sweep<CELL, uint16_t, CPL, TW>>(a, false);
+      if (grid <= 0) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((k_chan_sweep<CELL, uint16_t, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+      const int grid = chan_grid<k_chan_sweep<CELL, float, CPL, TW>>(a, false);
+      if (grid <= 0) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((k_chan_sweep<CELL, float, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
+    }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s) {
+  PR_CHAN_CFG(cell, a.n, true, {
+    int grid;
+    if (bf16) grid = chan_grid<k_chan_adjoint<CELL, uint16_t, CPL, TW>>(a, true);
+    else grid = chan_grid<k_chan_adjoint<CELL, float, CPL, TW>>(a, true);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    a.part_per_block = (grid % a.stripes == 0) ? 1 : 0;
+    a.nparts = grid;
+    if (bf16) hipLaunchKernelGGL((k_chan_adjoint<CELL, uint16_t, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_chan_adjoint<CELL, float, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
+                              hipStream_t s) {
+  const ChanGeomInfo gi = chan_geom(cell, a.n, true);
+  const unsigned blocks = (unsigned)((a.n * CHAN_P + 255) / 256);
+  if (gi.CH == 128) hipLaunchKernelGGL((k_chan_reduce<128>), dim3(blocks), dim3(256), 0, s, a, dWh, dbh, dpeep, dbx);
+  else hipLaunchKernelGGL((k_chan_reduce<64>), dim3(blocks), dim3(256), 0, s, a, dWh, dbh, dpeep, dbx);
+  return hipGetLastError();
+}
+
+hipError_t launch_chan_scan(int SW, ChanArgs &a, hipStream_t s) {
+  if (SW == 1 && a.n % 2 == 0) {
+    const int grid = chan_grid<k_chan_scan<1, 2, 16>>(a, false);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_chan_scan<1, 2, 16>), dim3(grid), dim3(256), 0, s, a);
+  } else if (SW == 1) {
+    const int grid = chan_grid<k_chan_scan<1, 1, 16>>(a, false);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_chan_scan<1, 1, 16>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    const int grid = chan_grid<k_chan_scan<2, 1, 8>>(a, false);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_chan_scan<2, 1, 8>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pr

@@ -1,0 +1,707 @@
+// Channel-parallel kernels for per-channel state (diagonal ParaGRU, SW = 1;
+// CIFG/peephole ParaLSTM with a 2x2 block Jacobian, SW = 2): one fused
+// Newton sweep per launch, the standalone diagonal / 2x2-block affine scan,
+// and the fused adjoint.
+//
+// Channels are independent, so a scan runs per (sequence, channel) along time
+// (Para-Seq README, Main features: diagonal and 2x2 block scans).  Layout: a
+// lane owns CPL adjacent channels (coalesced loads across the wavefront), a
+// tile is 4 wavefronts x TW steps of those 64*CPL channels; each lane
+// composes its TW steps serially per channel, the 4 wavefronts combine in LDS,
+// and consecutive time tiles of a stripe (sequence b, channel group) chain
+// through a decoupled look-back whose descriptors are per channel.  A
+// persistent grid walks the tiles in increasing time-major order.
+#pragma once
+
+#include "cells_chan.h"
+#include "internal.h"
+
+namespace pr {
+
+template <typename ST, int CNT>
+__device__ inline void ld_vec(const ST *p, float *out) {
+  if constexpr (sizeof(ST) * CNT == 16) {
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    unsigned w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (sizeof(ST) == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) out[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) out[i] = __uint_as_float((w[i / 2] >> (16 * (i & 1))) << 16);
+    }
+  } else if constexpr (sizeof(ST) * CNT == 8) {
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    unsigned w[2] = {u.x, u.y};
+    if constexpr (sizeof(ST) == 4) {
+      out[0] = __uint_as_float(w[0]);
+      out[1] = __uint_as_float(w[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) out[i] = __uint_as_float((w[i / 2] >> (16 * (i & 1))) << 16);
+    }
+  } else if constexpr (sizeof(ST) * CNT == 4) {
+    unsigned u = *reinterpret_cast<const unsigned *>(p);
+    if constexpr (sizeof(ST) == 4) {
+      out[0] = __uint_as_float(u);
+    } else {
+      out[0] = __uint_as_float(u << 16);
+      out[1] = __uint_as_float(u & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CNT; i++) out[i] = ldf(p, i);
+  }
+}
+
+template <typename ST, int CNT>
+__device__ inline void st_vec(ST *p, const float *in) {
+  if constexpr (sizeof(ST) == 2 && CNT % 2 == 0) {
+    unsigned w[CNT / 2];
+#pragma unroll
+    for (int i = 0; i < CNT / 2; i++) w[i] = (unsigned)f2bf(in[2 * i]) | ((unsigned)f2bf(in[2 * i + 1]) << 16);
+    if constexpr (CNT == 2) *reinterpret_cast<unsigned *>(p) = w[0];
+    else if constexpr (CNT == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    else {
+#pragma unroll
+      for (int i = 0; i < CNT / 2; i++) reinterpret_cast<unsigned *>(p)[i] = w[i];
+    }
+  } else if constexpr (sizeof(ST) == 4 && CNT == 2) {
+    *reinterpret_cast<float2 *>(p) = make_float2(in[0], in[1]);
+  } else if constexpr (sizeof(ST) == 4 && CNT == 4) {
+    *reinterpret_cast<float4 *>(p) = make_float4(in[0], in[1], in[2], in[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CNT; i++) stf(p, i, in[i]);
+  }
+}
+
+// Tile geometry and stripe bookkeeping shared by the kernels.
+template <int SW, int CPL, int TW>
+struct ChanGeom {
+  static constexpr int CH = 64 * CPL;   // channels per tile
+  static constexpr int TT = 4 * TW;     // steps per tile
+  static constexpr int AW = SW * SW + SW;
+};
+
+// Combine the four wavefronts' per-channel aggregates (wave w covers steps
+// [w*TW, (w+1)*TW) of the tile).  pre[c] = composition of the waves before
+// this one, tot[c] = tile aggregate.  Contains one __syncthreads.
+template <int SW, int CPL>
+__device__ inline void chan_combine(const Op<SW> (&agg)[CPL], Op<SW> (&pre)[CPL], Op<SW> (&tot)[CPL],
+                                    float *s_agg /*[4][64*CPL][SW*SW+SW]*/) {
+  constexpr int AW = SW * SW + SW, CH = 64 * CPL;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    float *d = s_agg + ((size_t)wid * CH + lane * CPL + c) * AW;
+#pragma unroll
+    for (int i = 0; i < SW * SW; i++) d[i] = agg[c].A[i];
+#pragma unroll
+    for (int i = 0; i < SW; i++) d[SW * SW + i] = agg[c].b[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    Op<SW> p = op_identity<SW>(), t = op_identity<SW>();
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float *s = s_agg + ((size_t)w * CH + lane * CPL + c) * AW;
+      Op<SW> o;
+#pragma unroll
+      for (int i = 0; i < SW * SW; i++) o.A[i] = s[i];
+#pragma unroll
+      for (int i = 0; i < SW; i++) o.b[i] = s[SW * SW + i];
+      if (w < wid) p = compose(o, p);
+      t = compose(o, t);
+    }
+    pre[c] = p;
+    tot[c] = t;
+  }
+}
+
+// Per-lane decoupled look-back over the time tiles of one stripe (run by
+// wavefront 0; lane l owns the same CPL channels in every tile of the
+// stripe).  Descriptor words: agg [tile][64*CPL][SW*SW+SW], incl
+// [tile][64*CPL][SW], each tagged with the sweep number.  Each round trip
+// reads W predecessors; carry[c] receives the state after tile j - 1.
+template <int SW, int CPL, int W>
+__device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, bool active,
+                                     unsigned long long *agg, unsigned long long *incl, float (&carry)[CPL][SW]) {
+  constexpr int AW = SW * SW + SW, CH = 64 * CPL;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < CPL; c++)
+#pragma unroll
+    for (int i = 0; i < SW; i++) carry[c][i] = 0.f;
+  if (!active) return;
+  if (j > 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      unsigned long long *d = agg + ((size_t)j * CH + lane * CPL + c) * AW;
+#pragma unroll
+      for (int i = 0; i < SW * SW; i++) desc_put(d + i, tag_agg(k), tot[c].A[i]);
+#pragma unroll
+      for (int i = 0; i < SW; i++) desc_put(d + SW * SW + i, tag_agg(k), tot[c].b[i]);
+    }
+    Op<SW> acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) acc[c] = op_identity<SW>();
+    int p0 = j - 1;
+    bool done = false;
+    while (!done) {
+      unsigned long long wi[W][CPL][SW], wa[W][CPL][AW];
+#pragma unroll
+      for (int q = 0; q < W; q++) {
+        const int p = p0 - q;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+#pragma unroll
+          for (int i = 0; i < SW; i++)
+            wi[q][c][i] = p >= 0 ? ld_agent64(incl + ((size_t)p * CH + lane * CPL + c) * SW + i) : 0ull;
+#pragma unroll
+          for (int i = 0; i < AW; i++)
+            wa[q][c][i] = p >= 0 ? ld_agent64(agg + ((size_t)p * CH + lane * CPL + c) * AW + i) : 0ull;
+        }
+      }
+      int q = 0;
+      for (; q < W; q++) {
+        bool hi = true, ha = true;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+#pragma unroll
+          for (int i = 0; i < SW; i++) hi = hi && (unsigned)(wi[q][c][i] >> 32) == tag_incl(k);
+#pragma unroll
+          for (int i = 0; i < AW; i++) ha = ha && (unsigned)(wa[q][c][i] >> 32) == tag_agg(k);
+        }
+        if (hi) {
+#pragma unroll
+          for (int c = 0; c < CPL; c++) {
+            float v[SW];
+#pragma unroll
+            for (int i = 0; i < SW; i++) v[i] = __uint_as_float((unsigned)wi[q][c][i]);
+            op_apply(acc[c], v, carry[c]);
+          }
+          done = true;
+          break;
+        }
+        if (!ha) break;  // predecessor not published yet: retry from here
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          Op<SW> o;
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) o.A[i] = __uint_as_float((unsigned)wa[q][c][i]);
+#pragma unroll
+          for (int i = 0; i < SW; i++) o.b[i] = __uint_as_float((unsigned)wa[q][c][SW * SW + i]);
+          acc[c] = compose(acc[c], o);
+        }
+      }
+      if (!done) {
+        if (q < W) __builtin_amdgcn_s_sleep(1);
+        p0 -= q;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    float inc[SW];
+    op_apply(tot[c], carry[c], inc);
+    unsigned long long *d = incl + ((size_t)j * CH + lane * CPL + c) * SW;
+#pragma unroll
+    for (int i = 0; i < SW; i++) desc_put(d + i, tag_incl(k), inc[i]);
+  }
+}
+
+template <typename ST>
+__device__ inline ChanW load_chan_w(const ChanArgs &a, int c) {
+  const ST *Wh = (const ST *)a.Wh, *bh = (const ST *)a.bh, *pp = (const ST *)a.peep;
+  const int n = a.n;
+  ChanW w;
+  w.a0 = ldf(Wh, c);
+  w.a1 = ldf(Wh, (size_t)n + c);
+  w.a2 = ldf(Wh, (size_t)2 * n + c);
+  w.b0 = bh ? ldf(bh, c) : 0.f;
+  w.b1 = bh ? ldf(bh, (size_t)n + c) : 0.f;
+  w.b2 = bh ? ldf(bh, (size_t)2 * n + c) : 0.f;
+  w.p0 = pp ? ldf(pp, c) : 0.f;
+  w.p1 = pp ? ldf(pp, (size_t)n + c) : 0.f;
+  return w;
+}
+
+// Stop rule on the previous sweep's measure; block 0 finalises the history
+// and clears the next sweep's shards.  Returns true when the solve stopped.
+__device__ inline bool chan_stopped(const ChanArgs &a, int *s_stop) {
+  const int k = a.k;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int stop = ld_agent(&a.st->stopped) != 0;
+    if (!stop && k >= 2) {
+      unsigned d = wave_max_u32(ld_agent(&a.st->dslot[(k - 1) & 3][lane]));
+      int status;
+      if (stop_rule(__uint_as_float(d), k - 1, a.tol, a.T, a.max_iters, &status)) {
+        stop = 1;
+        if (blockIdx.x == 0 && lane == 0) {
+          st_agent((unsigned *)&a.st->iters, (unsigned)(k - 1));
+          st_agent((unsigned *)&a.st->status, (unsigned)status);
+          st_agent(&a.st->stopped, 1u);
+        }
+      }
+      if (blockIdx.x == 0 && lane == 0) st_agent(&a.st->hist[(k - 1) % PR_HIST], d);
+    }
+    if (!stop && blockIdx.x == 0) st_agent(&a.st->dslot[(k + 1) & 3][lane], 0u);
+    if (lane == 0) *s_stop = stop;
+  }
+  __syncthreads();
+  return *s_stop != 0;
+}
+
+// ---------------------------------------------------------------------------
+// one Newton sweep
+// ---------------------------------------------------------------------------
+template <int CELL, typename ST, int CPL, int TW>
+__global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1;
+  using Gm = ChanGeom<SW, CPL, TW>;
+  constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
+  __shared__ float s_agg[4 * CH * AW];
+  __shared__ float s_carry[CH * SW];
+  __shared__ int s_stop;
+  __shared__ unsigned s_dmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, k = a.k;
+  const int T = a.T, n = a.n, S = SW * n;
+  if (chan_stopped(a, &s_stop)) return;
+  const int CG = (n + CH - 1) / CH;
+  const ST *U = (const ST *)a.U;
+  ST *H = (ST *)a.h;
+  const ST *H0 = (const ST *)a.h0;
+  unsigned dmax = 0;
+
+  for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
+    const int j = id / a.stripes, stripe = id % a.stripes;
+    const int b = stripe / CG, cg = stripe % CG, L = stripe * a.tps + j;
+    const int c0 = cg * CH + lane * CPL;  // first channel of this lane
+    const bool active = c0 < n;           // n is a multiple of CPL
+    const int t0 = j * TT + wid * TW;     // first step of this wave
+    ChanW w[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+
+    float sp[CPL * SW];  // state before step t0
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) sp[i] = 0.f;
+    if (active && t0 < T) {
+      if (t0 == 0) {
+        if (H0) ld_vec<ST, CPL * SW>(H0 + (size_t)b * S + (size_t)c0 * SW, sp);
+      } else if (k >= 2) {
+        if (wid == 0) {
+          const float *bd = a.bnd + ((size_t)((k - 1) & 1) * a.ntiles + (L - 1)) * CH * SW + (size_t)lane * CPL * SW;
+#pragma unroll
+          for (int i = 0; i < CPL * SW; i++) sp[i] = bd[i];
+        } else {
+          ld_vec<ST, CPL * SW>(H + ((size_t)b * T + t0 - 1) * S + (size_t)c0 * SW, sp);
+        }
+      }
+    }
+    float Jv[TW][CPL][SW * SW], rv[TW][CPL][SW], hv[TW][CPL][SW];
+    Op<SW> agg[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int t = t0 + s;
+      const bool valid = active && t < T;
+      float hc[CPL * SW], u0[CPL], u1[CPL], u2[CPL];
+      if (valid) {
+        const size_t row = (size_t)b * T + t;
+        if (k >= 2) ld_vec<ST, CPL * SW>(H + row * S + (size_t)c0 * SW, hc);
+        else {
+#pragma unroll
+          for (int i = 0; i < CPL * SW; i++) hc[i] = 0.f;
+        }
+        ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
+        ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
+        ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          float Uc[3] = {u0[c], u1[c], u2[c]}, f[SW];
+          chan_cell<CELL>(sp + c * SW, Uc, w[c], f, Jv[s][c]);
+          Op<SW> e;
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            hv[s][c][i] = hc[c * SW + i];
+            rv[s][c][i] = f[i] - hc[c * SW + i];
+            e.b[i] = rv[s][c][i];
+          }
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) e.A[i] = Jv[s][c][i];
+          agg[c] = compose(e, agg[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL * SW; i++) sp[i] = hc[i];
+      }
+    }
+    Op<SW> pre[CPL], tot[CPL];
+    chan_combine<SW, CPL>(agg, pre, tot, s_agg);
+    if (wid == 0) {
+      float carry[CPL][SW];
+      chan_lookback<SW, CPL, 4>(tot, j, k, active, a.agg + (size_t)stripe * a.tps * CH * AW,
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int i = 0; i < SW; i++) s_carry[(lane * CPL + c) * SW + i] = carry[c][i];
+    }
+    __syncthreads();
+    float dh[CPL][SW];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) op_apply(pre[c], &s_carry[(lane * CPL + c) * SW], dh[c]);
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int t = t0 + s;
+      if (active && t < T) {
+        float hn[CPL * SW];
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          float nd[SW];
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            float acc = rv[s][c][i];
+#pragma unroll
+            for (int m = 0; m < SW; m++) acc = fmaf(Jv[s][c][i * SW + m], dh[c][m], acc);
+            nd[i] = acc;
+          }
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            dh[c][i] = nd[i];
+            hn[c * SW + i] = hv[s][c][i] + nd[i];
+            const unsigned u = __float_as_uint(fabsf(nd[i]));
+            dmax = u > dmax ? u : dmax;
+          }
+        }
+        st_vec<ST, CPL * SW>(H + ((size_t)b * T + t) * S + (size_t)c0 * SW, hn);
+        if (wid == 3 && s == TW - 1) {
+          float *bd = a.bnd + ((size_t)(k & 1) * a.ntiles + L) * CH * SW + (size_t)lane * CPL * SW;
+#pragma unroll
+          for (int i = 0; i < CPL * SW; i++) bd[i] = sizeof(ST) == 2 ? bf2f(f2bf(hn[i])) : hn[i];
+        }
+      }
+    }
+    __syncthreads();  // s_agg / s_carry are rewritten by the next tile
+  }
+  dmax = wave_max_u32(dmax);
+  if (lane == 0) s_dmax[wid] = dmax;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned m = s_dmax[0];
+    for (int q = 1; q < 4; q++) m = s_dmax[q] > m ? s_dmax[q] : m;
+    max_agent(&a.st->dslot[k & 3][blockIdx.x % PR_DSHARDS], m);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// standalone scan with given operators (fp32):  y_t = A_t y_{t-1} + b_t, or
+// in reverse time y_t = A_t y_{t+1} + b_t.  SW = 1: A, b [B,T,n];
+// SW = 2: A [B,T,n,2,2], b [B,T,n,2].
+// ---------------------------------------------------------------------------
+template <int SW, int CPL, int TW>
+__global__ __launch_bounds__(256) void k_chan_scan(const ChanArgs a) {
+  using Gm = ChanGeom<SW, CPL, TW>;
+  constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
+  __shared__ float s_agg[4 * CH * AW];
+  __shared__ float s_carry[CH * SW];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T, n = a.n, S = SW * n;
+  const int CG = (n + CH - 1) / CH;
+  for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
+    const int j = id / a.stripes, stripe = id % a.stripes;
+    const int b = stripe / CG, cg = stripe % CG;
+    const int c0 = cg * CH + lane * CPL;
+    const bool active = c0 < n;
+    const int s0 = j * TT + wid * TW;  // scan positions of this wave
+    Op<SW> el[TW][CPL], agg[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int sp = s0 + s;
+      const int t = a.reverse ? T - 1 - sp : sp;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        el[s][c] = op_identity<SW>();
+        if (active && sp < T) {
+          const size_t e = ((size_t)b * T + t) * n + c0 + c;
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) el[s][c].A[i] = a.A[e * SW * SW + i];
+#pragma unroll
+          for (int i = 0; i < SW; i++) el[s][c].b[i] = a.b[e * SW + i];
+          agg[c] = compose(el[s][c], agg[c]);
+        }
+      }
+    }
+    Op<SW> pre[CPL], tot[CPL];
+    chan_combine<SW, CPL>(agg, pre, tot, s_agg);
+    if (wid == 0) {
+      float carry[CPL][SW];
+      chan_lookback<SW, CPL, 4>(tot, j, 1, active, a.agg + (size_t)stripe * a.tps * CH * AW,
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int i = 0; i < SW; i++) s_carry[(lane * CPL + c) * SW + i] = carry[c][i];
+    }
+    __syncthreads();
+    float y[CPL][SW];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) op_apply(pre[c], &s_carry[(lane * CPL + c) * SW], y[c]);
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int sp = s0 + s;
+      if (active && sp < T) {
+        const int t = a.reverse ? T - 1 - sp : sp;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          float ny[SW];
+          op_apply(el[s][c], y[c], ny);
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            y[c][i] = ny[i];
+            a.y[(((size_t)b * T + t) * n + c0 + c) * SW + i] = ny[i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pr
+
+namespace pr {
+
+// ---------------------------------------------------------------------------
+// adjoint: per channel, lam_t = g_t + J_{t+1}^T lam_{t+1} by a reverse-time
+// scan; then the chain rule through each cell gives dU (for the dx and dW_x
+// products), dh0 and the per-channel weight-gradient partials
+// [a0 a1 a2 | b0 b1 b2 | p0 p1 | sum dU0 dU1 dU2] (CHAN_P values).
+// When every block keeps one stripe (grid a multiple of the stripe count)
+// the partials are summed per block, else per tile.
+// ---------------------------------------------------------------------------
+constexpr int CHAN_P = 11;
+
+template <int CELL, typename ST, int CPL, int TW>
+__global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1;
+  using Gm = ChanGeom<SW, CPL, TW>;
+  constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
+  __shared__ float s_agg[4 * CH * AW];
+  __shared__ float s_carry[CH * SW];
+  __shared__ float s_red[4 * CH * CHAN_P];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T, n = a.n, S = SW * n;
+  const int CG = (n + CH - 1) / CH;
+  const ST *U = (const ST *)a.U, *H = (const ST *)a.h, *Gr = (const ST *)a.g, *H0 = (const ST *)a.h0;
+  ST *LAM = (ST *)a.lam, *DH0 = (ST *)a.dh0, *DU = (ST *)a.dU;
+  float acc[CPL][CHAN_P];
+#pragma unroll
+  for (int c = 0; c < CPL; c++)
+#pragma unroll
+    for (int p = 0; p < CHAN_P; p++) acc[c][p] = 0.f;
+  const bool per_block = a.part_per_block != 0;
+
+  for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
+    const int j = id / a.stripes, stripe = id % a.stripes;
+    const int b = stripe / CG, cg = stripe % CG;
+    const int c0 = cg * CH + lane * CPL;
+    const bool active = c0 < n;
+    const int s0 = j * TT + wid * TW;  // scan positions; time t = T - 1 - s
+    ChanW w[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+
+    float Av[TW][CPL][SW * SW], gv[TW][CPL][SW], hv[TW][CPL][SW], uv[TW][CPL][3];
+    float un[CPL][3];  // U at the step after the wave's range
+    float hp[CPL * SW];  // h at the step before the wave's range
+    const int thi = T - 1 - s0;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) un[c][0] = un[c][1] = un[c][2] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) hp[i] = 0.f;
+    if (active && thi >= 0 && thi + 1 < T) {
+      float u0[CPL], u1[CPL], u2[CPL];
+      const size_t row = (size_t)b * T + thi + 1;
+      ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
+      ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
+      ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
+#pragma unroll
+      for (int c = 0; c < CPL; c++) { un[c][0] = u0[c]; un[c][1] = u1[c]; un[c][2] = u2[c]; }
+    }
+    const int tlo = thi - TW + 1;
+    float hz[CPL * SW];  // h0, used by the step t = 0 when this wave covers it
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) hz[i] = 0.f;
+    if (active && tlo >= 1 && tlo < T) ld_vec<ST, CPL * SW>(H + ((size_t)b * T + tlo - 1) * S + (size_t)c0 * SW, hp);
+    if (active && tlo <= 0 && thi >= 0 && H0) ld_vec<ST, CPL * SW>(H0 + (size_t)b * S + (size_t)c0 * SW, hz);
+    Op<SW> agg[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int t = thi - s;
+      if (active && t >= 0) {
+        const size_t row = (size_t)b * T + t;
+        float hc[CPL * SW], gc[CPL * SW], u0[CPL], u1[CPL], u2[CPL];
+        ld_vec<ST, CPL * SW>(H + row * S + (size_t)c0 * SW, hc);
+        ld_vec<ST, CPL * SW>(Gr + row * S + (size_t)c0 * SW, gc);
+        ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
+        ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
+        ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          uv[s][c][0] = u0[c]; uv[s][c][1] = u1[c]; uv[s][c][2] = u2[c];
+          float J[SW * SW];
+          if (t + 1 < T) {
+            float f[SW];
+            chan_cell<CELL>(hc + c * SW, s == 0 ? un[c] : uv[s - 1][c], w[c], f, J);
+          } else {
+#pragma unroll
+            for (int i = 0; i < SW * SW; i++) J[i] = 0.f;
+          }
+          Op<SW> o;
+#pragma unroll
+          for (int r = 0; r < SW; r++) {
+#pragma unroll
+            for (int q = 0; q < SW; q++) o.A[r * SW + q] = J[q * SW + r];
+            o.b[r] = gc[c * SW + r];
+            gv[s][c][r] = gc[c * SW + r];
+            hv[s][c][r] = hc[c * SW + r];
+          }
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) Av[s][c][i] = o.A[i];
+          agg[c] = compose(o, agg[c]);
+        }
+      }
+    }
+    Op<SW> pre[CPL], tot[CPL];
+    chan_combine<SW, CPL>(agg, pre, tot, s_agg);
+    if (wid == 0) {
+      float carry[CPL][SW];
+      chan_lookback<SW, CPL, 4>(tot, j, 1, active, a.agg + (size_t)stripe * a.tps * CH * AW,
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int i = 0; i < SW; i++) s_carry[(lane * CPL + c) * SW + i] = carry[c][i];
+    }
+    __syncthreads();
+    float lam[CPL][SW];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) op_apply(pre[c], &s_carry[(lane * CPL + c) * SW], lam[c]);
+    float tacc[CPL][CHAN_P];
+#pragma unroll
+    for (int c = 0; c < CPL; c++)
+#pragma unroll
+      for (int p = 0; p < CHAN_P; p++) tacc[c][p] = 0.f;
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int t = thi - s;
+      if (active && t >= 0) {
+        const size_t row = (size_t)b * T + t;
+        float lo[CPL * SW], du[3][CPL], dso[CPL * SW];
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          float nl[SW];
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            float x = gv[s][c][i];
+#pragma unroll
+            for (int m = 0; m < SW; m++) x = fmaf(Av[s][c][i * SW + m], lam[c][m], x);
+            nl[i] = x;
+          }
+#pragma unroll
+          for (int i = 0; i < SW; i++) { lam[c][i] = nl[i]; lo[c * SW + i] = nl[i]; }
+          // state before step t: h_{t-1} (the next element in scan order)
+          float spv[SW];
+#pragma unroll
+          for (int i = 0; i < SW; i++) spv[i] = s + 1 < TW ? hv[s + 1][c][i] : hp[c * SW + i];
+          if (t == 0) {
+#pragma unroll
+            for (int i = 0; i < SW; i++) spv[i] = hz[c * SW + i];
+          }
+          float ds[SW], dU[3];
+          chan_cell_vjp<CELL>(spv, uv[s][c], nl, w[c], ds, dU, tacc[c]);
+          tacc[c][8] += dU[0];
+          tacc[c][9] += dU[1];
+          tacc[c][10] += dU[2];
+#pragma unroll
+          for (int g = 0; g < 3; g++) du[g][c] = dU[g];
+#pragma unroll
+          for (int i = 0; i < SW; i++) dso[c * SW + i] = ds[i];
+        }
+        if (LAM) st_vec<ST, CPL * SW>(LAM + row * S + (size_t)c0 * SW, lo);
+#pragma unroll
+        for (int g = 0; g < 3; g++) st_vec<ST, CPL>(DU + row * 3 * n + (size_t)g * n + c0, du[g]);
+        if (t == 0 && DH0) st_vec<ST, CPL * SW>(DH0 + (size_t)b * S + (size_t)c0 * SW, dso);
+      }
+    }
+    if (per_block) {
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int p = 0; p < CHAN_P; p++) acc[c][p] += tacc[c][p];
+    } else {
+      // per-tile partials: combine the 4 wavefronts, write [L][CH][CHAN_P]
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int p = 0; p < CHAN_P; p++) s_red[((size_t)wid * CH + lane * CPL + c) * CHAN_P + p] = tacc[c][p];
+      __syncthreads();
+      const int L = stripe * a.tps + j;
+      for (int e = tid; e < CH * CHAN_P; e += 256)
+        a.part[(size_t)L * CH * CHAN_P + e] =
+            (s_red[e] + s_red[CH * CHAN_P + e]) + (s_red[2 * CH * CHAN_P + e] + s_red[3 * CH * CHAN_P + e]);
+    }
+    __syncthreads();
+  }
+  if (per_block) {
+#pragma unroll
+    for (int c = 0; c < CPL; c++)
+#pragma unroll
+      for (int p = 0; p < CHAN_P; p++) s_red[((size_t)wid * CH + lane * CPL + c) * CHAN_P + p] = acc[c][p];
+    __syncthreads();
+    for (int e = tid; e < CH * CHAN_P; e += 256)
+      a.part[(size_t)blockIdx.x * CH * CHAN_P + e] =
+          (s_red[e] + s_red[CH * CHAN_P + e]) + (s_red[2 * CH * CHAN_P + e] + s_red[3 * CH * CHAN_P + e]);
+  }
+}
+
+// Sum the partials of every channel in fp64, in slot order, and scatter to
+// the fp32 gradient outputs (dW_h [3n], db_h [3n], dpeep [2n], db_x [3n]).
+template <int CH>
+__global__ __launch_bounds__(256) void k_chan_reduce(const ChanArgs a, float *dWh, float *dbh, float *dpeep,
+                                                     float *dbx) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n = a.n;
+  if (e >= n * CHAN_P) return;
+  const int c = e / CHAN_P, p = e % CHAN_P;
+  const int CG = (n + CH - 1) / CH, cg = c / CH, cl = c % CH;
+  double s = 0.0;
+  if (a.part_per_block) {
+    const int B = a.stripes / CG, G = a.nparts, S = a.stripes;
+    for (int bb = 0; bb < B; bb++)
+      for (int slot = cg + CG * bb; slot < G; slot += S) s += (double)a.part[((size_t)slot * CH + cl) * CHAN_P + p];
+  } else {
+    const int B = a.stripes / CG;
+    for (int bb = 0; bb < B; bb++) {
+      const int stripe = bb * CG + cg;
+      for (int j = 0; j < a.tps; j++)
+        s += (double)a.part[(((size_t)stripe * a.tps + j) * CH + cl) * CHAN_P + p];
+    }
+  }
+  const float v = (float)s;
+  if (p < 3) { if (dWh) dWh[(size_t)p * n + c] = v; }
+  else if (p < 6) { if (dbh) dbh[(size_t)(p - 3) * n + c] = v; }
+  else if (p < 8) { if (dpeep && a.SW == 2) dpeep[(size_t)(p - 6) * n + c] = v; }
+  else { if (dbx) dbx[(size_t)(p - 8) * n + c] = v; }
+}
+
+}  // namespace pr

@@ -36,13 +36,16 @@ int fail(int code, const char *fmt, ...) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-enum { PATH_NONE = 0, PATH_TIME = 1 };
+enum { PATH_NONE = 0, PATH_TIME = 1, PATH_CHAN = 2 };
 
 struct Plan {
   int path = PATH_NONE;
-  int G = 1, S = 1, N = 1;
+  int G = 1, S = 1, N = 1, SW = 1;
   int tile = 0, tps = 0, ntiles = 0;
+  // channel path: stripes (sequence x channel group), tiles of sweep / adjoint
+  int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
+  size_t off_U = 0, off_dU = 0, off_gws = 0;
   size_t zero_bytes = 0;     // bytes cleared at the start of each call
   size_t solve_bytes = 0, adjoint_bytes = 0;
 };
@@ -88,8 +91,56 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->adjoint_bytes = o;
     return PR_OK;
   }
+  if (p->cell == PR_CELL_GRU_DIAG || p->cell == PR_CELL_LSTM_CIFG_DIAG) {
+    const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
+    pl->path = PATH_CHAN;
+    pl->SW = p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1;
+    const ChanGeomInfo gf = chan_geom(kc, p->n, false), ga = chan_geom(kc, p->n, true);
+    pl->CH = gf.CH;
+    const long long CG = (p->n + gf.CH - 1) / gf.CH;
+    if ((long long)p->B * CG > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many stripes");
+    pl->stripes = (int)(p->B * CG);
+    pl->tps = (p->T + gf.TT - 1) / gf.TT;
+    pl->tps_a = (p->T + ga.TT - 1) / ga.TT;
+    if ((long long)pl->tps * pl->stripes > 2147483647LL || (long long)pl->tps_a * pl->stripes > 2147483647LL)
+      return fail(PR_EUNSUPPORTED, "too many tiles");
+    pl->ntiles = pl->tps * pl->stripes;
+    pl->ntiles_a = pl->tps_a * pl->stripes;
+    const size_t es = p->dtype == PR_BF16 ? 2 : 4;
+    const int SW = pl->SW, AW = SW * SW + SW;
+    const size_t nt = (size_t)(pl->ntiles > pl->ntiles_a ? pl->ntiles : pl->ntiles_a);
+    const size_t rows = (size_t)p->B * p->T;
+    size_t o = 0;
+    pl->off_state = o; o = align256(o + sizeof(SolveState));
+    pl->off_agg = o; o = align256(o + nt * gf.CH * AW * 8);
+    pl->off_incl = o; o = align256(o + nt * gf.CH * SW * 8);
+    pl->zero_bytes = o;
+    pl->off_bnd = o; o = align256(o + (size_t)2 * pl->ntiles * gf.CH * SW * 4);
+    pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
+    pl->solve_bytes = o;
+    pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
+    pl->off_part = o; o = align256(o + (size_t)pl->ntiles_a * gf.CH * 11 * 4);
+    const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
+    pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
+    pl->adjoint_bytes = o;
+    return PR_OK;
+  }
   return fail(PR_EUNSUPPORTED, "no kernel for cell %d jac %d dtype %d n %d d %d", p->cell, p->jac, p->dtype, p->n,
               p->d);
+}
+
+// U = x W_x^T + b_x on MFMA ([B*T, d] x [3n, d]^T).
+hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void *x, void *U, hipStream_t s) {
+  const bool bf = p->dtype == PR_BF16;
+  const size_t es = bf ? 2 : 4;
+  GemmArgs g{};
+  g.A = x; g.B = w->W_x; g.C = U; g.bias = w->b_x; g.ws = nullptr;
+  g.M = p->B * p->T; g.N = gates_of(p->cell) * p->n; g.K = p->d;
+  g.lda = p->d; g.ldb = p->d; g.ldc = g.N; g.splits = 1;
+  g.a_kc = true; g.b_kc = true; g.bf16 = bf; g.out_f32 = !bf;
+  g.vec_a = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+  g.vec_b = ((uintptr_t)w->W_x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+  return launch_gemm(g, s);
 }
 
 int kcell(int cell) { return cell == PR_CELL_TANH_RNN ? C_TANH : cell == PR_CELL_LINEAR ? C_LINEAR : C_GRU; }
@@ -236,6 +287,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
   const int kmax = max_iters < p->T ? max_iters : p->T;
 
   TimeArgs a{};
+  ChanArgs ca{};
   if (pl.path == PATH_TIME) {
     a.x = (const float *)x;
     a.h = (float *)h;
@@ -254,7 +306,26 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     a.tiles_per_seq = pl.tps;
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0);
+  } else {
+    ca.U = ws + pl.off_U;
+    ca.h = h;
+    ca.h0 = h0;
+    ca.Wh = w->W_h;
+    ca.bh = w->b_h;
+    ca.peep = p->cell == PR_CELL_LSTM_CIFG_DIAG ? w->peep : nullptr;
+    ca.B = p->B; ca.T = p->T; ca.n = p->n; ca.SW = pl.SW;
+    ca.tol = tol;
+    ca.max_iters = max_iters;
+    ca.st = (SolveState *)(ws + pl.off_state);
+    ca.agg = (unsigned long long *)(ws + pl.off_agg);
+    ca.incl = (unsigned long long *)(ws + pl.off_incl);
+    ca.bnd = (float *)(ws + pl.off_bnd);
+    ca.stripes = pl.stripes;
+    ca.tps = pl.tps;
+    ca.ntiles = pl.ntiles;
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
   }
+  const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : kcell(p->cell);
 
   int first, next;
   poll_schedule(&first, &next);
@@ -268,7 +339,12 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       a.k = kk;
       const bool ev = tr.on && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      HIPCHK(launch_time_sweep(kcell(p->cell), pl.N, a, s));
+      if (pl.path == PATH_TIME) {
+        HIPCHK(launch_time_sweep(kc, pl.N, a, s));
+      } else {
+        ca.k = kk;
+        HIPCHK(launch_chan_sweep(kc, p->dtype == PR_BF16, ca, s));
+      }
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
     HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
@@ -356,6 +432,61 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
       HIPCHK(launch_time_reduce(kcell(p->cell), pl.N, a, a.part, dW->W_x, dW->b_x, dW->W_h, dW->b_h, s));
     return PR_OK;
   }
+  if (pl.path == PATH_CHAN) {
+    const bool bf = p->dtype == PR_BF16;
+    const size_t es = bf ? 2 : 4;
+    const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    ChanArgs ca{};
+    ca.U = ws + pl.off_U;
+    ca.h = (void *)h;
+    ca.h0 = h0;
+    ca.Wh = w->W_h;
+    ca.bh = w->b_h;
+    ca.peep = p->cell == PR_CELL_LSTM_CIFG_DIAG ? w->peep : nullptr;
+    ca.g = g;
+    ca.lam = lambda;
+    ca.dh0 = dh0;
+    ca.dU = ws + pl.off_dU;
+    ca.part = (float *)(ws + pl.off_part);
+    ca.B = p->B; ca.T = p->T; ca.n = p->n; ca.SW = pl.SW;
+    ca.k = 1;
+    ca.st = (SolveState *)(ws + pl.off_state);
+    ca.agg = (unsigned long long *)(ws + pl.off_agg);
+    ca.incl = (unsigned long long *)(ws + pl.off_incl);
+    ca.stripes = pl.stripes;
+    ca.tps = pl.tps_a;
+    ca.ntiles = pl.ntiles_a;
+    Trace &tr = trace();
+    const bool ev = tr.on && tr.made;
+    if (ev && tr.ad_pending == Trace::CAP) HIPCHK(tr.drain_adjoint());
+    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending], s));
+    HIPCHK(launch_chan_adjoint(kc, bf, ca, s));
+    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending++ + 1], s));
+    if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
+      HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
+    const int rows = p->B * p->T, G3 = 3 * p->n;
+    if (dx) {  // dx = dU W_x
+      GemmArgs gm{};
+      gm.A = ws + pl.off_dU; gm.B = w->W_x; gm.C = dx; gm.bias = nullptr; gm.ws = nullptr;
+      gm.M = rows; gm.N = p->d; gm.K = G3; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d; gm.splits = 1;
+      gm.a_kc = true; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = !bf;
+      gm.vec_a = ((size_t)G3 * es) % 16 == 0;
+      gm.vec_b = ((uintptr_t)w->W_x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+      HIPCHK(launch_gemm(gm, s));
+    }
+    if (dW && dW->W_x) {  // dW_x = dU^T x
+      GemmArgs gm{};
+      gm.A = ws + pl.off_dU; gm.B = x; gm.C = dW->W_x; gm.bias = nullptr; gm.ws = (float *)(ws + pl.off_gws);
+      gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d;
+      gm.splits = gemm_splits(G3, p->d, rows);
+      gm.a_kc = false; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = true;
+      gm.vec_a = ((size_t)G3 * es) % 16 == 0;
+      gm.vec_b = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+      HIPCHK(launch_gemm(gm, s));
+    }
+    return PR_OK;
+  }
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
 }
 
@@ -366,6 +497,12 @@ size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n) {
     if (!N) return 0;
     const size_t nt = (size_t)B * ((T + time_tile(N) - 1) / time_tile(N));
     return align256(sizeof(SolveState)) + align256(nt * (N * N + N) * 8) + align256(nt * N * 8);
+  }
+  if (jac == PR_JAC_DIAG || jac == PR_JAC_BLOCK2) {
+    const int SW = jac == PR_JAC_BLOCK2 ? 2 : 1;
+    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n, false);
+    const size_t nt = (size_t)B * ((n + gi.CH - 1) / gi.CH) * ((T + gi.TT - 1) / gi.TT);
+    return align256(sizeof(SolveState)) + align256(nt * gi.CH * (SW * SW + SW) * 8) + align256(nt * gi.CH * SW * 8);
   }
   return 0;
 }
@@ -383,6 +520,22 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
   HIPCHK(launch_zero(ws, need, s));
+  if (jac != PR_JAC_DENSE) {
+    const int SW = jac == PR_JAC_BLOCK2 ? 2 : 1;
+    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n, false);
+    ChanArgs ca{};
+    ca.A = A; ca.b = b; ca.y = y;
+    ca.B = B; ca.T = T; ca.n = n; ca.SW = SW; ca.reverse = reverse ? 1 : 0;
+    ca.stripes = B * ((n + gi.CH - 1) / gi.CH);
+    ca.tps = (T + gi.TT - 1) / gi.TT;
+    ca.ntiles = ca.stripes * ca.tps;
+    ca.st = (SolveState *)ws;
+    ca.agg = (unsigned long long *)(ws + align256(sizeof(SolveState)));
+    ca.incl = (unsigned long long *)(ws + align256(sizeof(SolveState)) +
+                                     align256((size_t)ca.ntiles * gi.CH * (SW * SW + SW) * 8));
+    HIPCHK(launch_chan_scan(SW, ca, s));
+    return PR_OK;
+  }
   const int N = time_padded_n(n);
   ScanArgs a{};
   a.A = A; a.b = b; a.y = y;
