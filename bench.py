@@ -13,15 +13,19 @@ Prints one JSON line (rank 0, N = 1).
 """
 from __future__ import annotations
 
-import argparse
-import json
 import os
 import sys
-import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import time  # noqa: E402
+
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy  # noqa: E402  (input generator only)
+
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFS = 157.3
@@ -29,37 +33,71 @@ FP32_MFMA_PEAK_TFS = 157.3
 V100_DEER_TSB_PER_S = 16 * (1 << 20) / 15e-3
 
 
-def sweep_bytes_per_unit(p: dict, k: int) -> float:
-    """Algorithmic HBM bytes per (b, t) unit of one fused Newton sweep.
+def units_of(p: dict) -> int:
+    """Work units of one sweep: (b, t) for a dense state, (b, t, channel) else."""
+    if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
+        return p["B"] * p["T"] * p["n"]
+    return p["B"] * p["T"]
 
-    Sweep 1 starts from h = 0, so it reads x and writes h; later sweeps also
-    read the current iterate h.  (fp32: x, h in, h out = 4 + 4 + 4 bytes for
-    the scalar GRU.)
+
+def sweep_bytes_per_unit(p: dict, k: int) -> float:
+    """Algorithmic HBM bytes per unit of one fused Newton sweep.
+
+    Dense small state (time-parallel kernel): reads x (fused projection) and,
+    from sweep 2 on, the current iterate h; writes the new h.  Per-channel
+    cells: read U (3 gates), read h (sweep >= 2), write h.  Sweep 1 starts from
+    h = 0 and does not read it.
     """
-    es = 2 if p["dtype"] == 1 else 4
-    xin = p["d"] * 4 if p["cfg"] in (1, 2) else 0
-    hb = p["S"] * es
-    return xin + hb + (hb if k >= 2 else 0)
+    es = 2 if p["dtype"] == sy.DT_BF16 else 4
+    sw = 2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1
+    if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
+        return 3 * es + sw * es + (sw * es if k >= 2 else 0)
+    return p["d"] * 4 + p["n"] * 4 + (p["n"] * 4 if k >= 2 else 0)
 
 
 def adjoint_bytes_per_unit(p: dict) -> float:
-    """Reads x, h, g; writes lambda and dx (fp32, fused projection)."""
-    es = 2 if p["dtype"] == 1 else 4
-    return p["d"] * 4 + 2 * p["S"] * es + p["S"] * es + p["d"] * 4
+    """Adjoint scan kernel: dense small state reads x, h, g and writes lambda,
+    dx; per-channel cells read U, h, g and write lambda and dU (3 gates)."""
+    es = 2 if p["dtype"] == sy.DT_BF16 else 4
+    sw = 2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1
+    if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
+        return 3 * es + 2 * sw * es + sw * es + 3 * es
+    return 2 * p["d"] * 4 + 3 * p["n"] * 4
 
 
 def cpu_baseline(p: dict) -> dict:
+    """The oracle's fp64 sequential rollout, timed on this host.
+
+    Per-channel cells are independent across channels given x, so for them a
+    sample of channels is rolled out (the full input width, every sequence and
+    step) and the time is scaled by n / sample; dense cells run in full.
+    """
     import numpy as np
     import oracle
     threads = min(oracle.num_threads(), p["B"])
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    t0 = time.perf_counter()
-    oracle.rollout(p)
-    dt = time.perf_counter() - t0
     units = p["B"] * p["T"]
+    if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
+        ns = min(p["n"], max(1, int(16 * 1024 * 4096 * 8 / (p["d"] * p["T"] * p["B"] * 16))))  # ~5-10 s of fp64 work
+        ch = np.arange(ns)
+        n = p["n"]
+        rows = np.concatenate([g * n + ch for g in range(3)])
+        q = dict(p, n=ns, S=ns * (2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1), W_x=p["W_x"][rows],
+                 b_x=p["b_x"][rows], W_h=p["W_h"][rows], b_h=p["b_h"][rows],
+                 peep=None if p["peep"] is None else np.concatenate([p["peep"][ch], p["peep"][n + ch]]))
+        q["h0"] = np.zeros((p["B"], q["S"]))
+        t0 = time.perf_counter()
+        oracle.rollout(q)
+        dt = (time.perf_counter() - t0) * n / ns
+        sample = (f"fp64 sequential rollout of {ns} of {n} channels (all {p['B']} sequences x {p['T']} steps, "
+                  f"full input width), OpenMP over sequences, time scaled by {n}/{ns}")
+    else:
+        t0 = time.perf_counter()
+        oracle.rollout(p)
+        dt = time.perf_counter() - t0
+        sample = (f"full workload: fp64 sequential rollout of all {p['B']} sequences x {p['T']} steps, "
+                  f"OpenMP over sequences")
     return {"value": units / dt, "unit": "timesteps*batch/s", "cores": threads, "kind": "oracle",
-            "sample": f"full workload: fp64 sequential rollout of all {p['B']} sequences x {p['T']} steps, "
-                      f"OpenMP over sequences; {dt:.2f} s wall", "seconds": dt}
+            "sample": sample + f"; {dt:.2f} s", "seconds": dt}
 
 
 def main() -> int:
@@ -81,7 +119,6 @@ def main() -> int:
     import torch
 
     from nonlinear_rnn_evaluation_newton_amd import binding as bd
-    from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -131,7 +168,6 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     tr = bd.trace_read() if not args.no_trace else None
-    bd.trace(False)
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     # solve alone (context; same inputs)
@@ -145,21 +181,35 @@ def main() -> int:
     iters = iters_seen[-1]
     roofline = None
     extra = {}
+    wu = units_of(p)
+    chan = p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
     if tr is not None and tr["sweep_launches"] > 0:
-        per_step_bytes = sum(sweep_bytes_per_unit(p, k) for k in range(1, iters + 1)) * units
-        nsteps = tr["sweep_launches"] / iters
+        per_solve_bytes = sum(sweep_bytes_per_unit(p, k) for k in range(1, iters + 1)) * wu
+        nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
-        achieved = per_step_bytes * nsteps / (tr["sweep_ms"] * 1e-3) / 1e9
+        achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "k_time_sweep (fused cell + Jacobian + scan + update)",
+                    "kernel": ("k_chan_sweep" if chan else "k_time_sweep") +
+                              " (fused cell + Jacobian + scan + update)",
                     "avg_launch_us": round(avg_ms * 1e3, 2),
-                    "bytes_per_launch": per_step_bytes / iters}
+                    "bytes_per_launch": per_solve_bytes / iters}
         if tr["adjoint_launches"] > 0:
             adj_ms = tr["adjoint_ms"] / tr["adjoint_launches"]
             extra["adjoint_kernel"] = {"avg_launch_us": round(adj_ms * 1e3, 2),
-                                       "achieved_GBs": round(adjoint_bytes_per_unit(p) * units / (adj_ms * 1e-3) / 1e9, 1)}
+                                       "achieved_GBs": round(adjoint_bytes_per_unit(p) * wu / (adj_ms * 1e-3) / 1e9, 1)}
+        pm, pn = bd.trace_kernel(bd.TRACE_PROJECTION)
+        if pn > 0:
+            flops = 2.0 * B * T * p["d"] * p["G"] * p["n"]
+            peak = 2500.0 if p["dtype"] == sy.DT_BF16 else FP32_MFMA_PEAK_TFS
+            tfs = flops / (pm / pn * 1e-3) / 1e12
+            extra["projection_gemm"] = {"avg_launch_us": round(pm / pn * 1e3, 2), "TFLOP/s": round(tfs, 1),
+                                        "peak": peak, "frac": round(tfs / peak, 4)}
+        gm, gn = bd.trace_kernel(bd.TRACE_ADJOINT_PRODUCTS)
+        if gn > 0:
+            extra["adjoint_products_us"] = round(gm / gn * 1e3, 2)
 
+    bd.trace(False)
     value = units / (ms_step * 1e-3)
     line = {
         "metric": "timesteps*batch/sec per converged Newton solve; scan HBM GB/s; speedup vs seq",

@@ -22,7 +22,8 @@ PR_F32, PR_BF16 = 0, 1
 PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2 = 0, 1, 2
 
 EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_scan_workspace_bytes",
-           "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read"]
+           "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
+           "pararnn_trace_kernel"]
 
 
 class Problem(C.Structure):
@@ -75,6 +76,8 @@ def lib():
         L.pararnn_trace.restype = I
         L.pararnn_trace_read.argtypes = [P, P, P, P]
         L.pararnn_trace_read.restype = I
+        L.pararnn_trace_kernel.argtypes = [I, P, P]
+        L.pararnn_trace_kernel.restype = I
         _lib = L
     return _lib
 
@@ -146,6 +149,18 @@ def trace_read() -> dict:
     if st < 0:
         raise PararnnError(st, "pararnn_trace_read")
     return dict(sweep_ms=sm.value, sweep_launches=sl.value, adjoint_ms=am.value, adjoint_launches=al.value)
+
+
+TRACE_SWEEP, TRACE_ADJOINT, TRACE_PROJECTION, TRACE_ADJOINT_PRODUCTS = 0, 1, 2, 3
+
+
+def trace_kernel(which: int):
+    """(total ms, launches) of one traced category."""
+    ms, n = C.c_double(0), C.c_longlong(0)
+    st = lib().pararnn_trace_kernel(int(which), C.byref(ms), C.byref(n))
+    if st < 0:
+        raise PararnnError(st, "pararnn_trace_kernel")
+    return ms.value, n.value
 
 
 def scan_workspace_bytes(jac: int, B: int, T: int, n: int) -> int:

@@ -156,39 +156,61 @@ SolveState *host_state() {
   return hs;
 }
 
-// Event timing of the main kernels (pararnn_trace).
+// Event timing of the main kernels (pararnn_trace).  Categories: Newton
+// sweeps (only launches that did work are counted), the adjoint's scan
+// kernel, the input projection, the adjoint's products and reductions.
+enum { TR_SWEEP = 0, TR_ADJ = 1, TR_PROJ = 2, TR_AGEMM = 3, TR_N = 4 };
 struct Trace {
   bool on = false;
-  double sweep_ms = 0, adj_ms = 0;
-  long long sweeps = 0, adjs = 0;
-  static constexpr int CAP = 256;
-  hipEvent_t sw[2 * CAP] = {};
-  hipEvent_t ad[2 * CAP] = {};
-  int ad_pending = 0;
   bool made = false;
+  double ms[TR_N] = {};
+  long long cnt[TR_N] = {};
+  static constexpr int CAP = 256;
+  hipEvent_t sw[2 * CAP] = {};        // per sweep of the current solve
+  hipEvent_t ev[TR_N][2 * CAP] = {};  // rings of the other categories
+  int pending[TR_N] = {};
   hipError_t make() {
     if (made) return hipSuccess;
     for (int i = 0; i < 2 * CAP; i++) {
       hipError_t e = hipEventCreate(&sw[i]);
       if (e != hipSuccess) return e;
-      e = hipEventCreate(&ad[i]);
-      if (e != hipSuccess) return e;
+      for (int c = 1; c < TR_N; c++) {
+        e = hipEventCreate(&ev[c][i]);
+        if (e != hipSuccess) return e;
+      }
     }
     made = true;
     return hipSuccess;
   }
-  hipError_t drain_adjoint() {
-    for (int i = 0; i < ad_pending; i++) {
-      hipError_t e = hipEventSynchronize(ad[2 * i + 1]);
+  hipError_t drain(int cat) {
+    for (int i = 0; i < pending[cat]; i++) {
+      hipError_t e = hipEventSynchronize(ev[cat][2 * i + 1]);
       if (e != hipSuccess) return e;
-      float ms = 0.f;
-      e = hipEventElapsedTime(&ms, ad[2 * i], ad[2 * i + 1]);
+      float m = 0.f;
+      e = hipEventElapsedTime(&m, ev[cat][2 * i], ev[cat][2 * i + 1]);
       if (e != hipSuccess) return e;
-      adj_ms += ms;
-      adjs++;
+      ms[cat] += m;
+      cnt[cat]++;
     }
-    ad_pending = 0;
+    pending[cat] = 0;
     return hipSuccess;
+  }
+  hipError_t drain_all() {
+    for (int c = 1; c < TR_N; c++) {
+      hipError_t e = drain(c);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  // bracket a launch group of category cat (cat != TR_SWEEP); returns the slot or -1
+  int begin(int cat, hipStream_t s) {
+    if (!on || !made) return -1;
+    if (pending[cat] == CAP && drain(cat) != hipSuccess) return -1;
+    const int i = pending[cat]++;
+    return hipEventRecord(ev[cat][2 * i], s) == hipSuccess ? i : -1;
+  }
+  void end(int cat, int i, hipStream_t s) {
+    if (i >= 0) hipEventRecord(ev[cat][2 * i + 1], s);
   }
 };
 Trace &trace() {
@@ -231,12 +253,14 @@ const char *pararnn_last_error(void) { return g_err.c_str(); }
 int pararnn_trace(int enable) {
   Trace &t = trace();
   if (t.on) {
-    hipError_t e = t.drain_adjoint();
+    hipError_t e = t.drain_all();
     if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
   }
   t.on = enable != 0;
-  t.sweep_ms = t.adj_ms = 0;
-  t.sweeps = t.adjs = 0;
+  for (int c = 0; c < TR_N; c++) {
+    t.ms[c] = 0;
+    t.cnt[c] = 0;
+  }
   if (t.on) {
     hipError_t e = t.make();
     if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
@@ -244,15 +268,20 @@ int pararnn_trace(int enable) {
   return PR_OK;
 }
 
-int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches) {
+int pararnn_trace_kernel(int which, double *ms, long long *launches) {
+  if (which < 0 || which >= TR_N) return fail(PR_EINVAL, "unknown trace category %d", which);
   Trace &t = trace();
-  hipError_t e = t.drain_adjoint();
+  hipError_t e = t.drain_all();
   if (e != hipSuccess) return fail(PR_EHIP, "trace: %s", hipGetErrorString(e));
-  if (sweep_ms) *sweep_ms = t.sweep_ms;
-  if (sweep_launches) *sweep_launches = t.sweeps;
-  if (adjoint_ms) *adjoint_ms = t.adj_ms;
-  if (adjoint_launches) *adjoint_launches = t.adjs;
+  if (ms) *ms = t.ms[which];
+  if (launches) *launches = t.cnt[which];
   return PR_OK;
+}
+
+int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches) {
+  int rc = pararnn_trace_kernel(TR_SWEEP, sweep_ms, sweep_launches);
+  if (rc != PR_OK) return rc;
+  return pararnn_trace_kernel(TR_ADJ, adjoint_ms, adjoint_launches);
 }
 
 size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
@@ -323,7 +352,9 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     ca.stripes = pl.stripes;
     ca.tps = pl.tps;
     ca.ntiles = pl.ntiles;
+    const int ti = tr.begin(TR_PROJ, s);
     HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    tr.end(TR_PROJ, ti, s);
   }
   const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : kcell(p->cell);
 
@@ -371,8 +402,8 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     for (int kk = 1; kk <= m; kk++) {
       float ms = 0.f;
       HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (kk - 1)], tr.sw[2 * (kk - 1) + 1]));
-      tr.sweep_ms += ms;
-      tr.sweeps++;
+      tr.ms[TR_SWEEP] += ms;
+      tr.cnt[TR_SWEEP]++;
     }
   }
   if (iters) *iters = out_iters;
@@ -423,11 +454,9 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0) | (al16(g) ? 4 : 0) | (al16(lambda) ? 8 : 0);
     Trace &tr = trace();
-    const bool ev = tr.on && tr.made;
-    if (ev && tr.ad_pending == Trace::CAP) HIPCHK(tr.drain_adjoint());
-    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending], s));
+    const int ti = tr.begin(TR_ADJ, s);
     HIPCHK(launch_time_adjoint(kcell(p->cell), pl.N, a, s));
-    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending++ + 1], s));
+    tr.end(TR_ADJ, ti, s);
     if (dW && (dW->W_x || dW->b_x || dW->W_h || dW->b_h))
       HIPCHK(launch_time_reduce(kcell(p->cell), pl.N, a, a.part, dW->W_x, dW->b_x, dW->W_h, dW->b_h, s));
     return PR_OK;
@@ -436,7 +465,10 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     const bool bf = p->dtype == PR_BF16;
     const size_t es = bf ? 2 : 4;
     const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
+    Trace &tr = trace();
+    const int tp = tr.begin(TR_PROJ, s);
     HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    tr.end(TR_PROJ, tp, s);
     ChanArgs ca{};
     ca.U = ws + pl.off_U;
     ca.h = (void *)h;
@@ -457,12 +489,10 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     ca.stripes = pl.stripes;
     ca.tps = pl.tps_a;
     ca.ntiles = pl.ntiles_a;
-    Trace &tr = trace();
-    const bool ev = tr.on && tr.made;
-    if (ev && tr.ad_pending == Trace::CAP) HIPCHK(tr.drain_adjoint());
-    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending], s));
+    const int ta = tr.begin(TR_ADJ, s);
     HIPCHK(launch_chan_adjoint(kc, bf, ca, s));
-    if (ev) HIPCHK(hipEventRecord(tr.ad[2 * tr.ad_pending++ + 1], s));
+    tr.end(TR_ADJ, ta, s);
+    const int tg = tr.begin(TR_AGEMM, s);
     if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
       HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
     const int rows = p->B * p->T, G3 = 3 * p->n;
@@ -485,6 +515,7 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
       gm.vec_b = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
       HIPCHK(launch_gemm(gm, s));
     }
+    tr.end(TR_AGEMM, tg, s);
     return PR_OK;
   }
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
