@@ -77,16 +77,23 @@ def cpu_baseline(p: dict) -> dict:
     threads = min(oracle.num_threads(), p["B"])
     units = p["B"] * p["T"]
     if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
-        ns = min(p["n"], max(1, int(16 * 1024 * 4096 * 8 / (p["d"] * p["T"] * p["B"] * 16))))  # ~5-10 s of fp64 work
-        ch = np.arange(ns)
         n = p["n"]
-        rows = np.concatenate([g * n + ch for g in range(3)])
-        q = dict(p, n=ns, S=ns * (2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1), W_x=p["W_x"][rows],
-                 b_x=p["b_x"][rows], W_h=p["W_h"][rows], b_h=p["b_h"][rows],
-                 peep=None if p["peep"] is None else np.concatenate([p["peep"][ch], p["peep"][n + ch]]))
-        q["h0"] = np.zeros((p["B"], q["S"]))
+
+        def sub(ns):
+            ch = np.arange(ns)
+            rows = np.concatenate([g * n + ch for g in range(3)])
+            q = dict(p, n=ns, S=ns * (2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1), W_x=p["W_x"][rows],
+                     b_x=p["b_x"][rows], W_h=p["W_h"][rows], b_h=p["b_h"][rows],
+                     peep=None if p["peep"] is None else np.concatenate([p["peep"][ch], p["peep"][n + ch]]))
+            q["h0"] = np.zeros((p["B"], q["S"]))
+            return q
+
         t0 = time.perf_counter()
-        oracle.rollout(q)
+        oracle.rollout(sub(1))
+        t1 = time.perf_counter() - t0
+        ns = int(min(n, max(1, 10.0 / max(t1, 1e-3))))  # about 10 s of fp64 work
+        t0 = time.perf_counter()
+        oracle.rollout(sub(ns))
         dt = (time.perf_counter() - t0) * n / ns
         sample = (f"fp64 sequential rollout of {ns} of {n} channels (all {p['B']} sequences x {p['T']} steps, "
                   f"full input width), OpenMP over sequences, time scaled by {n}/{ns}")
