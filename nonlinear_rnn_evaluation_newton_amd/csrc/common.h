@@ -229,3 +229,47 @@ __device__ inline float wave_sum(float v) {
 }
 
 }  // namespace pr
+
+namespace pr {
+
+// Start-of-sweep control shared by every kernel that opens a sweep: apply the
+// stop rule to the previous sweep's measure (k >= 2); block 0 finalises the
+// history entry and clears the shards sweep k + 1 will use.  Returns true
+// (to every thread of the block) when the solve has stopped.
+__device__ inline bool sweep_open(SolveState *st, int k, float tol, int T, int max_iters, int *s_stop) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int stop = ld_agent(&st->stopped) != 0;
+    if (!stop && k >= 2) {
+      unsigned d = ld_agent(&st->dslot[(k - 1) & 3][lane]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        unsigned o = (unsigned)__shfl_xor((int)d, off, 64);
+        d = d > o ? d : o;
+      }
+      int status;
+      if (stop_rule(__uint_as_float(d), k - 1, tol, T, max_iters, &status)) {
+        stop = 1;
+        if (blockIdx.x == 0 && lane == 0) {
+          st_agent((unsigned *)&st->iters, (unsigned)(k - 1));
+          st_agent((unsigned *)&st->status, (unsigned)status);
+          st_agent(&st->stopped, 1u);
+        }
+      }
+      if (blockIdx.x == 0 && lane == 0) st_agent(&st->hist[(k - 1) % PR_HIST], d);
+    }
+    if (!stop && blockIdx.x == 0) st_agent(&st->dslot[(k + 1) & 3][lane], 0u);
+    if (lane == 0) *s_stop = stop;
+  }
+  __syncthreads();
+  return *s_stop != 0;
+}
+
+// Later kernels of a sweep only test the sticky flag.
+__device__ inline bool sweep_is_stopped(const SolveState *st, int *s_stop) {
+  if (threadIdx.x == 0) *s_stop = ld_agent(&st->stopped) != 0;
+  __syncthreads();
+  return *s_stop != 0;
+}
+
+}  // namespace pr

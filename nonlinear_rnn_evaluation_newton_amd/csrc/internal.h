@@ -84,6 +84,39 @@ hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, flo
                               hipStream_t s);
 hipError_t launch_chan_scan(int SW, ChanArgs &a, hipStream_t s);
 
+// ---------------- dense n = 64 path (MFMA scan) ----------------------------
+constexpr int D64_N = 64, D64_L = 64;  // state width, steps per chunk
+struct D64Args {
+  const float *U;       // [B*T, 192] input projection
+  float *h;             // [B*T, 64] iterate (read-only in the adjoint)
+  const float *h0;      // [B, 64] or null
+  const float *Wh, *bh; // [192, 64], [192] or null
+  float *gates;         // [B*T, 5, 64]: z, alpha, beta, gamma, and res (sweep) or eta (adjoint)
+  float *aggP;          // [nchunks, 64, 64] chunk products
+  float *aggb;          // [nchunks, 64] chunk offsets
+  float *carry;         // [nchunks, 64] state entering each chunk
+  const float *g;       // adjoint: [B*T, 64]
+  float *lam;           // adjoint: [B*T, 64]
+  int B, T, cps, nchunks;  // chunks per sequence, total chunks
+  int k;
+  float tol;
+  int max_iters;
+  SolveState *st;
+  int adjoint;          // reverse-time scan with transposed Jacobians
+};
+hipError_t launch_d64_sweep(D64Args &a, hipStream_t s);  // the 4 kernels of one sweep
+hipError_t launch_d64_adjoint_scan(D64Args &a, hipStream_t s);
+struct D64AdjArgs {
+  const float *gates, *lam, *h, *h0, *Wh;
+  float *dU;            // [B*T, 192] gate pre-activation gradients
+  float *dA;            // [B*T, 192] gradients of the recurrent pre-activations
+  float *hprev;         // [B*T, 64] state entering each step
+  float *dh0;           // [B, 64] or null
+  int B, T;
+};
+hipError_t launch_d64_adjoint_epilogue(const D64AdjArgs &a, hipStream_t s);
+hipError_t launch_colsum(const float *X, int rows, int cols, float *out, hipStream_t s);
+
 // ---------------- MFMA GEMM ------------------------------------------------
 struct GemmArgs {
   const void *A, *B;    // A: [M,K] (a_kc) or [K,M]; B: [N,K] (b_kc) or [K,N]

@@ -1,0 +1,495 @@
+// Full-DEER path for a dense 64 x 64 Jacobian (GRU, n = 64): the cubic-cost
+// case the DEER summary flags ("Surprising findings": the explicit Jacobian
+// and its matrix products scale as O(n^3)), on fp32 MFMA.
+//
+// A sweep is four launches:
+//  1. gates: a = W_h h_{t-1} for all steps on MFMA, then per step the GRU
+//     gates and the vectors that define J_t = diag(z) + diag(alpha) W_hz +
+//     diag(beta) W_hn + diag(gamma) W_hr, plus the residual r_t = f_t - h_t.
+//     J_t itself (16 KB per step) is never stored: it is rebuilt on the fly.
+//  2. chunk products: each wavefront composes the affine operators of L = 64
+//     consecutive steps, P = J_L ... J_1 on MFMA (v_mfma_f32_32x32x2_f32) and
+//     the offset b by a matrix-vector chain, and stores (P, b).
+//  3. chunk carries: per sequence, c_{j+1} = P_j c_j + b_j.
+//  4. chunk replay: each chunk re-runs dh_t = J_t dh_{t-1} + r_t from its
+//     carry, updates h in place and measures max |dh|.
+// The adjoint runs the same scan backwards in time with J^T (step 2 with the
+// Jacobian transposed, step 4 as lambda_t = J_{t+1}^T lambda_{t+1} + g_t).
+//
+// Register trick of step 2: a 32x32 MFMA result lane holds rows
+// 8(r/4) + 4(l/32) + r%4 of column l%32 in register r.  Taking the k index of
+// the next product in that same order makes register r of the previous
+// product exactly the B operand of k-step r, so the running product never
+// leaves the accumulators; only the A operand (J_t) is rebuilt, one value per
+// lane and k-step, from the three weight matrices held in LDS.
+#include "internal.h"
+
+namespace pr {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_d;
+
+constexpr int WLD = 68;  // padded LDS row stride (floats) of 64-wide matrices
+
+__device__ inline int r0_of(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// 1. gates (sweep: z, alpha, beta, gamma, res;  adjoint: z, alpha, beta, gamma, eta)
+// ---------------------------------------------------------------------------
+template <bool ADJ>
+__global__ __launch_bounds__(256) void k_d64_gates(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ __attribute__((aligned(16))) float sH[64 * WLD];
+  __shared__ __attribute__((aligned(16))) float sW[192 * WLD];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (!ADJ && sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
+  const int rows = a.B * a.T, T = a.T;
+  const int r0 = blockIdx.x * 64;
+  const bool first = !ADJ && a.k == 1;  // the iterate is h = 0 before sweep 1
+  for (int e = tid; e < 192 * 16; e += 256) {
+    const int row = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<float4 *>(&sW[row * WLD + c4]) = *reinterpret_cast<const float4 *>(a.Wh + row * 64 + c4);
+  }
+  for (int e = tid; e < 64 * 16; e += 256) {
+    const int rr = e >> 4, c4 = (e & 15) * 4, row = r0 + rr;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < rows) {
+      const int t = row % T, b = row / T;
+      if (t > 0) {
+        if (!first) v = *reinterpret_cast<const float4 *>(a.h + (size_t)(row - 1) * 64 + c4);
+      } else if (a.h0) {
+        v = *reinterpret_cast<const float4 *>(a.h0 + (size_t)b * 64 + c4);
+      }
+    }
+    *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = v;
+  }
+  __syncthreads();
+  // [64 rows] x [192 gate channels], K = 64: wave w owns row block (w & 1)
+  // and column blocks 3*(w >> 1) + {0, 1, 2}
+  const int rb = wid & 1, cb0 = 3 * (wid >> 1);
+  f32x16_d acc[3];
+#pragma unroll
+  for (int q = 0; q < 3; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[q][r] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < 32; s++) {
+    const int kk = 2 * s + (lane >> 5);
+    const float av = sH[(rb * 32 + (lane & 31)) * WLD + kk];
+#pragma unroll
+    for (int q = 0; q < 3; q++)
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sW[((cb0 + q) * 32 + (lane & 31)) * WLD + kk], acc[q], 0, 0, 0);
+  }
+  __syncthreads();
+  constexpr int CLD = 196;
+  float *sC = sW;  // reuse: [64][196]
+#pragma unroll
+  for (int q = 0; q < 3; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      sC[(rb * 32 + r0_of(r) + 4 * (lane >> 5)) * CLD + (cb0 + q) * 32 + (lane & 31)] = acc[q][r];
+  __syncthreads();
+  const int i = lane;
+  const float bhr = a.bh ? a.bh[i] : 0.f, bhz = a.bh ? a.bh[64 + i] : 0.f, bhn = a.bh ? a.bh[128 + i] : 0.f;
+  for (int rr = wid; rr < 64; rr += 4) {
+    const int row = r0 + rr;
+    if (row >= rows) break;
+    const float *Ur = a.U + (size_t)row * 192;
+    const float ar = sC[rr * CLD + i] + Ur[i] + bhr;
+    const float az = sC[rr * CLD + 64 + i] + Ur[64 + i] + bhz;
+    const float q = sC[rr * CLD + 128 + i] + bhn;
+    const float s = sH[rr * WLD + i];
+    const float r = fsigm(ar), z = fsigm(az);
+    const float c = ftanh(fmaf(r, q, Ur[128 + i]));
+    const float eta = (1.f - z) * (1.f - c * c);
+    float *G = a.gates + (size_t)row * 320;
+    G[i] = z;
+    G[64 + i] = (s - c) * z * (1.f - z);
+    G[128 + i] = eta * r;
+    G[192 + i] = eta * q * r * (1.f - r);
+    if (ADJ) {
+      G[256 + i] = eta;
+    } else {
+      const float f = fmaf(z, s - c, c);
+      const float hc = first ? 0.f : a.h[(size_t)row * 64 + i];
+      G[256 + i] = f - hc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. chunk products on MFMA
+// ---------------------------------------------------------------------------
+// Weight matrices in LDS, laid out so that lane (row i, k-run) reads 4
+// consecutive k with one 16-byte load: forward W*[i][k]; transposed
+// (adjoint) W*[k][i].  Order: z, n, r (the coefficients alpha, beta, gamma).
+template <bool TR>
+__device__ inline void stage_w3(const float *Wh, float *sW) {
+  const int mats[3] = {64, 128, 0};  // row offsets of W_hz, W_hn, W_hr in W_h [192, 64]
+  for (int e = threadIdx.x; e < 3 * 64 * 64; e += blockDim.x) {
+    const int m = e / 4096, rem = e % 4096, i = rem / 64, k = rem % 64;
+    const float v = TR ? Wh[(mats[m] + k) * 64 + i] : Wh[(mats[m] + i) * 64 + k];
+    sW[m * 64 * WLD + i * WLD + k] = v;
+  }
+}
+
+template <bool ADJ>
+__global__ __launch_bounds__(256) void k_d64_scanA(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ __attribute__((aligned(16))) float sW[3 * 64 * WLD];
+  __shared__ __attribute__((aligned(16))) float sB[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (!ADJ && sweep_is_stopped(a.st, &s_stop)) return;
+  stage_w3<ADJ>(a.Wh, sW);
+  __syncthreads();
+  const int chunk = blockIdx.x * 4 + wid;
+  if (chunk >= a.nchunks) return;
+  const int b = chunk / a.cps, j = chunk % a.cps, T = a.T;
+  const int h = lane >> 5, li = lane & 31;
+  const float *sWz = sW, *sWn = sW + 64 * WLD, *sWr = sW + 2 * 64 * WLD;
+
+  f32x16_d P[2][2];  // running product, [row block][column block]
+#pragma unroll
+  for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) P[ob][cb][r] = (ob == cb && r0_of(r) + 4 * h == li) ? 1.f : 0.f;
+  float bk[2][16];  // offset at this lane's k set {ib*32 + r0(r) + 4h}
+  float brow[2];    // offset at this lane's rows {ob*32 + li}
+#pragma unroll
+  for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) bk[ib][r] = 0.f;
+  brow[0] = brow[1] = 0.f;
+
+  for (int s = 0; s < D64_L; s++) {
+    const int sidx = j * D64_L + s;  // position in scan order
+    if (sidx >= T) break;
+    const int t = ADJ ? T - 1 - sidx : sidx;
+    const int cr = ADJ ? t + 1 : t;  // row holding the Jacobian's coefficients
+    const bool live = cr < T;        // the adjoint's last step has J = 0
+    const float *G = a.gates + (size_t)((size_t)b * T + (live ? cr : 0)) * 320;
+    float zk[2][16];  // z at this lane's rows of P (same index pattern as the k set)
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int kb = ib * 32 + 8 * r4 + 4 * h;
+        const float4 zv = live ? *reinterpret_cast<const float4 *>(G + kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+        zk[ib][4 * r4 + 0] = zv.x; zk[ib][4 * r4 + 1] = zv.y; zk[ib][4 * r4 + 2] = zv.z; zk[ib][4 * r4 + 3] = zv.w;
+      }
+    float crow[3][2], zrow[2], brhs[2];
+#pragma unroll
+    for (int ob = 0; ob < 2; ob++) {
+      const int i = ob * 32 + li;
+      zrow[ob] = live ? G[i] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 3; m++) crow[m][ob] = live ? G[64 * (m + 1) + i] : 0.f;
+      brhs[ob] = ADJ ? a.g[((size_t)b * T + t) * 64 + i] : a.gates[((size_t)b * T + t) * 320 + 256 + i];
+    }
+    // P_new = diag(z) P + M P,  b_new = z * b + M b + rhs
+    f32x16_d Pn[2][2];
+#pragma unroll
+    for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) Pn[ob][cb][r] = zk[ob][r] * P[ob][cb][r];
+    float part[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int kb = ib * 32 + 8 * r4 + 4 * h;
+        float ck[3][4];  // adjoint: coefficients at this run of k
+        if (ADJ) {
+#pragma unroll
+          for (int m = 0; m < 3; m++) {
+            const float4 cv = live ? *reinterpret_cast<const float4 *>(G + 64 * (m + 1) + kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+            ck[m][0] = cv.x; ck[m][1] = cv.y; ck[m][2] = cv.z; ck[m][3] = cv.w;
+          }
+        }
+#pragma unroll
+        for (int ob = 0; ob < 2; ob++) {
+          const int i = ob * 32 + li;
+          const float4 wz = *reinterpret_cast<const float4 *>(&sWz[i * WLD + kb]);
+          const float4 wn = *reinterpret_cast<const float4 *>(&sWn[i * WLD + kb]);
+          const float4 wr = *reinterpret_cast<const float4 *>(&sWr[i * WLD + kb]);
+          const float wzv[4] = {wz.x, wz.y, wz.z, wz.w}, wnv[4] = {wn.x, wn.y, wn.z, wn.w},
+                      wrv[4] = {wr.x, wr.y, wr.z, wr.w};
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int r = 4 * r4 + q;
+            float jv;
+            if (ADJ) jv = fmaf(ck[0][q], wzv[q], fmaf(ck[1][q], wnv[q], ck[2][q] * wrv[q]));
+            else jv = fmaf(crow[0][ob], wzv[q], fmaf(crow[1][ob], wnv[q], crow[2][ob] * wrv[q]));
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++)
+              Pn[ob][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(jv, P[ib][cb][r], Pn[ob][cb], 0, 0, 0);
+            part[ob] = fmaf(jv, bk[ib][r], part[ob]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ob = 0; ob < 2; ob++) {
+      part[ob] += __shfl_xor(part[ob], 32, 64);
+      brow[ob] = fmaf(zrow[ob], brow[ob], part[ob] + brhs[ob]);
+    }
+    // redistribute b to the k layout through this wavefront's LDS row
+    if (lane < 32) {
+      sB[wid][lane] = brow[0];
+      sB[wid][32 + lane] = brow[1];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const float4 v = *reinterpret_cast<const float4 *>(&sB[wid][ib * 32 + 8 * r4 + 4 * h]);
+        bk[ib][4 * r4 + 0] = v.x; bk[ib][4 * r4 + 1] = v.y; bk[ib][4 * r4 + 2] = v.z; bk[ib][4 * r4 + 3] = v.w;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++) P[ob][cb] = Pn[ob][cb];
+  }
+  float *Po = a.aggP + (size_t)chunk * 4096;
+#pragma unroll
+  for (int ob = 0; ob < 2; ob++)
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) Po[(ob * 32 + r0_of(r) + 4 * h) * 64 + cb * 32 + li] = P[ob][cb][r];
+  if (lane < 32) {
+    a.aggb[(size_t)chunk * 64 + lane] = brow[0];
+    a.aggb[(size_t)chunk * 64 + 32 + lane] = brow[1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. chunk carries, one block per sequence
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_d64_scanB(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ float sc[64];
+  if (!a.adjoint && sweep_is_stopped(a.st, &s_stop)) return;
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int i = tid >> 2, q = tid & 3;
+  if (tid < 64) sc[tid] = 0.f;
+  __syncthreads();
+  float4 pv[4];
+  auto loadP = [&](int chunk) {
+    const float *P = a.aggP + (size_t)chunk * 4096 + i * 64 + q * 16;
+#pragma unroll
+    for (int m = 0; m < 4; m++) pv[m] = *reinterpret_cast<const float4 *>(P + 4 * m);
+  };
+  const int c0 = b * a.cps;
+  loadP(c0);
+  for (int j = 0; j < a.cps; j++) {
+    const int chunk = c0 + j;
+    float4 cur[4] = {pv[0], pv[1], pv[2], pv[3]};
+    const float bj = q == 0 ? a.aggb[(size_t)chunk * 64 + i] : 0.f;
+    if (j + 1 < a.cps) loadP(chunk + 1);
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int k = q * 16 + 4 * m;
+      s = fmaf(cur[m].x, sc[k], s);
+      s = fmaf(cur[m].y, sc[k + 1], s);
+      s = fmaf(cur[m].z, sc[k + 2], s);
+      s = fmaf(cur[m].w, sc[k + 3], s);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (tid < 64) a.carry[(size_t)chunk * 64 + tid] = sc[tid];
+    __syncthreads();
+    if (q == 0) sc[i] = s + bj;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. chunk replay (one wavefront per chunk, lane = state row)
+// ---------------------------------------------------------------------------
+template <bool ADJ>
+__global__ __launch_bounds__(256) void k_d64_scanC(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ __attribute__((aligned(16))) float sY[4][3][64];
+  __shared__ unsigned s_dmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (!ADJ && sweep_is_stopped(a.st, &s_stop)) return;
+  const int chunk = blockIdx.x * 4 + wid;
+  unsigned dmax = 0;
+  if (chunk < a.nchunks) {
+    const int b = chunk / a.cps, j = chunk % a.cps, T = a.T;
+    const int i = lane;
+    // this lane's weights: forward row i of W_hz, W_hn, W_hr; adjoint column i
+    float w[3][64];
+    const int mats[3] = {64, 128, 0};
+#pragma unroll
+    for (int m = 0; m < 3; m++)
+#pragma unroll
+      for (int k = 0; k < 64; k++) w[m][k] = ADJ ? a.Wh[(mats[m] + k) * 64 + i] : a.Wh[(mats[m] + i) * 64 + k];
+    float y = a.carry[(size_t)chunk * 64 + i];
+    const bool first = !ADJ && a.k == 1;
+    for (int s = 0; s < D64_L; s++) {
+      const int sidx = j * D64_L + s;
+      if (sidx >= T) break;
+      const int t = ADJ ? T - 1 - sidx : sidx;
+      const size_t row = (size_t)b * T + t;
+      float yn;
+      if (!ADJ) {
+        const float *G = a.gates + row * 320;
+        sY[wid][0][i] = y;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float sz = 0.f, sn = 0.f, sr = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < 16; k4++) {
+          const float4 v = *reinterpret_cast<const float4 *>(&sY[wid][0][4 * k4]);
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            sz = fmaf(w[0][4 * k4 + q], vv[q], sz);
+            sn = fmaf(w[1][4 * k4 + q], vv[q], sn);
+            sr = fmaf(w[2][4 * k4 + q], vv[q], sr);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        yn = fmaf(G[i], y, fmaf(G[64 + i], sz, fmaf(G[128 + i], sn, fmaf(G[192 + i], sr, G[256 + i]))));
+        const float hc = first ? 0.f : a.h[row * 64 + i];
+        a.h[row * 64 + i] = hc + yn;
+        const unsigned u = __float_as_uint(fabsf(yn));
+        dmax = u > dmax ? u : dmax;
+      } else {
+        const bool live = t + 1 < T;
+        const float *G = a.gates + (row + (live ? 1 : 0)) * 320;
+        const float z = live ? G[i] : 0.f;
+        sY[wid][0][i] = live ? G[64 + i] * y : 0.f;
+        sY[wid][1][i] = live ? G[128 + i] * y : 0.f;
+        sY[wid][2][i] = live ? G[192 + i] * y : 0.f;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 3; m++)
+#pragma unroll
+          for (int k4 = 0; k4 < 16; k4++) {
+            const float4 v = *reinterpret_cast<const float4 *>(&sY[wid][m][4 * k4]);
+            acc = fmaf(w[m][4 * k4], v.x, acc);
+            acc = fmaf(w[m][4 * k4 + 1], v.y, acc);
+            acc = fmaf(w[m][4 * k4 + 2], v.z, acc);
+            acc = fmaf(w[m][4 * k4 + 3], v.w, acc);
+          }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        yn = fmaf(z, y, acc) + a.g[row * 64 + i];
+        a.lam[row * 64 + i] = yn;
+      }
+      y = yn;
+    }
+  }
+  if (!ADJ) {
+    dmax = wave_max_u32(dmax);
+    if (lane == 0) s_dmax[wid] = dmax;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned m = s_dmax[0];
+      for (int q = 1; q < 4; q++) m = s_dmax[q] > m ? s_dmax[q] : m;
+      max_agent(&a.st->dslot[a.k & 3][blockIdx.x % PR_DSHARDS], m);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// adjoint epilogue: gate pre-activation gradients and the shifted states
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_d64_adj_epi(const D64AdjArgs a) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t rows = (size_t)a.B * a.T;
+  if (e >= rows * 64) return;
+  const size_t row = e >> 6;
+  const int i = (int)(e & 63);
+  const int t = (int)(row % a.T), b = (int)(row / a.T);
+  const float l = a.lam[e];
+  const float *G = a.gates + row * 320;
+  const float al = G[64 + i], be = G[128 + i], ga = G[192 + i], eta = G[256 + i];
+  a.dU[row * 192 + i] = l * ga;        // r gate
+  a.dU[row * 192 + 64 + i] = l * al;   // z gate
+  a.dU[row * 192 + 128 + i] = l * eta; // n gate (input part)
+  a.dA[row * 192 + i] = l * ga;
+  a.dA[row * 192 + 64 + i] = l * al;
+  a.dA[row * 192 + 128 + i] = l * be;  // n gate (recurrent part, inside r * (.))
+  a.hprev[e] = t > 0 ? a.h[e - 64] : (a.h0 ? a.h0[(size_t)b * 64 + i] : 0.f);
+}
+
+// dh0 = J_0^T lambda_0, with J_0 from the gates of step 0
+__global__ __launch_bounds__(64) void k_d64_dh0(const D64AdjArgs a) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  const size_t row = (size_t)b * a.T;
+  const float *G = a.gates + row * 320;
+  const float *L = a.lam + row * 64;
+  float acc = G[i] * L[i];
+  for (int k = 0; k < 64; k++) {
+    const float lk = L[k];
+    acc = fmaf(G[64 + k] * lk, a.Wh[(64 + k) * 64 + i], acc);
+    acc = fmaf(G[128 + k] * lk, a.Wh[(128 + k) * 64 + i], acc);
+    acc = fmaf(G[192 + k] * lk, a.Wh[k * 64 + i], acc);
+  }
+  a.dh0[(size_t)b * 64 + i] = acc;
+}
+
+// column sums in fp64, fixed order (one block per column)
+__global__ __launch_bounds__(256) void k_colsum(const float *X, int rows, int cols, float *out) {
+  __shared__ double s[256];
+  const int c = blockIdx.x;
+  double acc = 0.0;
+  for (int r = threadIdx.x; r < rows; r += 256) acc += (double)X[(size_t)r * cols + c];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[c] = (float)s[0];
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_d64_sweep(D64Args &a, hipStream_t s) {
+  a.adjoint = 0;
+  const int rows = a.B * a.T;
+  hipLaunchKernelGGL(k_d64_gates<false>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanA<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanC<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_d64_adjoint_scan(D64Args &a, hipStream_t s) {
+  a.adjoint = 1;
+  const int rows = a.B * a.T;
+  hipLaunchKernelGGL(k_d64_gates<true>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanA<true>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_d64_scanC<true>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_d64_adjoint_epilogue(const D64AdjArgs &a, hipStream_t s) {
+  const size_t tot = (size_t)a.B * a.T * 64;
+  hipLaunchKernelGGL(k_d64_adj_epi, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a);
+  if (a.dh0) hipLaunchKernelGGL(k_d64_dh0, dim3(a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const float *X, int rows, int cols, float *out, hipStream_t s) {
+  hipLaunchKernelGGL(k_colsum, dim3(cols), dim3(256), 0, s, X, rows, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace pr

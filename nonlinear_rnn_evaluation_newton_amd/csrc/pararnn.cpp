@@ -36,7 +36,7 @@ int fail(int code, const char *fmt, ...) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-enum { PATH_NONE = 0, PATH_TIME = 1, PATH_CHAN = 2 };
+enum { PATH_NONE = 0, PATH_TIME = 1, PATH_CHAN = 2, PATH_D64 = 3 };
 
 struct Plan {
   int path = PATH_NONE;
@@ -46,6 +46,9 @@ struct Plan {
   int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0;
+  // dense n = 64 path
+  int cps = 0, nchunks = 0;
+  size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0;
   size_t zero_bytes = 0;     // bytes cleared at the start of each call
   size_t solve_bytes = 0, adjoint_bytes = 0;
 };
@@ -88,6 +91,35 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_bnd = o; o = align256(o + (size_t)2 * pl->ntiles * N * 4);
     pl->solve_bytes = o;
     pl->off_part = o; o = align256(o + (size_t)pl->ntiles * time_part_count(p->cell, N) * 4);
+    pl->adjoint_bytes = o;
+    return PR_OK;
+  }
+  if (p->cell == PR_CELL_GRU && p->jac == PR_JAC_DENSE && p->n == D64_N) {
+    if (p->dtype != PR_F32) return fail(PR_EUNSUPPORTED, "the dense n = 64 GRU runs in fp32 storage only");
+    pl->path = PATH_D64;
+    pl->cps = (p->T + D64_L - 1) / D64_L;
+    if ((long long)pl->cps * p->B > 2147483647LL || (long long)p->B * p->T * 320 > (1LL << 62))
+      return fail(PR_EUNSUPPORTED, "problem too large");
+    pl->nchunks = pl->cps * p->B;
+    const size_t rows = (size_t)p->B * p->T;
+    size_t o = 0;
+    pl->off_state = o; o = align256(o + sizeof(SolveState));
+    pl->zero_bytes = o;
+    pl->off_U = o; o = align256(o + rows * 192 * 4);
+    pl->off_gates = o; o = align256(o + rows * 320 * 4);
+    pl->off_aggP = o; o = align256(o + (size_t)pl->nchunks * 4096 * 4);
+    pl->off_aggb = o; o = align256(o + (size_t)pl->nchunks * 64 * 4);
+    pl->off_carry = o; o = align256(o + (size_t)pl->nchunks * 64 * 4);
+    pl->solve_bytes = o;
+    pl->off_dU = o; o = align256(o + rows * 192 * 4);
+    pl->off_dA = o; o = align256(o + rows * 192 * 4);
+    pl->off_hprev = o; o = align256(o + rows * 64 * 4);
+    const int K = (int)(rows < 2147483647ULL ? rows : 2147483647ULL);
+    const int s1 = gemm_splits(192, p->d, K), s2 = gemm_splits(192, 64, K);
+    const size_t gw = (size_t)(s1 > 1 ? s1 * 192 * p->d : 0) > (size_t)(s2 > 1 ? s2 * 192 * 64 : 0)
+                          ? (size_t)(s1 > 1 ? s1 * 192 * p->d : 0)
+                          : (size_t)(s2 > 1 ? s2 * 192 * 64 : 0);
+    pl->off_gws = o; o = align256(o + gw * 4);
     pl->adjoint_bytes = o;
     return PR_OK;
   }
@@ -317,7 +349,27 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
 
   TimeArgs a{};
   ChanArgs ca{};
-  if (pl.path == PATH_TIME) {
+  D64Args da{};
+  if (pl.path == PATH_D64) {
+    da.U = (const float *)(ws + pl.off_U);
+    da.h = (float *)h;
+    da.h0 = (const float *)h0;
+    da.Wh = (const float *)w->W_h;
+    da.bh = (const float *)w->b_h;
+    da.gates = (float *)(ws + pl.off_gates);
+    da.aggP = (float *)(ws + pl.off_aggP);
+    da.aggb = (float *)(ws + pl.off_aggb);
+    da.carry = (float *)(ws + pl.off_carry);
+    da.B = p->B; da.T = p->T; da.cps = pl.cps; da.nchunks = pl.nchunks;
+    da.tol = tol;
+    da.max_iters = max_iters;
+    da.st = (SolveState *)(ws + pl.off_state);
+    if (((uintptr_t)h % 16) || (h0 && ((uintptr_t)h0 % 16)) || ((uintptr_t)w->W_h % 16))
+      return fail(PR_EINVAL, "h, h0 and W_h must be 16-byte aligned for n = 64");
+    const int ti = tr.begin(TR_PROJ, s);
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    tr.end(TR_PROJ, ti, s);
+  } else if (pl.path == PATH_TIME) {
     a.x = (const float *)x;
     a.h = (float *)h;
     a.h0 = (const float *)h0;
@@ -372,6 +424,9 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
       if (pl.path == PATH_TIME) {
         HIPCHK(launch_time_sweep(kc, pl.N, a, s));
+      } else if (pl.path == PATH_D64) {
+        da.k = kk;
+        HIPCHK(launch_d64_sweep(da, s));
       } else {
         ca.k = kk;
         HIPCHK(launch_chan_sweep(kc, p->dtype == PR_BF16, ca, s));
@@ -459,6 +514,74 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     tr.end(TR_ADJ, ti, s);
     if (dW && (dW->W_x || dW->b_x || dW->W_h || dW->b_h))
       HIPCHK(launch_time_reduce(kcell(p->cell), pl.N, a, a.part, dW->W_x, dW->b_x, dW->W_h, dW->b_h, s));
+    return PR_OK;
+  }
+  if (pl.path == PATH_D64) {
+    if (((uintptr_t)h % 16) || (h0 && ((uintptr_t)h0 % 16)) || ((uintptr_t)w->W_h % 16) || ((uintptr_t)g % 16))
+      return fail(PR_EINVAL, "h, h0, g and W_h must be 16-byte aligned for n = 64");
+    if (!lambda) return fail(PR_EINVAL, "the dense n = 64 adjoint needs the lambda output buffer");
+    Trace &tr = trace();
+    const int tp = tr.begin(TR_PROJ, s);
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    tr.end(TR_PROJ, tp, s);
+    D64Args da{};
+    da.U = (const float *)(ws + pl.off_U);
+    da.h = (float *)h;
+    da.h0 = (const float *)h0;
+    da.Wh = (const float *)w->W_h;
+    da.bh = (const float *)w->b_h;
+    da.gates = (float *)(ws + pl.off_gates);
+    da.aggP = (float *)(ws + pl.off_aggP);
+    da.aggb = (float *)(ws + pl.off_aggb);
+    da.carry = (float *)(ws + pl.off_carry);
+    da.g = (const float *)g;
+    da.lam = (float *)lambda;
+    da.B = p->B; da.T = p->T; da.cps = pl.cps; da.nchunks = pl.nchunks;
+    da.st = (SolveState *)(ws + pl.off_state);
+    const int ta = tr.begin(TR_ADJ, s);
+    HIPCHK(launch_d64_adjoint_scan(da, s));
+    tr.end(TR_ADJ, ta, s);
+    const int tg = tr.begin(TR_AGEMM, s);
+    D64AdjArgs ea{};
+    ea.gates = da.gates; ea.lam = da.lam; ea.h = da.h; ea.h0 = da.h0; ea.Wh = da.Wh;
+    ea.dU = (float *)(ws + pl.off_dU);
+    ea.dA = (float *)(ws + pl.off_dA);
+    ea.hprev = (float *)(ws + pl.off_hprev);
+    ea.dh0 = (float *)dh0;
+    ea.B = p->B; ea.T = p->T;
+    HIPCHK(launch_d64_adjoint_epilogue(ea, s));
+    const int rows = p->B * p->T;
+    if (dW && dW->b_x) HIPCHK(launch_colsum(ea.dU, rows, 192, dW->b_x, s));
+    if (dW && dW->b_h) HIPCHK(launch_colsum(ea.dA, rows, 192, dW->b_h, s));
+    if (dx) {  // dx = dU W_x
+      GemmArgs gm{};
+      gm.A = ea.dU; gm.B = w->W_x; gm.C = dx;
+      gm.M = rows; gm.N = p->d; gm.K = 192; gm.lda = 192; gm.ldb = p->d; gm.ldc = p->d; gm.splits = 1;
+      gm.a_kc = true; gm.b_kc = false; gm.bf16 = false; gm.out_f32 = true;
+      gm.vec_a = true;
+      gm.vec_b = ((uintptr_t)w->W_x % 16 == 0) && (p->d % 4) == 0;
+      HIPCHK(launch_gemm(gm, s));
+    }
+    if (dW && dW->W_x) {  // dW_x = dU^T x
+      GemmArgs gm{};
+      gm.A = ea.dU; gm.B = x; gm.C = dW->W_x; gm.ws = (float *)(ws + pl.off_gws);
+      gm.M = 192; gm.N = p->d; gm.K = rows; gm.lda = 192; gm.ldb = p->d; gm.ldc = p->d;
+      gm.splits = gemm_splits(192, p->d, rows);
+      gm.a_kc = false; gm.b_kc = false; gm.bf16 = false; gm.out_f32 = true;
+      gm.vec_a = true;
+      gm.vec_b = ((uintptr_t)x % 16 == 0) && (p->d % 4) == 0;
+      HIPCHK(launch_gemm(gm, s));
+    }
+    if (dW && dW->W_h) {  // dW_h = dA^T h_prev
+      GemmArgs gm{};
+      gm.A = ea.dA; gm.B = ea.hprev; gm.C = dW->W_h; gm.ws = (float *)(ws + pl.off_gws);
+      gm.M = 192; gm.N = 64; gm.K = rows; gm.lda = 192; gm.ldb = 64; gm.ldc = 64;
+      gm.splits = gemm_splits(192, 64, rows);
+      gm.a_kc = false; gm.b_kc = false; gm.bf16 = false; gm.out_f32 = true;
+      gm.vec_a = true; gm.vec_b = true;
+      HIPCHK(launch_gemm(gm, s));
+    }
+    tr.end(TR_AGEMM, tg, s);
     return PR_OK;
   }
   if (pl.path == PATH_CHAN) {
