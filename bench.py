@@ -190,7 +190,25 @@ def main() -> int:
     extra = {}
     wu = units_of(p)
     chan = p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
-    if tr is not None and tr["sweep_launches"] > 0:
+    dense64 = p["cell"] == sy.CELL_GRU and p["n"] == 64
+    if tr is not None and tr["sweep_launches"] > 0 and dense64:
+        # full DEER, n = 64: the chunk-product kernel composes one 64 x 64
+        # Jacobian per step on fp32 MFMA (2 n^3 flops) and carries the offset
+        # (2 n^2): 532,480 algorithmic flops per step
+        dm, dn = bd.trace_kernel(bd.TRACE_DENSE_PRODUCTS)
+        flops = 2.0 * 64 ** 3 + 2.0 * 64 ** 2
+        tfs = flops * B * T / (dm / dn * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                    "frac": round(tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": None,
+                    "kernel": "k_d64_scanA (64x64 Jacobian chunk products, fp32 MFMA)",
+                    "avg_launch_us": round(dm / dn * 1e3, 2), "flops_per_launch": flops * B * T}
+        extra["sweep_avg_us"] = round(tr["sweep_ms"] / tr["sweep_launches"] * 1e3, 2)
+        if tr["adjoint_launches"] > 0:
+            extra["adjoint_scan_us"] = round(tr["adjoint_ms"] / tr["adjoint_launches"] * 1e3, 2)
+        gm, gn = bd.trace_kernel(bd.TRACE_ADJOINT_PRODUCTS)
+        if gn > 0:
+            extra["adjoint_products_us"] = round(gm / gn * 1e3, 2)
+    elif tr is not None and tr["sweep_launches"] > 0:
         per_solve_bytes = sum(sweep_bytes_per_unit(p, k) for k in range(1, iters + 1)) * wu
         nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]

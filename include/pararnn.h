@@ -163,12 +163,14 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
  */
 int pararnn_trace(int enable);
 int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches);
-/* Totals of one category: 0 Newton sweeps, 1 the adjoint's scan kernel,
- * 2 the input projection, 3 the adjoint's products and reductions. */
+/* Totals of one category: 0 Newton sweeps, 1 the adjoint's scan kernel(s),
+ * 2 the input projection, 3 the adjoint's products and reductions, 4 the
+ * chunk-product kernel of the dense n = 64 path (within its sweeps). */
 #define PR_TRACE_SWEEP 0
 #define PR_TRACE_ADJOINT 1
 #define PR_TRACE_PROJECTION 2
 #define PR_TRACE_ADJOINT_PRODUCTS 3
+#define PR_TRACE_DENSE_PRODUCTS 4
 int pararnn_trace_kernel(int which, double *ms, long long *launches);
 
 /* Static text for a status code. */

@@ -151,7 +151,7 @@ def trace_read() -> dict:
     return dict(sweep_ms=sm.value, sweep_launches=sl.value, adjoint_ms=am.value, adjoint_launches=al.value)
 
 
-TRACE_SWEEP, TRACE_ADJOINT, TRACE_PROJECTION, TRACE_ADJOINT_PRODUCTS = 0, 1, 2, 3
+TRACE_SWEEP, TRACE_ADJOINT, TRACE_PROJECTION, TRACE_ADJOINT_PRODUCTS, TRACE_DENSE_PRODUCTS = 0, 1, 2, 3, 4
 
 
 def trace_kernel(which: int):

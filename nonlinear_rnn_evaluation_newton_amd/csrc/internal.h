@@ -104,7 +104,8 @@ struct D64Args {
   SolveState *st;
   int adjoint;          // reverse-time scan with transposed Jacobians
 };
-hipError_t launch_d64_sweep(D64Args &a, hipStream_t s);  // the 4 kernels of one sweep
+// one sweep = part 0 (gates), part 1 (chunk products), part 2 (carries + replay)
+hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s);
 hipError_t launch_d64_adjoint_scan(D64Args &a, hipStream_t s);
 struct D64AdjArgs {
   const float *gates, *lam, *h, *h0, *Wh;
@@ -115,7 +116,8 @@ struct D64AdjArgs {
   int B, T;
 };
 hipError_t launch_d64_adjoint_epilogue(const D64AdjArgs &a, hipStream_t s);
-hipError_t launch_colsum(const float *X, int rows, int cols, float *out, hipStream_t s);
+// column sums of X [rows, cols] (cols <= 256 per pass), fp64 partials [512][cols] in `part`
+hipError_t launch_colsum(const float *X, int rows, int cols, float *out, double *part, hipStream_t s);
 
 // ---------------- MFMA GEMM ------------------------------------------------
 struct GemmArgs {

@@ -281,19 +281,30 @@ __global__ __launch_bounds__(256) void k_d64_scanB(const D64Args a) {
   const int i = tid >> 2, q = tid & 3;
   if (tid < 64) sc[tid] = 0.f;
   __syncthreads();
-  float4 pv[4];
-  auto loadP = [&](int chunk) {
+  constexpr int PF = 4;  // chunks prefetched ahead of the carry chain
+  float4 pv[PF][4];
+  const int c0 = b * a.cps;
+  auto loadP = [&](int slot, int chunk) {
     const float *P = a.aggP + (size_t)chunk * 4096 + i * 64 + q * 16;
 #pragma unroll
-    for (int m = 0; m < 4; m++) pv[m] = *reinterpret_cast<const float4 *>(P + 4 * m);
+    for (int m = 0; m < 4; m++) pv[slot][m] = *reinterpret_cast<const float4 *>(P + 4 * m);
   };
-  const int c0 = b * a.cps;
-  loadP(c0);
+#pragma unroll
+  for (int f = 0; f < PF; f++)
+    if (f < a.cps) loadP(f, c0 + f);
   for (int j = 0; j < a.cps; j++) {
     const int chunk = c0 + j;
-    float4 cur[4] = {pv[0], pv[1], pv[2], pv[3]};
+    const int slot = j % PF;
+    float4 cur[4];
+#pragma unroll
+    for (int f = 0; f < PF; f++)
+      if (f == slot) { cur[0] = pv[f][0]; cur[1] = pv[f][1]; cur[2] = pv[f][2]; cur[3] = pv[f][3]; }
     const float bj = q == 0 ? a.aggb[(size_t)chunk * 64 + i] : 0.f;
-    if (j + 1 < a.cps) loadP(chunk + 1);
+    if (j + PF < a.cps) {
+#pragma unroll
+      for (int f = 0; f < PF; f++)
+        if (f == slot) loadP(f, chunk + PF);
+    }
     float s = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; m++) {
@@ -444,29 +455,36 @@ __global__ __launch_bounds__(64) void k_d64_dh0(const D64AdjArgs a) {
   a.dh0[(size_t)b * 64 + i] = acc;
 }
 
-// column sums in fp64, fixed order (one block per column)
-__global__ __launch_bounds__(256) void k_colsum(const float *X, int rows, int cols, float *out) {
-  __shared__ double s[256];
-  const int c = blockIdx.x;
-  double acc = 0.0;
-  for (int r = threadIdx.x; r < rows; r += 256) acc += (double)X[(size_t)r * cols + c];
-  s[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
-    __syncthreads();
+// Column sums in fp64 in a fixed order: block q sums rows [q*R, (q+1)*R) of
+// every column (coalesced across threads), then one pass sums the blocks.
+constexpr int CS_BLOCKS = 512;
+__global__ __launch_bounds__(256) void k_colsum_part(const float *X, int rows, int cols, double *part) {
+  const int R = (rows + CS_BLOCKS - 1) / CS_BLOCKS;
+  const int r0 = blockIdx.x * R, r1 = min(rows, r0 + R);
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    double acc = 0.0;
+    for (int r = r0; r < r1; r++) acc += (double)X[(size_t)r * cols + c];
+    part[(size_t)blockIdx.x * cols + c] = acc;
   }
-  if (threadIdx.x == 0) out[c] = (float)s[0];
+}
+__global__ __launch_bounds__(256) void k_colsum_final(const double *part, int cols, float *out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  double acc = 0.0;
+  for (int q = 0; q < CS_BLOCKS; q++) acc += part[(size_t)q * cols + c];
+  out[c] = (float)acc;
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_d64_sweep(D64Args &a, hipStream_t s) {
+hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s) {
   a.adjoint = 0;
   const int rows = a.B * a.T;
-  hipLaunchKernelGGL(k_d64_gates<false>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_d64_scanA<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_d64_scanC<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  if (part == 0) hipLaunchKernelGGL(k_d64_gates<false>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
+  if (part == 1) hipLaunchKernelGGL(k_d64_scanA<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  if (part == 2) {
+    hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_d64_scanC<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -487,8 +505,9 @@ hipError_t launch_d64_adjoint_epilogue(const D64AdjArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float *X, int rows, int cols, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_colsum, dim3(cols), dim3(256), 0, s, X, rows, cols, out);
+hipError_t launch_colsum(const float *X, int rows, int cols, float *out, double *part, hipStream_t s) {
+  hipLaunchKernelGGL(k_colsum_part, dim3(CS_BLOCKS), dim3(256), 0, s, X, rows, cols, part);
+  hipLaunchKernelGGL(k_colsum_final, dim3((cols + 255) / 256), dim3(256), 0, s, part, cols, out);
   return hipGetLastError();
 }
 

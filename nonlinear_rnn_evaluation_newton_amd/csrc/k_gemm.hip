@@ -199,11 +199,13 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// splits chosen so that the grid covers the device at least once
+// Split K until the grid covers the device a few times over (long-K
+// products such as dW = dU^T x have few output tiles), keeping at least
+// 8 K tiles per split.
 int gemm_splits(int M, int N, int K) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   int s = 1;
-  while (tiles * s < 512 && K / (s * 2) >= 4 * GBK && s < 16) s *= 2;
+  while (tiles * s < 1024 && K / (s * 2) >= 8 * GBK && s < 512) s *= 2;
   return s;
 }
 

@@ -48,7 +48,7 @@ struct Plan {
   size_t off_U = 0, off_dU = 0, off_gws = 0;
   // dense n = 64 path
   int cps = 0, nchunks = 0;
-  size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0;
+  size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0, off_csum = 0;
   size_t zero_bytes = 0;     // bytes cleared at the start of each call
   size_t solve_bytes = 0, adjoint_bytes = 0;
 };
@@ -114,6 +114,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_dU = o; o = align256(o + rows * 192 * 4);
     pl->off_dA = o; o = align256(o + rows * 192 * 4);
     pl->off_hprev = o; o = align256(o + rows * 64 * 4);
+    pl->off_csum = o; o = align256(o + (size_t)512 * 192 * 8);
     const int K = (int)(rows < 2147483647ULL ? rows : 2147483647ULL);
     const int s1 = gemm_splits(192, p->d, K), s2 = gemm_splits(192, 64, K);
     const size_t gw = (size_t)(s1 > 1 ? s1 * 192 * p->d : 0) > (size_t)(s2 > 1 ? s2 * 192 * 64 : 0)
@@ -191,7 +192,7 @@ SolveState *host_state() {
 // Event timing of the main kernels (pararnn_trace).  Categories: Newton
 // sweeps (only launches that did work are counted), the adjoint's scan
 // kernel, the input projection, the adjoint's products and reductions.
-enum { TR_SWEEP = 0, TR_ADJ = 1, TR_PROJ = 2, TR_AGEMM = 3, TR_N = 4 };
+enum { TR_SWEEP = 0, TR_ADJ = 1, TR_PROJ = 2, TR_AGEMM = 3, TR_DPROD = 4, TR_N = 5 };
 struct Trace {
   bool on = false;
   bool made = false;
@@ -199,12 +200,15 @@ struct Trace {
   long long cnt[TR_N] = {};
   static constexpr int CAP = 256;
   hipEvent_t sw[2 * CAP] = {};        // per sweep of the current solve
+  hipEvent_t swa[2 * CAP] = {};       // per sweep: the dense path's chunk-product kernel
   hipEvent_t ev[TR_N][2 * CAP] = {};  // rings of the other categories
   int pending[TR_N] = {};
   hipError_t make() {
     if (made) return hipSuccess;
     for (int i = 0; i < 2 * CAP; i++) {
       hipError_t e = hipEventCreate(&sw[i]);
+      if (e != hipSuccess) return e;
+      e = hipEventCreate(&swa[i]);
       if (e != hipSuccess) return e;
       for (int c = 1; c < TR_N; c++) {
         e = hipEventCreate(&ev[c][i]);
@@ -426,7 +430,11 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
         HIPCHK(launch_time_sweep(kc, pl.N, a, s));
       } else if (pl.path == PATH_D64) {
         da.k = kk;
-        HIPCHK(launch_d64_sweep(da, s));
+        HIPCHK(launch_d64_sweep_part(da, 0, s));
+        if (ev) HIPCHK(hipEventRecord(tr.swa[2 * (kk - 1)], s));
+        HIPCHK(launch_d64_sweep_part(da, 1, s));
+        if (ev) HIPCHK(hipEventRecord(tr.swa[2 * (kk - 1) + 1], s));
+        HIPCHK(launch_d64_sweep_part(da, 2, s));
       } else {
         ca.k = kk;
         HIPCHK(launch_chan_sweep(kc, p->dtype == PR_BF16, ca, s));
@@ -459,6 +467,11 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (kk - 1)], tr.sw[2 * (kk - 1) + 1]));
       tr.ms[TR_SWEEP] += ms;
       tr.cnt[TR_SWEEP]++;
+      if (pl.path == PATH_D64) {
+        HIPCHK(hipEventElapsedTime(&ms, tr.swa[2 * (kk - 1)], tr.swa[2 * (kk - 1) + 1]));
+        tr.ms[TR_DPROD] += ms;
+        tr.cnt[TR_DPROD]++;
+      }
     }
   }
   if (iters) *iters = out_iters;
@@ -551,8 +564,9 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     ea.B = p->B; ea.T = p->T;
     HIPCHK(launch_d64_adjoint_epilogue(ea, s));
     const int rows = p->B * p->T;
-    if (dW && dW->b_x) HIPCHK(launch_colsum(ea.dU, rows, 192, dW->b_x, s));
-    if (dW && dW->b_h) HIPCHK(launch_colsum(ea.dA, rows, 192, dW->b_h, s));
+    double *csp = (double *)(ws + pl.off_csum);
+    if (dW && dW->b_x) HIPCHK(launch_colsum(ea.dU, rows, 192, dW->b_x, csp, s));
+    if (dW && dW->b_h) HIPCHK(launch_colsum(ea.dA, rows, 192, dW->b_h, csp, s));
     if (dx) {  // dx = dU W_x
       GemmArgs gm{};
       gm.A = ea.dU; gm.B = w->W_x; gm.C = dx;
