@@ -2,7 +2,7 @@
 // GRU and the linear cell, with their Jacobians and vector-Jacobian products.
 // Weights are read from LDS, padded with zeros so padded state entries stay 0.
 //
-// Cell equations follow PyTorch's RNN and GRU (the familiar interface the
+// Cell equations follow PyTorch's RNN and GRU (the standard interface the
 // Para-Seq README keeps): GRU gate order r|z|n, b_hn inside r*(.), and
 // h' = (1 - z) c + z h.  The Jacobian is the one Newton linearises with
 // ("Parallelizing non-linear sequential models over the sequence length",

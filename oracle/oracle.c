@@ -11,7 +11,7 @@
  *  - orc_rollout: the plain sequential evaluation h_t = f(h_{t-1}, x_t) that
  *    DEER is measured against ("Parallelizing non-linear sequential models
  *    over the sequence length", Key results and Measured effects: sequential
- *    GRU evaluation; ParaRNN abstract: "naive sequential application").
+ *    GRU evaluation; ParaRNN abstract: the plain one-step-at-a-time baseline).
  *  - orc_deer: Newton on the residual system F(h)_t = h_t - f(h_{t-1}, x_t) = 0
  *    (ParaRNN abstract: the recurrences cast as one system of equations solved
  *    with Newton's iterations; Gonzalez et al. abstract: the states as the
@@ -26,14 +26,14 @@
  *    backpropagation through time).  At a converged trajectory this equals
  *    the single reverse linear solve lambda_t = g_t + J_{t+1}^T lambda_{t+1}
  *    that the DEER summary describes (Surprising findings: the backward pass
- *    needs one inverse linear operator evaluation; Para-Seq README, Main
+ *    costs a single extra linear solve; Para-Seq README, Main
  *    features: reverse adjoint scans).
  *  - orc_affine_solve: y_t = A_t y_{t-1} + b_t (or the reverse-time recurrence)
  *    by its definition, for the dense, diagonal and 2x2-block operators that
  *    the Para-Seq README lists (Main features: src.utils scans).
  *
  * The pages never print the cell equations.  The cells follow the PyTorch
- * conventions that Para-Seq keeps (README intro: the familiar RNN/GRU/LSTM
+ * conventions that Para-Seq keeps (README intro: the standard RNN/GRU/LSTM
  * interface); the CIFG/peephole ParaLSTM (README, Main features) is read as:
  *   f = sigm(U_f + w_f h + p_f c + b_f),  g = tanh(U_g + w_g h + b_g),
  *   c' = f c + (1-f) g,  o = sigm(U_o + w_o h + p_o c' + b_o),  h' = o tanh(c').
