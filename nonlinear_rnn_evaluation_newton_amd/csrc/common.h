@@ -22,7 +22,8 @@ struct SolveState {
   unsigned int stopped;      // sticky: a sweep saw the stop rule hold
   int iters;                 // sweep count at the stop
   int status;                // PR_OK / PR_NOT_CONVERGED / PR_NONFINITE
-  unsigned int pad[13];
+  unsigned int fault;        // a look-back wait exceeded PR_SPIN_LIMIT (grid not co-resident)
+  unsigned int pad[12];
   unsigned int dslot[4][PR_DSHARDS];  // shards of delta_k for sweep k % 4
   unsigned int hist[PR_HIST];         // delta_k (slot k % PR_HIST), finalised by sweep k + 1 or the host
 };
@@ -54,6 +55,14 @@ __device__ inline unsigned ld_agent(const unsigned *p) {
 }
 __device__ inline void st_agent(unsigned *p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Bound on the retries of a look-back wait.  A healthy wait needs a few
+// hundred at most; past the bound the waiter records a fault in the solve
+// state and gives up (its results are then undefined), so a grid that is not
+// co-resident ends with an error instead of hanging the device.
+constexpr int PR_SPIN_LIMIT = 1 << 16;
+__device__ inline void spin_fault(SolveState *st) {
+  if (st) st_agent(&st->fault, 1u);
 }
 __device__ inline unsigned long long ld_agent64(const unsigned long long *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

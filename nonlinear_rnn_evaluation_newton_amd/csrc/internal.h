@@ -31,6 +31,7 @@ struct TimeArgs {
   float *bnd;                      // [2][ntiles][N] boundary states
   int tiles_per_seq, ntiles, vec_ok;
   int nparts;  // adjoint: blocks that wrote weight partials (set by the launcher)
+  const float *coef;  // scalar-state sweep: cell coefficients folded from the weights
 };
 
 int time_tile(int N);               // elements per tile for padded width N
@@ -38,6 +39,11 @@ int time_padded_n(int n);           // N for a given n (0 if unsupported)
 int time_part_count(int cell, int N);  // floats per tile of gradient partials
 hipError_t launch_time_sweep(int cell, int N, const TimeArgs &a, hipStream_t s);
 hipError_t launch_time_adjoint(int cell, int N, TimeArgs &a, hipStream_t s);
+// Scalar-state sweep (n = d = 1, T % 4 == 0, x and h 16-byte aligned); same
+// tile geometry as the generic sweep at N = 1.
+int scalar_tile();
+hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s);
+hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s);
 hipError_t launch_time_reduce(int cell, int N, const TimeArgs &a, const float *part, float *dWx, float *dbx,
                               float *dWh, float *dbh, hipStream_t s);
 

@@ -127,7 +127,8 @@ __device__ inline void chan_combine(const Op<SW> (&agg)[CPL], Op<SW> (&pre)[CPL]
 // reads W predecessors; carry[c] receives the state after tile j - 1.
 template <int SW, int CPL, int W>
 __device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, bool active,
-                                     unsigned long long *agg, unsigned long long *incl, float (&carry)[CPL][SW]) {
+                                     unsigned long long *agg, unsigned long long *incl, float (&carry)[CPL][SW],
+                                     SolveState *st) {
   constexpr int AW = SW * SW + SW, CH = 64 * CPL;
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -147,7 +148,7 @@ __device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, boo
     Op<SW> acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; c++) acc[c] = op_identity<SW>();
-    int p0 = j - 1;
+    int p0 = j - 1, spins = 0;
     bool done = false;
     while (!done) {
       unsigned long long wi[W][CPL][SW], wa[W][CPL][AW];
@@ -197,7 +198,13 @@ __device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, boo
         }
       }
       if (!done) {
-        if (q < W) __builtin_amdgcn_s_sleep(1);
+        if (q < W) {
+          if (++spins > PR_SPIN_LIMIT) {  // carry stays 0; the fault is reported by the host
+            spin_fault(st);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
         p0 -= q;
       }
     }
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
     if (wid == 0) {
       float carry[CPL][SW];
       chan_lookback<SW, CPL, 4>(tot, j, k, active, a.agg + (size_t)stripe * a.tps * CH * AW,
-                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry, a.st);
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(256) void k_chan_scan(const ChanArgs a) {
     if (wid == 0) {
       float carry[CPL][SW];
       chan_lookback<SW, CPL, 4>(tot, j, 1, active, a.agg + (size_t)stripe * a.tps * CH * AW,
-                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry, a.st);
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll
@@ -586,7 +593,7 @@ __global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
     if (wid == 0) {
       float carry[CPL][SW];
       chan_lookback<SW, CPL, 4>(tot, j, 1, active, a.agg + (size_t)stripe * a.tps * CH * AW,
-                                a.incl + (size_t)stripe * a.tps * CH * SW, carry);
+                                a.incl + (size_t)stripe * a.tps * CH * SW, carry, a.st);
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll

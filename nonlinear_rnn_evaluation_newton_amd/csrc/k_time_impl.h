@@ -131,7 +131,7 @@ __device__ inline void tile_scan(const Op<N> (&ops)[Q], Op<N> (&ex)[Q], Op<N> &t
 // inclusive prefix.  carry receives the state after tile j - 1.
 template <int N>
 __device__ inline void lookback(const Op<N> &tot, int j, int k, unsigned long long *agg, unsigned long long *incl,
-                                float *carry) {
+                                float *carry, SolveState *st) {
   constexpr int AW = N * N + N;
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -144,7 +144,7 @@ __device__ inline void lookback(const Op<N> &tot, int j, int k, unsigned long lo
       for (int i = 0; i < N; i++) desc_put(agg + (size_t)j * AW + N * N + i, tag_agg(k), tot.b[i]);
     }
     Op<N> acc = op_identity<N>();
-    int wend = j - 1;
+    int wend = j - 1, spins = 0;
     while (true) {
       const int p = wend - 63 + lane;
       unsigned long long wi[N], wa[AW];
@@ -168,6 +168,11 @@ __device__ inline void lookback(const Op<N> &tot, int j, int k, unsigned long lo
       const int m = bi ? 63 - __clzll((long long)bi) : -1;  // nearest tile with an inclusive prefix
       const bool ok = !(lane > m && p >= 0) || ha;
       if (!__all(ok)) {
+        if (++spins > PR_SPIN_LIMIT) {
+          if (lane == 0) spin_fault(st);
+          acc = op_identity<N>();
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
         continue;
       }
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(256) void k_time_sweep(const TimeArgs a) {
     if (wid == 0) {
       float c[N];
       lookback<N>(tot, j, k, a.agg + (size_t)b * a.tiles_per_seq * (N * N + N),
-                  a.incl + (size_t)b * a.tiles_per_seq * N, c);
+                  a.incl + (size_t)b * a.tiles_per_seq * N, c, a.st);
       if (lane == 0) {
 #pragma unroll
         for (int i = 0; i < N; i++) s_carry[i] = c[i];
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256) void k_time_adjoint(const TimeArgs a) {
     if (wid == 0) {
       float c[N];
       lookback<N>(tot, j, 1, a.agg + (size_t)b * a.tiles_per_seq * (N * N + N),
-                  a.incl + (size_t)b * a.tiles_per_seq * N, c);
+                  a.incl + (size_t)b * a.tiles_per_seq * N, c, a.st);
       if (lane == 0) {
 #pragma unroll
         for (int i = 0; i < N; i++) s_carry[i] = c[i];
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(256) void k_time_scan(const ScanArgs a) {
     if (wid == 0) {
       float c[N];
       lookback<N>(tot, j, 1, a.agg + (size_t)b * a.tiles_per_seq * (N * N + N),
-                  a.incl + (size_t)b * a.tiles_per_seq * N, c);
+                  a.incl + (size_t)b * a.tiles_per_seq * N, c, a.st);
       if (lane == 0) {
 #pragma unroll
         for (int i = 0; i < N; i++) s_carry[i] = c[i];
@@ -752,19 +757,19 @@ inline int device_cu_count() {
   return cus;
 }
 
-template <auto KERN>
+template <auto KERN, int THREADS = 256>
 int resident_blocks() {
   static int cached = 0;  // one per kernel instantiation
   if (cached) return cached;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, 256, 0) != hipSuccess || per_cu < 1) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, THREADS, 0) != hipSuccess || per_cu < 1) return 0;
   cached = per_cu * device_cu_count();
   return cached;
 }
 
-template <auto KERN>
+template <auto KERN, int THREADS = 256>
 int persistent_grid(int ntiles) {
-  const int r = resident_blocks<KERN>();
+  const int r = resident_blocks<KERN, THREADS>();
   if (r <= 0) return 0;
   return ntiles < r ? ntiles : r;
 }

@@ -42,10 +42,12 @@ struct Plan {
   int path = PATH_NONE;
   int G = 1, S = 1, N = 1, SW = 1;
   int tile = 0, tps = 0, ntiles = 0;
+  // scalar-state sweep (n = d = 1, T % 4 == 0): its own tile size
+  int scalar_ok = 0, tps_s = 0, ntiles_s = 0;
   // channel path: stripes (sequence x channel group), tiles of sweep / adjoint
   int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
-  size_t off_U = 0, off_dU = 0, off_gws = 0;
+  size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
   // dense n = 64 path
   int cps = 0, nchunks = 0;
   size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0, off_csum = 0;
@@ -83,12 +85,24 @@ int make_plan(const pr_problem *p, Plan *pl) {
     if ((long long)pl->tps * p->B > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
     pl->ntiles = pl->tps * p->B;
     const int N = pl->N;
+    int nt = pl->ntiles;  // descriptor and boundary slots for either sweep
+    // (buffer resources of the scalar sweep address rows, descriptors and
+    // boundary states with 31-bit byte offsets)
+    if (p->n == 1 && p->d == 1 && p->T % 4 == 0 && (long long)p->T * 4 < (1LL << 31) &&
+        (long long)p->B * ((p->T + scalar_tile() - 1) / scalar_tile()) * 16 < (1LL << 31)) {
+      pl->scalar_ok = 1;
+      pl->tps_s = (p->T + scalar_tile() - 1) / scalar_tile();
+      if ((long long)pl->tps_s * p->B > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
+      pl->ntiles_s = pl->tps_s * p->B;
+      nt = nt > pl->ntiles_s ? nt : pl->ntiles_s;
+    }
     size_t o = 0;
     pl->off_state = o; o = align256(o + sizeof(SolveState));
-    pl->off_agg = o; o = align256(o + (size_t)pl->ntiles * (N * N + N) * 8);
-    pl->off_incl = o; o = align256(o + (size_t)pl->ntiles * N * 8);
+    pl->off_agg = o; o = align256(o + (size_t)nt * (N * N + N) * 8);
+    pl->off_incl = o; o = align256(o + (size_t)nt * N * 8);
     pl->zero_bytes = o;
-    pl->off_bnd = o; o = align256(o + (size_t)2 * pl->ntiles * N * 4);
+    pl->off_bnd = o; o = align256(o + (size_t)2 * nt * N * 4);
+    pl->off_coef = o; o = align256(o + 64 * 4);
     pl->solve_bytes = o;
     pl->off_part = o; o = align256(o + (size_t)pl->ntiles * time_part_count(p->cell, N) * 4);
     pl->adjoint_bytes = o;
@@ -391,6 +405,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     a.tiles_per_seq = pl.tps;
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0);
+    a.coef = (const float *)(ws + pl.off_coef);
   } else {
     ca.U = ws + pl.off_U;
     ca.h = h;
@@ -413,6 +428,13 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     tr.end(TR_PROJ, ti, s);
   }
   const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : kcell(p->cell);
+  // n = d = 1 with vector-friendly sizes takes the scalar-state sweep
+  const bool scalar = pl.path == PATH_TIME && pl.scalar_ok && a.vec_ok == 3 && !getenv("PARARNN_NO_SCALAR");
+  if (scalar) {
+    a.tiles_per_seq = pl.tps_s;
+    a.ntiles = pl.ntiles_s;
+    HIPCHK(launch_scalar_coef(a, kc, (float *)(ws + pl.off_coef), s));
+  }
 
   int first, next;
   poll_schedule(&first, &next);
@@ -426,7 +448,9 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       a.k = kk;
       const bool ev = tr.on && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      if (pl.path == PATH_TIME) {
+      if (scalar) {
+        HIPCHK(launch_scalar_sweep(kc, a, s));
+      } else if (pl.path == PATH_TIME) {
         HIPCHK(launch_time_sweep(kc, pl.N, a, s));
       } else if (pl.path == PATH_D64) {
         da.k = kk;
@@ -443,6 +467,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     }
     HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
     HIPCHK(hipStreamSynchronize(s));
+    if (hs->fault) return fail(PR_EHIP, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
     if (hs->stopped) {
       out_iters = hs->iters;
       out_status = hs->status;

@@ -66,6 +66,24 @@ def test_scalar_gru_lengths_and_ragged_tiles(T):
     check_solve(p, tol=1e-6, max_iters=T)
 
 
+@pytest.mark.parametrize("cell", [sy.CELL_GRU, sy.CELL_TANH_RNN, sy.CELL_LINEAR])
+@pytest.mark.parametrize("T", [4, 8, 1020, 4096, 4100, 12292, 40000])
+def test_scalar_state_kernel(cell, T):
+    """n = d = 1 with T % 4 == 0: the scalar-state sweep (coefficient table,
+    four steps per lane, full and partial tiles, h0 and biases)."""
+    p = sy.custom_problem(cell, B=3, T=T, d=1, n=1, seed=7 * T + cell, w_scale=0.5 if cell == sy.CELL_LINEAR else 1.0,
+                          h0=True)
+    if cell == sy.CELL_LINEAR:  # keep the linear recurrence contracting
+        p["W_h"] = np.clip(p["W_h"], -0.9, 0.9)
+    check_solve(p, tol=1e-4 if cell == sy.CELL_LINEAR else 1e-6, max_iters=T)
+
+
+def test_scalar_state_kernel_without_biases_and_fixed_sweeps():
+    p = sy.custom_problem(sy.CELL_GRU, B=5, T=8192, d=1, n=1, seed=3, bias=False)
+    for it in (1, 2, 3):
+        check_solve(p, tol=0.0, max_iters=it)
+
+
 @pytest.mark.parametrize("cell,n,d", [(sy.CELL_TANH_RNN, 3, 5), (sy.CELL_TANH_RNN, 8, 2), (sy.CELL_GRU, 2, 3),
                                       (sy.CELL_GRU, 4, 8), (sy.CELL_GRU, 7, 1), (sy.CELL_LINEAR, 4, 2)])
 @pytest.mark.parametrize("T", [77, 1000, 2049])
