@@ -22,7 +22,10 @@
 
 namespace pr {
 
-constexpr int SC_V = 4, SC_Q = 2;
+#ifndef SC_QDEF
+#define SC_QDEF 2
+#endif
+constexpr int SC_V = 4, SC_Q = SC_QDEF;
 constexpr int SC_CW = 7;                       // compute wavefronts per block
 constexpr int SC_WSTEPS = SC_Q * 64 * SC_V;    // steps per compute wavefront
 constexpr int SC_TILE = SC_CW * SC_WSTEPS;     // steps per tile
@@ -209,9 +212,21 @@ struct ScTile {
 struct ScShared {
   float wA[2][SC_CW], wb[2][SC_CW];
   float carry[2];
+  unsigned done[2];  // compute wavefronts finished with the tile in each buffer
   int stop;
   unsigned dmax[SC_CW];
 };
+
+// Descriptor resources of one sequence.
+struct ScDesc {
+  Rsrc agg, incl;
+};
+__device__ inline ScDesc sc_desc(const TimeArgs &a, int b) {
+  ScDesc d;
+  d.agg = sc_rsrc(a.agg + (size_t)b * a.tiles_per_seq * 2, (unsigned)a.tiles_per_seq * 16u);
+  d.incl = sc_rsrc(a.incl + (size_t)b * a.tiles_per_seq, (unsigned)a.tiles_per_seq * 8u);
+  return d;
+}
 
 // Cell, Jacobian and residual of every step of tile `id`, lane-serial
 // composition of each lane's steps, wavefront scans, and the wavefront totals
@@ -262,6 +277,33 @@ __device__ inline void sc_compute(const TimeArgs &a, const float *C, int id, con
     sh.wA[buf][wid] = wA;
     sh.wb[buf][wid] = wb;
   }
+  // The last compute wavefront to finish publishes the tile aggregate at once
+  // (tile 0 of a sequence only ever publishes its inclusive prefix).  Every
+  // compute wavefront executes the store; the others' offsets fall outside
+  // the resource.  LDS operations of a wavefront complete in order, so the
+  // totals written above are visible before its count is.
+  unsigned prev = 0;
+  // the totals reach LDS before the count (wait on this wavefront's LDS
+  // operations; the clobber keeps the compiler from moving memory accesses
+  // across)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) prev = atomicAdd(&sh.done[buf], 1u);
+  const bool last = __builtin_amdgcn_readfirstlane(prev) == SC_CW - 1;
+  asm volatile("" ::: "memory");
+  float tA = 1.f, tb = 0.f;
+  if (last) {
+#pragma unroll
+    for (int w = 0; w < SC_CW; w++) {
+      tb = fmaf(sh.wA[buf][w], tb, sh.wb[buf][w]);
+      tA *= sh.wA[buf][w];
+    }
+    if (lane == 0) sh.done[buf] = 0;  // reused two tiles on, after two barriers
+  }
+  const ScDesc d = sc_desc(a, id % B);
+  u32x4 v;
+  v.x = __float_as_uint(tA); v.y = tag_agg(a.k); v.z = __float_as_uint(tb); v.w = tag_agg(a.k);
+  __builtin_amdgcn_raw_buffer_store_b128(v, d.agg, (last && lane == 0 && j > 0) ? (unsigned)j * 16u : SC_OOB, 0,
+                                         SC_SC1);
 }
 
 // Look-back descriptors of the 64 tiles before tile wend + 1 (lane l holds
@@ -306,15 +348,14 @@ __device__ inline int sc_window(const ScPoll &P, int wend, int k, float &accA, f
   return m >= 0 ? 2 : 1;
 }
 
-// dh after tile j - 1 of one sequence (descriptor bases offset to that
-// sequence) from the decoupled look-back, starting from descriptors polled
-// earlier (window ending at j - 1).  Every wavefront of the block runs it
-// with the same result.  The first window is evaluated outside the retry
-// loop so that its wait covers only those early polls, not the loads issued
-// after them.
-__device__ inline float sc_resolve(Rsrc ragg, Rsrc rincl, int j, int k, ScPoll P, SolveState *st) {
-  float accA = 1.f, accb = 0.f;
-  int wend = j - 1, spins = 0;
+// dh after the window ending at tile wend of one sequence (descriptor
+// resources of that sequence), composing after acc, from descriptors polled
+// earlier for that window: the decoupled look-back, re-polling while a
+// needed aggregate is not yet published and stepping back while no window
+// holds an inclusive prefix.
+__device__ inline float sc_resolve_from(Rsrc ragg, Rsrc rincl, int wend, int k, ScPoll P, float accA, float accb,
+                                        SolveState *st) {
+  int spins = 0;
   int r = sc_window(P, wend, k, accA, accb);
   while (r != 2) {
     if (r == 1) {
@@ -330,6 +371,21 @@ __device__ inline float sc_resolve(Rsrc ragg, Rsrc rincl, int j, int k, ScPoll P
     r = sc_window(P, wend, k, accA, accb);
   }
   return accb;  // the composition ends in a constant map
+}
+
+// As sc_resolve, with a second, later poll of the first window to fall back on
+// before re-polling.
+__device__ inline float sc_resolve2(Rsrc ragg, Rsrc rincl, int j, int k, const ScPoll &P0, const ScPoll &P1,
+                                    SolveState *st) {
+  float accA = 1.f, accb = 0.f;
+  const int r = sc_window(P0, j - 1, k, accA, accb);
+  if (r == 2) return accb;
+  if (r == 1) {  // the window holds no inclusive prefix yet but every aggregate: go further back
+    ScPoll P;
+    sc_poll(ragg, rincl, j - 65, P);
+    return sc_resolve_from(ragg, rincl, j - 65, k, P, accA, accb, st);
+  }
+  return sc_resolve_from(ragg, rincl, j - 1, k, P1, 1.f, 0.f, st);
 }
 
 // Composition of wavefronts [0, wid) (pre) and of all four (tot) of a
@@ -354,21 +410,9 @@ __device__ inline ScTot sc_tot(const ScShared &sh, int buf, int wid) {
   return r;
 }
 
-// Descriptor resources of one sequence.
-struct ScDesc {
-  Rsrc agg, incl;
-};
-__device__ inline ScDesc sc_desc(const TimeArgs &a, int b) {
-  ScDesc d;
-  d.agg = sc_rsrc(a.agg + (size_t)b * a.tiles_per_seq * 2, (unsigned)a.tiles_per_seq * 16u);
-  d.incl = sc_rsrc(a.incl + (size_t)b * a.tiles_per_seq, (unsigned)a.tiles_per_seq * 8u);
-  return d;
-}
-
 // Look-back wavefront, for computed tile `id` whose wavefront totals are in
-// LDS buffer `buf`: publish its aggregate, resolve its carry from the
-// predecessors' descriptors, publish its inclusive prefix, leave the carry in
-// LDS.  This wavefront issues no other memory operations, so its waits on
+// LDS buffer `buf`: resolve its carry from the predecessors' descriptors,
+// publish its inclusive prefix, leave the carry in LDS.  This wavefront issues no other memory operations, so its waits on
 // the descriptors never queue behind the bulk loads and stores of the
 // compute wavefronts.
 __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh, int buf) {
@@ -376,13 +420,15 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
   const ScTot tt = sc_tot(sh, buf, SC_CW);
   const ScDesc d = sc_desc(a, id % a.B);
   float carry = 0.f;
-  if (j > 0) {  // tile 0 of a sequence only ever publishes its inclusive prefix
-    u32x4 v;
-    v.x = __float_as_uint(tt.totA); v.y = tag_agg(k); v.z = __float_as_uint(tt.totb); v.w = tag_agg(k);
-    __builtin_amdgcn_raw_buffer_store_b128(v, d.agg, (threadIdx.x & 63) == 0 ? (unsigned)j * 16u : SC_OOB, 0, SC_SC1);
-    ScPoll P;
-    sc_poll(d.agg, d.incl, j - 1, P);
-    carry = sc_resolve(d.agg, d.incl, j, k, P, a.st);
+  if (j > 0) {
+    // two polls of the same window a few hundred cycles apart: predecessors
+    // of this stage publish about when this wavefront starts, and a second
+    // poll already in flight costs less than a retry after the first fails
+    ScPoll P0, P1;
+    sc_poll(d.agg, d.incl, j - 1, P0);
+    __builtin_amdgcn_s_sleep(8);
+    sc_poll(d.agg, d.incl, j - 1, P1);
+    carry = sc_resolve2(d.agg, d.incl, j, k, P0, P1, a.st);
   }
   u32x2 w;
   w.x = __float_as_uint(fmaf(tt.totA, carry, tt.totb));
@@ -462,6 +508,10 @@ __global__ __launch_bounds__(SC_THREADS) void k_scalar_sweep(const TimeArgs a) {
   const int G = gridDim.x, nt = a.ntiles;
   unsigned dmax = 0;
   if (wid == SC_LB) {
+    if (lane == 0) {
+      sh.done[0] = 0;
+      sh.done[1] = 0;
+    }
     if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
     __syncthreads();  // end of stage 0
     for (int id = blockIdx.x; id < nt; id += G) {
