@@ -41,9 +41,11 @@ hipError_t launch_time_sweep(int cell, int N, const TimeArgs &a, hipStream_t s);
 hipError_t launch_time_adjoint(int cell, int N, TimeArgs &a, hipStream_t s);
 // Scalar-state sweep (n = d = 1, T % 4 == 0, x and h 16-byte aligned); same
 // tile geometry as the generic sweep at N = 1.
-int scalar_tile();
+int scalar_tile();      // steps per tile of the scalar sweep
+int scalar_adj_tile();  // steps per tile of the scalar adjoint
 hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s);
 hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s);
+hipError_t launch_scalar_adjoint(int cell, TimeArgs &a, hipStream_t s);  // sets a.nparts
 hipError_t launch_time_reduce(int cell, int N, const TimeArgs &a, const float *part, float *dWx, float *dbx,
                               float *dWh, float *dbh, hipStream_t s);
 

@@ -1,57 +1,54 @@
-// Scalar-state Newton sweep (n = 1, d = 1), the shape of DEER's headline
+// Scalar-state kernels (n = 1, d = 1), the shape of DEER's headline
 // measurement ("Parallelizing non-linear sequential models over the sequence
-// length", Experiments: GRU with batch 16 and 2^20 steps).  Same algorithm
-// as the generic time-parallel sweep -- cell, Jacobian and residual at every
-// step, affine scan of (J_t, r_t), in-place update, convergence measure --
-// written so that a step costs about forty VALU instructions and the memory
-// system never idles:
-//  * the cell's weights are folded once per solve into a coefficient table
-//    (exp2 scale factors included) read through the scalar cache;
-//  * each lane owns 4 consecutive steps per group (16-byte loads and
-//    stores), 2 groups per wavefront, 7 compute wavefronts per tile;
-//  * two register sets alternate between tiles: the loads of the block's
-//    next tile are issued before the current tile is computed, so HBM
-//    streams while the VALU works and while the look-back waits;
-//  * the wavefront scan runs on DPP-fused multiply/FMA instructions (lanes
-//    whose source falls outside the pattern keep their value, which is the
-//    identity of the composition);
-//  * a lane's entering state comes from its neighbour's exit state by one
-//    DPP shift in the update phase;
-//  * full tiles are compiled without per-step bounds selects.
+// length", Experiments: GRU with batch 16 and 2^20 steps): the Newton sweep
+// (cell, Jacobian and residual at every step, affine scan of (J_t, r_t),
+// in-place update, convergence measure) and the adjoint (reverse scan of
+// (J_{t+1}, g_t) for lambda, then dx, dh0 and the weight gradients), both on
+// one pipeline designed so that HBM streams while the VALU works:
+//  * the cell's weights are folded once per call into a coefficient table
+//    (exp2 scale factors included) held in scalar registers;
+//  * each lane owns 4 consecutive steps per group (16-byte accesses), 2
+//    groups per wavefront, 7 compute wavefronts per tile;
+//  * memory access goes through buffer instructions whose range check
+//    drops out-of-range lanes, so no load or store sits under a branch;
+//  * a block computes tile N while the tile before it waits for its carry:
+//    two register sets alternate, and the loads of the tile after N are in
+//    flight during N;
+//  * an eighth wavefront per block does the decoupled look-back alone, so its
+//    waits never queue behind the bulk loads and stores of the others;
+//  * the wavefront scan runs on DPP-fused multiply/FMA instructions.
 #include "k_time_impl.h"
 
 namespace pr {
 
-#ifndef SC_QDEF
-#define SC_QDEF 2
-#endif
-constexpr int SC_V = 4, SC_Q = SC_QDEF;
+constexpr int SC_V = 4;
 constexpr int SC_CW = 7;                       // compute wavefronts per block
-constexpr int SC_WSTEPS = SC_Q * 64 * SC_V;    // steps per compute wavefront
-constexpr int SC_TILE = SC_CW * SC_WSTEPS;     // steps per tile
 constexpr int SC_THREADS = 64 * (SC_CW + 1);   // + the look-back wavefront (a multiple of 4 wavefronts)
 constexpr int SC_LB = SC_CW;                   // wavefront id of the look-back wavefront
+constexpr int SC_NC = 16;                      // coefficient table size
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Coefficient table (16 floats) derived from the weights once per solve.
+// Coefficient table derived from the weights once per call.
 // GRU (gate rows r, z, n of W_x [3,1], W_h [3,1], b_x [3], b_h [3]):
 //  0..2  -log2e * (w_xr, w_hr, b_xr + b_hr)      -> exp2 argument of sigm(a_r)
 //  3..5  -log2e * (w_xz, w_hz, b_xz + b_hz)
 //  6..7  2 log2e * (w_xn, b_xn)                  -> 2 log2e * U_n
 //  8..9  2 log2e * (w_hn, b_hn)                  -> 2 log2e * q
 //  10    w_hz, 11 w_hn, 12 w_hr / (2 log2e)      -> Jacobian
+//  13..15 w_xr, w_xz, w_xn                       -> dx
 // tanh RNN / linear: 0 w_x, 1 w_h, 2 b_x + b_h.
 __global__ void k_scalar_coef(const float *Wx, const float *bx, const float *Wh, const float *bh, int cell,
                               float *coef) {
   if (threadIdx.x != 0) return;
   auto B = [&](const float *p, int i) { return p ? p[i] : 0.f; };
-  for (int i = 0; i < 16; i++) coef[i] = 0.f;
+  for (int i = 0; i < SC_NC; i++) coef[i] = 0.f;
   if (cell == C_GRU) {
     coef[0] = -LOG2E * Wx[0]; coef[1] = -LOG2E * Wh[0]; coef[2] = -LOG2E * (B(bx, 0) + B(bh, 0));
     coef[3] = -LOG2E * Wx[1]; coef[4] = -LOG2E * Wh[1]; coef[5] = -LOG2E * (B(bx, 1) + B(bh, 1));
     coef[6] = 2.f * LOG2E * Wx[2]; coef[7] = 2.f * LOG2E * B(bx, 2);
     coef[8] = 2.f * LOG2E * Wh[2]; coef[9] = 2.f * LOG2E * B(bh, 2);
     coef[10] = Wh[1]; coef[11] = Wh[2]; coef[12] = Wh[0] / (2.f * LOG2E);
+    coef[13] = Wx[0]; coef[14] = Wx[1]; coef[15] = Wx[2];
   } else {
     coef[0] = Wx[0]; coef[1] = Wh[0]; coef[2] = B(bx, 0) + B(bh, 0);
   }
@@ -82,6 +79,42 @@ __device__ inline void scalar_cell(const float *__restrict__ C, float s, float x
     J = fmaf(-f, f, 1.f) * C[1];
   } else {
     f = fmaf(C[0], x, fmaf(C[1], s, C[2]));
+    J = C[1];
+  }
+}
+
+// Reverse-mode coefficients of the scalar cell at (s, x): the derivative of f
+// with respect to each pre-activation.  GRU: co = (df/da_r, df/da_z, df/da_n,
+// df/dq) with q = w_hn s + b_hn; tanh / linear: co[0] = df/da.  J = df/ds.
+template <int CELL>
+__device__ inline void scalar_vjp(const float *__restrict__ C, float s, float x, float (&co)[4], float &J) {
+  if constexpr (CELL == C_GRU) {
+    const float er = __builtin_amdgcn_exp2f(fmaf(C[0], x, fmaf(C[1], s, C[2])));
+    const float ez = __builtin_amdgcn_exp2f(fmaf(C[3], x, fmaf(C[4], s, C[5])));
+    const float r = __builtin_amdgcn_rcpf(1.f + er);
+    const float z = __builtin_amdgcn_rcpf(1.f + ez);
+    const float q2 = fmaf(C[8], s, C[9]);
+    const float ec = __builtin_amdgcn_exp2f(fmaf(r, q2, fmaf(C[6], x, C[7])));
+    const float c = fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + ec), 1.f);
+    const float sc = s - c;
+    const float zz = fmaf(-z, z, z);
+    const float cc = fmaf(-c, c, 1.f);
+    const float eta = fmaf(-z, cc, cc);               // (1 - z)(1 - c^2)
+    const float rr = fmaf(-r, r, r);
+    co[0] = eta * (q2 * (0.5f / LOG2E)) * rr;          // eta q r (1 - r)
+    co[1] = sc * zz;                                   // (s - c) z (1 - z)
+    co[2] = eta;
+    co[3] = eta * r;
+    J = fmaf(co[3], C[11], fmaf(co[1], C[10], fmaf(co[0], C[12] * (2.f * LOG2E), z)));
+  } else if constexpr (CELL == C_TANH) {
+    const float e = __builtin_amdgcn_exp2f(2.f * LOG2E * fmaf(C[0], x, fmaf(C[1], s, C[2])));
+    const float f = fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+    co[0] = fmaf(-f, f, 1.f);
+    co[1] = co[2] = co[3] = 0.f;
+    J = co[0] * C[1];
+  } else {
+    co[0] = 1.f;
+    co[1] = co[2] = co[3] = 0.f;
     J = C[1];
   }
 }
@@ -128,24 +161,29 @@ __device__ inline float rdlane(float v, int l) { return __int_as_float(__builtin
 __device__ inline float shift_in(float first, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
+// lane l receives v of lane l + 1; lane 63 receives last
+__device__ inline float shift_out(float last, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));
+}
 
-// Memory access of the sweep goes through buffer instructions on per-row
-// buffer resources: the hardware range check returns zero for loads past the
-// end of a row and drops stores past it (and at offset SC_OOB), so every
-// load and store in the tile loop is unconditional.  That keeps the
-// compiler's count of memory operations in flight exact: loads and stores
-// share one in-order counter on this architecture, and a memory instruction
-// under a branch would make later waits conservative, draining recent
-// stores before the prefetched data can be used.
+// Memory access goes through buffer instructions on per-row buffer
+// resources: the hardware range check returns zero for loads outside a
+// resource and drops stores outside it (offset SC_OOB is outside every
+// resource; a null base gets an empty resource), so every load and store in
+// the tile loop is unconditional.  That keeps the compiler's count of memory
+// operations in flight exact: loads and stores share one in-order counter on
+// this architecture, and a memory instruction under a branch would make later
+// waits conservative, draining recent stores before prefetched data can be
+// used.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr unsigned SC_OOB = 0x80000000u;  // offset beyond every resource: load 0, store dropped
-constexpr int SC_SC1 = 16;                // cache policy: device-scope coherent access
+constexpr unsigned SC_OOB = 0x80000000u;
+constexpr int SC_SC1 = 16;  // cache policy: device-scope coherent access
 
 __device__ inline Rsrc sc_rsrc(const void *base, unsigned bytes) {
   // raw buffer, stride 0, 32-bit data format in the fourth descriptor word
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, base ? (int)bytes : 0, 0x00020000);
 }
 __device__ inline float4 ld4(Rsrc r, unsigned off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -162,51 +200,8 @@ __device__ inline void st4(Rsrc r, unsigned off, float a, float b, float c, floa
 __device__ inline void st1(Rsrc r, unsigned off, float a) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
 }
-
-// Raw inputs of one tile for one thread: x and the current iterate h for its
-// groups, and (lane 0's) state before the wavefront's first step.
-struct ScRaw {
-  float4 x[SC_Q], h[SC_Q];
-  float sw;
-};
-
-// Issue the loads of tile `id`.  Needs T % 4 == 0, so a lane's 4 steps are all
-// inside or all outside [0, T).  In the first sweep the iterate is the zero
-// guess and h is not read.
-template <bool FIRST>
-__device__ inline void sc_load(const TimeArgs &a, int id, ScRaw &R) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
-  const int j = id / B, b = id % B;
-  const int t0 = j * SC_TILE + wid * SC_WSTEPS;
-  const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, (unsigned)T * 4u);
-  const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
-#pragma unroll
-  for (int q = 0; q < SC_Q; q++) {
-    const unsigned off = (unsigned)(t0 + (q * 64 + lane) * SC_V) * 4u;
-    R.x[q] = ld4(rx, off);
-    if (!FIRST) R.h[q] = ld4(rh, off);
-  }
-  // the state before step t0: h0 (t0 = 0; zero without h0), the predecessor
-  // tile's last state from the previous sweep (wavefront 0), or h[t0 - 1],
-  // which this block writes only after this load, later in this sweep.  An
-  // empty resource reads zero.
-  const float *sb = a.x;
-  unsigned nb = 0, so = 0;
-  if (t0 == 0) {
-    if (a.h0) { sb = a.h0 + b; nb = 4; }
-  } else if (!FIRST && t0 < T) {
-    if (wid == 0) { sb = a.bnd + (size_t)((k - 1) & 1) * a.ntiles + (b * a.tiles_per_seq + j - 1); nb = 4; }
-    else { sb = a.h + (size_t)b * T; nb = (unsigned)T * 4u; so = (unsigned)(t0 - 1) * 4u; }
-  }
-  R.sw = ld1(sc_rsrc(sb, nb), so);
-}
-
-// A computed tile waiting for its carry: per-step Jacobians, residuals and
-// iterate, per-group inclusive lane scans (iA, ib) and group totals (tA, tb).
-struct ScTile {
-  float J[SC_Q][SC_V], R[SC_Q][SC_V], H[SC_Q][SC_V];
-  float iA[SC_Q], ib[SC_Q], tA[SC_Q], tb[SC_Q];
-};
+// byte offset of step t in a row of floats, or SC_OOB when t is outside [0, T)
+__device__ inline unsigned toff(int t, int T) { return (t >= 0 && t < T) ? (unsigned)t * 4u : SC_OOB; }
 
 // Wavefront totals of the last two computed tiles and their carries.
 struct ScShared {
@@ -215,6 +210,7 @@ struct ScShared {
   unsigned done[2];  // compute wavefronts finished with the tile in each buffer
   int stop;
   unsigned dmax[SC_CW];
+  float red[SC_CW][12];
 };
 
 // Descriptor resources of one sequence.
@@ -228,64 +224,20 @@ __device__ inline ScDesc sc_desc(const TimeArgs &a, int b) {
   return d;
 }
 
-// Cell, Jacobian and residual of every step of tile `id`, lane-serial
-// composition of each lane's steps, wavefront scans, and the wavefront totals
-// into LDS buffer `buf` (read after the next block barrier).
-template <int CELL, bool FIRST, bool FULL>
-__device__ inline void sc_compute(const TimeArgs &a, const float *C, int id, const ScRaw &R, ScTile &Tl,
-                                  ScShared &sh, int buf) {
-  constexpr int V = SC_V, Q = SC_Q;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
-  const int j = id / B;
-  const int t0 = j * SC_TILE + wid * SC_WSTEPS;
-#pragma unroll
-  for (int q = 0; q < Q; q++) {
-    const float xv[V] = {R.x[q].x, R.x[q].y, R.x[q].z, R.x[q].w};
-    float hv[V] = {0.f, 0.f, 0.f, 0.f};
-    if (!FIRST) {
-      hv[0] = R.h[q].x; hv[1] = R.h[q].y; hv[2] = R.h[q].z; hv[3] = R.h[q].w;
-    }
-    float s = shift_in(q == 0 ? R.sw : FIRST ? 0.f : rdlane(R.h[q - 1].w, 63), hv[V - 1]);
-    float A = 1.f, bb = 0.f;
-    const bool in = FULL || t0 + (q * 64 + lane) * V < T;
-#pragma unroll
-    for (int v = 0; v < V; v++) {
-      float f, Jv;
-      scalar_cell<CELL>(C, s, xv[v], f, Jv);
-      float rv = f - hv[v];
-      if (!FULL && !in) { Jv = 1.f; rv = 0.f; }
-      Tl.J[q][v] = Jv;
-      Tl.R[q][v] = rv;
-      Tl.H[q][v] = hv[v];
-      bb = fmaf(Jv, bb, rv);
-      A *= Jv;
-      s = hv[v];
-    }
-    wave_scan_affine1(A, bb);
-    Tl.iA[q] = A;
-    Tl.ib[q] = bb;
-    Tl.tA[q] = rdlane(A, 63);
-    Tl.tb[q] = rdlane(bb, 63);
-  }
-  float wA = Tl.tA[0], wb = Tl.tb[0];
-#pragma unroll
-  for (int q = 1; q < Q; q++) {
-    wb = fmaf(Tl.tA[q], wb, Tl.tb[q]);
-    wA *= Tl.tA[q];
-  }
+// The wavefront's total (wA, wb) into LDS buffer `buf`; the last compute
+// wavefront to get here publishes the tile aggregate at once (tile 0 of a
+// sequence only ever publishes its inclusive prefix).  Every compute
+// wavefront executes the store; the others' offsets fall outside the
+// resource.  LDS operations of a wavefront complete in order, so the totals
+// written here are visible before its count is.
+__device__ inline void sc_publish(const TimeArgs &a, int id, float wA, float wb, ScShared &sh, int buf) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, j = id / a.B;
   if (lane == 0) {
     sh.wA[buf][wid] = wA;
     sh.wb[buf][wid] = wb;
   }
-  // The last compute wavefront to finish publishes the tile aggregate at once
-  // (tile 0 of a sequence only ever publishes its inclusive prefix).  Every
-  // compute wavefront executes the store; the others' offsets fall outside
-  // the resource.  LDS operations of a wavefront complete in order, so the
-  // totals written above are visible before its count is.
   unsigned prev = 0;
-  // the totals reach LDS before the count (wait on this wavefront's LDS
-  // operations; the clobber keeps the compiler from moving memory accesses
-  // across)
+  // the clobber keeps the compiler from moving memory accesses across
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (lane == 0) prev = atomicAdd(&sh.done[buf], 1u);
   const bool last = __builtin_amdgcn_readfirstlane(prev) == SC_CW - 1;
@@ -299,7 +251,7 @@ __device__ inline void sc_compute(const TimeArgs &a, const float *C, int id, con
     }
     if (lane == 0) sh.done[buf] = 0;  // reused two tiles on, after two barriers
   }
-  const ScDesc d = sc_desc(a, id % B);
+  const ScDesc d = sc_desc(a, id % a.B);
   u32x4 v;
   v.x = __float_as_uint(tA); v.y = tag_agg(a.k); v.z = __float_as_uint(tb); v.w = tag_agg(a.k);
   __builtin_amdgcn_raw_buffer_store_b128(v, d.agg, (last && lane == 0 && j > 0) ? (unsigned)j * 16u : SC_OOB, 0,
@@ -388,7 +340,7 @@ __device__ inline float sc_resolve2(Rsrc ragg, Rsrc rincl, int j, int k, const S
   return sc_resolve_from(ragg, rincl, j - 1, k, P1, 1.f, 0.f, st);
 }
 
-// Composition of wavefronts [0, wid) (pre) and of all four (tot) of a
+// Composition of wavefronts [0, wid) (pre) and of all of them (tot) of a
 // computed tile, from its LDS totals.
 struct ScTot {
   float preA, preb, totA, totb;
@@ -412,9 +364,9 @@ __device__ inline ScTot sc_tot(const ScShared &sh, int buf, int wid) {
 
 // Look-back wavefront, for computed tile `id` whose wavefront totals are in
 // LDS buffer `buf`: resolve its carry from the predecessors' descriptors,
-// publish its inclusive prefix, leave the carry in LDS.  This wavefront issues no other memory operations, so its waits on
-// the descriptors never queue behind the bulk loads and stores of the
-// compute wavefronts.
+// publish its inclusive prefix, leave the carry in LDS.  This wavefront
+// issues no other memory operations, so its waits on the descriptors never
+// queue behind the bulk loads and stores of the compute wavefronts.
 __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh, int buf) {
   const int k = a.k, j = id / a.B;
   const ScTot tt = sc_tot(sh, buf, SC_CW);
@@ -437,82 +389,428 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
   if ((threadIdx.x & 63) == 0) sh.carry[buf] = carry;
 }
 
-// Update of tile `id` from its carry: the steps' new iterate, the
-// convergence measure, the stores.
-__device__ inline void sc_apply(const TimeArgs &a, int id, const ScTile &Tl, const ScTot &tt, const ScShared &sh,
-                                int buf, unsigned &dmax) {
-  constexpr int V = SC_V, Q = SC_Q;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
-  const int j = id / B, b = id % B, L = b * a.tiles_per_seq + j;
-  const int t0 = j * SC_TILE + wid * SC_WSTEPS;
-  const bool full = j * SC_TILE + SC_TILE <= T;
-  float c = fmaf(tt.preA, sh.carry[buf], tt.preb);  // dh entering this wavefront's steps
-  const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
-  const Rsrc rb = sc_rsrc(a.bnd, (unsigned)a.ntiles * 8u);
-#pragma unroll
-  for (int q = 0; q < Q; q++) {
-    float dh = shift_in(c, fmaf(Tl.iA[q], c, Tl.ib[q]));
-    float hn[V];
-#pragma unroll
-    for (int v = 0; v < V; v++) {
-      dh = fmaf(Tl.J[q][v], dh, Tl.R[q][v]);
-      hn[v] = Tl.H[q][v] + dh;
-      const unsigned u = __float_as_uint(dh) & 0x7fffffffu;
-      dmax = u > dmax ? u : dmax;
-    }
-    st4(rh, (unsigned)(t0 + (q * 64 + lane) * V) * 4u, hn[0], hn[1], hn[2], hn[3]);  // past T: dropped
-    if (q == Q - 1)  // the tile's last state, kept for the next sweep
-      st1(rb, (full && wid == SC_CW - 1 && lane == 63) ? (unsigned)((k & 1) * a.ntiles + L) * 4u : SC_OOB, hn[V - 1]);
-    c = fmaf(Tl.tA[q], c, Tl.tb[q]);
-  }
-}
-
+// ---------------------------------------------------------------------------
+// Newton sweep policy.  Scan positions are time steps; tile j, wavefront w,
+// group q, lane l holds steps t0 + 4 (64 q + l) .. + 3 with t0 = j TILE +
+// w WSTEPS.  Needs T % 4 == 0, so a lane's 4 steps are all inside or all
+// outside [0, T).
+// ---------------------------------------------------------------------------
 template <int CELL, bool FIRST>
-__device__ inline void sc_compute_any(const TimeArgs &a, const float *C, int id, const ScRaw &R, ScTile &Tl,
-                                      ScShared &sh, int buf) {
-  if ((id / a.B) * SC_TILE + SC_TILE <= a.T) sc_compute<CELL, FIRST, true>(a, C, id, R, Tl, sh, buf);
-  else sc_compute<CELL, FIRST, false>(a, C, id, R, Tl, sh, buf);
+struct SweepPol {
+  static constexpr int Q = 2, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
+  // raw inputs of one tile: x and the current iterate h per group, and the
+  // state before the wavefront's first step (zero when its resource is empty)
+  struct Raw {
+    float4 x[Q], h[Q];
+    float sw;
+  };
+  // a computed tile waiting for its carry
+  struct Tile {
+    float J[Q][SC_V], R[Q][SC_V], H[Q][SC_V];
+    float iA[Q], ib[Q], tA[Q], tb[Q];
+  };
+  struct Lds {};
+  struct Acc {
+    unsigned dmax;
+  };
+  static constexpr bool kCheckStop = true;
+
+  __device__ static void acc_init(Acc &c) { c.dmax = 0; }
+
+  // In the first sweep the iterate is the zero guess and h is not read.
+  __device__ static void load(const TimeArgs &a, int id, Raw &R) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
+    const int j = id / B, b = id % B;
+    const int t0 = j * TILE + wid * WSTEPS;
+    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, (unsigned)T * 4u);
+    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const unsigned off = toff(t0 + (q * 64 + lane) * SC_V, T);
+      R.x[q] = ld4(rx, off);
+      if (!FIRST) R.h[q] = ld4(rh, off);
+    }
+    // the state before step t0: h0 (t0 = 0), the predecessor tile's last
+    // state from the previous sweep (wavefront 0), or h[t0 - 1], which this
+    // block writes only after this load, later in this sweep
+    const float *sb = a.x;
+    unsigned nb = 0, so = 0;
+    if (t0 == 0) {
+      if (a.h0) { sb = a.h0 + b; nb = 4; }
+    } else if (!FIRST && t0 < T) {
+      if (wid == 0) { sb = a.bnd + (size_t)((k - 1) & 1) * a.ntiles + (b * a.tiles_per_seq + j - 1); nb = 4; }
+      else { sb = a.h + (size_t)b * T; nb = (unsigned)T * 4u; so = (unsigned)(t0 - 1) * 4u; }
+    }
+    R.sw = ld1(sc_rsrc(sb, nb), so);
+  }
+
+  // cell, Jacobian and residual of every step, lane-serial composition,
+  // wavefront scans, totals and the aggregate
+  template <bool FULL>
+  __device__ static void compute(const TimeArgs &a, const float *C, int id, const Raw &R, Tile &Tl, ScShared &sh,
+                                 Lds &, int buf) {
+    constexpr int V = SC_V;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, T = a.T;
+    const int t0 = (id / a.B) * TILE + wid * WSTEPS;
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const float xv[V] = {R.x[q].x, R.x[q].y, R.x[q].z, R.x[q].w};
+      float hv[V] = {0.f, 0.f, 0.f, 0.f};
+      if (!FIRST) {
+        hv[0] = R.h[q].x; hv[1] = R.h[q].y; hv[2] = R.h[q].z; hv[3] = R.h[q].w;
+      }
+      float s = shift_in(q == 0 ? R.sw : FIRST ? 0.f : rdlane(R.h[q - 1].w, 63), hv[V - 1]);
+      float A = 1.f, bb = 0.f;
+      const bool in = FULL || t0 + (q * 64 + lane) * V < T;
+#pragma unroll
+      for (int v = 0; v < V; v++) {
+        float f, Jv;
+        scalar_cell<CELL>(C, s, xv[v], f, Jv);
+        float rv = f - hv[v];
+        if (!FULL && !in) { Jv = 1.f; rv = 0.f; }
+        Tl.J[q][v] = Jv;
+        Tl.R[q][v] = rv;
+        Tl.H[q][v] = hv[v];
+        bb = fmaf(Jv, bb, rv);
+        A *= Jv;
+        s = hv[v];
+      }
+      wave_scan_affine1(A, bb);
+      Tl.iA[q] = A;
+      Tl.ib[q] = bb;
+      Tl.tA[q] = rdlane(A, 63);
+      Tl.tb[q] = rdlane(bb, 63);
+    }
+    float wA = Tl.tA[0], wb = Tl.tb[0];
+#pragma unroll
+    for (int q = 1; q < Q; q++) {
+      wb = fmaf(Tl.tA[q], wb, Tl.tb[q]);
+      wA *= Tl.tA[q];
+    }
+    sc_publish(a, id, wA, wb, sh, buf);
+  }
+
+  // update of the tile's steps from its carry, convergence measure, stores
+  __device__ static void apply(const TimeArgs &a, const float *, int id, const Tile &Tl, const ScTot &tt,
+                               const ScShared &sh, Lds &, int buf, Acc &acc) {
+    constexpr int V = SC_V;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
+    const int j = id / B, b = id % B, L = b * a.tiles_per_seq + j;
+    const int t0 = j * TILE + wid * WSTEPS;
+    const bool full = j * TILE + TILE <= T;
+    float c = fmaf(tt.preA, sh.carry[buf], tt.preb);  // dh entering this wavefront's steps
+    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
+    const Rsrc rb = sc_rsrc(a.bnd, (unsigned)a.ntiles * 8u);
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      float dh = shift_in(c, fmaf(Tl.iA[q], c, Tl.ib[q]));
+      float hn[V];
+#pragma unroll
+      for (int v = 0; v < V; v++) {
+        dh = fmaf(Tl.J[q][v], dh, Tl.R[q][v]);
+        hn[v] = Tl.H[q][v] + dh;
+        const unsigned u = __float_as_uint(dh) & 0x7fffffffu;
+        acc.dmax = u > acc.dmax ? u : acc.dmax;
+      }
+      st4(rh, toff(t0 + (q * 64 + lane) * V, T), hn[0], hn[1], hn[2], hn[3]);
+      if (q == Q - 1)  // the tile's last state, kept for the next sweep
+        st1(rb, (full && wid == SC_CW - 1 && lane == 63) ? (unsigned)((k & 1) * a.ntiles + L) * 4u : SC_OOB, hn[V - 1]);
+      c = fmaf(Tl.tA[q], c, Tl.tb[q]);
+    }
+  }
+
+  // block maximum of |dh| into a shard of the sweep's convergence measure
+  __device__ static void finish(const TimeArgs &a, Acc &acc, ScShared &sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const unsigned m = wave_max_u32(acc.dmax);
+    if (lane == 0 && wid < SC_CW) sh.dmax[wid] = m;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned v = sh.dmax[0];
+      for (int w = 1; w < SC_CW; w++) v = sh.dmax[w] > v ? sh.dmax[w] : v;
+      max_agent(&a.st->dslot[a.k & 3][blockIdx.x % PR_DSHARDS], v);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Adjoint policy: lambda_t = g_t + J_{t+1} lambda_{t+1} (lambda_{T-1} =
+// g_{T-1}) by a scan over reversed time, then per step the reverse-mode
+// coefficients of the cell (recomputed from x and h, which the tile keeps)
+// give dx_t, dh0 (t = 0) and the weight-gradient sums.  Scan position p
+// holds step T - 1 - p; a lane's 4 steps are t_lo .. t_lo + 3 with t_lo =
+// T - 4 - p0, visited from t_lo + 3 down.  Needs T % 4 == 0.
+// ---------------------------------------------------------------------------
+template <int CELL>
+struct AdjPol {
+  static constexpr int Q = 1, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
+  struct Raw {
+    float4 x[Q], h[Q], g[Q];
+    float hp;   // h before the wavefront's earliest step (0 at t = 0: h0 is taken then)
+    float xn;   // x after the wavefront's latest step
+    float h0b;  // h0 of the sequence (0 without h0)
+  };
+  struct Tile {
+    float4 x[Q], h[Q];
+    float hp, h0b;
+    float iA[Q], ib[Q], tA[Q], tb[Q];
+  };
+  // per lane and group: the scan multipliers A_t = J_{t+1} and g_t of the
+  // computed tile (lane-private slots, so no cross-wavefront hazard)
+  struct Lds {
+    float4 A[2][SC_CW][Q][64];
+    float4 g[2][SC_CW][Q][64];
+  };
+  struct Acc {
+    float v[10];
+  };
+  static constexpr bool kCheckStop = false;
+
+  __device__ static void acc_init(Acc &c) {
+#pragma unroll
+    for (int i = 0; i < 10; i++) c.v[i] = 0.f;
+  }
+
+  __device__ static int tlo(const TimeArgs &a, int id, int q) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int p0 = (id / a.B) * TILE + wid * WSTEPS + (q * 64 + lane) * SC_V;
+    return a.T - SC_V - p0;
+  }
+
+  __device__ static void load(const TimeArgs &a, int id, Raw &R) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
+    const int b = id % B;
+    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, (unsigned)T * 4u);
+    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
+    const Rsrc rg = sc_rsrc(a.g + (size_t)b * T, (unsigned)T * 4u);
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const int t = tlo(a, id, q);
+      const unsigned off = (t >= 0 && t < T) ? (unsigned)t * 4u : SC_OOB;
+      R.x[q] = ld4(rx, off);
+      R.h[q] = ld4(rh, off);
+      R.g[q] = ld4(rg, off);
+    }
+    // latest step of the wavefront: lane 0 of group 0; earliest: lane 63 of
+    // the last group
+    const int p_first = (id / B) * TILE + wid * WSTEPS;
+    const int t_late = T - 1 - p_first, t_early = T - p_first - WSTEPS;
+    (void)lane;
+    R.xn = ld1(rx, toff(t_late + 1, T));
+    R.hp = ld1(rh, toff(t_early - 1, T));
+    R.h0b = ld1(sc_rsrc(a.h0 ? a.h0 + b : nullptr, 4u), 0u);
+  }
+
+  template <bool FULL>
+  __device__ static void compute(const TimeArgs &a, const float *C, int id, const Raw &R, Tile &Tl, ScShared &sh,
+                                 Lds &lds, int buf) {
+    constexpr int V = SC_V;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, T = a.T;
+    // J of the step after the wavefront's latest step (lane 0, group 0)
+    float Jn;
+    {
+      float f;
+      scalar_cell<CELL>(C, R.h[0].w, R.xn, f, Jn);
+    }
+    float Jprev = 0.f;  // J at the earliest step of the previous group's lane 63
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const int t = tlo(a, id, q);
+      const bool in = FULL || t >= 0;
+      const float xv[V] = {R.x[q].x, R.x[q].y, R.x[q].z, R.x[q].w};
+      const float hv[V] = {R.h[q].x, R.h[q].y, R.h[q].z, R.h[q].w};
+      // state before the lane's earliest step: the next lane's latest h
+      const float last = q + 1 < Q ? rdlane(R.h[q + 1].w, 0) : R.hp;
+      float s0 = shift_out(last, hv[V - 1]);
+      if (t == 0) s0 = R.h0b;
+      float J[V];
+#pragma unroll
+      for (int e = 0; e < V; e++) {
+        float f;
+        scalar_cell<CELL>(C, e == 0 ? s0 : hv[e - 1], xv[e], f, J[e]);
+      }
+      // A_e = J of step t + e + 1: own cells for e < 3, the previous lane's
+      // earliest cell for e = 3 (zero after the sequence's last step)
+      float A3 = shift_in(q == 0 ? Jn : Jprev, J[0]);
+      if (t + V >= T) A3 = 0.f;
+      Jprev = rdlane(J[0], 63);
+      float Av[V] = {J[1], J[2], J[3], A3};
+      float gv[V] = {R.g[q].x, R.g[q].y, R.g[q].z, R.g[q].w};
+      if (!in) {
+#pragma unroll
+        for (int e = 0; e < V; e++) { Av[e] = 1.f; gv[e] = 0.f; }
+      }
+      float A = 1.f, bb = 0.f;
+#pragma unroll
+      for (int e = V - 1; e >= 0; e--) {
+        bb = fmaf(Av[e], bb, gv[e]);
+        A *= Av[e];
+      }
+      lds.A[buf][wid][q][lane] = make_float4(Av[0], Av[1], Av[2], Av[3]);
+      lds.g[buf][wid][q][lane] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+      Tl.x[q] = R.x[q];
+      Tl.h[q] = R.h[q];
+      wave_scan_affine1(A, bb);
+      Tl.iA[q] = A;
+      Tl.ib[q] = bb;
+      Tl.tA[q] = rdlane(A, 63);
+      Tl.tb[q] = rdlane(bb, 63);
+    }
+    Tl.hp = R.hp;
+    Tl.h0b = R.h0b;
+    float wA = Tl.tA[0], wb = Tl.tb[0];
+#pragma unroll
+    for (int q = 1; q < Q; q++) {
+      wb = fmaf(Tl.tA[q], wb, Tl.tb[q]);
+      wA *= Tl.tA[q];
+    }
+    sc_publish(a, id, wA, wb, sh, buf);
+  }
+
+  __device__ static void apply(const TimeArgs &a, const float *C, int id, const Tile &Tl, const ScTot &tt,
+                               const ScShared &sh, Lds &lds, int buf, Acc &acc) {
+    constexpr int V = SC_V;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
+    const int b = id % B;
+    float c = fmaf(tt.preA, sh.carry[buf], tt.preb);  // lambda entering this wavefront (after its latest step)
+    const Rsrc rl = sc_rsrc(a.lam ? a.lam + (size_t)b * T : nullptr, (unsigned)T * 4u);
+    const Rsrc rd = sc_rsrc(a.dx ? a.dx + (size_t)b * T : nullptr, (unsigned)T * 4u);
+    const Rsrc r0 = sc_rsrc(a.dh0 ? a.dh0 + b : nullptr, 4u);
+#pragma unroll
+    for (int q = 0; q < Q; q++) {
+      const int t = tlo(a, id, q);
+      const bool in = t >= 0;
+      const float4 A4 = lds.A[buf][wid][q][lane], g4 = lds.g[buf][wid][q][lane];
+      const float Av[V] = {A4.x, A4.y, A4.z, A4.w}, gv[V] = {g4.x, g4.y, g4.z, g4.w};
+      const float xv[V] = {Tl.x[q].x, Tl.x[q].y, Tl.x[q].z, Tl.x[q].w};
+      const float hv[V] = {Tl.h[q].x, Tl.h[q].y, Tl.h[q].z, Tl.h[q].w};
+      const float last = q + 1 < Q ? rdlane(Tl.h[q + 1].w, 0) : Tl.hp;
+      float s0 = shift_out(last, hv[V - 1]);
+      if (t == 0) s0 = Tl.h0b;
+      float lam = shift_in(c, fmaf(Tl.iA[q], c, Tl.ib[q]));
+      float lv[V], dxv[V];
+      float dh0 = 0.f;
+#pragma unroll
+      for (int e = V - 1; e >= 0; e--) {
+        lam = fmaf(Av[e], lam, gv[e]);
+        lv[e] = lam;
+        const float s = e == 0 ? s0 : hv[e - 1];
+        float co[4], J;
+        scalar_vjp<CELL>(C, s, xv[e], co, J);
+        const float l = in ? lam : 0.f;
+        if constexpr (CELL == C_GRU) {
+          const float ur = l * co[0], uz = l * co[1], un = l * co[2], an = l * co[3];
+          dxv[e] = fmaf(C[15], un, fmaf(C[14], uz, C[13] * ur));
+          acc.v[0] = fmaf(ur, xv[e], acc.v[0]);
+          acc.v[1] = fmaf(uz, xv[e], acc.v[1]);
+          acc.v[2] = fmaf(un, xv[e], acc.v[2]);
+          acc.v[3] += ur;
+          acc.v[4] += uz;
+          acc.v[5] += un;
+          acc.v[6] = fmaf(ur, s, acc.v[6]);
+          acc.v[7] = fmaf(uz, s, acc.v[7]);
+          acc.v[8] = fmaf(an, s, acc.v[8]);
+          acc.v[9] += an;
+        } else {
+          const float u = l * co[0];
+          dxv[e] = C[0] * u;
+          acc.v[0] = fmaf(u, xv[e], acc.v[0]);
+          acc.v[1] += u;
+          acc.v[2] = fmaf(u, s, acc.v[2]);
+        }
+        if (e == 0) dh0 = J * l;
+      }
+      const unsigned off = (in && t < T) ? (unsigned)t * 4u : SC_OOB;
+      st4(rl, off, lv[0], lv[1], lv[2], lv[3]);
+      st4(rd, off, dxv[0], dxv[1], dxv[2], dxv[3]);
+      st1(r0, t == 0 ? 0u : SC_OOB, dh0);
+      c = fmaf(Tl.tA[q], c, Tl.tb[q]);
+    }
+  }
+
+  // block sums of the weight-gradient partials, in the layout the reduction
+  // kernel reads: [W_x (G), b_x (G), W_h (G), b_h (G)]
+  __device__ static void finish(const TimeArgs &a, Acc &acc, ScShared &sh) {
+    constexpr int G = CELL == C_GRU ? 3 : 1, P = 4 * G;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    float v[P];
+    if constexpr (CELL == C_GRU) {
+      const float m[12] = {acc.v[0], acc.v[1], acc.v[2], acc.v[3], acc.v[4], acc.v[5],
+                           acc.v[6], acc.v[7], acc.v[8], acc.v[3], acc.v[4], acc.v[9]};
+#pragma unroll
+      for (int i = 0; i < 12; i++) v[i] = m[i];
+    } else {
+      v[0] = acc.v[0]; v[1] = acc.v[1]; v[2] = acc.v[2]; v[3] = acc.v[1];
+    }
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const float w = wave_sum(v[i]);
+      if (lane == 0 && wid < SC_CW) sh.red[wid][i] = w;
+    }
+    __syncthreads();
+    if (tid < P) {
+      float s = 0.f;
+      for (int w = 0; w < SC_CW; w++) s += sh.red[w][tid];
+      a.part[(size_t)blockIdx.x * P + tid] = s;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// pipeline skeleton
+// ---------------------------------------------------------------------------
+template <class Pol, int CELL>
+__device__ inline void sc_compute_any(const TimeArgs &a, const float *C, int id, const typename Pol::Raw &R,
+                                      typename Pol::Tile &Tl, ScShared &sh, typename Pol::Lds &lds, int buf) {
+  if ((id / a.B) * Pol::TILE + Pol::TILE <= a.T) Pol::template compute<true>(a, C, id, R, Tl, sh, lds, buf);
+  else Pol::template compute<false>(a, C, id, R, Tl, sh, lds, buf);
 }
 
 // One stage of the compute wavefronts: read P's wavefront totals (LDS buffer
 // bufN ^ 1; rewritten two stages on), issue the loads of the tile after N,
 // compute N into buffer bufN, block barrier (the look-back wavefront has left
 // P's carry), update P.
-template <int CELL, bool FIRST>
-__device__ inline void sc_stage(const TimeArgs &a, const float *C, int idP, const ScTile &TP, int idN,
-                                const ScRaw &RN, ScRaw &Rnext, ScTile &TN, ScShared &sh, int bufN, unsigned &dmax) {
+template <class Pol, int CELL>
+__device__ inline void sc_stage(const TimeArgs &a, const float *C, int idP, const typename Pol::Tile &TP, int idN,
+                                const typename Pol::Raw &RN, typename Pol::Raw &Rnext, typename Pol::Tile &TN,
+                                ScShared &sh, typename Pol::Lds &lds, int bufN, typename Pol::Acc &acc) {
   const ScTot tt = sc_tot(sh, bufN ^ 1, threadIdx.x >> 6);
   const int nn = idN + (int)gridDim.x < a.ntiles ? idN + (int)gridDim.x : idN;  // the last reloads itself
-  sc_load<FIRST>(a, nn, Rnext);
-  sc_compute_any<CELL, FIRST>(a, C, idN, RN, TN, sh, bufN);
+  Pol::load(a, nn, Rnext);
+  sc_compute_any<Pol, CELL>(a, C, idN, RN, TN, sh, lds, bufN);
   __syncthreads();
-  sc_apply(a, idP, TP, tt, sh, bufN ^ 1, dmax);
+  Pol::apply(a, C, idP, TP, tt, sh, lds, bufN ^ 1, acc);
 }
-
 
 // Persistent grid (every block resident, grid <= tile count); block g takes
 // tiles g, g + grid, ... in order.  Stage s of a block computes its tile s
-// (compute wavefronts) while the look-back wavefront resolves tile s - 1; after
-// the stage's barrier the compute wavefronts update tile s - 1.  Every
+// (compute wavefronts) while the look-back wavefront resolves tile s - 1;
+// after the stage's barrier the compute wavefronts update tile s - 1.  Every
 // look-back needs only aggregates of tiles computed in an earlier or the same
 // stage of resident blocks and published before their look-backs wait, so the
 // grid cannot deadlock.  The two wavefront roles run separate loops with the
 // same number of barriers (tiles + 1).
-template <int CELL, bool FIRST>
-__global__ __launch_bounds__(SC_THREADS) void k_scalar_sweep(const TimeArgs a) {
+template <class Pol, int CELL>
+__global__ __launch_bounds__(SC_THREADS, 4) void k_scalar_pipe(const TimeArgs a) {
   __shared__ ScShared sh;
+  __shared__ typename Pol::Lds lds;
   // the wavefront id through readfirstlane: the compiler then knows the role
   // branch is uniform, so each wavefront runs exactly one role's loop (and
   // its barriers) instead of both under an execution mask
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = gridDim.x, nt = a.ntiles;
-  unsigned dmax = 0;
+  typename Pol::Acc acc;
+  Pol::acc_init(acc);
   if (wid == SC_LB) {
     if (lane == 0) {
       sh.done[0] = 0;
       sh.done[1] = 0;
     }
-    if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
+    if (Pol::kCheckStop) {
+      if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
+    } else {
+      __syncthreads();
+    }
     __syncthreads();  // end of stage 0
     for (int id = blockIdx.x; id < nt; id += G) {
       sc_lookback_tile(a, id, sh, ((id - (int)blockIdx.x) / G) & 1);
@@ -521,74 +819,87 @@ __global__ __launch_bounds__(SC_THREADS) void k_scalar_sweep(const TimeArgs a) {
   } else {
     // coefficients into scalar registers before any other load: a vector
     // load inside the tile loop would wait behind the prefetched tile
-    float C[13];
+    float C[SC_NC];
 #pragma unroll
-    for (int i = 0; i < 13; i++) C[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.coef[i])));
-    ScRaw R0, R1;
-    ScTile T0, T1;
+    for (int i = 0; i < SC_NC; i++) C[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.coef[i])));
+    typename Pol::Raw R0, R1;
+    typename Pol::Tile T0, T1;
     int id = blockIdx.x;
-    sc_load<FIRST>(a, id, R0);  // overlaps the stop check
-    if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
+    Pol::load(a, id, R0);  // overlaps the stop check
+    if (Pol::kCheckStop) {
+      if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
+    } else {
+      __syncthreads();
+    }
     // stage 0: compute the first tile
-    sc_load<FIRST>(a, id + G < nt ? id + G : id, R1);
-    sc_compute_any<CELL, FIRST>(a, C, id, R0, T0, sh, 0);
+    Pol::load(a, id + G < nt ? id + G : id, R1);
+    sc_compute_any<Pol, CELL>(a, C, id, R0, T0, sh, lds, 0);
     __syncthreads();
     int idP = id;
     id += G;
     int last = 0;  // register set of the final pending tile
     while (true) {
       if (id >= nt) { last = 0; break; }
-      sc_stage<CELL, FIRST>(a, C, idP, T0, id, R1, R0, T1, sh, 1, dmax);
+      sc_stage<Pol, CELL>(a, C, idP, T0, id, R1, R0, T1, sh, lds, 1, acc);
       idP = id;
       id += G;
       if (id >= nt) { last = 1; break; }
-      sc_stage<CELL, FIRST>(a, C, idP, T1, id, R0, R1, T0, sh, 0, dmax);
+      sc_stage<Pol, CELL>(a, C, idP, T1, id, R0, R1, T0, sh, lds, 0, acc);
       idP = id;
       id += G;
     }
     __syncthreads();  // final stage: the look-back wavefront has resolved the last tile
     const ScTot tt = sc_tot(sh, last, wid);
-    if (last == 0) sc_apply(a, idP, T0, tt, sh, 0, dmax);
-    else sc_apply(a, idP, T1, tt, sh, 1, dmax);
+    if (last == 0) Pol::apply(a, C, idP, T0, tt, sh, lds, 0, acc);
+    else Pol::apply(a, C, idP, T1, tt, sh, lds, 1, acc);
   }
-  dmax = wave_max_u32(dmax);
-  if (lane == 0 && wid < SC_CW) sh.dmax[wid] = dmax;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned m = sh.dmax[0];
-    for (int w = 1; w < SC_CW; w++) m = sh.dmax[w] > m ? sh.dmax[w] : m;
-    max_agent(&a.st->dslot[a.k & 3][blockIdx.x % PR_DSHARDS], m);
-  }
+  Pol::finish(a, acc, sh);
 }
 
-int scalar_tile() { return SC_TILE; }
+int scalar_tile() { return SweepPol<C_GRU, false>::TILE; }
+int scalar_adj_tile() { return AdjPol<C_GRU>::TILE; }
 
 hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s) {
   hipLaunchKernelGGL(k_scalar_coef, dim3(1), dim3(64), 0, s, a.Wx, a.bx, a.Wh, a.bh, cell, coef);
   return hipGetLastError();
 }
 
-template <int CELL>
-static hipError_t scalar_launch(const TimeArgs &a, hipStream_t s) {
-  if (a.k == 1) {
-    const int grid = persistent_grid<k_scalar_sweep<CELL, true>, SC_THREADS>(a.ntiles);
-    if (grid <= 0) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_scalar_sweep<CELL, true>), dim3(grid), dim3(SC_THREADS), 0, s, a);
-  } else {
-    const int grid = persistent_grid<k_scalar_sweep<CELL, false>, SC_THREADS>(a.ntiles);
-    if (grid <= 0) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_scalar_sweep<CELL, false>), dim3(grid), dim3(SC_THREADS), 0, s, a);
-  }
+template <class Pol, int CELL>
+static hipError_t pipe_launch(const TimeArgs &a, hipStream_t s, int *grid_out = nullptr) {
+  const int grid = persistent_grid<k_scalar_pipe<Pol, CELL>, SC_THREADS>(a.ntiles);
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+  if (grid_out) *grid_out = grid;
+  hipLaunchKernelGGL((k_scalar_pipe<Pol, CELL>), dim3(grid), dim3(SC_THREADS), 0, s, a);
   return hipGetLastError();
+}
+
+template <int CELL>
+static hipError_t scalar_sweep_cell(const TimeArgs &a, hipStream_t s) {
+  return a.k == 1 ? pipe_launch<SweepPol<CELL, true>, CELL>(a, s) : pipe_launch<SweepPol<CELL, false>, CELL>(a, s);
 }
 
 hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s) {
   switch (cell) {
-    case C_GRU: return scalar_launch<C_GRU>(a, s);
-    case C_TANH: return scalar_launch<C_TANH>(a, s);
-    case C_LINEAR: return scalar_launch<C_LINEAR>(a, s);
+    case C_GRU: return scalar_sweep_cell<C_GRU>(a, s);
+    case C_TANH: return scalar_sweep_cell<C_TANH>(a, s);
+    case C_LINEAR: return scalar_sweep_cell<C_LINEAR>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The adjoint writes one row of weight-gradient partials per block (the
+// block count is returned in a.nparts for the reduction).
+hipError_t launch_scalar_adjoint(int cell, TimeArgs &a, hipStream_t s) {
+  int grid = 0;
+  hipError_t e;
+  switch (cell) {
+    case C_GRU: e = pipe_launch<AdjPol<C_GRU>, C_GRU>(a, s, &grid); break;
+    case C_TANH: e = pipe_launch<AdjPol<C_TANH>, C_TANH>(a, s, &grid); break;
+    case C_LINEAR: e = pipe_launch<AdjPol<C_LINEAR>, C_LINEAR>(a, s, &grid); break;
+    default: return hipErrorInvalidValue;
+  }
+  a.nparts = grid;
+  return e;
 }
 
 }  // namespace pr

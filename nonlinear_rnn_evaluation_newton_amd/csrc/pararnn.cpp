@@ -43,7 +43,7 @@ struct Plan {
   int G = 1, S = 1, N = 1, SW = 1;
   int tile = 0, tps = 0, ntiles = 0;
   // scalar-state sweep (n = d = 1, T % 4 == 0): its own tile size
-  int scalar_ok = 0, tps_s = 0, ntiles_s = 0;
+  int scalar_ok = 0, tps_s = 0, ntiles_s = 0, tps_sa = 0, ntiles_sa = 0;
   // channel path: stripes (sequence x channel group), tiles of sweep / adjoint
   int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
@@ -89,12 +89,16 @@ int make_plan(const pr_problem *p, Plan *pl) {
     // (buffer resources of the scalar sweep address rows, descriptors and
     // boundary states with 31-bit byte offsets)
     if (p->n == 1 && p->d == 1 && p->T % 4 == 0 && (long long)p->T * 4 < (1LL << 31) &&
-        (long long)p->B * ((p->T + scalar_tile() - 1) / scalar_tile()) * 16 < (1LL << 31)) {
+        (long long)p->B * ((p->T + scalar_adj_tile() - 1) / scalar_adj_tile()) * 16 < (1LL << 31)) {
       pl->scalar_ok = 1;
       pl->tps_s = (p->T + scalar_tile() - 1) / scalar_tile();
       if ((long long)pl->tps_s * p->B > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
       pl->ntiles_s = pl->tps_s * p->B;
+      pl->tps_sa = (p->T + scalar_adj_tile() - 1) / scalar_adj_tile();
+      if ((long long)pl->tps_sa * p->B > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
+      pl->ntiles_sa = pl->tps_sa * p->B;
       nt = nt > pl->ntiles_s ? nt : pl->ntiles_s;
+      nt = nt > pl->ntiles_sa ? nt : pl->ntiles_sa;
     }
     size_t o = 0;
     pl->off_state = o; o = align256(o + sizeof(SolveState));
@@ -104,7 +108,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_bnd = o; o = align256(o + (size_t)2 * nt * N * 4);
     pl->off_coef = o; o = align256(o + 64 * 4);
     pl->solve_bytes = o;
-    pl->off_part = o; o = align256(o + (size_t)pl->ntiles * time_part_count(p->cell, N) * 4);
+    pl->off_part = o; o = align256(o + (size_t)nt * time_part_count(p->cell, N) * 4);
     pl->adjoint_bytes = o;
     return PR_OK;
   }
@@ -546,9 +550,18 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     a.tiles_per_seq = pl.tps;
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0) | (al16(g) ? 4 : 0) | (al16(lambda) ? 8 : 0);
+    // n = d = 1 with vector-friendly sizes takes the scalar-state adjoint
+    const bool scalar = pl.scalar_ok && a.vec_ok == 15 && al16(dx) && !getenv("PARARNN_NO_SCALAR");
+    if (scalar) {
+      a.coef = (const float *)(ws + pl.off_coef);
+      a.tiles_per_seq = pl.tps_sa;
+      a.ntiles = pl.ntiles_sa;
+      HIPCHK(launch_scalar_coef(a, kcell(p->cell), (float *)(ws + pl.off_coef), s));
+    }
     Trace &tr = trace();
     const int ti = tr.begin(TR_ADJ, s);
-    HIPCHK(launch_time_adjoint(kcell(p->cell), pl.N, a, s));
+    if (scalar) HIPCHK(launch_scalar_adjoint(kcell(p->cell), a, s));
+    else HIPCHK(launch_time_adjoint(kcell(p->cell), pl.N, a, s));
     tr.end(TR_ADJ, ti, s);
     if (dW && (dW->W_x || dW->b_x || dW->W_h || dW->b_h))
       HIPCHK(launch_time_reduce(kcell(p->cell), pl.N, a, a.part, dW->W_x, dW->b_x, dW->W_h, dW->b_h, s));

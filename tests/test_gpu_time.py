@@ -163,6 +163,24 @@ def test_adjoint_small_cells(cell, n, d, T):
     adjoint_check(p, h, a)
 
 
+@pytest.mark.parametrize("cell", [sy.CELL_GRU, sy.CELL_TANH_RNN, sy.CELL_LINEAR])
+@pytest.mark.parametrize("T", [4, 8, 1020, 1792, 1796, 4100, 12292])
+def test_scalar_state_adjoint(cell, T):
+    """n = d = 1 with T % 4 == 0: the scalar-state adjoint (reverse scan over
+    tiles of 1792 steps, ragged tails, h0 and biases) against the oracle's
+    backpropagation through the sequential rollout."""
+    p = sy.custom_problem(cell, B=3, T=T, d=1, n=1, seed=11 * T + cell,
+                          w_scale=0.5 if cell == sy.CELL_LINEAR else 1.0, h0=True)
+    if cell == sy.CELL_LINEAR:
+        p["W_h"] = np.clip(p["W_h"], -0.9, 0.9)
+    say("adjoint scalar case", p["name"], T)
+    dp, st, it, dl, h = gpu_solve(p, tol=1e-4 if cell == sy.CELL_LINEAR else 1e-6, max_iters=T)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_check(p, h, a)
+
+
 def _int_ops(rng, B, T, n):
     A = np.zeros((B, T, n, n))
     col = rng.integers(0, n, size=(B, T, n))
