@@ -156,10 +156,13 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
 /*
  * Kernel timing for profiling and benchmarks (per calling thread).
  * pararnn_trace(1) clears the counters and starts bracketing, with HIP events
- * on the call's stream, every Newton-sweep launch that does work (launches
- * after the stop rule has fired are not counted) and the main kernel of each
- * adjoint; pararnn_trace(0) stops.  pararnn_trace_read waits for pending
- * events and returns the totals (any pointer may be NULL).
+ * on the call's stream, the Newton sweeps and the main kernel of each
+ * adjoint; pararnn_trace(0) stops.  Sweeps are bracketed per batch of
+ * back-to-back launches (per launch on the dense n = 64 path, whose parts are
+ * timed too); launches after the stop rule has fired exit at once and are
+ * not counted, their few microseconds stay in the total.
+ * pararnn_trace_read waits for pending events and returns the totals (any
+ * pointer may be NULL).
  */
 int pararnn_trace(int enable);
 int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches);

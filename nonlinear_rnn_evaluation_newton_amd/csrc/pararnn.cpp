@@ -444,13 +444,25 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
   poll_schedule(&first, &next);
   if (tol <= 0.f) first = kmax;
   int k = 1, out_iters = 0, out_status = PR_OK;
+  // Sweep timing: the dense n = 64 path brackets every sweep (its parts are
+  // timed too); the others bracket each batch of back-to-back sweeps, so the
+  // per-launch figure carries no event overhead between launches.
+  const bool per_sweep_events = pl.path == PATH_D64;
+  int nbatch = 0, batch_first[Trace::CAP], batch_last[Trace::CAP];
   while (true) {
     const int batch = k == 1 ? first : next;
     int k_last = k + batch - 1;
     if (k_last > kmax) k_last = kmax;
+    const bool bev = tr.on && !per_sweep_events && k_last <= Trace::CAP && nbatch < Trace::CAP;
+    if (bev) {
+      HIPCHK(hipEventRecord(tr.sw[2 * (k - 1)], s));
+      batch_first[nbatch] = k;
+      batch_last[nbatch] = k_last;
+      nbatch++;
+    }
     for (int kk = k; kk <= k_last; kk++) {
       a.k = kk;
-      const bool ev = tr.on && kk <= Trace::CAP;
+      const bool ev = tr.on && per_sweep_events && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
       if (scalar) {
         HIPCHK(launch_scalar_sweep(kc, a, s));
@@ -469,6 +481,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       }
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
+    if (bev) HIPCHK(hipEventRecord(tr.sw[2 * (k_last - 1) + 1], s));
     HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
     HIPCHK(hipStreamSynchronize(s));
     if (hs->fault) return fail(PR_EHIP, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
@@ -489,7 +502,16 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     }
     k = k_last + 1;
   }
-  if (tr.on) {
+  if (tr.on && !per_sweep_events) {
+    // a batch's launches past the stop exit at once; count the ones that worked
+    for (int i = 0; i < nbatch && batch_first[i] <= out_iters; i++) {
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (batch_first[i] - 1)], tr.sw[2 * (batch_last[i] - 1) + 1]));
+      tr.ms[TR_SWEEP] += ms;
+      tr.cnt[TR_SWEEP] += (batch_last[i] < out_iters ? batch_last[i] : out_iters) - batch_first[i] + 1;
+    }
+  }
+  if (tr.on && per_sweep_events) {
     const int m = out_iters < Trace::CAP ? out_iters : Trace::CAP;
     for (int kk = 1; kk <= m; kk++) {
       float ms = 0.f;
