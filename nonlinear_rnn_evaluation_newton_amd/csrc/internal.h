@@ -141,5 +141,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
 // ---------------- utilities ------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// dst [C, R] = transpose of row-major src [R, C]; elem_bytes 2 or 4
+hipError_t launch_transpose(const void *src, void *dst, int R, int C, int elem_bytes, hipStream_t s);
 
 }  // namespace pr

@@ -48,6 +48,7 @@ struct Plan {
   int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
+  size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
   // dense n = 64 path
   int cps = 0, nchunks = 0;
   size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0, off_csum = 0;
@@ -173,6 +174,8 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_part = o; o = align256(o + (size_t)pl->ntiles_a * gf.CH * 11 * 4);
     const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
     pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
+    pl->off_xt = o; o = align256(o + rows * p->d * es);
+    pl->off_wt = o; o = align256(o + (size_t)3 * p->n * p->d * es);
     pl->adjoint_bytes = o;
     return PR_OK;
   }
@@ -692,24 +695,31 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     const int tg = tr.begin(TR_AGEMM, s);
     if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
       HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
+    // Both products contract over an outer dimension of a stored operand;
+    // transposed copies (HBM-bound, a few percent of the products) put K
+    // innermost in every operand, the layout the GEMM reads fastest.
     const int rows = p->B * p->T, G3 = 3 * p->n;
-    if (dx) {  // dx = dU W_x
+    if (dx) {  // dx = dU W_x: B operand W_x^T [d, 3n]
+      HIPCHK(launch_transpose(w->W_x, ws + pl.off_wt, G3, p->d, (int)es, s));
       GemmArgs gm{};
-      gm.A = ws + pl.off_dU; gm.B = w->W_x; gm.C = dx; gm.bias = nullptr; gm.ws = nullptr;
-      gm.M = rows; gm.N = p->d; gm.K = G3; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d; gm.splits = 1;
-      gm.a_kc = true; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = !bf;
+      gm.A = ws + pl.off_dU; gm.B = ws + pl.off_wt; gm.C = dx; gm.bias = nullptr; gm.ws = nullptr;
+      gm.M = rows; gm.N = p->d; gm.K = G3; gm.lda = G3; gm.ldb = G3; gm.ldc = p->d; gm.splits = 1;
+      gm.a_kc = true; gm.b_kc = true; gm.bf16 = bf; gm.out_f32 = !bf;
       gm.vec_a = ((size_t)G3 * es) % 16 == 0;
-      gm.vec_b = ((uintptr_t)w->W_x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+      gm.vec_b = gm.vec_a;
       HIPCHK(launch_gemm(gm, s));
     }
-    if (dW && dW->W_x) {  // dW_x = dU^T x
+    if (dW && dW->W_x) {  // dW_x = dU^T x: operands dU^T [3n, rows] (in U's space) and x^T [d, rows]
+      HIPCHK(launch_transpose(ws + pl.off_dU, ws + pl.off_U, rows, G3, (int)es, s));
+      HIPCHK(launch_transpose(x, ws + pl.off_xt, rows, p->d, (int)es, s));
       GemmArgs gm{};
-      gm.A = ws + pl.off_dU; gm.B = x; gm.C = dW->W_x; gm.bias = nullptr; gm.ws = (float *)(ws + pl.off_gws);
-      gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d;
+      gm.A = ws + pl.off_U; gm.B = ws + pl.off_xt; gm.C = dW->W_x; gm.bias = nullptr;
+      gm.ws = (float *)(ws + pl.off_gws);
+      gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = rows; gm.ldb = rows; gm.ldc = p->d;
       gm.splits = gemm_splits(G3, p->d, rows);
-      gm.a_kc = false; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = true;
-      gm.vec_a = ((size_t)G3 * es) % 16 == 0;
-      gm.vec_b = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
+      gm.a_kc = true; gm.b_kc = true; gm.bf16 = bf; gm.out_f32 = true;
+      gm.vec_a = ((size_t)rows * es) % 16 == 0;
+      gm.vec_b = gm.vec_a;
       HIPCHK(launch_gemm(gm, s));
     }
     tr.end(TR_AGEMM, tg, s);
