@@ -4,28 +4,16 @@
 // (cell, Jacobian and residual at every step, affine scan of (J_t, r_t),
 // in-place update, convergence measure) and the adjoint (reverse scan of
 // (J_{t+1}, g_t) for lambda, then dx, dh0 and the weight gradients), both on
-// one pipeline designed so that HBM streams while the VALU works:
-//  * the cell's weights are folded once per call into a coefficient table
-//    (exp2 scale factors included) held in scalar registers;
-//  * each lane owns 4 consecutive steps per group (16-byte accesses), 2
-//    groups per wavefront, 7 compute wavefronts per tile;
-//  * memory access goes through buffer instructions whose range check
-//    drops out-of-range lanes, so no load or store sits under a branch;
-//  * a block computes tile N while the tile before it waits for its carry:
-//    two register sets alternate, and the loads of the tile after N are in
-//    flight during N;
-//  * an eighth wavefront per block does the decoupled look-back alone, so its
-//    waits never queue behind the bulk loads and stores of the others;
-//  * the wavefront scan runs on DPP-fused multiply/FMA instructions.
-#include "k_time_impl.h"
+// the tile pipeline of pipe.h.  Per lane: 4 consecutive steps per group
+// (16-byte accesses); the cell's weights are folded once per call into a
+// coefficient table held in scalar registers; the wavefront scan runs on
+// DPP-fused multiply/FMA instructions.
+#include "pipe.h"
 
 namespace pr {
 
 constexpr int SC_V = 4;
-constexpr int SC_CW = 7;                       // compute wavefronts per block
-constexpr int SC_THREADS = 64 * (SC_CW + 1);   // + the look-back wavefront (a multiple of 4 wavefronts)
-constexpr int SC_LB = SC_CW;                   // wavefront id of the look-back wavefront
-constexpr int SC_NC = 16;                      // coefficient table size
+constexpr int SC_NC = 16;  // coefficient table size
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Coefficient table derived from the weights once per call.
@@ -154,54 +142,6 @@ __device__ inline void wave_scan_affine1(float &A, float &b) {
       "s_nop 1"
       : "+v"(A), "+v"(b));
 }
-
-__device__ inline float rdlane(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
-
-// lane l receives v of lane l - 1; lane 0 receives first
-__device__ inline float shift_in(float first, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(v), 0x138, 0xf, 0xf, false));
-}
-// lane l receives v of lane l + 1; lane 63 receives last
-__device__ inline float shift_out(float last, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));
-}
-
-// Memory access goes through buffer instructions on per-row buffer
-// resources: the hardware range check returns zero for loads outside a
-// resource and drops stores outside it (offset SC_OOB is outside every
-// resource; a null base gets an empty resource), so every load and store in
-// the tile loop is unconditional.  That keeps the compiler's count of memory
-// operations in flight exact: loads and stores share one in-order counter on
-// this architecture, and a memory instruction under a branch would make later
-// waits conservative, draining recent stores before prefetched data can be
-// used.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr unsigned SC_OOB = 0x80000000u;
-constexpr int SC_SC1 = 16;  // cache policy: device-scope coherent access
-
-__device__ inline Rsrc sc_rsrc(const void *base, unsigned bytes) {
-  // raw buffer, stride 0, 32-bit data format in the fourth descriptor word
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, base ? (int)bytes : 0, 0x00020000);
-}
-__device__ inline float4 ld4(Rsrc r, unsigned off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-}
-__device__ inline float ld1(Rsrc r, unsigned off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ inline void st4(Rsrc r, unsigned off, float a, float b, float c, float d) {
-  u32x4 v;
-  v.x = __float_as_uint(a); v.y = __float_as_uint(b); v.z = __float_as_uint(c); v.w = __float_as_uint(d);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-}
-__device__ inline void st1(Rsrc r, unsigned off, float a) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
-}
-// byte offset of step t in a row of floats, or SC_OOB when t is outside [0, T)
-__device__ inline unsigned toff(int t, int T) { return (t >= 0 && t < T) ? (unsigned)t * 4u : SC_OOB; }
 
 // Wavefront totals of the last two computed tiles and their carries.
 struct ScShared {
@@ -389,6 +329,27 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
   if ((threadIdx.x & 63) == 0) sh.carry[buf] = carry;
 }
 
+// Members common to the scalar-state policies.
+struct ScBase {
+  using Args = TimeArgs;
+  using Shared = ScShared;
+  using Tot = ScTot;
+  struct Consts {
+    float c[SC_NC];
+  };
+  __device__ static void shared_init(Shared &sh) {
+    sh.done[0] = 0;
+    sh.done[1] = 0;
+  }
+  __device__ static void consts(const Args &a, Consts &K) {
+#pragma unroll
+    for (int i = 0; i < SC_NC; i++) K.c[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.coef[i])));
+  }
+  __host__ __device__ static int ntiles(const Args &a) { return a.ntiles; }
+  __device__ static Tot tot(const Shared &sh, int buf, int wid) { return sc_tot(sh, buf, wid); }
+  __device__ static void lookback_tile(const Args &a, int id, Shared &sh, int buf) { sc_lookback_tile(a, id, sh, buf); }
+};
+
 // ---------------------------------------------------------------------------
 // Newton sweep policy.  Scan positions are time steps; tile j, wavefront w,
 // group q, lane l holds steps t0 + 4 (64 q + l) .. + 3 with t0 = j TILE +
@@ -396,7 +357,7 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
 // outside [0, T).
 // ---------------------------------------------------------------------------
 template <int CELL, bool FIRST>
-struct SweepPol {
+struct SweepPol : ScBase {
   static constexpr int Q = 2, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   // raw inputs of one tile: x and the current iterate h per group, and the
   // state before the wavefront's first step (zero when its resource is empty)
@@ -413,8 +374,11 @@ struct SweepPol {
   struct Acc {
     unsigned dmax;
   };
-  static constexpr bool kCheckStop = true;
-
+  // the stop rule on the previous sweep's measure (every block exits once it holds)
+  __device__ static bool open(const Args &a, Shared &sh) {
+    return sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop);
+  }
+  __device__ static bool full(const Args &a, int id) { return (id / a.B) * TILE + TILE <= a.T; }
   __device__ static void acc_init(Acc &c) { c.dmax = 0; }
 
   // In the first sweep the iterate is the zero guess and h is not read.
@@ -447,8 +411,9 @@ struct SweepPol {
   // cell, Jacobian and residual of every step, lane-serial composition,
   // wavefront scans, totals and the aggregate
   template <bool FULL>
-  __device__ static void compute(const TimeArgs &a, const float *C, int id, const Raw &R, Tile &Tl, ScShared &sh,
+  __device__ static void compute(const TimeArgs &a, const Consts &K, int id, const Raw &R, Tile &Tl, ScShared &sh,
                                  Lds &, int buf) {
+    const float *C = K.c;
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, T = a.T;
     const int t0 = (id / a.B) * TILE + wid * WSTEPS;
@@ -491,7 +456,7 @@ struct SweepPol {
   }
 
   // update of the tile's steps from its carry, convergence measure, stores
-  __device__ static void apply(const TimeArgs &a, const float *, int id, const Tile &Tl, const ScTot &tt,
+  __device__ static void apply(const TimeArgs &a, const Consts &, int id, const Tile &Tl, const ScTot &tt,
                                const ScShared &sh, Lds &, int buf, Acc &acc) {
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
@@ -542,7 +507,7 @@ struct SweepPol {
 // T - 4 - p0, visited from t_lo + 3 down.  Needs T % 4 == 0.
 // ---------------------------------------------------------------------------
 template <int CELL>
-struct AdjPol {
+struct AdjPol : ScBase {
   static constexpr int Q = 1, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   struct Raw {
     float4 x[Q], h[Q], g[Q];
@@ -564,8 +529,11 @@ struct AdjPol {
   struct Acc {
     float v[10];
   };
-  static constexpr bool kCheckStop = false;
-
+  __device__ static bool open(const Args &, Shared &) {
+    __syncthreads();
+    return false;
+  }
+  __device__ static bool full(const Args &a, int id) { return (id / a.B) * TILE + TILE <= a.T; }
   __device__ static void acc_init(Acc &c) {
 #pragma unroll
     for (int i = 0; i < 10; i++) c.v[i] = 0.f;
@@ -602,8 +570,9 @@ struct AdjPol {
   }
 
   template <bool FULL>
-  __device__ static void compute(const TimeArgs &a, const float *C, int id, const Raw &R, Tile &Tl, ScShared &sh,
+  __device__ static void compute(const TimeArgs &a, const Consts &K, int id, const Raw &R, Tile &Tl, ScShared &sh,
                                  Lds &lds, int buf) {
+    const float *C = K.c;
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, T = a.T;
     // J of the step after the wavefront's latest step (lane 0, group 0)
@@ -667,8 +636,9 @@ struct AdjPol {
     sc_publish(a, id, wA, wb, sh, buf);
   }
 
-  __device__ static void apply(const TimeArgs &a, const float *C, int id, const Tile &Tl, const ScTot &tt,
+  __device__ static void apply(const TimeArgs &a, const Consts &K, int id, const Tile &Tl, const ScTot &tt,
                                const ScShared &sh, Lds &lds, int buf, Acc &acc) {
+    const float *C = K.c;
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
     const int b = id % B;
@@ -756,106 +726,6 @@ struct AdjPol {
   }
 };
 
-// ---------------------------------------------------------------------------
-// pipeline skeleton
-// ---------------------------------------------------------------------------
-template <class Pol, int CELL>
-__device__ inline void sc_compute_any(const TimeArgs &a, const float *C, int id, const typename Pol::Raw &R,
-                                      typename Pol::Tile &Tl, ScShared &sh, typename Pol::Lds &lds, int buf) {
-  if ((id / a.B) * Pol::TILE + Pol::TILE <= a.T) Pol::template compute<true>(a, C, id, R, Tl, sh, lds, buf);
-  else Pol::template compute<false>(a, C, id, R, Tl, sh, lds, buf);
-}
-
-// One stage of the compute wavefronts: read P's wavefront totals (LDS buffer
-// bufN ^ 1; rewritten two stages on), issue the loads of the tile after N,
-// compute N into buffer bufN, block barrier (the look-back wavefront has left
-// P's carry), update P.
-template <class Pol, int CELL>
-__device__ inline void sc_stage(const TimeArgs &a, const float *C, int idP, const typename Pol::Tile &TP, int idN,
-                                const typename Pol::Raw &RN, typename Pol::Raw &Rnext, typename Pol::Tile &TN,
-                                ScShared &sh, typename Pol::Lds &lds, int bufN, typename Pol::Acc &acc) {
-  const ScTot tt = sc_tot(sh, bufN ^ 1, threadIdx.x >> 6);
-  const int nn = idN + (int)gridDim.x < a.ntiles ? idN + (int)gridDim.x : idN;  // the last reloads itself
-  Pol::load(a, nn, Rnext);
-  sc_compute_any<Pol, CELL>(a, C, idN, RN, TN, sh, lds, bufN);
-  __syncthreads();
-  Pol::apply(a, C, idP, TP, tt, sh, lds, bufN ^ 1, acc);
-}
-
-// Persistent grid (every block resident, grid <= tile count); block g takes
-// tiles g, g + grid, ... in order.  Stage s of a block computes its tile s
-// (compute wavefronts) while the look-back wavefront resolves tile s - 1;
-// after the stage's barrier the compute wavefronts update tile s - 1.  Every
-// look-back needs only aggregates of tiles computed in an earlier or the same
-// stage of resident blocks and published before their look-backs wait, so the
-// grid cannot deadlock.  The two wavefront roles run separate loops with the
-// same number of barriers (tiles + 1).
-template <class Pol, int CELL>
-__global__ __launch_bounds__(SC_THREADS, 4) void k_scalar_pipe(const TimeArgs a) {
-  __shared__ ScShared sh;
-  __shared__ typename Pol::Lds lds;
-  // the wavefront id through readfirstlane: the compiler then knows the role
-  // branch is uniform, so each wavefront runs exactly one role's loop (and
-  // its barriers) instead of both under an execution mask
-  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x, nt = a.ntiles;
-  typename Pol::Acc acc;
-  Pol::acc_init(acc);
-  if (wid == SC_LB) {
-    if (lane == 0) {
-      sh.done[0] = 0;
-      sh.done[1] = 0;
-    }
-    if (Pol::kCheckStop) {
-      if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
-    } else {
-      __syncthreads();
-    }
-    __syncthreads();  // end of stage 0
-    for (int id = blockIdx.x; id < nt; id += G) {
-      sc_lookback_tile(a, id, sh, ((id - (int)blockIdx.x) / G) & 1);
-      __syncthreads();
-    }
-  } else {
-    // coefficients into scalar registers before any other load: a vector
-    // load inside the tile loop would wait behind the prefetched tile
-    float C[SC_NC];
-#pragma unroll
-    for (int i = 0; i < SC_NC; i++) C[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.coef[i])));
-    typename Pol::Raw R0, R1;
-    typename Pol::Tile T0, T1;
-    int id = blockIdx.x;
-    Pol::load(a, id, R0);  // overlaps the stop check
-    if (Pol::kCheckStop) {
-      if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &sh.stop)) return;
-    } else {
-      __syncthreads();
-    }
-    // stage 0: compute the first tile
-    Pol::load(a, id + G < nt ? id + G : id, R1);
-    sc_compute_any<Pol, CELL>(a, C, id, R0, T0, sh, lds, 0);
-    __syncthreads();
-    int idP = id;
-    id += G;
-    int last = 0;  // register set of the final pending tile
-    while (true) {
-      if (id >= nt) { last = 0; break; }
-      sc_stage<Pol, CELL>(a, C, idP, T0, id, R1, R0, T1, sh, lds, 1, acc);
-      idP = id;
-      id += G;
-      if (id >= nt) { last = 1; break; }
-      sc_stage<Pol, CELL>(a, C, idP, T1, id, R0, R1, T0, sh, lds, 0, acc);
-      idP = id;
-      id += G;
-    }
-    __syncthreads();  // final stage: the look-back wavefront has resolved the last tile
-    const ScTot tt = sc_tot(sh, last, wid);
-    if (last == 0) Pol::apply(a, C, idP, T0, tt, sh, lds, 0, acc);
-    else Pol::apply(a, C, idP, T1, tt, sh, lds, 1, acc);
-  }
-  Pol::finish(a, acc, sh);
-}
-
 int scalar_tile() { return SweepPol<C_GRU, false>::TILE; }
 int scalar_adj_tile() { return AdjPol<C_GRU>::TILE; }
 
@@ -864,18 +734,9 @@ hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStrea
   return hipGetLastError();
 }
 
-template <class Pol, int CELL>
-static hipError_t pipe_launch(const TimeArgs &a, hipStream_t s, int *grid_out = nullptr) {
-  const int grid = persistent_grid<k_scalar_pipe<Pol, CELL>, SC_THREADS>(a.ntiles);
-  if (grid <= 0) return hipErrorInvalidConfiguration;
-  if (grid_out) *grid_out = grid;
-  hipLaunchKernelGGL((k_scalar_pipe<Pol, CELL>), dim3(grid), dim3(SC_THREADS), 0, s, a);
-  return hipGetLastError();
-}
-
 template <int CELL>
 static hipError_t scalar_sweep_cell(const TimeArgs &a, hipStream_t s) {
-  return a.k == 1 ? pipe_launch<SweepPol<CELL, true>, CELL>(a, s) : pipe_launch<SweepPol<CELL, false>, CELL>(a, s);
+  return a.k == 1 ? pipe_launch<SweepPol<CELL, true>>(a, s) : pipe_launch<SweepPol<CELL, false>>(a, s);
 }
 
 hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s) {
@@ -893,9 +754,9 @@ hipError_t launch_scalar_adjoint(int cell, TimeArgs &a, hipStream_t s) {
   int grid = 0;
   hipError_t e;
   switch (cell) {
-    case C_GRU: e = pipe_launch<AdjPol<C_GRU>, C_GRU>(a, s, &grid); break;
-    case C_TANH: e = pipe_launch<AdjPol<C_TANH>, C_TANH>(a, s, &grid); break;
-    case C_LINEAR: e = pipe_launch<AdjPol<C_LINEAR>, C_LINEAR>(a, s, &grid); break;
+    case C_GRU: e = pipe_launch<AdjPol<C_GRU>>(a, s, &grid); break;
+    case C_TANH: e = pipe_launch<AdjPol<C_TANH>>(a, s, &grid); break;
+    case C_LINEAR: e = pipe_launch<AdjPol<C_LINEAR>>(a, s, &grid); break;
     default: return hipErrorInvalidValue;
   }
   a.nparts = grid;
