@@ -188,6 +188,181 @@ __global__ void k_gemm_splitk_sum(const GemmArgs g) {
   store_out<TO>((TO *)g.C + row * g.ldc + col, s);
 }
 
+// ---------------------------------------------------------------------------
+// Large bf16 products with both operands K-contiguous (the input projection
+// and the adjoint's dx and dW_x at channel widths of hundreds and more).
+//
+// 256 x 256 block tile, K step 64, 8 wavefronts of 128 (M) x 64 (N) each:
+// per 16-wide K slice a wavefront reads 6 operand fragments from LDS for 8
+// MFMAs, half the LDS traffic per MFMA of a 64 x 64 wavefront tile, which
+// saturates LDS bandwidth before the matrix cores.  Operands are staged
+// global -> registers -> LDS (rows padded by 16 B, so the 16-byte fragment
+// reads of 8 consecutive rows fall in distinct banks), double-buffered.
+// The MFMA takes the B fragment as its first operand, so a lane's results
+// are 4 adjacent columns of one output row (8- or 16-byte stores).
+// Loads go through buffer resources on the block's rows: rows past M or N
+// and K chunks past the split's end read as zero.
+// Tile order: blocks are dealt round-robin over the 8 XCDs, so block ids are
+// regrouped to give each XCD a contiguous range of tiles, walked in groups
+// of 8 tile rows; concurrently running tiles of one XCD share operand rows
+// in its L2.
+constexpr int BT = 256, BK = 64, BLD = BK + 8;
+
+typedef __amdgpu_buffer_rsrc_t GRsrc;
+__device__ inline GRsrc g_rsrc(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
+
+template <typename TO>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BT * BLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BT * BLD];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 2, wn = wid & 3;
+  const int tiles = tiles_m * tiles_n;
+  int id = blockIdx.x;
+  if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
+  constexpr int GM = 8;
+  const int width = GM * tiles_n, fm = (id / width) * GM;
+  const int gm = min(tiles_m - fm, GM);
+  const int tm = fm + (id % width) % gm, tn = (id % width) / gm;
+  const int m0 = tm * BT, n0 = tn * BT;
+  const int split = blockIdx.y;
+  const int kchunk = ((g.K + g.splits - 1) / g.splits + BK - 1) / BK * BK;
+  const int kb = split * kchunk, ke = min(g.K, kb + kchunk);
+
+  const uint16_t *A = (const uint16_t *)g.A + (size_t)m0 * g.lda;
+  const uint16_t *B = (const uint16_t *)g.B + (size_t)n0 * g.ldb;
+  const GRsrc ra = g_rsrc(A, (unsigned)(min(BT, g.M - m0) * g.lda * 2));
+  const GRsrc rb = g_rsrc(B, (unsigned)(min(BT, g.N - n0) * g.ldb * 2));
+
+  // staging: 4 chunks of 8 K-consecutive elements per operand per thread
+  int srow[4], skc[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int e = tid + q * 512;
+    srow[q] = e >> 3;
+    skc[q] = (e & 7) * 8;
+  }
+  gu32x4 va[4], vb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const bool in = k0 + skc[q] < ke;
+      va[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          ra, in ? (unsigned)(srow[q] * g.lda + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
+      vb[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, in ? (unsigned)(srow[q] * g.ldb + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      *reinterpret_cast<gu32x4 *>(&sA[buf][srow[q] * BLD + skc[q]]) = va[q];
+      *reinterpret_cast<gu32x4 *>(&sB[buf][srow[q] * BLD + skc[q]]) = vb[q];
+    }
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; j++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[j][i][r] = 0.f;
+
+  int buf = 0;
+  if (kb < ke) {
+    gload(kb);
+    lstore(0);
+  }
+  __syncthreads();
+  const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), kl = (lane >> 5) * 8;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    const bool more = k0 + BK < ke;
+    if (more) gload(k0 + BK);
+    const uint16_t *cA = sA[buf], *cB = sB[buf];
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8_t a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
+#pragma unroll
+      for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // lane holds rows m = (lane & 31) of each 32 x 32 tile and, per group of 4
+  // registers, the 4 adjacent columns 8 * (r / 4) + 4 * (lane / 32) + (0..3)
+  const bool vec_c = g.splits == 1 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int rg = 0; rg < 4; rg++) {
+        const int n = n0 + wn * 64 + j * 32 + 8 * rg + 4 * (lane >> 5);
+        if (n >= g.N) continue;
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const float bias = (g.bias && split == 0 && n + c < g.N) ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
+          v[c] = acc[j][i][4 * rg + c] + bias;
+        }
+        if (g.splits > 1) {
+          float *w = g.ws + ((size_t)split * g.M + m) * g.N + n;
+          if (n + 4 <= g.N && (g.N % 4) == 0) *reinterpret_cast<float4 *>(w) = make_float4(v[0], v[1], v[2], v[3]);
+          else
+            for (int c = 0; c < 4 && n + c < g.N; c++) w[c] = v[c];
+          continue;
+        }
+        TO *o = (TO *)g.C + (size_t)m * g.ldc + n;
+        if (vec_c && n + 4 <= g.N) {
+          if constexpr (sizeof(TO) == 2) {
+            uint2 u;
+            u.x = (unsigned)f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16);
+            u.y = (unsigned)f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2 *>(o) = u;
+          } else {
+            *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+          for (int c = 0; c < 4 && n + c < g.N; c++) store_out<TO>(o + c, v[c]);
+        }
+      }
+  }
+}
+
+// The large-tile kernel takes bf16 products with both operands K-contiguous,
+// 16-byte rows (K, lda, ldb multiples of 8, aligned bases), both output
+// extents of at least one block tile, and 256 rows of either operand within
+// the 31-bit reach of a buffer offset.
+static bool big_nt(const GemmArgs &g) {
+  return g.bf16 && g.a_kc && g.b_kc && g.vec_a && g.vec_b && g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         g.M >= BT && g.N >= BT && (long long)BT * g.lda * 2 < (1LL << 31) && (long long)BT * g.ldb * 2 < (1LL << 31);
+}
+
+template <typename TO>
+static hipError_t gemm_big_launch(const GemmArgs &g, hipStream_t s) {
+  const int tm = (g.M + BT - 1) / BT, tn = (g.N + BT - 1) / BT;
+  hipLaunchKernelGGL((k_gemm_bf16_nt<TO>), dim3(tm * tn, g.splits), dim3(512), 0, s, g, tm, tn);
+  if (g.splits > 1) {
+    const size_t tot = (size_t)g.M * g.N;
+    hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
 template <typename T, bool AKC, bool BKC, typename TO>
 static hipError_t gemm_launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
@@ -211,6 +386,8 @@ int gemm_splits(int M, int N, int K) {
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   const bool bf = g.bf16;
+  if (big_nt(g) && !getenv("PARARNN_SMALL_GEMM"))
+    return g.out_f32 ? gemm_big_launch<float>(g, s) : gemm_big_launch<uint16_t>(g, s);
 #define PR_G(AKC, BKC)                                                                        \
   if (g.a_kc == AKC && g.b_kc == BKC) {                                                       \
     if (bf) return g.out_f32 ? gemm_launch<uint16_t, AKC, BKC, float>(g, s)                   \

@@ -188,3 +188,18 @@ def test_adjoint_bf16_reduced(cfg):
     torch.cuda.synchronize()
     assert st == bd.PR_OK
     adjoint_compare(p, to64(dp.h), a, True)
+
+
+@pytest.mark.parametrize("cell", [sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG])
+@pytest.mark.parametrize("B,T,d,n", [(3, 704, 264, 304), (1, 512, 512, 256)])
+def test_bf16_large_products(cell, B, T, d, n):
+    """Shapes that take the 256 x 256-tile bf16 products in all three places
+    (input projection with bias, dx = dU W_x, dW_x = dU^T x), with ragged
+    row, column and K tails (first case) and exact tile multiples (second)."""
+    p = sy.custom_problem(cell, B=B, T=T, d=d, n=n, seed=T + n, w_scale=0.8, h0=True, dtype=sy.DT_BF16)
+    say("large-product case", p["name"], "B", B, "T", T, "d", d, "n", n)
+    dp, h = check_solve(p, 0.0, 3, True)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_compare(p, h, a, True)
