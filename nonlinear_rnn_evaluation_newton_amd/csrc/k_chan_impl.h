@@ -15,8 +15,39 @@
 
 #include "cells_chan.h"
 #include "internal.h"
+#include "pipe.h"  // buffer-resource loads and stores
 
 namespace pr {
+
+// Packed buffer loads: BYTES (2, 4, 8 or 16) into 32-bit words as stored (a
+// 2-byte value in the low half); out-of-range offsets read zero.  A tile's
+// loads are issued together, unconditionally, so they are all in flight
+// before the first one is waited for.
+template <int BYTES>
+__device__ inline void bldw(Rsrc r, unsigned off, unsigned *w) {
+  if constexpr (BYTES == 2) {
+    w[0] = ld_u16(r, off);
+  } else if constexpr (BYTES == 4) {
+    w[0] = ld_u32(r, off);
+  } else if constexpr (BYTES == 8) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = u.x; w[1] = u.y;
+  } else {
+    static_assert(BYTES == 16, "unsupported access width");
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+  }
+}
+// value i of packed words w (storage type ST)
+template <typename ST>
+__device__ inline float unpackw(const unsigned *w, int i) {
+  if constexpr (sizeof(ST) == 2) return __uint_as_float((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+  else return __uint_as_float(w[i]);
+}
+template <typename ST, int CNT>
+constexpr int words_of() {
+  return (CNT * (int)sizeof(ST) + 3) / 4;
+}
 
 template <typename ST, int CNT>
 __device__ inline void ld_vec(const ST *p, float *out) {
@@ -309,43 +340,50 @@ __global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
         }
       }
     }
-    float Jv[TW][CPL][SW * SW], rv[TW][CPL][SW], hv[TW][CPL][SW];
+    // Every input of the wavefront's TW steps is requested before the first
+    // is used: buffer loads on the tile's rows (rows past T lie outside the
+    // resource and read zero, as does the iterate of sweep 1, h = 0).
+    constexpr int ES = (int)sizeof(ST), UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>();
+    const int r0 = j * TT, nrows = min(TT, T - r0);
+    const Rsrc ru = sc_rsrc(U + ((size_t)b * T + r0) * 3 * n, (unsigned)(nrows * 3 * n * ES));
+    const Rsrc rh = sc_rsrc(k >= 2 ? H + ((size_t)b * T + r0) * S : nullptr, (unsigned)(nrows * S * ES));
+    unsigned uw[TW][3][UW], hw[TW][HW];
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int tr = wid * TW + s;  // row within the tile
+#pragma unroll
+      for (int g = 0; g < 3; g++)
+        bldw<CPL * ES>(ru, active ? (unsigned)((tr * 3 * n + g * n + c0) * ES) : SC_OOB, uw[s][g]);
+      bldw<CPL * SW * ES>(rh, active ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, hw[s]);
+    }
+    float Jv[TW][CPL][SW * SW], rv[TW][CPL][SW];
     Op<SW> agg[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
 #pragma unroll
     for (int s = 0; s < TW; s++) {
-      const int t = t0 + s;
-      const bool valid = active && t < T;
-      float hc[CPL * SW], u0[CPL], u1[CPL], u2[CPL];
-      if (valid) {
-        const size_t row = (size_t)b * T + t;
-        if (k >= 2) ld_vec<ST, CPL * SW>(H + row * S + (size_t)c0 * SW, hc);
-        else {
+      // steps past T (and idle lanes) take the identity element J = I, r = 0
+      const bool valid = active && t0 + s < T;
 #pragma unroll
-          for (int i = 0; i < CPL * SW; i++) hc[i] = 0.f;
-        }
-        ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
-        ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
-        ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
+      for (int c = 0; c < CPL; c++) {
+        const float Uc[3] = {unpackw<ST>(uw[s][0], c), unpackw<ST>(uw[s][1], c), unpackw<ST>(uw[s][2], c)};
+        float f[SW], J[SW * SW];
+        chan_cell<CELL>(sp + c * SW, Uc, w[c], f, J);
+        Op<SW> e;
 #pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          float Uc[3] = {u0[c], u1[c], u2[c]}, f[SW];
-          chan_cell<CELL>(sp + c * SW, Uc, w[c], f, Jv[s][c]);
-          Op<SW> e;
-#pragma unroll
-          for (int i = 0; i < SW; i++) {
-            hv[s][c][i] = hc[c * SW + i];
-            rv[s][c][i] = f[i] - hc[c * SW + i];
-            e.b[i] = rv[s][c][i];
-          }
-#pragma unroll
-          for (int i = 0; i < SW * SW; i++) e.A[i] = Jv[s][c][i];
-          agg[c] = compose(e, agg[c]);
+        for (int i = 0; i < SW; i++) {
+          rv[s][c][i] = valid ? f[i] - unpackw<ST>(hw[s], c * SW + i) : 0.f;
+          e.b[i] = rv[s][c][i];
         }
 #pragma unroll
-        for (int i = 0; i < CPL * SW; i++) sp[i] = hc[i];
+        for (int i = 0; i < SW * SW; i++) {
+          Jv[s][c][i] = valid ? J[i] : ((i % (SW + 1)) == 0 ? 1.f : 0.f);
+          e.A[i] = Jv[s][c][i];
+        }
+        agg[c] = compose(e, agg[c]);
       }
+#pragma unroll
+      for (int i = 0; i < CPL * SW; i++) sp[i] = unpackw<ST>(hw[s], i);
     }
     Op<SW> pre[CPL], tot[CPL];
     chan_combine<SW, CPL>(agg, pre, tot, s_agg);
@@ -380,7 +418,7 @@ __global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
 #pragma unroll
           for (int i = 0; i < SW; i++) {
             dh[c][i] = nd[i];
-            hn[c * SW + i] = hv[s][c][i] + nd[i];
+            hn[c * SW + i] = unpackw<ST>(hw[s], c * SW + i) + nd[i];
             const unsigned u = __float_as_uint(fabsf(nd[i]));
             dmax = u > dmax ? u : dmax;
           }
@@ -551,17 +589,42 @@ __global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
     Op<SW> agg[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
+    // Every input of the wavefront's TW steps is requested before the first
+    // is used: buffer loads on the wavefront's rows [tlo, thi] (rows before
+    // t = 0 lie outside the resource and read zero).
+    constexpr int ES = (int)sizeof(ST), UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>();
+    const int rlo = tlo < 0 ? 0 : tlo, nr = thi - rlo + 1;  // rows of this wavefront in [0, T)
+    const size_t rbase = (size_t)b * T + rlo;
+    const Rsrc ru = sc_rsrc(U + rbase * 3 * n, nr > 0 ? (unsigned)(nr * 3 * n * ES) : 0u);
+    const Rsrc rhh = sc_rsrc(H + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
+    const Rsrc rg = sc_rsrc(Gr + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
+    unsigned uw[TW][3][UW], hw[TW][HW], gw[TW][HW];
+#pragma unroll
+    for (int s = 0; s < TW; s++) {
+      const int tr = thi - s - rlo;  // row within the wavefront's range (negative: before t = 0)
+      const bool in = active && tr >= 0;
+#pragma unroll
+      for (int g = 0; g < 3; g++)
+        bldw<CPL * ES>(ru, in ? (unsigned)((tr * 3 * n + g * n + c0) * ES) : SC_OOB, uw[s][g]);
+      bldw<CPL * SW * ES>(rhh, in ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, hw[s]);
+      bldw<CPL * SW * ES>(rg, in ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, gw[s]);
+    }
 #pragma unroll
     for (int s = 0; s < TW; s++) {
       const int t = thi - s;
       if (active && t >= 0) {
-        const size_t row = (size_t)b * T + t;
         float hc[CPL * SW], gc[CPL * SW], u0[CPL], u1[CPL], u2[CPL];
-        ld_vec<ST, CPL * SW>(H + row * S + (size_t)c0 * SW, hc);
-        ld_vec<ST, CPL * SW>(Gr + row * S + (size_t)c0 * SW, gc);
-        ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
-        ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
-        ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
+#pragma unroll
+        for (int i = 0; i < CPL * SW; i++) {
+          hc[i] = unpackw<ST>(hw[s], i);
+          gc[i] = unpackw<ST>(gw[s], i);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          u0[c] = unpackw<ST>(uw[s][0], c);
+          u1[c] = unpackw<ST>(uw[s][1], c);
+          u2[c] = unpackw<ST>(uw[s][2], c);
+        }
 #pragma unroll
         for (int c = 0; c < CPL; c++) {
           uv[s][c][0] = u0[c]; uv[s][c][1] = u1[c]; uv[s][c][2] = u2[c];

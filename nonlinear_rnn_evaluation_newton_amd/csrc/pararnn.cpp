@@ -159,6 +159,9 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->ntiles = pl->tps * pl->stripes;
     pl->ntiles_a = pl->tps_a * pl->stripes;
     const size_t es = p->dtype == PR_BF16 ? 2 : 4;
+    // a tile's rows of U are addressed with 31-bit byte offsets
+    if ((long long)(gf.TT > ga.TT ? gf.TT : ga.TT) * 3 * p->n * (long long)es >= (1LL << 31))
+      return fail(PR_EUNSUPPORTED, "channel count too large");
     const int SW = pl->SW, AW = SW * SW + SW;
     const size_t nt = (size_t)(pl->ntiles > pl->ntiles_a ? pl->ntiles : pl->ntiles_a);
     const size_t rows = (size_t)p->B * p->T;
