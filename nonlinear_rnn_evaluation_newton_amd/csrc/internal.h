@@ -87,6 +87,13 @@ struct ChanGeomInfo {
 };
 ChanGeomInfo chan_geom(int cell, int n, bool adjoint);
 hipError_t launch_chan_sweep(int cell, bool bf16, ChanArgs &a, hipStream_t s);
+// streaming sweep passes (no chain between tiles): tiles of CHAN2_TT steps,
+// one wavefront each; per sweep a carry scan then a pass that applies the
+// sweep and composes the next sweep's tile aggregates
+constexpr int CHAN2_TT = 64;
+enum { CHAN2_FIRST = 0, CHAN2_CARRY = 1, CHAN2_APPLY_NEXT = 2, CHAN2_APPLY = 3 };
+ChanGeomInfo chan2_geom(int cell, int n);
+hipError_t launch_chan2(int cell, bool bf16, const ChanArgs &a, int what, hipStream_t s);
 hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s);
 hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
                               hipStream_t s);

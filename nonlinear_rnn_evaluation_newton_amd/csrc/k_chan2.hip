@@ -1,0 +1,435 @@
+// Newton sweep of the per-channel cells (diagonal ParaGRU; CIFG/peephole
+// ParaLSTM with 2x2 blocks) as streaming passes with no chain between tiles.
+//
+// The sweep's linear recurrence dh_t = J_t dh_{t-1} + r_t (DEER summary,
+// Approach; Para-Seq README, Main features: diagonal and 2x2 block scans) is
+// solved tile by tile from per-tile carries, and the carries come from the
+// tiles' aggregates by a short scan.  The aggregates of sweep k + 1 depend
+// only on the iterate that sweep k writes, so the pass that applies sweep k
+// also composes them, step by step, right after it has written each new
+// state.  Per sweep:
+//
+//   k_chan_carry   the first step of every tile (whose linearisation point is
+//                  the previous tile's last state) is evaluated and composed
+//                  with the tile's partial aggregate; an exclusive scan over
+//                  each stripe's tiles gives the carries (dh entering a tile);
+//   k_chan_pass    each wavefront walks one tile (64 steps x 64*CPL channels)
+//                  serially: applies sweep k from its carry (cell, Jacobian,
+//                  residual, dh, h += dh, stores, max |dh|) and composes the
+//                  partial aggregate of sweep k + 1 at the new iterate.
+//
+// Before sweep 1 a pass composes the aggregates at the initial guess only.
+// The iterate is read once and written once per sweep, like a single-pass
+// scan, at the price of a second cell evaluation per step; no wavefront ever
+// waits for another, so there is no look-back latency and no co-residency
+// requirement.  Both sides of a tile boundary use the stored (rounded) state
+// of the previous tile's last step, so aggregates and updates agree exactly.
+#include "k_chan_impl.h"
+
+namespace pr {
+
+constexpr int C2_P = 4;                 // steps per load group (two groups in flight)
+constexpr int C2_NG = CHAN2_TT / C2_P;  // load groups per tile
+constexpr int C2_CW = 16;               // wavefronts per carry block
+constexpr int C2_R = 4;                 // tiles per carry chunk (their loads are issued together)
+
+// Store CNT values as ST (bf16: round to nearest even); out-of-range offsets
+// are dropped.
+template <typename ST, int CNT>
+__device__ inline void bst(Rsrc r, unsigned off, const float *in) {
+  constexpr int BYTES = CNT * (int)sizeof(ST);
+  auto word = [&](int i) -> unsigned {
+    if constexpr (sizeof(ST) == 2) return (unsigned)f2bf(in[2 * i]) | ((unsigned)f2bf(in[2 * i + 1]) << 16);
+    else return __float_as_uint(in[i]);
+  };
+  if constexpr (BYTES == 2) {
+    st_u16(r, off, f2bf(in[0]));
+  } else if constexpr (BYTES == 4) {
+    st_u32(r, off, word(0));
+  } else if constexpr (BYTES == 8) {
+    u32x2 v;
+    v.x = word(0); v.y = word(1);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  } else {
+    static_assert(BYTES == 16, "unsupported access width");
+    u32x4 v;
+    v.x = word(0); v.y = word(1); v.z = word(2); v.w = word(3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  }
+}
+
+// the value a float takes once stored as ST
+template <typename ST>
+__device__ inline float as_stored(float v) {
+  if constexpr (sizeof(ST) == 2) return bf2f(f2bf(v));
+  else return v;
+}
+
+// State before step t0 of tile L at iterate k - 1 (fp32, as stored; CPL
+// channels of SW values): h0 for the first tile, the previous tile's last
+// state kept by pass k - 1, or the initial guess 0.
+template <typename ST, int CPL, int SW, int CH>
+__device__ inline void state_before(const ChanArgs &a, int k, int t0, int b, int L, int c0, int lane, bool active,
+                                    float *s) {
+#pragma unroll
+  for (int i = 0; i < CPL * SW; i++) s[i] = 0.f;
+  if (!active) return;
+  if (t0 == 0) {
+    if (a.h0) {
+      const ST *p = (const ST *)a.h0 + (size_t)b * SW * a.n + (size_t)c0 * SW;
+#pragma unroll
+      for (int i = 0; i < CPL * SW; i++) s[i] = ldf(p, i);
+    }
+  } else if (k >= 2) {
+    const float *p = a.bnd + ((size_t)((k - 1) & 1) * a.ntiles + (L - 1)) * CH * SW + (size_t)lane * CPL * SW;
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) s[i] = p[i];
+  }
+}
+
+template <int CELL, typename ST, int CPL, bool APPLY, bool NEXT>
+__global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
+  constexpr int UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>(), TT = CHAN2_TT;
+  __shared__ int s_stop;
+  __shared__ unsigned s_dmax[4];
+  const int k = a.k;
+  if (APPLY && chan_stopped(a, &s_stop)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int tile = blockIdx.x * 4 + wid;
+  const int T = a.T, n = a.n, S = SW * n;
+  unsigned dmax = 0;
+  if (tile < a.ntiles) {
+    const int j = tile / a.stripes, stripe = tile % a.stripes;
+    const int CG = (n + CH - 1) / CH, b = stripe / CG;
+    const int c0 = (stripe % CG) * CH + lane * CPL;
+    const bool active = c0 < n;  // n is a multiple of CPL
+    const int L = stripe * a.tps + j, t0 = j * TT, nrows = min(TT, T - t0);
+    ChanW w[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+
+    // the tile's rows; the iterate is read from sweep 2 on (sweep 1 starts from 0)
+    const size_t row0 = (size_t)b * T + t0;
+    const Rsrc ru = sc_rsrc((const ST *)a.U + row0 * 3 * n, (unsigned)(nrows * 3 * n * ES));
+    const Rsrc rh = sc_rsrc((APPLY && k >= 2) ? (const ST *)a.h + row0 * S : nullptr, (unsigned)(nrows * S * ES));
+    const Rsrc rw = sc_rsrc((ST *)a.h + row0 * S, (unsigned)(nrows * S * ES));
+
+    float s_old[CPL * SW], s_new[CPL * SW], dh[CPL * SW];
+    Op<SW> agg[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
+    state_before<ST, CPL, SW, CH>(a, APPLY ? k : 1, t0, b, L, c0, lane, active, s_old);
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) {
+      s_new[i] = s_old[i];
+      dh[i] = 0.f;
+    }
+    if (APPLY && active) {
+      const float *cp = (const float *)a.incl + ((size_t)L * CH + lane * CPL) * SW;
+#pragma unroll
+      for (int i = 0; i < CPL * SW; i++) dh[i] = cp[i];
+    }
+
+    unsigned ua[C2_P][3][UW], ha[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW];
+    auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) {
+#pragma unroll
+      for (int q = 0; q < C2_P; q++) {
+        const int s = g * C2_P + q;  // rows past the tile (or past T) read zero
+        const bool in = active && s < TT;
+#pragma unroll
+        for (int gi = 0; gi < 3; gi++)
+          bldw<CPL * ES>(ru, in ? (unsigned)((s * 3 * n + gi * n + c0) * ES) : SC_OOB, u[q][gi]);
+        bldw<CPL * SW * ES>(rh, in ? (unsigned)((s * S + c0 * SW) * ES) : SC_OOB, h[q]);
+      }
+    };
+    auto steps = [&](int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW]) {
+#pragma unroll
+      for (int q = 0; q < C2_P; q++) {
+        const int s = g * C2_P + q;
+        const bool valid = active && s < nrows;
+        float hn[CPL * SW];
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          const float uc[3] = {unpackw<ST>(u[q][0], c), unpackw<ST>(u[q][1], c), unpackw<ST>(u[q][2], c)};
+          float hold[SW];
+#pragma unroll
+          for (int i = 0; i < SW; i++) hold[i] = unpackw<ST>(h[q], c * SW + i);
+          if constexpr (APPLY) {
+            // sweep k at this step: J, r at the old iterate, then the update
+            float f[SW], J[SW * SW], nd[SW];
+            chan_cell<CELL>(&s_old[c * SW], uc, w[c], f, J);
+#pragma unroll
+            for (int i = 0; i < SW; i++) {
+              float v = f[i] - hold[i];
+#pragma unroll
+              for (int m = 0; m < SW; m++) v = fmaf(J[i * SW + m], dh[c * SW + m], v);
+              nd[i] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < SW; i++) {
+              dh[c * SW + i] = nd[i];
+              hn[c * SW + i] = as_stored<ST>(hold[i] + nd[i]);
+              const unsigned ab = valid ? __float_as_uint(nd[i]) & 0x7fffffffu : 0u;
+              dmax = ab > dmax ? ab : dmax;
+              s_old[c * SW + i] = hold[i];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < SW; i++) hn[c * SW + i] = hold[i];
+          }
+          if constexpr (NEXT) {
+            // sweep k + 1 at this step (the tile's first step is composed by
+            // the carry kernel): J, r at the new iterate
+            if (s > 0) {
+              float f[SW], J[SW * SW];
+              chan_cell<CELL>(&s_new[c * SW], uc, w[c], f, J);
+              Op<SW> e;
+#pragma unroll
+              for (int i = 0; i < SW; i++) e.b[i] = valid ? f[i] - hn[c * SW + i] : 0.f;
+#pragma unroll
+              for (int i = 0; i < SW * SW; i++) e.A[i] = valid ? J[i] : ((i % (SW + 1)) == 0 ? 1.f : 0.f);
+              agg[c] = compose(e, agg[c]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < SW; i++) s_new[c * SW + i] = hn[c * SW + i];
+        }
+        if constexpr (APPLY) bst<ST, CPL * SW>(rw, valid ? (unsigned)((s * S + c0 * SW) * ES) : SC_OOB, hn);
+      }
+    };
+    load(0, ua, ha);
+    for (int g = 0; g < C2_NG; g += 2) {
+      load(g + 1, ub, hb);
+      steps(g, ua, ha);
+      load(g + 2, ua, ha);
+      steps(g + 1, ub, hb);
+    }
+    if (active) {
+      if constexpr (APPLY) {  // the tile's last state, as stored, for the next sweep's neighbour
+        if (nrows == TT) {
+          float *bp = a.bnd + ((size_t)(k & 1) * a.ntiles + L) * CH * SW + (size_t)lane * CPL * SW;
+#pragma unroll
+          for (int i = 0; i < CPL * SW; i++) bp[i] = s_new[i];
+        }
+      }
+      if constexpr (NEXT) {
+        float *pa = (float *)a.agg + ((size_t)L * CH + lane * CPL) * AW;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) pa[c * AW + i] = agg[c].A[i];
+#pragma unroll
+          for (int i = 0; i < SW; i++) pa[c * AW + SW * SW + i] = agg[c].b[i];
+        }
+      }
+    }
+  }
+  if constexpr (APPLY) {
+    dmax = wave_max_u32(dmax);
+    if (lane == 0) s_dmax[wid] = dmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned m = s_dmax[0];
+      for (int q = 1; q < 4; q++) m = s_dmax[q] > m ? s_dmax[q] : m;
+      max_agent(&a.st->dslot[k & 3][blockIdx.x % PR_DSHARDS], m);
+    }
+  }
+}
+
+// Carries of sweep k for one stripe (block), C2_CW wavefronts splitting its
+// tiles into contiguous ranges: the first-step element of each tile composed
+// under the tile's partial aggregate (written back as the full aggregate),
+// the range totals combined in LDS, then the exclusive prefix walked again.
+template <int CELL, typename ST, int CPL>
+__global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, TT = CHAN2_TT;
+  constexpr int R = C2_R;
+  __shared__ float s_tot[C2_CW][CH][AW];
+  __shared__ int s_skip;
+  const int k = a.k, lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // nothing to do once the previous sweep met the stop rule (its pass then
+  // records the stop)
+  if (threadIdx.x == 0) {
+    int skip = ld_agent(&a.st->stopped) != 0;
+    if (!skip && k >= 2) {
+      unsigned d = 0;
+      for (int i = 0; i < PR_DSHARDS; i++) {
+        const unsigned v = ld_agent(&a.st->dslot[(k - 1) & 3][i]);
+        d = v > d ? v : d;
+      }
+      int status;
+      skip = stop_rule(__uint_as_float(d), k - 1, a.tol, a.T, a.max_iters, &status) ? 1 : 0;
+    }
+    s_skip = skip;
+  }
+  __syncthreads();
+  if (s_skip) return;
+  const int T = a.T, n = a.n, S = SW * n, stripe = blockIdx.x;
+  const int CG = (n + CH - 1) / CH, b = stripe / CG;
+  const int c0 = (stripe % CG) * CH + lane * CPL;
+  const bool active = c0 < n;
+  const int nt = a.tps, per = (nt + C2_CW - 1) / C2_CW;
+  const int j0 = min(nt, wid * per), j1 = min(nt, j0 + per);
+  ChanW w[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+  const ST *U = (const ST *)a.U, *H = (const ST *)a.h;
+  float *pagg = (float *)a.agg;
+  float *carry = (float *)a.incl;
+
+  Op<SW> tot[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) tot[c] = op_identity<SW>();
+  for (int jc = j0; jc < j1; jc += R) {
+    float u[R][CPL][3], hc[R][CPL * SW], sb[R][CPL * SW], pg[R][CPL][AW];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int j = jc + r, L = stripe * nt + j, t0 = j * TT;
+      const bool in = active && j < j1;
+      const size_t row = (size_t)b * T + (in ? t0 : 0);
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int gi = 0; gi < 3; gi++) u[r][c][gi] = in ? ldf(U, row * 3 * n + (size_t)gi * n + c0 + c) : 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL * SW; i++) hc[r][i] = (in && k >= 2) ? ldf(H, row * S + (size_t)c0 * SW + i) : 0.f;
+      state_before<ST, CPL, SW, CH>(a, k, in ? t0 : 0, b, L, c0, lane, in, sb[r]);
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int i = 0; i < AW; i++) pg[r][c][i] = in ? pagg[((size_t)L * CH + lane * CPL + c) * AW + i] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int j = jc + r, L = stripe * nt + j;
+      if (!(active && j < j1)) continue;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        float f[SW], J[SW * SW];
+        chan_cell<CELL>(&sb[r][c * SW], u[r][c], w[c], f, J);
+        Op<SW> e, p;
+#pragma unroll
+        for (int i = 0; i < SW * SW; i++) {
+          e.A[i] = J[i];
+          p.A[i] = pg[r][c][i];
+        }
+#pragma unroll
+        for (int i = 0; i < SW; i++) {
+          e.b[i] = f[i] - hc[r][c * SW + i];
+          p.b[i] = pg[r][c][SW * SW + i];
+        }
+        const Op<SW> full = compose(p, e);
+        float *pa = pagg + ((size_t)L * CH + lane * CPL + c) * AW;
+#pragma unroll
+        for (int i = 0; i < SW * SW; i++) pa[i] = full.A[i];
+#pragma unroll
+        for (int i = 0; i < SW; i++) pa[SW * SW + i] = full.b[i];
+        tot[c] = compose(full, tot[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+#pragma unroll
+    for (int i = 0; i < SW * SW; i++) s_tot[wid][lane * CPL + c][i] = tot[c].A[i];
+#pragma unroll
+    for (int i = 0; i < SW; i++) s_tot[wid][lane * CPL + c][SW * SW + i] = tot[c].b[i];
+  }
+  __syncthreads();
+  float cur[CPL][SW];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+#pragma unroll
+    for (int i = 0; i < SW; i++) cur[c][i] = 0.f;
+    for (int v = 0; v < wid; v++) {
+      Op<SW> o;
+      const float *q = s_tot[v][lane * CPL + c];
+#pragma unroll
+      for (int i = 0; i < SW * SW; i++) o.A[i] = q[i];
+#pragma unroll
+      for (int i = 0; i < SW; i++) o.b[i] = q[SW * SW + i];
+      float y[SW];
+      op_apply(o, cur[c], y);
+#pragma unroll
+      for (int i = 0; i < SW; i++) cur[c][i] = y[i];
+    }
+  }
+  if (!active) return;
+  for (int jc = j0; jc < j1; jc += R) {
+    float pg[R][CPL][AW];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int j = jc + r, L = stripe * nt + j;
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+#pragma unroll
+        for (int i = 0; i < AW; i++) pg[r][c][i] = j < j1 ? pagg[((size_t)L * CH + lane * CPL + c) * AW + i] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int j = jc + r, L = stripe * nt + j;
+      if (j >= j1) continue;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        float *cp = carry + ((size_t)L * CH + lane * CPL + c) * SW;
+#pragma unroll
+        for (int i = 0; i < SW; i++) cp[i] = cur[c][i];
+        Op<SW> o;
+#pragma unroll
+        for (int i = 0; i < SW * SW; i++) o.A[i] = pg[r][c][i];
+#pragma unroll
+        for (int i = 0; i < SW; i++) o.b[i] = pg[r][c][SW * SW + i];
+        float y[SW];
+        op_apply(o, cur[c], y);
+#pragma unroll
+        for (int i = 0; i < SW; i++) cur[c][i] = y[i];
+      }
+    }
+  }
+}
+
+ChanGeomInfo chan2_geom(int cell, int n) {
+  ChanGeomInfo g;
+  g.CPL = (cell == C_GRU_DIAG && n % 2 == 0) ? 2 : 1;
+  g.TW = CHAN2_TT;
+  g.CH = 64 * g.CPL;
+  g.TT = CHAN2_TT;
+  return g;
+}
+
+template <int CELL, typename ST, int CPL>
+static hipError_t chan2_launch(const ChanArgs &a, int what, hipStream_t s) {
+  const unsigned pass_grid = (unsigned)((a.ntiles + 3) / 4);
+  switch (what) {
+    case CHAN2_FIRST:
+      hipLaunchKernelGGL((k_chan_pass<CELL, ST, CPL, false, true>), dim3(pass_grid), dim3(256), 0, s, a);
+      break;
+    case CHAN2_CARRY:
+      hipLaunchKernelGGL((k_chan_carry<CELL, ST, CPL>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
+      break;
+    case CHAN2_APPLY_NEXT:
+      hipLaunchKernelGGL((k_chan_pass<CELL, ST, CPL, true, true>), dim3(pass_grid), dim3(256), 0, s, a);
+      break;
+    case CHAN2_APPLY:
+      hipLaunchKernelGGL((k_chan_pass<CELL, ST, CPL, true, false>), dim3(pass_grid), dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_chan2(int cell, bool bf16, const ChanArgs &a, int what, hipStream_t s) {
+  const ChanGeomInfo g = chan2_geom(cell, a.n);
+  if (cell == C_GRU_DIAG) {
+    if (g.CPL == 2)
+      return bf16 ? chan2_launch<C_GRU_DIAG, uint16_t, 2>(a, what, s) : chan2_launch<C_GRU_DIAG, float, 2>(a, what, s);
+    return bf16 ? chan2_launch<C_GRU_DIAG, uint16_t, 1>(a, what, s) : chan2_launch<C_GRU_DIAG, float, 1>(a, what, s);
+  }
+  if (cell == C_LSTM)
+    return bf16 ? chan2_launch<C_LSTM, uint16_t, 1>(a, what, s) : chan2_launch<C_LSTM, float, 1>(a, what, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pr

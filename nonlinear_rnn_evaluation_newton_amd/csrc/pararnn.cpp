@@ -46,6 +46,8 @@ struct Plan {
   int scalar_ok = 0, tps_s = 0, ntiles_s = 0, tps_sa = 0, ntiles_sa = 0;
   // channel path: stripes (sequence x channel group), tiles of sweep / adjoint
   int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
+  // channel path, streaming sweep passes (tiles of CHAN2_TT steps)
+  int tps_2 = 0, ntiles_2 = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
   size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
@@ -160,17 +162,23 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->ntiles_a = pl->tps_a * pl->stripes;
     const size_t es = p->dtype == PR_BF16 ? 2 : 4;
     // a tile's rows of U are addressed with 31-bit byte offsets
-    if ((long long)(gf.TT > ga.TT ? gf.TT : ga.TT) * 3 * p->n * (long long)es >= (1LL << 31))
+    const int ttmax = gf.TT > ga.TT ? (gf.TT > CHAN2_TT ? gf.TT : CHAN2_TT) : (ga.TT > CHAN2_TT ? ga.TT : CHAN2_TT);
+    if ((long long)ttmax * 3 * p->n * (long long)es >= (1LL << 31))
       return fail(PR_EUNSUPPORTED, "channel count too large");
+    pl->tps_2 = (p->T + CHAN2_TT - 1) / CHAN2_TT;
+    if ((long long)pl->tps_2 * pl->stripes > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
+    pl->ntiles_2 = pl->tps_2 * pl->stripes;
     const int SW = pl->SW, AW = SW * SW + SW;
-    const size_t nt = (size_t)(pl->ntiles > pl->ntiles_a ? pl->ntiles : pl->ntiles_a);
+    size_t nt = (size_t)(pl->ntiles > pl->ntiles_a ? pl->ntiles : pl->ntiles_a);
+    if ((size_t)pl->ntiles_2 > nt) nt = (size_t)pl->ntiles_2;
+    const size_t nt_sweep = (size_t)(pl->ntiles > pl->ntiles_2 ? pl->ntiles : pl->ntiles_2);
     const size_t rows = (size_t)p->B * p->T;
     size_t o = 0;
     pl->off_state = o; o = align256(o + sizeof(SolveState));
     pl->off_agg = o; o = align256(o + nt * gf.CH * AW * 8);
     pl->off_incl = o; o = align256(o + nt * gf.CH * SW * 8);
     pl->zero_bytes = o;
-    pl->off_bnd = o; o = align256(o + (size_t)2 * pl->ntiles * gf.CH * SW * 4);
+    pl->off_bnd = o; o = align256(o + (size_t)2 * nt_sweep * gf.CH * SW * 4);
     pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
     pl->solve_bytes = o;
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
@@ -446,6 +454,13 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     HIPCHK(launch_scalar_coef(a, kc, (float *)(ws + pl.off_coef), s));
   }
 
+  // channel cells: streaming passes unless the look-back sweep is asked for
+  const bool chan2 = pl.path == PATH_CHAN && !getenv("PARARNN_CHAN_LOOKBACK");
+  if (chan2) {
+    ca.tps = pl.tps_2;
+    ca.ntiles = pl.ntiles_2;
+  }
+
   int first, next;
   poll_schedule(&first, &next);
   if (tol <= 0.f) first = kmax;
@@ -481,6 +496,13 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
         HIPCHK(launch_d64_sweep_part(da, 1, s));
         if (ev) HIPCHK(hipEventRecord(tr.swa[2 * (kk - 1) + 1], s));
         HIPCHK(launch_d64_sweep_part(da, 2, s));
+      } else if (chan2) {
+        ca.k = kk;
+        const bool bf = p->dtype == PR_BF16;
+        if (kk == 1) HIPCHK(launch_chan2(kc, bf, ca, CHAN2_FIRST, s));
+        HIPCHK(launch_chan2(kc, bf, ca, CHAN2_CARRY, s));
+        // the last possible sweep composes no aggregates for a next one
+        HIPCHK(launch_chan2(kc, bf, ca, kk == kmax ? CHAN2_APPLY : CHAN2_APPLY_NEXT, s));
       } else {
         ca.k = kk;
         HIPCHK(launch_chan_sweep(kc, p->dtype == PR_BF16, ca, s));
