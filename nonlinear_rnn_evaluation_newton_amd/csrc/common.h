@@ -102,12 +102,8 @@ __device__ inline bool desc_get(const unsigned long long *p, unsigned tag, float
 // storage conversion
 // ---------------------------------------------------------------------------
 __device__ inline float bf2f(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
-__device__ inline uint16_t f2bf(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ inline uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ inline float ldf(const float *p, size_t i) { return p[i]; }
 __device__ inline float ldf(const uint16_t *p, size_t i) { return bf2f(p[i]); }
 __device__ inline void stf(float *p, size_t i, float v) { p[i] = v; }

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
   __shared__ unsigned s_dmax[4];
   const int k = a.k;
   if (APPLY && chan_stopped(a, &s_stop)) return;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = blockIdx.x * 4 + wid;
   const int T = a.T, n = a.n, S = SW * n;
   unsigned dmax = 0;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
   constexpr int R = C2_R;
   __shared__ float s_tot[C2_CW][CH][AW];
   __shared__ int s_skip;
-  const int k = a.k, lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = a.k, lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // nothing to do once the previous sweep met the stop rule (its pass then
   // records the stop)
   if (threadIdx.x == 0) {

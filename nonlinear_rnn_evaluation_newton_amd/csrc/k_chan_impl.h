@@ -122,7 +122,7 @@ template <int SW, int CPL>
 __device__ inline void chan_combine(const Op<SW> (&agg)[CPL], Op<SW> (&pre)[CPL], Op<SW> (&tot)[CPL],
                                     float *s_agg /*[4][64*CPL][SW*SW+SW]*/) {
   constexpr int AW = SW * SW + SW, CH = 64 * CPL;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int c = 0; c < CPL; c++) {
     float *d = s_agg + ((size_t)wid * CH + lane * CPL + c) * AW;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
   __shared__ float s_carry[CH * SW];
   __shared__ int s_stop;
   __shared__ unsigned s_dmax[4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, k = a.k;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6), k = a.k;
   const int T = a.T, n = a.n, S = SW * n;
   if (chan_stopped(a, &s_stop)) return;
   const int CG = (n + CH - 1) / CH;
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void k_chan_scan(const ChanArgs a) {
   constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
   __shared__ float s_agg[4 * CH * AW];
   __shared__ float s_carry[CH * SW];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, n = a.n, S = SW * n;
   const int CG = (n + CH - 1) / CH;
   for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
   __shared__ float s_agg[4 * CH * AW];
   __shared__ float s_carry[CH * SW];
   __shared__ float s_red[4 * CH * CHAN_P];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, n = a.n, S = SW * n;
   const int CG = (n + CH - 1) / CH;
   const ST *U = (const ST *)a.U, *H = (const ST *)a.h, *Gr = (const ST *)a.g, *H0 = (const ST *)a.h0;

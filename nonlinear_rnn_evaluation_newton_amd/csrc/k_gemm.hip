@@ -214,12 +214,22 @@ __device__ inline GRsrc g_rsrc(const void *base, unsigned bytes) {
 }
 typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef PR_GEMM_WGM
+#define PR_GEMM_WGM 2
+#define PR_GEMM_WGN 4
+#endif
+// wavefront grid WGM x WGN over the 256 x 256 tile; each wavefront holds
+// FM x FN MFMA tiles of 32 x 32
+constexpr int WGM = PR_GEMM_WGM, WGN = PR_GEMM_WGN, FM = BT / 32 / WGM, FN = BT / 32 / WGN;
+constexpr int GT = 64 * WGM * WGN;  // threads per block
+constexpr int GQ = BT * (BK / 8) / GT;  // 16-byte staging chunks per operand per thread
+
 template <typename TO>
-__global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BT * BLD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BT * BLD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 2, wn = wid & 3;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int tiles = tiles_m * tiles_n;
   int id = blockIdx.x;
   if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
@@ -237,18 +247,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int t
   const GRsrc ra = g_rsrc(A, (unsigned)(min(BT, g.M - m0) * g.lda * 2));
   const GRsrc rb = g_rsrc(B, (unsigned)(min(BT, g.N - n0) * g.ldb * 2));
 
-  // staging: 4 chunks of 8 K-consecutive elements per operand per thread
-  int srow[4], skc[4];
+  // staging: GQ chunks of 8 K-consecutive elements per operand per thread
+  int srow[GQ], skc[GQ];
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int e = tid + q * 512;
+  for (int q = 0; q < GQ; q++) {
+    const int e = tid + q * GT;
     srow[q] = e >> 3;
     skc[q] = (e & 7) * 8;
   }
-  gu32x4 va[4], vb[4];
+  gu32x4 va[GQ], vb[GQ];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
+    for (int q = 0; q < GQ; q++) {
       const bool in = k0 + skc[q] < ke;
       va[q] = __builtin_amdgcn_raw_buffer_load_b128(
           ra, in ? (unsigned)(srow[q] * g.lda + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
@@ -258,17 +268,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int t
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
+    for (int q = 0; q < GQ; q++) {
       *reinterpret_cast<gu32x4 *>(&sA[buf][srow[q] * BLD + skc[q]]) = va[q];
       *reinterpret_cast<gu32x4 *>(&sB[buf][srow[q] * BLD + skc[q]]) = vb[q];
     }
   };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[FN][FM];
 #pragma unroll
-  for (int j = 0; j < 2; j++)
+  for (int j = 0; j < FN; j++)
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < FM; i++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[j][i][r] = 0.f;
 
@@ -278,22 +288,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int t
     lstore(0);
   }
   __syncthreads();
-  const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), kl = (lane >> 5) * 8;
+  const int arow = wm * (FM * 32) + (lane & 31), brow = wn * (FN * 32) + (lane & 31), kl = (lane >> 5) * 8;
   for (int k0 = kb; k0 < ke; k0 += BK) {
     const bool more = k0 + BK < ke;
     if (more) gload(k0 + BK);
     const uint16_t *cA = sA[buf], *cB = sB[buf];
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8_t a[4], b[2];
+      bf16x8_t a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
+      for (int i = 0; i < FM; i++) a[i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
 #pragma unroll
-      for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+      for (int j = 0; j < FN; j++) b[j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
 #pragma unroll
-      for (int j = 0; j < 2; j++)
+      for (int j = 0; j < FN; j++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+        for (int i = 0; i < FM; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
     }
     if (more) lstore(buf ^ 1);
     __syncthreads();
@@ -304,14 +314,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_nt(const GemmArgs g, int t
   // registers, the 4 adjacent columns 8 * (r / 4) + 4 * (lane / 32) + (0..3)
   const bool vec_c = g.splits == 1 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < FM; i++) {
+    const int m = m0 + wm * (FM * 32) + i * 32 + (lane & 31);
     if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < FN; j++)
 #pragma unroll
       for (int rg = 0; rg < 4; rg++) {
-        const int n = n0 + wn * 64 + j * 32 + 8 * rg + 4 * (lane >> 5);
+        const int n = n0 + wn * (FN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
         if (n >= g.N) continue;
         float v[4];
 #pragma unroll
@@ -355,7 +365,7 @@ static bool big_nt(const GemmArgs &g) {
 template <typename TO>
 static hipError_t gemm_big_launch(const GemmArgs &g, hipStream_t s) {
   const int tm = (g.M + BT - 1) / BT, tn = (g.N + BT - 1) / BT;
-  hipLaunchKernelGGL((k_gemm_bf16_nt<TO>), dim3(tm * tn, g.splits), dim3(512), 0, s, g, tm, tn);
+  hipLaunchKernelGGL((k_gemm_bf16_nt<TO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
   if (g.splits > 1) {
     const size_t tot = (size_t)g.M * g.N;
     hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
