@@ -71,19 +71,16 @@ __device__ inline float as_stored(float v) {
 template <typename ST, int CPL, int SW, int CH>
 __device__ inline void state_before(const ChanArgs &a, int k, int t0, int b, int L, int c0, int lane, bool active,
                                     float *s) {
+  // both candidate loads are issued unconditionally (from valid addresses),
+  // then one is selected
+  const bool from_h0 = t0 == 0 && a.h0 != nullptr, from_bnd = t0 > 0 && k >= 2;
+  const float *bp =
+      a.bnd + ((size_t)((k - 1) & 1) * a.ntiles + (from_bnd ? L - 1 : 0)) * CH * SW + (size_t)lane * CPL * SW;
+  const ST *hp = from_h0 ? (const ST *)a.h0 + (size_t)b * SW * a.n + (size_t)(active ? c0 : 0) * SW : (const ST *)a.Wh;
 #pragma unroll
-  for (int i = 0; i < CPL * SW; i++) s[i] = 0.f;
-  if (!active) return;
-  if (t0 == 0) {
-    if (a.h0) {
-      const ST *p = (const ST *)a.h0 + (size_t)b * SW * a.n + (size_t)c0 * SW;
-#pragma unroll
-      for (int i = 0; i < CPL * SW; i++) s[i] = ldf(p, i);
-    }
-  } else if (k >= 2) {
-    const float *p = a.bnd + ((size_t)((k - 1) & 1) * a.ntiles + (L - 1)) * CH * SW + (size_t)lane * CPL * SW;
-#pragma unroll
-    for (int i = 0; i < CPL * SW; i++) s[i] = p[i];
+  for (int i = 0; i < CPL * SW; i++) {
+    const float vb = bp[i], vh = ldf(hp, i);
+    s[i] = !active ? 0.f : from_bnd ? vb : from_h0 ? vh : 0.f;
   }
 }
 
@@ -125,22 +122,24 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
       s_new[i] = s_old[i];
       dh[i] = 0.f;
     }
-    if (APPLY && active) {
+    if constexpr (APPLY) {
       const float *cp = (const float *)a.incl + ((size_t)L * CH + lane * CPL) * SW;
 #pragma unroll
       for (int i = 0; i < CPL * SW; i++) dh[i] = cp[i];
     }
 
+    // Offsets carry bit 31 for idle lanes (outside every resource); rows past
+    // the tile or past T lie outside the tile's resources.  No selects or
+    // branches sit between the loads, so they all stay in flight.
+    const unsigned lane_oob = active ? 0u : SC_OOB;
     unsigned ua[C2_P][3][UW], ha[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW];
     auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) {
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
-        const int s = g * C2_P + q;  // rows past the tile (or past T) read zero
-        const bool in = active && s < TT;
+        const int s = g * C2_P + q;
 #pragma unroll
-        for (int gi = 0; gi < 3; gi++)
-          bldw<CPL * ES>(ru, in ? (unsigned)((s * 3 * n + gi * n + c0) * ES) : SC_OOB, u[q][gi]);
-        bldw<CPL * SW * ES>(rh, in ? (unsigned)((s * S + c0 * SW) * ES) : SC_OOB, h[q]);
+        for (int gi = 0; gi < 3; gi++) bldw<CPL * ES>(ru, (unsigned)((s * 3 * n + gi * n + c0) * ES) | lane_oob, u[q][gi]);
+        bldw<CPL * SW * ES>(rh, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, h[q]);
       }
     };
     auto steps = [&](int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW]) {
@@ -195,7 +194,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
 #pragma unroll
           for (int i = 0; i < SW; i++) s_new[c * SW + i] = hn[c * SW + i];
         }
-        if constexpr (APPLY) bst<ST, CPL * SW>(rw, valid ? (unsigned)((s * S + c0 * SW) * ES) : SC_OOB, hn);
+        if constexpr (APPLY) bst<ST, CPL * SW>(rw, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, hn);
       }
     };
     load(0, ua, ha);
@@ -250,18 +249,14 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
   const int k = a.k, lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // nothing to do once the previous sweep met the stop rule (its pass then
   // records the stop)
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {  // one shard of the previous sweep's measure per lane
     int skip = ld_agent(&a.st->stopped) != 0;
     if (!skip && k >= 2) {
-      unsigned d = 0;
-      for (int i = 0; i < PR_DSHARDS; i++) {
-        const unsigned v = ld_agent(&a.st->dslot[(k - 1) & 3][i]);
-        d = v > d ? v : d;
-      }
+      const unsigned d = wave_max_u32(ld_agent(&a.st->dslot[(k - 1) & 3][threadIdx.x]));
       int status;
       skip = stop_rule(__uint_as_float(d), k - 1, a.tol, a.T, a.max_iters, &status) ? 1 : 0;
     }
-    s_skip = skip;
+    if (threadIdx.x == 0) s_skip = skip;
   }
   __syncthreads();
   if (s_skip) return;
@@ -282,23 +277,28 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
 #pragma unroll
   for (int c = 0; c < CPL; c++) tot[c] = op_identity<SW>();
   for (int jc = j0; jc < j1; jc += R) {
+    // every load of the chunk is issued unconditionally (idle slots read a
+    // valid tile's data and are discarded), then used
     float u[R][CPL][3], hc[R][CPL * SW], sb[R][CPL * SW], pg[R][CPL][AW];
 #pragma unroll
     for (int r = 0; r < R; r++) {
-      const int j = jc + r, L = stripe * nt + j, t0 = j * TT;
-      const bool in = active && j < j1;
-      const size_t row = (size_t)b * T + (in ? t0 : 0);
+      const int jj = jc + r < j1 ? jc + r : j0, L = stripe * nt + jj, t0 = jj * TT;
+      const int cc = active ? c0 : 0;
+      const size_t row = (size_t)b * T + t0;
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll
-        for (int gi = 0; gi < 3; gi++) u[r][c][gi] = in ? ldf(U, row * 3 * n + (size_t)gi * n + c0 + c) : 0.f;
+        for (int gi = 0; gi < 3; gi++) u[r][c][gi] = ldf(U, row * 3 * n + (size_t)gi * n + cc + c);
+      state_before<ST, CPL, SW, CH>(a, k, t0, b, L, c0, lane, active, sb[r]);
 #pragma unroll
-      for (int i = 0; i < CPL * SW; i++) hc[r][i] = (in && k >= 2) ? ldf(H, row * S + (size_t)c0 * SW + i) : 0.f;
-      state_before<ST, CPL, SW, CH>(a, k, in ? t0 : 0, b, L, c0, lane, in, sb[r]);
+      for (int i = 0; i < CPL * SW; i++) {
+        const float v = ldf(H, row * S + (size_t)cc * SW + i);
+        hc[r][i] = k >= 2 ? v : 0.f;  // sweep 1 starts from h = 0
+      }
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll
-        for (int i = 0; i < AW; i++) pg[r][c][i] = in ? pagg[((size_t)L * CH + lane * CPL + c) * AW + i] : 0.f;
+        for (int i = 0; i < AW; i++) pg[r][c][i] = pagg[((size_t)L * CH + lane * CPL + c) * AW + i];
     }
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -360,11 +360,11 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
     float pg[R][CPL][AW];
 #pragma unroll
     for (int r = 0; r < R; r++) {
-      const int j = jc + r, L = stripe * nt + j;
+      const int L = stripe * nt + (jc + r < j1 ? jc + r : j0);
 #pragma unroll
       for (int c = 0; c < CPL; c++)
 #pragma unroll
-        for (int i = 0; i < AW; i++) pg[r][c][i] = j < j1 ? pagg[((size_t)L * CH + lane * CPL + c) * AW + i] : 0.f;
+        for (int i = 0; i < AW; i++) pg[r][c][i] = pagg[((size_t)L * CH + lane * CPL + c) * AW + i];
     }
 #pragma unroll
     for (int r = 0; r < R; r++) {

@@ -254,15 +254,20 @@ template <typename ST>
 __device__ inline ChanW load_chan_w(const ChanArgs &a, int c) {
   const ST *Wh = (const ST *)a.Wh, *bh = (const ST *)a.bh, *pp = (const ST *)a.peep;
   const int n = a.n;
+  // all eight loads unconditional (an absent vector reads W_h instead and is
+  // replaced by zeros), so they are in flight together
+  const ST *bq = bh ? bh : Wh, *pq = pp ? pp : Wh;
   ChanW w;
   w.a0 = ldf(Wh, c);
   w.a1 = ldf(Wh, (size_t)n + c);
   w.a2 = ldf(Wh, (size_t)2 * n + c);
-  w.b0 = bh ? ldf(bh, c) : 0.f;
-  w.b1 = bh ? ldf(bh, (size_t)n + c) : 0.f;
-  w.b2 = bh ? ldf(bh, (size_t)2 * n + c) : 0.f;
-  w.p0 = pp ? ldf(pp, c) : 0.f;
-  w.p1 = pp ? ldf(pp, (size_t)n + c) : 0.f;
+  const float b0 = ldf(bq, c), b1 = ldf(bq, (size_t)n + c), b2 = ldf(bq, (size_t)2 * n + c);
+  const float p0 = ldf(pq, c), p1 = ldf(pq, (size_t)n + c);
+  w.b0 = bh ? b0 : 0.f;
+  w.b1 = bh ? b1 : 0.f;
+  w.b2 = bh ? b2 : 0.f;
+  w.p0 = pp ? p0 : 0.f;
+  w.p1 = pp ? p1 : 0.f;
   return w;
 }
 

@@ -163,7 +163,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     const size_t es = p->dtype == PR_BF16 ? 2 : 4;
     // a tile's rows of U are addressed with 31-bit byte offsets
     const int ttmax = gf.TT > ga.TT ? (gf.TT > CHAN2_TT ? gf.TT : CHAN2_TT) : (ga.TT > CHAN2_TT ? ga.TT : CHAN2_TT);
-    if ((long long)ttmax * 3 * p->n * (long long)es >= (1LL << 31))
+    if ((long long)(2 * ttmax) * 3 * p->n * (long long)es >= (1LL << 31))
       return fail(PR_EUNSUPPORTED, "channel count too large");
     pl->tps_2 = (p->T + CHAN2_TT - 1) / CHAN2_TT;
     if ((long long)pl->tps_2 * pl->stripes > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
