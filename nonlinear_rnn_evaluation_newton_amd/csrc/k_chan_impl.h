@@ -353,13 +353,13 @@ __global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
     const Rsrc ru = sc_rsrc(U + ((size_t)b * T + r0) * 3 * n, (unsigned)(nrows * 3 * n * ES));
     const Rsrc rh = sc_rsrc(k >= 2 ? H + ((size_t)b * T + r0) * S : nullptr, (unsigned)(nrows * S * ES));
     unsigned uw[TW][3][UW], hw[TW][HW];
+    const unsigned lane_oob = active ? 0u : SC_OOB;  // idle lanes: outside every resource
 #pragma unroll
     for (int s = 0; s < TW; s++) {
       const int tr = wid * TW + s;  // row within the tile
 #pragma unroll
-      for (int g = 0; g < 3; g++)
-        bldw<CPL * ES>(ru, active ? (unsigned)((tr * 3 * n + g * n + c0) * ES) : SC_OOB, uw[s][g]);
-      bldw<CPL * SW * ES>(rh, active ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, hw[s]);
+      for (int g = 0; g < 3; g++) bldw<CPL * ES>(ru, (unsigned)((tr * 3 * n + g * n + c0) * ES) | lane_oob, uw[s][g]);
+      bldw<CPL * SW * ES>(rh, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, hw[s]);
     }
     float Jv[TW][CPL][SW * SW], rv[TW][CPL][SW];
     Op<SW> agg[CPL];
@@ -598,21 +598,24 @@ __global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
     // is used: buffer loads on the wavefront's rows [tlo, thi] (rows before
     // t = 0 lie outside the resource and read zero).
     constexpr int ES = (int)sizeof(ST), UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>();
-    const int rlo = tlo < 0 ? 0 : tlo, nr = thi - rlo + 1;  // rows of this wavefront in [0, T)
-    const size_t rbase = (size_t)b * T + rlo;
+    // rows of this wavefront in [0, T) (wavefront-uniform: the resources live in scalar registers)
+    const int rlo = __builtin_amdgcn_readfirstlane(tlo < 0 ? 0 : tlo);
+    const int nr = __builtin_amdgcn_readfirstlane(thi - rlo + 1);
+    const size_t rbase = (size_t)__builtin_amdgcn_readfirstlane(b) * T + rlo;
     const Rsrc ru = sc_rsrc(U + rbase * 3 * n, nr > 0 ? (unsigned)(nr * 3 * n * ES) : 0u);
     const Rsrc rhh = sc_rsrc(H + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
     const Rsrc rg = sc_rsrc(Gr + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
+    // idle lanes carry bit 31; rows before t = 0 give negative offsets,
+    // which wrap past every resource, so no select sits between the loads
+    const unsigned lane_oob = active ? 0u : SC_OOB;
     unsigned uw[TW][3][UW], hw[TW][HW], gw[TW][HW];
 #pragma unroll
     for (int s = 0; s < TW; s++) {
       const int tr = thi - s - rlo;  // row within the wavefront's range (negative: before t = 0)
-      const bool in = active && tr >= 0;
 #pragma unroll
-      for (int g = 0; g < 3; g++)
-        bldw<CPL * ES>(ru, in ? (unsigned)((tr * 3 * n + g * n + c0) * ES) : SC_OOB, uw[s][g]);
-      bldw<CPL * SW * ES>(rhh, in ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, hw[s]);
-      bldw<CPL * SW * ES>(rg, in ? (unsigned)((tr * S + c0 * SW) * ES) : SC_OOB, gw[s]);
+      for (int g = 0; g < 3; g++) bldw<CPL * ES>(ru, (unsigned)((tr * 3 * n + g * n + c0) * ES) | lane_oob, uw[s][g]);
+      bldw<CPL * SW * ES>(rhh, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, hw[s]);
+      bldw<CPL * SW * ES>(rg, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, gw[s]);
     }
 #pragma unroll
     for (int s = 0; s < TW; s++) {
