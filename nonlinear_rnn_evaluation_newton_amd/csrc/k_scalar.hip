@@ -331,6 +331,7 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
 
 // Members common to the scalar-state policies.
 struct ScBase {
+  static constexpr int WPE = 4;  // wavefronts per SIMD the register budget is sized for
   using Args = TimeArgs;
   using Shared = ScShared;
   using Tot = ScTot;
@@ -358,7 +359,10 @@ struct ScBase {
 // ---------------------------------------------------------------------------
 template <int CELL, bool FIRST>
 struct SweepPol : ScBase {
-  static constexpr int Q = 2, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
+  // long tiles (4 groups per wavefront, one block per CU): fewer look-back
+  // stages per sequence, which the chain of carries pays for one by one
+  static constexpr int WPE = 2;
+  static constexpr int Q = 4, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   // raw inputs of one tile: x and the current iterate h per group, and the
   // state before the wavefront's first step (zero when its resource is empty)
   struct Raw {
@@ -508,7 +512,8 @@ struct SweepPol : ScBase {
 // ---------------------------------------------------------------------------
 template <int CELL>
 struct AdjPol : ScBase {
-  static constexpr int Q = 1, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
+  static constexpr int WPE = 2;
+  static constexpr int Q = 2, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   struct Raw {
     float4 x[Q], h[Q], g[Q];
     float hp;   // h before the wavefront's earliest step (0 at t = 0: h0 is taken then)

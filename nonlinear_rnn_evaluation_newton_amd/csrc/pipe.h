@@ -9,7 +9,8 @@
 // lanes, so no load or store sits under a branch (see below).
 //
 // A policy type supplies the work of one tile (Raw inputs, computed Tile,
-// LDS, accumulators, constants, look-back) through static members; see
+// LDS, accumulators, constants, look-back) through static members, and
+// WPE, the wavefronts per SIMD its register budget is sized for; see
 // k_scalar.hip.
 #pragma once
 
@@ -113,7 +114,7 @@ __device__ inline void pipe_stage(const typename Pol::Args &a, const typename Po
 // grid cannot deadlock.  The two wavefront roles run separate loops with the
 // same number of barriers (tiles + 1).
 template <class Pol>
-__global__ __launch_bounds__(SC_THREADS, 4) void k_pipe(const typename Pol::Args a) {
+__global__ __launch_bounds__(SC_THREADS, Pol::WPE) void k_pipe(const typename Pol::Args a) {
   __shared__ typename Pol::Shared sh;
   __shared__ typename Pol::Lds lds;
   // the wavefront id through readfirstlane: the compiler then knows the role
