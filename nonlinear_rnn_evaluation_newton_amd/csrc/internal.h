@@ -94,6 +94,14 @@ constexpr int CHAN2_TT = 64;
 enum { CHAN2_FIRST = 0, CHAN2_CARRY = 1, CHAN2_APPLY_NEXT = 2, CHAN2_APPLY = 3 };
 ChanGeomInfo chan2_geom(int cell, int n);
 hipError_t launch_chan2(int cell, bool bf16, const ChanArgs &a, int what, hipStream_t s);
+// adjoint as streaming passes on the same tiles (aggregates, reverse carry
+// scan, apply); per-tile weight partials [tiles][CH][11]
+hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s);
+// weight gradients from per-tile partials: CHAN_RED_SPLITS fp64 partial sums
+// per (channel, slot) in `red`, then their sum in order
+constexpr int CHAN_RED_SPLITS = 32;
+hipError_t launch_chan_reduce_tiles(int cell, ChanArgs &a, double *red, float *dWh, float *dbh, float *dpeep,
+                                   float *dbx, hipStream_t s);
 hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s);
 hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
                               hipStream_t s);

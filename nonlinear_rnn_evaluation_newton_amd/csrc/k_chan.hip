@@ -77,6 +77,19 @@ hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, flo
   return hipGetLastError();
 }
 
+hipError_t launch_chan_reduce_tiles(int cell, ChanArgs &a, double *red, float *dWh, float *dbh, float *dpeep,
+                                   float *dbx, hipStream_t s) {
+  const ChanGeomInfo gi = chan2_geom(cell, a.n);
+  const unsigned blocks = (unsigned)((a.n * CHAN_P + 255) / 256);
+  if (gi.CH == 128)
+    hipLaunchKernelGGL((k_chan_red_split<128>), dim3(blocks, CHAN_RED_SPLITS), dim3(256), 0, s, a, red);
+  else
+    hipLaunchKernelGGL((k_chan_red_split<64>), dim3(blocks, CHAN_RED_SPLITS), dim3(256), 0, s, a, red);
+  hipLaunchKernelGGL(k_chan_red_final<CHAN_RED_SPLITS>, dim3(blocks), dim3(256), 0, s, a, (const double *)red, dWh,
+                     dbh, dpeep, dbx);
+  return hipGetLastError();
+}
+
 hipError_t launch_chan_scan(int SW, ChanArgs &a, hipStream_t s) {
   if (SW == 1 && a.n % 2 == 0) {
     const int grid = chan_grid<k_chan_scan<1, 2, 16>>(a, false);

@@ -389,6 +389,289 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Adjoint as streaming passes.  With mu_t = J_t^T lambda_t, the reverse
+// recurrence lambda_t = g_t + J_{t+1}^T lambda_{t+1} (lambda past the last
+// step is 0) becomes mu_t = J_t^T mu_{t+1} + J_t^T g_t, whose element at step
+// t needs only that step's inputs (h_{t-1}, U_t, g_t) -- the same ones the
+// cell's vector-Jacobian product at step t takes, which returns mu_t itself.
+//   k_chan_adj_pass<false>  each wavefront composes its tile's elements, top
+//                           step first, into the tile aggregate;
+//   k_chan_adj_carry        reverse exclusive scan: mu entering each tile
+//                           from the tile above (0 for the last tile);
+//   k_chan_adj_pass<true>   each wavefront walks its tile downwards from its
+//                           carry: lambda_t = g_t + mu_{t+1}, then the
+//                           cell's VJP gives mu_t, dU_t and the weight
+//                           partials; stores lambda, dU and dh0 = mu_0.
+// ---------------------------------------------------------------------------
+template <int CELL, typename ST, int CPL, bool APPLY>
+__global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
+  constexpr int UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>(), TT = CHAN2_TT;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x * 4 + wid;
+  if (tile >= a.ntiles) return;
+  const int T = a.T, n = a.n, S = SW * n;
+  const int j = tile / a.stripes, stripe = tile % a.stripes;
+  const int CG = (n + CH - 1) / CH, b = stripe / CG;
+  const int c0 = (stripe % CG) * CH + lane * CPL;
+  const bool active = c0 < n;
+  const int L = stripe * a.tps + j, t0 = j * TT, nrows = min(TT, T - t0);
+  const unsigned lane_oob = active ? 0u : SC_OOB;
+  ChanW w[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+
+  // rows of the tile: U_t and g_t at [t0, t0 + nrows); h_{t-1} from the row
+  // before (the first tile's step 0 takes h0 instead: its row offset is -1,
+  // outside the resource)
+  const size_t row0 = (size_t)b * T + t0;
+  const int hsh = t0 > 0 ? 0 : 1;  // h row of step s is s - hsh
+  const Rsrc ru = sc_rsrc((const ST *)a.U + row0 * 3 * n, (unsigned)(nrows * 3 * n * ES));
+  const Rsrc rg = sc_rsrc((const ST *)a.g + row0 * S, (unsigned)(nrows * S * ES));
+  const Rsrc rh = sc_rsrc((const ST *)a.h + (row0 - 1 + hsh) * S, (unsigned)((nrows - hsh) * S * ES));
+  float h0v[CPL * SW];
+  {
+    const ST *hp = (t0 == 0 && a.h0) ? (const ST *)a.h0 + (size_t)b * S + (size_t)(active ? c0 : 0) * SW
+                                     : (const ST *)a.Wh;
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) {
+      const float v = ldf(hp, i);
+      h0v[i] = (t0 == 0 && a.h0) ? v : 0.f;
+    }
+  }
+  float mu[CPL * SW];
+  Op<SW> agg[CPL];
+  float acc[CPL][CHAN_P];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    agg[c] = op_identity<SW>();
+#pragma unroll
+    for (int p = 0; p < CHAN_P; p++) acc[c][p] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < CPL * SW; i++) mu[i] = 0.f;
+  if constexpr (APPLY) {
+    const float *cp = (const float *)a.incl + ((size_t)L * CH + lane * CPL) * SW;
+#pragma unroll
+    for (int i = 0; i < CPL * SW; i++) mu[i] = cp[i];
+  }
+  const Rsrc rl = sc_rsrc(APPLY && a.lam ? (ST *)a.lam + row0 * S : nullptr, (unsigned)(nrows * S * ES));
+  const Rsrc rd = sc_rsrc(APPLY ? (ST *)a.dU + row0 * 3 * n : nullptr, (unsigned)(nrows * 3 * n * ES));
+
+  unsigned ua[C2_P][3][UW], ha[C2_P][HW], ga[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW], gb[C2_P][HW];
+  // group gi holds steps s = TT - 1 - (gi * C2_P + q), top step first
+  auto load = [&](int gi, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW], unsigned (&g)[C2_P][HW]) {
+#pragma unroll
+    for (int q = 0; q < C2_P; q++) {
+      const int s = TT - 1 - (gi * C2_P + q);  // negative past the tile: outside every resource
+#pragma unroll
+      for (int k3 = 0; k3 < 3; k3++) bldw<CPL * ES>(ru, (unsigned)((s * 3 * n + k3 * n + c0) * ES) | lane_oob, u[q][k3]);
+      bldw<CPL * SW * ES>(rh, (unsigned)(((s - hsh) * S + c0 * SW) * ES) | lane_oob, h[q]);
+      bldw<CPL * SW * ES>(rg, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, g[q]);
+    }
+  };
+  auto steps = [&](int gi, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW],
+                   const unsigned (&g)[C2_P][HW]) {
+#pragma unroll
+    for (int q = 0; q < C2_P; q++) {
+      const int s = TT - 1 - (gi * C2_P + q);
+      const bool valid = active && s < nrows;
+      float lo[CPL * SW], du[3][CPL], dso[CPL * SW];
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        const float uc[3] = {unpackw<ST>(u[q][0], c), unpackw<ST>(u[q][1], c), unpackw<ST>(u[q][2], c)};
+        float sp[SW], gc[SW];
+#pragma unroll
+        for (int i = 0; i < SW; i++) {
+          const float hv = unpackw<ST>(h[q], c * SW + i);
+          sp[i] = (t0 + s == 0) ? h0v[c * SW + i] : hv;
+          gc[i] = unpackw<ST>(g[q], c * SW + i);
+        }
+        if constexpr (!APPLY) {
+          // element (J^T, J^T g) of mu's recurrence, composed after the steps above
+          float f[SW], J[SW * SW];
+          chan_cell<CELL>(sp, uc, w[c], f, J);
+          Op<SW> e;
+#pragma unroll
+          for (int r = 0; r < SW; r++) {
+            float v = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < SW; q2++) {
+              e.A[r * SW + q2] = valid ? J[q2 * SW + r] : (r == q2 ? 1.f : 0.f);
+              v = fmaf(J[q2 * SW + r], gc[q2], v);
+            }
+            e.b[r] = valid ? v : 0.f;
+          }
+          agg[c] = compose(e, agg[c]);
+        } else {
+          float lam[SW], ds[SW], dU[3], tacc[CHAN_P];
+#pragma unroll
+          for (int i = 0; i < SW; i++) lam[i] = gc[i] + mu[c * SW + i];
+#pragma unroll
+          for (int p = 0; p < CHAN_P; p++) tacc[p] = 0.f;
+          chan_cell_vjp<CELL>(sp, uc, lam, w[c], ds, dU, tacc);
+          tacc[8] += dU[0];
+          tacc[9] += dU[1];
+          tacc[10] += dU[2];
+#pragma unroll
+          for (int p = 0; p < CHAN_P; p++) acc[c][p] += valid ? tacc[p] : 0.f;
+#pragma unroll
+          for (int i = 0; i < SW; i++) {
+            mu[c * SW + i] = valid ? ds[i] : mu[c * SW + i];
+            lo[c * SW + i] = lam[i];
+            dso[c * SW + i] = ds[i];
+          }
+#pragma unroll
+          for (int k3 = 0; k3 < 3; k3++) du[k3][c] = dU[k3];
+        }
+      }
+      if constexpr (APPLY) {
+        bst<ST, CPL * SW>(rl, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, lo);
+#pragma unroll
+        for (int k3 = 0; k3 < 3; k3++) bst<ST, CPL>(rd, (unsigned)((s * 3 * n + k3 * n + c0) * ES) | lane_oob, du[k3]);
+        if (t0 + s == 0 && a.dh0 && active) {
+#pragma unroll
+          for (int i = 0; i < CPL * SW; i++) stf((ST *)a.dh0 + (size_t)b * S + (size_t)c0 * SW + i, 0, dso[i]);
+        }
+      }
+    }
+  };
+  load(0, ua, ha, ga);
+  for (int gi = 0; gi < C2_NG; gi += 2) {
+    load(gi + 1, ub, hb, gb);
+    steps(gi, ua, ha, ga);
+    load(gi + 2, ua, ha, ga);
+    steps(gi + 1, ub, hb, gb);
+  }
+  if (!active) return;
+  if constexpr (!APPLY) {
+    float *pa = (float *)a.agg + ((size_t)L * CH + lane * CPL) * AW;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+#pragma unroll
+      for (int i = 0; i < SW * SW; i++) pa[c * AW + i] = agg[c].A[i];
+#pragma unroll
+      for (int i = 0; i < SW; i++) pa[c * AW + SW * SW + i] = agg[c].b[i];
+    }
+  } else {
+    float *pp = a.part + ((size_t)L * CH + lane * CPL) * CHAN_P;
+#pragma unroll
+    for (int c = 0; c < CPL; c++)
+#pragma unroll
+      for (int p = 0; p < CHAN_P; p++) pp[c * CHAN_P + p] = acc[c][p];
+  }
+}
+
+// Reverse exclusive scan of the tile aggregates of one stripe (block): mu
+// entering each tile from the tile above, C2_CW wavefronts over contiguous
+// ranges of tiles (loads of C2_R tiles issued together).
+template <int SW, int CPL>
+__global__ __launch_bounds__(64 * C2_CW) void k_chan_adj_carry(const ChanArgs a) {
+  constexpr int CH = 64 * CPL, AW = SW * SW + SW, R = C2_R;
+  __shared__ float s_tot[C2_CW][CH][AW];
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stripe = blockIdx.x, nt = a.tps, per = (nt + C2_CW - 1) / C2_CW;
+  // wavefront wid takes the wid-th range from the top
+  const int j1 = max(0, nt - wid * per), j0 = max(0, j1 - per);
+  const float *pagg = (const float *)a.agg;
+  float *carry = (float *)a.incl;
+  auto ld_op = [&](int j, int c) {
+    Op<SW> o;
+    const float *q = pagg + (((size_t)stripe * nt + j) * CH + lane * CPL + c) * AW;
+#pragma unroll
+    for (int i = 0; i < SW * SW; i++) o.A[i] = q[i];
+#pragma unroll
+    for (int i = 0; i < SW; i++) o.b[i] = q[SW * SW + i];
+    return o;
+  };
+  Op<SW> tot[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) tot[c] = op_identity<SW>();
+  for (int jc = j1 - 1; jc >= j0; jc -= R) {  // top tile of the range first
+    Op<SW> o[R][CPL];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+      for (int c = 0; c < CPL; c++) o[r][c] = ld_op(jc - r >= j0 ? jc - r : j0, c);
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+      for (int c = 0; c < CPL; c++)
+        if (jc - r >= j0) tot[c] = compose(o[r][c], tot[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+#pragma unroll
+    for (int i = 0; i < SW * SW; i++) s_tot[wid][lane * CPL + c][i] = tot[c].A[i];
+#pragma unroll
+    for (int i = 0; i < SW; i++) s_tot[wid][lane * CPL + c][SW * SW + i] = tot[c].b[i];
+  }
+  __syncthreads();
+  float cur[CPL][SW];
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+#pragma unroll
+    for (int i = 0; i < SW; i++) cur[c][i] = 0.f;
+    for (int v = 0; v < wid; v++) {  // ranges above this one, top first
+      Op<SW> o;
+      const float *q = s_tot[v][lane * CPL + c];
+#pragma unroll
+      for (int i = 0; i < SW * SW; i++) o.A[i] = q[i];
+#pragma unroll
+      for (int i = 0; i < SW; i++) o.b[i] = q[SW * SW + i];
+      float y[SW];
+      op_apply(o, cur[c], y);
+#pragma unroll
+      for (int i = 0; i < SW; i++) cur[c][i] = y[i];
+    }
+  }
+  for (int jc = j1 - 1; jc >= j0; jc -= R) {
+    Op<SW> o[R][CPL];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+      for (int c = 0; c < CPL; c++) o[r][c] = ld_op(jc - r >= j0 ? jc - r : j0, c);
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int jj = jc - r;
+      if (jj < j0) continue;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        float *cp = carry + (((size_t)stripe * nt + jj) * CH + lane * CPL + c) * SW;
+#pragma unroll
+        for (int i = 0; i < SW; i++) cp[i] = cur[c][i];
+        float y[SW];
+        op_apply(o[r][c], cur[c], y);
+#pragma unroll
+        for (int i = 0; i < SW; i++) cur[c][i] = y[i];
+      }
+    }
+  }
+}
+
+template <int CELL, typename ST, int CPL>
+static hipError_t chan2_adj_launch(const ChanArgs &a, hipStream_t s) {
+  constexpr int SW = CELL == C_LSTM ? 2 : 1;
+  const unsigned grid = (unsigned)((a.ntiles + 3) / 4);
+  hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, false>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_chan_adj_carry<SW, CPL>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
+  hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, true>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s) {
+  const ChanGeomInfo g = chan2_geom(cell, a.n);
+  if (cell == C_GRU_DIAG) {
+    if (g.CPL == 2)
+      return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 2>(a, s) : chan2_adj_launch<C_GRU_DIAG, float, 2>(a, s);
+    return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 1>(a, s) : chan2_adj_launch<C_GRU_DIAG, float, 1>(a, s);
+  }
+  if (cell == C_LSTM)
+    return bf16 ? chan2_adj_launch<C_LSTM, uint16_t, 1>(a, s) : chan2_adj_launch<C_LSTM, float, 1>(a, s);
+  return hipErrorInvalidValue;
+}
+
 ChanGeomInfo chan2_geom(int cell, int n) {
   ChanGeomInfo g;
   g.CPL = (cell == C_GRU_DIAG && n % 2 == 0) ? 2 : 1;

@@ -782,4 +782,41 @@ __global__ __launch_bounds__(256) void k_chan_reduce(const ChanArgs a, float *dW
   else { if (dbx) dbx[(size_t)(p - 8) * n + c] = v; }
 }
 
+// Per-tile partials [stripe][tile][CH][CHAN_P] summed in two fixed-order
+// stages: split q of the (sequence, tile) terms of every (channel, slot) into
+// red[q][n][CHAN_P] (fp64), then the splits in order into the gradients.
+template <int CH>
+__global__ __launch_bounds__(256) void k_chan_red_split(const ChanArgs a, double *red) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n = a.n;
+  if (e >= n * CHAN_P) return;
+  const int c = e / CHAN_P, p = e % CHAN_P;
+  const int CG = (n + CH - 1) / CH, cg = c / CH, cl = c % CH;
+  const int terms = (a.stripes / CG) * a.tps, per = (terms + gridDim.y - 1) / gridDim.y;
+  const int q0 = blockIdx.y * per, q1 = min(terms, q0 + per);
+  double s = 0.0;
+#pragma unroll 8
+  for (int q = q0; q < q1; q++) {
+    const int stripe = (q / a.tps) * CG + cg, j = q % a.tps;
+    s += (double)a.part[(((size_t)stripe * a.tps + j) * CH + cl) * CHAN_P + p];
+  }
+  red[(size_t)blockIdx.y * n * CHAN_P + e] = s;
+}
+
+template <int SPLITS>
+__global__ __launch_bounds__(256) void k_chan_red_final(const ChanArgs a, const double *red, float *dWh,
+                                                        float *dbh, float *dpeep, float *dbx) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n = a.n;
+  if (e >= n * CHAN_P) return;
+  const int c = e / CHAN_P, p = e % CHAN_P;
+  double s = 0.0;
+  for (int q = 0; q < SPLITS; q++) s += red[(size_t)q * n * CHAN_P + e];
+  const float v = (float)s;
+  if (p < 3) { if (dWh) dWh[(size_t)p * n + c] = v; }
+  else if (p < 6) { if (dbh) dbh[(size_t)(p - 3) * n + c] = v; }
+  else if (p < 8) { if (dpeep && a.SW == 2) dpeep[(size_t)(p - 6) * n + c] = v; }
+  else { if (dbx) dbx[(size_t)(p - 8) * n + c] = v; }
+}
+
 }  // namespace pr

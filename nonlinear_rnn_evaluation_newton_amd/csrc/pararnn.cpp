@@ -51,6 +51,7 @@ struct Plan {
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
   size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
+  size_t off_red = 0;             // channel path adjoint: fp64 split sums of the weight partials
   // dense n = 64 path
   int cps = 0, nchunks = 0;
   size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0, off_csum = 0;
@@ -182,7 +183,8 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
     pl->solve_bytes = o;
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
-    pl->off_part = o; o = align256(o + (size_t)pl->ntiles_a * gf.CH * 11 * 4);
+    pl->off_part = o; o = align256(o + (size_t)(pl->ntiles_a > pl->ntiles_2 ? pl->ntiles_a : pl->ntiles_2) * gf.CH * 11 * 4);
+    pl->off_red = o; o = align256(o + (size_t)CHAN_RED_SPLITS * p->n * 11 * 8);
     const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
     pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
     pl->off_xt = o; o = align256(o + rows * p->d * es);
@@ -712,14 +714,26 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     ca.agg = (unsigned long long *)(ws + pl.off_agg);
     ca.incl = (unsigned long long *)(ws + pl.off_incl);
     ca.stripes = pl.stripes;
-    ca.tps = pl.tps_a;
-    ca.ntiles = pl.ntiles_a;
     const int ta = tr.begin(TR_ADJ, s);
-    HIPCHK(launch_chan_adjoint(kc, bf, ca, s));
+    const bool adj2 = !getenv("PARARNN_CHAN_LOOKBACK");
+    if (adj2) {  // streaming passes
+      ca.tps = pl.tps_2;
+      ca.ntiles = pl.ntiles_2;
+      ca.part_per_block = 0;
+      HIPCHK(launch_chan2_adjoint(kc, bf, ca, s));
+    } else {
+      ca.tps = pl.tps_a;
+      ca.ntiles = pl.ntiles_a;
+      HIPCHK(launch_chan_adjoint(kc, bf, ca, s));
+    }
     tr.end(TR_ADJ, ta, s);
     const int tg = tr.begin(TR_AGEMM, s);
-    if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
-      HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
+    if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x)) {
+      if (adj2)
+        HIPCHK(launch_chan_reduce_tiles(kc, ca, (double *)(ws + pl.off_red), dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
+      else
+        HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
+    }
     // Both products contract over an outer dimension of a stored operand;
     // transposed copies (HBM-bound, a few percent of the products) put K
     // innermost in every operand, the layout the GEMM reads fastest.
