@@ -239,10 +239,13 @@ def main() -> int:
         nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
         achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
-        kname = ("k_chan_sweep" if chan else "k_pipe<SweepPol>" if scalar_path(p) else "k_time_sweep")
+        kname = ("k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
+                 "sweep's tile aggregates)" if chan else
+                 ("k_pipe<SweepPol>" if scalar_path(p) else "k_time_sweep") +
+                 " (fused cell + Jacobian + scan + update)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(p["name"]),
-                    "kernel": kname + " (fused cell + Jacobian + scan + update)",
+                    "kernel": kname,
                     "avg_launch_us": round(avg_ms * 1e3, 2),
                     "bytes_per_launch": per_solve_bytes / iters}
         if tr["adjoint_launches"] > 0:

@@ -76,17 +76,17 @@ struct ChanArgs {
   float tol;
   int max_iters;
   SolveState *st;
+  // standalone scan: tagged look-back descriptors; sweep and adjoint passes:
+  // fp32 tile aggregates [ntiles][CH][SW*SW+SW] and carries [ntiles][CH][SW]
   unsigned long long *agg, *incl;
-  float *bnd;           // [2][ntiles][CH*SW]
+  float *bnd;           // [2][ntiles][CH*SW] each tile's last state, per sweep parity
   int stripes, tps, ntiles;
   int reverse;
-  int part_per_block, nparts;
 };
 struct ChanGeomInfo {
   int CPL, TW, CH, TT;
 };
-ChanGeomInfo chan_geom(int cell, int n, bool adjoint);
-hipError_t launch_chan_sweep(int cell, bool bf16, ChanArgs &a, hipStream_t s);
+ChanGeomInfo chan_geom(int cell, int n);  // tiles of the standalone scan
 // streaming sweep passes (no chain between tiles): tiles of CHAN2_TT steps,
 // one wavefront each; per sweep a carry scan then a pass that applies the
 // sweep and composes the next sweep's tile aggregates
@@ -102,9 +102,6 @@ hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStrea
 constexpr int CHAN_RED_SPLITS = 32;
 hipError_t launch_chan_reduce_tiles(int cell, ChanArgs &a, double *red, float *dWh, float *dbh, float *dpeep,
                                    float *dbx, hipStream_t s);
-hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s);
-hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
-                              hipStream_t s);
 hipError_t launch_chan_scan(int SW, ChanArgs &a, hipStream_t s);
 
 // ---------------- dense n = 64 path (MFMA scan) ----------------------------

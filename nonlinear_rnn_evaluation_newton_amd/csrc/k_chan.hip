@@ -4,12 +4,13 @@
 
 namespace pr {
 
-// Tile geometry per cell: lanes own CPL adjacent channels, wavefronts TW steps.
-ChanGeomInfo chan_geom(int cell, int n, bool adjoint) {
+// Tile geometry of the standalone scan: lanes own CPL adjacent channels,
+// wavefronts TW steps.
+ChanGeomInfo chan_geom(int cell, int n) {
   ChanGeomInfo g;
   if (cell == C_GRU_DIAG) {
     g.CPL = (n % 2 == 0) ? 2 : 1;
-    g.TW = adjoint ? 8 : 16;
+    g.TW = 16;
   } else {
     g.CPL = 1;
     g.TW = 8;
@@ -26,55 +27,6 @@ static int chan_grid(const ChanArgs &a, bool stripe_aligned) {
   int grid = a.ntiles < r ? a.ntiles : r;
   if (stripe_aligned && a.stripes <= grid) grid = grid / a.stripes * a.stripes;
   return grid;
-}
-
-#define PR_CHAN_CFG(cell, n, adj, ...)                                                    \
-  {                                                                                       \
-    const ChanGeomInfo gi = chan_geom(cell, n, adj);                                      \
-    if (cell == C_GRU_DIAG && gi.CPL == 2 && gi.TW == 16) { constexpr int CELL = C_GRU_DIAG, CPL = 2, TW = 16; __VA_ARGS__; } \
-    else if (cell == C_GRU_DIAG && gi.CPL == 2 && gi.TW == 8) { constexpr int CELL = C_GRU_DIAG, CPL = 2, TW = 8; __VA_ARGS__; } \
-    else if (cell == C_GRU_DIAG && gi.CPL == 1 && gi.TW == 16) { constexpr int CELL = C_GRU_DIAG, CPL = 1, TW = 16; __VA_ARGS__; } \
-    else if (cell == C_GRU_DIAG && gi.CPL == 1 && gi.TW == 8) { constexpr int CELL = C_GRU_DIAG, CPL = 1, TW = 8; __VA_ARGS__; } \
-    else if (cell == C_LSTM && gi.CPL == 1 && gi.TW == 8) { constexpr int CELL = C_LSTM, CPL = 1, TW = 8; __VA_ARGS__; } \
-    else return hipErrorInvalidValue;                                                     \
-  }
-
-hipError_t launch_chan_sweep(int cell, bool bf16, ChanArgs &a, hipStream_t s) {
-  PR_CHAN_CFG(cell, a.n, false, {
-    if (bf16) {
-      const int grid = chan_grid<k_chan_sweep<CELL, uint16_t, CPL, TW>>(a, false);
-      if (grid <= 0) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((k_chan_sweep<CELL, uint16_t, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
-    } else {
-      const int grid = chan_grid<k_chan_sweep<CELL, float, CPL, TW>>(a, false);
-      if (grid <= 0) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((k_chan_sweep<CELL, float, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
-    }
-  });
-  return hipGetLastError();
-}
-
-hipError_t launch_chan_adjoint(int cell, bool bf16, ChanArgs &a, hipStream_t s) {
-  PR_CHAN_CFG(cell, a.n, true, {
-    int grid;
-    if (bf16) grid = chan_grid<k_chan_adjoint<CELL, uint16_t, CPL, TW>>(a, true);
-    else grid = chan_grid<k_chan_adjoint<CELL, float, CPL, TW>>(a, true);
-    if (grid <= 0) return hipErrorInvalidConfiguration;
-    a.part_per_block = (grid % a.stripes == 0) ? 1 : 0;
-    a.nparts = grid;
-    if (bf16) hipLaunchKernelGGL((k_chan_adjoint<CELL, uint16_t, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_chan_adjoint<CELL, float, CPL, TW>), dim3(grid), dim3(256), 0, s, a);
-  });
-  return hipGetLastError();
-}
-
-hipError_t launch_chan_reduce(int cell, ChanArgs &a, float *dWh, float *dbh, float *dpeep, float *dbx,
-                              hipStream_t s) {
-  const ChanGeomInfo gi = chan_geom(cell, a.n, true);
-  const unsigned blocks = (unsigned)((a.n * CHAN_P + 255) / 256);
-  if (gi.CH == 128) hipLaunchKernelGGL((k_chan_reduce<128>), dim3(blocks), dim3(256), 0, s, a, dWh, dbh, dpeep, dbx);
-  else hipLaunchKernelGGL((k_chan_reduce<64>), dim3(blocks), dim3(256), 0, s, a, dWh, dbh, dpeep, dbx);
-  return hipGetLastError();
 }
 
 hipError_t launch_chan_reduce_tiles(int cell, ChanArgs &a, double *red, float *dWh, float *dbh, float *dpeep,

@@ -1,16 +1,19 @@
-// Channel-parallel kernels for per-channel state (diagonal ParaGRU, SW = 1;
-// CIFG/peephole ParaLSTM with a 2x2 block Jacobian, SW = 2): one fused
-// Newton sweep per launch, the standalone diagonal / 2x2-block affine scan,
-// and the fused adjoint.
+// Channel-parallel building blocks for per-channel state (diagonal ParaGRU,
+// SW = 1; CIFG/peephole ParaLSTM with a 2x2 block Jacobian, SW = 2): buffer
+// loads, per-channel weights, the start-of-sweep stop check, the standalone
+// diagonal / 2x2-block affine scan, and the fixed-order reduction of the
+// adjoint's weight partials.  The Newton sweep and the adjoint are streaming
+// passes (k_chan2.hip).
 //
 // Channels are independent, so a scan runs per (sequence, channel) along time
-// (Para-Seq README, Main features: diagonal and 2x2 block scans).  Layout: a
-// lane owns CPL adjacent channels (coalesced loads across the wavefront), a
-// tile is 4 wavefronts x TW steps of those 64*CPL channels; each lane
-// composes its TW steps serially per channel, the 4 wavefronts combine in LDS,
-// and consecutive time tiles of a stripe (sequence b, channel group) chain
-// through a decoupled look-back whose descriptors are per channel.  A
-// persistent grid walks the tiles in increasing time-major order.
+// (Para-Seq README, Main features: diagonal and 2x2 block scans).  Layout of
+// the standalone scan: a lane owns CPL adjacent channels (coalesced loads
+// across the wavefront), a tile is 4 wavefronts x TW steps of those 64*CPL
+// channels; each lane composes its TW steps serially per channel, the 4
+// wavefronts combine in LDS, and consecutive time tiles of a stripe (sequence
+// b, channel group) chain through a decoupled look-back whose descriptors are
+// per channel.  A persistent grid walks the tiles in increasing time-major
+// order.
 #pragma once
 
 #include "cells_chan.h"
@@ -299,156 +302,6 @@ __device__ inline bool chan_stopped(const ChanArgs &a, int *s_stop) {
 }
 
 // ---------------------------------------------------------------------------
-// one Newton sweep
-// ---------------------------------------------------------------------------
-template <int CELL, typename ST, int CPL, int TW>
-__global__ __launch_bounds__(256) void k_chan_sweep(const ChanArgs a) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1;
-  using Gm = ChanGeom<SW, CPL, TW>;
-  constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
-  __shared__ float s_agg[4 * CH * AW];
-  __shared__ float s_carry[CH * SW];
-  __shared__ int s_stop;
-  __shared__ unsigned s_dmax[4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6), k = a.k;
-  const int T = a.T, n = a.n, S = SW * n;
-  if (chan_stopped(a, &s_stop)) return;
-  const int CG = (n + CH - 1) / CH;
-  const ST *U = (const ST *)a.U;
-  ST *H = (ST *)a.h;
-  const ST *H0 = (const ST *)a.h0;
-  unsigned dmax = 0;
-
-  for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
-    const int j = id / a.stripes, stripe = id % a.stripes;
-    const int b = stripe / CG, cg = stripe % CG, L = stripe * a.tps + j;
-    const int c0 = cg * CH + lane * CPL;  // first channel of this lane
-    const bool active = c0 < n;           // n is a multiple of CPL
-    const int t0 = j * TT + wid * TW;     // first step of this wave
-    ChanW w[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
-
-    float sp[CPL * SW];  // state before step t0
-#pragma unroll
-    for (int i = 0; i < CPL * SW; i++) sp[i] = 0.f;
-    if (active && t0 < T) {
-      if (t0 == 0) {
-        if (H0) ld_vec<ST, CPL * SW>(H0 + (size_t)b * S + (size_t)c0 * SW, sp);
-      } else if (k >= 2) {
-        if (wid == 0) {
-          const float *bd = a.bnd + ((size_t)((k - 1) & 1) * a.ntiles + (L - 1)) * CH * SW + (size_t)lane * CPL * SW;
-#pragma unroll
-          for (int i = 0; i < CPL * SW; i++) sp[i] = bd[i];
-        } else {
-          ld_vec<ST, CPL * SW>(H + ((size_t)b * T + t0 - 1) * S + (size_t)c0 * SW, sp);
-        }
-      }
-    }
-    // Every input of the wavefront's TW steps is requested before the first
-    // is used: buffer loads on the tile's rows (rows past T lie outside the
-    // resource and read zero, as does the iterate of sweep 1, h = 0).
-    constexpr int ES = (int)sizeof(ST), UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>();
-    const int r0 = j * TT, nrows = min(TT, T - r0);
-    const Rsrc ru = sc_rsrc(U + ((size_t)b * T + r0) * 3 * n, (unsigned)(nrows * 3 * n * ES));
-    const Rsrc rh = sc_rsrc(k >= 2 ? H + ((size_t)b * T + r0) * S : nullptr, (unsigned)(nrows * S * ES));
-    unsigned uw[TW][3][UW], hw[TW][HW];
-    const unsigned lane_oob = active ? 0u : SC_OOB;  // idle lanes: outside every resource
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      const int tr = wid * TW + s;  // row within the tile
-#pragma unroll
-      for (int g = 0; g < 3; g++) bldw<CPL * ES>(ru, (unsigned)((tr * 3 * n + g * n + c0) * ES) | lane_oob, uw[s][g]);
-      bldw<CPL * SW * ES>(rh, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, hw[s]);
-    }
-    float Jv[TW][CPL][SW * SW], rv[TW][CPL][SW];
-    Op<SW> agg[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      // steps past T (and idle lanes) take the identity element J = I, r = 0
-      const bool valid = active && t0 + s < T;
-#pragma unroll
-      for (int c = 0; c < CPL; c++) {
-        const float Uc[3] = {unpackw<ST>(uw[s][0], c), unpackw<ST>(uw[s][1], c), unpackw<ST>(uw[s][2], c)};
-        float f[SW], J[SW * SW];
-        chan_cell<CELL>(sp + c * SW, Uc, w[c], f, J);
-        Op<SW> e;
-#pragma unroll
-        for (int i = 0; i < SW; i++) {
-          rv[s][c][i] = valid ? f[i] - unpackw<ST>(hw[s], c * SW + i) : 0.f;
-          e.b[i] = rv[s][c][i];
-        }
-#pragma unroll
-        for (int i = 0; i < SW * SW; i++) {
-          Jv[s][c][i] = valid ? J[i] : ((i % (SW + 1)) == 0 ? 1.f : 0.f);
-          e.A[i] = Jv[s][c][i];
-        }
-        agg[c] = compose(e, agg[c]);
-      }
-#pragma unroll
-      for (int i = 0; i < CPL * SW; i++) sp[i] = unpackw<ST>(hw[s], i);
-    }
-    Op<SW> pre[CPL], tot[CPL];
-    chan_combine<SW, CPL>(agg, pre, tot, s_agg);
-    if (wid == 0) {
-      float carry[CPL][SW];
-      chan_lookback<SW, CPL, 4>(tot, j, k, active, a.agg + (size_t)stripe * a.tps * CH * AW,
-                                a.incl + (size_t)stripe * a.tps * CH * SW, carry, a.st);
-#pragma unroll
-      for (int c = 0; c < CPL; c++)
-#pragma unroll
-        for (int i = 0; i < SW; i++) s_carry[(lane * CPL + c) * SW + i] = carry[c][i];
-    }
-    __syncthreads();
-    float dh[CPL][SW];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) op_apply(pre[c], &s_carry[(lane * CPL + c) * SW], dh[c]);
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      const int t = t0 + s;
-      if (active && t < T) {
-        float hn[CPL * SW];
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          float nd[SW];
-#pragma unroll
-          for (int i = 0; i < SW; i++) {
-            float acc = rv[s][c][i];
-#pragma unroll
-            for (int m = 0; m < SW; m++) acc = fmaf(Jv[s][c][i * SW + m], dh[c][m], acc);
-            nd[i] = acc;
-          }
-#pragma unroll
-          for (int i = 0; i < SW; i++) {
-            dh[c][i] = nd[i];
-            hn[c * SW + i] = unpackw<ST>(hw[s], c * SW + i) + nd[i];
-            const unsigned u = __float_as_uint(fabsf(nd[i]));
-            dmax = u > dmax ? u : dmax;
-          }
-        }
-        st_vec<ST, CPL * SW>(H + ((size_t)b * T + t) * S + (size_t)c0 * SW, hn);
-        if (wid == 3 && s == TW - 1) {
-          float *bd = a.bnd + ((size_t)(k & 1) * a.ntiles + L) * CH * SW + (size_t)lane * CPL * SW;
-#pragma unroll
-          for (int i = 0; i < CPL * SW; i++) bd[i] = sizeof(ST) == 2 ? bf2f(f2bf(hn[i])) : hn[i];
-        }
-      }
-    }
-    __syncthreads();  // s_agg / s_carry are rewritten by the next tile
-  }
-  dmax = wave_max_u32(dmax);
-  if (lane == 0) s_dmax[wid] = dmax;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned m = s_dmax[0];
-    for (int q = 1; q < 4; q++) m = s_dmax[q] > m ? s_dmax[q] : m;
-    max_agent(&a.st->dslot[k & 3][blockIdx.x % PR_DSHARDS], m);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // standalone scan with given operators (fp32):  y_t = A_t y_{t-1} + b_t, or
 // in reverse time y_t = A_t y_{t+1} + b_t.  SW = 1: A, b [B,T,n];
 // SW = 2: A [B,T,n,2,2], b [B,T,n,2].
@@ -529,258 +382,10 @@ __global__ __launch_bounds__(256) void k_chan_scan(const ChanArgs a) {
 namespace pr {
 
 // ---------------------------------------------------------------------------
-// adjoint: per channel, lam_t = g_t + J_{t+1}^T lam_{t+1} by a reverse-time
-// scan; then the chain rule through each cell gives dU (for the dx and dW_x
-// products), dh0 and the per-channel weight-gradient partials
-// [a0 a1 a2 | b0 b1 b2 | p0 p1 | sum dU0 dU1 dU2] (CHAN_P values).
-// When every block keeps one stripe (grid a multiple of the stripe count)
-// the partials are summed per block, else per tile.
+// adjoint weight-gradient partials per channel:
+// [a0 a1 a2 | b0 b1 b2 | p0 p1 | sum dU0 dU1 dU2] (CHAN_P values)
 // ---------------------------------------------------------------------------
 constexpr int CHAN_P = 11;
-
-template <int CELL, typename ST, int CPL, int TW>
-__global__ __launch_bounds__(256) void k_chan_adjoint(const ChanArgs a) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1;
-  using Gm = ChanGeom<SW, CPL, TW>;
-  constexpr int CH = Gm::CH, TT = Gm::TT, AW = Gm::AW;
-  __shared__ float s_agg[4 * CH * AW];
-  __shared__ float s_carry[CH * SW];
-  __shared__ float s_red[4 * CH * CHAN_P];
-  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = a.T, n = a.n, S = SW * n;
-  const int CG = (n + CH - 1) / CH;
-  const ST *U = (const ST *)a.U, *H = (const ST *)a.h, *Gr = (const ST *)a.g, *H0 = (const ST *)a.h0;
-  ST *LAM = (ST *)a.lam, *DH0 = (ST *)a.dh0, *DU = (ST *)a.dU;
-  float acc[CPL][CHAN_P];
-#pragma unroll
-  for (int c = 0; c < CPL; c++)
-#pragma unroll
-    for (int p = 0; p < CHAN_P; p++) acc[c][p] = 0.f;
-  const bool per_block = a.part_per_block != 0;
-
-  for (int id = blockIdx.x; id < a.ntiles; id += gridDim.x) {
-    const int j = id / a.stripes, stripe = id % a.stripes;
-    const int b = stripe / CG, cg = stripe % CG;
-    const int c0 = cg * CH + lane * CPL;
-    const bool active = c0 < n;
-    const int s0 = j * TT + wid * TW;  // scan positions; time t = T - 1 - s
-    ChanW w[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
-
-    float Av[TW][CPL][SW * SW], gv[TW][CPL][SW], hv[TW][CPL][SW], uv[TW][CPL][3];
-    float un[CPL][3];  // U at the step after the wave's range
-    float hp[CPL * SW];  // h at the step before the wave's range
-    const int thi = T - 1 - s0;
-#pragma unroll
-    for (int c = 0; c < CPL; c++) un[c][0] = un[c][1] = un[c][2] = 0.f;
-#pragma unroll
-    for (int i = 0; i < CPL * SW; i++) hp[i] = 0.f;
-    if (active && thi >= 0 && thi + 1 < T) {
-      float u0[CPL], u1[CPL], u2[CPL];
-      const size_t row = (size_t)b * T + thi + 1;
-      ld_vec<ST, CPL>(U + row * 3 * n + c0, u0);
-      ld_vec<ST, CPL>(U + row * 3 * n + n + c0, u1);
-      ld_vec<ST, CPL>(U + row * 3 * n + 2 * n + c0, u2);
-#pragma unroll
-      for (int c = 0; c < CPL; c++) { un[c][0] = u0[c]; un[c][1] = u1[c]; un[c][2] = u2[c]; }
-    }
-    const int tlo = thi - TW + 1;
-    float hz[CPL * SW];  // h0, used by the step t = 0 when this wave covers it
-#pragma unroll
-    for (int i = 0; i < CPL * SW; i++) hz[i] = 0.f;
-    if (active && tlo >= 1 && tlo < T) ld_vec<ST, CPL * SW>(H + ((size_t)b * T + tlo - 1) * S + (size_t)c0 * SW, hp);
-    if (active && tlo <= 0 && thi >= 0 && H0) ld_vec<ST, CPL * SW>(H0 + (size_t)b * S + (size_t)c0 * SW, hz);
-    Op<SW> agg[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) agg[c] = op_identity<SW>();
-    // Every input of the wavefront's TW steps is requested before the first
-    // is used: buffer loads on the wavefront's rows [tlo, thi] (rows before
-    // t = 0 lie outside the resource and read zero).
-    constexpr int ES = (int)sizeof(ST), UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>();
-    // rows of this wavefront in [0, T) (wavefront-uniform: the resources live in scalar registers)
-    const int rlo = __builtin_amdgcn_readfirstlane(tlo < 0 ? 0 : tlo);
-    const int nr = __builtin_amdgcn_readfirstlane(thi - rlo + 1);
-    const size_t rbase = (size_t)__builtin_amdgcn_readfirstlane(b) * T + rlo;
-    const Rsrc ru = sc_rsrc(U + rbase * 3 * n, nr > 0 ? (unsigned)(nr * 3 * n * ES) : 0u);
-    const Rsrc rhh = sc_rsrc(H + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
-    const Rsrc rg = sc_rsrc(Gr + rbase * S, nr > 0 ? (unsigned)(nr * S * ES) : 0u);
-    // idle lanes carry bit 31; rows before t = 0 give negative offsets,
-    // which wrap past every resource, so no select sits between the loads
-    const unsigned lane_oob = active ? 0u : SC_OOB;
-    unsigned uw[TW][3][UW], hw[TW][HW], gw[TW][HW];
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      const int tr = thi - s - rlo;  // row within the wavefront's range (negative: before t = 0)
-#pragma unroll
-      for (int g = 0; g < 3; g++) bldw<CPL * ES>(ru, (unsigned)((tr * 3 * n + g * n + c0) * ES) | lane_oob, uw[s][g]);
-      bldw<CPL * SW * ES>(rhh, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, hw[s]);
-      bldw<CPL * SW * ES>(rg, (unsigned)((tr * S + c0 * SW) * ES) | lane_oob, gw[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      const int t = thi - s;
-      if (active && t >= 0) {
-        float hc[CPL * SW], gc[CPL * SW], u0[CPL], u1[CPL], u2[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL * SW; i++) {
-          hc[i] = unpackw<ST>(hw[s], i);
-          gc[i] = unpackw<ST>(gw[s], i);
-        }
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          u0[c] = unpackw<ST>(uw[s][0], c);
-          u1[c] = unpackw<ST>(uw[s][1], c);
-          u2[c] = unpackw<ST>(uw[s][2], c);
-        }
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          uv[s][c][0] = u0[c]; uv[s][c][1] = u1[c]; uv[s][c][2] = u2[c];
-          float J[SW * SW];
-          if (t + 1 < T) {
-            float f[SW];
-            chan_cell<CELL>(hc + c * SW, s == 0 ? un[c] : uv[s - 1][c], w[c], f, J);
-          } else {
-#pragma unroll
-            for (int i = 0; i < SW * SW; i++) J[i] = 0.f;
-          }
-          Op<SW> o;
-#pragma unroll
-          for (int r = 0; r < SW; r++) {
-#pragma unroll
-            for (int q = 0; q < SW; q++) o.A[r * SW + q] = J[q * SW + r];
-            o.b[r] = gc[c * SW + r];
-            gv[s][c][r] = gc[c * SW + r];
-            hv[s][c][r] = hc[c * SW + r];
-          }
-#pragma unroll
-          for (int i = 0; i < SW * SW; i++) Av[s][c][i] = o.A[i];
-          agg[c] = compose(o, agg[c]);
-        }
-      }
-    }
-    Op<SW> pre[CPL], tot[CPL];
-    chan_combine<SW, CPL>(agg, pre, tot, s_agg);
-    if (wid == 0) {
-      float carry[CPL][SW];
-      chan_lookback<SW, CPL, 4>(tot, j, 1, active, a.agg + (size_t)stripe * a.tps * CH * AW,
-                                a.incl + (size_t)stripe * a.tps * CH * SW, carry, a.st);
-#pragma unroll
-      for (int c = 0; c < CPL; c++)
-#pragma unroll
-        for (int i = 0; i < SW; i++) s_carry[(lane * CPL + c) * SW + i] = carry[c][i];
-    }
-    __syncthreads();
-    float lam[CPL][SW];
-#pragma unroll
-    for (int c = 0; c < CPL; c++) op_apply(pre[c], &s_carry[(lane * CPL + c) * SW], lam[c]);
-    float tacc[CPL][CHAN_P];
-#pragma unroll
-    for (int c = 0; c < CPL; c++)
-#pragma unroll
-      for (int p = 0; p < CHAN_P; p++) tacc[c][p] = 0.f;
-#pragma unroll
-    for (int s = 0; s < TW; s++) {
-      const int t = thi - s;
-      if (active && t >= 0) {
-        const size_t row = (size_t)b * T + t;
-        float lo[CPL * SW], du[3][CPL], dso[CPL * SW];
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-          float nl[SW];
-#pragma unroll
-          for (int i = 0; i < SW; i++) {
-            float x = gv[s][c][i];
-#pragma unroll
-            for (int m = 0; m < SW; m++) x = fmaf(Av[s][c][i * SW + m], lam[c][m], x);
-            nl[i] = x;
-          }
-#pragma unroll
-          for (int i = 0; i < SW; i++) { lam[c][i] = nl[i]; lo[c * SW + i] = nl[i]; }
-          // state before step t: h_{t-1} (the next element in scan order)
-          float spv[SW];
-#pragma unroll
-          for (int i = 0; i < SW; i++) spv[i] = s + 1 < TW ? hv[s + 1][c][i] : hp[c * SW + i];
-          if (t == 0) {
-#pragma unroll
-            for (int i = 0; i < SW; i++) spv[i] = hz[c * SW + i];
-          }
-          float ds[SW], dU[3];
-          chan_cell_vjp<CELL>(spv, uv[s][c], nl, w[c], ds, dU, tacc[c]);
-          tacc[c][8] += dU[0];
-          tacc[c][9] += dU[1];
-          tacc[c][10] += dU[2];
-#pragma unroll
-          for (int g = 0; g < 3; g++) du[g][c] = dU[g];
-#pragma unroll
-          for (int i = 0; i < SW; i++) dso[c * SW + i] = ds[i];
-        }
-        if (LAM) st_vec<ST, CPL * SW>(LAM + row * S + (size_t)c0 * SW, lo);
-#pragma unroll
-        for (int g = 0; g < 3; g++) st_vec<ST, CPL>(DU + row * 3 * n + (size_t)g * n + c0, du[g]);
-        if (t == 0 && DH0) st_vec<ST, CPL * SW>(DH0 + (size_t)b * S + (size_t)c0 * SW, dso);
-      }
-    }
-    if (per_block) {
-#pragma unroll
-      for (int c = 0; c < CPL; c++)
-#pragma unroll
-        for (int p = 0; p < CHAN_P; p++) acc[c][p] += tacc[c][p];
-    } else {
-      // per-tile partials: combine the 4 wavefronts, write [L][CH][CHAN_P]
-#pragma unroll
-      for (int c = 0; c < CPL; c++)
-#pragma unroll
-        for (int p = 0; p < CHAN_P; p++) s_red[((size_t)wid * CH + lane * CPL + c) * CHAN_P + p] = tacc[c][p];
-      __syncthreads();
-      const int L = stripe * a.tps + j;
-      for (int e = tid; e < CH * CHAN_P; e += 256)
-        a.part[(size_t)L * CH * CHAN_P + e] =
-            (s_red[e] + s_red[CH * CHAN_P + e]) + (s_red[2 * CH * CHAN_P + e] + s_red[3 * CH * CHAN_P + e]);
-    }
-    __syncthreads();
-  }
-  if (per_block) {
-#pragma unroll
-    for (int c = 0; c < CPL; c++)
-#pragma unroll
-      for (int p = 0; p < CHAN_P; p++) s_red[((size_t)wid * CH + lane * CPL + c) * CHAN_P + p] = acc[c][p];
-    __syncthreads();
-    for (int e = tid; e < CH * CHAN_P; e += 256)
-      a.part[(size_t)blockIdx.x * CH * CHAN_P + e] =
-          (s_red[e] + s_red[CH * CHAN_P + e]) + (s_red[2 * CH * CHAN_P + e] + s_red[3 * CH * CHAN_P + e]);
-  }
-}
-
-// Sum the partials of every channel in fp64, in slot order, and scatter to
-// the fp32 gradient outputs (dW_h [3n], db_h [3n], dpeep [2n], db_x [3n]).
-template <int CH>
-__global__ __launch_bounds__(256) void k_chan_reduce(const ChanArgs a, float *dWh, float *dbh, float *dpeep,
-                                                     float *dbx) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int n = a.n;
-  if (e >= n * CHAN_P) return;
-  const int c = e / CHAN_P, p = e % CHAN_P;
-  const int CG = (n + CH - 1) / CH, cg = c / CH, cl = c % CH;
-  double s = 0.0;
-  if (a.part_per_block) {
-    const int B = a.stripes / CG, G = a.nparts, S = a.stripes;
-    for (int bb = 0; bb < B; bb++)
-      for (int slot = cg + CG * bb; slot < G; slot += S) s += (double)a.part[((size_t)slot * CH + cl) * CHAN_P + p];
-  } else {
-    const int B = a.stripes / CG;
-    for (int bb = 0; bb < B; bb++) {
-      const int stripe = bb * CG + cg;
-      for (int j = 0; j < a.tps; j++)
-        s += (double)a.part[(((size_t)stripe * a.tps + j) * CH + cl) * CHAN_P + p];
-    }
-  }
-  const float v = (float)s;
-  if (p < 3) { if (dWh) dWh[(size_t)p * n + c] = v; }
-  else if (p < 6) { if (dbh) dbh[(size_t)(p - 3) * n + c] = v; }
-  else if (p < 8) { if (dpeep && a.SW == 2) dpeep[(size_t)(p - 6) * n + c] = v; }
-  else { if (dbx) dbx[(size_t)(p - 8) * n + c] = v; }
-}
 
 // Per-tile partials [stripe][tile][CH][CHAN_P] summed in two fixed-order
 // stages: split q of the (sequence, tile) terms of every (channel, slot) into

@@ -45,7 +45,7 @@ struct Plan {
   // scalar-state sweep (n = d = 1, T % 4 == 0): its own tile size
   int scalar_ok = 0, tps_s = 0, ntiles_s = 0, tps_sa = 0, ntiles_sa = 0;
   // channel path: stripes (sequence x channel group), tiles of sweep / adjoint
-  int stripes = 0, tps_a = 0, ntiles_a = 0, CH = 0;
+  int stripes = 0, CH = 0;
   // channel path, streaming sweep passes (tiles of CHAN2_TT steps)
   int tps_2 = 0, ntiles_2 = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
@@ -150,40 +150,34 @@ int make_plan(const pr_problem *p, Plan *pl) {
     const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
     pl->path = PATH_CHAN;
     pl->SW = p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1;
-    const ChanGeomInfo gf = chan_geom(kc, p->n, false), ga = chan_geom(kc, p->n, true);
-    pl->CH = gf.CH;
-    const long long CG = (p->n + gf.CH - 1) / gf.CH;
+    const ChanGeomInfo g = chan2_geom(kc, p->n);
+    pl->CH = g.CH;
+    const long long CG = (p->n + g.CH - 1) / g.CH;
     if ((long long)p->B * CG > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many stripes");
     pl->stripes = (int)(p->B * CG);
-    pl->tps = (p->T + gf.TT - 1) / gf.TT;
-    pl->tps_a = (p->T + ga.TT - 1) / ga.TT;
-    if ((long long)pl->tps * pl->stripes > 2147483647LL || (long long)pl->tps_a * pl->stripes > 2147483647LL)
-      return fail(PR_EUNSUPPORTED, "too many tiles");
-    pl->ntiles = pl->tps * pl->stripes;
-    pl->ntiles_a = pl->tps_a * pl->stripes;
     const size_t es = p->dtype == PR_BF16 ? 2 : 4;
-    // a tile's rows of U are addressed with 31-bit byte offsets
-    const int ttmax = gf.TT > ga.TT ? (gf.TT > CHAN2_TT ? gf.TT : CHAN2_TT) : (ga.TT > CHAN2_TT ? ga.TT : CHAN2_TT);
-    if ((long long)(2 * ttmax) * 3 * p->n * (long long)es >= (1LL << 31))
+    // a tile's rows of U (and the load groups just past it) are addressed
+    // with 31-bit byte offsets
+    if ((long long)(2 * CHAN2_TT) * 3 * p->n * (long long)es >= (1LL << 31))
       return fail(PR_EUNSUPPORTED, "channel count too large");
     pl->tps_2 = (p->T + CHAN2_TT - 1) / CHAN2_TT;
     if ((long long)pl->tps_2 * pl->stripes > 2147483647LL) return fail(PR_EUNSUPPORTED, "too many tiles");
     pl->ntiles_2 = pl->tps_2 * pl->stripes;
     const int SW = pl->SW, AW = SW * SW + SW;
-    size_t nt = (size_t)(pl->ntiles > pl->ntiles_a ? pl->ntiles : pl->ntiles_a);
-    if ((size_t)pl->ntiles_2 > nt) nt = (size_t)pl->ntiles_2;
-    const size_t nt_sweep = (size_t)(pl->ntiles > pl->ntiles_2 ? pl->ntiles : pl->ntiles_2);
+    const size_t nt = (size_t)pl->ntiles_2;
     const size_t rows = (size_t)p->B * p->T;
     size_t o = 0;
     pl->off_state = o; o = align256(o + sizeof(SolveState));
-    pl->off_agg = o; o = align256(o + nt * gf.CH * AW * 8);
-    pl->off_incl = o; o = align256(o + nt * gf.CH * SW * 8);
     pl->zero_bytes = o;
-    pl->off_bnd = o; o = align256(o + (size_t)2 * nt_sweep * gf.CH * SW * 4);
+    // tile aggregates, carries and each tile's last state (written before
+    // they are read in every call, so never cleared)
+    pl->off_agg = o; o = align256(o + nt * g.CH * AW * 4);
+    pl->off_incl = o; o = align256(o + nt * g.CH * SW * 4);
+    pl->off_bnd = o; o = align256(o + (size_t)2 * nt * g.CH * SW * 4);
     pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
     pl->solve_bytes = o;
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
-    pl->off_part = o; o = align256(o + (size_t)(pl->ntiles_a > pl->ntiles_2 ? pl->ntiles_a : pl->ntiles_2) * gf.CH * 11 * 4);
+    pl->off_part = o; o = align256(o + nt * g.CH * 11 * 4);
     pl->off_red = o; o = align256(o + (size_t)CHAN_RED_SPLITS * p->n * 11 * 8);
     const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
     pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
@@ -441,8 +435,8 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     ca.incl = (unsigned long long *)(ws + pl.off_incl);
     ca.bnd = (float *)(ws + pl.off_bnd);
     ca.stripes = pl.stripes;
-    ca.tps = pl.tps;
-    ca.ntiles = pl.ntiles;
+    ca.tps = pl.tps_2;
+    ca.ntiles = pl.ntiles_2;
     const int ti = tr.begin(TR_PROJ, s);
     HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
     tr.end(TR_PROJ, ti, s);
@@ -454,13 +448,6 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     a.tiles_per_seq = pl.tps_s;
     a.ntiles = pl.ntiles_s;
     HIPCHK(launch_scalar_coef(a, kc, (float *)(ws + pl.off_coef), s));
-  }
-
-  // channel cells: streaming passes unless the look-back sweep is asked for
-  const bool chan2 = pl.path == PATH_CHAN && !getenv("PARARNN_CHAN_LOOKBACK");
-  if (chan2) {
-    ca.tps = pl.tps_2;
-    ca.ntiles = pl.ntiles_2;
   }
 
   int first, next;
@@ -498,16 +485,13 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
         HIPCHK(launch_d64_sweep_part(da, 1, s));
         if (ev) HIPCHK(hipEventRecord(tr.swa[2 * (kk - 1) + 1], s));
         HIPCHK(launch_d64_sweep_part(da, 2, s));
-      } else if (chan2) {
+      } else {  // channel cells: carry scan, then the pass applying this sweep
         ca.k = kk;
         const bool bf = p->dtype == PR_BF16;
         if (kk == 1) HIPCHK(launch_chan2(kc, bf, ca, CHAN2_FIRST, s));
         HIPCHK(launch_chan2(kc, bf, ca, CHAN2_CARRY, s));
         // the last possible sweep composes no aggregates for a next one
         HIPCHK(launch_chan2(kc, bf, ca, kk == kmax ? CHAN2_APPLY : CHAN2_APPLY_NEXT, s));
-      } else {
-        ca.k = kk;
-        HIPCHK(launch_chan_sweep(kc, p->dtype == PR_BF16, ca, s));
       }
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
@@ -715,25 +699,13 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     ca.incl = (unsigned long long *)(ws + pl.off_incl);
     ca.stripes = pl.stripes;
     const int ta = tr.begin(TR_ADJ, s);
-    const bool adj2 = !getenv("PARARNN_CHAN_LOOKBACK");
-    if (adj2) {  // streaming passes
-      ca.tps = pl.tps_2;
-      ca.ntiles = pl.ntiles_2;
-      ca.part_per_block = 0;
-      HIPCHK(launch_chan2_adjoint(kc, bf, ca, s));
-    } else {
-      ca.tps = pl.tps_a;
-      ca.ntiles = pl.ntiles_a;
-      HIPCHK(launch_chan_adjoint(kc, bf, ca, s));
-    }
+    ca.tps = pl.tps_2;
+    ca.ntiles = pl.ntiles_2;
+    HIPCHK(launch_chan2_adjoint(kc, bf, ca, s));
     tr.end(TR_ADJ, ta, s);
     const int tg = tr.begin(TR_AGEMM, s);
-    if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x)) {
-      if (adj2)
-        HIPCHK(launch_chan_reduce_tiles(kc, ca, (double *)(ws + pl.off_red), dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
-      else
-        HIPCHK(launch_chan_reduce(kc, ca, dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
-    }
+    if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
+      HIPCHK(launch_chan_reduce_tiles(kc, ca, (double *)(ws + pl.off_red), dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
     // Both products contract over an outer dimension of a stored operand;
     // transposed copies (HBM-bound, a few percent of the products) put K
     // innermost in every operand, the layout the GEMM reads fastest.
@@ -777,7 +749,7 @@ size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n) {
   }
   if (jac == PR_JAC_DIAG || jac == PR_JAC_BLOCK2) {
     const int SW = jac == PR_JAC_BLOCK2 ? 2 : 1;
-    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n, false);
+    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n);
     const size_t nt = (size_t)B * ((n + gi.CH - 1) / gi.CH) * ((T + gi.TT - 1) / gi.TT);
     return align256(sizeof(SolveState)) + align256(nt * gi.CH * (SW * SW + SW) * 8) + align256(nt * gi.CH * SW * 8);
   }
@@ -799,7 +771,7 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
   HIPCHK(launch_zero(ws, need, s));
   if (jac != PR_JAC_DENSE) {
     const int SW = jac == PR_JAC_BLOCK2 ? 2 : 1;
-    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n, false);
+    const ChanGeomInfo gi = chan_geom(SW == 2 ? C_LSTM : C_GRU_DIAG, n);
     ChanArgs ca{};
     ca.A = A; ca.b = b; ca.y = y;
     ca.B = B; ca.T = T; ca.n = n; ca.SW = SW; ca.reverse = reverse ? 1 : 0;
