@@ -289,23 +289,52 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
   }
   __syncthreads();
   const int arow = wm * (FM * 32) + (lane & 31), brow = wn * (FN * 32) + (lane & 31), kl = (lane >> 5) * 8;
+  // Per K step: the next step's operands are requested from global memory
+  // (past the range they read zero and are never used); the fragments of
+  // 16-wide K slice q + 1 are read from LDS while slice q's MFMAs run, and
+  // the staged next step is written to the other LDS buffer during the last
+  // slice's MFMAs, so LDS traffic overlaps the matrix cores instead of
+  // alternating with them between barriers.
+  constexpr int NQ = BK / 16;
   for (int k0 = kb; k0 < ke; k0 += BK) {
-    const bool more = k0 + BK < ke;
-    if (more) gload(k0 + BK);
+    gload(k0 + BK);
     const uint16_t *cA = sA[buf], *cB = sB[buf];
+    bf16x8_t a[2][FM], b[2][FN];
+    auto frag = [&](int h, int ks) {
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8_t a[FM], b[FN];
+      for (int i = 0; i < FM; i++) a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
 #pragma unroll
-      for (int i = 0; i < FM; i++) a[i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
+      for (int j = 0; j < FN; j++) b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+    };
+    frag(0, 0);
+    // the global loads first, then the first slice's fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * GQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
 #pragma unroll
-      for (int j = 0; j < FN; j++) b[j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+    for (int q = 0; q < NQ; q++) {
+      if (q + 1 < NQ) frag((q + 1) & 1, (q + 1) * 16);
+      else lstore(buf ^ 1);
 #pragma unroll
       for (int j = 0; j < FN; j++)
 #pragma unroll
-        for (int i = 0; i < FM; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+        for (int i = 0; i < FM; i++)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q & 1][j], a[q & 1][i], acc[j][i], 0, 0, 0);
+      if (q + 1 < NQ) {  // one fragment read after each MFMA, then the remaining MFMAs
+#pragma unroll
+        for (int r = 0; r < FM + FN; r++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      } else {  // one LDS store after each MFMA
+#pragma unroll
+        for (int r = 0; r < 2 * GQ; r++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2 * GQ, 0);
+      }
     }
-    if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
