@@ -39,8 +39,49 @@ __global__ __launch_bounds__(256) void k_transpose(const E *__restrict__ src, E 
     if (c0 + i < C && r0 + tx < R) dst[(size_t)(c0 + i) * R + r0 + tx] = tile[tx][i];
 }
 
+// The same for 2-byte elements with 16-byte accesses on both sides (R and C
+// multiples of 8, 16-byte aligned matrices): a thread loads 8 adjacent
+// elements of a row, the tile sits in LDS with chunk c8 of row r at chunk
+// c8 ^ ((r / 8) % 8) (the 8 rows r8, r8 + 8, ... read together for one
+// output chunk fall in distinct banks), and a thread gathers 8 adjacent
+// rows of one column into one 16-byte store.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
+                                                     int R, int C) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int e = tid + 256 * q, r = e >> 3, ch = e & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < R && c0 + ch * 8 < C) v = *reinterpret_cast<const uint4 *>(src + (size_t)(r0 + r) * C + c0 + ch * 8);
+    *reinterpret_cast<uint4 *>(&tile[r * 64 + ((ch ^ ((r >> 3) & 7)) * 8)]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int e = tid + 256 * q, cc = e >> 3, r8 = (e & 7) * 8;
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int ra = r8 + 2 * i, rb = ra + 1;
+      const unsigned lo = tile[ra * 64 + (((cc >> 3) ^ ((ra >> 3) & 7)) * 8) + (cc & 7)];
+      const unsigned hi = tile[rb * 64 + (((cc >> 3) ^ ((rb >> 3) & 7)) * 8) + (cc & 7)];
+      w[i] = lo | (hi << 16);
+    }
+    if (c0 + cc < C && r0 + r8 < R)
+      *reinterpret_cast<uint4 *>(dst + (size_t)(c0 + cc) * R + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 hipError_t launch_transpose(const void *src, void *dst, int R, int C, int elem_bytes, hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
+  if (elem_bytes == 2 && R % 8 == 0 && C % 8 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0) {
+    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+    if (grid.y > 65535u) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, s, (const uint16_t *)src, (uint16_t *)dst, R, C);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
   if (grid.y > 65535u) return hipErrorInvalidValue;
   if (elem_bytes == 2)
