@@ -115,7 +115,9 @@ __device__ inline void stf(uint16_t *p, size_t i, float v) { p[i] = f2bf(v); }
 __device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float fsigm(float a) { return frcp(1.f + fexp(-a)); }
-__device__ inline float ftanh(float a) { return 1.f - 2.f * frcp(1.f + fexp(2.f * a)); }
+__device__ inline float ftanh(float a) {
+  return 1.f - 2.f * frcp(1.f + __builtin_amdgcn_exp2f(a * (2.f * 1.4426950408889634f)));
+}
 
 // ---------------------------------------------------------------------------
 // The affine operator y -> A y + b (dense N x N) and its composition.
@@ -146,9 +148,9 @@ __device__ inline Op<N> compose(const Op<N> &l, const Op<N> &e) {
   for (int i = 0; i < N; i++) {
 #pragma unroll
     for (int j = 0; j < N; j++) {
-      float a = 0.f;
+      float a = l.A[i * N] * e.A[j];
 #pragma unroll
-      for (int k = 0; k < N; k++) a = fmaf(l.A[i * N + k], e.A[k * N + j], a);
+      for (int k = 1; k < N; k++) a = fmaf(l.A[i * N + k], e.A[k * N + j], a);
       o.A[i * N + j] = a;
     }
     float bb = l.b[i];

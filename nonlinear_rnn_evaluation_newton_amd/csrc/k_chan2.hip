@@ -24,6 +24,8 @@
 // waits for another, so there is no look-back latency and no co-residency
 // requirement.  Both sides of a tile boundary use the stored (rounded) state
 // of the previous tile's last step, so aggregates and updates agree exactly.
+#include <type_traits>
+
 #include "k_chan_impl.h"
 
 namespace pr {
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
     // branches sit between the loads, so they all stay in flight.
     const unsigned lane_oob = active ? 0u : SC_OOB;
     unsigned ua[C2_P][3][UW], ha[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW];
-    auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) {
+    auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
         const int s = g * C2_P + q;
@@ -142,11 +144,15 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
         bldw<CPL * SW * ES>(rh, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, h[q]);
       }
     };
-    auto steps = [&](int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW]) {
+    // FULL: every lane active and every step inside [0, T) (all tiles but a
+    // sequence's last one when n fills the stripe): no identity selects
+    auto steps = [&](auto full, int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW])
+                     __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full)::value;
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
         const int s = g * C2_P + q;
-        const bool valid = active && s < nrows;
+        const bool valid = FULL || (active && s < nrows);
         float hn[CPL * SW];
 #pragma unroll
         for (int c = 0; c < CPL; c++) {
@@ -197,13 +203,18 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
         if constexpr (APPLY) bst<ST, CPL * SW>(rw, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, hn);
       }
     };
-    load(0, ua, ha);
-    for (int g = 0; g < C2_NG; g += 2) {
-      load(g + 1, ub, hb);
-      steps(g, ua, ha);
-      load(g + 2, ua, ha);
-      steps(g + 1, ub, hb);
-    }
+    auto walk = [&](auto full) __attribute__((always_inline)) {
+      load(0, ua, ha);
+      for (int g = 0; g < C2_NG; g += 2) {
+        load(g + 1, ub, hb);
+        steps(full, g, ua, ha);
+        load(g + 2, ua, ha);
+        steps(full, g + 1, ub, hb);
+      }
+    };
+    const int last_c = (stripe % CG) * CH + 63 * CPL;  // first channel of lane 63
+    if (nrows == TT && last_c < n) walk(std::true_type{});
+    else walk(std::false_type{});
     if (active) {
       if constexpr (APPLY) {  // the tile's last state, as stored, for the next sweep's neighbour
         if (nrows == TT) {
