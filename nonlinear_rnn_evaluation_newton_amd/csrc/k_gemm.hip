@@ -342,6 +342,17 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
   // lane holds rows m = (lane & 31) of each 32 x 32 tile and, per group of 4
   // registers, the 4 adjacent columns 8 * (r / 4) + 4 * (lane / 32) + (0..3)
   const bool vec_c = g.splits == 1 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0;
+  // the bias of this lane's columns, loaded once (they do not depend on the row)
+  float bias[FN][4][4];
+#pragma unroll
+  for (int j = 0; j < FN; j++)
+#pragma unroll
+    for (int rg = 0; rg < 4; rg++) {
+      const int n = n0 + wn * (FN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        bias[j][rg][c] = (g.bias && split == 0 && n + c < g.N) ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
+    }
 #pragma unroll
   for (int i = 0; i < FM; i++) {
     const int m = m0 + wm * (FM * 32) + i * 32 + (lane & 31);
@@ -354,10 +365,7 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
         if (n >= g.N) continue;
         float v[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          const float bias = (g.bias && split == 0 && n + c < g.N) ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
-          v[c] = acc[j][i][4 * rg + c] + bias;
-        }
+        for (int c = 0; c < 4; c++) v[c] = acc[j][i][4 * rg + c] + bias[j][rg][c];
         if (g.splits > 1) {
           float *w = g.ws + ((size_t)split * g.M + m) * g.N + n;
           if (n + 4 <= g.N && (g.N % 4) == 0) *reinterpret_cast<float4 *>(w) = make_float4(v[0], v[1], v[2], v[3]);
@@ -413,13 +421,13 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Split K until the grid covers the device a few times over (long-K
-// products such as dW = dU^T x have few output tiles), keeping at least
-// 8 K tiles per split.
+// Split K until the grid covers the device about twice (long-K products
+// such as dW = dU^T x have few output tiles; every split writes a full fp32
+// partial of C), keeping at least 8 K tiles per split.
 int gemm_splits(int M, int N, int K) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   int s = 1;
-  while (tiles * s < 1024 && K / (s * 2) >= 8 * GBK && s < 512) s *= 2;
+  while (tiles * s < 512 && K / (s * 2) >= 8 * GBK && s < 512) s *= 2;
   return s;
 }
 
