@@ -203,3 +203,17 @@ def test_bf16_large_products(cell, B, T, d, n):
     torch.cuda.synchronize()
     assert st == bd.PR_OK
     adjoint_compare(p, h, a, True)
+
+
+@pytest.mark.parametrize("cell", [sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG])
+@pytest.mark.parametrize("T", [63, 64, 65, 128, 129])
+def test_tile_boundaries(cell, T):
+    """Sequence lengths around the 64-step tiles of the sweep and adjoint
+    passes (one partial tile, exactly one or two full tiles, a one-step
+    tail), with h0, biases and a channel count that leaves idle lanes."""
+    p = sy.custom_problem(cell, B=2, T=T, d=12, n=66, seed=7 * T + cell, w_scale=0.8, h0=True)
+    dp, h = check_solve(p, 1e-6, T, False)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_compare(p, h, a, False)
