@@ -217,3 +217,16 @@ def test_tile_boundaries(cell, T):
     torch.cuda.synchronize()
     assert st == bd.PR_OK
     adjoint_compare(p, h, a, False)
+
+
+def test_bf16_products_on_the_small_tile_gemm(monkeypatch):
+    """A large-product shape with the 256 x 256-tile GEMM switched off
+    (PARARNN_SMALL_GEMM): the 128 x 128-tile kernel on the same products."""
+    monkeypatch.setenv("PARARNN_SMALL_GEMM", "1")
+    p = sy.custom_problem(sy.CELL_LSTM_CIFG_DIAG, B=3, T=704, d=264, n=304, seed=11, w_scale=0.8, h0=True,
+                          dtype=sy.DT_BF16)
+    dp, h = check_solve(p, 0.0, 3, True)
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_compare(p, h, a, True)

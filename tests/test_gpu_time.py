@@ -60,6 +60,23 @@ def test_cfg2_scalar_gru(T):
     check_solve(p)
 
 
+def test_cfg2_shape_on_the_general_time_path(monkeypatch):
+    """The scalar workload's shape with the scalar-state kernels switched off
+    (PARARNN_NO_SCALAR): the general time-parallel sweep and adjoint."""
+    monkeypatch.setenv("PARARNN_NO_SCALAR", "1")
+    p = sy.make_problem(2, T=65536)
+    check_solve(p)
+    dp = bd.DeviceProblem(p)
+    dp.solve()
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    ref = oracle.adjoint(p, dp.h.float().cpu().numpy().astype(np.float64))
+    err = float(np.abs(a["lam"].float().cpu().numpy() - ref["lam"]).max())
+    say("  general path lambda err", err)
+    assert err <= 1e-4
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 64, 65, 4095, 4096, 4097, 10001])
 def test_scalar_gru_lengths_and_ragged_tiles(T):
     p = sy.custom_problem(sy.CELL_GRU, B=3, T=T, d=2, n=1, seed=T, w_scale=1.0, h0=True)
