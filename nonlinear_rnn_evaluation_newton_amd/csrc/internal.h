@@ -149,6 +149,11 @@ struct GemmArgs {
   bool a_kc, b_kc, bf16, out_f32, vec_a, vec_b;
 };
 int gemm_splits(int M, int N, int K);
+// C[192,N] = A^T B and csum = column sums of A for K-outer fp32 A [K,192],
+// B [K,N] (N <= 64); C or csum may be null; ws of tn_workspace_bytes(K)
+size_t tn_workspace_bytes(int K);
+hipError_t launch_tn_products(const float *A, const float *B, int K, int N, float *C, float *csum, void *ws,
+                              hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
 // ---------------- utilities ------------------------------------------------

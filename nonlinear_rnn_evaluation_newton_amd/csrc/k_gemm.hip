@@ -421,6 +421,104 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Long-K fp32 products with both operands stored K-outer and a small output,
+// as the dense n = 64 adjoint's weight gradients: C[M,N] = sum_k A[k,m] B[k,n]
+// (A [K,M], B [K,N] row-major, M = 192, N <= 64), with the column sums of A
+// (bias gradients) from the same reads.  Each block takes 1024 rows of K in
+// LDS chunks of 32 and accumulates on v_mfma_f32_32x32x2_f32 (4 wavefronts,
+// 3 of the 12 32x32 output tiles each); the per-block partials are summed in
+// fp64, in block order, by k_tn_final.
+constexpr int TN_M = 192, TN_N = 64, TN_KS = 1024, TN_KC = 32;
+
+__global__ __launch_bounds__(256) void k_tn_part(const float *__restrict__ A, const float *__restrict__ B, int K,
+                                                 int N, float *__restrict__ part, float *__restrict__ cpart) {
+  __shared__ float sA[TN_KC][TN_M];
+  __shared__ float sB[TN_KC][TN_N];
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k0 = blockIdx.x * TN_KS, k1 = min(K, k0 + TN_KS);
+  f32x16_t acc[3];
+#pragma unroll
+  for (int t = 0; t < 3; t++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[t][r] = 0.f;
+  float csum = 0.f;
+  for (int kc = k0; kc < k1; kc += TN_KC) {
+    // A chunk: 32 rows x 192 = 1536 float4, 6 per thread; B chunk: 32 x N
+#pragma unroll
+    for (int q = 0; q < 6; q++) {
+      const int e = tid + 256 * q, r = e / (TN_M / 4), c4 = (e % (TN_M / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kc + r < k1) v = *reinterpret_cast<const float4 *>(A + (size_t)(kc + r) * TN_M + c4);
+      *reinterpret_cast<float4 *>(&sA[r][c4]) = v;
+    }
+    for (int e = tid; e < TN_KC * TN_N; e += 256) {
+      const int r = e / TN_N, c = e % TN_N;
+      sB[r][c] = (kc + r < k1 && c < N) ? B[(size_t)(kc + r) * N + c] : 0.f;
+    }
+    __syncthreads();
+    if (tid < TN_M) {
+#pragma unroll 8
+      for (int r = 0; r < TN_KC; r++) csum += sA[r][tid];
+    }
+#pragma unroll 4
+    for (int k2 = 0; k2 < TN_KC; k2 += 2) {
+      const int kr = k2 + (lane >> 5);
+#pragma unroll
+      for (int t = 0; t < 3; t++) {
+        const int tile = wid + 4 * t, tm = tile >> 1, tn = tile & 1;
+        const float a = sA[kr][tm * 32 + (lane & 31)], b = sB[kr][tn * 32 + (lane & 31)];
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // lane holds column n = tn*32 + (lane & 31) of rows 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+  for (int t = 0; t < 3; t++) {
+    const int tile = wid + 4 * t, tm = tile >> 1, tn = tile & 1;
+    const int n = tn * 32 + (lane & 31);
+    if (n >= N) continue;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int m = tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      part[((size_t)blockIdx.x * TN_M + m) * N + n] = acc[t][r];
+    }
+  }
+  if (tid < TN_M) cpart[(size_t)blockIdx.x * TN_M + tid] = csum;
+}
+
+__global__ __launch_bounds__(256) void k_tn_final(const float *__restrict__ part, const float *__restrict__ cpart,
+                                                  int nblk, int N, float *C, float *csum) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < TN_M * N && C) {
+    double s = 0.0;
+    for (int q = 0; q < nblk; q++) s += (double)part[(size_t)q * TN_M * N + e];
+    C[e] = (float)s;
+  }
+  if (e < TN_M && csum) {
+    double s = 0.0;
+    for (int q = 0; q < nblk; q++) s += (double)cpart[(size_t)q * TN_M + e];
+    csum[e] = (float)s;
+  }
+}
+
+size_t tn_workspace_bytes(int K) {
+  const size_t nblk = (size_t)((K + TN_KS - 1) / TN_KS);
+  return nblk * TN_M * TN_N * 4 + nblk * TN_M * 4;
+}
+
+hipError_t launch_tn_products(const float *A, const float *B, int K, int N, float *C, float *csum, void *ws,
+                              hipStream_t s) {
+  if (N < 1 || N > TN_N) return hipErrorInvalidValue;
+  const int nblk = (K + TN_KS - 1) / TN_KS;
+  float *part = (float *)ws, *cpart = part + (size_t)nblk * TN_M * TN_N;
+  hipLaunchKernelGGL(k_tn_part, dim3(nblk), dim3(256), 0, s, A, B, K, N, part, cpart);
+  hipLaunchKernelGGL(k_tn_final, dim3((TN_M * N + 255) / 256), dim3(256), 0, s, (const float *)part,
+                     (const float *)cpart, nblk, N, C, csum);
+  return hipGetLastError();
+}
+
 // Split K until the grid covers the device about twice (long-K products
 // such as dW = dU^T x have few output tiles; every split writes a full fp32
 // partial of C), keeping at least 8 K tiles per split.

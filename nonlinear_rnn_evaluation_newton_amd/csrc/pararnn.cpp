@@ -52,6 +52,7 @@ struct Plan {
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
   size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
   size_t off_red = 0;             // channel path adjoint: fp64 split sums of the weight partials
+  size_t off_tn = 0;              // dense n = 64 adjoint: partials of the K-outer weight products
   // dense n = 64 path
   int cps = 0, nchunks = 0;
   size_t off_gates = 0, off_aggP = 0, off_aggb = 0, off_carry = 0, off_dA = 0, off_hprev = 0, off_csum = 0;
@@ -143,6 +144,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
                           ? (size_t)(s1 > 1 ? s1 * 192 * p->d : 0)
                           : (size_t)(s2 > 1 ? s2 * 192 * 64 : 0);
     pl->off_gws = o; o = align256(o + gw * 4);
+    pl->off_tn = o; o = align256(o + tn_workspace_bytes(K));
     pl->adjoint_bytes = o;
     return PR_OK;
   }
@@ -639,8 +641,13 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     HIPCHK(launch_d64_adjoint_epilogue(ea, s));
     const int rows = p->B * p->T;
     double *csp = (double *)(ws + pl.off_csum);
-    if (dW && dW->b_x) HIPCHK(launch_colsum(ea.dU, rows, 192, dW->b_x, csp, s));
-    if (dW && dW->b_h) HIPCHK(launch_colsum(ea.dA, rows, 192, dW->b_h, csp, s));
+    // dW_x = dU^T x with db_x = column sums of dU, and dW_h = dA^T h_prev with
+    // db_h = column sums of dA, each from one pass over its K-outer operands
+    const bool tn_x = dW && (dW->W_x || dW->b_x) && p->d <= 64;
+    if (tn_x) HIPCHK(launch_tn_products(ea.dU, (const float *)x, rows, p->d, dW->W_x, dW->b_x, ws + pl.off_tn, s));
+    if (dW && (dW->W_h || dW->b_h))
+      HIPCHK(launch_tn_products(ea.dA, ea.hprev, rows, 64, dW->W_h, dW->b_h, ws + pl.off_tn, s));
+    if (dW && dW->b_x && !tn_x) HIPCHK(launch_colsum(ea.dU, rows, 192, dW->b_x, csp, s));
     if (dx) {  // dx = dU W_x
       GemmArgs gm{};
       gm.A = ea.dU; gm.B = w->W_x; gm.C = dx;
@@ -650,7 +657,7 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
       gm.vec_b = ((uintptr_t)w->W_x % 16 == 0) && (p->d % 4) == 0;
       HIPCHK(launch_gemm(gm, s));
     }
-    if (dW && dW->W_x) {  // dW_x = dU^T x
+    if (dW && dW->W_x && !tn_x) {  // dW_x = dU^T x (input widths past 64)
       GemmArgs gm{};
       gm.A = ea.dU; gm.B = x; gm.C = dW->W_x; gm.ws = (float *)(ws + pl.off_gws);
       gm.M = 192; gm.N = p->d; gm.K = rows; gm.lda = 192; gm.ldb = p->d; gm.ldc = p->d;
@@ -658,15 +665,6 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
       gm.a_kc = false; gm.b_kc = false; gm.bf16 = false; gm.out_f32 = true;
       gm.vec_a = true;
       gm.vec_b = ((uintptr_t)x % 16 == 0) && (p->d % 4) == 0;
-      HIPCHK(launch_gemm(gm, s));
-    }
-    if (dW && dW->W_h) {  // dW_h = dA^T h_prev
-      GemmArgs gm{};
-      gm.A = ea.dA; gm.B = ea.hprev; gm.C = dW->W_h; gm.ws = (float *)(ws + pl.off_gws);
-      gm.M = 192; gm.N = 64; gm.K = rows; gm.lda = 192; gm.ldb = 64; gm.ldc = 64;
-      gm.splits = gemm_splits(192, 64, rows);
-      gm.a_kc = false; gm.b_kc = false; gm.bf16 = false; gm.out_f32 = true;
-      gm.vec_a = true; gm.vec_b = true;
       HIPCHK(launch_gemm(gm, s));
     }
     tr.end(TR_AGEMM, tg, s);
