@@ -22,6 +22,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 OK, EINVAL, ENOMEM, NOT_CONVERGED, NONFINITE = 0, -1, -4, 1, 2
 DENSE, DIAG, BLOCK2 = 0, 1, 2
+NEWTON, QUASI, JACOBI = 0, 1, 2  # Jacobian used by a sweep: the cell's own, its diagonal, zero
 
 _lib = None
 
@@ -54,6 +55,7 @@ def _load():
         lib.orc_rollout.argtypes = [P, P, P, P]
         lib.orc_affine_solve.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P]
         lib.orc_deer.argtypes = [P, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
+        lib.orc_deer_approx.argtypes = [P, C.c_int, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
         lib.orc_adjoint.argtypes = [P] + [P] * 12
         lib.orc_num_threads.restype = C.c_int
         _lib = lib
@@ -134,8 +136,11 @@ def rollout(p: dict, x=None, h0=None):
     return h
 
 
-def deer(p: dict, tol=None, max_iters=None, x=None, h0=None, hist_cap=4096):
-    """CPU DEER: returns (h, iters, status, deltas[iters])."""
+def deer(p: dict, tol=None, max_iters=None, x=None, h0=None, hist_cap=4096, approx=NEWTON):
+    """CPU DEER: returns (h, iters, status, deltas[iters]).
+
+    approx: NEWTON (the cell's Jacobian), QUASI (its diagonal) or JACOBI (zero).
+    """
     lib = _load()
     x = _f64(p["x"] if x is None else x)
     h0 = _f64(p["h0"] if h0 is None else h0)
@@ -146,8 +151,8 @@ def deer(p: dict, tol=None, max_iters=None, x=None, h0=None, hist_cap=4096):
     h = np.zeros((B, T, p["S"]))
     it, st = C.c_int(0), C.c_int(0)
     deltas = np.zeros(hist_cap)
-    _check(lib.orc_deer(bd.ref, _ptr(x), _ptr(h0), float(tol), int(max_iters), _ptr(h),
-                        C.byref(it), C.byref(st), _ptr(deltas), hist_cap))
+    _check(lib.orc_deer_approx(bd.ref, int(approx), _ptr(x), _ptr(h0), float(tol), int(max_iters), _ptr(h),
+                               C.byref(it), C.byref(st), _ptr(deltas), hist_cap))
     return h, it.value, st.value, deltas[:min(it.value, hist_cap)].copy()
 
 

@@ -12,14 +12,16 @@
  *    DEER is measured against ("Parallelizing non-linear sequential models
  *    over the sequence length", Key results and Measured effects: sequential
  *    GRU evaluation; ParaRNN abstract: the plain one-step-at-a-time baseline).
- *  - orc_deer: Newton on the residual system F(h)_t = h_t - f(h_{t-1}, x_t) = 0
+ *  - orc_deer / orc_deer_approx: Newton on the residual system F(h)_t = h_t - f(h_{t-1}, x_t) = 0
  *    (ParaRNN abstract: the recurrences cast as one system of equations solved
  *    with Newton's iterations; Gonzalez et al. abstract: the states as the
  *    solution of a fixed-point problem; Para-Seq README, Background: linearise
  *    and solve the resulting linear recurrence).  Each sweep evaluates the cell
  *    and its Jacobian at every step, solves dh_t = J_t dh_{t-1} + r_t, and
  *    updates.  The linear recurrence is solved here by its plain sequential
- *    definition, not by a scan.  Stopping uses the single tolerance
+ *    definition, not by a scan.  orc_deer_approx replaces the Jacobian by its
+ *    diagonal (quasi-DEER) or by zero (Jacobi iteration) (Gonzalez et al.
+ *    abstract: quasi-Newton approximations; Para-Seq README, Main features).  Stopping uses the single tolerance
  *    hyperparameter of DEER (DEER summary, Limitations) on max |dh|.
  *  - orc_adjoint: the gradient of L = sum_t <g_t, h_t> by reverse-mode
  *    differentiation through the recurrence at a given trajectory (textbook
@@ -386,21 +388,55 @@ int orc_affine_solve(int kind, int B, int T, int n, int reverse, const double *A
 }
 
 /*
+ * Which Jacobian the linear solve of a sweep uses (Gonzalez et al. abstract:
+ * quasi-Newton approximations of DEER; Para-Seq README, Main features: the
+ * Jacobi, quasi-DEER and DEER solvers):
+ *   ORC_NEWTON  the cell's own Jacobian (DEER);
+ *   ORC_QUASI   its diagonal only: the entries J[i][i] of a dense Jacobian,
+ *               the two diagonal entries of each 2x2 block; a diagonal
+ *               Jacobian is kept whole (quasi-DEER);
+ *   ORC_JACOBI  zero: the sweep sets h_t to f(h_{t-1}, x_t) of the previous
+ *               iterate (Jacobi / Picard iteration).
+ * All three have the rollout as their fixed point and reproduce it exactly
+ * on steps t < k after k sweeps, so a solve also ends after sweep T.
+ */
+enum { ORC_NEWTON = 0, ORC_QUASI = 1, ORC_JACOBI = 2 };
+
+/* Apply the approximation to one step's Jacobian, stored in the cell's structure. */
+static void approx_jac(const orc_model *m, int approx, double *J) {
+  int kind = jkind(m->cell), S = swidth(m);
+  size_t js = jsize(m);
+  if (approx == ORC_JACOBI) {
+    for (size_t e = 0; e < js; e++) J[e] = 0.0;
+  } else if (approx == ORC_QUASI && kind == ORC_DENSE) {
+    for (int i = 0; i < S; i++)
+      for (int k = 0; k < S; k++)
+        if (k != i) J[(size_t)i * S + k] = 0.0;
+  } else if (approx == ORC_QUASI && kind == ORC_BLOCK2) {
+    for (int c = 0; c < m->n; c++) {
+      J[(size_t)4 * c + 1] = 0.0; /* d c' / d h */
+      J[(size_t)4 * c + 2] = 0.0; /* d h' / d c */
+    }
+  }
+}
+
+/*
  * CPU DEER.  h: [B,T,S] output (the last iterate); iters, status out;
  * deltas: [hist_cap] history of delta_k = max |dh| (entry k-1 for sweep k).
  *
  * Sweep k, for every sequence:
  *   1. for every t: s_prev = (t == 0 ? h0 : h_{t-1}) of the current iterate;
- *      f_t, J_t = cell(s_prev, U_t);  r_t = f_t - h_t;
+ *      f_t, J_t = cell(s_prev, U_t);  r_t = f_t - h_t;  J_t approximated as
+ *      `approx` says;
  *   2. dh_0-1 = 0;  for t = 0..T-1: dh_t = J_t dh_{t-1} + r_t  (sequential);
  *   3. h_t += dh_t.
  * delta_k is the max over the whole batch.  Stop rule: non-finite delta ->
- * NONFINITE; tol > 0 and delta < tol -> OK; k == T -> OK (Newton is exact
- * after T sweeps); k == max_iters -> NOT_CONVERGED (OK when tol <= 0).
+ * NONFINITE; tol > 0 and delta < tol -> OK; k == T -> OK (every variant is
+ * exact after T sweeps); k == max_iters -> NOT_CONVERGED (OK when tol <= 0).
  */
-int orc_deer(const orc_model *m, const double *x, const double *h0, double tol, int max_iters,
-             double *h, int *iters, int *status, double *deltas, int hist_cap) {
-  if (!model_ok(m) || max_iters < 1) return ORC_EINVAL;
+int orc_deer_approx(const orc_model *m, int approx, const double *x, const double *h0, double tol, int max_iters,
+                    double *h, int *iters, int *status, double *deltas, int hist_cap) {
+  if (!model_ok(m) || max_iters < 1 || approx < ORC_NEWTON || approx > ORC_JACOBI) return ORC_EINVAL;
   int S = swidth(m), Gn = n_gates(m->cell) * m->n, T = m->T;
   size_t js = jsize(m);
   int kind = jkind(m->cell);
@@ -428,6 +464,7 @@ int orc_deer(const orc_model *m, const double *x, const double *h0, double tol, 
           const double *sp = t == 0 ? (h0 ? h0 + (size_t)b * S : zero) : hb + (size_t)(t - 1) * S;
           input_proj(m, x + ((size_t)b * T + t) * m->d, U);
           cell_fwd(m, sp, U, F + (size_t)t * S, Jb + (size_t)t * js);
+          approx_jac(m, approx, Jb + (size_t)t * js);
           for (int i = 0; i < S; i++) R[(size_t)t * S + i] = F[(size_t)t * S + i] - hb[(size_t)t * S + i];
         }
         /* 2. the linear recurrence, sequentially. */
@@ -454,6 +491,12 @@ int orc_deer(const orc_model *m, const double *x, const double *h0, double tol, 
   }
   *status = tol > 0.0 ? ORC_NOT_CONVERGED : ORC_OK;
   return ORC_OK;
+}
+
+/* DEER with the cell's own Jacobian. */
+int orc_deer(const orc_model *m, const double *x, const double *h0, double tol, int max_iters, double *h,
+             int *iters, int *status, double *deltas, int hist_cap) {
+  return orc_deer_approx(m, ORC_NEWTON, x, h0, tol, max_iters, h, iters, status, deltas, hist_cap);
 }
 
 /*

@@ -15,6 +15,11 @@ sign or index, a transposed operand) fails at least one test:
 * special cases: zero recurrence (Jacobi-like, exact after one update), a
   linear cell (Newton exact in one update), a dense GRU with diagonal weights
   equal to the diagonal GRU;
+* the approximate-Jacobian sweeps: Jacobi equals the Picard iteration run
+  with torch.nn layers one step at a time; quasi-DEER equals Newton where the
+  Jacobian is diagonal, equals Jacobi for a tanh RNN whose recurrent matrix
+  has a zero diagonal, and equals Newton on the LSTM cell state when that
+  state does not depend on h; both reach the rollout;
 * quadratic convergence (DEER summary, Approach) and the [-1, 1] bound of the
   gated cells' states.
 """
@@ -274,16 +279,18 @@ def test_fixed_point_is_rollout(cfg, kw):
     np.testing.assert_allclose(h, h_seq, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("approx", [oracle.NEWTON, oracle.QUASI, oracle.JACOBI])
 @pytest.mark.parametrize("cell", LIB_CELLS + [sy.CELL_LINEAR])
-def test_prefix_exactness_any_jacobian(cell):
-    # a strongly non-contractive recurrence: Newton still fixes one more step per sweep
+def test_prefix_exactness_any_jacobian(cell, approx):
+    # a strongly non-contractive recurrence: every variant still fixes one more step per sweep
     p = sy.custom_problem(cell, B=2, T=8, d=2, n=4, seed=9, w_scale=2.0, h0=True)
     h_seq = oracle.rollout(p)
     for k in range(1, p["T"] + 1):
-        h, iters, status, _ = oracle.deer(p, tol=0.0, max_iters=k)
+        h, iters, status, _ = oracle.deer(p, tol=0.0, max_iters=k, approx=approx)
         assert iters == k and status == oracle.OK
-        np.testing.assert_allclose(h[:, :k], h_seq[:, :k], rtol=0, atol=1e-13)
-    assert np.abs(h - h_seq).max() < 1e-13
+        # (the linear cell's states grow to ~1e3 here: a relative bound of a few ulps)
+        np.testing.assert_allclose(h[:, :k], h_seq[:, :k], rtol=1e-14, atol=1e-13)
+    np.testing.assert_allclose(h, h_seq, rtol=1e-14, atol=1e-13)
 
 
 def test_hand_worked_scalar_tanh():
@@ -426,3 +433,99 @@ def test_affine_solve_geometric_closed_form():
     y = oracle.affine_solve(oracle.DIAG, A, b)[0, :, 0]
     t = np.arange(T)
     np.testing.assert_allclose(y, (1 - a ** (t + 1)) / (1 - a), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# quasi-DEER (diagonal Jacobian) and Jacobi (zero Jacobian) sweeps
+# ---------------------------------------------------------------------------
+def torch_step_all(p, m, x, s_prev):
+    """f(s_prev[b, t], x[b, t]) for every (b, t) at once: a torch layer run one step on B*T rows."""
+    B, T, d = x.shape
+    n = p["n"]
+    xr = x.reshape(B * T, 1, d)
+    if p["cell"] == sy.CELL_LSTM_CIFG_DIAG:
+        c_prev = s_prev[..., 0::2].reshape(1, B * T, n).contiguous()
+        h_prev = s_prev[..., 1::2].reshape(1, B * T, n).contiguous()
+        _, (hn, cn) = m(xr, (h_prev, c_prev))
+        return torch.stack([cn[0], hn[0]], -1).reshape(B, T, 2 * n)
+    out, _ = m(xr, s_prev.reshape(1, B * T, n).contiguous())
+    return out.reshape(B, T, n)
+
+
+def picard(p, k):
+    """k Picard iterations h_t <- f(h_{t-1}, x_t) from h = 0, with torch.nn cells."""
+    m = torch_layer(p)
+    x, h0 = _t(p["x"]), _t(p["h0"])
+    h = torch.zeros(x.shape[0], x.shape[1], p["S"])
+    with torch.no_grad():
+        for _ in range(k):
+            h = torch_step_all(p, m, x, torch.cat([h0[:, None], h[:, :-1]], 1))
+    return h.numpy()
+
+
+@pytest.mark.parametrize("cell", LIB_CELLS)
+def test_jacobi_is_picard_iteration(cell):
+    p = small_problem(cell, peep_zero=True)
+    for k in range(1, p["T"] + 1):
+        h, iters, status, _ = oracle.deer(p, tol=0.0, max_iters=k, approx=oracle.JACOBI)
+        assert iters == k and status == oracle.OK
+        np.testing.assert_allclose(h, picard(p, k), rtol=0, atol=1e-13)
+
+
+def test_quasi_equals_newton_where_the_jacobian_is_diagonal():
+    # the diagonal GRU (its Jacobian is diagonal), the same GRU written with
+    # dense diagonal matrices, and dense cells of one channel
+    g = sy.custom_problem(sy.CELL_GRU_DIAG, B=2, T=30, d=3, n=5, seed=4, w_scale=0.9)
+    n = g["n"]
+    dense = dict(g, cell=sy.CELL_GRU, jac=sy.JAC_DENSE,
+                 W_h=np.concatenate([np.diag(g["W_h"][k * n:(k + 1) * n]) for k in range(3)]))
+    probs = [g, dense, sy.custom_problem(sy.CELL_GRU, B=2, T=30, d=2, n=1, seed=5, w_scale=1.5),
+             sy.custom_problem(sy.CELL_TANH_RNN, B=2, T=30, d=2, n=1, seed=6, w_scale=1.5)]
+    for p in probs:
+        for k in (1, 2, 3, 6):
+            hn_, _, _, dn = oracle.deer(p, tol=0.0, max_iters=k)
+            hq, _, _, dq = oracle.deer(p, tol=0.0, max_iters=k, approx=oracle.QUASI)
+            np.testing.assert_allclose(hq, hn_, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(dq, dn, rtol=1e-12, atol=1e-15)
+
+
+def test_quasi_tanh_rnn_with_hollow_weights_is_jacobi():
+    # J = diag(1 - f^2) W_h: with a zero diagonal in W_h the quasi Jacobian is
+    # zero, so quasi-DEER must produce the Picard iterates; any off-diagonal
+    # entry it kept would show
+    p = sy.custom_problem(sy.CELL_TANH_RNN, B=3, T=10, d=3, n=4, seed=8, w_scale=1.2)
+    p["W_h"] = p["W_h"] - np.diag(np.diag(p["W_h"]))
+    for k in range(1, p["T"] + 1):
+        hq, _, _, _ = oracle.deer(p, tol=0.0, max_iters=k, approx=oracle.QUASI)
+        np.testing.assert_allclose(hq, picard(p, k), rtol=0, atol=1e-13)
+    hn_, _, _, _ = oracle.deer(p, tol=0.0, max_iters=2)
+    assert np.abs(hn_ - picard(p, 2)).max() > 1e-3  # Newton itself differs
+
+
+def test_quasi_lstm_cell_state_is_newton_when_it_ignores_h():
+    # with w_f = w_g = 0 the cell state c follows c' = f(c) c + (1 - f(c)) g on
+    # its own, and its Jacobian d c'/d c is the kept diagonal entry: quasi and
+    # Newton then produce the same c at every sweep, while h (whose Jacobian
+    # row loses d h'/d c) differs
+    p = sy.custom_problem(sy.CELL_LSTM_CIFG_DIAG, B=2, T=24, d=3, n=4, seed=11, w_scale=0.9)
+    n = p["n"]
+    p["W_h"] = p["W_h"].copy()
+    p["W_h"][:2 * n] = 0.0
+    for k in (1, 2, 3, 5):
+        hn_, _, _, _ = oracle.deer(p, tol=0.0, max_iters=k)
+        hq, _, _, _ = oracle.deer(p, tol=0.0, max_iters=k, approx=oracle.QUASI)
+        np.testing.assert_allclose(hq[..., 0::2], hn_[..., 0::2], rtol=0, atol=1e-14)
+        if k <= 3:  # (by sweep 5 both have nearly converged)
+            assert np.abs(hq[..., 1::2] - hn_[..., 1::2]).max() > 1e-4
+
+
+@pytest.mark.parametrize("approx", [oracle.QUASI, oracle.JACOBI])
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (4, dict(T=128, n=16, d=16)), (5, dict(B=2, T=256))])
+def test_approximate_sweeps_reach_the_rollout(cfg, kw, approx):
+    p = sy.make_problem(cfg, **kw)
+    h, iters, status, dl = oracle.deer(p, tol=1e-11, max_iters=p["T"], approx=approx)
+    assert status == oracle.OK and iters < p["T"]
+    np.testing.assert_allclose(h, oracle.rollout(p), rtol=0, atol=1e-10)
+    # linear, not quadratic, convergence: later ratios stay bounded away from 0
+    r = dl[-4:-1] / dl[-5:-2]
+    assert np.all(r > 1e-3)
