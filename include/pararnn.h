@@ -54,10 +54,22 @@ extern "C" {
  * exact after one update.                                          G = 1, S = n */
 #define PR_CELL_LINEAR 4
 
-/* ---- Jacobian structure used by the Newton linear solve ------------------ */
-#define PR_JAC_DENSE 0   /* n x n per step: TANH_RNN, GRU, LINEAR                */
-#define PR_JAC_DIAG 1    /* n per step: GRU_DIAG (exact); GRU with n == 1         */
-#define PR_JAC_BLOCK2 2  /* 2x2 per channel: LSTM_CIFG_DIAG                       */
+/* ---- Jacobian used by the linear solve of each sweep --------------------- */
+/* The cell's own structure gives Newton (DEER).  A simpler one gives a
+ * quasi-Newton sweep with the same fixed point (Gonzalez et al. abstract:
+ * quasi-Newton approximations converge comparably, use less memory and are
+ * faster; Para-Seq README, Main features: Jacobi, quasi-DEER and DEER
+ * solvers): every variant reproduces the sequential evaluation exactly on
+ * the first k steps after k sweeps, so a solve still ends by sweep T.  Only
+ * the solve changes; residuals, updates and pararnn_adjoint use the cell's
+ * exact Jacobian whatever jac the solve used.                                */
+#define PR_JAC_DENSE 0   /* n x n per step: Newton for TANH_RNN, GRU, LINEAR     */
+#define PR_JAC_DIAG 1    /* the diagonal: Newton for GRU_DIAG (and dense cells with
+                            n == 1); quasi-DEER for the other cells (the LSTM
+                            keeps dc'/dc and dh'/dh of each 2x2 block)           */
+#define PR_JAC_BLOCK2 2  /* 2x2 per channel: Newton for LSTM_CIFG_DIAG           */
+#define PR_JAC_ZERO 3    /* none: Jacobi (Picard) sweeps h_t <- f(h_{t-1}, x_t),
+                            any cell                                             */
 
 /* ---- storage dtype of x, weights, h0, h, g, lambda, dx, dh0 -------------- */
 /* Arithmetic, scan carries and the convergence measure are always fp32.
@@ -76,7 +88,7 @@ extern "C" {
 
 typedef struct {
   int cell;   /* PR_CELL_*                              */
-  int jac;    /* PR_JAC_*, must suit the cell (above)   */
+  int jac;    /* PR_JAC_*: the cell's own, DIAG or ZERO  */
   int dtype;  /* PR_F32 or PR_BF16                      */
   int B;      /* batch (independent sequences), >= 1    */
   int T;      /* sequence length, >= 1                  */
@@ -108,7 +120,11 @@ typedef struct {
 size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint);
 
 /*
- * Newton solve of the recurrence from the initial guess h = 0 everywhere.
+ * Newton (or, per p->jac, quasi-Newton or Jacobi) solve of the recurrence
+ * from the initial guess h = 0 everywhere.  Kernels exist for: TANH_RNN, GRU
+ * and LINEAR with n <= 8 (fp32, any jac); GRU with n = 64 (fp32; DENSE, DIAG
+ * or ZERO); GRU_DIAG and LSTM_CIFG_DIAG (fp32 or bf16, any jac that suits
+ * them).  Other problems return PR_EUNSUPPORTED.
  *   x     [B, T, d]                input sequence
  *   h0    [B, S] or NULL (= 0)     state before the first step
  *   tol   stop when delta_k = max over (b, t, i) of |dh| is < tol; tol <= 0

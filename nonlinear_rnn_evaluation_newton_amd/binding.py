@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "libpararnn.so")
 PR_OK, PR_EINVAL, PR_EWORKSPACE, PR_EHIP, PR_EUNSUPPORTED = 0, -1, -2, -3, -5
 PR_NOT_CONVERGED, PR_NONFINITE = 1, 2
 PR_F32, PR_BF16 = 0, 1
-PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2 = 0, 1, 2
+PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3
 
 EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_scan_workspace_bytes",
            "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",

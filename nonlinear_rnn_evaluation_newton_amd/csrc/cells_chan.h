@@ -23,10 +23,12 @@ struct ChanW {  // per-channel weights (fp32)
   float p0, p1;      // LSTM peepholes p_f, p_o
 };
 
-// f and J at state s (SW values) with projection U (3 gates).
+// f and J at state s (SW values) with projection U (3 gates).  CELL carries
+// the approximation in its upper bits (cell_apx): the LSTM's diagonal keeps
+// dc'/dc and dh'/dh; zero drops every entry.
 template <int CELL>
 __device__ inline void chan_cell(const float *s, const float *U, const ChanW &w, float *f, float *J) {
-  if constexpr (CELL == C_GRU_DIAG) {
+  if constexpr (cell_code(CELL) == C_GRU_DIAG) {
     const float h = s[0];
     const float r = fsigm(fmaf(w.a0, h, U[0] + w.b0));
     const float z = fsigm(fmaf(w.a1, h, U[1] + w.b1));
@@ -53,6 +55,14 @@ __device__ inline void chan_cell(const float *s, const float *U, const ChanW &w,
     J[1] = dch;
     J[2] = dhdcn * dcc;
     J[3] = fmaf(oo, w.a2, dhdcn * dch);
+  }
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1;
+  if constexpr (cell_apx(CELL) == APX_ZERO) {
+#pragma unroll
+    for (int i = 0; i < SW * SW; i++) J[i] = 0.f;
+  } else if constexpr (cell_apx(CELL) == APX_DIAG && SW == 2) {
+    J[1] = 0.f;
+    J[2] = 0.f;
   }
 }
 

@@ -32,6 +32,17 @@ enum { ST_OK = 0, ST_NOT_CONVERGED = 1, ST_NONFINITE = 2 };
 
 // kernel-side cell codes (same values as the ABI's PR_CELL_*)
 enum { C_TANH = 0, C_GRU = 1, C_GRU_DIAG = 2, C_LSTM = 3, C_LINEAR = 4 };
+
+// The Jacobian a sweep's linear solve uses: the cell's own (Newton, DEER),
+// its diagonal (quasi-DEER), or zero (Jacobi) (Gonzalez et al. abstract:
+// quasi-Newton approximations; Para-Seq README, Main features: Jacobi,
+// quasi-DEER and DEER solvers).  Only the solve changes: the residual, the
+// update and the adjoint use the cell itself.
+enum { APX_NEWTON = 0, APX_DIAG = 1, APX_ZERO = 2 };
+// Channel kernels take the approximation in the cell template argument:
+// cell code + 16 * approximation.
+constexpr int cell_code(int CELL) { return CELL & 15; }
+constexpr int cell_apx(int CELL) { return CELL >> 4; }
 __host__ __device__ constexpr int cell_gates(int cell) {
   return (cell == C_GRU || cell == C_GRU_DIAG || cell == C_LSTM) ? 3 : 1;
 }

@@ -32,6 +32,7 @@ struct TimeArgs {
   int tiles_per_seq, ntiles, vec_ok;
   int nparts;  // adjoint: blocks that wrote weight partials (set by the launcher)
   const float *coef;  // scalar-state sweep: cell coefficients folded from the weights
+  int approx;         // sweep: APX_NEWTON, APX_DIAG or APX_ZERO (not the scalar-state sweep)
 };
 
 int time_tile(int N);               // elements per tile for padded width N
@@ -93,7 +94,8 @@ ChanGeomInfo chan_geom(int cell, int n);  // tiles of the standalone scan
 constexpr int CHAN2_TT = 64;
 enum { CHAN2_FIRST = 0, CHAN2_CARRY = 1, CHAN2_APPLY_NEXT = 2, CHAN2_APPLY = 3 };
 ChanGeomInfo chan2_geom(int cell, int n);
-hipError_t launch_chan2(int cell, bool bf16, const ChanArgs &a, int what, hipStream_t s);
+// apx: APX_NEWTON, APX_DIAG (LSTM) or APX_ZERO
+hipError_t launch_chan2(int cell, int apx, bool bf16, const ChanArgs &a, int what, hipStream_t s);
 // adjoint as streaming passes on the same tiles (aggregates, reverse carry
 // scan, apply); per-tile weight partials [tiles][CH][11]
 hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s);
@@ -123,8 +125,11 @@ struct D64Args {
   int max_iters;
   SolveState *st;
   int adjoint;          // reverse-time scan with transposed Jacobians
+  int approx;           // sweep: APX_NEWTON (dense chunk products) or APX_DIAG / APX_ZERO (per-channel scan)
 };
-// one sweep = part 0 (gates), part 1 (chunk products), part 2 (carries + replay)
+// one sweep = part 0 (gates), part 1 (chunk products), part 2 (carries + replay);
+// with a.approx != APX_NEWTON: part 0 (gates, diagonal Jacobian, chunk
+// aggregates), part 1 (carries), part 2 (apply)
 hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s);
 hipError_t launch_d64_adjoint_scan(D64Args &a, hipStream_t s);
 struct D64AdjArgs {

@@ -24,6 +24,10 @@
 // waits for another, so there is no look-back latency and no co-residency
 // requirement.  Both sides of a tile boundary use the stored (rounded) state
 // of the previous tile's last step, so aggregates and updates agree exactly.
+//
+// The sweep kernels' cell argument may carry a Jacobian approximation
+// (cell_apx: the 2x2 blocks' diagonal, or zero for Jacobi sweeps); it changes
+// the operator of the linear recurrence and nothing else.
 #include <type_traits>
 
 #include "k_chan_impl.h"
@@ -88,7 +92,7 @@ __device__ inline void state_before(const ChanArgs &a, int k, int t0, int b, int
 
 template <int CELL, typename ST, int CPL, bool APPLY, bool NEXT>
 __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
   constexpr int UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>(), TT = CHAN2_TT;
   __shared__ int s_stop;
   __shared__ unsigned s_dmax[4];
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
 // the range totals combined in LDS, then the exclusive prefix walked again.
 template <int CELL, typename ST, int CPL>
 __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, TT = CHAN2_TT;
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, TT = CHAN2_TT;
   constexpr int R = C2_R;
   __shared__ float s_tot[C2_CW][CH][AW];
   __shared__ int s_skip;
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
 // ---------------------------------------------------------------------------
 template <int CELL, typename ST, int CPL, bool APPLY>
 __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
   constexpr int UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>(), TT = CHAN2_TT;
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = blockIdx.x * 4 + wid;
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_adj_carry(const ChanArgs a)
 
 template <int CELL, typename ST, int CPL>
 static hipError_t chan2_adj_launch(const ChanArgs &a, hipStream_t s) {
-  constexpr int SW = CELL == C_LSTM ? 2 : 1;
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1;
   const unsigned grid = (unsigned)((a.ntiles + 3) / 4);
   hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, false>), dim3(grid), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_chan_adj_carry<SW, CPL>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
@@ -714,15 +718,24 @@ static hipError_t chan2_launch(const ChanArgs &a, int what, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_chan2(int cell, bool bf16, const ChanArgs &a, int what, hipStream_t s) {
-  const ChanGeomInfo g = chan2_geom(cell, a.n);
-  if (cell == C_GRU_DIAG) {
-    if (g.CPL == 2)
-      return bf16 ? chan2_launch<C_GRU_DIAG, uint16_t, 2>(a, what, s) : chan2_launch<C_GRU_DIAG, float, 2>(a, what, s);
-    return bf16 ? chan2_launch<C_GRU_DIAG, uint16_t, 1>(a, what, s) : chan2_launch<C_GRU_DIAG, float, 1>(a, what, s);
+template <int CELL>
+static hipError_t chan2_dtype(bool bf16, int CPL, const ChanArgs &a, int what, hipStream_t s) {
+  if constexpr (cell_code(CELL) == C_GRU_DIAG) {
+    if (CPL == 2) return bf16 ? chan2_launch<CELL, uint16_t, 2>(a, what, s) : chan2_launch<CELL, float, 2>(a, what, s);
   }
-  if (cell == C_LSTM)
-    return bf16 ? chan2_launch<C_LSTM, uint16_t, 1>(a, what, s) : chan2_launch<C_LSTM, float, 1>(a, what, s);
+  return bf16 ? chan2_launch<CELL, uint16_t, 1>(a, what, s) : chan2_launch<CELL, float, 1>(a, what, s);
+}
+
+hipError_t launch_chan2(int cell, int apx, bool bf16, const ChanArgs &a, int what, hipStream_t s) {
+  const int CPL = chan2_geom(cell, a.n).CPL;
+  if (cell == C_GRU_DIAG) {  // its Jacobian is diagonal: the diagonal approximation is exact
+    if (apx == APX_NEWTON || apx == APX_DIAG) return chan2_dtype<C_GRU_DIAG>(bf16, CPL, a, what, s);
+    if (apx == APX_ZERO) return chan2_dtype<C_GRU_DIAG + 16 * APX_ZERO>(bf16, CPL, a, what, s);
+  } else if (cell == C_LSTM) {
+    if (apx == APX_NEWTON) return chan2_dtype<C_LSTM>(bf16, CPL, a, what, s);
+    if (apx == APX_DIAG) return chan2_dtype<C_LSTM + 16 * APX_DIAG>(bf16, CPL, a, what, s);
+    if (apx == APX_ZERO) return chan2_dtype<C_LSTM + 16 * APX_ZERO>(bf16, CPL, a, what, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -32,6 +32,39 @@ constexpr int WLD = 68;  // padded LDS row stride (floats) of 64-wide matrices
 
 __device__ inline int r0_of(int r) { return 8 * (r >> 2) + (r & 3); }
 
+// Gate pre-activations of 64 rows on MFMA: sC[row][0..191] = (W_h s_row)
+// for the states in sH (rows x 64, stride WLD); sW holds W_h [192][64]
+// (stride WLD) and is overwritten by sC ([64][D64_CLD]).  Ends with a block
+// barrier.
+constexpr int D64_CLD = 196;
+__device__ inline void d64_preacts(const float *sH, float *sW) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // [64 rows] x [192 gate channels], K = 64: wave w owns row block (w & 1)
+  // and column blocks 3*(w >> 1) + {0, 1, 2}
+  const int rb = wid & 1, cb0 = 3 * (wid >> 1);
+  f32x16_d acc[3];
+#pragma unroll
+  for (int q = 0; q < 3; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[q][r] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < 32; s++) {
+    const int kk = 2 * s + (lane >> 5);
+    const float av = sH[(rb * 32 + (lane & 31)) * WLD + kk];
+#pragma unroll
+    for (int q = 0; q < 3; q++)
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sW[((cb0 + q) * 32 + (lane & 31)) * WLD + kk], acc[q], 0, 0, 0);
+  }
+  __syncthreads();
+  float *sC = sW;
+#pragma unroll
+  for (int q = 0; q < 3; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      sC[(rb * 32 + r0_of(r) + 4 * (lane >> 5)) * D64_CLD + (cb0 + q) * 32 + (lane & 31)] = acc[q][r];
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // 1. gates (sweep: z, alpha, beta, gamma, res;  adjoint: z, alpha, beta, gamma, eta)
 // ---------------------------------------------------------------------------
@@ -63,31 +96,9 @@ __global__ __launch_bounds__(256) void k_d64_gates(const D64Args a) {
     *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = v;
   }
   __syncthreads();
-  // [64 rows] x [192 gate channels], K = 64: wave w owns row block (w & 1)
-  // and column blocks 3*(w >> 1) + {0, 1, 2}
-  const int rb = wid & 1, cb0 = 3 * (wid >> 1);
-  f32x16_d acc[3];
-#pragma unroll
-  for (int q = 0; q < 3; q++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) acc[q][r] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < 32; s++) {
-    const int kk = 2 * s + (lane >> 5);
-    const float av = sH[(rb * 32 + (lane & 31)) * WLD + kk];
-#pragma unroll
-    for (int q = 0; q < 3; q++)
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sW[((cb0 + q) * 32 + (lane & 31)) * WLD + kk], acc[q], 0, 0, 0);
-  }
-  __syncthreads();
-  constexpr int CLD = 196;
-  float *sC = sW;  // reuse: [64][196]
-#pragma unroll
-  for (int q = 0; q < 3; q++)
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-      sC[(rb * 32 + r0_of(r) + 4 * (lane >> 5)) * CLD + (cb0 + q) * 32 + (lane & 31)] = acc[q][r];
-  __syncthreads();
+  d64_preacts(sH, sW);
+  constexpr int CLD = D64_CLD;
+  const float *sC = sW;
   const int i = lane;
   const float bhr = a.bh ? a.bh[i] : 0.f, bhz = a.bh ? a.bh[64 + i] : 0.f, bhn = a.bh ? a.bh[128 + i] : 0.f;
   for (int rr = wid; rr < 64; rr += 4) {
@@ -476,9 +487,193 @@ __global__ __launch_bounds__(256) void k_colsum_final(const double *part, int co
 }
 
 // ---------------------------------------------------------------------------
+// quasi-DEER and Jacobi sweeps: J_t replaced by its diagonal, or by zero
+// ---------------------------------------------------------------------------
+// The GRU Jacobian's diagonal is
+//   J_ii = z_i + alpha_i W_hz[i][i] + beta_i W_hn[i][i] + gamma_i W_hr[i][i]
+// (alpha, beta, gamma as in the gates kernel), so the linear recurrence
+// splits into 64 scalar ones per sequence and costs O(n) per step instead of
+// the chunk products' O(n^3) (Gonzalez et al. abstract: quasi-Newton
+// approximations converge comparably, use less memory and are faster).
+// A sweep is three launches over chunks of D64_L steps:
+//  1. k_d64q_gates: one block per chunk: W_h h_{t-1} on MFMA, the gates, the
+//     diagonal J_t and r_t (stored [row][J | r]), and the chunk's aggregate
+//     per channel (A = product of J, b), stored channel-major [b][i][chunk];
+//  2. k_d64q_carry: one wavefront per (sequence, channel), lane = chunk: an
+//     inclusive scan of the aggregates gives the state entering each chunk;
+//  3. k_d64q_apply: one wavefront per chunk, lane = channel: dh_t = J_t
+//     dh_{t-1} + r_t from the carry, h += dh, max |dh|.
+__global__ __launch_bounds__(256) void k_d64q_gates(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ __attribute__((aligned(16))) float sH[64 * WLD];
+  __shared__ __attribute__((aligned(16))) float sW[192 * WLD];
+  __shared__ float sAgg[4][2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
+  const int T = a.T, cps = a.cps, chunk = blockIdx.x;
+  const int b = chunk / cps, j = chunk % cps;
+  const int t0 = j * D64_L, nr = min(D64_L, T - t0);
+  const size_t row0 = (size_t)b * T + t0;
+  const bool first = a.k == 1;  // the iterate is h = 0 before sweep 1
+  for (int e = tid; e < 192 * 16; e += 256) {
+    const int row = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<float4 *>(&sW[row * WLD + c4]) = *reinterpret_cast<const float4 *>(a.Wh + row * 64 + c4);
+  }
+  for (int e = tid; e < 64 * 16; e += 256) {
+    const int rr = e >> 4, c4 = (e & 15) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rr < nr) {
+      if (t0 + rr > 0) {
+        if (!first) v = *reinterpret_cast<const float4 *>(a.h + (row0 + rr - 1) * 64 + c4);
+      } else if (a.h0) {
+        v = *reinterpret_cast<const float4 *>(a.h0 + (size_t)b * 64 + c4);
+      }
+    }
+    *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = v;
+  }
+  __syncthreads();
+  d64_preacts(sH, sW);
+  float *sC = sW;
+  constexpr int CLD = D64_CLD;
+  const int i = lane;
+  const float bhr = a.bh ? a.bh[i] : 0.f, bhz = a.bh ? a.bh[64 + i] : 0.f, bhn = a.bh ? a.bh[128 + i] : 0.f;
+  const float wr = a.Wh[i * 64 + i], wz = a.Wh[(64 + i) * 64 + i], wn = a.Wh[(128 + i) * 64 + i];
+  const bool diag = a.approx == APX_DIAG;
+  for (int rr = wid; rr < nr; rr += 4) {
+    const size_t row = row0 + rr;
+    const float *Ur = a.U + row * 192;
+    const float ar = sC[rr * CLD + i] + Ur[i] + bhr;
+    const float az = sC[rr * CLD + 64 + i] + Ur[64 + i] + bhz;
+    const float q = sC[rr * CLD + 128 + i] + bhn;
+    const float sv = sH[rr * WLD + i];
+    const float r = fsigm(ar), z = fsigm(az);
+    const float c = ftanh(fmaf(r, q, Ur[128 + i]));
+    const float f = fmaf(z, sv - c, c);
+    const float be = (1.f - z) * (1.f - c * c);
+    const float Jd = diag ? z + (sv - c) * z * (1.f - z) * wz + be * r * (wn + q * (1.f - r) * wr) : 0.f;
+    const float res = f - (first ? 0.f : a.h[row * 64 + i]);
+    a.gates[row * 128 + i] = Jd;
+    a.gates[row * 128 + 64 + i] = res;
+    // this lane's own entries of row rr, already read
+    sC[rr * CLD + i] = Jd;
+    sC[rr * CLD + 64 + i] = res;
+  }
+  __syncthreads();
+  // chunk aggregate: wavefront w composes rows [16w, 16w + 16), wavefront 0
+  // composes the four
+  {
+    float A = 1.f, B = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      const int rr = wid * 16 + q;
+      if (rr < nr) {
+        const float Jv = sC[rr * CLD + i], rv = sC[rr * CLD + 64 + i];
+        B = fmaf(Jv, B, rv);
+        A *= Jv;
+      }
+    }
+    sAgg[wid][0][i] = A;
+    sAgg[wid][1][i] = B;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    float A = sAgg[0][0][i], B = sAgg[0][1][i];
+#pragma unroll
+    for (int w = 1; w < 4; w++) {
+      B = fmaf(sAgg[w][0][i], B, sAgg[w][1][i]);
+      A *= sAgg[w][0][i];
+    }
+    const size_t o = ((size_t)b * 64 + i) * cps + j;
+    a.aggP[o] = A;
+    a.aggb[o] = B;
+  }
+}
+
+// One wavefront per (sequence, channel); lanes take 64 chunks at a time.
+__global__ __launch_bounds__(256) void k_d64q_carry(const D64Args a) {
+  __shared__ int s_stop;
+  if (sweep_is_stopped(a.st, &s_stop)) return;
+  const int lane = threadIdx.x & 63, sc = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sc >= a.B * 64) return;
+  const int b = sc >> 6, i = sc & 63, cps = a.cps;
+  const float *Ap = a.aggP + (size_t)sc * cps, *Bp = a.aggb + (size_t)sc * cps;
+  float c = 0.f;  // state entering the current group of chunks
+  for (int g0 = 0; g0 < cps; g0 += 64) {
+    const int jj = g0 + lane;
+    float A = jj < cps ? Ap[jj] : 1.f, B = jj < cps ? Bp[jj] : 0.f;
+    // inclusive scan of the maps y -> A y + B, earlier lanes applied first
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float Ae = __shfl_up(A, off, 64), Be = __shfl_up(B, off, 64);
+      if (lane >= off) {
+        B = fmaf(A, Be, B);
+        A *= Ae;
+      }
+    }
+    const float Ai = __shfl_up(A, 1, 64), Bi = __shfl_up(B, 1, 64);
+    if (jj < cps) a.carry[((size_t)b * cps + jj) * 64 + i] = lane == 0 ? c : fmaf(Ai, c, Bi);
+    // lanes past the last chunk hold the identity, so lane 63 has the group's map
+    c = fmaf(__shfl(A, 63, 64), c, __shfl(B, 63, 64));
+  }
+}
+
+// One wavefront per chunk, lane = channel.
+__global__ __launch_bounds__(256) void k_d64q_apply(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ unsigned s_dmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (sweep_is_stopped(a.st, &s_stop)) return;
+  const int chunk = blockIdx.x * 4 + wid;
+  unsigned dmax = 0;
+  if (chunk < a.nchunks) {
+    const int T = a.T, b = chunk / a.cps, j = chunk % a.cps;
+    const int t0 = j * D64_L, nr = min(D64_L, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    const int i = lane;
+    const bool first = a.k == 1;
+    float y = a.carry[(size_t)chunk * 64 + i];
+    constexpr int U = 16;  // rows whose loads are issued together
+    for (int s0 = 0; s0 < nr; s0 += U) {
+      float Jv[U], rv[U], hv[U];
+#pragma unroll
+      for (int q = 0; q < U; q++) {
+        const size_t row = row0 + s0 + q;
+        const bool ok = s0 + q < nr;
+        Jv[q] = ok ? a.gates[row * 128 + i] : 0.f;
+        rv[q] = ok ? a.gates[row * 128 + 64 + i] : 0.f;
+        hv[q] = (ok && !first) ? a.h[row * 64 + i] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < U; q++) {
+        if (s0 + q < nr) {
+          y = fmaf(Jv[q], y, rv[q]);
+          a.h[(row0 + s0 + q) * 64 + i] = hv[q] + y;
+          const unsigned u = __float_as_uint(fabsf(y));
+          dmax = u > dmax ? u : dmax;
+        }
+      }
+    }
+  }
+  dmax = wave_max_u32(dmax);
+  if (lane == 0) s_dmax[wid] = dmax;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned m = s_dmax[0];
+    for (int q = 1; q < 4; q++) m = s_dmax[q] > m ? s_dmax[q] : m;
+    max_agent(&a.st->dslot[a.k & 3][blockIdx.x % PR_DSHARDS], m);
+  }
+}
+
+// ---------------------------------------------------------------------------
 hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s) {
   a.adjoint = 0;
   const int rows = a.B * a.T;
+  if (a.approx != APX_NEWTON) {
+    if (part == 0) hipLaunchKernelGGL(k_d64q_gates, dim3(a.nchunks), dim3(256), 0, s, a);
+    if (part == 1) hipLaunchKernelGGL(k_d64q_carry, dim3((a.B * 64 + 3) / 4), dim3(256), 0, s, a);
+    if (part == 2) hipLaunchKernelGGL(k_d64q_apply, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (part == 0) hipLaunchKernelGGL(k_d64_gates<false>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
   if (part == 1) hipLaunchKernelGGL(k_d64_scanA<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
   if (part == 2) {

@@ -351,6 +351,13 @@ __global__ __launch_bounds__(256) void k_time_sweep(const TimeArgs a) {
           float U[G * N], f[N];
           input_proj<N, G, DX>(sWx, sbx, R.x[q][v], U);
           dense_cell<N, CELL>(sp, U, sWh, sbh, f, Jv[q][v]);
+          if (a.approx != APX_NEWTON) {  // quasi-DEER keeps the diagonal, Jacobi nothing
+#pragma unroll
+            for (int i = 0; i < N; i++)
+#pragma unroll
+              for (int m = 0; m < N; m++)
+                if (a.approx == APX_ZERO || m != i) Jv[q][v][i * N + m] = 0.f;
+          }
           Op<N> e;
 #pragma unroll
           for (int i = 0; i < N; i++) {

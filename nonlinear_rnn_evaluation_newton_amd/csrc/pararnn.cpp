@@ -40,6 +40,7 @@ enum { PATH_NONE = 0, PATH_TIME = 1, PATH_CHAN = 2, PATH_D64 = 3 };
 
 struct Plan {
   int path = PATH_NONE;
+  int approx = APX_NEWTON;  // Jacobian of the sweeps' linear solve (the adjoint always uses the cell's)
   int G = 1, S = 1, N = 1, SW = 1;
   int tile = 0, tps = 0, ntiles = 0;
   // scalar-state sweep (n = d = 1, T % 4 == 0): its own tile size
@@ -67,16 +68,19 @@ int gates_of(int cell) { return (cell == PR_CELL_GRU || cell == PR_CELL_GRU_DIAG
 int make_plan(const pr_problem *p, Plan *pl) {
   if (!p) return fail(PR_EINVAL, "problem is NULL");
   if (p->cell < 0 || p->cell > 4) return fail(PR_EINVAL, "unknown cell %d", p->cell);
-  if (p->jac < 0 || p->jac > 2) return fail(PR_EINVAL, "unknown jac %d", p->jac);
+  if (p->jac < 0 || p->jac > 3) return fail(PR_EINVAL, "unknown jac %d", p->jac);
   if (p->dtype != PR_F32 && p->dtype != PR_BF16) return fail(PR_EINVAL, "unknown dtype %d", p->dtype);
   if (p->B < 1 || p->T < 1 || p->d < 1 || p->n < 1)
     return fail(PR_EINVAL, "sizes must be >= 1 (B=%d T=%d d=%d n=%d)", p->B, p->T, p->d, p->n);
   const bool dense_cell = p->cell == PR_CELL_TANH_RNN || p->cell == PR_CELL_GRU || p->cell == PR_CELL_LINEAR;
-  bool jac_ok = false;
-  if (dense_cell) jac_ok = p->jac == PR_JAC_DENSE || (p->jac == PR_JAC_DIAG && p->n == 1);
-  if (p->cell == PR_CELL_GRU_DIAG) jac_ok = p->jac == PR_JAC_DIAG;
-  if (p->cell == PR_CELL_LSTM_CIFG_DIAG) jac_ok = p->jac == PR_JAC_BLOCK2;
+  // the cell's own structure is Newton; PR_JAC_DIAG on a dense or block cell
+  // keeps the diagonal (quasi-DEER); PR_JAC_ZERO runs Jacobi sweeps
+  bool jac_ok = p->jac == PR_JAC_DIAG || p->jac == PR_JAC_ZERO;
+  if (dense_cell) jac_ok = jac_ok || p->jac == PR_JAC_DENSE;
+  if (p->cell == PR_CELL_LSTM_CIFG_DIAG) jac_ok = jac_ok || p->jac == PR_JAC_BLOCK2;
   if (!jac_ok) return fail(PR_EINVAL, "jac %d does not suit cell %d", p->jac, p->cell);
+  if (p->jac == PR_JAC_ZERO) pl->approx = APX_ZERO;
+  else if (p->jac == PR_JAC_DIAG && p->cell != PR_CELL_GRU_DIAG && !(dense_cell && p->n == 1)) pl->approx = APX_DIAG;
   if ((double)p->B * p->T * p->n * 2 > 2147483647.0 * 64) return fail(PR_EUNSUPPORTED, "problem too large");
 
   pl->G = gates_of(p->cell);
@@ -93,7 +97,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     int nt = pl->ntiles;  // descriptor and boundary slots for either sweep
     // (buffer resources of the scalar sweep address rows, descriptors and
     // boundary states with 31-bit byte offsets)
-    if (p->n == 1 && p->d == 1 && p->T % 4 == 0 && (long long)p->T * 4 < (1LL << 31) &&
+    if (pl->approx == APX_NEWTON && p->n == 1 && p->d == 1 && p->T % 4 == 0 && (long long)p->T * 4 < (1LL << 31) &&
         (long long)p->B * ((p->T + scalar_adj_tile() - 1) / scalar_adj_tile()) * 16 < (1LL << 31)) {
       pl->scalar_ok = 1;
       pl->tps_s = (p->T + scalar_tile() - 1) / scalar_tile();
@@ -117,7 +121,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->adjoint_bytes = o;
     return PR_OK;
   }
-  if (p->cell == PR_CELL_GRU && p->jac == PR_JAC_DENSE && p->n == D64_N) {
+  if (p->cell == PR_CELL_GRU && p->n == D64_N) {
     if (p->dtype != PR_F32) return fail(PR_EUNSUPPORTED, "the dense n = 64 GRU runs in fp32 storage only");
     pl->path = PATH_D64;
     pl->cps = (p->T + D64_L - 1) / D64_L;
@@ -395,6 +399,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     da.aggb = (float *)(ws + pl.off_aggb);
     da.carry = (float *)(ws + pl.off_carry);
     da.B = p->B; da.T = p->T; da.cps = pl.cps; da.nchunks = pl.nchunks;
+    da.approx = pl.approx;
     da.tol = tol;
     da.max_iters = max_iters;
     da.st = (SolveState *)(ws + pl.off_state);
@@ -422,6 +427,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0);
     a.coef = (const float *)(ws + pl.off_coef);
+    a.approx = pl.approx;
   } else {
     ca.U = ws + pl.off_U;
     ca.h = h;
@@ -490,10 +496,10 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       } else {  // channel cells: carry scan, then the pass applying this sweep
         ca.k = kk;
         const bool bf = p->dtype == PR_BF16;
-        if (kk == 1) HIPCHK(launch_chan2(kc, bf, ca, CHAN2_FIRST, s));
-        HIPCHK(launch_chan2(kc, bf, ca, CHAN2_CARRY, s));
+        if (kk == 1) HIPCHK(launch_chan2(kc, pl.approx, bf, ca, CHAN2_FIRST, s));
+        HIPCHK(launch_chan2(kc, pl.approx, bf, ca, CHAN2_CARRY, s));
         // the last possible sweep composes no aggregates for a next one
-        HIPCHK(launch_chan2(kc, bf, ca, kk == kmax ? CHAN2_APPLY : CHAN2_APPLY_NEXT, s));
+        HIPCHK(launch_chan2(kc, pl.approx, bf, ca, kk == kmax ? CHAN2_APPLY : CHAN2_APPLY_NEXT, s));
       }
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
@@ -626,6 +632,7 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     da.g = (const float *)g;
     da.lam = (float *)lambda;
     da.B = p->B; da.T = p->T; da.cps = pl.cps; da.nchunks = pl.nchunks;
+    da.approx = pl.approx;
     da.st = (SolveState *)(ws + pl.off_state);
     const int ta = tr.begin(TR_ADJ, s);
     HIPCHK(launch_d64_adjoint_scan(da, s));

@@ -32,6 +32,7 @@ CELL_LINEAR = 4
 JAC_DENSE = 0
 JAC_DIAG = 1
 JAC_BLOCK2 = 2
+JAC_ZERO = 3  # Jacobi sweeps (no Jacobian in the linear solve)
 
 DT_F32 = 0
 DT_BF16 = 1

@@ -48,11 +48,25 @@ def test_workspace_bytes_for_supported_problems():
             assert bd.workspace_bytes(pb, True) >= bd.workspace_bytes(pb, False)
 
 
+def test_workspace_bytes_for_approximate_jacobians():
+    # quasi-DEER (diagonal) and Jacobi (zero) sweeps on every kernel family
+    for cfg in (1, 2, 3, 4, 5):
+        w = sy.WORKLOADS[cfg]
+        for jac in (bd.PR_JAC_DIAG, bd.PR_JAC_ZERO):
+            pb = bd.Problem(w["cell"], jac, w["dtype"], w["B"], w["T"], w["d"], w["n"])
+            assert bd.workspace_bytes(pb, True) >= bd.workspace_bytes(pb, False) > 0, (cfg, jac, bd.last_error())
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(cell=9), bd.PR_EINVAL), (dict(jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL), (dict(dtype=7), bd.PR_EINVAL),
     (dict(B=0), bd.PR_EINVAL), (dict(T=0), bd.PR_EINVAL), (dict(d=0), bd.PR_EINVAL), (dict(n=-3), bd.PR_EINVAL),
     (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
     (dict(cell=sy.CELL_TANH_RNN, n=13), bd.PR_EUNSUPPORTED),
+    (dict(jac=4), bd.PR_EINVAL), (dict(jac=-1), bd.PR_EINVAL),
+    (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL),
+    (dict(cell=sy.CELL_LSTM_CIFG_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
+    (dict(cell=sy.CELL_GRU, jac=bd.PR_JAC_DIAG, n=13), bd.PR_EUNSUPPORTED),
+    (dict(cell=sy.CELL_TANH_RNN, jac=bd.PR_JAC_ZERO, n=64), bd.PR_EUNSUPPORTED),
 ])
 def test_invalid_problems_rejected_without_device(kw, code):
     L = bd.lib()
