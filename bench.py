@@ -139,6 +139,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GRU n=1, B=16, T=2^20)")
+    ap.add_argument("--jac", choices=("own", "diag", "zero"), default="own",
+                    help="Jacobian of the sweeps' linear solve: the cell's own (Newton), its diagonal "
+                         "(quasi-DEER) or zero (Jacobi)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="do not bracket kernels with events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -164,6 +167,10 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
         return 0
     p = sy.make_problem(args.config)
+    if args.jac != "own":
+        p = dict(p, jac=sy.JAC_DIAG if args.jac == "diag" else sy.JAC_ZERO,
+                 name=p["name"] + ("_quasi" if args.jac == "diag" else "_jacobi"))
+    approx = args.jac != "own" and not (args.jac == "diag" and (p["cell"] == sy.CELL_GRU_DIAG or p["n"] == 1))
     dp = bd.DeviceProblem(p)
     B, T = p["B"], p["T"]
     units = B * T
@@ -217,7 +224,27 @@ def main() -> int:
     wu = units_of(p)
     chan = p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
     dense64 = p["cell"] == sy.CELL_GRU and p["n"] == 64
-    if tr is not None and tr["sweep_launches"] > 0 and dense64:
+    if tr is not None and tr["sweep_launches"] > 0 and dense64 and approx:
+        # diagonal (or zero) Jacobian, n = 64: the sweep is the gates GEMM,
+        # a per-channel scan and the update.  Algorithmic bytes per step: read
+        # U (192 floats) and, from sweep 2 on, h (64); write h (64)
+        per_solve_bytes = sum(4.0 * (192 + (64 if k >= 2 else 0) + 64) for k in range(1, iters + 1)) * units
+        avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
+        achieved = per_solve_bytes / iters / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(p["name"]),
+                    "kernel": "k_d64q_gates + k_d64q_carry + k_d64q_apply per sweep (gates GEMM with the "
+                              "diagonal Jacobian and chunk aggregates; chunk carries; update)",
+                    "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": per_solve_bytes / iters}
+        dm, dn = bd.trace_kernel(bd.TRACE_DENSE_PRODUCTS)
+        if dn > 0:
+            extra["carry_kernel_us"] = round(dm / dn * 1e3, 2)
+        if tr["adjoint_launches"] > 0:
+            extra["adjoint_scan_us"] = round(tr["adjoint_ms"] / tr["adjoint_launches"] * 1e3, 2)
+        gm, gn = bd.trace_kernel(bd.TRACE_ADJOINT_PRODUCTS)
+        if gn > 0:
+            extra["adjoint_products_us"] = round(gm / gn * 1e3, 2)
+    elif tr is not None and tr["sweep_launches"] > 0 and dense64:
         # full DEER, n = 64: the chunk-product kernel composes one 64 x 64
         # Jacobian per step on fp32 MFMA (2 n^3 flops) and carries the offset
         # (2 n^2): 532,480 algorithmic flops per step
@@ -241,7 +268,7 @@ def main() -> int:
         achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
         kname = ("k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
                  "sweep's tile aggregates)" if chan else
-                 ("k_pipe<SweepPol>" if scalar_path(p) else "k_time_sweep") +
+                 ("k_pipe<SweepPol>" if scalar_path(p) and not approx else "k_time_sweep") +
                  " (fused cell + Jacobian + scan + update)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(p["name"]),
@@ -279,7 +306,9 @@ def main() -> int:
         "dtype": "bf16" if p["dtype"] == 1 else "f32",
         "data": "synthetic",
         "config": {"workload": p["name"], "cell": sy.CELL_NAMES[p["cell"]], "B": B, "T": T, "d": p["d"],
-                   "n": p["n"], "tol": p["tol"], "max_iters": p["max_iters"], "step": "solve + adjoint"},
+                   "n": p["n"], "tol": p["tol"], "max_iters": p["max_iters"], "step": "solve + adjoint",
+                   "jacobian": {"own": "the cell's", "diag": "diagonal (quasi-DEER)",
+                                "zero": "zero (Jacobi)"}[args.jac]},
         "iters": iters,
         "final_delta": float(dl[-1]) if len(dl) else None,
         "solve_ms": ms_solve,
@@ -287,7 +316,7 @@ def main() -> int:
         "roofline": roofline,
         **extra,
     }
-    if args.config == 2:
+    if args.config == 2 and args.jac == "own":
         # context only: the pages time the forward evaluation alone, on a V100
         line["pages_context"] = {"v100_deer_forward_ms": 15.0, "this_forward_ms": round(ms_solve, 4),
                                  "forward_ratio": round(15.0 / ms_solve, 2)}

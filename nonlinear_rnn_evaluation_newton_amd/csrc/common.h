@@ -290,4 +290,34 @@ __device__ inline bool sweep_is_stopped(const SolveState *st, int *s_stop) {
   return *s_stop != 0;
 }
 
+// Blocks of `kernel` that fit on the device at once: the grid of a
+// persistent kernel (every block resident, so an in-order tile walk cannot
+// deadlock).
+inline int device_cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  return cus;
+}
+
+template <auto KERN, int THREADS = 256>
+int resident_blocks() {
+  static int cached = 0;  // one per kernel instantiation
+  if (cached) return cached;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, THREADS, 0) != hipSuccess || per_cu < 1) return 0;
+  cached = per_cu * device_cu_count();
+  return cached;
+}
+
+template <auto KERN, int THREADS = 256>
+int persistent_grid(int ntiles) {
+  const int r = resident_blocks<KERN, THREADS>();
+  if (r <= 0) return 0;
+  return ntiles < r ? ntiles : r;
+}
+
 }  // namespace pr

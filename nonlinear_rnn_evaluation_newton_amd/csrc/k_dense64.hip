@@ -32,98 +32,181 @@ constexpr int WLD = 68;  // padded LDS row stride (floats) of 64-wide matrices
 
 __device__ inline int r0_of(int r) { return 8 * (r >> 2) + (r & 3); }
 
-// Gate pre-activations of 64 rows on MFMA: sC[row][0..191] = (W_h s_row)
-// for the states in sH (rows x 64, stride WLD); sW holds W_h [192][64]
-// (stride WLD) and is overwritten by sC ([64][D64_CLD]).  Ends with a block
-// barrier.
-constexpr int D64_CLD = 196;
-__device__ inline void d64_preacts(const float *sH, float *sW) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  // [64 rows] x [192 gate channels], K = 64: wave w owns row block (w & 1)
-  // and column blocks 3*(w >> 1) + {0, 1, 2}
-  const int rb = wid & 1, cb0 = 3 * (wid >> 1);
-  f32x16_d acc[3];
-#pragma unroll
-  for (int q = 0; q < 3; q++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) acc[q][r] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < 32; s++) {
-    const int kk = 2 * s + (lane >> 5);
-    const float av = sH[(rb * 32 + (lane & 31)) * WLD + kk];
-#pragma unroll
-    for (int q = 0; q < 3; q++)
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sW[((cb0 + q) * 32 + (lane & 31)) * WLD + kk], acc[q], 0, 0, 0);
-  }
-  __syncthreads();
-  float *sC = sW;
-#pragma unroll
-  for (int q = 0; q < 3; q++)
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-      sC[(rb * 32 + r0_of(r) + 4 * (lane >> 5)) * D64_CLD + (cb0 + q) * 32 + (lane & 31)] = acc[q][r];
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// 1. gates (sweep: z, alpha, beta, gamma, res;  adjoint: z, alpha, beta, gamma, eta)
-// ---------------------------------------------------------------------------
-template <bool ADJ>
-__global__ __launch_bounds__(256) void k_d64_gates(const D64Args a) {
-  __shared__ int s_stop;
-  __shared__ __attribute__((aligned(16))) float sH[64 * WLD];
-  __shared__ __attribute__((aligned(16))) float sW[192 * WLD];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (!ADJ && sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
-  const int rows = a.B * a.T, T = a.T;
-  const int r0 = blockIdx.x * 64;
-  const bool first = !ADJ && a.k == 1;  // the iterate is h = 0 before sweep 1
-  for (int e = tid; e < 192 * 16; e += 256) {
+// W_h [192][64] into LDS (stride WLD)
+__device__ inline void d64_stage(const D64Args &a, float *sW) {
+  for (int e = threadIdx.x; e < 192 * 16; e += 256) {
     const int row = e >> 4, c4 = (e & 15) * 4;
     *reinterpret_cast<float4 *>(&sW[row * WLD + c4]) = *reinterpret_cast<const float4 *>(a.Wh + row * 64 + c4);
   }
-  for (int e = tid; e < 64 * 16; e += 256) {
-    const int rr = e >> 4, c4 = (e & 15) * 4, row = r0 + rr;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < rows) {
-      const int t = row % T, b = row / T;
-      if (t > 0) {
-        if (!first) v = *reinterpret_cast<const float4 *>(a.h + (size_t)(row - 1) * 64 + c4);
-      } else if (a.h0) {
-        v = *reinterpret_cast<const float4 *>(a.h0 + (size_t)b * 64 + c4);
+}
+
+// ---------------------------------------------------------------------------
+// 1. gates: per step the GRU gates on top of W_h h_{t-1} (MFMA).  Outputs:
+//    GM_SWEEP  [row][5][64]: z, alpha, beta, gamma, res (J_t = diag(z) +
+//              diag(alpha) W_hz + diag(beta) W_hn + diag(gamma) W_hr)
+//    GM_ADJ    the same with eta = (1 - z)(1 - c^2) in place of res
+//    GM_QUASI  [row][2][64]: the Jacobian's diagonal (or 0) and res, plus
+//              each chunk's per-channel aggregate (see the quasi sweep below)
+// ---------------------------------------------------------------------------
+enum { GM_SWEEP = 0, GM_ADJ = 1, GM_QUASI = 2 };
+
+// Persistent over units of D64_L steps of one sequence (unit = chunk):
+// W_h stays in LDS; each block prefetches the states entering its next
+// unit's rows (the MFMA's input) while it computes the current one, and
+// issues the current unit's U and iterate loads before its MFMA, which
+// covers their latency.  MFMA layout: wavefront w computes rows
+// [32 (w & 1), +32) x channels [32 (w >> 1), +32) of all three gates, so a
+// lane ends up holding, for one channel, the three pre-activations of 16
+// rows, and the gate arithmetic runs in registers with no transpose.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_d64_gates(const D64Args a) {
+  __shared__ int s_stop;
+  __shared__ __attribute__((aligned(16))) float sW[192 * WLD];
+  __shared__ __attribute__((aligned(16))) float sH[64 * WLD];
+  __shared__ float sAgg[2][2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (MODE != GM_ADJ && sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
+  const int T = a.T, cps = a.cps, nunits = a.nchunks, G = gridDim.x;
+  const bool first = MODE != GM_ADJ && a.k == 1;  // the iterate is h = 0 before sweep 1
+  const int rb = wid & 1, cbk = wid >> 1, hl = lane >> 5, li = lane & 31;
+  const int c = cbk * 32 + li;  // this lane's channel
+  const float bhr = a.bh ? a.bh[c] : 0.f, bhz = a.bh ? a.bh[64 + c] : 0.f, bhn = a.bh ? a.bh[128 + c] : 0.f;
+  float wr = 0.f, wz = 0.f, wn = 0.f;
+  if (MODE == GM_QUASI) {
+    wr = a.Wh[c * 64 + c];
+    wz = a.Wh[(64 + c) * 64 + c];
+    wn = a.Wh[(128 + c) * 64 + c];
+  }
+  const bool diag = a.approx == APX_DIAG;
+
+  // row of MFMA result register r within the unit
+  auto row_of = [&](int r) { return 32 * rb + 8 * (r >> 2) + 4 * hl + (r & 3); };
+  // This thread's share of the states entering a unit's 64 rows (h_{t-1},
+  // h0 at t = 0, or 0; bit m of zmask set when share m must be 0).
+  // Addresses are clamped into the unit, so the loads are unconditional.
+  auto load_states = [&](int unit, float4 (&hs)[4], unsigned &zmask) __attribute__((always_inline)) {
+    const int b = unit / cps, t0 = (unit % cps) * D64_L, nr = min(D64_L, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    zmask = 0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int e = tid + 256 * m, rr = e >> 4, c4 = (e & 15) * 4;
+      const int rc = min(rr, nr - 1), t = t0 + rc;
+      const float *src = t > 0 ? a.h + (row0 + rc - 1) * 64 + c4 : (a.h0 ? a.h0 + (size_t)b * 64 + c4 : a.h + row0 * 64 + c4);
+      hs[m] = *reinterpret_cast<const float4 *>(src);
+      const bool zero = rr >= nr || (t > 0 ? first : a.h0 == nullptr);
+      zmask |= zero ? 1u << m : 0u;
+    }
+  };
+
+  int unit = blockIdx.x;
+  if (unit >= nunits) return;
+  float4 nhs[4];
+  unsigned nz;
+  load_states(unit, nhs, nz);
+  d64_stage(a, sW);
+  while (true) {
+    __syncthreads();  // the previous unit's MFMA has read sH (and W_h is staged)
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int e = tid + 256 * m, rr = e >> 4, c4 = (e & 15) * 4;
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = ((nz >> m) & 1u) ? z4 : nhs[m];
+    }
+    __syncthreads();
+    const int b = unit / cps, j = unit % cps, t0 = j * D64_L, nr = min(D64_L, T - t0);
+    const size_t row0 = (size_t)b * T + t0;
+    // U and the iterate at this lane's 16 rows (rows past the end load the
+    // last row and are not stored), then the next unit's states
+    float u[3][16], hc[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const size_t row = row0 + min(row_of(r), nr - 1);
+#pragma unroll
+      for (int g = 0; g < 3; g++) u[g][r] = a.U[row * 192 + 64 * g + c];
+      hc[r] = MODE == GM_ADJ ? 0.f : a.h[row * 64 + c];
+    }
+    const int next = unit + G;
+    load_states(next < nunits ? next : unit, nhs, nz);  // the last unit reloads itself
+
+    f32x16_d acc[3];
+#pragma unroll
+    for (int g = 0; g < 3; g++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[g][r] = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < 32; s++) {
+      const int kk = 2 * s + hl;
+      const float av = sH[(32 * rb + li) * WLD + kk];
+#pragma unroll
+      for (int g = 0; g < 3; g++)
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sW[(64 * g + 32 * cbk + li) * WLD + kk], acc[g], 0, 0, 0);
+    }
+
+    float ga[4], gb[4];  // quasi: aggregates of this lane's four runs of 4 rows
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      ga[r4] = 1.f;
+      gb[r4] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int r = 4 * r4 + q, R = row_of(r);
+        const bool live = R < nr;
+        const size_t row = row0 + R;
+        const float sv = sH[R * WLD + c];
+        const float ar = acc[0][r] + u[0][r] + bhr;
+        const float az = acc[1][r] + u[1][r] + bhz;
+        const float qv = acc[2][r] + bhn;
+        const float rg = fsigm(ar), z = fsigm(az);
+        const float cc = ftanh(fmaf(rg, qv, u[2][r]));
+        const float eta = (1.f - z) * (1.f - cc * cc);
+        if constexpr (MODE == GM_QUASI) {
+          const float f = fmaf(z, sv - cc, cc);
+          const float Jd = diag ? z + (sv - cc) * z * (1.f - z) * wz + eta * rg * (wn + qv * (1.f - rg) * wr) : 0.f;
+          const float res = f - (first ? 0.f : hc[r]);
+          if (live) {
+            a.gates[row * 128 + c] = Jd;
+            a.gates[row * 128 + 64 + c] = res;
+          }
+          gb[r4] = live ? fmaf(Jd, gb[r4], res) : gb[r4];
+          ga[r4] = live ? Jd * ga[r4] : ga[r4];
+        } else if (live) {
+          float *Gr = a.gates + row * 320;
+          Gr[c] = z;
+          Gr[64 + c] = (sv - cc) * z * (1.f - z);
+          Gr[128 + c] = eta * rg;
+          Gr[192 + c] = eta * qv * rg * (1.f - rg);
+          Gr[256 + c] = MODE == GM_ADJ ? eta : fmaf(z, sv - cc, cc) - (first ? 0.f : hc[r]);
+        }
       }
     }
-    *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = v;
-  }
-  __syncthreads();
-  d64_preacts(sH, sW);
-  constexpr int CLD = D64_CLD;
-  const float *sC = sW;
-  const int i = lane;
-  const float bhr = a.bh ? a.bh[i] : 0.f, bhz = a.bh ? a.bh[64 + i] : 0.f, bhn = a.bh ? a.bh[128 + i] : 0.f;
-  for (int rr = wid; rr < 64; rr += 4) {
-    const int row = r0 + rr;
-    if (row >= rows) break;
-    const float *Ur = a.U + (size_t)row * 192;
-    const float ar = sC[rr * CLD + i] + Ur[i] + bhr;
-    const float az = sC[rr * CLD + 64 + i] + Ur[64 + i] + bhz;
-    const float q = sC[rr * CLD + 128 + i] + bhn;
-    const float s = sH[rr * WLD + i];
-    const float r = fsigm(ar), z = fsigm(az);
-    const float c = ftanh(fmaf(r, q, Ur[128 + i]));
-    const float eta = (1.f - z) * (1.f - c * c);
-    float *G = a.gates + (size_t)row * 320;
-    G[i] = z;
-    G[64 + i] = (s - c) * z * (1.f - z);
-    G[128 + i] = eta * r;
-    G[192 + i] = eta * q * r * (1.f - r);
-    if (ADJ) {
-      G[256 + i] = eta;
-    } else {
-      const float f = fmaf(z, s - c, c);
-      const float hc = first ? 0.f : a.h[(size_t)row * 64 + i];
-      G[256 + i] = f - hc;
+    if constexpr (MODE == GM_QUASI) {
+      // rows 8 r4 + [0, 4) sit in the lower half-wave, 8 r4 + [4, 8) in the
+      // upper one: compose each pair in time order, then the four runs
+      float A = 1.f, B = 0.f;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const float pa = __shfl_xor(ga[r4], 32, 64), pb = __shfl_xor(gb[r4], 32, 64);
+        const float ea = hl ? pa : ga[r4], eb = hl ? pb : gb[r4];  // earlier 4 rows
+        const float la = hl ? ga[r4] : pa, lb = hl ? gb[r4] : pb;  // later 4 rows
+        const float a8 = la * ea, b8 = fmaf(la, eb, lb);
+        B = fmaf(a8, B, b8);
+        A *= a8;
+      }
+      if (hl == 0) {
+        sAgg[rb][0][c] = A;
+        sAgg[rb][1][c] = B;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const float a0 = sAgg[0][0][tid], b0 = sAgg[0][1][tid], a1 = sAgg[1][0][tid], b1 = sAgg[1][1][tid];
+        const size_t o = ((size_t)b * 64 + tid) * cps + j;
+        a.aggP[o] = a1 * a0;
+        a.aggb[o] = fmaf(a1, b0, b1);
+      }
     }
+    if (next >= nunits) break;
+    unit = next;
   }
 }
 
@@ -496,99 +579,13 @@ __global__ __launch_bounds__(256) void k_colsum_final(const double *part, int co
 // the chunk products' O(n^3) (Gonzalez et al. abstract: quasi-Newton
 // approximations converge comparably, use less memory and are faster).
 // A sweep is three launches over chunks of D64_L steps:
-//  1. k_d64q_gates: one block per chunk: W_h h_{t-1} on MFMA, the gates, the
-//     diagonal J_t and r_t (stored [row][J | r]), and the chunk's aggregate
-//     per channel (A = product of J, b), stored channel-major [b][i][chunk];
+//  1. k_d64_gates<GM_QUASI>: W_h h_{t-1} on MFMA, the gates, the diagonal
+//     J_t and r_t (stored [row][J | r]), and each chunk's aggregate per
+//     channel (A = product of J, b), stored channel-major [b][i][chunk];
 //  2. k_d64q_carry: one wavefront per (sequence, channel), lane = chunk: an
 //     inclusive scan of the aggregates gives the state entering each chunk;
 //  3. k_d64q_apply: one wavefront per chunk, lane = channel: dh_t = J_t
 //     dh_{t-1} + r_t from the carry, h += dh, max |dh|.
-__global__ __launch_bounds__(256) void k_d64q_gates(const D64Args a) {
-  __shared__ int s_stop;
-  __shared__ __attribute__((aligned(16))) float sH[64 * WLD];
-  __shared__ __attribute__((aligned(16))) float sW[192 * WLD];
-  __shared__ float sAgg[4][2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
-  const int T = a.T, cps = a.cps, chunk = blockIdx.x;
-  const int b = chunk / cps, j = chunk % cps;
-  const int t0 = j * D64_L, nr = min(D64_L, T - t0);
-  const size_t row0 = (size_t)b * T + t0;
-  const bool first = a.k == 1;  // the iterate is h = 0 before sweep 1
-  for (int e = tid; e < 192 * 16; e += 256) {
-    const int row = e >> 4, c4 = (e & 15) * 4;
-    *reinterpret_cast<float4 *>(&sW[row * WLD + c4]) = *reinterpret_cast<const float4 *>(a.Wh + row * 64 + c4);
-  }
-  for (int e = tid; e < 64 * 16; e += 256) {
-    const int rr = e >> 4, c4 = (e & 15) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (rr < nr) {
-      if (t0 + rr > 0) {
-        if (!first) v = *reinterpret_cast<const float4 *>(a.h + (row0 + rr - 1) * 64 + c4);
-      } else if (a.h0) {
-        v = *reinterpret_cast<const float4 *>(a.h0 + (size_t)b * 64 + c4);
-      }
-    }
-    *reinterpret_cast<float4 *>(&sH[rr * WLD + c4]) = v;
-  }
-  __syncthreads();
-  d64_preacts(sH, sW);
-  float *sC = sW;
-  constexpr int CLD = D64_CLD;
-  const int i = lane;
-  const float bhr = a.bh ? a.bh[i] : 0.f, bhz = a.bh ? a.bh[64 + i] : 0.f, bhn = a.bh ? a.bh[128 + i] : 0.f;
-  const float wr = a.Wh[i * 64 + i], wz = a.Wh[(64 + i) * 64 + i], wn = a.Wh[(128 + i) * 64 + i];
-  const bool diag = a.approx == APX_DIAG;
-  for (int rr = wid; rr < nr; rr += 4) {
-    const size_t row = row0 + rr;
-    const float *Ur = a.U + row * 192;
-    const float ar = sC[rr * CLD + i] + Ur[i] + bhr;
-    const float az = sC[rr * CLD + 64 + i] + Ur[64 + i] + bhz;
-    const float q = sC[rr * CLD + 128 + i] + bhn;
-    const float sv = sH[rr * WLD + i];
-    const float r = fsigm(ar), z = fsigm(az);
-    const float c = ftanh(fmaf(r, q, Ur[128 + i]));
-    const float f = fmaf(z, sv - c, c);
-    const float be = (1.f - z) * (1.f - c * c);
-    const float Jd = diag ? z + (sv - c) * z * (1.f - z) * wz + be * r * (wn + q * (1.f - r) * wr) : 0.f;
-    const float res = f - (first ? 0.f : a.h[row * 64 + i]);
-    a.gates[row * 128 + i] = Jd;
-    a.gates[row * 128 + 64 + i] = res;
-    // this lane's own entries of row rr, already read
-    sC[rr * CLD + i] = Jd;
-    sC[rr * CLD + 64 + i] = res;
-  }
-  __syncthreads();
-  // chunk aggregate: wavefront w composes rows [16w, 16w + 16), wavefront 0
-  // composes the four
-  {
-    float A = 1.f, B = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      const int rr = wid * 16 + q;
-      if (rr < nr) {
-        const float Jv = sC[rr * CLD + i], rv = sC[rr * CLD + 64 + i];
-        B = fmaf(Jv, B, rv);
-        A *= Jv;
-      }
-    }
-    sAgg[wid][0][i] = A;
-    sAgg[wid][1][i] = B;
-  }
-  __syncthreads();
-  if (wid == 0) {
-    float A = sAgg[0][0][i], B = sAgg[0][1][i];
-#pragma unroll
-    for (int w = 1; w < 4; w++) {
-      B = fmaf(sAgg[w][0][i], B, sAgg[w][1][i]);
-      A *= sAgg[w][0][i];
-    }
-    const size_t o = ((size_t)b * 64 + i) * cps + j;
-    a.aggP[o] = A;
-    a.aggb[o] = B;
-  }
-}
-
 // One wavefront per (sequence, channel); lanes take 64 chunks at a time.
 __global__ __launch_bounds__(256) void k_d64q_carry(const D64Args a) {
   __shared__ int s_stop;
@@ -669,12 +666,20 @@ hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s) {
   a.adjoint = 0;
   const int rows = a.B * a.T;
   if (a.approx != APX_NEWTON) {
-    if (part == 0) hipLaunchKernelGGL(k_d64q_gates, dim3(a.nchunks), dim3(256), 0, s, a);
+    if (part == 0) {
+      const int grid = persistent_grid<k_d64_gates<GM_QUASI>>(a.nchunks);
+      if (grid <= 0) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(k_d64_gates<GM_QUASI>, dim3(grid), dim3(256), 0, s, a);
+    }
     if (part == 1) hipLaunchKernelGGL(k_d64q_carry, dim3((a.B * 64 + 3) / 4), dim3(256), 0, s, a);
     if (part == 2) hipLaunchKernelGGL(k_d64q_apply, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (part == 0) hipLaunchKernelGGL(k_d64_gates<false>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
+  if (part == 0) {
+    const int grid = persistent_grid<k_d64_gates<GM_SWEEP>>(a.nchunks);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_d64_gates<GM_SWEEP>, dim3(grid), dim3(256), 0, s, a);
+  }
   if (part == 1) hipLaunchKernelGGL(k_d64_scanA<false>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
   if (part == 2) {
     hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
@@ -686,7 +691,11 @@ hipError_t launch_d64_sweep_part(D64Args &a, int part, hipStream_t s) {
 hipError_t launch_d64_adjoint_scan(D64Args &a, hipStream_t s) {
   a.adjoint = 1;
   const int rows = a.B * a.T;
-  hipLaunchKernelGGL(k_d64_gates<true>, dim3((rows + 63) / 64), dim3(256), 0, s, a);
+  {
+    const int grid = persistent_grid<k_d64_gates<GM_ADJ>>(a.nchunks);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_d64_gates<GM_ADJ>, dim3(grid), dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(k_d64_scanA<true>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_d64_scanB, dim3(a.B), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_d64_scanC<true>, dim3((a.nchunks + 3) / 4), dim3(256), 0, s, a);

@@ -751,36 +751,6 @@ __global__ __launch_bounds__(256) void k_time_scan(const ScanArgs a) {
 // ---------------------------------------------------------------------------
 static inline int dx_pad(int d) { return d <= 1 ? 1 : d <= 2 ? 2 : d <= 4 ? 4 : 8; }
 
-// Blocks of `kernel` (256 threads) that fit on the device at once: the grid
-// of a persistent kernel, so that every block is resident and the in-order
-// tile walk cannot deadlock.
-inline int device_cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
-  }
-  return cus;
-}
-
-template <auto KERN, int THREADS = 256>
-int resident_blocks() {
-  static int cached = 0;  // one per kernel instantiation
-  if (cached) return cached;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, THREADS, 0) != hipSuccess || per_cu < 1) return 0;
-  cached = per_cu * device_cu_count();
-  return cached;
-}
-
-template <auto KERN, int THREADS = 256>
-int persistent_grid(int ntiles) {
-  const int r = resident_blocks<KERN, THREADS>();
-  if (r <= 0) return 0;
-  return ntiles < r ? ntiles : r;
-}
-
 #define PR_DISPATCH_DX(d, ...)                                   \
   switch (dx_pad(d)) {                                           \
     case 1: { constexpr int DX = 1; __VA_ARGS__; } break;        \
