@@ -233,7 +233,7 @@ def main() -> int:
         achieved = per_solve_bytes / iters / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(p["name"]),
-                    "kernel": "k_d64q_gates + k_d64q_carry + k_d64q_apply per sweep (gates GEMM with the "
+                    "kernel": "k_d64_gates<GM_QUASI> + k_d64q_carry + k_d64q_apply per sweep (gates GEMM with the "
                               "diagonal Jacobian and chunk aggregates; chunk carries; update)",
                     "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": per_solve_bytes / iters}
         dm, dn = bd.trace_kernel(bd.TRACE_DENSE_PRODUCTS)

@@ -359,10 +359,11 @@ struct ScBase {
 // ---------------------------------------------------------------------------
 template <int CELL, bool FIRST>
 struct SweepPol : ScBase {
-  // long tiles (4 groups per wavefront, one block per CU): fewer look-back
-  // stages per sequence, which the chain of carries pays for one by one
-  static constexpr int WPE = 2;
-  static constexpr int Q = 4, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
+  // long tiles (3 groups per wavefront x 11 wavefronts, one block per CU):
+  // few look-back stages per sequence, which the chain of carries pays for
+  // one by one, with three wavefronts per SIMD to overlap memory and ALU
+  static constexpr int WPE = 3;
+  static constexpr int Q = 3, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   // raw inputs of one tile: x and the current iterate h per group, and the
   // state before the wavefront's first step (zero when its resource is empty)
   struct Raw {
@@ -512,7 +513,7 @@ struct SweepPol : ScBase {
 // ---------------------------------------------------------------------------
 template <int CELL>
 struct AdjPol : ScBase {
-  static constexpr int WPE = 2;
+  static constexpr int WPE = 3;
   static constexpr int Q = 2, WSTEPS = Q * 64 * SC_V, TILE = SC_CW * WSTEPS;
   struct Raw {
     float4 x[Q], h[Q], g[Q];

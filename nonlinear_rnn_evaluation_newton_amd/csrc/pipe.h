@@ -1,6 +1,6 @@
 // Tile pipeline shared by the sweep and adjoint kernels of the scalar-state
-// path: a persistent grid of blocks of 7 compute wavefronts
-// and one look-back wavefront.  A block computes tile N while the tile before
+// path: a persistent grid of blocks of 11 compute wavefronts
+// and one look-back wavefront (three wavefronts per SIMD, one block per CU).  A block computes tile N while the tile before
 // it waits for its carry (two register sets alternate; the loads of the tile
 // after N are in flight during N); the look-back wavefront resolves carries
 // alone, so its waits on the tile descriptors never queue behind the bulk
@@ -18,7 +18,7 @@
 
 namespace pr {
 
-constexpr int SC_CW = 7;                      // compute wavefronts per block
+constexpr int SC_CW = 11;                      // compute wavefronts per block
 constexpr int SC_THREADS = 64 * (SC_CW + 1);  // + the look-back wavefront (a multiple of 4 wavefronts)
 constexpr int SC_LB = SC_CW;                  // wavefront id of the look-back wavefront
 
