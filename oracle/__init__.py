@@ -57,6 +57,7 @@ def _load():
         lib.orc_deer.argtypes = [P, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
         lib.orc_deer_approx.argtypes = [P, C.c_int, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
         lib.orc_adjoint.argtypes = [P] + [P] * 12
+        lib.orc_lsim_discrete.argtypes = [C.c_int] * 5 + [P] * 8
         lib.orc_num_threads.restype = C.c_int
         _lib = lib
     return _lib
@@ -192,3 +193,44 @@ def affine_solve(kind: int, A, b, reverse: bool = False):
     y = np.zeros_like(b)
     _check(lib.orc_affine_solve(kind, B, T, n, int(reverse), _ptr(A), _ptr(b), _ptr(y)))
     return y
+
+
+def zoh(A, Bm, dt):
+    """Zero-order-hold discretisation: Ad = exp(A dt), Bd = int_0^dt exp(A s) ds B,
+    read off one matrix exponential of the augmented matrix [[A, B], [0, 0]] dt
+    (scipy.linalg.expm)."""
+    import scipy.linalg
+    A, Bm = _f64(A), _f64(Bm)
+    nx, m = Bm.shape
+    M = np.zeros((nx + m, nx + m))
+    M[:nx, :nx] = A * dt
+    M[:nx, nx:] = Bm * dt
+    E = scipy.linalg.expm(M)
+    return E[:nx, :nx].copy(), E[:nx, nx:].copy()
+
+
+def lsim(A, Bm, Cm, Dm, U, t, x0=None):
+    """Linear state-space simulation dx/dt = A x + B u, y = C x + D u sampled at
+    the uniform times t with the input held between samples (zero-order hold).
+
+    U [B, T, m] (or [T, m]); x0 [B, nx] or None (= 0).  Returns (y [B, T, p],
+    x [B, T, nx]) with x[:, k] the state at t[k]."""
+    lib = _load()
+    U = _f64(U)
+    squeeze = U.ndim == 2
+    if squeeze:
+        U = U[None]
+    Bn, T, m = U.shape
+    A, Bm, Cm, Dm = _f64(A), _f64(Bm), _f64(Cm), _f64(Dm)
+    nx, p = A.shape[0], Cm.shape[0]
+    t = np.asarray(t, dtype=np.float64)
+    dt = float(t[1] - t[0]) if T > 1 else 1.0
+    if T > 2 and not np.allclose(np.diff(t), dt, rtol=1e-9, atol=0):
+        raise ValueError("lsim needs uniformly spaced times")
+    Ad, Bd = zoh(A, Bm, dt)
+    x0 = None if x0 is None else _f64(np.broadcast_to(x0, (Bn, nx)))
+    x = np.zeros((Bn, T, nx))
+    y = np.zeros((Bn, T, p))
+    _check(lib.orc_lsim_discrete(Bn, T, nx, m, p, _ptr(Ad), _ptr(Bd), _ptr(Cm), _ptr(Dm), _ptr(U), _ptr(x0),
+                                 _ptr(x), _ptr(y)))
+    return (y[0], x[0]) if squeeze else (y, x)

@@ -33,6 +33,12 @@
  *  - orc_affine_solve: y_t = A_t y_{t-1} + b_t (or the reverse-time recurrence)
  *    by its definition, for the dense, diagonal and 2x2-block operators that
  *    the Para-Seq README lists (Main features: src.utils scans).
+ *  - orc_lsim_discrete: the sampled linear state-space simulation behind the
+ *    README's lsim (Main features: ODE solvers; Example: lsim(A, B, C, D, U,
+ *    t)) once the system is discretised: x_0 = x0, y_k = C x_k + D u_k,
+ *    x_{k+1} = Ad x_k + Bd u_k, sequentially.  The discretisation (zero-order
+ *    hold: Ad = exp(A dt), Bd = int_0^dt exp(A s) ds B) is done by the Python
+ *    front end with a library matrix exponential.
  *
  * The pages never print the cell equations.  The cells follow the PyTorch
  * conventions that Para-Seq keeps (README intro: the standard RNN/GRU/LSTM
@@ -577,4 +583,44 @@ int orc_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/*
+ * Sampled linear state-space system, per sequence b, by its definition:
+ *   x_0 = x0 (0 if NULL);  for k = 0..T-1: y_k = C x_k + D u_k;
+ *   x_{k+1} = Ad x_k + Bd u_k.
+ * Ad [nx,nx], Bd [nx,m], C [p,nx], D [p,m] row-major; U [B,T,m]; x0 [B,nx];
+ * outputs x [B,T,nx] (x_k, the state before input k) and y [B,T,p].
+ */
+int orc_lsim_discrete(int B, int T, int nx, int m, int p, const double *Ad, const double *Bd, const double *C,
+                      const double *D, const double *U, const double *x0, double *x, double *y) {
+  if (B < 0 || T < 0 || nx < 1 || m < 1 || p < 1) return ORC_EINVAL;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int b = 0; b < B; b++) {
+    double *s = (double *)calloc(nx, sizeof(double)), *sn = (double *)calloc(nx, sizeof(double));
+    if (!s || !sn) { err |= 1; free(s); free(sn); continue; }
+    if (x0)
+      for (int i = 0; i < nx; i++) s[i] = x0[(size_t)b * nx + i];
+    for (int k = 0; k < T; k++) {
+      const double *u = U + ((size_t)b * T + k) * m;
+      for (int i = 0; i < nx; i++) x[((size_t)b * T + k) * nx + i] = s[i];
+      for (int o = 0; o < p; o++) {
+        double v = 0.0;
+        for (int i = 0; i < nx; i++) v += C[(size_t)o * nx + i] * s[i];
+        for (int j = 0; j < m; j++) v += D[(size_t)o * m + j] * u[j];
+        y[((size_t)b * T + k) * p + o] = v;
+      }
+      for (int i = 0; i < nx; i++) {
+        double v = 0.0;
+        for (int l = 0; l < nx; l++) v += Ad[(size_t)i * nx + l] * s[l];
+        for (int j = 0; j < m; j++) v += Bd[(size_t)i * m + j] * u[j];
+        sn[i] = v;
+      }
+      for (int i = 0; i < nx; i++) s[i] = sn[i];
+    }
+    free(s);
+    free(sn);
+  }
+  return err ? ORC_ENOMEM : ORC_OK;
 }

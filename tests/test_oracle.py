@@ -20,6 +20,9 @@ sign or index, a transposed operand) fails at least one test:
   Jacobian is diagonal, equals Jacobi for a tanh RNN whose recurrent matrix
   has a zero diagonal, and equals Newton on the LSTM cell state when that
   state does not depend on h; both reach the rollout;
+* lsim: the README's decay example and closed forms (held constant input,
+  rotation, double integrator), feedthrough, and scipy.signal.lsim with a
+  zero-order hold;
 * quadratic convergence (DEER summary, Approach) and the [-1, 1] bound of the
   gated cells' states.
 """
@@ -529,3 +532,63 @@ def test_approximate_sweeps_reach_the_rollout(cfg, kw, approx):
     # linear, not quadratic, convergence: later ratios stay bounded away from 0
     r = dl[-4:-1] / dl[-5:-2]
     assert np.all(r > 1e-3)
+
+
+# ---------------------------------------------------------------------------
+# lsim: sampled linear state-space simulation (zero-order hold)
+# ---------------------------------------------------------------------------
+def test_lsim_pages_example_decay():
+    # the README's example system dx/dt = -0.5 x + u, y = x on t = linspace(0, 1, 128)
+    t = np.linspace(0.0, 1.0, 128)
+    A, Bm, Cm, Dm = np.array([[-0.5]]), np.array([[1.0]]), np.array([[1.0]]), np.array([[0.0]])
+    y, x = oracle.lsim(A, Bm, Cm, Dm, np.zeros((128, 1)), t)
+    assert np.all(y == 0) and np.all(x == 0)  # zero input, zero initial state
+    y, x = oracle.lsim(A, Bm, Cm, Dm, np.zeros((128, 1)), t, x0=[1.0])
+    np.testing.assert_allclose(y[:, 0], np.exp(-0.5 * t), rtol=0, atol=1e-14)
+    # a constant input held between samples: x(t) = e^{at} x0 + (b u / -a)(1 - e^{at})
+    y, x = oracle.lsim(A, Bm, Cm, Dm, np.full((128, 1), 3.0), t, x0=[0.25])
+    np.testing.assert_allclose(x[:, 0], np.exp(-0.5 * t) * 0.25 + 6.0 * (1 - np.exp(-0.5 * t)), rtol=0, atol=1e-13)
+
+
+def test_lsim_rotation_and_double_integrator_closed_forms():
+    t = np.arange(400) * 0.05
+    w = 1.7
+    A = np.array([[0.0, w], [-w, 0.0]])  # exp(A t) is a rotation by w t
+    y, x = oracle.lsim(A, np.zeros((2, 1)), np.eye(2), np.zeros((2, 1)), np.zeros((400, 1)), t, x0=[1.0, 0.5])
+    ref = np.stack([np.cos(w * t) * 1.0 + np.sin(w * t) * 0.5, -np.sin(w * t) * 1.0 + np.cos(w * t) * 0.5], 1)
+    np.testing.assert_allclose(x, ref, rtol=0, atol=1e-12)
+    # double integrator with a held input u: position x0 + v0 t + u t^2 / 2
+    A = np.array([[0.0, 1.0], [0.0, 0.0]])
+    y, x = oracle.lsim(A, np.array([[0.0], [1.0]]), np.array([[1.0, 0.0]]), np.zeros((1, 1)),
+                       np.full((400, 1), -0.3), t, x0=[2.0, 0.7])
+    np.testing.assert_allclose(y[:, 0], 2.0 + 0.7 * t - 0.15 * t * t, rtol=0, atol=1e-11)
+
+
+def test_lsim_feedthrough_and_batch():
+    rng = np.random.default_rng(3)
+    A = rng.normal(size=(4, 4)) - 3 * np.eye(4)
+    Bm, Cm, Dm = rng.normal(size=(4, 2)), np.zeros((3, 4)), rng.normal(size=(3, 2))
+    U = rng.normal(size=(5, 60, 2))
+    y, x = oracle.lsim(A, Bm, Cm, Dm, U, np.arange(60) * 0.1)
+    np.testing.assert_allclose(y, U @ Dm.T, rtol=0, atol=1e-14)  # C = 0: y = D u
+    C2 = rng.normal(size=(3, 4))
+    y1, x1 = oracle.lsim(A, Bm, C2, Dm, U[2], np.arange(60) * 0.1)
+    yb, xb = oracle.lsim(A, Bm, C2, Dm, U, np.arange(60) * 0.1)
+    assert x1.shape == (60, 4) and xb.shape == (5, 60, 4)
+    np.testing.assert_allclose(xb[2], x1, rtol=0, atol=1e-14)  # sequences are independent
+    np.testing.assert_allclose(yb[2], y1, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("nx,m,p", [(1, 1, 1), (3, 2, 2), (8, 4, 3)])
+def test_lsim_matches_scipy_signal(nx, m, p):
+    import scipy.signal
+    rng = np.random.default_rng(nx * 10 + m)
+    A = rng.normal(size=(nx, nx)) / np.sqrt(nx) - 1.5 * np.eye(nx)
+    Bm, Cm, Dm = rng.normal(size=(nx, m)), rng.normal(size=(p, nx)), rng.normal(size=(p, m))
+    t = np.arange(300) * 0.02
+    U = rng.normal(size=(300, m))
+    x0 = rng.normal(size=nx)
+    y, x = oracle.lsim(A, Bm, Cm, Dm, U, t, x0=x0)
+    _, ys, xs = scipy.signal.lsim((A, Bm, Cm, Dm), U, t, X0=x0, interp=False)
+    np.testing.assert_allclose(y, np.reshape(ys, y.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(x, np.reshape(xs, x.shape), rtol=0, atol=1e-12)
