@@ -133,6 +133,72 @@ def cpu_baseline(p: dict) -> dict:
             "sample": sample + f"; {dt:.2f} s", "seconds": dt}
 
 
+def bench_lsim(args) -> int:
+    """One step = one pararnn_lsim call over the whole batch (discretisation,
+    chunk aggregates, chunk carries, outputs)."""
+    import numpy as np
+    import torch
+
+    from nonlinear_rnn_evaluation_newton_amd import binding as bd
+
+    q = sy.make_lsim()
+    B, T, nx, m, p = q["B"], q["T"], q["nx"], q["m"], q["p"]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    A, Bm, Cm, Dm, U, x0 = (dev(q[k]) for k in ("A", "Bm", "Cm", "Dm", "U", "x0"))
+    x = torch.empty((B, T, nx), device="cuda")
+    y = torch.empty((B, T, p), device="cuda")
+    ws = torch.empty(bd.lsim_workspace_bytes(B, T, nx, m, p), dtype=torch.uint8, device="cuda")
+
+    def step():
+        bd.lsim(A, Bm, Cm, Dm, q["dt"], U, x0, x, y, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_trace:
+        bd.trace(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    roofline = None
+    if not args.no_trace:
+        lm, ln = bd.trace_kernel(bd.TRACE_LSIM)
+        bd.trace(False)
+        # algorithmic bytes per step: read u (m floats), write x (nx) and y (p)
+        per_call = 4.0 * (m + nx + p) * B * T
+        achieved = per_call / (lm / ln * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_lsim_disc + k_lsim_pass<aggregate> + k_lsim_carry + k_lsim_pass<apply> per call",
+                    "avg_launch_us": round(lm / ln * 1e3, 2), "bytes_per_launch": per_call}
+    line = {
+        "metric": "timesteps*batch/sec of a linear state-space simulation (lsim, no Newton loop)",
+        "value": B * T / (ms_step * 1e-3), "unit": "timesteps*batch/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": q["name"], "B": B, "T": T, "nx": nx, "m": m, "p": p, "dt": q["dt"],
+                   "step": "one lsim call (zero-order hold)"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"], x0=q["x0"])
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": B * T / dt, "unit": "timesteps*batch/s",
+                                "cores": min(oracle.num_threads(), B), "kind": "oracle",
+                                "sample": f"full workload: fp64 sequential lsim of all {B} sequences x {T} steps, "
+                                          f"OpenMP over sequences; {dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +208,8 @@ def main() -> int:
     ap.add_argument("--jac", choices=("own", "diag", "zero"), default="own",
                     help="Jacobian of the sweeps' linear solve: the cell's own (Newton), its diagonal "
                          "(quasi-DEER) or zero (Jacobi)")
+    ap.add_argument("--lsim", action="store_true",
+                    help="time the linear state-space simulation workload (B=16, T=2^20, 4 states) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="do not bracket kernels with events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -166,6 +234,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
         return 0
+    if args.lsim:
+        return bench_lsim(args)
     p = sy.make_problem(args.config)
     if args.jac != "own":
         p = dict(p, jac=sy.JAC_DIAG if args.jac == "diag" else sy.JAC_ZERO,

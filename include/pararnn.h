@@ -170,6 +170,29 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
                         float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Linear state-space simulation (Para-Seq README, Main features: ODE
+ * solvers; Example: lsim(A, B, C, D, U, t)): the system dx/dt = A x + B u,
+ * y = C x + D u sampled every dt with the input held between samples
+ * (zero-order hold), i.e. per sequence
+ *   x_0 = x0,  y_k = C x_k + D u_k,  x_{k+1} = Ad x_k + Bd u_k,
+ *   Ad = exp(A dt),  Bd = int_0^dt exp(A s) ds B,
+ * evaluated with parallel scans over time (no Newton loop).  fp32 storage;
+ * the discretisation is computed on the device in fp64.
+ *   A [nx, nx], B [nx, m], C [p, nx], D [p, m]   row-major, shared by all sequences
+ *   U  [B, T, m]            input samples
+ *   x0 [B, nx] or NULL (= 0)
+ *   x  [B, T, nx] or NULL   output: x_k, the state at sample k
+ *   y  [B, T, p]            output
+ * 1 <= nx, m, p <= 8 (else PR_EUNSUPPORTED); dt > 0 and finite.  The
+ * workspace (256-byte aligned) must hold pararnn_lsim_workspace_bytes.
+ * Asynchronous on `stream`.
+ */
+size_t pararnn_lsim_workspace_bytes(int B, int T, int nx, int m, int p);
+int pararnn_lsim(int B, int T, int nx, int m, int p, const float *A, const float *Bm, const float *C,
+                 const float *D, float dt, const float *U, const float *x0, float *x, float *y,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Kernel timing for profiling and benchmarks (per calling thread).
  * pararnn_trace(1) clears the counters and starts bracketing, with HIP events
  * on the call's stream, the Newton sweeps and the main kernel of each
@@ -184,12 +207,15 @@ int pararnn_trace(int enable);
 int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjoint_ms, long long *adjoint_launches);
 /* Totals of one category: 0 Newton sweeps, 1 the adjoint's scan kernel(s),
  * 2 the input projection, 3 the adjoint's products and reductions, 4 the
- * chunk-product kernel of the dense n = 64 path (within its sweeps). */
+ * chunk-product kernel of the dense n = 64 path (within its sweeps; with an
+ * approximate Jacobian, its chunk-carry kernel), 5 linear state-space
+ * simulations. */
 #define PR_TRACE_SWEEP 0
 #define PR_TRACE_ADJOINT 1
 #define PR_TRACE_PROJECTION 2
 #define PR_TRACE_ADJOINT_PRODUCTS 3
 #define PR_TRACE_DENSE_PRODUCTS 4
+#define PR_TRACE_LSIM 5  /* the kernels of each pararnn_lsim call */
 int pararnn_trace_kernel(int which, double *ms, long long *launches);
 
 /* Static text for a status code. */

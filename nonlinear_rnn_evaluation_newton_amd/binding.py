@@ -23,7 +23,7 @@ PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3
 
 EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_scan_workspace_bytes",
            "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
-           "pararnn_trace_kernel"]
+           "pararnn_trace_kernel", "pararnn_lsim_workspace_bytes", "pararnn_lsim"]
 
 
 class Problem(C.Structure):
@@ -78,6 +78,10 @@ def lib():
         L.pararnn_trace_read.restype = I
         L.pararnn_trace_kernel.argtypes = [I, P, P]
         L.pararnn_trace_kernel.restype = I
+        L.pararnn_lsim_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.pararnn_lsim_workspace_bytes.restype = S
+        L.pararnn_lsim.argtypes = [I, I, I, I, I, P, P, P, P, F, P, P, P, P, P, S, P]
+        L.pararnn_lsim.restype = I
         _lib = L
     return _lib
 
@@ -152,6 +156,7 @@ def trace_read() -> dict:
 
 
 TRACE_SWEEP, TRACE_ADJOINT, TRACE_PROJECTION, TRACE_ADJOINT_PRODUCTS, TRACE_DENSE_PRODUCTS = 0, 1, 2, 3, 4
+TRACE_LSIM = 5
 
 
 def trace_kernel(which: int):
@@ -173,6 +178,22 @@ def affine_scan(jac: int, A, b, y, workspace, reverse: bool = False, check: bool
                                    workspace.numel() * workspace.element_size(), _stream())
     if check and st < 0:
         raise PararnnError(st, "pararnn_affine_scan")
+    return st
+
+
+def lsim_workspace_bytes(B: int, T: int, nx: int, m: int, p: int) -> int:
+    return lib().pararnn_lsim_workspace_bytes(B, T, nx, m, p)
+
+
+def lsim(A, Bm, Cm, Dm, dt: float, U, x0, x, y, workspace, check: bool = True) -> int:
+    """pararnn_lsim on fp32 device tensors: U [B,T,m], x0 [B,nx] or None,
+    outputs x [B,T,nx] (or None) and y [B,T,p]."""
+    B, T, m = U.shape[0], U.shape[1], U.shape[2]
+    nx, p = A.shape[0], Cm.shape[0]
+    st = lib().pararnn_lsim(B, T, nx, m, p, _p(A), _p(Bm), _p(Cm), _p(Dm), float(dt), _p(U), _p(x0), _p(x), _p(y),
+                            _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if check and st < 0:
+        raise PararnnError(st, "pararnn_lsim")
     return st
 
 

@@ -166,4 +166,21 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 // dst [C, R] = transpose of row-major src [R, C]; elem_bytes 2 or 4
 hipError_t launch_transpose(const void *src, void *dst, int R, int C, int elem_bytes, hipStream_t s);
 
+// linear state-space simulation (k_lsim.hip)
+struct LsimArgs {
+  const float *A, *Bm, *Cm, *Dm;  // [nx,nx], [nx,m], [p,nx], [p,m]
+  float dt;
+  const float *U;    // [B,T,m]
+  const float *x0;   // [B,nx] or null
+  float *x;          // [B,T,nx] or null
+  float *y;          // [B,T,p]
+  float *table;      // lsim_table_floats(): Ad, Bd and power tables
+  float *agg, *carry;  // [nchunks][8]
+  int B, T, nx, m, p;
+  int V, cps, nchunks;  // steps per lane, chunks per sequence, chunks (set by launch_lsim)
+};
+int lsim_table_floats();
+int lsim_chunk_len(int m);  // steps per chunk
+hipError_t launch_lsim(LsimArgs &a, hipStream_t s);
+
 }  // namespace pr

@@ -226,7 +226,7 @@ SolveState *host_state() {
 // Event timing of the main kernels (pararnn_trace).  Categories: Newton
 // sweeps (only launches that did work are counted), the adjoint's scan
 // kernel, the input projection, the adjoint's products and reductions.
-enum { TR_SWEEP = 0, TR_ADJ = 1, TR_PROJ = 2, TR_AGEMM = 3, TR_DPROD = 4, TR_N = 5 };
+enum { TR_SWEEP = 0, TR_ADJ = 1, TR_PROJ = 2, TR_AGEMM = 3, TR_DPROD = 4, TR_SWEEP_LSIM = 5, TR_N = 6 };
 struct Trace {
   bool on = false;
   bool made = false;
@@ -742,6 +742,48 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     return PR_OK;
   }
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
+}
+
+static bool lsim_sizes_ok(int B, int T, int nx, int m, int p) {
+  return B >= 1 && T >= 1 && nx >= 1 && nx <= 8 && m >= 1 && m <= 8 && p >= 1 && p <= 8 &&
+         (long long)B * ((T + lsim_chunk_len(m) - 1) / lsim_chunk_len(m)) < (1LL << 31) &&
+         (long long)B * T < (1LL << 40);
+}
+
+size_t pararnn_lsim_workspace_bytes(int B, int T, int nx, int m, int p) {
+  if (!lsim_sizes_ok(B, T, nx, m, p)) return 0;
+  const size_t nchunks = (size_t)B * ((T + lsim_chunk_len(m) - 1) / lsim_chunk_len(m));
+  return align256((size_t)lsim_table_floats() * 4) + 2 * align256(nchunks * 8 * 4);
+}
+
+int pararnn_lsim(int B, int T, int nx, int m, int p, const float *A, const float *Bm, const float *Cm,
+                 const float *Dm, float dt, const float *U, const float *x0, float *x, float *y, void *workspace,
+                 size_t ws_bytes, void *stream) {
+  g_err.clear();
+  if (B < 1 || T < 1 || nx < 1 || m < 1 || p < 1) return fail(PR_EINVAL, "sizes must be >= 1");
+  if (nx > 8 || m > 8 || p > 8) return fail(PR_EUNSUPPORTED, "state, input and output widths are limited to 8");
+  if (!lsim_sizes_ok(B, T, nx, m, p)) return fail(PR_EUNSUPPORTED, "problem too large");
+  if (!A || !Bm || !Cm || !Dm || !U || !y) return fail(PR_EINVAL, "A, B, C, D, U and y are required");
+  if (!(dt > 0.f) || dt != dt || dt > 3.0e38f) return fail(PR_EINVAL, "dt must be positive and finite");
+  const size_t need = pararnn_lsim_workspace_bytes(B, T, nx, m, p);
+  if (!workspace || ws_bytes < need) return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
+  char *ws = (char *)workspace;
+  const size_t nchunks = (size_t)B * ((T + lsim_chunk_len(m) - 1) / lsim_chunk_len(m));
+  LsimArgs a{};
+  a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dm = Dm; a.dt = dt;
+  a.U = U; a.x0 = x0; a.x = x; a.y = y;
+  a.table = (float *)ws;
+  a.agg = (float *)(ws + align256((size_t)lsim_table_floats() * 4));
+  a.carry = (float *)(ws + align256((size_t)lsim_table_floats() * 4) + align256(nchunks * 8 * 4));
+  a.B = B; a.T = T; a.nx = nx; a.m = m; a.p = p;
+  hipStream_t s = (hipStream_t)stream;
+  Trace &tr = trace();
+  if (tr.on) HIPCHK(tr.make());
+  const int ti = tr.begin(TR_SWEEP_LSIM, s);
+  HIPCHK(launch_lsim(a, s));
+  tr.end(TR_SWEEP_LSIM, ti, s);
+  return PR_OK;
 }
 
 size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n) {

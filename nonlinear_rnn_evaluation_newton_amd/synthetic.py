@@ -197,3 +197,32 @@ def custom_problem(cell: int, B: int, T: int, d: int, n: int, seed: int = 0,
                 dtype=dtype, B=B, T=T, d=d, n=n, G=G, S=S,
                 W_x=r(Wx), b_x=r(bx), W_h=r(Wh), b_h=r(bh), peep=r(peep),
                 x=r(x), g=r(g), h0=r(hz), tol=1e-6, max_iters=T)
+
+
+# The linear state-space workload (the README's lsim example, scaled up): a
+# stable system of nx states driven by m inputs with p outputs, sampled every
+# dt.  Draw order: A, B, C, D, x0, U.  A = -I + 0.5 G / sqrt(nx) with G
+# standard normal keeps the eigenvalues' real parts negative for these sizes.
+LSIM_WORKLOAD = dict(name="lsim_T1M", B=16, T=1 << 20, nx=4, m=1, p=1, dt=0.01)
+
+
+def make_lsim(B: int | None = None, T: int | None = None, nx: int | None = None, m: int | None = None,
+              p: int | None = None, dt: float | None = None, seed: int = 6, x0: bool = True) -> dict:
+    w = LSIM_WORKLOAD
+    B = w["B"] if B is None else B
+    T = w["T"] if T is None else T
+    nx = w["nx"] if nx is None else nx
+    m = w["m"] if m is None else m
+    p = w["p"] if p is None else p
+    dt = w["dt"] if dt is None else dt
+    rng = np.random.default_rng(seed)
+    A = -np.eye(nx) + 0.5 * rng.standard_normal((nx, nx)) / np.sqrt(nx)
+    Bm = rng.standard_normal((nx, m))
+    Cm = rng.standard_normal((p, nx))
+    Dm = rng.standard_normal((p, m))
+    x0v = rng.standard_normal((B, nx)) if x0 else None
+    U = rng.standard_normal((B, T, m))
+    f32 = lambda a: None if a is None else round_storage(a, DT_F32)  # noqa: E731
+    return dict(name=w["name"] if (B, T, nx, m, p) == (w["B"], w["T"], w["nx"], w["m"], w["p"]) else "lsim_custom",
+                B=B, T=T, nx=nx, m=m, p=p, dt=float(np.float32(dt)), A=f32(A), Bm=f32(Bm), Cm=f32(Cm), Dm=f32(Dm),
+                x0=f32(x0v), U=f32(U))

@@ -98,3 +98,22 @@ def test_missing_pointers_and_workspace_rejected():
                              None, C.c_void_p(256), 1 << 30, None) == bd.PR_EINVAL
     assert L.pararnn_affine_scan(5, 1, 8, 1, 0, C.c_void_p(16), C.c_void_p(16), C.c_void_p(16), C.c_void_p(256),
                                  1 << 20, None) == bd.PR_EINVAL
+
+
+def test_lsim_arguments_rejected_without_device():
+    L = bd.lib()
+    v = C.c_void_p(16)
+    ws = bd.lsim_workspace_bytes(2, 5000, 4, 1, 1)
+    assert ws > 0
+    assert bd.lsim_workspace_bytes(2, 5000, 9, 1, 1) == 0 and bd.lsim_workspace_bytes(0, 5, 1, 1, 1) == 0
+
+    def call(B=2, T=5000, nx=4, m=1, p=1, A=v, Bm=v, Cm=v, Dm=v, dt=0.01, U=v, y=v, w=C.c_void_p(256), n=ws):
+        return L.pararnn_lsim(B, T, nx, m, p, A, Bm, Cm, Dm, dt, U, None, None, y, w, n, None)
+
+    assert call(B=0) == bd.PR_EINVAL
+    assert call(nx=9) == bd.PR_EUNSUPPORTED and call(m=9) == bd.PR_EUNSUPPORTED and call(p=9) == bd.PR_EUNSUPPORTED
+    assert call(A=None) == bd.PR_EINVAL and call(U=None) == bd.PR_EINVAL and call(y=None) == bd.PR_EINVAL
+    assert call(dt=0.0) == bd.PR_EINVAL and call(dt=-1.0) == bd.PR_EINVAL and call(dt=float("nan")) == bd.PR_EINVAL
+    assert call(n=ws - 1) == bd.PR_EWORKSPACE and call(w=None) == bd.PR_EWORKSPACE
+    assert call(w=C.c_void_p(264)) == bd.PR_EINVAL  # not 256-byte aligned
+    assert bd.last_error() != ""

@@ -1,0 +1,86 @@
+"""GPU parity of the linear state-space simulation (pararnn_lsim: zero-order
+hold discretisation on the device, scans over time) against the fp64 oracle's
+lsim, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOL = 1e-4  # max-abs, relative to max(1, max |ref|) of the tensor
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run(q, want_x=True):
+    B, T, nx, m, p = q["B"], q["T"], q["nx"], q["m"], q["p"]
+    ws = torch.empty(bd.lsim_workspace_bytes(B, T, nx, m, p), dtype=torch.uint8, device="cuda")
+    x = torch.full((B, T, nx), float("nan"), device="cuda") if want_x else None
+    y = torch.full((B, T, p), float("nan"), device="cuda")
+    bd.lsim(dev(q["A"]), dev(q["Bm"]), dev(q["Cm"]), dev(q["Dm"]), q["dt"], dev(q["U"]), dev(q["x0"]), x, y, ws)
+    torch.cuda.synchronize()
+    return (None if x is None else x.double().cpu().numpy()), y.double().cpu().numpy()
+
+
+def err(a, ref):
+    return float(np.abs(a - ref).max() / max(1.0, np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("nx,m,p", [(1, 1, 1), (2, 1, 1), (3, 2, 2), (4, 1, 1), (5, 3, 2), (8, 8, 8)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 1023, 1025, 4097, 9000])
+def test_lsim_against_oracle(nx, m, p, T):
+    q = sy.make_lsim(B=3, T=T, nx=nx, m=m, p=p, seed=nx * 100 + T)
+    say("case lsim nx", nx, "m", m, "p", p, "T", T)
+    x, y = run(q)
+    yo, xo = oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"], x0=q["x0"])
+    ex, ey = err(x, xo), err(y, yo)
+    say("  err x", ex, "y", ey)
+    assert ex <= TOL and ey <= TOL
+
+
+def test_lsim_no_initial_state_no_state_output():
+    q = sy.make_lsim(B=2, T=2500, nx=3, m=2, p=1, seed=9, x0=False)
+    _, y = run(q, want_x=False)
+    yo, _ = oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(q["T"]) * q["dt"])
+    assert err(y, yo) <= TOL
+
+
+def test_lsim_pages_example():
+    # the README's example: dx/dt = -0.5 x + u, y = x, 128 samples on [0, 1]
+    t = np.linspace(0.0, 1.0, 128)
+    q = dict(B=1, T=128, nx=1, m=1, p=1, dt=float(np.float32(t[1] - t[0])), A=np.array([[-0.5]]),
+             Bm=np.array([[1.0]]), Cm=np.array([[1.0]]), Dm=np.array([[0.0]]), x0=np.array([[1.0]]),
+             U=np.zeros((1, 128, 1)))
+    x, y = run(q)
+    assert np.abs(y[0, :, 0] - np.exp(-0.5 * np.arange(128) * q["dt"])).max() <= 1e-6
+
+
+def test_lsim_full_size_sampled():
+    """The benchmark's workload (B=16, T=2^20, 4 states, 1 input, 1 output):
+    three sequences against the oracle in full."""
+    q = sy.make_lsim()
+    say("case lsim full size")
+    x, y = run(q)
+    t = np.arange(q["T"]) * q["dt"]
+    for b in (0, 7, q["B"] - 1):
+        yo, xo = oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"][b], t, x0=q["x0"][b])
+        ex, ey = err(x[b], xo), err(y[b], yo)
+        say("  sequence", b, "err x", ex, "y", ey)
+        assert ex <= TOL and ey <= TOL
