@@ -387,12 +387,16 @@ struct SweepPol : ScBase {
   __device__ static void acc_init(Acc &c) { c.dmax = 0; }
 
   // In the first sweep the iterate is the zero guess and h is not read.
+  // id < 0: no tile (empty resources: the loads return zeros and move no data)
   __device__ static void load(const TimeArgs &a, int id, Raw &R) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
+    const bool none = id < 0;
+    id = none ? 0 : id;
     const int j = id / B, b = id % B;
     const int t0 = j * TILE + wid * WSTEPS;
-    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, (unsigned)T * 4u);
-    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
+    const unsigned rbytes = none ? 0u : (unsigned)T * 4u;
+    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, rbytes);
+    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, rbytes);
 #pragma unroll
     for (int q = 0; q < Q; q++) {
       const unsigned off = toff(t0 + (q * 64 + lane) * SC_V, T);
@@ -410,7 +414,7 @@ struct SweepPol : ScBase {
       if (wid == 0) { sb = a.bnd + (size_t)((k - 1) & 1) * a.ntiles + (b * a.tiles_per_seq + j - 1); nb = 4; }
       else { sb = a.h + (size_t)b * T; nb = (unsigned)T * 4u; so = (unsigned)(t0 - 1) * 4u; }
     }
-    R.sw = ld1(sc_rsrc(sb, nb), so);
+    R.sw = ld1(sc_rsrc(sb, none ? 0u : nb), so);
   }
 
   // cell, Jacobian and residual of every step, lane-serial composition,
@@ -551,12 +555,16 @@ struct AdjPol : ScBase {
     return a.T - SC_V - p0;
   }
 
+  // id < 0: no tile (empty resources: the loads return zeros and move no data)
   __device__ static void load(const TimeArgs &a, int id, Raw &R) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
+    const bool none = id < 0;
+    id = none ? 0 : id;
     const int b = id % B;
-    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, (unsigned)T * 4u);
-    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
-    const Rsrc rg = sc_rsrc(a.g + (size_t)b * T, (unsigned)T * 4u);
+    const unsigned rbytes = none ? 0u : (unsigned)T * 4u;
+    const Rsrc rx = sc_rsrc(a.x + (size_t)b * T, rbytes);
+    const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, rbytes);
+    const Rsrc rg = sc_rsrc(a.g + (size_t)b * T, rbytes);
 #pragma unroll
     for (int q = 0; q < Q; q++) {
       const int t = tlo(a, id, q);
@@ -572,7 +580,7 @@ struct AdjPol : ScBase {
     (void)lane;
     R.xn = ld1(rx, toff(t_late + 1, T));
     R.hp = ld1(rh, toff(t_early - 1, T));
-    R.h0b = ld1(sc_rsrc(a.h0 ? a.h0 + b : nullptr, 4u), 0u);
+    R.h0b = ld1(sc_rsrc(a.h0 ? a.h0 + b : nullptr, none ? 0u : 4u), 0u);
   }
 
   template <bool FULL>

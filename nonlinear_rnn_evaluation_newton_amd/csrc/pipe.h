@@ -9,7 +9,9 @@
 // lanes, so no load or store sits under a branch (see below).
 //
 // A policy type supplies the work of one tile (Raw inputs, computed Tile,
-// LDS, accumulators, constants, look-back) through static members, and
+// LDS, accumulators, constants, look-back) through static members (load
+// with tile id -1 must move no data: it stands for the tile after a block's
+// last), and
 // WPE, the wavefronts per SIMD its register budget is sized for; see
 // k_scalar.hip.
 #pragma once
@@ -98,7 +100,7 @@ __device__ inline void pipe_stage(const typename Pol::Args &a, const typename Po
                                   typename Pol::Lds &lds, int bufN, typename Pol::Acc &acc) {
   const typename Pol::Tot tt = Pol::tot(sh, bufN ^ 1, threadIdx.x >> 6);
   const int nt = Pol::ntiles(a);
-  const int nn = idN + (int)gridDim.x < nt ? idN + (int)gridDim.x : idN;  // the last reloads itself
+  const int nn = idN + (int)gridDim.x < nt ? idN + (int)gridDim.x : -1;  // -1: an empty load
   Pol::load(a, nn, Rnext);
   pipe_compute_any<Pol>(a, K, idN, RN, TN, sh, lds, bufN);
   __syncthreads();
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(SC_THREADS, Pol::WPE) void k_pipe(const typename Po
     Pol::load(a, id, R0);  // overlaps the stop check
     if (Pol::open(a, sh)) return;
     // stage 0: compute the first tile
-    Pol::load(a, id + G < nt ? id + G : id, R1);
+    Pol::load(a, id + G < nt ? id + G : -1, R1);
     pipe_compute_any<Pol>(a, K, id, R0, T0, sh, lds, 0);
     __syncthreads();
     int idP = id;
