@@ -231,6 +231,8 @@ __global__ __launch_bounds__(256) void k_d64_scanA(const D64Args a) {
   __shared__ int s_stop;
   __shared__ __attribute__((aligned(16))) float sW[3 * 64 * WLD];
   __shared__ __attribute__((aligned(16))) float sB[4][64];
+  // per wavefront, two steps' coefficients: z, alpha, beta, gamma, right-hand side
+  __shared__ __attribute__((aligned(16))) float sCo[4][2][5][64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (!ADJ && sweep_is_stopped(a.st, &s_stop)) return;
   stage_w3<ADJ>(a.Wh, sW);
@@ -256,30 +258,51 @@ __global__ __launch_bounds__(256) void k_d64_scanA(const D64Args a) {
     for (int r = 0; r < 16; r++) bk[ib][r] = 0.f;
   brow[0] = brow[1] = 0.f;
 
+  // Entry `lane` of one step's coefficients (z, alpha, beta, gamma of the
+  // row holding the Jacobian, the right-hand side of the step's own row),
+  // fetched a step ahead; addresses are clamped into the sequence and the
+  // adjoint's last step (J = 0) or a step past the chunk read as zero.
+  auto fetch = [&](int sidx, float (&co)[5]) __attribute__((always_inline)) {
+    const int sc = min(sidx, T - 1);
+    const int t = ADJ ? T - 1 - sc : sc;
+    const int cr = ADJ ? t + 1 : t;  // row holding the Jacobian's coefficients
+    const bool live = cr < T && sidx < T;
+    const size_t rowc = (size_t)b * T + (cr < T ? cr : t), rowt = (size_t)b * T + t;
+#pragma unroll
+    for (int m = 0; m < 4; m++) co[m] = a.gates[rowc * 320 + 64 * m + lane];
+    co[4] = ADJ ? a.g[rowt * 64 + lane] : a.gates[rowt * 320 + 256 + lane];
+#pragma unroll
+    for (int m = 0; m < 4; m++) co[m] = live ? co[m] : 0.f;
+  };
+  float co[5];
+  fetch(j * D64_L, co);
+
   for (int s = 0; s < D64_L; s++) {
     const int sidx = j * D64_L + s;  // position in scan order
     if (sidx >= T) break;
-    const int t = ADJ ? T - 1 - sidx : sidx;
-    const int cr = ADJ ? t + 1 : t;  // row holding the Jacobian's coefficients
-    const bool live = cr < T;        // the adjoint's last step has J = 0
-    const float *G = a.gates + (size_t)((size_t)b * T + (live ? cr : 0)) * 320;
+    float(*cs)[64] = sCo[wid][s & 1];
+#pragma unroll
+    for (int m = 0; m < 5; m++) cs[m][lane] = co[m];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS order within the wavefront
+    __builtin_amdgcn_wave_barrier();
+    fetch(sidx + 1, co);  // the next step's, in flight during this step's products
     float zk[2][16];  // z at this lane's rows of P (same index pattern as the k set)
 #pragma unroll
     for (int ib = 0; ib < 2; ib++)
 #pragma unroll
       for (int r4 = 0; r4 < 4; r4++) {
         const int kb = ib * 32 + 8 * r4 + 4 * h;
-        const float4 zv = live ? *reinterpret_cast<const float4 *>(G + kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 zv = *reinterpret_cast<const float4 *>(&cs[0][kb]);
         zk[ib][4 * r4 + 0] = zv.x; zk[ib][4 * r4 + 1] = zv.y; zk[ib][4 * r4 + 2] = zv.z; zk[ib][4 * r4 + 3] = zv.w;
       }
     float crow[3][2], zrow[2], brhs[2];
 #pragma unroll
     for (int ob = 0; ob < 2; ob++) {
       const int i = ob * 32 + li;
-      zrow[ob] = live ? G[i] : 0.f;
+      zrow[ob] = cs[0][i];
 #pragma unroll
-      for (int m = 0; m < 3; m++) crow[m][ob] = live ? G[64 * (m + 1) + i] : 0.f;
-      brhs[ob] = ADJ ? a.g[((size_t)b * T + t) * 64 + i] : a.gates[((size_t)b * T + t) * 320 + 256 + i];
+      for (int m = 0; m < 3; m++) crow[m][ob] = cs[m + 1][i];
+      brhs[ob] = cs[4][i];
     }
     // P_new = diag(z) P + M P,  b_new = z * b + M b + rhs
     f32x16_d Pn[2][2];
@@ -299,7 +322,7 @@ __global__ __launch_bounds__(256) void k_d64_scanA(const D64Args a) {
         if (ADJ) {
 #pragma unroll
           for (int m = 0; m < 3; m++) {
-            const float4 cv = live ? *reinterpret_cast<const float4 *>(G + 64 * (m + 1) + kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 cv = *reinterpret_cast<const float4 *>(&cs[m + 1][kb]);
             ck[m][0] = cv.x; ck[m][1] = cv.y; ck[m][2] = cv.z; ck[m][3] = cv.w;
           }
         }
