@@ -290,6 +290,13 @@ __device__ inline bool sweep_is_stopped(const SolveState *st, int *s_stop) {
   return *s_stop != 0;
 }
 
+// Block barrier that orders LDS accesses only: waits for this wavefront's
+// LDS operations, then s_barrier.  Unlike __syncthreads it does not wait for
+// outstanding global loads and stores, so loads prefetched for later steps
+// stay in flight across it.  Global memory written before it is not
+// guaranteed visible to other wavefronts after it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Blocks of `kernel` that fit on the device at once: the grid of a
 // persistent kernel (every block resident, so an in-order tile walk cannot
 // deadlock).

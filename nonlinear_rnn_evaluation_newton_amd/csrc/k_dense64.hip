@@ -398,45 +398,45 @@ __global__ __launch_bounds__(256) void k_d64_scanB(const D64Args a) {
   const int i = tid >> 2, q = tid & 3;
   if (tid < 64) sc[tid] = 0.f;
   __syncthreads();
-  constexpr int PF = 4;  // chunks prefetched ahead of the carry chain
+  constexpr int PF = 8;  // chunks prefetched ahead of the carry chain (matrix rows and offsets)
   float4 pv[PF][4];
+  float bv[PF];
   const int c0 = b * a.cps;
   auto loadP = [&](int slot, int chunk) {
     const float *P = a.aggP + (size_t)chunk * 4096 + i * 64 + q * 16;
 #pragma unroll
     for (int m = 0; m < 4; m++) pv[slot][m] = *reinterpret_cast<const float4 *>(P + 4 * m);
+    bv[slot] = a.aggb[(size_t)chunk * 64 + i];
   };
+  // ring slots are static (the loop is unrolled by PF) and the loads are
+  // unconditional (chunk indices clamped), so no wait drains the ring early
 #pragma unroll
-  for (int f = 0; f < PF; f++)
-    if (f < a.cps) loadP(f, c0 + f);
-  for (int j = 0; j < a.cps; j++) {
-    const int chunk = c0 + j;
-    const int slot = j % PF;
-    float4 cur[4];
+  for (int f = 0; f < PF; f++) loadP(f, c0 + min(f, a.cps - 1));
+  for (int j0 = 0; j0 < a.cps; j0 += PF) {
 #pragma unroll
-    for (int f = 0; f < PF; f++)
-      if (f == slot) { cur[0] = pv[f][0]; cur[1] = pv[f][1]; cur[2] = pv[f][2]; cur[3] = pv[f][3]; }
-    const float bj = q == 0 ? a.aggb[(size_t)chunk * 64 + i] : 0.f;
-    if (j + PF < a.cps) {
+    for (int f = 0; f < PF; f++) {
+      const int j = j0 + f;
+      if (j >= a.cps) break;
+      const int chunk = c0 + j;
+      const float4 cur[4] = {pv[f][0], pv[f][1], pv[f][2], pv[f][3]};
+      const float bj = q == 0 ? bv[f] : 0.f;
+      loadP(f, c0 + min(j + PF, a.cps - 1));
+      float s = 0.f;
 #pragma unroll
-      for (int f = 0; f < PF; f++)
-        if (f == slot) loadP(f, chunk + PF);
+      for (int m = 0; m < 4; m++) {
+        const int k = q * 16 + 4 * m;
+        s = fmaf(cur[m].x, sc[k], s);
+        s = fmaf(cur[m].y, sc[k + 1], s);
+        s = fmaf(cur[m].z, sc[k + 2], s);
+        s = fmaf(cur[m].w, sc[k + 3], s);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (tid < 64) a.carry[(size_t)chunk * 64 + tid] = sc[tid];
+      lds_barrier();  // (keeps the prefetched chunks in flight)
+      if (q == 0) sc[i] = s + bj;
+      lds_barrier();
     }
-    float s = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const int k = q * 16 + 4 * m;
-      s = fmaf(cur[m].x, sc[k], s);
-      s = fmaf(cur[m].y, sc[k + 1], s);
-      s = fmaf(cur[m].z, sc[k + 2], s);
-      s = fmaf(cur[m].w, sc[k + 3], s);
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if (tid < 64) a.carry[(size_t)chunk * 64 + tid] = sc[tid];
-    __syncthreads();
-    if (q == 0) sc[i] = s + bj;
-    __syncthreads();
   }
 }
 
@@ -464,16 +464,42 @@ __global__ __launch_bounds__(256) void k_d64_scanC(const D64Args a) {
       for (int k = 0; k < 64; k++) w[m][k] = ADJ ? a.Wh[(mats[m] + k) * 64 + i] : a.Wh[(mats[m] + i) * 64 + k];
     float y = a.carry[(size_t)chunk * 64 + i];
     const bool first = !ADJ && a.k == 1;
+    // this lane's per-step values, fetched a step ahead (rows clamped into
+    // the sequence): forward z, alpha, beta, gamma, res and the iterate at
+    // row t; adjoint z, alpha, beta, gamma at row t + 1 (0 past the end) and g
+    auto fetch = [&](int sidx, float (&co)[6]) __attribute__((always_inline)) {
+      const int t = ADJ ? T - 1 - min(sidx, T - 1) : min(sidx, T - 1);
+      const size_t row = (size_t)b * T + t;
+      if (!ADJ) {
+#pragma unroll
+        for (int m = 0; m < 5; m++) co[m] = a.gates[row * 320 + 64 * m + i];
+        co[5] = a.h[row * 64 + i];
+      } else {
+        const bool live = t + 1 < T;
+        const size_t rc = live ? row + 1 : row;
+#pragma unroll
+        for (int m = 0; m < 4; m++) co[m] = a.gates[rc * 320 + 64 * m + i];
+#pragma unroll
+        for (int m = 0; m < 4; m++) co[m] = live ? co[m] : 0.f;
+        co[4] = a.g[row * 64 + i];
+        co[5] = 0.f;
+      }
+    };
+    float cn[6];
+    fetch(j * D64_L, cn);
     for (int s = 0; s < D64_L; s++) {
       const int sidx = j * D64_L + s;
       if (sidx >= T) break;
       const int t = ADJ ? T - 1 - sidx : sidx;
       const size_t row = (size_t)b * T + t;
+      float co[6];
+#pragma unroll
+      for (int m = 0; m < 6; m++) co[m] = cn[m];
+      fetch(sidx + 1, cn);
       float yn;
       if (!ADJ) {
-        const float *G = a.gates + row * 320;
         sY[wid][0][i] = y;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS order within the wavefront
         __builtin_amdgcn_wave_barrier();
         float sz = 0.f, sn = 0.f, sr = 0.f;
 #pragma unroll
@@ -487,21 +513,17 @@ __global__ __launch_bounds__(256) void k_d64_scanC(const D64Args a) {
             sr = fmaf(w[2][4 * k4 + q], vv[q], sr);
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
-        yn = fmaf(G[i], y, fmaf(G[64 + i], sz, fmaf(G[128 + i], sn, fmaf(G[192 + i], sr, G[256 + i]))));
-        const float hc = first ? 0.f : a.h[row * 64 + i];
-        a.h[row * 64 + i] = hc + yn;
+        yn = fmaf(co[0], y, fmaf(co[1], sz, fmaf(co[2], sn, fmaf(co[3], sr, co[4]))));
+        a.h[row * 64 + i] = (first ? 0.f : co[5]) + yn;
         const unsigned u = __float_as_uint(fabsf(yn));
         dmax = u > dmax ? u : dmax;
       } else {
-        const bool live = t + 1 < T;
-        const float *G = a.gates + (row + (live ? 1 : 0)) * 320;
-        const float z = live ? G[i] : 0.f;
-        sY[wid][0][i] = live ? G[64 + i] * y : 0.f;
-        sY[wid][1][i] = live ? G[128 + i] * y : 0.f;
-        sY[wid][2][i] = live ? G[192 + i] * y : 0.f;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        sY[wid][0][i] = co[1] * y;
+        sY[wid][1][i] = co[2] * y;
+        sY[wid][2][i] = co[3] * y;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
         float acc = 0.f;
 #pragma unroll
@@ -514,9 +536,9 @@ __global__ __launch_bounds__(256) void k_d64_scanC(const D64Args a) {
             acc = fmaf(w[m][4 * k4 + 2], v.z, acc);
             acc = fmaf(w[m][4 * k4 + 3], v.w, acc);
           }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
-        yn = fmaf(z, y, acc) + a.g[row * 64 + i];
+        yn = fmaf(co[0], y, acc) + co[4];
         a.lam[row * 64 + i] = yn;
       }
       y = yn;
