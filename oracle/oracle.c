@@ -33,6 +33,11 @@
  *  - orc_affine_solve: y_t = A_t y_{t-1} + b_t (or the reverse-time recurrence)
  *    by its definition, for the dense, diagonal and 2x2-block operators that
  *    the Para-Seq README lists (Main features: src.utils scans).
+ *  - orc_elk: quasi-ELK, the Levenberg-Marquardt-damped quasi-Newton sweep
+ *    solved as a Kalman smoother (Gonzalez et al. abstract: ELK connects
+ *    Levenberg-Marquardt with Kalman smoothing to stabilise DEER; Para-Seq
+ *    README, Main features: ELK and quasi-ELK solvers), with the textbook
+ *    Kalman filter and Rauch-Tung-Striebel smoother run sequentially.
  *  - orc_lsim_discrete: the sampled linear state-space simulation behind the
  *    README's lsim (Main features: ODE solvers; Example: lsim(A, B, C, D, U,
  *    t)) once the system is discretised: x_0 = x0, y_k = C x_k + D u_k,
@@ -623,4 +628,98 @@ int orc_lsim_discrete(int B, int T, int nx, int m, int p, const double *Ad, cons
     free(sn);
   }
   return err ? ORC_ENOMEM : ORC_OK;
+}
+
+/*
+ * Quasi-ELK.  Each sweep takes the Levenberg-Marquardt step of the residual
+ * system with the Jacobian's diagonal d_t (as ORC_QUASI) and damping lambda:
+ *   dh = argmin sum_t ||dh_t - d_t dh_{t-1} - r_t||^2 + lambda sum_t ||dh_t||^2,
+ * dh_{-1} = 0, which is the posterior mean of the linear-Gaussian model
+ *   dh_t = d_t dh_{t-1} + r_t + w_t,  w_t ~ N(0, 1);  0 = dh_t + v_t,
+ *   v_t ~ N(0, 1 / lambda),
+ * computed per state entry by the Kalman filter and the Rauch-Tung-Striebel
+ * smoother.  lambda = 0 gives the quasi-DEER step.  Then h += dh and the stop
+ * rule of orc_deer_approx.
+ */
+int orc_elk(const orc_model *m, double lambda, const double *x, const double *h0, double tol, int max_iters,
+            double *h, int *iters, int *status, double *deltas, int hist_cap) {
+  if (!model_ok(m) || max_iters < 1 || !(lambda >= 0.0)) return ORC_EINVAL;
+  int S = swidth(m), Gn = n_gates(m->cell) * m->n, T = m->T;
+  size_t js = jsize(m);
+  int kind = jkind(m->cell);
+  memset(h, 0, sizeof(double) * (size_t)m->B * T * S);
+  *iters = 0;
+  *status = ORC_OK;
+  if (T == 0 || m->B == 0) return ORC_OK;
+  for (int k = 1; k <= max_iters; k++) {
+    double delta = 0.0;
+    int err = 0, nonfin = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : delta) reduction(| : err, nonfin)
+    for (int b = 0; b < m->B; b++) {
+      double *U = (double *)malloc(sizeof(double) * Gn);
+      double *F = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *D = (double *)malloc(sizeof(double) * (size_t)T * S);  /* d_t: the Jacobian's diagonal */
+      double *R = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *J = (double *)malloc(sizeof(double) * js);
+      double *Pp = (double *)malloc(sizeof(double) * T), *Mp = (double *)malloc(sizeof(double) * T);
+      double *Pf = (double *)malloc(sizeof(double) * T), *Mf = (double *)malloc(sizeof(double) * T);
+      double *Ms = (double *)malloc(sizeof(double) * T);
+      double *zero = (double *)calloc(S, sizeof(double));
+      if (!U || !F || !D || !R || !J || !Pp || !Mp || !Pf || !Mf || !Ms || !zero) {
+        err |= 1;
+      } else {
+        double *hb = h + (size_t)b * T * S;
+        for (int t = 0; t < T; t++) {
+          const double *sp = t == 0 ? (h0 ? h0 + (size_t)b * S : zero) : hb + (size_t)(t - 1) * S;
+          input_proj(m, x + ((size_t)b * T + t) * m->d, U);
+          cell_fwd(m, sp, U, F + (size_t)t * S, J);
+          for (int i = 0; i < S; i++) {
+            double di;
+            if (kind == ORC_DENSE) di = J[(size_t)i * S + i];
+            else if (kind == ORC_DIAG) di = J[i];
+            else di = J[(size_t)4 * (i / 2) + ((i & 1) ? 3 : 0)]; /* dc'/dc, dh'/dh */
+            D[(size_t)t * S + i] = di;
+            R[(size_t)t * S + i] = F[(size_t)t * S + i] - hb[(size_t)t * S + i];
+          }
+        }
+        for (int i = 0; i < S; i++) {
+          /* Kalman filter: predicted (Pp, Mp) and filtered (Pf, Mf) moments */
+          double P = 0.0, Mn = 0.0;
+          for (int t = 0; t < T; t++) {
+            const double d = D[(size_t)t * S + i], r = R[(size_t)t * S + i];
+            const double pp = d * d * P + 1.0, mp = d * Mn + r;
+            const double K = lambda * pp / (lambda * pp + 1.0);  /* gain for an observation of variance 1/lambda */
+            Pp[t] = pp;
+            Mp[t] = mp;
+            P = (1.0 - K) * pp;
+            Mn = (1.0 - K) * mp;
+            Pf[t] = P;
+            Mf[t] = Mn;
+          }
+          /* Rauch-Tung-Striebel smoother */
+          Ms[T - 1] = Mf[T - 1];
+          for (int t = T - 2; t >= 0; t--) {
+            const double G = Pf[t] * D[(size_t)(t + 1) * S + i] / Pp[t + 1];
+            Ms[t] = Mf[t] + G * (Ms[t + 1] - Mp[t + 1]);
+          }
+          for (int t = 0; t < T; t++) {
+            hb[(size_t)t * S + i] += Ms[t];
+            const double a = fabs(Ms[t]);
+            if (!isfinite(a)) nonfin = 1;
+            else if (a > delta) delta = a;
+          }
+        }
+      }
+      free(U); free(F); free(D); free(R); free(J); free(Pp); free(Mp); free(Pf); free(Mf); free(Ms); free(zero);
+    }
+    if (err) return ORC_ENOMEM;
+    if (nonfin) delta = NAN;
+    if (deltas && k <= hist_cap) deltas[k - 1] = delta;
+    *iters = k;
+    if (!isfinite(delta)) { *status = ORC_NONFINITE; return ORC_OK; }
+    if (tol > 0.0 && delta < tol) { *status = ORC_OK; return ORC_OK; }
+    if (k == T) { *status = ORC_OK; return ORC_OK; }
+  }
+  *status = tol > 0.0 ? ORC_NOT_CONVERGED : ORC_OK;
+  return ORC_OK;
 }

@@ -20,6 +20,10 @@ sign or index, a transposed operand) fails at least one test:
   Jacobian is diagonal, equals Jacobi for a tanh RNN whose recurrent matrix
   has a zero diagonal, and equals Newton on the LSTM cell state when that
   state does not depend on h; both reach the rollout;
+* quasi-ELK: without damping it is quasi-DEER; each damped step solves the
+  Levenberg-Marquardt normal equations (an independent formulation, small
+  T); damped steps obey lam ||dh||^2 <= ||r||^2 and stay bounded where
+  Newton's grow to 1e31; it reaches the rollout;
 * lsim: the README's decay example and closed forms (held constant input,
   rotation, double integrator), feedthrough, and scipy.signal.lsim with a
   zero-order hold;
@@ -592,3 +596,83 @@ def test_lsim_matches_scipy_signal(nx, m, p):
     _, ys, xs = scipy.signal.lsim((A, Bm, Cm, Dm), U, t, X0=x0, interp=False)
     np.testing.assert_allclose(y, np.reshape(ys, y.shape), rtol=0, atol=1e-12)
     np.testing.assert_allclose(x, np.reshape(xs, x.shape), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# quasi-ELK: the damped (Levenberg-Marquardt) quasi-Newton step as a Kalman smoother
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cell", LIB_CELLS)
+def test_elk_without_damping_is_quasi_deer(cell):
+    p = small_problem(cell, T=30)
+    for k in (1, 2, 5):
+        he, _, _, de = oracle.elk(p, 0.0, tol=0.0, max_iters=k)
+        hq, _, _, dq = oracle.deer(p, tol=0.0, max_iters=k, approx=oracle.QUASI)
+        np.testing.assert_array_equal(he, hq)
+        np.testing.assert_array_equal(de, dq)
+
+
+def _diag_and_residual(p, h):
+    """The Jacobian's diagonal d [B,T,S] and the residual r = f - h at the iterate h (via oracle.cell)."""
+    B, T, S = h.shape
+    d, r = np.zeros_like(h), np.zeros_like(h)
+    for b in range(B):
+        for t in range(T):
+            sp = p["h0"][b] if t == 0 else h[b, t - 1]
+            f, J = oracle.cell(p, sp, p["x"][b, t])
+            if p["cell"] == sy.CELL_GRU_DIAG:
+                d[b, t] = J
+            elif p["cell"] == sy.CELL_LSTM_CIFG_DIAG:
+                d[b, t, 0::2], d[b, t, 1::2] = J[:, 0, 0], J[:, 1, 1]
+            else:
+                d[b, t] = np.diag(J)
+            r[b, t] = f - h[b, t]
+    return d, r
+
+
+def _damped_lsq(d, r, lam):
+    """argmin ||L x - r||^2 + lam ||x||^2 with (L x)_t = x_t - d_t x_{t-1}, by the normal equations."""
+    T = len(r)
+    L = np.eye(T) - np.diag(d[1:], -1)
+    return np.linalg.solve(L.T @ L + lam * np.eye(T), L.T @ r)
+
+
+@pytest.mark.parametrize("lam", [0.1, 1.0, 10.0])
+@pytest.mark.parametrize("cell", LIB_CELLS)
+def test_elk_step_solves_the_damped_least_squares(cell, lam):
+    # an independent formulation of the same step: the normal equations of
+    # the Levenberg-Marquardt problem, per state entry, on small T
+    p = small_problem(cell, B=2, T=7)
+    h1, _, _, _ = oracle.elk(p, lam, tol=0.0, max_iters=1)
+    h2, _, _, _ = oracle.elk(p, lam, tol=0.0, max_iters=2)
+    for h_prev, h_next in ((np.zeros_like(h1), h1), (h1, h2)):
+        d, r = _diag_and_residual(p, h_prev)
+        for b in range(p["B"]):
+            for i in range(p["S"]):
+                np.testing.assert_allclose(h_next[b, :, i] - h_prev[b, :, i], _damped_lsq(d[b, :, i], r[b, :, i], lam),
+                                           rtol=0, atol=1e-12)
+
+
+def test_elk_step_norm_bound_and_stability():
+    # lam ||dh||^2 <= ||r||^2 per state entry (dh = 0 is a candidate), so
+    # damped steps stay bounded on a strongly expanding tanh RNN on which
+    # Newton's steps grow to 1e31 before the prefix fixes them
+    p = sy.custom_problem(sy.CELL_TANH_RNN, B=2, T=120, d=3, n=4, seed=3, w_scale=4.0, h0=True)
+    lam = 0.3
+    h_prev = np.zeros((p["B"], p["T"], p["S"]))
+    for k in range(1, 6):
+        h_next, _, _, _ = oracle.elk(p, lam, tol=0.0, max_iters=k)
+        _, r = _diag_and_residual(p, h_prev)
+        step = h_next - h_prev
+        assert np.all(lam * (step ** 2).sum(1) <= (r ** 2).sum(1) * (1 + 1e-12) + 1e-300)
+        h_prev = h_next
+    _, _, _, dl_newton = oracle.deer(p, tol=0.0, max_iters=60)
+    _, _, _, dl_elk = oracle.elk(p, lam, tol=0.0, max_iters=60)
+    assert dl_newton.max() > 1e10 and dl_elk.max() < 10
+
+
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (4, dict(T=128, n=16, d=16)), (5, dict(B=2, T=256))])
+def test_elk_reaches_the_rollout(cfg, kw):
+    p = sy.make_problem(cfg, **kw)
+    h, iters, status, dl = oracle.elk(p, 0.1, tol=1e-11, max_iters=p["T"])
+    assert status == oracle.OK and iters < p["T"]
+    np.testing.assert_allclose(h, oracle.rollout(p), rtol=0, atol=1e-10)
