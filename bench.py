@@ -28,6 +28,8 @@ from nonlinear_rnn_evaluation_newton_amd import synthetic as sy  # noqa: E402  (
 
 
 HBM_PEAK_GBS = 8000.0
+ELK_KERNELS = ("quasi-ELK sweep: producer of the Jacobian's diagonal and the residual (k_elk_jr_chan, or "
+               "k_d64_gates<GM_QUASI> for the dense GRU) + k_elk_riccati/mean/gains/apply and their chunk carries")
 FP32_MFMA_PEAK_TFS = 157.3
 
 
@@ -208,6 +210,8 @@ def main() -> int:
     ap.add_argument("--jac", choices=("own", "diag", "zero"), default="own",
                     help="Jacobian of the sweeps' linear solve: the cell's own (Newton), its diagonal "
                          "(quasi-DEER) or zero (Jacobi)")
+    ap.add_argument("--elk", type=float, default=None, metavar="LAMBDA",
+                    help="solve with quasi-ELK at damping LAMBDA (workloads 3, 4, 5)")
     ap.add_argument("--lsim", action="store_true",
                     help="time the linear state-space simulation workload (B=16, T=2^20, 4 states) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,7 +245,11 @@ def main() -> int:
         p = dict(p, jac=sy.JAC_DIAG if args.jac == "diag" else sy.JAC_ZERO,
                  name=p["name"] + ("_quasi" if args.jac == "diag" else "_jacobi"))
     approx = args.jac != "own" and not (args.jac == "diag" and (p["cell"] == sy.CELL_GRU_DIAG or p["n"] == 1))
-    dp = bd.DeviceProblem(p)
+    elk = args.elk is not None
+    if elk:
+        p = dict(p, name=p["name"] + f"_elk{args.elk:g}")
+        approx = True
+    dp = bd.DeviceProblem(p, elk=elk)
     B, T = p["B"], p["T"]
     units = B * T
 
@@ -256,8 +264,11 @@ def main() -> int:
 
     iters_seen = []
 
+    def solve():
+        return dp.solve_elk(args.elk) if elk else dp.solve()
+
     def step():
-        st, it, dl = dp.solve()
+        st, it, dl = solve()
         if st < 0 or st == bd.PR_NONFINITE:
             raise RuntimeError(f"solve failed: {st}")
         iters_seen.append(it)
@@ -284,7 +295,7 @@ def main() -> int:
     torch.cuda.synchronize()
     s0 = time.perf_counter()
     for _ in range(args.steps):
-        dp.solve()
+        solve()
     torch.cuda.synchronize()
     ms_solve = (time.perf_counter() - s0) * 1e3 / args.steps
 
@@ -303,7 +314,8 @@ def main() -> int:
         achieved = per_solve_bytes / iters / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(p["name"]),
-                    "kernel": "k_d64_gates<GM_QUASI> + k_d64q_carry + k_d64q_apply per sweep (gates GEMM with the "
+                    "kernel": ELK_KERNELS if elk else
+                              "k_d64_gates<GM_QUASI> + k_d64q_carry + k_d64q_apply per sweep (gates GEMM with the "
                               "diagonal Jacobian and chunk aggregates; chunk carries; update)",
                     "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": per_solve_bytes / iters}
         dm, dn = bd.trace_kernel(bd.TRACE_DENSE_PRODUCTS)
@@ -336,7 +348,8 @@ def main() -> int:
         nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
         achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
-        kname = ("k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
+        kname = (ELK_KERNELS if elk else
+                 "k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
                  "sweep's tile aggregates)" if chan else
                  ("k_pipe<SweepPol>" if scalar_path(p) and not approx else "k_time_sweep") +
                  " (fused cell + Jacobian + scan + update)")
@@ -377,8 +390,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": p["name"], "cell": sy.CELL_NAMES[p["cell"]], "B": B, "T": T, "d": p["d"],
                    "n": p["n"], "tol": p["tol"], "max_iters": p["max_iters"], "step": "solve + adjoint",
-                   "jacobian": {"own": "the cell's", "diag": "diagonal (quasi-DEER)",
-                                "zero": "zero (Jacobi)"}[args.jac]},
+                   "jacobian": ("diagonal, quasi-ELK damping %g" % args.elk) if elk else
+                               {"own": "the cell's", "diag": "diagonal (quasi-DEER)", "zero": "zero (Jacobi)"}[args.jac]},
         "iters": iters,
         "final_delta": float(dl[-1]) if len(dl) else None,
         "solve_ms": ms_solve,

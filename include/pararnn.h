@@ -142,6 +142,27 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
                   size_t ws_bytes, void *stream);
 
 /*
+ * Quasi-ELK solve (Gonzalez et al. abstract: ELK stabilises DEER through the
+ * connection between Levenberg-Marquardt and Kalman smoothing; Para-Seq
+ * README, Main features: ELK and quasi-ELK solvers).  Each sweep takes the
+ * damped step
+ *   dh = argmin sum_t ||dh_t - d_t dh_{t-1} - r_t||^2 + lambda ||dh||^2
+ * with d_t the diagonal of J_t (the LSTM: dc'/dc and dh'/dh), computed per
+ * state entry as the Kalman filter / Rauch-Tung-Striebel smoother mean of
+ * dh_t = d_t dh_{t-1} + r_t + N(0, 1) observed as 0 with variance 1/lambda,
+ * then h += dh.  lambda = 0 is quasi-DEER; larger lambda shortens the steps
+ * (lambda ||dh||^2 <= ||r||^2).  p->jac is not used.  Kernels exist for the
+ * dense GRU with n = 64 (fp32) and for GRU_DIAG and LSTM_CIFG_DIAG (fp32 or
+ * bf16); other problems return PR_EUNSUPPORTED.  Arguments and results as
+ * pararnn_solve, plus lambda (>= 0, finite); the workspace must hold
+ * pararnn_elk_workspace_bytes (which also covers pararnn_adjoint).
+ */
+size_t pararnn_elk_workspace_bytes(const pr_problem *p);
+int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float lambda,
+                      float tol, int max_iters, void *h, int *iters, float *delta_hist, int hist_cap,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Gradient of L = sum_{b,t} <g_t, h_t> at the trajectory h (normally the
  * output of pararnn_solve), by one reverse linear solve
  *   lambda_t = g_t + J_{t+1}^T lambda_{t+1},  lambda_T-1 = g_T-1,

@@ -23,7 +23,8 @@ PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3
 
 EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_scan_workspace_bytes",
            "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
-           "pararnn_trace_kernel", "pararnn_lsim_workspace_bytes", "pararnn_lsim"]
+           "pararnn_trace_kernel", "pararnn_lsim_workspace_bytes", "pararnn_lsim", "pararnn_elk_workspace_bytes",
+           "pararnn_solve_elk"]
 
 
 class Problem(C.Structure):
@@ -82,6 +83,10 @@ def lib():
         L.pararnn_lsim_workspace_bytes.restype = S
         L.pararnn_lsim.argtypes = [I, I, I, I, I, P, P, P, P, F, P, P, P, P, P, S, P]
         L.pararnn_lsim.restype = I
+        L.pararnn_elk_workspace_bytes.argtypes = [P]
+        L.pararnn_elk_workspace_bytes.restype = S
+        L.pararnn_solve_elk.argtypes = [P, P, P, P, F, F, I, P, P, P, I, P, S, P]
+        L.pararnn_solve_elk.restype = I
         _lib = L
     return _lib
 
@@ -125,6 +130,23 @@ def solve(prob: Problem, w: Weights, x, h0, tol: float, max_iters: int, h, works
                              workspace.numel() * workspace.element_size(), _stream())
     if check and st < 0:
         raise PararnnError(st, "pararnn_solve")
+    return st, it.value, hist[:min(it.value, hist_cap)].copy()
+
+
+def elk_workspace_bytes(prob: Problem) -> int:
+    return lib().pararnn_elk_workspace_bytes(C.byref(prob))
+
+
+def solve_elk(prob: Problem, w: Weights, x, h0, lam: float, tol: float, max_iters: int, h, workspace,
+              hist_cap: int = 64, check: bool = True):
+    """Runs pararnn_solve_elk (quasi-ELK, damping lam); returns (status, iters, delta history)."""
+    it = C.c_int(0)
+    hist = np.zeros(max(hist_cap, 1), dtype=np.float32)
+    st = lib().pararnn_solve_elk(C.byref(prob), C.byref(w), _p(x), _p(h0), float(lam), float(tol), int(max_iters),
+                                 _p(h), C.byref(it), hist.ctypes.data_as(C.c_void_p), int(hist_cap), _p(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    if check and st < 0:
+        raise PararnnError(st, "pararnn_solve_elk")
     return st, it.value, hist[:min(it.value, hist_cap)].copy()
 
 
@@ -203,7 +225,7 @@ def lsim(A, Bm, Cm, Dm, dt: float, U, x0, x, y, workspace, check: bool = True) -
 class DeviceProblem:
     """Device copies of a synthetic problem in its storage dtype, plus a workspace."""
 
-    def __init__(self, p: dict, device="cuda", with_adjoint: bool = True):
+    def __init__(self, p: dict, device="cuda", with_adjoint: bool = True, elk: bool = False):
         import torch
         from . import synthetic as sy
         self.p = p
@@ -228,6 +250,10 @@ class DeviceProblem:
         nbytes = workspace_bytes(self.prob, with_adjoint)
         if nbytes == 0:
             raise RuntimeError(f"pararnn_workspace_bytes: {last_error()}")
+        if elk:
+            nbytes = elk_workspace_bytes(self.prob)
+            if nbytes == 0:
+                raise RuntimeError(f"pararnn_elk_workspace_bytes: {last_error()}")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.h = torch.empty((p["B"], p["T"], p["S"]), dtype=self.tdtype, device=device)
 
@@ -236,6 +262,12 @@ class DeviceProblem:
         tol = p["tol"] if tol is None else tol
         max_iters = p["max_iters"] if max_iters is None else max_iters
         return solve(self.prob, self.w, self.x, self.h0, tol, max_iters, self.h, self.ws, hist_cap, check)
+
+    def solve_elk(self, lam, tol=None, max_iters=None, hist_cap=64, check=True):
+        p = self.p
+        tol = p["tol"] if tol is None else tol
+        max_iters = p["max_iters"] if max_iters is None else max_iters
+        return solve_elk(self.prob, self.w, self.x, self.h0, lam, tol, max_iters, self.h, self.ws, hist_cap, check)
 
     def adjoint(self, h=None, g=None, want_grads=True, check=True):
         import torch

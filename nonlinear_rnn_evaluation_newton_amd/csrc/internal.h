@@ -183,4 +183,28 @@ int lsim_table_floats();
 int lsim_chunk_len(int m);  // steps per chunk
 hipError_t launch_lsim(LsimArgs &a, hipStream_t s);
 
+// quasi-ELK (k_elk.hip)
+struct ElkArgs {
+  float *jr;  // [rows][2S]: the Jacobian's diagonal d | residual r (producer output)
+  float *ge;  // [rows][2S]: smoother gains G | offsets e
+  float *r1, *pc, *r2, *mc, *r3, *msc;  // per chunk: Riccati maps [4][S], entering P [S],
+                                        // mean maps [2][S], entering m [S], reverse maps [2][S], m^s from the right [S]
+  void *h;    // [rows][S] iterate (storage dtype)
+  int h_bf16;
+  int B, T, S, cps, nch;
+  float lam;
+  int k;
+  float tol;
+  int max_iters;
+  SolveState *st;
+};
+struct ElkChanArgs {  // producer for the per-channel cells
+  ElkArgs e;
+  const void *U, *h0, *Wh, *bh, *peep;
+  int n;
+};
+int elk_chunk_len();
+hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s);
+hipError_t launch_elk_jr_chan(int cell, bool bf16, const ElkChanArgs &a, hipStream_t s);
+
 }  // namespace pr

@@ -360,13 +360,54 @@ size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
   return with_adjoint ? pl.adjoint_bytes : pl.solve_bytes;
 }
 
-int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol, int max_iters,
-                  void *h, int *iters, float *delta_hist, int hist_cap, void *workspace, size_t ws_bytes,
-                  void *stream) {
+// Quasi-ELK scratch beyond a solve's workspace: [d | r] (unless the dense
+// path's gates buffer holds it), [G | e], chunk aggregates and carries.
+struct ElkLayout {
+  size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_r2 = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
+  size_t bytes = 0;
+  int cps = 0, nch = 0;
+};
+static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
+  if (pl.path != PATH_D64 && pl.path != PATH_CHAN)
+    return fail(PR_EUNSUPPORTED, "quasi-ELK runs on the dense n = 64 GRU and the per-channel cells");
+  const size_t rows = (size_t)p->B * p->T, S = (size_t)pl.S;
+  el->cps = (p->T + elk_chunk_len() - 1) / elk_chunk_len();
+  if ((long long)el->cps * p->B * ((pl.S + 63) / 64) > 2147483647LL / 4 || (long long)p->B * pl.S > 2147483647LL / 4)
+    return fail(PR_EUNSUPPORTED, "problem too large");
+  el->nch = el->cps * p->B;
+  const size_t nch = (size_t)el->nch;
+  size_t o = pl.solve_bytes;
+  if (pl.path == PATH_D64) {
+    el->off_jr = pl.off_gates;  // [row][320] floats hold [d (64) | r (64)]
+  } else {
+    el->off_jr = o; o = align256(o + rows * 2 * S * 4);
+  }
+  el->off_ge = o; o = align256(o + rows * 2 * S * 4);
+  el->off_r1 = o; o = align256(o + nch * 4 * S * 4);
+  el->off_pc = o; o = align256(o + nch * S * 4);
+  el->off_r2 = o; o = align256(o + nch * 2 * S * 4);
+  el->off_mc = o; o = align256(o + nch * S * 4);
+  el->off_r3 = o; o = align256(o + nch * 2 * S * 4);
+  el->off_msc = o; o = align256(o + nch * S * 4);
+  el->bytes = o;
+  return PR_OK;
+}
+
+static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                      int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
+                      size_t ws_bytes, void *stream, const float *elk_lambda) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, &pl);
   if (rc != PR_OK) return rc;
+  ElkLayout el;
+  if (elk_lambda) {
+    if (!(*elk_lambda >= 0.f) || *elk_lambda > 3.0e38f) return fail(PR_EINVAL, "lambda must be >= 0 and finite");
+    rc = elk_layout(p, pl, &el);
+    if (rc != PR_OK) return rc;
+    pl.approx = APX_DIAG;  // the producer evaluates the Jacobian's diagonal
+    pl.solve_bytes = el.bytes;
+  }
   if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
   if (p->cell == PR_CELL_LSTM_CIFG_DIAG && !w->peep) return fail(PR_EINVAL, "the LSTM cell needs peepholes");
   if (!x || !h) return fail(PR_EINVAL, "x and h are required");
@@ -458,6 +499,35 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     HIPCHK(launch_scalar_coef(a, kc, (float *)(ws + pl.off_coef), s));
   }
 
+  ElkArgs ea{};
+  ElkChanArgs eca{};
+  if (elk_lambda) {
+    ea.jr = (float *)(ws + el.off_jr);
+    ea.ge = (float *)(ws + el.off_ge);
+    ea.r1 = (float *)(ws + el.off_r1);
+    ea.pc = (float *)(ws + el.off_pc);
+    ea.r2 = (float *)(ws + el.off_r2);
+    ea.mc = (float *)(ws + el.off_mc);
+    ea.r3 = (float *)(ws + el.off_r3);
+    ea.msc = (float *)(ws + el.off_msc);
+    ea.h = h;
+    ea.h_bf16 = p->dtype == PR_BF16;
+    ea.B = p->B; ea.T = p->T; ea.S = pl.S; ea.cps = el.cps; ea.nch = el.nch;
+    ea.lam = *elk_lambda;
+    ea.tol = tol;
+    ea.max_iters = max_iters;
+    ea.st = (SolveState *)(ws + pl.off_state);
+    if (pl.path == PATH_CHAN) {
+      eca.e = ea;
+      eca.U = ws + pl.off_U;
+      eca.h0 = h0;
+      eca.Wh = w->W_h;
+      eca.bh = w->b_h;
+      eca.peep = p->cell == PR_CELL_LSTM_CIFG_DIAG ? w->peep : nullptr;
+      eca.n = p->n;
+    }
+  }
+
   int first, next;
   poll_schedule(&first, &next);
   if (tol <= 0.f) first = kmax;
@@ -465,7 +535,7 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
   // Sweep timing: the dense n = 64 path brackets every sweep (its parts are
   // timed too); the others bracket each batch of back-to-back sweeps, so the
   // per-launch figure carries no event overhead between launches.
-  const bool per_sweep_events = pl.path == PATH_D64;
+  const bool per_sweep_events = pl.path == PATH_D64 && !elk_lambda;
   int nbatch = 0, batch_first[Trace::CAP], batch_last[Trace::CAP];
   while (true) {
     const int batch = k == 1 ? first : next;
@@ -482,7 +552,17 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
       a.k = kk;
       const bool ev = tr.on && per_sweep_events && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      if (scalar) {
+      if (elk_lambda) {  // producer of [d | r], then the damped step
+        if (pl.path == PATH_D64) {
+          da.k = kk;
+          HIPCHK(launch_d64_sweep_part(da, 0, s));
+        } else {
+          eca.e.k = kk;
+          HIPCHK(launch_elk_jr_chan(kc, p->dtype == PR_BF16, eca, s));
+        }
+        ea.k = kk;
+        HIPCHK(launch_elk_sweep(ea, s));
+      } else if (scalar) {
         HIPCHK(launch_scalar_sweep(kc, a, s));
       } else if (pl.path == PATH_TIME) {
         HIPCHK(launch_time_sweep(kc, pl.N, a, s));
@@ -554,6 +634,29 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
     for (int kk = 1; kk <= m; kk++) delta_hist[kk - 1] = __builtin_bit_cast(float, hs->hist[kk % PR_HIST]);
   }
   return out_status == ST_NONFINITE ? PR_NONFINITE : out_status == ST_NOT_CONVERGED ? PR_NOT_CONVERGED : PR_OK;
+}
+
+int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol, int max_iters,
+                  void *h, int *iters, float *delta_hist, int hist_cap, void *workspace, size_t ws_bytes,
+                  void *stream) {
+  return solve_impl(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
+                    nullptr);
+}
+
+size_t pararnn_elk_workspace_bytes(const pr_problem *p) {
+  g_err.clear();
+  Plan pl;
+  if (make_plan(p, &pl) != PR_OK) return 0;
+  ElkLayout el;
+  if (elk_layout(p, pl, &el) != PR_OK) return 0;
+  return el.bytes > pl.adjoint_bytes ? el.bytes : pl.adjoint_bytes;
+}
+
+int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float lambda,
+                      float tol, int max_iters, void *h, int *iters, float *delta_hist, int hist_cap,
+                      void *workspace, size_t ws_bytes, void *stream) {
+  return solve_impl(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
+                    &lambda);
 }
 
 int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,

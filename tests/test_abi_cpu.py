@@ -117,3 +117,24 @@ def test_lsim_arguments_rejected_without_device():
     assert call(n=ws - 1) == bd.PR_EWORKSPACE and call(w=None) == bd.PR_EWORKSPACE
     assert call(w=C.c_void_p(264)) == bd.PR_EINVAL  # not 256-byte aligned
     assert bd.last_error() != ""
+
+
+def test_elk_arguments_rejected_without_device():
+    L = bd.lib()
+    good = bd.Problem(sy.CELL_GRU_DIAG, sy.JAC_DIAG, bd.PR_F32, 2, 100, 3, 8)
+    assert bd.elk_workspace_bytes(good) >= bd.workspace_bytes(good, True) > 0
+    small = bd.Problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 4)
+    assert bd.elk_workspace_bytes(small) == 0  # no quasi-ELK kernels for the small dense cells
+    w = bd.Weights(1, None, 1, None, None)
+    v = C.c_void_p(16)
+    ws = bd.elk_workspace_bytes(good)
+
+    def call(pb=good, lam=0.5, n=ws, x=v):
+        return L.pararnn_solve_elk(C.byref(pb), C.byref(w), x, None, lam, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
+                                   n, None)
+
+    assert call(lam=-1.0) == bd.PR_EINVAL and call(lam=float("nan")) == bd.PR_EINVAL
+    assert call(lam=float("inf")) == bd.PR_EINVAL
+    assert call(pb=small) == bd.PR_EUNSUPPORTED
+    assert call(n=1024) == bd.PR_EWORKSPACE
+    assert call(x=None) == bd.PR_EINVAL
