@@ -198,13 +198,18 @@ struct ElkArgs {
   int max_iters;
   SolveState *st;
 };
-struct ElkChanArgs {  // producer for the per-channel cells
+struct ElkChanArgs {  // per-channel cells (the smoother's e.r3 and e.msc are shared)
   ElkArgs e;
   const void *U, *h0, *Wh, *bh, *peep;
+  float *fagg, *fcar;  // per filter chunk (4 apply chunks): filter maps [7][S], (P, m) entering [2][S]
+  float *fsub;         // per apply chunk (e.cps per sequence): (P, m) entering [2][S]
+  float *dr, *hb;      // per apply chunk: d, r at the next chunk's first step [2][S], state at the last step [S]
   int n;
+  int cpf, nchf;       // filter chunks per sequence and in all
 };
 int elk_chunk_len();
+int elk_chan_chunk_len(int sw);
 hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s);
-hipError_t launch_elk_jr_chan(int cell, bool bf16, const ElkChanArgs &a, hipStream_t s);
+hipError_t launch_elk_chan_sweep(int cell, bool bf16, ElkChanArgs &a, hipStream_t s);
 
 }  // namespace pr

@@ -360,18 +360,21 @@ size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
   return with_adjoint ? pl.adjoint_bytes : pl.solve_bytes;
 }
 
-// Quasi-ELK scratch beyond a solve's workspace: [d | r] (unless the dense
-// path's gates buffer holds it), [G | e], chunk aggregates and carries.
+// Quasi-ELK scratch beyond a solve's workspace.  Dense n = 64 GRU: [G | e]
+// per step ([d | r] sits in the gates buffer), chunk aggregates and carries.
+// Per-channel cells: chunk aggregates, carries and boundary values only.
 struct ElkLayout {
   size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_r2 = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
+  size_t off_fagg = 0, off_fcar = 0, off_fsub = 0, off_dr = 0, off_hb = 0;
   size_t bytes = 0;
-  int cps = 0, nch = 0;
+  int cps = 0, nch = 0, cpf = 0, nchf = 0;
 };
 static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   if (pl.path != PATH_D64 && pl.path != PATH_CHAN)
     return fail(PR_EUNSUPPORTED, "quasi-ELK runs on the dense n = 64 GRU and the per-channel cells");
   const size_t rows = (size_t)p->B * p->T, S = (size_t)pl.S;
-  el->cps = (p->T + elk_chunk_len() - 1) / elk_chunk_len();
+  const int L = pl.path == PATH_D64 ? elk_chunk_len() : elk_chan_chunk_len(p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1);
+  el->cps = (p->T + L - 1) / L;
   if ((long long)el->cps * p->B * ((pl.S + 63) / 64) > 2147483647LL / 4 || (long long)p->B * pl.S > 2147483647LL / 4)
     return fail(PR_EUNSUPPORTED, "problem too large");
   el->nch = el->cps * p->B;
@@ -379,14 +382,20 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   size_t o = pl.solve_bytes;
   if (pl.path == PATH_D64) {
     el->off_jr = pl.off_gates;  // [row][320] floats hold [d (64) | r (64)]
+    el->off_ge = o; o = align256(o + rows * 2 * S * 4);
+    el->off_r1 = o; o = align256(o + nch * 4 * S * 4);
+    el->off_pc = o; o = align256(o + nch * S * 4);
+    el->off_r2 = o; o = align256(o + nch * 2 * S * 4);
+    el->off_mc = o; o = align256(o + nch * S * 4);
   } else {
-    el->off_jr = o; o = align256(o + rows * 2 * S * 4);
+    el->cpf = (p->T + 4 * L - 1) / (4 * L);  // filter chunks of 4 apply chunks
+    el->nchf = el->cpf * p->B;
+    el->off_fagg = o; o = align256(o + (size_t)el->nchf * 7 * S * 4);
+    el->off_fcar = o; o = align256(o + (size_t)el->nchf * 2 * S * 4);
+    el->off_fsub = o; o = align256(o + nch * 2 * S * 4);
+    el->off_dr = o; o = align256(o + nch * 2 * S * 4);
+    el->off_hb = o; o = align256(o + nch * S * 4);
   }
-  el->off_ge = o; o = align256(o + rows * 2 * S * 4);
-  el->off_r1 = o; o = align256(o + nch * 4 * S * 4);
-  el->off_pc = o; o = align256(o + nch * S * 4);
-  el->off_r2 = o; o = align256(o + nch * 2 * S * 4);
-  el->off_mc = o; o = align256(o + nch * S * 4);
   el->off_r3 = o; o = align256(o + nch * 2 * S * 4);
   el->off_msc = o; o = align256(o + nch * S * 4);
   el->bytes = o;
@@ -502,12 +511,14 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   ElkArgs ea{};
   ElkChanArgs eca{};
   if (elk_lambda) {
-    ea.jr = (float *)(ws + el.off_jr);
-    ea.ge = (float *)(ws + el.off_ge);
-    ea.r1 = (float *)(ws + el.off_r1);
-    ea.pc = (float *)(ws + el.off_pc);
-    ea.r2 = (float *)(ws + el.off_r2);
-    ea.mc = (float *)(ws + el.off_mc);
+    if (pl.path == PATH_D64) {
+      ea.jr = (float *)(ws + el.off_jr);
+      ea.ge = (float *)(ws + el.off_ge);
+      ea.r1 = (float *)(ws + el.off_r1);
+      ea.pc = (float *)(ws + el.off_pc);
+      ea.r2 = (float *)(ws + el.off_r2);
+      ea.mc = (float *)(ws + el.off_mc);
+    }
     ea.r3 = (float *)(ws + el.off_r3);
     ea.msc = (float *)(ws + el.off_msc);
     ea.h = h;
@@ -525,6 +536,13 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       eca.bh = w->b_h;
       eca.peep = p->cell == PR_CELL_LSTM_CIFG_DIAG ? w->peep : nullptr;
       eca.n = p->n;
+      eca.fagg = (float *)(ws + el.off_fagg);
+      eca.fcar = (float *)(ws + el.off_fcar);
+      eca.fsub = (float *)(ws + el.off_fsub);
+      eca.cpf = el.cpf;
+      eca.nchf = el.nchf;
+      eca.dr = (float *)(ws + el.off_dr);
+      eca.hb = (float *)(ws + el.off_hb);
     }
   }
 
@@ -552,16 +570,16 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       a.k = kk;
       const bool ev = tr.on && per_sweep_events && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      if (elk_lambda) {  // producer of [d | r], then the damped step
-        if (pl.path == PATH_D64) {
+      if (elk_lambda) {  // the damped step
+        if (pl.path == PATH_D64) {  // producer of [d | r], then the scans
           da.k = kk;
           HIPCHK(launch_d64_sweep_part(da, 0, s));
+          ea.k = kk;
+          HIPCHK(launch_elk_sweep(ea, s));
         } else {
           eca.e.k = kk;
-          HIPCHK(launch_elk_jr_chan(kc, p->dtype == PR_BF16, eca, s));
+          HIPCHK(launch_elk_chan_sweep(kc, p->dtype == PR_BF16, eca, s));
         }
-        ea.k = kk;
-        HIPCHK(launch_elk_sweep(ea, s));
       } else if (scalar) {
         HIPCHK(launch_scalar_sweep(kc, a, s));
       } else if (pl.path == PATH_TIME) {
