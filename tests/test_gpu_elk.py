@@ -6,6 +6,9 @@ per-channel cells in fp32 and bf16 storage, with and without damping.
 Damped sweeps converge linearly; as for the other approximate sweeps, where
 the oracle's deciding delta lies within fp32 noise of tol the GPU may stop
 one sweep apart, and is then compared at its own sweep count."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -19,6 +22,7 @@ torch = pytest.importorskip("torch")
 ATOL = 1e-4
 RTOL_BF = 2e-2
 TOL_MARGIN, TOL_NOISE = 0.05, 2e-7
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -88,6 +92,64 @@ def test_channel_fp32(lam, cell, n, d, T):
 def test_channel_bf16(cell):
     p = sy.custom_problem(cell, B=3, T=500, d=24, n=96, seed=4, w_scale=0.8, h0=True, dtype=sy.DT_BF16)
     check(p, 0.3, 0.0, 6, bf16=True)
+
+
+def test_dense64_full_size():
+    """The full dense workload with quasi-ELK (lambda 0.1) in the benchmark's
+    configuration: sweep count and delta history against the oracle's record
+    at full size; h of two sampled sequences against the oracle's quasi-ELK
+    iterate at the GPU's sweep count."""
+    gold = json.load(open(os.path.join(GOLDEN, "dense64_gru_elk_full_history.json")))
+    p = sy.make_problem(5, with_g=False)
+    lam = gold["lambda"]
+    say("case dense64 quasi-ELK full size, lambda", lam)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, dl = dp.solve_elk(lam, hist_cap=4096)
+    torch.cuda.synchronize()
+    dlo = np.asarray(gold["deltas"])
+    ito = gold["iters"]
+    say("  gpu", it, st, dl[-3:], "| oracle", ito, dlo[-3:])
+    assert st == bd.PR_OK
+    k = min(it, ito)
+    assert it == ito or (abs(it - ito) == 1 and abs(dlo[k - 1] - p["tol"]) <= max(TOL_MARGIN * p["tol"], TOL_NOISE))
+    assert np.allclose(dl[:k], dlo[:k], rtol=1e-3, atol=ATOL)
+    for b in (0, p["B"] - 1):
+        qb = dict(p, B=1, x=p["x"][b:b + 1], h0=p["h0"][b:b + 1])
+        hb, *_ = oracle.elk(qb, lam, tol=0.0, max_iters=it)
+        err = np.abs(to64(dp.h[b]) - hb[0]).max()
+        say("  sequence", b, "max abs err", err)
+        assert err <= ATOL
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_channel_full_size_sampled(cfg):
+    """The full bf16 channel workloads (4 fixed sweeps) with quasi-ELK (lambda
+    0.1) in the benchmark's configuration; the oracle checks 12 sampled
+    channels (first, last and random ones)."""
+    lam = 0.1
+    p = sy.make_problem(cfg, with_g=False)
+    say("full-size case", p["name"], "quasi-ELK lambda", lam)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, dl = dp.solve_elk(lam)
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK and it == p["max_iters"]
+    rng = np.random.default_rng(300 + cfg)
+    n = p["n"]
+    ch = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 10, replace=False)]))
+    rows = np.concatenate([g * n + ch for g in range(3)])
+    qs = dict(p, n=len(ch), W_x=p["W_x"][rows], b_x=p["b_x"][rows], W_h=p["W_h"][rows], b_h=p["b_h"][rows])
+    if p["cell"] == sy.CELL_LSTM_CIFG_DIAG:
+        sidx = np.stack([2 * ch, 2 * ch + 1], 1).reshape(-1)
+        qs["peep"] = np.concatenate([p["peep"][ch], p["peep"][n + ch]])
+    else:
+        sidx = ch
+    qs["S"] = len(sidx)
+    qs["h0"] = p["h0"][:, sidx]
+    hq, *_ = oracle.elk(qs, lam, tol=p["tol"], max_iters=p["max_iters"])
+    hg = to64(dp.h[:, :, torch.as_tensor(sidx, device="cuda")])
+    r = float(np.abs(hg - hq).max() / max(np.abs(hq).max(), 1e-30))
+    say("  sampled channels", ch, "rel err", r)
+    assert r <= RTOL_BF
 
 
 def test_damping_keeps_steps_bounded():
