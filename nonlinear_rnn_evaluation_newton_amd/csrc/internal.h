@@ -187,8 +187,8 @@ hipError_t launch_lsim(LsimArgs &a, hipStream_t s);
 struct ElkArgs {
   float *jr;  // [rows][2S]: the Jacobian's diagonal d | residual r (producer output)
   float *ge;  // [rows][2S]: smoother gains G | offsets e
-  float *r1, *pc, *r2, *mc, *r3, *msc;  // per chunk: Riccati maps [4][S], entering P [S],
-                                        // mean maps [2][S], entering m [S], reverse maps [2][S], m^s from the right [S]
+  float *r1, *pc, *mc, *r3, *msc;  // per chunk: filter maps [7][S], entering P [S] and m [S],
+                                   // reverse maps [2][S], m^s from the right [S]
   void *h;    // [rows][S] iterate (storage dtype)
   int h_bf16;
   int B, T, S, cps, nch;

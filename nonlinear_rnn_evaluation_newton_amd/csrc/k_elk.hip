@@ -7,21 +7,23 @@
 //   dh_t = d_t dh_{t-1} + r_t + w_t,  w_t ~ N(0, 1),   0 = dh_t + v_t,
 //   v_t ~ N(0, 1 / lambda),   dh_{-1} = 0,
 // whose posterior mean is the damped step argmin ||L dh - r||^2 + lambda ||dh||^2.
-// A sweep, after a producer has stored d_t and r_t at the current iterate
-// ([row][d (S) | r (S)], fp32), runs three parallel scans over time, each in
-// chunks of ELK_L steps (one wavefront per (sequence, chunk, 64 entries), lane
-// = state entry), with a per-(sequence, entry) scan over the chunk aggregates:
-//  1. the filter variance: P_t = (1 - K_t) P^-_t with P^-_t = d_t^2 P_{t-1} + 1
-//     and K_t = lambda P^-_t / (lambda P^-_t + 1) is a linear-fractional map of
-//     P_{t-1}, i.e. a 2x2 matrix on (P, 1) (composed with rescaling, since only
-//     ratios matter): k_elk_riccati + k_elk_riccati_carry;
-//  2. the filter mean m_t = (1 - K_t)(d_t m_{t-1} + r_t), an affine scan:
-//     k_elk_mean + k_elk_mean_carry;
-//  3. the Rauch-Tung-Striebel smoother m^s_t = G_t m^s_{t+1} + e_t with
-//     G_t = P_t d_{t+1} / P^-_{t+1}, e_t = m_t - G_t (d_{t+1} m_t + r_{t+1}), a
-//     reverse affine scan: k_elk_gains (stores G, e and each chunk's reverse
-//     aggregate) + k_elk_smooth_carry, then k_elk_apply walks each chunk back
-//     from its carry, h += m^s, and measures max |m^s|.
+// The filter, P_t = (1 - K_t) P^-_t and m_t = (1 - K_t)(d_t m_{t-1} + r_t) with
+// P^-_t = d_t^2 P_{t-1} + 1 and K_t = lambda P^-_t / (lambda P^-_t + 1), is
+// one linear scan in homogeneous coordinates (H7 below); the
+// Rauch-Tung-Striebel smoother m^s_t = G_t m^s_{t+1} + e_t with
+// G_t = P_t d_{t+1} / P^-_{t+1} and e_t = m_t - G_t (d_{t+1} m_t + r_{t+1}) is a
+// reverse affine scan.
+//
+// Dense n = 64 GRU: the gates kernel has stored d_t and r_t at the current
+// iterate ([row][d (S) | r (S)], fp32); chunks of ELK_L steps, one wavefront
+// per (sequence, chunk, 64 entries), lane = state entry:
+//   k_elk_filter + k_elk_filter_carry   chunk filter maps, moments entering
+//                                       each chunk (shuffle scan over chunks);
+//   k_elk_gains + k_elk_smooth_carry    G, e per step and each chunk's
+//                                       reverse map, m^s entering from the right;
+//   k_elk_apply                         each chunk walked back from its carry,
+//                                       h += m^s, max |m^s|.
+// Per-channel cells: further below.
 // lambda = 0 gives K = 0 and the quasi-DEER step.
 #include <algorithm>
 
@@ -51,25 +53,69 @@ __device__ inline ElkGeom elk_geom(const ElkArgs &a) {
   return g;
 }
 
-// 1. Riccati: each chunk's 2x2 map on (P, 1), [chunk][4][S]
-__global__ __launch_bounds__(256) void k_elk_riccati(const ElkArgs a) {
+// Homogeneous filter map [[a, 0, b], [c, e, f], [g, 0, h]] on (p, mu, q) with
+// P = p / q and m = mu / q; one step is
+//   p' = d^2 p + q,  mu' = d mu + r q,  q' = lambda d^2 p + (lambda + 1) q.
+struct H7 {
+  float a, b, c, e, f, g, h;
+};
+__device__ inline void h7_scale(H7 &m) {
+  const float s = frcp(fmaxf(fmaxf(m.a, m.b), fmaxf(m.g, m.h)));  // any positive factor works
+  m.a *= s; m.b *= s; m.c *= s; m.e *= s; m.f *= s; m.g *= s; m.h *= s;
+}
+__device__ inline H7 h7_id() { return H7{1.f, 0.f, 0.f, 1.f, 0.f, 0.f, 1.f}; }
+// X applied after Y
+__device__ inline H7 h7_after(const H7 &X, const H7 &Y) {
+  H7 o;
+  o.a = fmaf(X.a, Y.a, X.b * Y.g);
+  o.b = fmaf(X.a, Y.b, X.b * Y.h);
+  o.g = fmaf(X.g, Y.a, X.h * Y.g);
+  o.h = fmaf(X.g, Y.b, X.h * Y.h);
+  o.e = X.e * Y.e;
+  o.c = fmaf(X.c, Y.a, fmaf(X.e, Y.c, X.f * Y.g));
+  o.f = fmaf(X.c, Y.b, fmaf(X.e, Y.f, X.f * Y.h));
+  h7_scale(o);
+  return o;
+}
+__device__ inline H7 h7_shfl_up(const H7 &M, int off) {
+  return H7{__shfl_up(M.a, off, 64), __shfl_up(M.b, off, 64), __shfl_up(M.c, off, 64), __shfl_up(M.e, off, 64),
+            __shfl_up(M.f, off, 64), __shfl_up(M.g, off, 64), __shfl_up(M.h, off, 64)};
+}
+__device__ inline H7 h7_shfl(const H7 &M, int lane) {
+  return H7{__shfl(M.a, lane, 64), __shfl(M.b, lane, 64), __shfl(M.c, lane, 64), __shfl(M.e, lane, 64),
+            __shfl(M.f, lane, 64), __shfl(M.g, lane, 64), __shfl(M.h, lane, 64)};
+}
+// one step (d, r) applied after m
+__device__ inline void h7_step(H7 &m, float d, float r, float lam, float lam1) {
+  const float d2 = d * d, ld2 = lam * d2;
+  H7 o;
+  o.a = fmaf(d2, m.a, m.g);
+  o.b = fmaf(d2, m.b, m.h);
+  o.c = fmaf(d, m.c, r * m.g);
+  o.e = d * m.e;
+  o.f = fmaf(d, m.f, r * m.h);
+  o.g = fmaf(ld2, m.a, lam1 * m.g);
+  o.h = fmaf(ld2, m.b, lam1 * m.h);
+  h7_scale(o);
+  m = o;
+}
+
+// 1. filter: each chunk's homogeneous filter map (seven numbers, as for the
+// per-channel cells below), [chunk][7][S]
+__global__ __launch_bounds__(256) void k_elk_filter(const ElkArgs a) {
   __shared__ int s_stop;
   if (sweep_is_stopped(a.st, &s_stop)) return;
   const ElkGeom g = elk_geom(a);
   if (!g.active) return;
   const int S = a.S;
-  const float lam = a.lam;
-  float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
+  const float lam = a.lam, lam1 = lam + 1.f;
+  H7 m = h7_id();
   for (int t = g.t0; t < g.t1; t++) {
-    const float d = a.jr[((size_t)g.b * a.T + t) * 2 * S + g.i], d2 = d * d;
-    // [[d^2, 1], [lambda d^2, lambda + 1]] applied after the maps so far
-    const float n00 = d2 * m00 + m10, n01 = d2 * m01 + m11;
-    const float n10 = lam * d2 * m00 + (lam + 1.f) * m10, n11 = lam * d2 * m01 + (lam + 1.f) * m11;
-    const float sc = frcp(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));  // entries are >= 0, n11 >= 1 before scaling
-    m00 = n00 * sc; m01 = n01 * sc; m10 = n10 * sc; m11 = n11 * sc;
+    const float *row = a.jr + ((size_t)g.b * a.T + t) * 2 * S;
+    h7_step(m, row[g.i], row[S + g.i], lam, lam1);
   }
-  float *o = a.r1 + ((size_t)g.b * a.cps + g.j) * 4 * S + g.i;
-  o[0] = m00; o[S] = m01; o[2 * S] = m10; o[3 * S] = m11;
+  float *o = a.r1 + ((size_t)g.b * a.cps + g.j) * 7 * S + g.i;
+  o[0] = m.a; o[S] = m.b; o[2 * S] = m.c; o[3 * S] = m.e; o[4 * S] = m.f; o[5 * S] = m.g; o[6 * S] = m.h;
 }
 
 // One wavefront per (sequence, entry); lanes take 64 chunks at a time.
@@ -80,67 +126,39 @@ __device__ inline bool elk_carry_geom(const ElkArgs &a, int &b, int &i) {
   return w < a.B * a.S;
 }
 
-// P entering each chunk, [chunk][S]
-__global__ __launch_bounds__(256) void k_elk_riccati_carry(const ElkArgs a) {
+// filtered moments (P, m) entering each chunk, [chunk][S] each: the chunk
+// maps composed by a shuffle scan, 64 chunks at a time
+__global__ __launch_bounds__(256) void k_elk_filter_carry(const ElkArgs a) {
   __shared__ int s_stop;
   if (sweep_is_stopped(a.st, &s_stop)) return;
   int b, i;
   if (!elk_carry_geom(a, b, i)) return;
   const int lane = threadIdx.x & 63, S = a.S, cps = a.cps;
-  // running map applied to (0, 1): the state entering the current group
-  float c0 = 0.f, c1 = 1.f;
+  float cp = 0.f, cm = 0.f;  // running (P, m); dh_{-1} = 0 is known exactly
   for (int g0 = 0; g0 < cps; g0 += 64) {
     const int jj = g0 + lane;
-    const float *r = a.r1 + ((size_t)b * cps + min(jj, cps - 1)) * 4 * S + i;
-    float m00 = r[0], m01 = r[S], m10 = r[2 * S], m11 = r[3 * S];
-    if (jj >= cps) { m00 = 1.f; m01 = 0.f; m10 = 0.f; m11 = 1.f; }
-    // inclusive scan: later maps applied after earlier ones
+    H7 M = h7_id();
+    if (jj < cps) {
+      const float *r = a.r1 + ((size_t)b * cps + jj) * 7 * S + i;
+      M = H7{r[0], r[S], r[2 * S], r[3 * S], r[4 * S], r[5 * S], r[6 * S]};
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const float e00 = __shfl_up(m00, off, 64), e01 = __shfl_up(m01, off, 64);
-      const float e10 = __shfl_up(m10, off, 64), e11 = __shfl_up(m11, off, 64);
-      if (lane >= off) {
-        const float n00 = m00 * e00 + m01 * e10, n01 = m00 * e01 + m01 * e11;
-        const float n10 = m10 * e00 + m11 * e10, n11 = m10 * e01 + m11 * e11;
-        const float sc = frcp(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
-        m00 = n00 * sc; m01 = n01 * sc; m10 = n10 * sc; m11 = n11 * sc;
-      }
+      const H7 E = h7_shfl_up(M, off);
+      if (lane >= off) M = h7_after(M, E);
     }
-    // exclusive prefix applied to the running (c0, c1)
-    const float p00 = __shfl_up(m00, 1, 64), p01 = __shfl_up(m01, 1, 64);
-    const float p10 = __shfl_up(m10, 1, 64), p11 = __shfl_up(m11, 1, 64);
-    const float u0 = lane == 0 ? c0 : p00 * c0 + p01 * c1, u1 = lane == 0 ? c1 : p10 * c0 + p11 * c1;
-    if (jj < cps) a.pc[((size_t)b * cps + jj) * S + i] = u0 / u1;
-    const float l00 = __shfl(m00, 63, 64), l01 = __shfl(m01, 63, 64), l10 = __shfl(m10, 63, 64),
-                l11 = __shfl(m11, 63, 64);
-    const float n0 = l00 * c0 + l01 * c1, n1 = l10 * c0 + l11 * c1;
-    const float sc = frcp(fmaxf(n0, n1));
-    c0 = n0 * sc;
-    c1 = n1 * sc;
+    H7 E = h7_shfl_up(M, 1);
+    if (lane == 0) E = h7_id();
+    if (jj < cps) {
+      const float p = fmaf(E.a, cp, E.b), mu = fmaf(E.c, cp, fmaf(E.e, cm, E.f)), q = fmaf(E.g, cp, E.h);
+      a.pc[((size_t)b * cps + jj) * S + i] = p / q;
+      a.mc[((size_t)b * cps + jj) * S + i] = mu / q;
+    }
+    const H7 L = h7_shfl(M, 63);
+    const float p = fmaf(L.a, cp, L.b), mu = fmaf(L.c, cp, fmaf(L.e, cm, L.f)), q = fmaf(L.g, cp, L.h);
+    cp = p / q;
+    cm = mu / q;
   }
-}
-
-// 2. filter mean: each chunk's affine map m -> A m + B, [chunk][2][S]
-__global__ __launch_bounds__(256) void k_elk_mean(const ElkArgs a) {
-  __shared__ int s_stop;
-  if (sweep_is_stopped(a.st, &s_stop)) return;
-  const ElkGeom g = elk_geom(a);
-  if (!g.active) return;
-  const int S = a.S;
-  const float lam = a.lam;
-  float P = a.pc[((size_t)g.b * a.cps + g.j) * S + g.i], A = 1.f, Bv = 0.f;
-  for (int t = g.t0; t < g.t1; t++) {
-    const float *row = a.jr + ((size_t)g.b * a.T + t) * 2 * S;
-    const float d = row[g.i], r = row[S + g.i];
-    const float pp = fmaf(d * d, P, 1.f), k1 = frcp(fmaf(lam, pp, 1.f));
-    const float ca = k1 * d;
-    Bv = fmaf(ca, Bv, k1 * r);
-    A *= ca;
-    P = k1 * pp;
-  }
-  float *o = a.r2 + ((size_t)g.b * a.cps + g.j) * 2 * S + g.i;
-  o[0] = A;
-  o[S] = Bv;
 }
 
 // affine scan over chunks (forward: state entering each chunk from 0;
@@ -168,13 +186,6 @@ __device__ inline void elk_affine_carry(const ElkArgs &a, const float *agg, floa
   }
 }
 
-__global__ __launch_bounds__(256) void k_elk_mean_carry(const ElkArgs a) {
-  __shared__ int s_stop;
-  if (sweep_is_stopped(a.st, &s_stop)) return;
-  int b, i;
-  if (!elk_carry_geom(a, b, i)) return;
-  elk_affine_carry<false>(a, a.r2, a.mc, b, i);
-}
 
 // 3. smoother gains: G_t, e_t stored [row][G (S) | e (S)], and each chunk's
 // reverse map m^s_{t0} = A m^s_{t1} + B, [chunk][2][S]
@@ -288,14 +299,7 @@ __global__ __launch_bounds__(256) void k_elk_apply(const ElkArgs a) {
 // One wavefront per (sequence, chunk, 64 channels); a lane owns one channel
 // and its SW state entries.
 // ---------------------------------------------------------------------------
-struct H7 {
-  float a, b, c, e, f, g, h;
-};
-__device__ inline void h7_scale(H7 &m) {
-  const float s = frcp(fmaxf(fmaxf(m.a, m.b), fmaxf(m.g, m.h)));  // any positive factor works
-  m.a *= s; m.b *= s; m.c *= s; m.e *= s; m.f *= s; m.g *= s; m.h *= s;
-}
-__device__ inline H7 h7_id() { return H7{1.f, 0.f, 0.f, 1.f, 0.f, 0.f, 1.f}; }
+
 
 template <int CELL>
 constexpr int elkc_sw() {
@@ -470,19 +474,7 @@ __global__ __launch_bounds__(256) void k_elkc_filter(const ElkChanArgs a) {
   for (int q = 0; q < SW; q++) m[q] = h7_id();
   elkc_walk<CELL, ST, LF>(a, g, w, first, s, [&](int, const float *d, const float *r) {
 #pragma unroll
-    for (int q = 0; q < SW; q++) {
-      const float d2 = d[q] * d[q], ld2 = lam * d2;
-      H7 o;
-      o.a = fmaf(d2, m[q].a, m[q].g);
-      o.b = fmaf(d2, m[q].b, m[q].h);
-      o.c = fmaf(d[q], m[q].c, r[q] * m[q].g);
-      o.e = d[q] * m[q].e;
-      o.f = fmaf(d[q], m[q].f, r[q] * m[q].h);
-      o.g = fmaf(ld2, m[q].a, lam1 * m[q].g);
-      o.h = fmaf(ld2, m[q].b, lam1 * m[q].h);
-      h7_scale(o);
-      m[q] = o;
-    }
+    for (int q = 0; q < SW; q++) h7_step(m[q], d[q], r[q], lam, lam1);
   });
   if (!g.on) return;
   const int S = a.e.S;
@@ -838,10 +830,8 @@ hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s) {
   const int CG = (a.S + 63) / 64;
   const unsigned gchunks = (unsigned)(((size_t)a.nch * CG + 3) / 4);
   const unsigned gcarry = (unsigned)(((size_t)a.B * a.S + 3) / 4);
-  hipLaunchKernelGGL(k_elk_riccati, dim3(gchunks), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_elk_riccati_carry, dim3(gcarry), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_elk_mean, dim3(gchunks), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_elk_mean_carry, dim3(gcarry), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_elk_filter, dim3(gchunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_elk_filter_carry, dim3(gcarry), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_elk_gains, dim3(gchunks), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_elk_smooth_carry, dim3(gcarry), dim3(256), 0, s, a);
   if (a.h_bf16) hipLaunchKernelGGL(k_elk_apply<uint16_t>, dim3(gchunks), dim3(256), 0, s, a);

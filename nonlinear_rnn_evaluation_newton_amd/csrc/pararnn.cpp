@@ -364,7 +364,7 @@ size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
 // per step ([d | r] sits in the gates buffer), chunk aggregates and carries.
 // Per-channel cells: chunk aggregates, carries and boundary values only.
 struct ElkLayout {
-  size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_r2 = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
+  size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
   size_t off_fagg = 0, off_fcar = 0, off_fsub = 0, off_dr = 0, off_hb = 0;
   size_t bytes = 0;
   int cps = 0, nch = 0, cpf = 0, nchf = 0;
@@ -383,9 +383,8 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   if (pl.path == PATH_D64) {
     el->off_jr = pl.off_gates;  // [row][320] floats hold [d (64) | r (64)]
     el->off_ge = o; o = align256(o + rows * 2 * S * 4);
-    el->off_r1 = o; o = align256(o + nch * 4 * S * 4);
+    el->off_r1 = o; o = align256(o + nch * 7 * S * 4);
     el->off_pc = o; o = align256(o + nch * S * 4);
-    el->off_r2 = o; o = align256(o + nch * 2 * S * 4);
     el->off_mc = o; o = align256(o + nch * S * 4);
   } else {
     el->cpf = (p->T + 4 * L - 1) / (4 * L);  // filter chunks of 4 apply chunks
@@ -516,7 +515,6 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       ea.ge = (float *)(ws + el.off_ge);
       ea.r1 = (float *)(ws + el.off_r1);
       ea.pc = (float *)(ws + el.off_pc);
-      ea.r2 = (float *)(ws + el.off_r2);
       ea.mc = (float *)(ws + el.off_mc);
     }
     ea.r3 = (float *)(ws + el.off_r3);

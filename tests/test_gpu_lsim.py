@@ -52,6 +52,8 @@ def test_lsim_against_oracle(nx, m, p, T):
     yo, xo = oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"], x0=q["x0"])
     ex, ey = err(x, xo), err(y, yo)
     say("  err x", ex, "y", ey)
+    if not (ex <= TOL and ey <= TOL):
+        say("  non-finite x at", np.argwhere(~np.isfinite(x))[:8].tolist(), "y at", np.argwhere(~np.isfinite(y))[:8].tolist())
     assert ex <= TOL and ey <= TOL
 
 
