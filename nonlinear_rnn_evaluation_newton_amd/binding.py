@@ -210,6 +210,10 @@ def lsim_workspace_bytes(B: int, T: int, nx: int, m: int, p: int) -> int:
 def lsim(A, Bm, Cm, Dm, dt: float, U, x0, x, y, workspace, check: bool = True) -> int:
     """pararnn_lsim on fp32 device tensors: U [B,T,m], x0 [B,nx] or None,
     outputs x [B,T,nx] (or None) and y [B,T,p]."""
+    import torch
+    for name, t in (("A", A), ("B", Bm), ("C", Cm), ("D", Dm), ("U", U), ("x0", x0), ("x", x), ("y", y)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"lsim: {name} must be a contiguous float32 tensor, got {t.dtype}")
     B, T, m = U.shape[0], U.shape[1], U.shape[2]
     nx, p = A.shape[0], Cm.shape[0]
     st = lib().pararnn_lsim(B, T, nx, m, p, _p(A), _p(Bm), _p(Cm), _p(Dm), float(dt), _p(U), _p(x0), _p(x), _p(y),

@@ -32,8 +32,8 @@ def dev(a):
 def run(q, want_x=True):
     B, T, nx, m, p = q["B"], q["T"], q["nx"], q["m"], q["p"]
     ws = torch.empty(bd.lsim_workspace_bytes(B, T, nx, m, p), dtype=torch.uint8, device="cuda")
-    x = torch.full((B, T, nx), float("nan"), device="cuda") if want_x else None
-    y = torch.full((B, T, p), float("nan"), device="cuda")
+    x = torch.full((B, T, nx), float("nan"), dtype=torch.float32, device="cuda") if want_x else None
+    y = torch.full((B, T, p), float("nan"), dtype=torch.float32, device="cuda")
     bd.lsim(dev(q["A"]), dev(q["Bm"]), dev(q["Cm"]), dev(q["Dm"]), q["dt"], dev(q["U"]), dev(q["x0"]), x, y, ws)
     torch.cuda.synchronize()
     return (None if x is None else x.double().cpu().numpy()), y.double().cpu().numpy()

@@ -41,7 +41,16 @@ import oracle
 from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _fp64_default_dtype():
+    """torch.nn references here are built in fp64; the default dtype is
+    restored after each test so other test modules see torch's default."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 # ---------------------------------------------------------------------------
