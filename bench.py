@@ -269,11 +269,17 @@ def main() -> int:
         return dp.solve_elk(args.elk) if elk else dp.solve()
 
     def step():
-        st, it, dl = solve()
-        if st < 0 or st == bd.PR_NONFINITE:
-            raise RuntimeError(f"solve failed: {st}")
+        if elk:
+            st, it, dl = solve()
+            if st < 0 or st == bd.PR_NONFINITE:
+                raise RuntimeError(f"solve failed: {st}")
+            bd.adjoint(dp.prob, dp.w, dp.x, dp.h0, dp.h, dp.g, dp.ws, lam, dx, dh0, grads)
+        else:  # the solve and its adjoint in one call
+            st, it, dl = bd.solve_adjoint(dp.prob, dp.w, dp.x, dp.h0, p["tol"], p["max_iters"], dp.h, dp.g, dp.ws,
+                                          lam, dx, dh0, grads)
+            if st < 0 or st == bd.PR_NONFINITE:
+                raise RuntimeError(f"solve failed: {st}")
         iters_seen.append(it)
-        bd.adjoint(dp.prob, dp.w, dp.x, dp.h0, dp.h, dp.g, dp.ws, lam, dx, dh0, grads)
         return it, dl
 
     for _ in range(args.warmup):

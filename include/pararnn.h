@@ -179,6 +179,29 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
                     void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * pararnn_solve followed by pararnn_adjoint at the returned trajectory, in
+ * one call (a training step's forward and backward evaluation; DEER summary,
+ * Surprising findings: the gradient costs one more linear solve).  Results
+ * are those of the two calls.  The adjoint is enqueued right behind the
+ * solve's first batch of sweeps, before the host waits for its convergence
+ * poll, when that batch is sure to be the last (tol <= 0: a fixed number of
+ * sweeps) or, for n = d = 1, when the previous call on the same problem,
+ * tol and max_iters converged within it; if the solve then needs more
+ * sweeps, its state is restored and the adjoint runs again at the end.
+ * Otherwise the adjoint follows the solve's last poll.  Arguments as the two
+ * calls (h is the solve's output and the adjoint's trajectory); the
+ * workspace must be at least pararnn_workspace_bytes(p, 1).  Returns the
+ * solve's error, else the adjoint's error, else the solve's status (PR_OK,
+ * PR_NOT_CONVERGED or PR_NONFINITE; with PR_NONFINITE the adjoint's outputs
+ * are unspecified).  The adjoint's outputs are complete once the stream
+ * reaches this point.
+ */
+int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
  * The linear recurrence alone (the Newton inner solve), fp32, per sequence:
  *   reverse = 0:  y_t = A_t y_{t-1} + b_t,  y_{-1} = 0
  *   reverse = 1:  y_t = A_t y_{t+1} + b_t,  y_T = 0

@@ -21,8 +21,8 @@ PR_NOT_CONVERGED, PR_NONFINITE = 1, 2
 PR_F32, PR_BF16 = 0, 1
 PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3
 
-EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_scan_workspace_bytes",
-           "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
+EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_solve_adjoint",
+           "pararnn_scan_workspace_bytes", "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
            "pararnn_trace_kernel", "pararnn_lsim_workspace_bytes", "pararnn_lsim", "pararnn_elk_workspace_bytes",
            "pararnn_solve_elk"]
 
@@ -65,6 +65,8 @@ def lib():
         L.pararnn_solve.restype = I
         L.pararnn_adjoint.argtypes = [P, P, P, P, P, P, P, P, P, P, P, S, P]
         L.pararnn_adjoint.restype = I
+        L.pararnn_solve_adjoint.argtypes = [P, P, P, P, F, I, P, P, P, I, P, P, P, P, P, P, S, P]
+        L.pararnn_solve_adjoint.restype = I
         L.pararnn_scan_workspace_bytes.argtypes = [I, I, I, I]
         L.pararnn_scan_workspace_bytes.restype = S
         L.pararnn_affine_scan.argtypes = [I, I, I, I, I, P, P, P, P, S, P]
@@ -161,6 +163,23 @@ def adjoint(prob: Problem, w: Weights, x, h0, h, g, workspace, lam=None, dx=None
     if check and st < 0:
         raise PararnnError(st, "pararnn_adjoint")
     return st
+
+
+def solve_adjoint(prob: Problem, w: Weights, x, h0, tol: float, max_iters: int, h, g, workspace, lam=None, dx=None,
+                  dh0=None, grads: dict | None = None, hist_cap: int = 64, check: bool = True):
+    """Runs pararnn_solve_adjoint; returns (status, iters, delta history)."""
+    it = C.c_int(0)
+    hist = np.zeros(max(hist_cap, 1), dtype=np.float32)
+    gr = None
+    if grads is not None:
+        gr = Grads(*[_p(grads.get(k)) for k in ("W_x", "b_x", "W_h", "b_h", "peep")])
+    st = lib().pararnn_solve_adjoint(C.byref(prob), C.byref(w), _p(x), _p(h0), float(tol), int(max_iters), _p(h),
+                                     C.byref(it), hist.ctypes.data_as(C.c_void_p), int(hist_cap), _p(g), _p(lam),
+                                     _p(dx), _p(dh0), C.byref(gr) if gr is not None else None, _p(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream())
+    if check and st < 0:
+        raise PararnnError(st, "pararnn_solve_adjoint")
+    return st, it.value, hist[:min(it.value, hist_cap)].copy()
 
 
 def trace(enable: bool) -> None:

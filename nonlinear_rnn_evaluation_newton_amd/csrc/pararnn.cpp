@@ -401,9 +401,46 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   return PR_OK;
 }
 
+// An adjoint that pararnn_solve_adjoint lets the solve enqueue right after
+// its first batch of sweeps, before the convergence poll waits: when that
+// batch turns out to be the last, the device runs the adjoint with no gap.
+struct SpecAdjoint {
+  const void *g;
+  void *lambda, *dx, *dh0;
+  const pr_grads *dW;
+  bool done = false;  // out: the adjoint ran at the returned trajectory
+  int rc = PR_OK;     // out: its status when done
+};
+// Whether the last combined call on a problem converged within its first
+// batch (then the next one speculates on the scalar-state path).
+struct SpecMemo {
+  pr_problem p{};
+  float tol = 0.f;
+  int max_iters = 0;
+  bool valid = false, first_batch = false;
+  bool same(const pr_problem *q, float t, int m) const {
+    return valid && p.cell == q->cell && p.jac == q->jac && p.dtype == q->dtype && p.B == q->B && p.T == q->T &&
+           p.d == q->d && p.n == q->n && tol == t && max_iters == m;
+  }
+};
+// Event marking a convergence poll's state snapshot (null if it cannot be made).
+static hipEvent_t poll_event() {
+  thread_local hipEvent_t ev = nullptr;
+  thread_local bool tried = false;
+  if (!tried) {
+    tried = true;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
+  }
+  return ev;
+}
+static SpecMemo &spec_memo() {
+  thread_local SpecMemo m;
+  return m;
+}
+
 static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
                       int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
-                      size_t ws_bytes, void *stream, const float *elk_lambda) {
+                      size_t ws_bytes, void *stream, const float *elk_lambda, SpecAdjoint *spec = nullptr) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, &pl);
@@ -547,6 +584,14 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   int first, next;
   poll_schedule(&first, &next);
   if (tol <= 0.f) first = kmax;
+  // Speculate when the first batch is surely the last (a fixed sweep count),
+  // or on the scalar-state path (whose adjoint leaves nothing the later sweeps
+  // read besides the solve state, which is restored) when the last call on
+  // this problem converged within its first batch.
+  const bool speculate = spec && !elk_lambda &&
+                         (first >= kmax || (scalar && al16(spec->g) && al16(spec->lambda) && al16(spec->dx) &&
+                                            spec_memo().same(p, tol, max_iters) && spec_memo().first_batch));
+  bool spec_enqueued = false;
   int k = 1, out_iters = 0, out_status = PR_OK;
   // Sweep timing: the dense n = 64 path brackets every sweep (its parts are
   // timed too); the others bracket each batch of back-to-back sweeps, so the
@@ -601,7 +646,16 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     }
     if (bev) HIPCHK(hipEventRecord(tr.sw[2 * (k_last - 1) + 1], s));
     HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
+    // the poll waits for the snapshot only: a speculative adjoint enqueued
+    // behind it keeps the device busy while the host decides
+    hipEvent_t poll_ev = poll_event();
+    if (poll_ev) HIPCHK(hipEventRecord(poll_ev, s));
+    if (speculate && k == 1) {
+      spec->rc = pararnn_adjoint(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
+                                 ws_bytes, stream);
+      spec_enqueued = spec->rc >= 0;
+    }
+    HIPCHK(poll_ev ? hipEventSynchronize(poll_ev) : hipStreamSynchronize(s));
     if (hs->fault) return fail(PR_EHIP, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
     if (hs->stopped) {
       out_iters = hs->iters;
@@ -618,7 +672,20 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       out_status = status;
       break;
     }
+    if (spec_enqueued) {  // the speculative adjoint reset the solve state: put the snapshot back
+      HIPCHK(hipMemcpyAsync(ws + pl.off_state, hs, sizeof(SolveState), hipMemcpyHostToDevice, s));
+      spec_enqueued = false;
+    }
     k = k_last + 1;
+  }
+  if (spec) {
+    spec->done = spec_enqueued;
+    SpecMemo &m = spec_memo();
+    m.p = *p;
+    m.tol = tol;
+    m.max_iters = max_iters;
+    m.valid = true;
+    m.first_batch = out_iters <= first;
   }
   if (tr.on && !per_sweep_events) {
     // a batch's launches past the stop exit at once; count the ones that worked
@@ -861,6 +928,28 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     return PR_OK;
   }
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
+}
+
+int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  if (p && workspace && ws_bytes < pararnn_workspace_bytes(p, 1))
+    return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, pararnn_workspace_bytes(p, 1));
+  SpecAdjoint sa;
+  sa.g = g;
+  sa.lambda = lambda;
+  sa.dx = dx;
+  sa.dh0 = dh0;
+  sa.dW = dW;
+  const int rc = solve_impl(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
+                            nullptr, &sa);
+  if (rc < 0) return rc;
+  if (sa.done) return sa.rc < 0 ? sa.rc : rc;
+  if (sa.rc < 0) return sa.rc;  // the speculative enqueue was rejected: the same arguments fail again
+  if (rc == PR_NONFINITE) return rc;
+  const int ra = pararnn_adjoint(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream);
+  return ra < 0 ? ra : rc;
 }
 
 static bool lsim_sizes_ok(int B, int T, int nx, int m, int p) {

@@ -138,3 +138,22 @@ def test_elk_arguments_rejected_without_device():
     assert call(pb=small) == bd.PR_EUNSUPPORTED
     assert call(n=1024) == bd.PR_EWORKSPACE
     assert call(x=None) == bd.PR_EINVAL
+
+
+def test_solve_adjoint_arguments_rejected_without_device():
+    L = bd.lib()
+    pb = _prob()
+    w = bd.Weights()
+    solve_ws = bd.workspace_bytes(pb, False)
+    full_ws = bd.workspace_bytes(pb, True)
+    assert full_ws >= solve_ws > 0
+
+    def call(p=pb, x=C.c_void_p(16), h=C.c_void_p(16), g=C.c_void_p(16), ws=C.c_void_p(256), n=full_ws):
+        return L.pararnn_solve_adjoint(C.byref(p), C.byref(w), x, None, 1e-6, 8, h, None, None, 0, g, None, None,
+                                       None, None, ws, n, None)
+
+    # the adjoint's workspace is required up front, before the solve runs
+    assert call(n=full_ws - 1) == bd.PR_EWORKSPACE
+    assert call(p=_prob(B=0)) == bd.PR_EINVAL
+    assert call(x=None) == bd.PR_EINVAL
+    assert bd.last_error() != ""
