@@ -25,9 +25,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 //  10    w_hz, 11 w_hn, 12 w_hr / (2 log2e)      -> Jacobian
 //  13..15 w_xr, w_xz, w_xn                       -> dx
 // tanh RNN / linear: 0 w_x, 1 w_h, 2 b_x + b_h.
-__global__ void k_scalar_coef(const float *Wx, const float *bx, const float *Wh, const float *bh, int cell,
-                              float *coef) {
-  if (threadIdx.x != 0) return;
+__device__ inline void scalar_coef_fill(const float *Wx, const float *bx, const float *Wh, const float *bh, int cell,
+                                        float *coef) {
   auto B = [&](const float *p, int i) { return p ? p[i] : 0.f; };
   for (int i = 0; i < SC_NC; i++) coef[i] = 0.f;
   if (cell == C_GRU) {
@@ -40,6 +39,21 @@ __global__ void k_scalar_coef(const float *Wx, const float *bx, const float *Wh,
   } else {
     coef[0] = Wx[0]; coef[1] = Wh[0]; coef[2] = B(bx, 0) + B(bh, 0);
   }
+}
+
+__global__ void k_scalar_coef(const float *Wx, const float *bx, const float *Wh, const float *bh, int cell,
+                              float *coef) {
+  if (threadIdx.x == 0) scalar_coef_fill(Wx, bx, Wh, bh, cell, coef);
+}
+
+// The call's workspace clearing and the coefficients in one launch (the
+// coefficients lie past the cleared bytes).
+__global__ void k_zero_coef(uint4 *p, size_t n16, unsigned char *tail, size_t ntail, const float *Wx,
+                            const float *bx, const float *Wh, const float *bh, int cell, float *coef) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) scalar_coef_fill(Wx, bx, Wh, bh, cell, coef);
 }
 
 // f and J of the scalar cell at state s, input x.
@@ -745,6 +759,17 @@ int scalar_adj_tile() { return AdjPol<C_GRU>::TILE; }
 
 hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s) {
   hipLaunchKernelGGL(k_scalar_coef, dim3(1), dim3(64), 0, s, a.Wx, a.bx, a.Wh, a.bh, cell, coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_coef(void *p, size_t bytes, const float *Wx, const float *bx, const float *Wh,
+                            const float *bh, int cell, float *coef, hipStream_t s) {
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(k_zero_coef, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)p, n16,
+                     (unsigned char *)p + n16 * 16, ntail, Wx, bx, Wh, bh, cell, coef);
   return hipGetLastError();
 }
 

@@ -468,7 +468,13 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
 
   Trace &tr = trace();
   if (tr.on) HIPCHK(tr.make());
-  HIPCHK(launch_zero(ws, pl.zero_bytes, s));
+  // n = d = 1 with vector-friendly sizes takes the scalar-state sweep
+  const bool scalar = pl.path == PATH_TIME && pl.scalar_ok && al16(h) && al16(x) && !getenv("PARARNN_NO_SCALAR");
+  if (scalar)
+    HIPCHK(launch_zero_coef(ws, pl.zero_bytes, (const float *)w->W_x, (const float *)w->b_x, (const float *)w->W_h,
+                            (const float *)w->b_h, kcell(p->cell), (float *)(ws + pl.off_coef), s));
+  else
+    HIPCHK(launch_zero(ws, pl.zero_bytes, s));
   const int kmax = max_iters < p->T ? max_iters : p->T;
 
   TimeArgs a{};
@@ -536,12 +542,9 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     tr.end(TR_PROJ, ti, s);
   }
   const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : kcell(p->cell);
-  // n = d = 1 with vector-friendly sizes takes the scalar-state sweep
-  const bool scalar = pl.path == PATH_TIME && pl.scalar_ok && a.vec_ok == 3 && !getenv("PARARNN_NO_SCALAR");
-  if (scalar) {
+  if (scalar) {  // its coefficients were computed with the clearing
     a.tiles_per_seq = pl.tps_s;
     a.ntiles = pl.ntiles_s;
-    HIPCHK(launch_scalar_coef(a, kc, (float *)(ws + pl.off_coef), s));
   }
 
   ElkArgs ea{};
@@ -757,7 +760,14 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
   if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
-  HIPCHK(launch_zero(ws, pl.zero_bytes, s));
+  // n = d = 1 with vector-friendly sizes takes the scalar-state adjoint
+  const bool scalar = pl.path == PATH_TIME && pl.scalar_ok && al16(h) && al16(x) && al16(g) && al16(lambda) &&
+                      al16(dx) && !getenv("PARARNN_NO_SCALAR");
+  if (scalar)
+    HIPCHK(launch_zero_coef(ws, pl.zero_bytes, (const float *)w->W_x, (const float *)w->b_x, (const float *)w->W_h,
+                            (const float *)w->b_h, kcell(p->cell), (float *)(ws + pl.off_coef), s));
+  else
+    HIPCHK(launch_zero(ws, pl.zero_bytes, s));
   if (pl.path == PATH_TIME) {
     TimeArgs a{};
     a.x = (const float *)x;
@@ -780,13 +790,10 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     a.tiles_per_seq = pl.tps;
     a.ntiles = pl.ntiles;
     a.vec_ok = (al16(h) ? 1 : 0) | (al16(x) ? 2 : 0) | (al16(g) ? 4 : 0) | (al16(lambda) ? 8 : 0);
-    // n = d = 1 with vector-friendly sizes takes the scalar-state adjoint
-    const bool scalar = pl.scalar_ok && a.vec_ok == 15 && al16(dx) && !getenv("PARARNN_NO_SCALAR");
-    if (scalar) {
+    if (scalar) {  // its coefficients were computed with the clearing
       a.coef = (const float *)(ws + pl.off_coef);
       a.tiles_per_seq = pl.tps_sa;
       a.ntiles = pl.ntiles_sa;
-      HIPCHK(launch_scalar_coef(a, kcell(p->cell), (float *)(ws + pl.off_coef), s));
     }
     Trace &tr = trace();
     const int ti = tr.begin(TR_ADJ, s);
