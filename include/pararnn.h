@@ -191,7 +191,8 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
  * Otherwise the adjoint follows the solve's last poll.  Arguments as the two
  * calls (h is the solve's output and the adjoint's trajectory); the
  * workspace must be at least pararnn_workspace_bytes(p, 1).  Returns the
- * solve's error, else the adjoint's error, else the solve's status (PR_OK,
+ * solve's error, else the adjoint's error (its arguments are checked when
+ * it is enqueued, after the solve has run), else the solve's status (PR_OK,
  * PR_NOT_CONVERGED or PR_NONFINITE; with PR_NONFINITE the adjoint's outputs
  * are unspecified).  The adjoint's outputs are complete once the stream
  * reaches this point.

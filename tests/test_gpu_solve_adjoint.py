@@ -128,3 +128,29 @@ def test_scalar_speculation_hit_and_miss(monkeypatch):
     same(ref_a, run_combined(da, tol, pb["max_iters"]))  # speculates and hits
     same(ref_b, run_combined(db, tol, pb["max_iters"]))  # speculates and misses
     same(ref_b, run_combined(db, tol, pb["max_iters"]))  # the record now says no: sequential
+
+
+@pytest.mark.parametrize("make", [lambda: sy.make_problem(2, B=2, T=1024),
+                                  lambda: sy.custom_problem(sy.CELL_GRU_DIAG, B=2, T=300, d=6, n=20, seed=2,
+                                                            w_scale=0.8, h0=True)],
+                         ids=["scalar GRU", "ParaGRU"])
+def test_not_converged_matches_separate_calls(make):
+    """max_iters below the sweeps needed: PR_NOT_CONVERGED from both, the
+    adjoint taken at the last iterate either way."""
+    p = make()
+    dp = bd.DeviceProblem(p)
+    ref = run_separate(dp, p["tol"], 2)
+    assert ref[0] == bd.PR_NOT_CONVERGED and ref[1] == 2
+    for _ in range(2):
+        same(ref, run_combined(dp, p["tol"], 2))
+
+
+def test_missing_adjoint_argument():
+    """g is required: the call reports PR_EINVAL (the solve has run)."""
+    p = sy.make_problem(2, B=2, T=1024)
+    dp = bd.DeviceProblem(p)
+    o = outputs(dp)
+    st, it, _ = bd.solve_adjoint(dp.prob, dp.w, dp.x, dp.h0, p["tol"], p["max_iters"], dp.h, None, dp.ws, o["lam"],
+                                 o["dx"], o["dh0"], grads_of(o), check=False)
+    torch.cuda.synchronize()
+    assert st == bd.PR_EINVAL and "g" in bd.last_error()
