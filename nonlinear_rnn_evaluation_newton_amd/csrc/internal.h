@@ -44,7 +44,6 @@ hipError_t launch_time_adjoint(int cell, int N, TimeArgs &a, hipStream_t s);
 // tile geometry as the generic sweep at N = 1.
 int scalar_tile();      // steps per tile of the scalar sweep
 int scalar_adj_tile();  // steps per tile of the scalar adjoint
-hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s);
 hipError_t launch_zero_coef(void *p, size_t bytes, const float *Wx, const float *bx, const float *Wh,
                             const float *bh, int cell, float *coef, hipStream_t s);
 hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s);

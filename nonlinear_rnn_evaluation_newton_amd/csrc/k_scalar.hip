@@ -41,11 +41,6 @@ __device__ inline void scalar_coef_fill(const float *Wx, const float *bx, const 
   }
 }
 
-__global__ void k_scalar_coef(const float *Wx, const float *bx, const float *Wh, const float *bh, int cell,
-                              float *coef) {
-  if (threadIdx.x == 0) scalar_coef_fill(Wx, bx, Wh, bh, cell, coef);
-}
-
 // The call's workspace clearing and the coefficients in one launch (the
 // coefficients lie past the cleared bytes).
 __global__ void k_zero_coef(uint4 *p, size_t n16, unsigned char *tail, size_t ntail, const float *Wx,
@@ -756,11 +751,6 @@ struct AdjPol : ScBase {
 
 int scalar_tile() { return SweepPol<C_GRU, false>::TILE; }
 int scalar_adj_tile() { return AdjPol<C_GRU>::TILE; }
-
-hipError_t launch_scalar_coef(const TimeArgs &a, int cell, float *coef, hipStream_t s) {
-  hipLaunchKernelGGL(k_scalar_coef, dim3(1), dim3(64), 0, s, a.Wx, a.bx, a.Wh, a.bh, cell, coef);
-  return hipGetLastError();
-}
 
 hipError_t launch_zero_coef(void *p, size_t bytes, const float *Wx, const float *bx, const float *Wh,
                             const float *bh, int cell, float *coef, hipStream_t s) {
