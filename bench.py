@@ -221,7 +221,7 @@ def main() -> int:
                     help="only run a plain device copy of MIB MiB (3 launches), to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported"}))
+        print(json.dumps({"error": "the library runs on one GPU per process; --gpus N > 1 is not supported"}))
         return 2
 
     import numpy as np

@@ -82,7 +82,7 @@ extern "C" {
 #define PR_EINVAL (-1)        /* bad enum, size <= 0, NULL required pointer, max_iters < 1 */
 #define PR_EWORKSPACE (-2)    /* workspace NULL or smaller than pararnn_*workspace_bytes   */
 #define PR_EHIP (-3)          /* a HIP runtime call failed                                */
-#define PR_EUNSUPPORTED (-5)  /* valid problem this build has no kernel for               */
+#define PR_EUNSUPPORTED (-5)  /* valid problem the library has no kernel for              */
 #define PR_NOT_CONVERGED 1    /* max_iters sweeps, delta never < tol; h = last iterate   */
 #define PR_NONFINITE 2        /* delta became NaN/Inf; h = that iterate                   */
 
