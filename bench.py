@@ -212,7 +212,7 @@ def main() -> int:
                     help="Jacobian of the sweeps' linear solve: the cell's own (Newton), its diagonal "
                          "(quasi-DEER) or zero (Jacobi)")
     ap.add_argument("--elk", type=float, default=None, metavar="LAMBDA",
-                    help="solve with quasi-ELK at damping LAMBDA (workloads 3, 4, 5)")
+                    help="solve with quasi-ELK at damping LAMBDA")
     ap.add_argument("--lsim", action="store_true",
                     help="time the linear state-space simulation workload (B=16, T=2^20, 4 states) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")

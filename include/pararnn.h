@@ -151,8 +151,9 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
  * state entry as the Kalman filter / Rauch-Tung-Striebel smoother mean of
  * dh_t = d_t dh_{t-1} + r_t + N(0, 1) observed as 0 with variance 1/lambda,
  * then h += dh.  lambda = 0 is quasi-DEER; larger lambda shortens the steps
- * (lambda ||dh||^2 <= ||r||^2).  p->jac is not used.  Kernels exist for the
- * dense GRU with n = 64 (fp32) and for GRU_DIAG and LSTM_CIFG_DIAG (fp32 or
+ * (lambda ||dh||^2 <= ||r||^2).  p->jac is not used.  Kernels exist for
+ * every problem pararnn_solve supports: the tanh RNN and GRU with n <= 8 and
+ * the dense GRU with n = 64 (fp32), GRU_DIAG and LSTM_CIFG_DIAG (fp32 or
  * bf16); other problems return PR_EUNSUPPORTED.  Arguments and results as
  * pararnn_solve, plus lambda (>= 0, finite); the workspace must hold
  * pararnn_elk_workspace_bytes (which also covers pararnn_adjoint).

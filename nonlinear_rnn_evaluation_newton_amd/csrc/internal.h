@@ -48,6 +48,7 @@ hipError_t launch_zero_coef(void *p, size_t bytes, const float *Wx, const float 
                             const float *bh, int cell, float *coef, hipStream_t s);
 hipError_t launch_scalar_sweep(int cell, const TimeArgs &a, hipStream_t s);
 hipError_t launch_scalar_adjoint(int cell, TimeArgs &a, hipStream_t s);  // sets a.nparts
+hipError_t launch_time_elk_jr(int cell, int N, const TimeArgs &a, float *jr, hipStream_t s);
 hipError_t launch_time_reduce(int cell, int N, const TimeArgs &a, const float *part, float *dWx, float *dbx,
                               float *dWh, float *dbh, hipStream_t s);
 

@@ -44,6 +44,15 @@ hipError_t launch_time_adjoint(int cell, int Nv, TimeArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_time_elk_jr(int cell, int Nv, const TimeArgs &a, float *jr, hipStream_t s) {
+  switch (cell) {
+    case C_TANH: return time_elk_jr_tanh(Nv, a, jr, s);
+    case C_GRU: return time_elk_jr_gru(Nv, a, jr, s);
+    case C_LINEAR: return time_elk_jr_linear(Nv, a, jr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_time_reduce(int cell, int Nv, const TimeArgs &a, const float *part, float *dWx, float *dbx,
                               float *dWh, float *dbh, hipStream_t s) {
   switch (cell) {

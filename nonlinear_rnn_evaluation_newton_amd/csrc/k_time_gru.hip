@@ -11,4 +11,8 @@ hipError_t time_reduce_gru(int Nv, const TimeArgs &a, const float *part, float *
   return time_reduce_cell<C_GRU>(Nv, a, part, dWx, dbx, dWh, dbh, s);
 }
 
+hipError_t time_elk_jr_gru(int Nv, const TimeArgs &a, float *jr, hipStream_t s) {
+  return time_elk_jr_cell<C_GRU>(Nv, a, jr, s);
+}
+
 }  // namespace pr

@@ -24,6 +24,8 @@
 // small boundary buffer.
 #pragma once
 
+#include <algorithm>
+
 #include "cells_dense.h"
 #include "internal.h"
 
@@ -747,6 +749,51 @@ __global__ __launch_bounds__(256) void k_time_scan(const ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Quasi-ELK producer for the small dense cells (Gonzalez et al. abstract:
+// quasi-ELK keeps the Jacobian's diagonal): at the current iterate, the
+// diagonal of J_t and the residual r_t = f_t - h_t of every step,
+// [row][d (n) | r (n)] fp32, one thread per step.  Opens the sweep.
+// ---------------------------------------------------------------------------
+template <int N, int CELL, int DX>
+__global__ __launch_bounds__(256) void k_time_elk_jr(const TimeArgs a, float *jr) {
+  constexpr int G = cell_gates(CELL);
+  __shared__ float sWh[G * N * N], sbh[G * N], sWx[G * N * DX], sbx[G * N];
+  __shared__ int s_stop;
+  if (sweep_open(a.st, a.k, a.tol, a.T, a.max_iters, &s_stop)) return;
+  stage_dense_weights<N, G, DX>(a, sWh, sbh, sWx, sbx);
+  __syncthreads();
+  const int n = a.n, d = a.d, T = a.T;
+  const size_t rows = (size_t)a.B * T;
+  const bool first = a.k == 1;  // the iterate is h = 0 before sweep 1
+  for (size_t row = (size_t)blockIdx.x * blockDim.x + threadIdx.x; row < rows; row += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(row % T), b = (int)(row / T);
+    float xt[DX], sp[N], hc[N], U[G * N], f[N], J[N * N];
+#pragma unroll
+    for (int c = 0; c < DX; c++) xt[c] = c < d ? a.x[row * d + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      float v = 0.f;
+      if (i < n) {
+        if (t > 0) v = first ? 0.f : a.h[(row - 1) * n + i];
+        else if (a.h0) v = a.h0[(size_t)b * n + i];
+      }
+      sp[i] = v;
+      hc[i] = (i < n && !first) ? a.h[row * n + i] : 0.f;
+    }
+    input_proj<N, G, DX>(sWx, sbx, xt, U);
+    dense_cell<N, CELL>(sp, U, sWh, sbh, f, J);
+    float *o = jr + row * 2 * n;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      if (i < n) {
+        o[i] = J[i * N + i];
+        o[n + i] = f[i] - hc[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
 static inline int dx_pad(int d) { return d <= 1 ? 1 : d <= 2 ? 2 : d <= 4 ? 4 : 8; }
@@ -811,5 +858,18 @@ hipError_t time_adjoint_linear(int Nv, TimeArgs &a, hipStream_t s);
 hipError_t time_reduce_tanh(int Nv, const TimeArgs &a, const float *, float *, float *, float *, float *, hipStream_t);
 hipError_t time_reduce_gru(int Nv, const TimeArgs &a, const float *, float *, float *, float *, float *, hipStream_t);
 hipError_t time_reduce_linear(int Nv, const TimeArgs &a, const float *, float *, float *, float *, float *, hipStream_t);
+hipError_t time_elk_jr_tanh(int Nv, const TimeArgs &a, float *jr, hipStream_t s);
+hipError_t time_elk_jr_gru(int Nv, const TimeArgs &a, float *jr, hipStream_t s);
+hipError_t time_elk_jr_linear(int Nv, const TimeArgs &a, float *jr, hipStream_t s);
+
+template <int CELL>
+hipError_t time_elk_jr_cell(int Nv, const TimeArgs &a, float *jr, hipStream_t s) {
+  const size_t rows = (size_t)a.B * a.T;
+  const unsigned grid = (unsigned)std::min<size_t>((rows + 255) / 256, 65536);
+  PR_DISPATCH_N(Nv, PR_DISPATCH_DX(a.d, {
+    hipLaunchKernelGGL((k_time_elk_jr<N, CELL, DX>), dim3(grid), dim3(256), 0, s, a, jr);
+  }));
+  return hipGetLastError();
+}
 
 }  // namespace pr

@@ -11,4 +11,8 @@ hipError_t time_reduce_linear(int Nv, const TimeArgs &a, const float *part, floa
   return time_reduce_cell<C_LINEAR>(Nv, a, part, dWx, dbx, dWh, dbh, s);
 }
 
+hipError_t time_elk_jr_linear(int Nv, const TimeArgs &a, float *jr, hipStream_t s) {
+  return time_elk_jr_cell<C_LINEAR>(Nv, a, jr, s);
+}
+
 }  // namespace pr

@@ -11,4 +11,8 @@ hipError_t time_reduce_tanh(int Nv, const TimeArgs &a, const float *part, float 
   return time_reduce_cell<C_TANH>(Nv, a, part, dWx, dbx, dWh, dbh, s);
 }
 
+hipError_t time_elk_jr_tanh(int Nv, const TimeArgs &a, float *jr, hipStream_t s) {
+  return time_elk_jr_cell<C_TANH>(Nv, a, jr, s);
+}
+
 }  // namespace pr

@@ -370,8 +370,8 @@ struct ElkLayout {
   int cps = 0, nch = 0, cpf = 0, nchf = 0;
 };
 static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
-  if (pl.path != PATH_D64 && pl.path != PATH_CHAN)
-    return fail(PR_EUNSUPPORTED, "quasi-ELK runs on the dense n = 64 GRU and the per-channel cells");
+  if (pl.path != PATH_D64 && pl.path != PATH_CHAN && pl.path != PATH_TIME)
+    return fail(PR_EUNSUPPORTED, "no quasi-ELK kernels for this problem");
   const size_t rows = (size_t)p->B * p->T, S = (size_t)pl.S;
   const int L = pl.path == PATH_D64 ? elk_chunk_len() : elk_chan_chunk_len(p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1);
   el->cps = (p->T + L - 1) / L;
@@ -380,8 +380,12 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   el->nch = el->cps * p->B;
   const size_t nch = (size_t)el->nch;
   size_t o = pl.solve_bytes;
-  if (pl.path == PATH_D64) {
-    el->off_jr = pl.off_gates;  // [row][320] floats hold [d (64) | r (64)]
+  if (pl.path == PATH_D64 || pl.path == PATH_TIME) {
+    if (pl.path == PATH_D64) {
+      el->off_jr = pl.off_gates;  // [row][320] floats hold [d (64) | r (64)]
+    } else {
+      el->off_jr = o; o = align256(o + rows * 2 * S * 4);
+    }
     el->off_ge = o; o = align256(o + rows * 2 * S * 4);
     el->off_r1 = o; o = align256(o + nch * 7 * S * 4);
     el->off_pc = o; o = align256(o + nch * S * 4);
@@ -550,7 +554,7 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   ElkArgs ea{};
   ElkChanArgs eca{};
   if (elk_lambda) {
-    if (pl.path == PATH_D64) {
+    if (pl.path == PATH_D64 || pl.path == PATH_TIME) {
       ea.jr = (float *)(ws + el.off_jr);
       ea.ge = (float *)(ws + el.off_ge);
       ea.r1 = (float *)(ws + el.off_r1);
@@ -620,6 +624,10 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
         if (pl.path == PATH_D64) {  // producer of [d | r], then the scans
           da.k = kk;
           HIPCHK(launch_d64_sweep_part(da, 0, s));
+          ea.k = kk;
+          HIPCHK(launch_elk_sweep(ea, s));
+        } else if (pl.path == PATH_TIME) {
+          HIPCHK(launch_time_elk_jr(kc, pl.N, a, ea.jr, s));
           ea.k = kk;
           HIPCHK(launch_elk_sweep(ea, s));
         } else {

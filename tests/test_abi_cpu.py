@@ -124,7 +124,9 @@ def test_elk_arguments_rejected_without_device():
     good = bd.Problem(sy.CELL_GRU_DIAG, sy.JAC_DIAG, bd.PR_F32, 2, 100, 3, 8)
     assert bd.elk_workspace_bytes(good) >= bd.workspace_bytes(good, True) > 0
     small = bd.Problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 4)
-    assert bd.elk_workspace_bytes(small) == 0  # no quasi-ELK kernels for the small dense cells
+    assert bd.elk_workspace_bytes(small) >= bd.workspace_bytes(small, True) > 0  # the small dense cells
+    wide = bd.Problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)  # no kernels for n = 16 at all
+    assert bd.workspace_bytes(wide, False) == 0 and bd.elk_workspace_bytes(wide) == 0
     w = bd.Weights(1, None, 1, None, None)
     v = C.c_void_p(16)
     ws = bd.elk_workspace_bytes(good)
@@ -135,7 +137,7 @@ def test_elk_arguments_rejected_without_device():
 
     assert call(lam=-1.0) == bd.PR_EINVAL and call(lam=float("nan")) == bd.PR_EINVAL
     assert call(lam=float("inf")) == bd.PR_EINVAL
-    assert call(pb=small) == bd.PR_EUNSUPPORTED
+    assert call(pb=wide) == bd.PR_EUNSUPPORTED
     assert call(n=1024) == bd.PR_EWORKSPACE
     assert call(x=None) == bd.PR_EINVAL
 

@@ -162,10 +162,42 @@ def test_damping_keeps_steps_bounded():
     assert np.max(dl) < 1.0
 
 
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+@pytest.mark.parametrize("cell,n,d,T", [(sy.CELL_TANH_RNN, 4, 2, 300), (sy.CELL_GRU, 3, 2, 257),
+                                        (sy.CELL_GRU, 1, 1, 1024), (sy.CELL_TANH_RNN, 8, 5, 65),
+                                        (sy.CELL_GRU, 2, 3, 1)])
+def test_small_dense_cells(lam, cell, n, d, T):
+    """The time-parallel cells (n <= 8, fp32): a producer kernel stores the
+    Jacobian's diagonal and the residual per step, then the same scans."""
+    p = sy.custom_problem(cell, B=2, T=T, d=d, n=n, seed=10 * n + T, w_scale=0.8, h0=True)
+    for k in (1, 3):
+        check(p, lam, 0.0, k)
+    check(p, lam, 1e-5, T)
+
+
+def test_small_dense_full_size_scalar_gru():
+    """The scalar GRU workload's shape (B=16, T=2^20) with quasi-ELK: two
+    sequences of the result against the oracle's quasi-ELK at the same sweep
+    count."""
+    p = sy.make_problem(2, with_g=False)
+    lam = 0.1
+    say("case scalar GRU full size, quasi-ELK lambda", lam)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, dl = dp.solve_elk(lam, hist_cap=4096)
+    torch.cuda.synchronize()
+    say("  gpu sweeps", it, "status", st, "last deltas", dl[-3:])
+    assert st == bd.PR_OK
+    for b in (0, p["B"] - 1):
+        qb = dict(p, B=1, x=p["x"][b:b + 1], h0=p["h0"][b:b + 1])
+        hb, *_ = oracle.elk(qb, lam, tol=0.0, max_iters=it)
+        err = np.abs(to64(dp.h[b]) - hb[0]).max()
+        say("  sequence", b, "max abs err", err)
+        assert err <= ATOL
+
+
 def test_unsupported_and_invalid():
-    p = sy.make_problem(1)
-    prob = bd.make_problem(p["cell"], p["jac"], p["dtype"], p["B"], p["T"], p["d"], p["n"])
-    assert bd.elk_workspace_bytes(prob) == 0  # small dense cells: no quasi-ELK kernels
+    prob = bd.make_problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)
+    assert bd.elk_workspace_bytes(prob) == 0  # no kernels for n = 16 at all
     q = sy.make_problem(5, B=1, T=64)
     dp = bd.DeviceProblem(q, elk=True)
     st, _, _ = dp.solve_elk(-1.0, check=False)
