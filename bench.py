@@ -30,7 +30,8 @@ from nonlinear_rnn_evaluation_newton_amd import synthetic as sy  # noqa: E402  (
 HBM_PEAK_GBS = 8000.0
 ELK_KERNELS = ("quasi-ELK sweep: per-channel cells k_elkc_filter + k_elkc_filter_carry + k_elkc_smooth + "
                "k_elkc_smooth_carry + k_elkc_apply (the cell re-evaluated in each pass); dense GRU "
-               "k_d64_gates<GM_QUASI> + k_elk_filter/gains/apply and their chunk carries")
+               "k_d64_gates<GM_QUASI>, small dense cells k_time_elk_jr, then k_elk_filter/gains/apply and "
+               "their chunk carries")
 FP32_MFMA_PEAK_TFS = 157.3
 
 
