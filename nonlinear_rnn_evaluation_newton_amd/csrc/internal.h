@@ -194,6 +194,7 @@ struct ElkArgs {
   void *h;    // [rows][S] iterate (storage dtype)
   int h_bf16;
   int B, T, S, cps, nch;
+  int L, sp;  // steps per chunk, lanes per chunk (the dense-family scans)
   float lam;
   int k;
   float tol;
@@ -209,7 +210,8 @@ struct ElkChanArgs {  // per-channel cells (the smoother's e.r3 and e.msc are sh
   int n;
   int cpf, nchf;       // filter chunks per sequence and in all
 };
-int elk_chunk_len();
+int elk_chunk_len(int S);         // steps per chunk of the dense-family quasi-ELK scans
+int elk_lanes_per_chunk(int S);
 int elk_chan_chunk_len(int sw);
 hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s);
 hipError_t launch_elk_chan_sweep(int cell, bool bf16, ElkChanArgs &a, hipStream_t s);

@@ -15,8 +15,8 @@
 // reverse affine scan.
 //
 // Dense n = 64 GRU: the gates kernel has stored d_t and r_t at the current
-// iterate ([row][d (S) | r (S)], fp32); chunks of ELK_L steps, one wavefront
-// per (sequence, chunk, 64 entries), lane = state entry:
+// iterate ([row][d (S) | r (S)], fp32); a lane per (chunk, state entry), a
+// wavefront per 64 entries of a chunk or per 64 / sp chunks of sp entries:
 //   k_elk_filter + k_elk_filter_carry   chunk filter maps, moments entering
 //                                       each chunk (shuffle scan over chunks);
 //   k_elk_gains + k_elk_smooth_carry    G, e per step and each chunk's
@@ -32,9 +32,20 @@
 
 namespace pr {
 
-constexpr int ELK_L = 64;  // steps per chunk
-
-int elk_chunk_len() { return ELK_L; }
+// Lanes per chunk (the state width rounded up to a power of two, at most 64)
+// and steps per chunk.  A narrow state packs 64 / sp chunks into a
+// wavefront, and takes longer chunks so the serial walks over chunk
+// aggregates stay short.
+static int elk_lanes(int S) {
+  int sp = 1;
+  while (sp < S && sp < 64) sp *= 2;
+  return sp;
+}
+int elk_chunk_len(int S) {
+  const int sp = elk_lanes(S);
+  return sp >= 4 ? 64 : 256 / sp;
+}
+int elk_lanes_per_chunk(int S) { return elk_lanes(S); }
 
 struct ElkGeom {
   int b, j, t0, t1, i;  // sequence, chunk, its steps [t0, t1), this lane's state entry
@@ -42,13 +53,14 @@ struct ElkGeom {
 };
 __device__ inline ElkGeom elk_geom(const ElkArgs &a) {
   ElkGeom g;
-  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), CG = (a.S + 63) / 64;
-  const int cg = wave % CG, chunk = wave / CG;
+  const int lane = threadIdx.x & 63, sp = a.sp;
+  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), CG = (a.S + sp - 1) / sp;
+  const int cg = wave % CG, chunk = (wave / CG) * (64 / sp) + lane / sp;
   g.b = chunk / a.cps;
   g.j = chunk % a.cps;
-  g.t0 = g.j * ELK_L;
-  g.t1 = min(a.T, g.t0 + ELK_L);
-  g.i = cg * 64 + (threadIdx.x & 63);
+  g.t0 = g.j * a.L;
+  g.t1 = min(a.T, g.t0 + a.L);
+  g.i = cg * sp + lane % sp;
   g.active = chunk < a.nch && g.i < a.S;
   return g;
 }
@@ -827,8 +839,8 @@ static void launch_elkc(ElkChanArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s) {
-  const int CG = (a.S + 63) / 64;
-  const unsigned gchunks = (unsigned)(((size_t)a.nch * CG + 3) / 4);
+  const int CG = (a.S + a.sp - 1) / a.sp, cpw = 64 / a.sp;
+  const unsigned gchunks = (unsigned)((((size_t)a.nch + cpw - 1) / cpw * CG + 3) / 4);
   const unsigned gcarry = (unsigned)(((size_t)a.B * a.S + 3) / 4);
   hipLaunchKernelGGL(k_elk_filter, dim3(gchunks), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_elk_filter_carry, dim3(gcarry), dim3(256), 0, s, a);

@@ -373,7 +373,8 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   if (pl.path != PATH_D64 && pl.path != PATH_CHAN && pl.path != PATH_TIME)
     return fail(PR_EUNSUPPORTED, "no quasi-ELK kernels for this problem");
   const size_t rows = (size_t)p->B * p->T, S = (size_t)pl.S;
-  const int L = pl.path == PATH_D64 ? elk_chunk_len() : elk_chan_chunk_len(p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1);
+  const int L = pl.path == PATH_CHAN ? elk_chan_chunk_len(p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1)
+                                      : elk_chunk_len(pl.S);
   el->cps = (p->T + L - 1) / L;
   if ((long long)el->cps * p->B * ((pl.S + 63) / 64) > 2147483647LL / 4 || (long long)p->B * pl.S > 2147483647LL / 4)
     return fail(PR_EUNSUPPORTED, "problem too large");
@@ -566,6 +567,8 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     ea.h = h;
     ea.h_bf16 = p->dtype == PR_BF16;
     ea.B = p->B; ea.T = p->T; ea.S = pl.S; ea.cps = el.cps; ea.nch = el.nch;
+    ea.L = elk_chunk_len(pl.S);
+    ea.sp = elk_lanes_per_chunk(pl.S);
     ea.lam = *elk_lambda;
     ea.tol = tol;
     ea.max_iters = max_iters;
