@@ -212,7 +212,16 @@ __global__ __launch_bounds__(64) void k_lsim_pass(const LsimArgs a) {
   }
   ls_sync();
   const int b = chunk / a.cps, j = chunk % a.cps;
-  const float *Ad = tab, *Bd = tab + LS_MAT, *pw = tab + 2 * LS_MAT;
+  const float *pw = tab + 2 * LS_MAT;
+  // the per-step operators Ad (NX x NX) and Bd (NX x MP) in registers
+  float Ad[LS_MAT], Bd[LS_MAT];
+#pragma unroll
+  for (int r = 0; r < NX; r++) {
+#pragma unroll
+    for (int c = 0; c < NX; c++) Ad[r * LS_W + c] = tab[r * LS_W + c];
+#pragma unroll
+    for (int c = 0; c < MP; c++) Bd[r * LS_W + c] = tab[LS_MAT + r * LS_W + c];
+  }
   const size_t rowb = (size_t)b * T;
   const int kc = j * LS_R * 64 * V;  // the chunk's first step
   // a lane's inputs in a round starting at k0 (addresses clamped into the
