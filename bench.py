@@ -95,16 +95,36 @@ def adjoint_bytes_per_unit(p: dict) -> float:
     return 2 * p["d"] * 4 + 3 * p["n"] * 4
 
 
+def host_cores() -> int:
+    """Cores this process may run on (the affinity mask), else the CPU count."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def median_of_3(fn) -> float:
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[1]
+
+
 def cpu_baseline(p: dict) -> dict:
-    """The oracle's fp64 sequential rollout, timed on this host.
+    """The oracle's fp64 sequential rollout, timed on this host (median of 3).
 
     Per-channel cells are independent across channels given x, so for them a
     sample of channels is rolled out (the full input width, every sequence and
     step) and the time is scaled by n / sample; dense cells run in full.
+    OpenMP runs over independent sequences only, so the threads that work are
+    min(OpenMP threads, B).
     """
     import numpy as np
     import oracle
-    threads = min(oracle.num_threads(), p["B"])
+    omp = oracle.num_threads()
+    threads = min(omp, p["B"])
     units = p["B"] * p["T"]
     if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
         n = p["n"]
@@ -121,20 +141,18 @@ def cpu_baseline(p: dict) -> dict:
         t0 = time.perf_counter()
         oracle.rollout(sub(1))
         t1 = time.perf_counter() - t0
-        ns = int(min(n, max(1, 10.0 / max(t1, 1e-3))))  # about 10 s of fp64 work
-        t0 = time.perf_counter()
-        oracle.rollout(sub(ns))
-        dt = (time.perf_counter() - t0) * n / ns
+        ns = int(min(n, max(1, 4.0 / max(t1, 1e-3))))  # about 4 s of fp64 work per run
+        q = sub(ns)
+        dt = median_of_3(lambda: oracle.rollout(q)) * n / ns
         sample = (f"fp64 sequential rollout of {ns} of {n} channels (all {p['B']} sequences x {p['T']} steps, "
                   f"full input width), OpenMP over sequences, time scaled by {n}/{ns}")
     else:
-        t0 = time.perf_counter()
-        oracle.rollout(p)
-        dt = time.perf_counter() - t0
+        dt = median_of_3(lambda: oracle.rollout(p))
         sample = (f"full workload: fp64 sequential rollout of all {p['B']} sequences x {p['T']} steps, "
                   f"OpenMP over sequences")
     return {"value": units / dt, "unit": "timesteps*batch/s", "cores": threads, "kind": "oracle",
-            "sample": sample + f"; {dt:.2f} s", "seconds": dt}
+            "sample": sample + f"; median of 3 runs {dt:.3f} s", "seconds": dt, "host_cores": host_cores(),
+            "omp_threads": omp}
 
 
 def bench_lsim(args) -> int:
@@ -192,13 +210,13 @@ def bench_lsim(args) -> int:
     }
     if not args.no_cpu_baseline:
         import oracle
-        t0 = time.perf_counter()
-        oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"], x0=q["x0"])
-        dt = time.perf_counter() - t0
+        dt = median_of_3(lambda: oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"],
+                                             x0=q["x0"]))
         line["cpu_baseline"] = {"value": B * T / dt, "unit": "timesteps*batch/s",
                                 "cores": min(oracle.num_threads(), B), "kind": "oracle",
                                 "sample": f"full workload: fp64 sequential lsim of all {B} sequences x {T} steps, "
-                                          f"OpenMP over sequences; {dt:.2f} s"}
+                                          f"OpenMP over sequences; median of 3 runs {dt:.3f} s",
+                                "host_cores": host_cores(), "omp_threads": oracle.num_threads()}
     print(json.dumps(line), flush=True)
     return 0
 
@@ -413,7 +431,8 @@ def main() -> int:
                                  "forward_ratio": round(15.0 / ms_solve, 2)}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(p)
-        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "host_cores",
+                                                     "omp_threads")}
         line["speedup_vs_seq"] = cb["seconds"] / (ms_solve * 1e-3)
     print(json.dumps(line), flush=True)
     return 0

@@ -27,6 +27,30 @@
  *    the device.  pararnn_last_error() gives a message for the calling thread.
  *  - Calls on the same workspace must not overlap; distinct workspaces may be
  *    used concurrently.
+ *
+ * Co-residency.  Some kernels chain the tiles of a sequence with a decoupled
+ * look-back: a tile waits until its predecessors have published their
+ * aggregates.  They run as persistent grids sized to the blocks the device
+ * holds at once, and assume every block of the grid is resident: the
+ * scalar-state sweep and adjoint (n = d = 1), the time-parallel sweep and
+ * adjoint of the small dense cells (n <= 8), and pararnn_affine_scan.  The
+ * channel-parallel passes (GRU_DIAG, LSTM_CIFG_DIAG), the dense n = 64 GRU,
+ * quasi-ELK and lsim have no waits between blocks.  If kernels on other
+ * streams keep compute units busy while such a grid runs, its blocks start
+ * late, and a wait that sees no progress for 2^16 polls (tens of
+ * milliseconds) gives up: the tile's carry becomes NaN, which makes every
+ * later state of that sequence NaN, and a fault flag is set in the
+ * workspace.  pararnn_solve checks the flag at each poll and then returns
+ * PR_ELOOKBACK; the asynchronous calls cannot return it, and their outputs
+ * hold the NaNs.  Two such grids on two streams at once can both give up.
+ *
+ * Run-to-run reproducibility.  How many predecessor aggregates a look-back
+ * composes depends on timing, so the kernels listed above can round
+ * differently from run to run (fp32 rounding of the carried state: up to a
+ * few units in the last place per composed tile; differences below 1e-6 on
+ * the scalar GRU at length 2^20).  The stop sweep can then differ between
+ * runs only where a delta lies within that distance of tol.  Every other
+ * kernel combines in a fixed order and is bitwise reproducible.
  */
 #ifndef PARARNN_H
 #define PARARNN_H
@@ -83,6 +107,7 @@ extern "C" {
 #define PR_EWORKSPACE (-2)    /* workspace NULL or smaller than pararnn_*workspace_bytes   */
 #define PR_EHIP (-3)          /* a HIP runtime call failed                                */
 #define PR_EUNSUPPORTED (-5)  /* valid problem the library has no kernel for              */
+#define PR_ELOOKBACK (-6)     /* a bounded look-back wait gave up (see "Co-residency")     */
 #define PR_NOT_CONVERGED 1    /* max_iters sweeps, delta never < tol; h = last iterate   */
 #define PR_NONFINITE 2        /* delta became NaN/Inf; h = that iterate                   */
 

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpararnn.so")
 
 # status codes (include/pararnn.h)
-PR_OK, PR_EINVAL, PR_EWORKSPACE, PR_EHIP, PR_EUNSUPPORTED = 0, -1, -2, -3, -5
+PR_OK, PR_EINVAL, PR_EWORKSPACE, PR_EHIP, PR_EUNSUPPORTED, PR_ELOOKBACK = 0, -1, -2, -3, -5, -6
 PR_NOT_CONVERGED, PR_NONFINITE = 1, 2
 PR_F32, PR_BF16 = 0, 1
 PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3

@@ -233,8 +233,12 @@ __device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, boo
       }
       if (!done) {
         if (q < W) {
-          if (++spins > PR_SPIN_LIMIT) {  // carry stays 0; the fault is reported by the host
+          if (++spins > PR_SPIN_LIMIT) {  // reported by the host; a NaN carry poisons the rest
             spin_fault(st);
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+              for (int i = 0; i < SW; i++) carry[c][i] = __builtin_nanf("");
             break;
           }
           __builtin_amdgcn_s_sleep(1);

@@ -262,9 +262,9 @@ __device__ inline float sc_resolve_from(Rsrc ragg, Rsrc rincl, int wend, int k, 
     if (r == 1) {
       wend -= 64;
     } else {
-      if (++spins > PR_SPIN_LIMIT) {  // the fault is reported by the host
+      if (++spins > PR_SPIN_LIMIT) {  // the fault is reported by the host; the carry poisons the rest
         if ((threadIdx.x & 63) == 0) spin_fault(st);
-        return 0.f;
+        return __builtin_nanf("");
       }
       __builtin_amdgcn_s_sleep(1);
     }

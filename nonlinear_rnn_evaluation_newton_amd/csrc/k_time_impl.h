@@ -170,9 +170,11 @@ __device__ inline void lookback(const Op<N> &tot, int j, int k, unsigned long lo
       const int m = bi ? 63 - __clzll((long long)bi) : -1;  // nearest tile with an inclusive prefix
       const bool ok = !(lane > m && p >= 0) || ha;
       if (!__all(ok)) {
-        if (++spins > PR_SPIN_LIMIT) {
+        if (++spins > PR_SPIN_LIMIT) {  // reported by the host; a NaN carry poisons the rest
           if (lane == 0) spin_fault(st);
           acc = op_identity<N>();
+#pragma unroll
+          for (int i = 0; i < N; i++) acc.b[i] = __builtin_nanf("");
           break;
         }
         __builtin_amdgcn_s_sleep(1);

@@ -82,6 +82,9 @@ int make_plan(const pr_problem *p, Plan *pl) {
   if (p->jac == PR_JAC_ZERO) pl->approx = APX_ZERO;
   else if (p->jac == PR_JAC_DIAG && p->cell != PR_CELL_GRU_DIAG && !(dense_cell && p->n == 1)) pl->approx = APX_DIAG;
   if ((double)p->B * p->T * p->n * 2 > 2147483647.0 * 64) return fail(PR_EUNSUPPORTED, "problem too large");
+  // rows of the products and row indices are 32-bit
+  if ((long long)p->B * p->T > 2147483647LL)
+    return fail(PR_EUNSUPPORTED, "B * T = %lld rows exceed 2^31 - 1", (long long)p->B * p->T);
 
   pl->G = gates_of(p->cell);
   pl->S = p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 * p->n : p->n;
@@ -312,6 +315,7 @@ const char *pararnn_strerror(int status) {
     case PR_EWORKSPACE: return "workspace too small";
     case PR_EHIP: return "HIP runtime error";
     case PR_EUNSUPPORTED: return "unsupported problem";
+    case PR_ELOOKBACK: return "a look-back wait gave up: the persistent grid's blocks were not all resident";
     case PR_NOT_CONVERGED: return "not converged within max_iters";
     case PR_NONFINITE: return "non-finite Newton update";
   }
@@ -670,7 +674,8 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       spec_enqueued = spec->rc >= 0;
     }
     HIPCHK(poll_ev ? hipEventSynchronize(poll_ev) : hipStreamSynchronize(s));
-    if (hs->fault) return fail(PR_EHIP, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
+    if (hs->fault)
+      return fail(PR_ELOOKBACK, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
     if (hs->stopped) {
       out_iters = hs->iters;
       out_status = hs->status;

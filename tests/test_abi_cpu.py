@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_all_codes():
-    for code in (0, -1, -2, -3, -5, 1, 2):
+    for code in (0, -1, -2, -3, -5, -6, 1, 2):
         assert bd.strerror(code) != "unknown status"
 
 
@@ -159,3 +159,21 @@ def test_solve_adjoint_arguments_rejected_without_device():
     assert call(p=_prob(B=0)) == bd.PR_EINVAL
     assert call(x=None) == bd.PR_EINVAL
     assert bd.last_error() != ""
+
+
+@pytest.mark.parametrize("cell,jac,dtype,B,T,d,n", [
+    (sy.CELL_GRU_DIAG, sy.JAC_DIAG, bd.PR_BF16, 4, (1 << 30) + 16, 1, 1),
+    (sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 3, (1 << 30), 1, 1),
+    (sy.CELL_LSTM_CIFG_DIAG, sy.JAC_BLOCK2, bd.PR_F32, 65536, 65536, 1, 1),
+])
+def test_rows_beyond_int32_rejected(cell, jac, dtype, B, T, d, n):
+    """B * T above 2^31 - 1 rows: rejected before any HIP call (products and
+    row indices are 32-bit), never wrapped into a smaller problem."""
+    L = bd.lib()
+    pb = bd.Problem(cell, jac, dtype, B, T, d, n)
+    assert L.pararnn_workspace_bytes(C.byref(pb), 1) == 0
+    w = bd.Weights(1, None, 1, None, 1)
+    rc = L.pararnn_solve(C.byref(pb), C.byref(w), C.c_void_p(16), None, 1e-6, 8, C.c_void_p(16), None, None, 0,
+                         C.c_void_p(256), 1 << 40, None)
+    assert rc == bd.PR_EUNSUPPORTED, bd.last_error()
+    assert "rows" in bd.last_error() or "too large" in bd.last_error()

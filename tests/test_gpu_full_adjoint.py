@@ -1,0 +1,190 @@
+"""GPU parity of the adjoint on the full-size workloads, in the launch
+configuration the benchmark times (pararnn_solve_adjoint: the solve and its
+adjoint in one call), against the fp64 oracle's reverse-mode adjoint taken at
+the GPU's trajectory.
+
+The per-channel workloads (diagonal ParaGRU, 2x2-block ParaLSTM) are
+compared on sampled channels (channels are independent given x, so the
+sliced problem's adjoint is exactly those channels' adjoint) and, for dx,
+which sums over every channel, on a window of the last steps of every
+sequence (the reverse recursion starts at the last step, so the window's
+adjoint needs only the window's inputs and the state just before it).  An
+fp32 per-channel case at the full length 8192 compares every tensor element
+by element; its 128 tiles per stripe take the reverse carry walk over more
+than one group of tiles.  The dense n = 64 GRU is compared on all 16
+sequences (many chunks per sequence: the adjoint's chunk products, carry
+chain and persistent gates loop at their full extent).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ATOL = 1e-4     # fp32: max-abs on lambda, dx, dh0 (scaled by max(1, |ref|))
+RTOL_BF = 2e-2  # bf16 storage: ||gpu - ref||_inf / ||ref||_inf per tensor
+RTOL_W = 1e-4   # fp32 weight gradients: norm-wise relative
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def grad_buffers(dp):
+    p = dp.p
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = dict(lam=torch.empty_like(dp.h), dx=torch.empty_like(dp.x),
+             dh0=torch.empty((p["B"], p["S"]), dtype=dp.tdtype, device="cuda"),
+             W_x=torch.empty(tuple(dp.W_x.shape), **f32), b_x=torch.empty(tuple(dp.b_x.shape), **f32),
+             W_h=torch.empty(tuple(dp.W_h.shape), **f32), b_h=torch.empty(tuple(dp.b_h.shape), **f32))
+    if dp.peep is not None:
+        o["peep"] = torch.empty(tuple(dp.peep.shape), **f32)
+    return o
+
+
+def solve_adjoint(dp):
+    """The benchmark's step: one pararnn_solve_adjoint call."""
+    p = dp.p
+    o = grad_buffers(dp)
+    grads = {k: o[k] for k in ("W_x", "b_x", "W_h", "b_h", "peep") if k in o}
+    st, it, dl = bd.solve_adjoint(dp.prob, dp.w, dp.x, dp.h0, p["tol"], p["max_iters"], dp.h, dp.g, dp.ws,
+                                  o["lam"], o["dx"], o["dh0"], grads)
+    torch.cuda.synchronize()
+    return st, it, dl, o
+
+
+def slice_channels(p, ch):
+    """The sub-problem of channels `ch` of a per-channel cell."""
+    n = p["n"]
+    rows = np.concatenate([g * n + ch for g in range(3)])
+    q = dict(p)
+    q["n"] = len(ch)
+    lstm = p["cell"] == sy.CELL_LSTM_CIFG_DIAG
+    q["S"] = q["n"] * (2 if lstm else 1)
+    q["W_x"] = p["W_x"][rows]
+    q["b_x"] = p["b_x"][rows]
+    q["W_h"] = p["W_h"][rows]
+    q["b_h"] = p["b_h"][rows]
+    if p["peep"] is not None:
+        q["peep"] = np.concatenate([p["peep"][ch], p["peep"][n + ch]])
+    sidx = np.stack([2 * ch, 2 * ch + 1], 1).reshape(-1) if lstm else ch
+    q["h0"] = p["h0"][:, sidx]
+    q["g"] = p["g"][:, :, sidx]
+    return q, rows, sidx
+
+
+def time_window(p, h, t0):
+    """Steps t0 .. T-1 as a problem of their own: the state before step t0
+    becomes h0.  Its adjoint equals the full adjoint on those steps."""
+    q = dict(p)
+    q["T"] = p["T"] - t0
+    q["x"] = p["x"][:, t0:]
+    q["g"] = p["g"][:, t0:]
+    q["h0"] = h[:, t0 - 1] if t0 > 0 else p["h0"]
+    return q, h[:, t0:]
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_adjoint_sampled_channels(cfg):
+    p = sy.make_problem(cfg)
+    say("full-size adjoint case", p["name"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"])
+    dp = bd.DeviceProblem(p)
+    st, it, dl, o = solve_adjoint(dp)
+    say("  status", st, "sweeps", it)
+    assert st == bd.PR_OK and it == p["max_iters"]
+    h = to64(dp.h)
+
+    # sampled channels: every output restricted to them
+    rng = np.random.default_rng(200 + cfg)
+    ch = np.unique(np.concatenate([[0, 1, p["n"] - 1], rng.choice(p["n"], 9, replace=False)]))
+    q, rows, sidx = slice_channels(p, ch)
+    ref = oracle.adjoint(q, h[:, :, sidx])
+    checks = [("lam", to64(o["lam"])[:, :, sidx], ref["lam"]), ("dh0", to64(o["dh0"])[:, sidx], ref["dh0"]),
+              ("dW_x", to64(o["W_x"])[rows], ref["dW_x"]), ("db_x", to64(o["b_x"])[rows], ref["db_x"]),
+              ("dW_h", to64(o["W_h"])[rows], ref["dW_h"]), ("db_h", to64(o["b_h"])[rows], ref["db_h"])]
+    if p["cell"] == sy.CELL_LSTM_CIFG_DIAG:
+        n = p["n"]
+        checks.append(("dpeep", to64(o["peep"])[np.concatenate([ch, n + ch])], ref["dpeep"]))
+    say("  sampled channels", ch)
+    for key, got, want in checks:
+        r = rel(got, want)
+        say("  ", key, "rel", r)
+        assert r <= RTOL_BF, key
+
+    # dx (a sum over all channels) on the last 40 steps of every sequence
+    t0 = p["T"] - 40
+    w, hw = time_window(p, h, t0)
+    refw = oracle.adjoint(w, hw)
+    for key, got in (("lam", to64(o["lam"])[:, t0:]), ("dx", to64(o["dx"])[:, t0:])):
+        r = rel(got, refw[key])
+        say("  window", key, "rel", r)
+        assert r <= RTOL_BF, key
+
+
+@pytest.mark.parametrize("cell", [sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG])
+@pytest.mark.parametrize("T", [8192, 8192 + 37])
+def test_fp32_full_length_adjoint(cell, T):
+    """fp32 per-channel adjoint at the ParaLSTM workload's length: 128 (or
+    129) tiles per stripe, so the reverse carry walk spans several groups;
+    every tensor element by element, h0 and biases included."""
+    p = sy.custom_problem(cell, B=2, T=T, d=12, n=66, seed=T + cell, w_scale=0.8, h0=True)
+    say("fp32 full-length adjoint case", p["name"], "T", T)
+    dp = bd.DeviceProblem(p)
+    st, it, dl, o = solve_adjoint(dp)
+    ho, ito, sto, dlo = oracle.deer(p, tol=p["tol"], max_iters=p["max_iters"])
+    say("  gpu sweeps", it, "status", st, "| oracle", ito, sto)
+    assert st == sto and it == ito
+    h = to64(dp.h)
+    assert np.abs(h - ho).max() <= ATOL
+    ref = oracle.adjoint(p, h)
+    for key in ("lam", "dx", "dh0"):
+        err = np.abs(to64(o[key]) - ref[key]).max()
+        say("  ", key, "abs", err)
+        assert err <= ATOL * max(1.0, np.abs(ref[key]).max()), key
+    keys = [("W_x", "dW_x"), ("b_x", "db_x"), ("W_h", "dW_h"), ("b_h", "db_h")]
+    if cell == sy.CELL_LSTM_CIFG_DIAG:
+        keys.append(("peep", "dpeep"))
+    for k, rk in keys:
+        r = rel(to64(o[k]), ref[rk])
+        say("  ", rk, "rel", r)
+        assert r <= RTOL_W, rk
+
+
+def test_dense64_full_size_adjoint():
+    """The dense n = 64 GRU workload (B = 16, T = 16384: 256 chunks of 64
+    steps per sequence), every sequence, every tensor."""
+    p = sy.make_problem(5)
+    say("full-size adjoint case", p["name"])
+    dp = bd.DeviceProblem(p)
+    st, it, dl, o = solve_adjoint(dp)
+    say("  status", st, "sweeps", it, "deltas", dl)
+    assert st == bd.PR_OK
+    h = to64(dp.h)
+    ref = oracle.adjoint(p, h)
+    for key in ("lam", "dx", "dh0"):
+        err = np.abs(to64(o[key]) - ref[key]).max()
+        say("  ", key, "abs", err, "max |ref|", np.abs(ref[key]).max())
+        assert err <= ATOL * max(1.0, np.abs(ref[key]).max()), key
+    for k, rk in (("W_x", "dW_x"), ("b_x", "db_x"), ("W_h", "dW_h"), ("b_h", "db_h")):
+        r = rel(to64(o[k]), ref[rk])
+        say("  ", rk, "rel", r)
+        assert r <= RTOL_W, rk

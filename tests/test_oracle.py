@@ -295,6 +295,47 @@ def test_fixed_point_is_rollout(cfg, kw):
     np.testing.assert_allclose(h, h_seq, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_fixed_point_is_rollout_full_size(cfg):
+    """The converged Newton iterate equals the sequential rollout at the full
+    workload sizes (the dense cells couple all channels, so every one runs
+    whole)."""
+    p = sy.make_problem(cfg, with_g=False)
+    h_seq = oracle.rollout(p)
+    h, iters, status, deltas = oracle.deer(p, tol=1e-11, max_iters=p["T"])
+    assert status == oracle.OK and iters < 12
+    np.testing.assert_allclose(h, h_seq, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_fixed_point_is_rollout_full_size_sampled_channels(cfg):
+    """The per-channel workloads at their full batch, length and input width
+    on 6 sampled channels (channels are independent given x, so the sliced
+    problem is exactly those channels of the full one)."""
+    p = sy.make_problem(cfg, with_g=False)
+    n = p["n"]
+    ch = np.array([0, 1, 77, n // 2, n - 2, n - 1])
+    rows = np.concatenate([g * n + ch for g in range(3)])
+    lstm = p["cell"] == sy.CELL_LSTM_CIFG_DIAG
+    q = dict(p, n=len(ch), S=len(ch) * (2 if lstm else 1), W_x=p["W_x"][rows], b_x=p["b_x"][rows],
+             W_h=p["W_h"][rows], b_h=p["b_h"][rows],
+             peep=np.concatenate([p["peep"][ch], p["peep"][n + ch]]) if lstm else None)
+    q["h0"] = np.zeros((p["B"], q["S"]))
+    h_seq = oracle.rollout(q)
+    h, iters, status, deltas = oracle.deer(q, tol=1e-11, max_iters=q["T"])
+    assert status == oracle.OK and iters < 16
+    np.testing.assert_allclose(h, h_seq, rtol=0, atol=1e-12)
+
+
+def test_dense64_full_history_record_is_the_rollout():
+    """The stored full-size dense-GRU history (written by
+    golden/make_dense64_history.py from the oracle alone) records a converged
+    iterate within 1e-12 of the rollout."""
+    gold = json.load(open(os.path.join(GOLDEN, "dense64_gru_full_history.json")))
+    assert gold["status"] == oracle.OK and gold["deltas"][-1] < 1e-5
+    assert gold["max_abs_deer_minus_rollout"] <= 1e-12
+
+
 @pytest.mark.parametrize("approx", [oracle.NEWTON, oracle.QUASI, oracle.JACOBI])
 @pytest.mark.parametrize("cell", LIB_CELLS + [sy.CELL_LINEAR])
 def test_prefix_exactness_any_jacobian(cell, approx):
