@@ -241,6 +241,27 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
                         float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * pararnn_affine_scan without a workspace, for callers that cannot allocate
+ * device memory at all: code under stream capture, tight serving loops,
+ * harnesses that forbid allocation.  The same recurrence, layouts, kernels
+ * and results as pararnn_affine_scan (jac, B, T, n, reverse, A, b, y as
+ * there).  Its scratch (look-back descriptors and a state record) lives in
+ * a static device array of PR_NOALLOC_SCRATCH_BYTES that every device this
+ * entry point runs on holds until the process ends; the call itself
+ * allocates nothing and makes no allocating runtime call.  A problem whose
+ * pararnn_scan_workspace_bytes exceeds PR_NOALLOC_SCRATCH_BYTES returns
+ * PR_EWORKSPACE before any HIP call.  `stream` must belong to the current
+ * device.  All calls on one device share that device's array, which keeps
+ * the last call's contents (each call clears what it needs before its
+ * scan): calls that overlap on one device (two streams, or two host
+ * threads) race and must be serialised by the caller.  Asynchronous on
+ * `stream`.
+ */
+#define PR_NOALLOC_SCRATCH_BYTES (16u << 20)
+int pararnn_affine_scan_noalloc(int jac, int B, int T, int n, int reverse, const float *A, const float *b, float *y,
+                                void *stream);
+
+/*
  * Linear state-space simulation (Para-Seq README, Main features: ODE
  * solvers; Example: lsim(A, B, C, D, U, t)): the system dx/dt = A x + B u,
  * y = C x + D u sampled every dt with the input held between samples

@@ -24,7 +24,8 @@ PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO = 0, 1, 2, 3
 EXPORTS = ["pararnn_workspace_bytes", "pararnn_solve", "pararnn_adjoint", "pararnn_solve_adjoint",
            "pararnn_scan_workspace_bytes", "pararnn_affine_scan", "pararnn_strerror", "pararnn_last_error", "pararnn_trace", "pararnn_trace_read",
            "pararnn_trace_kernel", "pararnn_lsim_workspace_bytes", "pararnn_lsim", "pararnn_elk_workspace_bytes",
-           "pararnn_solve_elk"]
+           "pararnn_solve_elk", "pararnn_affine_scan_noalloc"]
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PR_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(C.Structure):
@@ -71,6 +72,8 @@ def lib():
         L.pararnn_scan_workspace_bytes.restype = S
         L.pararnn_affine_scan.argtypes = [I, I, I, I, I, P, P, P, P, S, P]
         L.pararnn_affine_scan.restype = I
+        L.pararnn_affine_scan_noalloc.argtypes = [I, I, I, I, I, P, P, P, P]
+        L.pararnn_affine_scan_noalloc.restype = I
         L.pararnn_strerror.argtypes = [I]
         L.pararnn_strerror.restype = C.c_char_p
         L.pararnn_last_error.argtypes = []
@@ -219,6 +222,16 @@ def affine_scan(jac: int, A, b, y, workspace, reverse: bool = False, check: bool
                                    workspace.numel() * workspace.element_size(), _stream())
     if check and st < 0:
         raise PararnnError(st, "pararnn_affine_scan")
+    return st
+
+
+def affine_scan_noalloc(jac: int, A, b, y, reverse: bool = False, check: bool = True) -> int:
+    """pararnn_affine_scan_noalloc: the same scan with the library's static
+    device scratch instead of a workspace."""
+    B, T, n = b.shape[0], b.shape[1], b.shape[2]
+    st = lib().pararnn_affine_scan_noalloc(jac, B, T, n, int(reverse), _p(A), _p(b), _p(y), _stream())
+    if check and st < 0:
+        raise PararnnError(st, "pararnn_affine_scan_noalloc")
     return st
 
 

@@ -216,4 +216,15 @@ int elk_chan_chunk_len(int sw);
 hipError_t launch_elk_sweep(ElkArgs &a, hipStream_t s);
 hipError_t launch_elk_chan_sweep(int cell, bool bf16, ElkChanArgs &a, hipStream_t s);
 
+// ---------------- ABI layer helpers shared across translation units ---------
+// Records a message for pararnn_last_error() on the calling thread and
+// returns `code`.
+int fail(int code, const char *fmt, ...);
+void clear_error();
+// The linear recurrence of pararnn_affine_scan on a caller-provided scratch
+// buffer `ws` (256-byte aligned, ws_bytes long): validates the arguments,
+// clears what must start at zero and launches the scan on `s`.
+int affine_scan_run(int jac, int B, int T, int n, int reverse, const float *A, const float *b, float *y, void *ws,
+                    size_t ws_bytes, hipStream_t s);
+
 }  // namespace pr

@@ -14,7 +14,7 @@
 
 using namespace pr;
 
-namespace {
+namespace pr {
 
 thread_local std::string g_err;
 
@@ -27,6 +27,12 @@ int fail(int code, const char *fmt, ...) {
   g_err = buf;
   return code;
 }
+
+void clear_error() { g_err.clear(); }
+
+}  // namespace pr
+
+namespace {
 
 #define HIPCHK(expr)                                                                          \
   do {                                                                                        \
@@ -1037,6 +1043,15 @@ size_t pararnn_scan_workspace_bytes(int jac, int B, int T, int n) {
 int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *A, const float *b, float *y,
                         void *workspace, size_t ws_bytes, void *stream) {
   g_err.clear();
+  return affine_scan_run(jac, B, T, n, reverse, A, b, y, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace pr {
+
+int affine_scan_run(int jac, int B, int T, int n, int reverse, const float *A, const float *b, float *y, void *workspace,
+                    size_t ws_bytes, hipStream_t s) {
   if (jac < 0 || jac > 2) return fail(PR_EINVAL, "unknown jac %d", jac);
   if (B < 1 || T < 1 || n < 1) return fail(PR_EINVAL, "sizes must be >= 1");
   if (!A || !b || !y) return fail(PR_EINVAL, "A, b and y are required");
@@ -1044,7 +1059,6 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
   if (need == 0) return fail(PR_EUNSUPPORTED, "no scan kernel for jac %d n %d", jac, n);
   if (!workspace || ws_bytes < need) return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
   if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
   HIPCHK(launch_zero(ws, need, s));
   if (jac != PR_JAC_DENSE) {
@@ -1076,4 +1090,4 @@ int pararnn_affine_scan(int jac, int B, int T, int n, int reverse, const float *
   return PR_OK;
 }
 
-}  // extern "C"
+}  // namespace pr

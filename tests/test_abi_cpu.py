@@ -177,3 +177,18 @@ def test_rows_beyond_int32_rejected(cell, jac, dtype, B, T, d, n):
                          C.c_void_p(256), 1 << 40, None)
     assert rc == bd.PR_EUNSUPPORTED, bd.last_error()
     assert "rows" in bd.last_error() or "too large" in bd.last_error()
+
+
+def test_noalloc_scan_rejects_without_device():
+    """pararnn_affine_scan_noalloc refuses bad arguments and problems beyond
+    its static scratch before any HIP call."""
+    L = bd.lib()
+    v = C.c_void_p(16)
+    assert L.pararnn_affine_scan_noalloc(5, 1, 8, 1, 0, v, v, v, None) == bd.PR_EINVAL
+    assert L.pararnn_affine_scan_noalloc(bd.PR_JAC_DIAG, 0, 8, 1, 0, v, v, v, None) == bd.PR_EINVAL
+    assert L.pararnn_affine_scan_noalloc(bd.PR_JAC_DIAG, 1, 8, 1, 0, None, v, v, None) == bd.PR_EINVAL
+    assert L.pararnn_affine_scan_noalloc(bd.PR_JAC_DENSE, 1, 8, 13, 0, v, v, v, None) == bd.PR_EUNSUPPORTED
+    B, T, n = 8, 1 << 16, 1024
+    assert bd.scan_workspace_bytes(bd.PR_JAC_DIAG, B, T, n) > bd.NOALLOC_SCRATCH_BYTES
+    assert L.pararnn_affine_scan_noalloc(bd.PR_JAC_DIAG, B, T, n, 0, v, v, v, None) == bd.PR_EWORKSPACE
+    assert "static scratch" in bd.last_error()
