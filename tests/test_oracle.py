@@ -350,6 +350,25 @@ def test_prefix_exactness_any_jacobian(cell, approx):
     np.testing.assert_allclose(h, h_seq, rtol=1e-14, atol=1e-13)
 
 
+def test_cifg_peephole_hand_worked():
+    """The LSTM rollout against a one-channel example worked from the textbook
+    peephole equations with the coupled input gate (golden/make_cifg_hand.py,
+    math module only); the example separates the reading from its two easy
+    misreadings by far more than the tolerance."""
+    gold = json.load(open(os.path.join(GOLDEN, "cifg_peephole_hand.json")))
+    T = len(gold["x"])
+    p = dict(cell=sy.CELL_LSTM_CIFG_DIAG, jac=2, dtype=0, B=1, T=T, d=1, n=1, G=3, S=2,
+             W_x=np.array(gold["W_x"]).reshape(3, 1), b_x=np.array(gold["b_x"]), W_h=np.array(gold["W_h"]),
+             b_h=np.array(gold["b_h"]), peep=np.array(gold["peep"]), x=np.array(gold["x"]).reshape(1, T, 1),
+             h0=np.array(gold["h0_c_h"]).reshape(1, 2), tol=1e-12, max_iters=T)
+    want = np.array(gold["states_c_h"])
+    np.testing.assert_allclose(oracle.rollout(p)[0], want, rtol=0, atol=1e-15)
+    h, it, st, _ = oracle.deer(p, tol=0.0, max_iters=T)   # exact after T sweeps
+    np.testing.assert_allclose(h[0], want, rtol=0, atol=1e-15)
+    for wrong in ("misreading_output_peephole_on_old_c", "misreading_uncoupled_input_gate"):
+        assert np.abs(np.array(gold[wrong]) - want).max() > 1e-2, wrong
+
+
 def test_hand_worked_scalar_tanh():
     gold = json.load(open(os.path.join(GOLDEN, "p4_tanh_n1.json")))
     p = dict(cell=sy.CELL_TANH_RNN, jac=0, dtype=0, B=1, T=2, d=1, n=1, G=1, S=1,
