@@ -360,7 +360,7 @@ def main() -> int:
         flops = 2.0 * 64 ** 3 + 2.0 * 64 ** 2
         tfs = flops * B * T / (dm / dn * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                    "frac": round(tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": None,
+                    "frac": round(tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": measured_traffic(p["name"]),
                     "kernel": "k_d64_scanA (64x64 Jacobian chunk products, fp32 MFMA)",
                     "avg_launch_us": round(dm / dn * 1e3, 2), "flops_per_launch": flops * B * T}
         extra["sweep_avg_us"] = round(tr["sweep_ms"] / tr["sweep_launches"] * 1e3, 2)
