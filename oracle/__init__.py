@@ -59,6 +59,7 @@ def _load():
         lib.orc_adjoint.argtypes = [P] + [P] * 12
         lib.orc_lsim_discrete.argtypes = [C.c_int] * 5 + [P] * 8
         lib.orc_elk.argtypes = [P, C.c_double, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
+        lib.orc_elk_full.argtypes = [P, C.c_double, P, P, C.c_double, C.c_int, P, P, P, P, C.c_int]
         lib.orc_num_threads.restype = C.c_int
         _lib = lib
     return _lib
@@ -172,6 +173,24 @@ def elk(p: dict, lam: float, tol=None, max_iters=None, x=None, h0=None, hist_cap
     deltas = np.zeros(hist_cap)
     _check(lib.orc_elk(bd.ref, float(lam), _ptr(x), _ptr(h0), float(tol), int(max_iters), _ptr(h),
                        C.byref(it), C.byref(st), _ptr(deltas), hist_cap))
+    return h, it.value, st.value, deltas[:min(it.value, hist_cap)].copy()
+
+
+def elk_full(p: dict, lam: float, tol=None, max_iters=None, x=None, h0=None, hist_cap=4096):
+    """ELK with the cell's own Jacobian (dense, 2x2 blocks or diagonal) and
+    damping lam >= 0: returns (h, iters, status, deltas[iters])."""
+    lib = _load()
+    x = _f64(p["x"] if x is None else x)
+    h0 = _f64(p["h0"] if h0 is None else h0)
+    B, T = x.shape[0], x.shape[1]
+    tol = p["tol"] if tol is None else tol
+    max_iters = p["max_iters"] if max_iters is None else max_iters
+    bd = _Bound(p, B=B, T=T)
+    h = np.zeros((B, T, p["S"]))
+    it, st = C.c_int(0), C.c_int(0)
+    deltas = np.zeros(hist_cap)
+    _check(lib.orc_elk_full(bd.ref, float(lam), _ptr(x), _ptr(h0), float(tol), int(max_iters), _ptr(h),
+                            C.byref(it), C.byref(st), _ptr(deltas), hist_cap))
     return h, it.value, st.value, deltas[:min(it.value, hist_cap)].copy()
 
 

@@ -38,6 +38,10 @@
  *    Levenberg-Marquardt with Kalman smoothing to stabilise DEER; Para-Seq
  *    README, Main features: ELK and quasi-ELK solvers), with the textbook
  *    Kalman filter and Rauch-Tung-Striebel smoother run sequentially.
+ *  - orc_elk_full: ELK, the same damped step with the cell's own Jacobian
+ *    (dense for the tanh RNN, GRU and linear cells, 2x2 blocks per channel
+ *    for the LSTM, diagonal for the diagonal GRU), the Kalman filter and
+ *    smoother run with full covariance matrices, sequentially.
  *  - orc_lsim_discrete: the sampled linear state-space simulation behind the
  *    README's lsim (Main features: ODE solvers; Example: lsim(A, B, C, D, U,
  *    t)) once the system is discretised: x_0 = x0, y_k = C x_k + D u_k,
@@ -711,6 +715,190 @@ int orc_elk(const orc_model *m, double lambda, const double *x, const double *h0
         }
       }
       free(U); free(F); free(D); free(R); free(J); free(Pp); free(Mp); free(Pf); free(Mf); free(Ms); free(zero);
+    }
+    if (err) return ORC_ENOMEM;
+    if (nonfin) delta = NAN;
+    if (deltas && k <= hist_cap) deltas[k - 1] = delta;
+    *iters = k;
+    if (!isfinite(delta)) { *status = ORC_NONFINITE; return ORC_OK; }
+    if (tol > 0.0 && delta < tol) { *status = ORC_OK; return ORC_OK; }
+    if (k == T) { *status = ORC_OK; return ORC_OK; }
+  }
+  *status = tol > 0.0 ? ORC_NOT_CONVERGED : ORC_OK;
+  return ORC_OK;
+}
+
+/*
+ * Small dense linear algebra for orc_elk_full (q x q row-major, q <= a few
+ * dozen).  chol_solve: X = A^{-1} Bm for symmetric positive definite A and a
+ * q x nc right-hand side, by the Cholesky factorisation A = L L^T and two
+ * triangular solves.  Returns 0, or -1 if A is not positive definite.
+ */
+static int chol_solve(int q, const double *A, const double *Bm, int nc, double *X, double *L) {
+  for (int i = 0; i < q; i++) {
+    for (int j = 0; j <= i; j++) {
+      double v = A[(size_t)i * q + j];
+      for (int k = 0; k < j; k++) v -= L[(size_t)i * q + k] * L[(size_t)j * q + k];
+      if (i == j) {
+        if (!(v > 0.0)) return -1;
+        L[(size_t)i * q + i] = sqrt(v);
+      } else {
+        L[(size_t)i * q + j] = v / L[(size_t)j * q + j];
+      }
+    }
+  }
+  for (int c = 0; c < nc; c++) {
+    for (int i = 0; i < q; i++) {  /* L y = b */
+      double v = Bm[(size_t)i * nc + c];
+      for (int k = 0; k < i; k++) v -= L[(size_t)i * q + k] * X[(size_t)k * nc + c];
+      X[(size_t)i * nc + c] = v / L[(size_t)i * q + i];
+    }
+    for (int i = q - 1; i >= 0; i--) {  /* L^T x = y */
+      double v = X[(size_t)i * nc + c];
+      for (int k = i + 1; k < q; k++) v -= L[(size_t)k * q + i] * X[(size_t)k * nc + c];
+      X[(size_t)i * nc + c] = v / L[(size_t)i * q + i];
+    }
+  }
+  return 0;
+}
+
+/*
+ * ELK.  Each sweep takes the Levenberg-Marquardt step of the residual system
+ * with the cell's own Jacobian J_t and damping lambda:
+ *   dh = argmin sum_t ||dh_t - J_t dh_{t-1} - r_t||^2 + lambda sum_t ||dh_t||^2,
+ * dh_{-1} = 0: the posterior mean of the linear-Gaussian model
+ *   dh_t = J_t dh_{t-1} + r_t + w_t,  w_t ~ N(0, I);  0 = dh_t + v_t,
+ *   v_t ~ N(0, I / lambda).
+ * The Jacobian's structure splits the state into independent blocks (the
+ * whole state for dense cells, each channel's (c, h) for the LSTM, each entry
+ * for the diagonal GRU); per block the textbook Kalman filter
+ *   P^-_t = J_t P_{t-1} J_t^T + I,  m^-_t = J_t m_{t-1} + r_t,
+ *   P_t = (lambda P^-_t + I)^{-1} P^-_t,  m_t = (lambda P^-_t + I)^{-1} m^-_t
+ * (the gain for an observation of covariance I / lambda), from P_{-1} = 0,
+ * m_{-1} = 0, then the Rauch-Tung-Striebel smoother
+ *   m^s_{T-1} = m_{T-1},  m^s_t = m_t + G_t (m^s_{t+1} - m^-_{t+1}),
+ *   G_t = P_t J_{t+1}^T (P^-_{t+1})^{-1}.
+ * lambda = 0 gives the Newton step.  Then h += m^s and the stop rule of
+ * orc_deer_approx.
+ */
+int orc_elk_full(const orc_model *m, double lambda, const double *x, const double *h0, double tol, int max_iters,
+                 double *h, int *iters, int *status, double *deltas, int hist_cap) {
+  if (!model_ok(m) || max_iters < 1 || !(lambda >= 0.0)) return ORC_EINVAL;
+  const int S = swidth(m), Gn = n_gates(m->cell) * m->n, T = m->T, kind = jkind(m->cell);
+  const int q = kind == ORC_DENSE ? S : kind == ORC_BLOCK2 ? 2 : 1;  /* block size */
+  const int nblk = S / q;
+  const size_t js = jsize(m), qq = (size_t)q * q;
+  memset(h, 0, sizeof(double) * (size_t)m->B * T * S);
+  *iters = 0;
+  *status = ORC_OK;
+  if (T == 0 || m->B == 0) return ORC_OK;
+  for (int k = 1; k <= max_iters; k++) {
+    double delta = 0.0;
+    int err = 0, nonfin = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : delta) reduction(| : err, nonfin)
+    for (int b = 0; b < m->B; b++) {
+      double *U = (double *)malloc(sizeof(double) * Gn);
+      double *F = (double *)malloc(sizeof(double) * (size_t)T * S);
+      double *Jall = (double *)malloc(sizeof(double) * (size_t)T * js);
+      double *Jb = (double *)malloc(sizeof(double) * (size_t)T * qq);    /* one block's J_t */
+      double *Rb = (double *)malloc(sizeof(double) * (size_t)T * q);     /* its r_t */
+      double *Pp = (double *)malloc(sizeof(double) * (size_t)T * qq), *Mp = (double *)malloc(sizeof(double) * (size_t)T * q);
+      double *Pf = (double *)malloc(sizeof(double) * (size_t)T * qq), *Mf = (double *)malloc(sizeof(double) * (size_t)T * q);
+      double *Ms = (double *)malloc(sizeof(double) * (size_t)T * q);
+      double *W1 = (double *)malloc(sizeof(double) * qq), *W2 = (double *)malloc(sizeof(double) * qq);
+      double *W3 = (double *)malloc(sizeof(double) * qq), *Lw = (double *)malloc(sizeof(double) * qq);
+      double *v1 = (double *)malloc(sizeof(double) * q), *v2 = (double *)malloc(sizeof(double) * q);
+      double *zero = (double *)calloc(S, sizeof(double));
+      if (!U || !F || !Jall || !Jb || !Rb || !Pp || !Mp || !Pf || !Mf || !Ms || !W1 || !W2 || !W3 || !Lw || !v1 || !v2 ||
+          !zero) {
+        err |= 1;
+      } else {
+        double *hb = h + (size_t)b * T * S;
+        for (int t = 0; t < T; t++) {
+          const double *sp = t == 0 ? (h0 ? h0 + (size_t)b * S : zero) : hb + (size_t)(t - 1) * S;
+          input_proj(m, x + ((size_t)b * T + t) * m->d, U);
+          cell_fwd(m, sp, U, F + (size_t)t * S, Jall + (size_t)t * js);
+        }
+        for (int blk = 0; blk < nblk && !err; blk++) {
+          /* the block's Jacobians and residuals */
+          for (int t = 0; t < T; t++) {
+            const double *J = Jall + (size_t)t * js;
+            for (int i = 0; i < q; i++) {
+              const int gi = blk * q + i;
+              for (int j = 0; j < q; j++) {
+                double v;
+                if (kind == ORC_DENSE) v = J[(size_t)gi * S + blk * q + j];
+                else if (kind == ORC_DIAG) v = J[gi];
+                else v = J[(size_t)4 * blk + 2 * i + j];
+                Jb[(size_t)t * qq + (size_t)i * q + j] = v;
+              }
+              Rb[(size_t)t * q + i] = F[(size_t)t * S + gi] - hb[(size_t)t * S + gi];
+            }
+          }
+          /* Kalman filter */
+          double *P = W3, *mv = v2;
+          for (size_t e = 0; e < qq; e++) P[e] = 0.0;
+          for (int i = 0; i < q; i++) mv[i] = 0.0;
+          for (int t = 0; t < T && !err; t++) {
+            const double *J = Jb + (size_t)t * qq;
+            double *pp = Pp + (size_t)t * qq, *mp = Mp + (size_t)t * q;
+            for (int i = 0; i < q; i++) {            /* W1 = J P */
+              for (int j = 0; j < q; j++) {
+                double a = 0.0;
+                for (int l = 0; l < q; l++) a += J[(size_t)i * q + l] * P[(size_t)l * q + j];
+                W1[(size_t)i * q + j] = a;
+              }
+            }
+            for (int i = 0; i < q; i++) {            /* P^- = W1 J^T + I,  m^- = J m + r */
+              for (int j = 0; j < q; j++) {
+                double a = i == j ? 1.0 : 0.0;
+                for (int l = 0; l < q; l++) a += W1[(size_t)i * q + l] * J[(size_t)j * q + l];
+                pp[(size_t)i * q + j] = a;
+              }
+              double a = Rb[(size_t)t * q + i];
+              for (int l = 0; l < q; l++) a += J[(size_t)i * q + l] * mv[l];
+              mp[i] = a;
+            }
+            for (size_t e = 0; e < qq; e++) W2[e] = lambda * pp[e];   /* lambda P^- + I */
+            for (int i = 0; i < q; i++) W2[(size_t)i * q + i] += 1.0;
+            double *pf = Pf + (size_t)t * qq, *mf = Mf + (size_t)t * q;
+            if (chol_solve(q, W2, pp, q, pf, Lw) || chol_solve(q, W2, mp, 1, mf, Lw)) { nonfin = 1; break; }
+            memcpy(P, pf, sizeof(double) * qq);
+            memcpy(mv, mf, sizeof(double) * q);
+          }
+          /* Rauch-Tung-Striebel smoother */
+          memcpy(Ms + (size_t)(T - 1) * q, Mf + (size_t)(T - 1) * q, sizeof(double) * q);
+          for (int t = T - 2; t >= 0 && !nonfin; t--) {
+            const double *Jn = Jb + (size_t)(t + 1) * qq, *pf = Pf + (size_t)t * qq;
+            for (int i = 0; i < q; i++) {            /* W1 = J_{t+1} P_t */
+              for (int j = 0; j < q; j++) {
+                double a = 0.0;
+                for (int l = 0; l < q; l++) a += Jn[(size_t)i * q + l] * pf[(size_t)l * q + j];
+                W1[(size_t)i * q + j] = a;
+              }
+            }
+            /* G^T = (P^-_{t+1})^{-1} J_{t+1} P_t  (both covariances symmetric) */
+            if (chol_solve(q, Pp + (size_t)(t + 1) * qq, W1, q, W2, Lw)) { nonfin = 1; break; }
+            for (int i = 0; i < q; i++) v1[i] = Ms[(size_t)(t + 1) * q + i] - Mp[(size_t)(t + 1) * q + i];
+            for (int i = 0; i < q; i++) {
+              double a = Mf[(size_t)t * q + i];
+              for (int l = 0; l < q; l++) a += W2[(size_t)l * q + i] * v1[l];
+              Ms[(size_t)t * q + i] = a;
+            }
+          }
+          for (int t = 0; t < T; t++) {
+            for (int i = 0; i < q; i++) {
+              const double v = Ms[(size_t)t * q + i];
+              hb[(size_t)t * S + blk * q + i] += v;
+              const double a = fabs(v);
+              if (!isfinite(a)) nonfin = 1;
+              else if (a > delta) delta = a;
+            }
+          }
+        }
+      }
+      free(U); free(F); free(Jall); free(Jb); free(Rb); free(Pp); free(Mp); free(Pf); free(Mf); free(Ms);
+      free(W1); free(W2); free(W3); free(Lw); free(v1); free(v2); free(zero);
     }
     if (err) return ORC_ENOMEM;
     if (nonfin) delta = NAN;

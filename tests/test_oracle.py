@@ -745,3 +745,100 @@ def test_elk_reaches_the_rollout(cfg, kw):
     h, iters, status, dl = oracle.elk(p, 0.1, tol=1e-11, max_iters=p["T"])
     assert status == oracle.OK and iters < p["T"]
     np.testing.assert_allclose(h, oracle.rollout(p), rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# ELK: the damped (Levenberg-Marquardt) Newton step with the cell's own
+# Jacobian, as a Kalman smoother with full covariances
+# ---------------------------------------------------------------------------
+def _full_jacobian_and_residual(p, h):
+    """J_t as a dense S x S matrix ([B,T,S,S]) and r = f - h at the iterate h, via oracle.cell."""
+    B, T, S = h.shape
+    Jd, r = np.zeros((B, T, S, S)), np.zeros_like(h)
+    for b in range(B):
+        for t in range(T):
+            sp = p["h0"][b] if t == 0 else h[b, t - 1]
+            f, J = oracle.cell(p, sp, p["x"][b, t])
+            if p["cell"] == sy.CELL_GRU_DIAG:
+                Jd[b, t] = np.diag(J)
+            elif p["cell"] == sy.CELL_LSTM_CIFG_DIAG:
+                for c in range(p["n"]):
+                    Jd[b, t, 2 * c:2 * c + 2, 2 * c:2 * c + 2] = J[c]
+            else:
+                Jd[b, t] = J
+            r[b, t] = f - h[b, t]
+    return Jd, r
+
+
+def _damped_lsq_blocks(J, r, lam):
+    """argmin ||M z - r||^2 + lam ||z||^2 over z = (dh_0, ..., dh_{T-1}) with
+    (M z)_t = dh_t - J_t dh_{t-1}, by the normal equations (one sequence)."""
+    T, S = r.shape
+    M = np.eye(T * S)
+    for t in range(1, T):
+        M[t * S:(t + 1) * S, (t - 1) * S:t * S] = -J[t]
+    z = np.linalg.solve(M.T @ M + lam * np.eye(T * S), M.T @ r.reshape(-1))
+    return z.reshape(T, S)
+
+
+FULL_ELK_CELLS = [sy.CELL_TANH_RNN, sy.CELL_GRU, sy.CELL_LINEAR, sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG]
+
+
+@pytest.mark.parametrize("lam", [0.1, 1.0, 10.0])
+@pytest.mark.parametrize("cell", FULL_ELK_CELLS)
+def test_full_elk_step_solves_the_damped_least_squares(cell, lam):
+    # the Levenberg-Marquardt step by an independent route: the normal
+    # equations of the whole block-bidiagonal system, on small T
+    p = small_problem(cell, B=2, T=7, n=3)
+    h1, _, _, _ = oracle.elk_full(p, lam, tol=0.0, max_iters=1)
+    h2, _, _, _ = oracle.elk_full(p, lam, tol=0.0, max_iters=2)
+    for h_prev, h_next in ((np.zeros_like(h1), h1), (h1, h2)):
+        J, r = _full_jacobian_and_residual(p, h_prev)
+        for b in range(p["B"]):
+            np.testing.assert_allclose(h_next[b] - h_prev[b], _damped_lsq_blocks(J[b], r[b], lam), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cell", FULL_ELK_CELLS)
+def test_full_elk_without_damping_is_newton(cell):
+    p = small_problem(cell, T=30)
+    for k in (1, 2, 5):
+        he, _, _, de = oracle.elk_full(p, 0.0, tol=0.0, max_iters=k)
+        hn, _, _, dn = oracle.deer(p, tol=0.0, max_iters=k)
+        np.testing.assert_allclose(he, hn, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(de, dn, rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("cell,n", [(sy.CELL_GRU_DIAG, 4), (sy.CELL_GRU, 1), (sy.CELL_TANH_RNN, 1)])
+def test_full_elk_on_a_diagonal_jacobian_is_quasi_elk(cell, n):
+    # a diagonal Jacobian (the diagonal GRU, or any cell with one state entry)
+    # leaves nothing for the full covariances to couple
+    p = small_problem(cell, T=40, n=n)
+    for lam in (0.1, 2.0):
+        hf, itf, _, df = oracle.elk_full(p, lam, tol=0.0, max_iters=6)
+        hq, itq, _, dq = oracle.elk(p, lam, tol=0.0, max_iters=6)
+        np.testing.assert_allclose(hf, hq, rtol=0, atol=1e-13)
+
+
+def test_full_elk_step_norm_bound_and_stability():
+    # lam ||dh||^2 <= ||r||^2 per sequence (dh = 0 is a candidate); the
+    # damped steps stay bounded where Newton's grow to 1e10 and beyond
+    p = sy.custom_problem(sy.CELL_TANH_RNN, B=2, T=120, d=3, n=4, seed=3, w_scale=4.0, h0=True)
+    lam = 0.3
+    h_prev = np.zeros((p["B"], p["T"], p["S"]))
+    for k in range(1, 6):
+        h_next, _, _, _ = oracle.elk_full(p, lam, tol=0.0, max_iters=k)
+        _, r = _full_jacobian_and_residual(p, h_prev)
+        step = h_next - h_prev
+        assert np.all(lam * (step ** 2).sum((1, 2)) <= (r ** 2).sum((1, 2)) * (1 + 1e-12) + 1e-300)
+        h_prev = h_next
+    _, _, _, dl_newton = oracle.deer(p, tol=0.0, max_iters=60)
+    _, _, _, dl_elk = oracle.elk_full(p, lam, tol=0.0, max_iters=60)
+    assert dl_newton.max() > 1e10 and dl_elk.max() < 10
+
+
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (4, dict(T=128, n=16, d=16)), (3, dict(T=128, n=8, d=8))])
+def test_full_elk_reaches_the_rollout(cfg, kw):
+    p = sy.make_problem(cfg, **kw)
+    h, iters, status, dl = oracle.elk_full(p, 0.1, tol=1e-11, max_iters=p["T"])
+    assert status == oracle.OK and iters < p["T"]
+    np.testing.assert_allclose(h, oracle.rollout(p), rtol=0, atol=1e-10)
