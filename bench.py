@@ -32,6 +32,9 @@ ELK_KERNELS = ("quasi-ELK sweep: per-channel cells k_elkc_filter + k_elkc_filter
                "k_elkc_smooth_carry + k_elkc_apply (the cell re-evaluated in each pass); dense GRU "
                "k_d64_gates<GM_QUASI>, small dense cells k_time_elk_jr, then k_elk_filter/gains/apply and "
                "their chunk carries")
+ELK_FULL_KERNELS = ("ELK sweep (the cell's own Jacobian, full covariances): producer of J | r (k_elkf_jr_lstm or "
+                    "k_elkf_jr_dense), then k_elkf_elem (chunk filtering elements), k_elkf_fcarry, k_elkf_gains "
+                    "(in-chunk filter and smoother gains), k_elkf_scarry, k_elkf_apply")
 FP32_MFMA_PEAK_TFS = 157.3
 
 
@@ -231,7 +234,8 @@ def main() -> int:
                     help="Jacobian of the sweeps' linear solve: the cell's own (Newton), its diagonal "
                          "(quasi-DEER) or zero (Jacobi)")
     ap.add_argument("--elk", type=float, default=None, metavar="LAMBDA",
-                    help="solve with quasi-ELK at damping LAMBDA")
+                    help="solve with ELK at damping LAMBDA: the cell's own Jacobian (full covariances), or "
+                         "its diagonal (quasi-ELK) with --jac diag")
     ap.add_argument("--lsim", action="store_true",
                     help="time the linear state-space simulation workload (B=16, T=2^20, 4 states) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,7 +378,8 @@ def main() -> int:
         nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
         achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
-        kname = (ELK_KERNELS if elk else
+        kname = ((ELK_FULL_KERNELS if args.jac == "own" and not (p["cell"] == sy.CELL_GRU_DIAG or p["n"] == 1)
+                  else ELK_KERNELS) if elk else
                  "k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
                  "sweep's tile aggregates)" if chan else
                  ("k_pipe<SweepPol>" if scalar_path(p) and not approx else "k_time_sweep") +
@@ -416,7 +421,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": p["name"], "cell": sy.CELL_NAMES[p["cell"]], "B": B, "T": T, "d": p["d"],
                    "n": p["n"], "tol": p["tol"], "max_iters": p["max_iters"], "step": "solve + adjoint",
-                   "jacobian": ("diagonal, quasi-ELK damping %g" % args.elk) if elk else
+                   "jacobian": (("the cell's, ELK damping %g" if args.jac == "own" else
+                                 "diagonal, quasi-ELK damping %g") % args.elk) if elk else
                                {"own": "the cell's", "diag": "diagonal (quasi-DEER)", "zero": "zero (Jacobi)"}[args.jac]},
         "iters": iters,
         "final_delta": float(dl[-1]) if len(dl) else None,

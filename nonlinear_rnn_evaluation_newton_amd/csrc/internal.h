@@ -210,6 +210,27 @@ struct ElkChanArgs {  // per-channel cells (the smoother's e.r3 and e.msc are sh
   int n;
   int cpf, nchf;       // filter chunks per sequence and in all
 };
+// ELK with the cell's own Jacobian (full covariances per unit of N state
+// entries: each LSTM channel's (c, h), N = 2; a small dense cell's state, N =
+// n padded).  Per step [t][unit][N*N + N]: J_t | r_t (jr), then G_t | e_t (ge);
+// per (chunk, unit): the filtering element [3N^2 + 2N], (m, P) entering
+// [N + N^2], the reverse map Mr | vr [N^2 + N], m^s from the right [N].
+struct ElkFullArgs {
+  float *jr, *ge, *elem, *fin, *rev, *msin;
+  void *h;                              // iterate [B, T, S] (storage dtype)
+  const void *U, *h0, *Wh, *bh, *peep;  // the LSTM producer's inputs
+  int B, T, n, S;
+  int units, upb, NS;  // units, units per sequence, state entries per unit
+  int L, cpu;          // steps per chunk, chunks per unit
+  float lam;
+  int k;
+  float tol;
+  int max_iters;
+  SolveState *st;
+};
+int elk_full_chunk_len(int T);
+hipError_t launch_elk_full_lstm(bool bf16, const ElkFullArgs &a, hipStream_t s);
+hipError_t launch_elk_full_dense(int cell, int Nv, const TimeArgs &ta, const ElkFullArgs &a, hipStream_t s);
 int elk_chunk_len(int S);         // steps per chunk of the dense-family quasi-ELK scans
 int elk_lanes_per_chunk(int S);
 int elk_chan_chunk_len(int sw);

@@ -373,15 +373,56 @@ size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
 // Quasi-ELK scratch beyond a solve's workspace.  Dense n = 64 GRU: [G | e]
 // per step ([d | r] sits in the gates buffer), chunk aggregates and carries.
 // Per-channel cells: chunk aggregates, carries and boundary values only.
+// ELK with the cell's own Jacobian (full covariances): per step J | r and
+// G | e, per (chunk, unit) the filtering elements and carries.
 struct ElkLayout {
   size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
   size_t off_fagg = 0, off_fcar = 0, off_fsub = 0, off_dr = 0, off_hb = 0;
+  size_t off_elem = 0, off_fin = 0, off_rev = 0, off_msin = 0;
   size_t bytes = 0;
   int cps = 0, nch = 0, cpf = 0, nchf = 0;
+  bool full = false;           // the cell's own Jacobian (else its diagonal: quasi-ELK)
+  int Nf = 0, units = 0, L = 0, cpu = 0;
 };
+// Which ELK a problem asks for: the cell's own Jacobian gives ELK, the
+// diagonal quasi-ELK.  Where the own Jacobian is diagonal (the diagonal GRU,
+// a dense cell with one state entry) the two are the same and the quasi-ELK
+// kernels run.
+static int elk_kind(const pr_problem *p, const Plan &pl, bool *full) {
+  *full = false;
+  if (p->jac == PR_JAC_ZERO) return fail(PR_EINVAL, "ELK needs a Jacobian: jac must be the cell's own or PR_JAC_DIAG");
+  const bool own = (p->cell == PR_CELL_LSTM_CIFG_DIAG && p->jac == PR_JAC_BLOCK2) ||
+                   (pl.path != PATH_CHAN && p->jac == PR_JAC_DENSE && p->n > 1);
+  if (own && pl.path == PATH_D64)
+    return fail(PR_EUNSUPPORTED,
+                "ELK with the full 64 x 64 Jacobian is not built (its covariance updates cost O(n^3) per step); "
+                "jac = PR_JAC_DIAG runs quasi-ELK");
+  *full = own;
+  return PR_OK;
+}
 static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
   if (pl.path != PATH_D64 && pl.path != PATH_CHAN && pl.path != PATH_TIME)
     return fail(PR_EUNSUPPORTED, "no quasi-ELK kernels for this problem");
+  int rc = elk_kind(p, pl, &el->full);
+  if (rc != PR_OK) return rc;
+  if (el->full) {
+    const int N = pl.path == PATH_CHAN ? 2 : pl.N;
+    el->Nf = N;
+    el->units = pl.path == PATH_CHAN ? p->B * p->n : p->B;
+    el->L = elk_full_chunk_len(p->T);
+    el->cpu = (p->T + el->L - 1) / el->L;
+    if ((long long)el->units * el->cpu > 2147483647LL / 4) return fail(PR_EUNSUPPORTED, "problem too large");
+    const size_t steps = (size_t)p->T * el->units, pc = (size_t)el->cpu * el->units, NN = (size_t)N * N;
+    size_t o = pl.solve_bytes;
+    el->off_jr = o; o = align256(o + steps * (NN + N) * 4);
+    el->off_ge = o; o = align256(o + steps * (NN + N) * 4);
+    el->off_elem = o; o = align256(o + pc * (3 * NN + 2 * N) * 4);
+    el->off_fin = o; o = align256(o + pc * (NN + N) * 4);
+    el->off_rev = o; o = align256(o + pc * (NN + N) * 4);
+    el->off_msin = o; o = align256(o + pc * N * 4);
+    el->bytes = o;
+    return PR_OK;
+  }
   const size_t rows = (size_t)p->B * p->T, S = (size_t)pl.S;
   const int L = pl.path == PATH_CHAN ? elk_chan_chunk_len(p->cell == PR_CELL_LSTM_CIFG_DIAG ? 2 : 1)
                                       : elk_chunk_len(pl.S);
@@ -465,7 +506,7 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     if (!(*elk_lambda >= 0.f) || *elk_lambda > 3.0e38f) return fail(PR_EINVAL, "lambda must be >= 0 and finite");
     rc = elk_layout(p, pl, &el);
     if (rc != PR_OK) return rc;
-    pl.approx = APX_DIAG;  // the producer evaluates the Jacobian's diagonal
+    pl.approx = APX_DIAG;  // the quasi-ELK producers evaluate the Jacobian's diagonal
     pl.solve_bytes = el.bytes;
   }
   if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
@@ -564,7 +605,30 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
 
   ElkArgs ea{};
   ElkChanArgs eca{};
-  if (elk_lambda) {
+  ElkFullArgs fa{};
+  if (elk_lambda && el.full) {
+    fa.jr = (float *)(ws + el.off_jr);
+    fa.ge = (float *)(ws + el.off_ge);
+    fa.elem = (float *)(ws + el.off_elem);
+    fa.fin = (float *)(ws + el.off_fin);
+    fa.rev = (float *)(ws + el.off_rev);
+    fa.msin = (float *)(ws + el.off_msin);
+    fa.h = h;
+    fa.U = ws + pl.off_U;
+    fa.h0 = h0;
+    fa.Wh = w->W_h;
+    fa.bh = w->b_h;
+    fa.peep = w->peep;
+    fa.B = p->B; fa.T = p->T; fa.n = p->n; fa.S = pl.S;
+    fa.units = el.units;
+    fa.upb = pl.path == PATH_CHAN ? p->n : 1;
+    fa.NS = pl.path == PATH_CHAN ? 2 : p->n;
+    fa.L = el.L; fa.cpu = el.cpu;
+    fa.lam = *elk_lambda;
+    fa.tol = tol;
+    fa.max_iters = max_iters;
+    fa.st = (SolveState *)(ws + pl.off_state);
+  } else if (elk_lambda) {
     if (pl.path == PATH_D64 || pl.path == PATH_TIME) {
       ea.jr = (float *)(ws + el.off_jr);
       ea.ge = (float *)(ws + el.off_ge);
@@ -633,7 +697,11 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       a.k = kk;
       const bool ev = tr.on && per_sweep_events && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      if (elk_lambda) {  // the damped step
+      if (elk_lambda && el.full) {  // the damped step with the cell's own Jacobian
+        fa.k = kk;
+        if (pl.path == PATH_CHAN) HIPCHK(launch_elk_full_lstm(p->dtype == PR_BF16, fa, s));
+        else HIPCHK(launch_elk_full_dense(kc, pl.N, a, fa, s));
+      } else if (elk_lambda) {  // the damped step with the Jacobian's diagonal
         if (pl.path == PATH_D64) {  // producer of [d | r], then the scans
           da.k = kk;
           HIPCHK(launch_d64_sweep_part(da, 0, s));

@@ -192,3 +192,23 @@ def test_noalloc_scan_rejects_without_device():
     assert bd.scan_workspace_bytes(bd.PR_JAC_DIAG, B, T, n) > bd.NOALLOC_SCRATCH_BYTES
     assert L.pararnn_affine_scan_noalloc(bd.PR_JAC_DIAG, B, T, n, 0, v, v, v, None) == bd.PR_EWORKSPACE
     assert "static scratch" in bd.last_error()
+
+
+def test_elk_workspace_follows_the_jacobian():
+    """pararnn_solve_elk takes the cell's own Jacobian (ELK) or its diagonal
+    (quasi-ELK); ELK on the 64 x 64 GRU and ELK without a Jacobian are
+    refused before any HIP call."""
+    L = bd.lib()
+    P = bd.make_problem
+    lstm_full = bd.elk_workspace_bytes(P(sy.CELL_LSTM_CIFG_DIAG, sy.JAC_BLOCK2, bd.PR_BF16, 4, 8192, 2048, 2048))
+    lstm_quasi = bd.elk_workspace_bytes(P(sy.CELL_LSTM_CIFG_DIAG, sy.JAC_DIAG, bd.PR_BF16, 4, 8192, 2048, 2048))
+    assert lstm_full > lstm_quasi > 0
+    assert bd.elk_workspace_bytes(P(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 256, 2, 4)) > 0
+    assert bd.elk_workspace_bytes(P(sy.CELL_GRU, sy.JAC_DIAG, bd.PR_F32, 16, 16384, 32, 64)) > 0
+    for pb, code in ((P(sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 16, 16384, 32, 64), bd.PR_EUNSUPPORTED),
+                     (P(sy.CELL_GRU, sy.JAC_ZERO, bd.PR_F32, 2, 64, 3, 4), bd.PR_EINVAL)):
+        assert bd.elk_workspace_bytes(pb) == 0
+        w = bd.Weights(1, None, 1, None, None)
+        rc = L.pararnn_solve_elk(C.byref(pb), C.byref(w), C.c_void_p(16), None, 0.1, 1e-6, 8, C.c_void_p(16), None,
+                                 None, 0, C.c_void_p(256), 1 << 40, None)
+        assert rc == code, bd.last_error()

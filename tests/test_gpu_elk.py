@@ -1,7 +1,10 @@
-"""GPU parity of the quasi-ELK solve (pararnn_solve_elk: the damped
+"""GPU parity of the ELK solves (pararnn_solve_elk: the damped Newton or
 quasi-Newton step as a Kalman smoother, run as parallel scans) against the
-fp64 oracle's quasi-ELK, through the C ABI: the dense n = 64 GRU and the
-per-channel cells in fp32 and bf16 storage, with and without damping.
+fp64 oracle, through the C ABI.  Quasi-ELK (jac = PR_JAC_DIAG): the dense
+n = 64 GRU, the small dense cells and the per-channel cells in fp32 and bf16
+storage.  ELK with the cell's own Jacobian (full covariances): the small
+dense cells (n <= 8) and the 2x2-block LSTM in fp32 and bf16.  With and
+without damping.
 
 Damped sweeps converge linearly; as for the other approximate sweeps, where
 the oracle's deciding delta lies within fp32 noise of tol the GPU may stop
@@ -40,19 +43,29 @@ def to64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def check(p, lam, tol, max_iters, bf16=False):
-    say("case", p["name"], "lambda", lam, "B", p["B"], "T", p["T"], "n", p["n"], "tol", tol, "max_iters", max_iters,
-        "bf16", bf16)
+def quasi(p):
+    """The problem with the Jacobian's diagonal (quasi-ELK)."""
+    return dict(p, jac=sy.JAC_DIAG)
+
+
+def check(p, lam, tol, max_iters, bf16=False, full=False):
+    """full: ELK with the cell's own Jacobian (p keeps its natural jac);
+    else quasi-ELK (the diagonal)."""
+    if not full:
+        p = quasi(p)
+    ref = oracle.elk_full if full else oracle.elk
+    say("case", p["name"], "full" if full else "quasi", "lambda", lam, "B", p["B"], "T", p["T"], "n", p["n"], "tol",
+        tol, "max_iters", max_iters, "bf16", bf16)
     dp = bd.DeviceProblem(p, elk=True)
     st, it, dl = dp.solve_elk(lam, tol=tol, max_iters=max_iters, hist_cap=4096)
     torch.cuda.synchronize()
     h = to64(dp.h)
-    ho, ito, sto, dlo = oracle.elk(p, lam, tol=tol, max_iters=max_iters)
+    ho, ito, sto, dlo = ref(p, lam, tol=tol, max_iters=max_iters)
     say("  gpu iters", it, "status", st, "| oracle", ito, sto, "last deltas", dl[-3:], dlo[-3:])
     if it != ito:
         k = min(it, ito)
         assert abs(it - ito) == 1 and tol > 0 and abs(dlo[k - 1] - tol) <= max(TOL_MARGIN * tol, TOL_NOISE)
-        ho, ito, sto, dlo = oracle.elk(p, lam, tol=0.0, max_iters=it)
+        ho, ito, sto, dlo = ref(p, lam, tol=0.0, max_iters=it)
     else:
         assert st == sto
     m = min(len(dl), len(dlo))
@@ -100,7 +113,7 @@ def test_dense64_full_size():
     at full size; h of two sampled sequences against the oracle's quasi-ELK
     iterate at the GPU's sweep count."""
     gold = json.load(open(os.path.join(GOLDEN, "dense64_gru_elk_full_history.json")))
-    p = sy.make_problem(5, with_g=False)
+    p = quasi(sy.make_problem(5, with_g=False))
     lam = gold["lambda"]
     say("case dense64 quasi-ELK full size, lambda", lam)
     dp = bd.DeviceProblem(p, elk=True)
@@ -127,7 +140,7 @@ def test_channel_full_size_sampled(cfg):
     0.1) in the benchmark's configuration; the oracle checks 12 sampled
     channels (first, last and random ones)."""
     lam = 0.1
-    p = sy.make_problem(cfg, with_g=False)
+    p = quasi(sy.make_problem(cfg, with_g=False))
     say("full-size case", p["name"], "quasi-ELK lambda", lam)
     dp = bd.DeviceProblem(p, elk=True)
     st, it, dl = dp.solve_elk(lam)
@@ -179,7 +192,7 @@ def test_small_dense_full_size_scalar_gru():
     """The scalar GRU workload's shape (B=16, T=2^20) with quasi-ELK: two
     sequences of the result against the oracle's quasi-ELK at the same sweep
     count."""
-    p = sy.make_problem(2, with_g=False)
+    p = quasi(sy.make_problem(2, with_g=False))
     lam = 0.1
     say("case scalar GRU full size, quasi-ELK lambda", lam)
     dp = bd.DeviceProblem(p, elk=True)
@@ -198,9 +211,102 @@ def test_small_dense_full_size_scalar_gru():
 def test_unsupported_and_invalid():
     prob = bd.make_problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)
     assert bd.elk_workspace_bytes(prob) == 0  # no kernels for n = 16 at all
-    q = sy.make_problem(5, B=1, T=64)
+    # ELK with the full 64 x 64 Jacobian is not built; without a Jacobian ELK is undefined
+    assert bd.elk_workspace_bytes(bd.make_problem(sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 1, 64, 32, 64)) == 0
+    assert bd.elk_workspace_bytes(bd.make_problem(sy.CELL_GRU, sy.JAC_ZERO, bd.PR_F32, 1, 64, 3, 4)) == 0
+    q = quasi(sy.make_problem(5, B=1, T=64))
     dp = bd.DeviceProblem(q, elk=True)
     st, _, _ = dp.solve_elk(-1.0, check=False)
     assert st == bd.PR_EINVAL
     st, _, _ = dp.solve_elk(float("nan"), check=False)
     assert st == bd.PR_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# ELK with the cell's own Jacobian (full covariances)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lam", [0.0, 0.3, 3.0])
+@pytest.mark.parametrize("cell,n,d,T", [(sy.CELL_TANH_RNN, 4, 2, 300), (sy.CELL_GRU, 3, 2, 257),
+                                        (sy.CELL_GRU, 2, 3, 1), (sy.CELL_TANH_RNN, 8, 5, 65),
+                                        (sy.CELL_LINEAR, 4, 3, 100), (sy.CELL_GRU, 6, 4, 40)])
+def test_full_elk_small_dense(lam, cell, n, d, T):
+    """Dense Jacobians (n x n, padded to 2, 4 or 8), h0 and biases."""
+    p = sy.custom_problem(cell, B=2, T=T, d=d, n=n, seed=10 * n + T, w_scale=0.8, h0=True)
+    for k in (1, 3):
+        check(p, lam, 0.0, k, full=True)
+    if cell != sy.CELL_LINEAR or lam > 0:
+        check(p, lam, 1e-5, T, full=True)
+
+
+def test_full_elk_tanh_rnn_workload():
+    """The dense tanh RNN workload (B=2, T=256, n=4) to tolerance."""
+    p = sy.make_problem(1)
+    check(p, 0.1, p["tol"], p["max_iters"], full=True)
+
+
+@pytest.mark.parametrize("T", [3000, 20000])
+def test_full_elk_small_dense_long(T):
+    """Long sequences: many chunks (and longer chunks past 256 of them) in
+    the filter and smoother carries."""
+    p = sy.custom_problem(sy.CELL_GRU, B=2, T=T, d=2, n=3, seed=T, w_scale=0.8, h0=True)
+    check(p, 0.3, 0.0, 3, full=True)
+    check(p, 0.3, 1e-5, T, full=True)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3, 3.0])
+@pytest.mark.parametrize("n,d,T", [(64, 16, 200), (5, 3, 77), (130, 40, 300), (7, 9, 1), (66, 12, 65)])
+def test_full_elk_lstm_fp32(lam, n, d, T):
+    """The LSTM's 2x2 blocks per channel, fp32 storage."""
+    p = sy.custom_problem(sy.CELL_LSTM_CIFG_DIAG, B=2, T=T, d=d, n=n, seed=n + T, w_scale=0.8, h0=True)
+    for k in (1, 3):
+        check(p, lam, 0.0, k, full=True)
+    if lam < 1.0:
+        check(p, lam, 1e-5, T, full=True)
+
+
+def test_full_elk_lstm_long():
+    """Length 9000: 141 chunks of 64 steps per channel."""
+    p = sy.custom_problem(sy.CELL_LSTM_CIFG_DIAG, B=2, T=9000, d=12, n=66, seed=5, w_scale=0.8, h0=True)
+    check(p, 0.3, 0.0, 3, full=True)
+    check(p, 0.3, 1e-5, p["T"], full=True)
+
+
+def test_full_elk_lstm_bf16():
+    p = sy.custom_problem(sy.CELL_LSTM_CIFG_DIAG, B=3, T=500, d=24, n=96, seed=4, w_scale=0.8, h0=True,
+                          dtype=sy.DT_BF16)
+    check(p, 0.3, 0.0, 6, bf16=True, full=True)
+
+
+def test_full_elk_lstm_full_size_sampled():
+    """The full ParaLSTM workload (B=4, T=8192, d=n=2048, bf16, 4 fixed
+    sweeps) with ELK (lambda 0.1) in the benchmark's configuration; the
+    oracle's ELK checks 12 sampled channels."""
+    lam = 0.1
+    p = sy.make_problem(4, with_g=False)
+    say("full-size case", p["name"], "ELK lambda", lam)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, dl = dp.solve_elk(lam)
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK and it == p["max_iters"]
+    rng = np.random.default_rng(400)
+    n = p["n"]
+    ch = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 10, replace=False)]))
+    rows = np.concatenate([g * n + ch for g in range(3)])
+    sidx = np.stack([2 * ch, 2 * ch + 1], 1).reshape(-1)
+    qs = dict(p, n=len(ch), S=len(sidx), W_x=p["W_x"][rows], b_x=p["b_x"][rows], W_h=p["W_h"][rows],
+              b_h=p["b_h"][rows], peep=np.concatenate([p["peep"][ch], p["peep"][n + ch]]), h0=p["h0"][:, sidx])
+    hq, *_ = oracle.elk_full(qs, lam, tol=p["tol"], max_iters=p["max_iters"])
+    hg = to64(dp.h[:, :, torch.as_tensor(sidx, device="cuda")])
+    r = float(np.abs(hg - hq).max() / max(np.abs(hq).max(), 1e-30))
+    say("  sampled channels", ch, "rel err", r)
+    assert r <= RTOL_BF
+
+
+def test_full_elk_damping_keeps_steps_bounded():
+    # a tanh RNN with strongly expanding dense recurrent weights: Newton's
+    # steps grow past 1e10 before the prefix fixes them; ELK's stay small
+    p = sy.custom_problem(sy.CELL_TANH_RNN, B=2, T=120, d=3, n=4, seed=3, w_scale=4.0, h0=True)
+    _, _, _, dl_newton = oracle.deer(p, tol=0.0, max_iters=30)
+    assert dl_newton.max() > 1e10
+    dl = check(p, 0.3, 0.0, 30, full=True)
+    assert np.max(dl) < 10.0
