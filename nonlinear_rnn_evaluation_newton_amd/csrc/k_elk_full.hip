@@ -648,8 +648,11 @@ __global__ __launch_bounds__(256) void k_elkf_apply(const ElkFullArgs a) {
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
+// Steps per chunk: about sqrt(T) (the chunk passes walk L steps, the carries
+// T / L chunks), at least 8, and at most 256 chunks per unit.
 int elk_full_chunk_len(int T) {
-  int L = 32;
+  int L = 8;
+  while (L * L < T) L *= 2;
   while ((T + L - 1) / L > 256) L *= 2;
   return L;
 }
