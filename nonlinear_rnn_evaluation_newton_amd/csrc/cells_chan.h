@@ -19,10 +19,14 @@ namespace pr {
 
 struct ChanW {  // per-channel weights (fp32)
   float a0, a1, a2;  // GRU: a_r, a_z, a_n   LSTM: w_f, w_g, w_o
-  float b0, b1, b2;  // recurrent biases of the three gates
+  float b0, b1, b2;  // recurrent biases of the three gates (only the GRU's b2 = b_hn is read: the others are in U)
   float p0, p1;      // LSTM peepholes p_f, p_o
 };
 
+// U holds the input projection W_x x + b_x plus the recurrent biases of the
+// gates whose pre-activation is a plain sum (the LSTM's f, g and o, the GRU's
+// r and z), folded in once per solve; the GRU's b_hn stays inside r * (.).
+//
 // f and J at state s (SW values) with projection U (3 gates).  CELL carries
 // the approximation in its upper bits (cell_apx): the LSTM's diagonal keeps
 // dc'/dc and dh'/dh; zero drops every entry.
@@ -30,8 +34,8 @@ template <int CELL>
 __device__ inline void chan_cell(const float *s, const float *U, const ChanW &w, float *f, float *J) {
   if constexpr (cell_code(CELL) == C_GRU_DIAG) {
     const float h = s[0];
-    const float r = fsigm(fmaf(w.a0, h, U[0] + w.b0));
-    const float z = fsigm(fmaf(w.a1, h, U[1] + w.b1));
+    const float r = fsigm(fmaf(w.a0, h, U[0]));
+    const float z = fsigm(fmaf(w.a1, h, U[1]));
     const float q = fmaf(w.a2, h, w.b2);
     const float c = ftanh(fmaf(r, q, U[2]));
     f[0] = fmaf(z, h - c, c);
@@ -39,10 +43,10 @@ __device__ inline void chan_cell(const float *s, const float *U, const ChanW &w,
     J[0] = z + (h - c) * z * (1.f - z) * w.a1 + be * r * (w.a2 + q * (1.f - r) * w.a0);
   } else {  // C_LSTM
     const float c = s[0], h = s[1];
-    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0] + w.b0)));
-    const float g = ftanh(fmaf(w.a1, h, U[1] + w.b1));
+    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0])));
+    const float g = ftanh(fmaf(w.a1, h, U[1]));
     const float cn = fmaf(fg, c - g, g);
-    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2] + w.b2)));
+    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2])));
     const float tc = ftanh(cn);
     f[0] = cn;
     f[1] = o * tc;
@@ -73,8 +77,8 @@ __device__ inline void chan_cell_vjp(const float *s, const float *U, const float
                                      float *dU, float *acc) {
   if constexpr (CELL == C_GRU_DIAG) {
     const float h = s[0];
-    const float r = fsigm(fmaf(w.a0, h, U[0] + w.b0));
-    const float z = fsigm(fmaf(w.a1, h, U[1] + w.b1));
+    const float r = fsigm(fmaf(w.a0, h, U[0]));
+    const float z = fsigm(fmaf(w.a1, h, U[1]));
     const float q = fmaf(w.a2, h, w.b2);
     const float c = ftanh(fmaf(r, q, U[2]));
     const float l = lam[0];
@@ -94,10 +98,10 @@ __device__ inline void chan_cell_vjp(const float *s, const float *U, const float
     acc[5] += dq;
   } else {
     const float c = s[0], h = s[1];
-    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0] + w.b0)));
-    const float g = ftanh(fmaf(w.a1, h, U[1] + w.b1));
+    const float fg = fsigm(fmaf(w.a0, h, fmaf(w.p0, c, U[0])));
+    const float g = ftanh(fmaf(w.a1, h, U[1]));
     const float cn = fmaf(fg, c - g, g);
-    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2] + w.b2)));
+    const float o = fsigm(fmaf(w.a2, h, fmaf(w.p1, cn, U[2])));
     const float tc = ftanh(cn);
     const float lc = lam[0], lh = lam[1];
     const float dao = lh * tc * o * (1.f - o);

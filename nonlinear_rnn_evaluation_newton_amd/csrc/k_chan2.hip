@@ -64,6 +64,17 @@ __device__ inline void bst(Rsrc r, unsigned off, const float *in) {
   }
 }
 
+// Store CNT values that are already exact in ST (bf16 values rounded by
+// as_stored): a bf16 pair packs with one byte permute of the two high halves.
+template <typename ST, int CNT>
+__device__ inline void bst_exact(Rsrc r, unsigned off, const float *in) {
+  if constexpr (sizeof(ST) == 2 && CNT == 2) {
+    st_u32(r, off, __builtin_amdgcn_perm(__float_as_uint(in[1]), __float_as_uint(in[0]), 0x07060302u));
+  } else {
+    bst<ST, CNT>(r, off, in);
+  }
+}
+
 // the value a float takes once stored as ST
 template <typename ST>
 __device__ inline float as_stored(float v) {
@@ -137,15 +148,19 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
     // Offsets carry bit 31 for idle lanes (outside every resource); rows past
     // the tile or past T lie outside the tile's resources.  No selects or
     // branches sit between the loads, so they all stay in flight.
+    // The lane parts of the offsets (with the idle bit) are formed once; each
+    // access adds its row's wave-uniform part (one add; the sum stays below
+    // 2^32 and keeps bit 31).
     const unsigned lane_oob = active ? 0u : SC_OOB;
+    const unsigned ulane = (unsigned)(c0 * ES) | lane_oob, hlane = (unsigned)(c0 * SW * ES) | lane_oob;
     unsigned ua[C2_P][3][UW], ha[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW];
     auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
         const int s = g * C2_P + q;
 #pragma unroll
-        for (int gi = 0; gi < 3; gi++) bldw<CPL * ES>(ru, (unsigned)((s * 3 * n + gi * n + c0) * ES) | lane_oob, u[q][gi]);
-        bldw<CPL * SW * ES>(rh, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, h[q]);
+        for (int gi = 0; gi < 3; gi++) bldw<CPL * ES>(ru, ulane + (unsigned)((s * 3 * n + gi * n) * ES), u[q][gi]);
+        bldw<CPL * SW * ES>(rh, hlane + (unsigned)(s * S * ES), h[q]);
       }
     };
     // FULL: every lane active and every step inside [0, T) (all tiles but a
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
 #pragma unroll
           for (int i = 0; i < SW; i++) s_new[c * SW + i] = hn[c * SW + i];
         }
-        if constexpr (APPLY) bst<ST, CPL * SW>(rw, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, hn);
+        if constexpr (APPLY) bst_exact<ST, CPL * SW>(rw, hlane + (unsigned)(s * S * ES), hn);
       }
     };
     auto walk = [&](auto full) __attribute__((always_inline)) {
@@ -433,6 +448,8 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
   const bool active = c0 < n;
   const int L = stripe * a.tps + j, t0 = j * TT, nrows = min(TT, T - t0);
   const unsigned lane_oob = active ? 0u : SC_OOB;
+  // lane parts of the offsets with the idle bit, formed once (see k_chan_pass)
+  const unsigned ulane = (unsigned)(c0 * ES) | lane_oob, slane = (unsigned)(c0 * SW * ES) | lane_oob;
   ChanW w[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
@@ -481,9 +498,9 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
     for (int q = 0; q < C2_P; q++) {
       const int s = TT - 1 - (gi * C2_P + q);  // negative past the tile: outside every resource
 #pragma unroll
-      for (int k3 = 0; k3 < 3; k3++) bldw<CPL * ES>(ru, (unsigned)((s * 3 * n + k3 * n + c0) * ES) | lane_oob, u[q][k3]);
-      bldw<CPL * SW * ES>(rh, (unsigned)(((s - hsh) * S + c0 * SW) * ES) | lane_oob, h[q]);
-      bldw<CPL * SW * ES>(rg, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, g[q]);
+      for (int k3 = 0; k3 < 3; k3++) bldw<CPL * ES>(ru, ulane + (unsigned)((s * 3 * n + k3 * n) * ES), u[q][k3]);
+      bldw<CPL * SW * ES>(rh, slane + (unsigned)((s - hsh) * S * ES), h[q]);
+      bldw<CPL * SW * ES>(rg, slane + (unsigned)(s * S * ES), g[q]);
     }
   };
   auto steps = [&](int gi, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW],
@@ -542,9 +559,9 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
         }
       }
       if constexpr (APPLY) {
-        bst<ST, CPL * SW>(rl, (unsigned)((s * S + c0 * SW) * ES) | lane_oob, lo);
+        bst<ST, CPL * SW>(rl, slane + (unsigned)(s * S * ES), lo);
 #pragma unroll
-        for (int k3 = 0; k3 < 3; k3++) bst<ST, CPL>(rd, (unsigned)((s * 3 * n + k3 * n + c0) * ES) | lane_oob, du[k3]);
+        for (int k3 = 0; k3 < 3; k3++) bst<ST, CPL>(rd, ulane + (unsigned)((s * 3 * n + k3 * n) * ES), du[k3]);
         if (t0 + s == 0 && a.dh0 && active) {
 #pragma unroll
           for (int i = 0; i < CPL * SW; i++) stf((ST *)a.dh0 + (size_t)b * S + (size_t)c0 * SW + i, 0, dso[i]);

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     for (int j = 0; j < 2; j++) {
       const int col = n0 + wn * 64 + j * 32 + (lane & 31);
       if (col >= g.N) continue;
-      const float bias = (g.bias && split == 0) ? ldf((const T *)g.bias, col) : 0.f;
+      const float bias = split != 0 ? 0.f : g.bias32 ? g.bias32[col] : g.bias ? ldf((const T *)g.bias, col) : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -351,7 +351,9 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
       const int n = n0 + wn * (FN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
 #pragma unroll
       for (int c = 0; c < 4; c++)
-        bias[j][rg][c] = (g.bias && split == 0 && n + c < g.N) ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
+        bias[j][rg][c] = (split != 0 || n + c >= g.N) ? 0.f
+                         : g.bias32 ? g.bias32[n + c]
+                         : g.bias ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
     }
 #pragma unroll
   for (int i = 0; i < FM; i++) {

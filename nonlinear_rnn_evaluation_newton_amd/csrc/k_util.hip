@@ -21,6 +21,26 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename ST>
+__global__ void k_fold_bias(const ST *bx, const ST *bh, int n, int folded, float *out) {
+  const int total = 3 * n;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const float v = bx ? ldf(bx, i) : 0.f;
+    out[i] = (bh && i / n < folded) ? v + ldf(bh, i) : v;
+  }
+}
+
+hipError_t launch_fold_bias(bool bf16, const void *bx, const void *bh, int n, int folded, float *out, hipStream_t s) {
+  const int blocks = (3 * n + 255) / 256 < 1024 ? (3 * n + 255) / 256 : 1024;
+  if (bf16)
+    hipLaunchKernelGGL(k_fold_bias<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t *)bx,
+                       (const uint16_t *)bh, n, folded, out);
+  else
+    hipLaunchKernelGGL(k_fold_bias<float>, dim3(blocks), dim3(256), 0, s, (const float *)bx, (const float *)bh, n,
+                       folded, out);
+  return hipGetLastError();
+}
+
 // dst[c][r] = src[r][c] for a row-major [R, C] matrix of 2- or 4-byte
 // elements, through 64 x 64 LDS tiles (coalesced reads along C and writes
 // along R).  Turns the K-outer operands of the adjoint's products into the

@@ -57,6 +57,7 @@ struct Plan {
   int tps_2 = 0, ntiles_2 = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
+  size_t off_cb = 0;              // channel path: the projection's fp32 bias with the folded recurrent biases
   size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
   size_t off_red = 0;             // channel path adjoint: fp64 split sums of the weight partials
   size_t off_tn = 0;              // dense n = 64 adjoint: partials of the K-outer weight products
@@ -190,6 +191,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_incl = o; o = align256(o + nt * g.CH * SW * 4);
     pl->off_bnd = o; o = align256(o + (size_t)2 * nt * g.CH * SW * 4);
     pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
+    pl->off_cb = o; o = align256(o + (size_t)3 * p->n * 4);
     pl->solve_bytes = o;
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
     pl->off_part = o; o = align256(o + nt * g.CH * 11 * 4);
@@ -205,12 +207,23 @@ int make_plan(const pr_problem *p, Plan *pl) {
               p->d);
 }
 
-// U = x W_x^T + b_x on MFMA ([B*T, d] x [3n, d]^T).
-hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void *x, void *U, hipStream_t s) {
+// U = x W_x^T + b_x on MFMA ([B*T, d] x [3n, d]^T).  For the per-channel
+// cells (cb non-null) the bias also takes the recurrent biases of the gates
+// whose pre-activation is a plain sum (the LSTM's three, the GRU's r and z),
+// summed in fp32 into cb: the cells then add no bias per step.
+hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void *x, void *U, hipStream_t s,
+                            float *cb = nullptr) {
   const bool bf = p->dtype == PR_BF16;
   const size_t es = bf ? 2 : 4;
   GemmArgs g{};
   g.A = x; g.B = w->W_x; g.C = U; g.bias = w->b_x; g.ws = nullptr;
+  if (cb) {
+    const hipError_t e =
+        launch_fold_bias(bf, w->b_x, w->b_h, p->n, p->cell == PR_CELL_LSTM_CIFG_DIAG ? 3 : 2, cb, s);
+    if (e != hipSuccess) return e;
+    g.bias = nullptr;
+    g.bias32 = cb;
+  }
   g.M = p->B * p->T; g.N = gates_of(p->cell) * p->n; g.K = p->d;
   g.lda = p->d; g.ldb = p->d; g.ldc = g.N; g.splits = 1;
   g.a_kc = true; g.b_kc = true; g.bf16 = bf; g.out_f32 = !bf;
@@ -594,7 +607,7 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     ca.tps = pl.tps_2;
     ca.ntiles = pl.ntiles_2;
     const int ti = tr.begin(TR_PROJ, s);
-    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s, (float *)(ws + pl.off_cb)));
     tr.end(TR_PROJ, ti, s);
   }
   const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : kcell(p->cell);
@@ -966,7 +979,7 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
     Trace &tr = trace();
     const int tp = tr.begin(TR_PROJ, s);
-    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s, (float *)(ws + pl.off_cb)));
     tr.end(TR_PROJ, tp, s);
     ChanArgs ca{};
     ca.U = ws + pl.off_U;
