@@ -208,7 +208,8 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
  * pararnn_solve followed by pararnn_adjoint at the returned trajectory, in
  * one call (a training step's forward and backward evaluation; DEER summary,
  * Surprising findings: the gradient costs one more linear solve).  Results
- * are those of the two calls.  The adjoint is enqueued right behind the
+ * are those of the two calls; the adjoint reuses the input projection U the
+ * solve left in the workspace instead of computing it again.  The adjoint is enqueued right behind the
  * solve's first batch of sweeps, before the host waits for its convergence
  * poll, when that batch is sure to be the last (tol <= 0: a fixed number of
  * sweeps) or, for n = d = 1, when the previous call on the same problem,

@@ -507,6 +507,10 @@ static SpecMemo &spec_memo() {
   return m;
 }
 
+static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
+                        const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
+                        size_t ws_bytes, void *stream, bool u_ready);
+
 static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
                       int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
                       size_t ws_bytes, void *stream, const float *elk_lambda, SpecAdjoint *spec = nullptr) {
@@ -756,8 +760,8 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     hipEvent_t poll_ev = poll_event();
     if (poll_ev) HIPCHK(hipEventRecord(poll_ev, s));
     if (speculate && k == 1) {
-      spec->rc = pararnn_adjoint(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
-                                 ws_bytes, stream);
+      spec->rc = adjoint_impl(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
+                              ws_bytes, stream, true);
       spec_enqueued = spec->rc >= 0;
     }
     HIPCHK(poll_ev ? hipEventSynchronize(poll_ev) : hipStreamSynchronize(s));
@@ -851,6 +855,17 @@ int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, c
 int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                     const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
                     size_t ws_bytes, void *stream) {
+  return adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, false);
+}
+
+}  // extern "C"
+
+// The adjoint; u_ready: the workspace already holds this problem's input
+// projection U (a solve on the same workspace and inputs has just computed
+// it, as in pararnn_solve_adjoint), so it is not recomputed.
+static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
+                        const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
+                        size_t ws_bytes, void *stream, bool u_ready) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, &pl);
@@ -912,9 +927,11 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
       return fail(PR_EINVAL, "h, h0, g and W_h must be 16-byte aligned for n = 64");
     if (!lambda) return fail(PR_EINVAL, "the dense n = 64 adjoint needs the lambda output buffer");
     Trace &tr = trace();
-    const int tp = tr.begin(TR_PROJ, s);
-    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
-    tr.end(TR_PROJ, tp, s);
+    if (!u_ready) {
+      const int tp = tr.begin(TR_PROJ, s);
+      HIPCHK(input_projection(p, w, x, ws + pl.off_U, s));
+      tr.end(TR_PROJ, tp, s);
+    }
     D64Args da{};
     da.U = (const float *)(ws + pl.off_U);
     da.h = (float *)h;
@@ -978,9 +995,11 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
     const size_t es = bf ? 2 : 4;
     const int kc = p->cell == PR_CELL_GRU_DIAG ? C_GRU_DIAG : C_LSTM;
     Trace &tr = trace();
-    const int tp = tr.begin(TR_PROJ, s);
-    HIPCHK(input_projection(p, w, x, ws + pl.off_U, s, (float *)(ws + pl.off_cb)));
-    tr.end(TR_PROJ, tp, s);
+    if (!u_ready) {
+      const int tp = tr.begin(TR_PROJ, s);
+      HIPCHK(input_projection(p, w, x, ws + pl.off_U, s, (float *)(ws + pl.off_cb)));
+      tr.end(TR_PROJ, tp, s);
+    }
     ChanArgs ca{};
     ca.U = ws + pl.off_U;
     ca.h = (void *)h;
@@ -1040,6 +1059,8 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
 }
 
+extern "C" {
+
 int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
                           int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
                           void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
@@ -1058,7 +1079,7 @@ int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *
   if (sa.done) return sa.rc < 0 ? sa.rc : rc;
   if (sa.rc < 0) return sa.rc;  // the speculative enqueue was rejected: the same arguments fail again
   if (rc == PR_NONFINITE) return rc;
-  const int ra = pararnn_adjoint(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream);
+  const int ra = adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, true);
   return ra < 0 ? ra : rc;
 }
 
