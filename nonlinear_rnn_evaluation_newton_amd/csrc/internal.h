@@ -152,6 +152,7 @@ struct GemmArgs {
   void *C;              // [M,N] row stride ldc
   const void *bias;     // [N] or null (input dtype)
   const float *bias32;  // [N] fp32 or null: used instead of bias when set
+  const float *scale32; // [N] fp32 or null: C = scale * (A B^T) + bias per column
   float *ws;            // split-K workspace [splits][M][N]
   int M, N, K, lda, ldb, ldc, splits;
   bool a_kc, b_kc, bf16, out_f32, vec_a, vec_b;
@@ -166,10 +167,12 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
 // ---------------- utilities ------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
-// fp32 bias of the per-channel cells' input projection, [3n]: b_x plus the
-// recurrent biases of the first `folded` gates (their pre-activations are
-// plain sums: LSTM f, g, o; GRU r, z).  Either bias may be null (= 0).
-hipError_t launch_fold_bias(bool bf16, const void *bx, const void *bh, int n, int folded, float *out, hipStream_t s);
+// Epilogue of the per-channel cells' input projection, fp32 [6n]: [0, 3n) the
+// bias, b_x plus the recurrent biases of the gates whose pre-activations are
+// plain sums (LSTM f, g, o; GRU r, z), and [3n, 6n) the column scale, each
+// gate's chan_gate_scale; the bias is stored scaled.  Either bias may be null
+// (= 0).  cell is C_GRU_DIAG or C_LSTM.
+hipError_t launch_fold_bias(bool bf16, const void *bx, const void *bh, int n, int cell, float *out, hipStream_t s);
 // dst [C, R] = transpose of row-major src [R, C]; elem_bytes 2 or 4
 hipError_t launch_transpose(const void *src, void *dst, int R, int C, int elem_bytes, hipStream_t s);
 

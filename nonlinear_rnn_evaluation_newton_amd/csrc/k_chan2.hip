@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
     const int L = stripe * a.tps + j, t0 = j * TT, nrows = min(TT, T - t0);
     ChanW w[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST, CELL>(a, active ? c0 + c : 0);
 
     // the tile's rows; the iterate is read from sweep 2 on (sweep 1 starts from 0)
     const size_t row0 = (size_t)b * T + t0;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_carry(const ChanArgs a) {
   const int j0 = min(nt, wid * per), j1 = min(nt, j0 + per);
   ChanW w[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST, CELL>(a, active ? c0 + c : 0);
   const ST *U = (const ST *)a.U, *H = (const ST *)a.h;
   float *pagg = (float *)a.agg;
   float *carry = (float *)a.incl;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
   const unsigned ulane = (unsigned)(c0 * ES) | lane_oob, slane = (unsigned)(c0 * SW * ES) | lane_oob;
   ChanW w[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST>(a, active ? c0 + c : 0);
+  for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST, CELL>(a, active ? c0 + c : 0);
 
   // rows of the tile: U_t and g_t at [t0, t0 + nrows); h_{t-1} from the row
   // before (the first tile's step 0 takes h0 instead: its row offset is -1,

@@ -257,7 +257,7 @@ __device__ inline void chan_lookback(const Op<SW> (&tot)[CPL], int j, int k, boo
   }
 }
 
-template <typename ST>
+template <typename ST, int CELL>
 __device__ inline ChanW load_chan_w(const ChanArgs &a, int c) {
   const ST *Wh = (const ST *)a.Wh, *bh = (const ST *)a.bh, *pp = (const ST *)a.peep;
   const int n = a.n;
@@ -275,6 +275,7 @@ __device__ inline ChanW load_chan_w(const ChanArgs &a, int c) {
   w.b2 = bh ? b2 : 0.f;
   w.p0 = pp ? p0 : 0.f;
   w.p1 = pp ? p1 : 0.f;
+  chan_w_scale<CELL>(w);
   return w;
 }
 

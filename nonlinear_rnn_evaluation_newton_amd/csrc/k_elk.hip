@@ -347,7 +347,7 @@ __device__ inline ElkcGeom elkc_geom(const ElkChanArgs &a, int cps, int nch) {
   return g;
 }
 
-template <typename ST>
+template <typename ST, int CELL>
 __device__ inline ChanW elkc_weights(const ElkChanArgs &a, int c) {
   const int n = a.n;
   const ST *Wh = (const ST *)a.Wh, *bh = (const ST *)a.bh, *pe = (const ST *)a.peep;
@@ -355,6 +355,7 @@ __device__ inline ChanW elkc_weights(const ElkChanArgs &a, int c) {
   w.a0 = ldf(Wh, c); w.a1 = ldf(Wh, (size_t)n + c); w.a2 = ldf(Wh, (size_t)2 * n + c);
   w.b0 = bh ? ldf(bh, c) : 0.f; w.b1 = bh ? ldf(bh, (size_t)n + c) : 0.f; w.b2 = bh ? ldf(bh, (size_t)2 * n + c) : 0.f;
   w.p0 = pe ? ldf(pe, c) : 0.f; w.p1 = pe ? ldf(pe, (size_t)n + c) : 0.f;
+  chan_w_scale<CELL>(w);
   return w;
 }
 
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(256) void k_elkc_filter(const ElkChanArgs a) {
   if (!g.wave_on) return;
   const bool first = a.e.k == 1;
   const float lam = a.e.lam, lam1 = lam + 1.f;
-  const ChanW w = elkc_weights<ST>(a, g.c);
+  const ChanW w = elkc_weights<ST, CELL>(a, g.c);
   float s[SW];
   if (g.t0 == 0) elkc_ld_h0<ST, SW>(a, g.b, g.c, s);
   else elkc_ld_h<ST, SW>(a, first, (size_t)g.b * a.e.T + g.t0 - 1, g.c, s);
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(256) void k_elkc_smooth(const ElkChanArgs a) {
   const int S = a.e.S;
   const float lam = a.e.lam;
   const size_t sub0 = (size_t)g.b * a.e.cps + (size_t)g.j * ELKC_SUB, col = (size_t)g.c * SW;
-  const ChanW w = elkc_weights<ST>(a, g.c);
+  const ChanW w = elkc_weights<ST, CELL>(a, g.c);
   float s[SW], P[SW], m[SW], R[SW], Sa[SW], RF[SW], SF[SW];
   if (g.t0 == 0) elkc_ld_h0<ST, SW>(a, g.b, g.c, s);
   else elkc_ld_h<ST, SW>(a, first, (size_t)g.b * a.e.T + g.t0 - 1, g.c, s);
@@ -756,7 +757,7 @@ __global__ __launch_bounds__(256) void k_elkc_apply(const ElkChanArgs a) {
   const int S = a.e.S, T = a.e.T;
   unsigned dmax = 0;
   if (g.wave_on) {
-    const ChanW w = elkc_weights<ST>(a, g.c);
+    const ChanW w = elkc_weights<ST, CELL>(a, g.c);
     float s[SW], P[SW], m[SW], Gs[LC][SW], Es[LC][SW];
     // the previous chunk's last state as the smoother pass saw it (this
     // pass may already have overwritten it)

@@ -333,6 +333,7 @@ __global__ __launch_bounds__(256) void k_elkf_jr_lstm(const ElkFullArgs a) {
     w.a0 = ldf(Wh, c); w.a1 = ldf(Wh, (size_t)n + c); w.a2 = ldf(Wh, (size_t)2 * n + c);
     w.b0 = bh ? ldf(bh, c) : 0.f; w.b1 = bh ? ldf(bh, (size_t)n + c) : 0.f; w.b2 = bh ? ldf(bh, (size_t)2 * n + c) : 0.f;
     w.p0 = ldf(pe, c); w.p1 = ldf(pe, (size_t)n + c);
+    chan_w_scale<C_LSTM>(w);
     float u[3], s[2], hc[2], f[2], J[4];
 #pragma unroll
     for (int q = 0; q < 3; q++) u[q] = ldf(U, row * 3 * n + (size_t)q * n + c);

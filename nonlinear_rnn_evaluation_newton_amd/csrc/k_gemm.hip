@@ -167,11 +167,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
       const int col = n0 + wn * 64 + j * 32 + (lane & 31);
       if (col >= g.N) continue;
       const float bias = split != 0 ? 0.f : g.bias32 ? g.bias32[col] : g.bias ? ldf((const T *)g.bias, col) : 0.f;
+      const float scale = g.scale32 ? g.scale32[col] : 1.f;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= g.M) continue;
-        const float v = acc[i][j][r] + bias;
+        const float v = fmaf(acc[i][j][r], scale, bias);
         if (g.splits > 1) g.ws[((size_t)split * g.M + row) * g.N + col] = v;
         else store_out<TO>((TO *)g.C + (size_t)row * g.ldc + col, v);
       }
@@ -343,17 +344,19 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
   // registers, the 4 adjacent columns 8 * (r / 4) + 4 * (lane / 32) + (0..3)
   const bool vec_c = g.splits == 1 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0;
   // the bias of this lane's columns, loaded once (they do not depend on the row)
-  float bias[FN][4][4];
+  float bias[FN][4][4], scale[FN][4][4];
 #pragma unroll
   for (int j = 0; j < FN; j++)
 #pragma unroll
     for (int rg = 0; rg < 4; rg++) {
       const int n = n0 + wn * (FN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
 #pragma unroll
-      for (int c = 0; c < 4; c++)
+      for (int c = 0; c < 4; c++) {
         bias[j][rg][c] = (split != 0 || n + c >= g.N) ? 0.f
                          : g.bias32 ? g.bias32[n + c]
                          : g.bias ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
+        scale[j][rg][c] = (g.scale32 && n + c < g.N) ? g.scale32[n + c] : 1.f;
+      }
     }
 #pragma unroll
   for (int i = 0; i < FM; i++) {
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
         if (n >= g.N) continue;
         float v[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) v[c] = acc[j][i][4 * rg + c] + bias[j][rg][c];
+        for (int c = 0; c < 4; c++) v[c] = fmaf(acc[j][i][4 * rg + c], scale[j][rg][c], bias[j][rg][c]);
         if (g.splits > 1) {
           float *w = g.ws + ((size_t)split * g.M + m) * g.N + n;
           if (n + 4 <= g.N && (g.N % 4) == 0) *reinterpret_cast<float4 *>(w) = make_float4(v[0], v[1], v[2], v[3]);

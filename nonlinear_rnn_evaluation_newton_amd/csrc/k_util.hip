@@ -1,6 +1,7 @@
 // Small utility kernels: workspace clearing (a fill kernel rather than a
 // memset node, so the calls stay safe under stream capture).
 #include "internal.h"
+#include "cells_chan.h"
 
 namespace pr {
 
@@ -21,23 +22,30 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// out[0, 3n) = scale_g (b_x + b_h folded), out[3n, 6n) = scale_g, g = i / n
 template <typename ST>
-__global__ void k_fold_bias(const ST *bx, const ST *bh, int n, int folded, float *out) {
+__global__ void k_fold_bias(const ST *bx, const ST *bh, int n, int folded, float g0, float g1, float g2,
+                            float *out) {
   const int total = 3 * n;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int gate = i / n;
     const float v = bx ? ldf(bx, i) : 0.f;
-    out[i] = (bh && i / n < folded) ? v + ldf(bh, i) : v;
+    const float sc = gate == 0 ? g0 : gate == 1 ? g1 : g2;
+    out[i] = sc * ((bh && gate < folded) ? v + ldf(bh, i) : v);
+    out[total + i] = sc;
   }
 }
 
-hipError_t launch_fold_bias(bool bf16, const void *bx, const void *bh, int n, int folded, float *out, hipStream_t s) {
+hipError_t launch_fold_bias(bool bf16, const void *bx, const void *bh, int n, int cell, float *out, hipStream_t s) {
   const int blocks = (3 * n + 255) / 256 < 1024 ? (3 * n + 255) / 256 : 1024;
+  const int folded = cell == C_LSTM ? 3 : 2;
+  const float g0 = chan_gate_scale(cell, 0), g1 = chan_gate_scale(cell, 1), g2 = chan_gate_scale(cell, 2);
   if (bf16)
     hipLaunchKernelGGL(k_fold_bias<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t *)bx,
-                       (const uint16_t *)bh, n, folded, out);
+                       (const uint16_t *)bh, n, folded, g0, g1, g2, out);
   else
     hipLaunchKernelGGL(k_fold_bias<float>, dim3(blocks), dim3(256), 0, s, (const float *)bx, (const float *)bh, n,
-                       folded, out);
+                       folded, g0, g1, g2, out);
   return hipGetLastError();
 }
 

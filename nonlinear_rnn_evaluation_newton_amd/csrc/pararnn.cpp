@@ -57,7 +57,7 @@ struct Plan {
   int tps_2 = 0, ntiles_2 = 0;
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
-  size_t off_cb = 0;              // channel path: the projection's fp32 bias with the folded recurrent biases
+  size_t off_cb = 0;              // channel path: the projection's fp32 bias (folded recurrent biases) and column scale
   size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
   size_t off_red = 0;             // channel path adjoint: fp64 split sums of the weight partials
   size_t off_tn = 0;              // dense n = 64 adjoint: partials of the K-outer weight products
@@ -191,7 +191,7 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_incl = o; o = align256(o + nt * g.CH * SW * 4);
     pl->off_bnd = o; o = align256(o + (size_t)2 * nt * g.CH * SW * 4);
     pl->off_U = o; o = align256(o + rows * 3 * p->n * es);
-    pl->off_cb = o; o = align256(o + (size_t)3 * p->n * 4);
+    pl->off_cb = o; o = align256(o + (size_t)6 * p->n * 4);
     pl->solve_bytes = o;
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
     pl->off_part = o; o = align256(o + nt * g.CH * 11 * 4);
@@ -208,9 +208,10 @@ int make_plan(const pr_problem *p, Plan *pl) {
 }
 
 // U = x W_x^T + b_x on MFMA ([B*T, d] x [3n, d]^T).  For the per-channel
-// cells (cb non-null) the bias also takes the recurrent biases of the gates
-// whose pre-activation is a plain sum (the LSTM's three, the GRU's r and z),
-// summed in fp32 into cb: the cells then add no bias per step.
+// cells (cb non-null, 6n floats) the bias also takes the recurrent biases of
+// the gates whose pre-activation is a plain sum (the LSTM's three, the GRU's r
+// and z), summed in fp32 into cb, and each gate's column is scaled by its
+// exp2 factor: the cells then add no bias and multiply no constant per step.
 hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void *x, void *U, hipStream_t s,
                             float *cb = nullptr) {
   const bool bf = p->dtype == PR_BF16;
@@ -219,10 +220,11 @@ hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void
   g.A = x; g.B = w->W_x; g.C = U; g.bias = w->b_x; g.ws = nullptr;
   if (cb) {
     const hipError_t e =
-        launch_fold_bias(bf, w->b_x, w->b_h, p->n, p->cell == PR_CELL_LSTM_CIFG_DIAG ? 3 : 2, cb, s);
+        launch_fold_bias(bf, w->b_x, w->b_h, p->n, p->cell == PR_CELL_LSTM_CIFG_DIAG ? C_LSTM : C_GRU_DIAG, cb, s);
     if (e != hipSuccess) return e;
     g.bias = nullptr;
     g.bias32 = cb;
+    g.scale32 = cb + (size_t)3 * p->n;
   }
   g.M = p->B * p->T; g.N = gates_of(p->cell) * p->n; g.K = p->d;
   g.lda = p->d; g.ldb = p->d; g.ldc = g.N; g.splits = 1;
