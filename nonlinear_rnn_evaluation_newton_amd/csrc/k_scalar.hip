@@ -152,10 +152,11 @@ __device__ inline void wave_scan_affine1(float &A, float &b) {
       : "+v"(A), "+v"(b));
 }
 
-// Wavefront totals of the last two computed tiles and their carries.
+// Wavefront totals of the last two computed tiles and the carries entering
+// each of their wavefronts.
 struct ScShared {
   float wA[2][SC_CW], wb[2][SC_CW];
-  float carry[2];
+  float cw[2][SC_CW];
   unsigned done[2];  // compute wavefronts finished with the tile in each buffer
   int stop;
   unsigned dmax[SC_CW];
@@ -289,36 +290,21 @@ __device__ inline float sc_resolve2(Rsrc ragg, Rsrc rincl, int j, int k, const S
   return sc_resolve_from(ragg, rincl, j - 1, k, P1, 1.f, 0.f, st);
 }
 
-// Composition of wavefronts [0, wid) (pre) and of all of them (tot) of a
-// computed tile, from its LDS totals.
-struct ScTot {
-  float preA, preb, totA, totb;
-};
-
-__device__ inline ScTot sc_tot(const ScShared &sh, int buf, int wid) {
-  ScTot r;
-  r.preA = 1.f; r.preb = 0.f; r.totA = 1.f; r.totb = 0.f;
-#pragma unroll
-  for (int w = 0; w < SC_CW; w++) {
-    const float A = sh.wA[buf][w], b = sh.wb[buf][w];
-    if (w < wid) {
-      r.preb = fmaf(A, r.preb, b);
-      r.preA *= A;
-    }
-    r.totb = fmaf(A, r.totb, b);
-    r.totA *= A;
-  }
-  return r;
-}
-
 // Look-back wavefront, for computed tile `id` whose wavefront totals are in
 // LDS buffer `buf`: resolve its carry from the predecessors' descriptors,
-// publish its inclusive prefix, leave the carry in LDS.  This wavefront
-// issues no other memory operations, so its waits on the descriptors never
-// queue behind the bulk loads and stores of the compute wavefronts.
+// publish its inclusive prefix, and leave in LDS the carry entering each
+// compute wavefront (lane w composes the totals of wavefronts 0 .. w - 1, once
+// per tile rather than in every compute wavefront).  This wavefront issues no
+// other memory operations, so its waits on the descriptors never queue behind
+// the bulk loads and stores of the compute wavefronts.
 __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh, int buf) {
-  const int k = a.k, j = id / a.B;
-  const ScTot tt = sc_tot(sh, buf, SC_CW);
+  const int k = a.k, j = id / a.B, lane = threadIdx.x & 63;
+  float totA = 1.f, totb = 0.f;
+#pragma unroll
+  for (int w = 0; w < SC_CW; w++) {
+    totb = fmaf(sh.wA[buf][w], totb, sh.wb[buf][w]);
+    totA *= sh.wA[buf][w];
+  }
   const ScDesc d = sc_desc(a, id % a.B);
   float carry = 0.f;
   if (j > 0) {
@@ -332,10 +318,19 @@ __device__ inline void sc_lookback_tile(const TimeArgs &a, int id, ScShared &sh,
     carry = sc_resolve2(d.agg, d.incl, j, k, P0, P1, a.st);
   }
   u32x2 w;
-  w.x = __float_as_uint(fmaf(tt.totA, carry, tt.totb));
+  w.x = __float_as_uint(fmaf(totA, carry, totb));
   w.y = tag_incl(k);
-  __builtin_amdgcn_raw_buffer_store_b64(w, d.incl, (threadIdx.x & 63) == 0 ? (unsigned)j * 8u : SC_OOB, 0, SC_SC1);
-  if ((threadIdx.x & 63) == 0) sh.carry[buf] = carry;
+  __builtin_amdgcn_raw_buffer_store_b64(w, d.incl, lane == 0 ? (unsigned)j * 8u : SC_OOB, 0, SC_SC1);
+  float pA = 1.f, pb = 0.f;
+#pragma unroll
+  for (int v = 0; v < SC_CW - 1; v++) {
+    const float A = sh.wA[buf][v], b = sh.wb[buf][v];
+    if (v < lane) {
+      pb = fmaf(A, pb, b);
+      pA *= A;
+    }
+  }
+  if (lane < SC_CW) sh.cw[buf][lane] = fmaf(pA, carry, pb);
 }
 
 // Members common to the scalar-state policies.
@@ -343,7 +338,6 @@ struct ScBase {
   static constexpr int WPE = 4;  // wavefronts per SIMD the register budget is sized for
   using Args = TimeArgs;
   using Shared = ScShared;
-  using Tot = ScTot;
   struct Consts {
     float c[SC_NC];
   };
@@ -356,7 +350,6 @@ struct ScBase {
     for (int i = 0; i < SC_NC; i++) K.c[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.coef[i])));
   }
   __host__ __device__ static int ntiles(const Args &a) { return a.ntiles; }
-  __device__ static Tot tot(const Shared &sh, int buf, int wid) { return sc_tot(sh, buf, wid); }
   __device__ static void lookback_tile(const Args &a, int id, Shared &sh, int buf) { sc_lookback_tile(a, id, sh, buf); }
 };
 
@@ -474,14 +467,14 @@ struct SweepPol : ScBase {
   }
 
   // update of the tile's steps from its carry, convergence measure, stores
-  __device__ static void apply(const TimeArgs &a, const Consts &, int id, const Tile &Tl, const ScTot &tt,
-                               const ScShared &sh, Lds &, int buf, Acc &acc) {
+  __device__ static void apply(const TimeArgs &a, const Consts &, int id, const Tile &Tl, const ScShared &sh, Lds &,
+                               int buf, Acc &acc) {
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, k = a.k, B = a.B, T = a.T;
     const int j = id / B, b = id % B, L = b * a.tiles_per_seq + j;
     const int t0 = j * TILE + wid * WSTEPS;
     const bool full = j * TILE + TILE <= T;
-    float c = fmaf(tt.preA, sh.carry[buf], tt.preb);  // dh entering this wavefront's steps
+    float c = sh.cw[buf][wid];  // dh entering this wavefront's steps
     const Rsrc rh = sc_rsrc(a.h + (size_t)b * T, (unsigned)T * 4u);
     const Rsrc rb = sc_rsrc(a.bnd, (unsigned)a.ntiles * 8u);
 #pragma unroll
@@ -659,13 +652,13 @@ struct AdjPol : ScBase {
     sc_publish(a, id, wA, wb, sh, buf);
   }
 
-  __device__ static void apply(const TimeArgs &a, const Consts &K, int id, const Tile &Tl, const ScTot &tt,
-                               const ScShared &sh, Lds &lds, int buf, Acc &acc) {
+  __device__ static void apply(const TimeArgs &a, const Consts &K, int id, const Tile &Tl, const ScShared &sh,
+                               Lds &lds, int buf, Acc &acc) {
     const float *C = K.c;
     constexpr int V = SC_V;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, B = a.B, T = a.T;
     const int b = id % B;
-    float c = fmaf(tt.preA, sh.carry[buf], tt.preb);  // lambda entering this wavefront (after its latest step)
+    float c = sh.cw[buf][wid];  // lambda entering this wavefront (after its latest step)
     const Rsrc rl = sc_rsrc(a.lam ? a.lam + (size_t)b * T : nullptr, (unsigned)T * 4u);
     const Rsrc rd = sc_rsrc(a.dx ? a.dx + (size_t)b * T : nullptr, (unsigned)T * 4u);
     const Rsrc r0 = sc_rsrc(a.dh0 ? a.dh0 + b : nullptr, 4u);

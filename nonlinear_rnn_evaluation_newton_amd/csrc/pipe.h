@@ -89,22 +89,20 @@ __device__ inline void pipe_compute_any(const typename Pol::Args &a, const typen
   else Pol::template compute<false>(a, K, id, R, Tl, sh, lds, buf);
 }
 
-// One stage of the compute wavefronts: read P's wavefront totals (LDS buffer
-// bufN ^ 1; rewritten two stages on), issue the loads of the tile after N,
+// One stage of the compute wavefronts: issue the loads of the tile after N,
 // compute N into buffer bufN, block barrier (the look-back wavefront has left
-// P's carry), update P.
+// the carries entering P's wavefronts in LDS buffer bufN ^ 1), update P.
 template <class Pol>
 __device__ inline void pipe_stage(const typename Pol::Args &a, const typename Pol::Consts &K, int idP,
                                   const typename Pol::Tile &TP, int idN, const typename Pol::Raw &RN,
                                   typename Pol::Raw &Rnext, typename Pol::Tile &TN, typename Pol::Shared &sh,
                                   typename Pol::Lds &lds, int bufN, typename Pol::Acc &acc) {
-  const typename Pol::Tot tt = Pol::tot(sh, bufN ^ 1, threadIdx.x >> 6);
   const int nt = Pol::ntiles(a);
   const int nn = idN + (int)gridDim.x < nt ? idN + (int)gridDim.x : -1;  // -1: an empty load
   Pol::load(a, nn, Rnext);
   pipe_compute_any<Pol>(a, K, idN, RN, TN, sh, lds, bufN);
   __syncthreads();
-  Pol::apply(a, K, idP, TP, tt, sh, lds, bufN ^ 1, acc);
+  Pol::apply(a, K, idP, TP, sh, lds, bufN ^ 1, acc);
 }
 
 // Persistent grid (every block resident, grid <= tile count); block g takes
@@ -162,9 +160,8 @@ __global__ __launch_bounds__(SC_THREADS, Pol::WPE) void k_pipe(const typename Po
       id += G;
     }
     __syncthreads();  // final stage: the look-back wavefront has resolved the last tile
-    const typename Pol::Tot tt = Pol::tot(sh, last, wid);
-    if (last == 0) Pol::apply(a, K, idP, T0, tt, sh, lds, 0, acc);
-    else Pol::apply(a, K, idP, T1, tt, sh, lds, 1, acc);
+    if (last == 0) Pol::apply(a, K, idP, T0, sh, lds, 0, acc);
+    else Pol::apply(a, K, idP, T1, sh, lds, 1, acc);
   }
   Pol::finish(a, acc, sh);
 }
