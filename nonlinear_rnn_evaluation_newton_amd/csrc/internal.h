@@ -167,6 +167,9 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
 // ---------------- utilities ------------------------------------------------
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+// copy `bytes` (a multiple of 4) from device memory to host-coherent memory,
+// then store val to *seq with a system-scope release (one block)
+hipError_t launch_snapshot(const void *src, void *dst, size_t bytes, unsigned *seq, unsigned val, hipStream_t s);
 // Epilogue of the per-channel cells' input projection, fp32 [6n]: [0, 3n) the
 // bias, b_x plus the recurrent biases of the gates whose pre-activations are
 // plain sums (LSTM f, g, o; GRU r, z), and [3n, 6n) the column scale, each

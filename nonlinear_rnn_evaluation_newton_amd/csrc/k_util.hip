@@ -11,6 +11,20 @@ __global__ void k_zero(uint4 *p, size_t n16, unsigned char *tail, size_t ntail) 
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+__global__ __launch_bounds__(256) void k_snapshot(const unsigned *src, unsigned *dst, int nwords, unsigned *seq,
+                                                  unsigned val) {
+  for (int i = threadIdx.x; i < nwords; i += blockDim.x) dst[i] = src[i];
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(seq, val, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_snapshot(const void *src, void *dst, size_t bytes, unsigned *seq, unsigned val, hipStream_t s) {
+  hipLaunchKernelGGL(k_snapshot, dim3(1), dim3(256), 0, s, (const unsigned *)src, (unsigned *)dst, (int)(bytes / 4),
+                     seq, val);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
   const size_t n16 = bytes / 16, ntail = bytes % 16;

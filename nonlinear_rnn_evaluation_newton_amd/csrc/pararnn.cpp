@@ -238,13 +238,57 @@ int kcell(int cell) { return cell == PR_CELL_TANH_RNN ? C_TANH : cell == PR_CELL
 
 bool al16(const void *q) { return q == nullptr || ((uintptr_t)q & 15) == 0; }
 
-// Pinned host copy of the solve state, one per thread.
-SolveState *host_state() {
-  thread_local SolveState *hs = nullptr;
-  if (!hs) {
-    if (hipHostMalloc((void **)&hs, sizeof(SolveState), hipHostMallocDefault) != hipSuccess) hs = nullptr;
+// Host copy of the solve state, one per thread, in pinned device-coherent
+// memory: a small kernel stores the state there and then, with a
+// system-scope release, the sequence word the host waits on, so a solve's
+// stop test needs neither a copy-engine transfer nor an event between the
+// sweeps and the work enqueued after them.
+struct HostSnap {
+  SolveState st;
+  unsigned seq;
+  unsigned *seq_dev;  // the device's address of seq
+  SolveState *st_dev;
+  unsigned next;      // sequence value of the next snapshot
+};
+HostSnap *host_snap() {
+  thread_local HostSnap *hs = nullptr;
+  thread_local bool tried = false;
+  if (!hs && !tried) {
+    tried = true;
+    HostSnap *q = nullptr;
+    if (hipHostMalloc((void **)&q, sizeof(HostSnap), hipHostMallocCoherent | hipHostMallocPortable | hipHostMallocMapped) !=
+        hipSuccess)
+      return nullptr;
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, q, 0) != hipSuccess) return nullptr;
+    q->seq = 0;
+    q->next = 1;
+    q->st_dev = &((HostSnap *)d)->st;
+    q->seq_dev = &((HostSnap *)d)->seq;
+    hs = q;
   }
   return hs;
+}
+// Enqueue a snapshot of the device state at `dev` on s.
+hipError_t snapshot_enqueue(HostSnap *hs, const void *dev, hipStream_t s, unsigned *want) {
+  *want = hs->next++;
+  if (hs->next == 0) hs->next = 1;
+  return launch_snapshot(dev, hs->st_dev, sizeof(SolveState), hs->seq_dev, *want, s);
+}
+// Wait for snapshot `want` (spinning on the host word; the stream is queried
+// now and then so that a device error or a lost snapshot ends the wait).
+int snapshot_wait(HostSnap *hs, unsigned want, hipStream_t s) {
+  for (unsigned long n = 1;; n++) {
+    if (__atomic_load_n(&hs->seq, __ATOMIC_ACQUIRE) == want) return PR_OK;
+    if ((n & 1023) == 0) {
+      const hipError_t e = hipStreamQuery(s);
+      if (e == hipSuccess) {  // everything enqueued has finished: the word is there or lost
+        if (__atomic_load_n(&hs->seq, __ATOMIC_ACQUIRE) == want) return PR_OK;
+        return fail(PR_EHIP, "the solve-state snapshot did not arrive");
+      }
+      if (e != hipErrorNotReady) return fail(PR_EHIP, "%s", hipGetErrorString(e));
+    }
+  }
 }
 
 // Event timing of the main kernels (pararnn_trace).  Categories: Newton
@@ -263,13 +307,16 @@ struct Trace {
   int pending[TR_N] = {};
   hipError_t make() {
     if (made) return hipSuccess;
+    // timing-only events: no system-scope fence (cache write-back and
+    // invalidation) when they complete, which would stall the next launch
+    const unsigned fl = hipEventDefault | hipEventDisableSystemFence;
     for (int i = 0; i < 2 * CAP; i++) {
-      hipError_t e = hipEventCreate(&sw[i]);
+      hipError_t e = hipEventCreateWithFlags(&sw[i], fl);
       if (e != hipSuccess) return e;
-      e = hipEventCreate(&swa[i]);
+      e = hipEventCreateWithFlags(&swa[i], fl);
       if (e != hipSuccess) return e;
       for (int c = 1; c < TR_N; c++) {
-        e = hipEventCreate(&ev[c][i]);
+        e = hipEventCreateWithFlags(&ev[c][i], fl);
         if (e != hipSuccess) return e;
       }
     }
@@ -495,15 +542,6 @@ struct SpecMemo {
   }
 };
 // Event marking a convergence poll's state snapshot (null if it cannot be made).
-static hipEvent_t poll_event() {
-  thread_local hipEvent_t ev = nullptr;
-  thread_local bool tried = false;
-  if (!tried) {
-    tried = true;
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
-  }
-  return ev;
-}
 static SpecMemo &spec_memo() {
   thread_local SpecMemo m;
   return m;
@@ -538,8 +576,9 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
-  SolveState *hs = host_state();
-  if (!hs) return fail(PR_EHIP, "pinned host buffer allocation failed");
+  HostSnap *snap = host_snap();
+  if (!snap) return fail(PR_EHIP, "pinned host buffer allocation failed");
+  SolveState *hs = &snap->st;
 
   Trace &tr = trace();
   if (tr.on) HIPCHK(tr.make());
@@ -756,17 +795,19 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
     if (bev) HIPCHK(hipEventRecord(tr.sw[2 * (k_last - 1) + 1], s));
-    HIPCHK(hipMemcpyAsync(hs, ws + pl.off_state, sizeof(SolveState), hipMemcpyDeviceToHost, s));
-    // the poll waits for the snapshot only: a speculative adjoint enqueued
+    unsigned want = 0;
+    HIPCHK(snapshot_enqueue(snap, ws + pl.off_state, s, &want));
+    // the host waits for the snapshot only: a speculative adjoint enqueued
     // behind it keeps the device busy while the host decides
-    hipEvent_t poll_ev = poll_event();
-    if (poll_ev) HIPCHK(hipEventRecord(poll_ev, s));
     if (speculate && k == 1) {
       spec->rc = adjoint_impl(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
                               ws_bytes, stream, true);
       spec_enqueued = spec->rc >= 0;
     }
-    HIPCHK(poll_ev ? hipEventSynchronize(poll_ev) : hipStreamSynchronize(s));
+    {
+      const int rc = snapshot_wait(snap, want, s);
+      if (rc != PR_OK) return rc;
+    }
     if (hs->fault)
       return fail(PR_ELOOKBACK, "a look-back wait exceeded its bound (the persistent grid was not co-resident)");
     if (hs->stopped) {
