@@ -527,6 +527,7 @@ struct SpecAdjoint {
   void *lambda, *dx, *dh0;
   const pr_grads *dW;
   bool done = false;  // out: the adjoint ran at the returned trajectory
+  bool ran = false;   // out: an adjoint was enqueued (done or not)
   int rc = PR_OK;     // out: its status when done
 };
 // Whether the last combined call on a problem converged within its first
@@ -549,7 +550,10 @@ static SpecMemo &spec_memo() {
 
 static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                         const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
-                        size_t ws_bytes, void *stream, bool u_ready);
+                        size_t ws_bytes, void *stream, bool u_ready, bool fresh);
+// Sweep number of the descriptors of an adjoint that follows its solve
+// without clearing: above any sweep count (the scalar-state path has T < 2^29).
+constexpr int ADJ_TAG_SWEEP = 1 << 30;
 
 static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
                       int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
@@ -801,8 +805,9 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     // behind it keeps the device busy while the host decides
     if (speculate && k == 1) {
       spec->rc = adjoint_impl(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
-                              ws_bytes, stream, true);
+                              ws_bytes, stream, true, true);
       spec_enqueued = spec->rc >= 0;
+      spec->ran = spec_enqueued;
     }
     {
       const int rc = snapshot_wait(snap, want, s);
@@ -898,7 +903,7 @@ int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, c
 int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                     const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
                     size_t ws_bytes, void *stream) {
-  return adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, false);
+  return adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, false, false);
 }
 
 }  // extern "C"
@@ -906,9 +911,14 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
 // The adjoint; u_ready: the workspace already holds this problem's input
 // projection U (a solve on the same workspace and inputs has just computed
 // it, as in pararnn_solve_adjoint), so it is not recomputed.
+// u_ready: the solve of the same call left the input projection in the
+// workspace.  fresh: the solve of the same call cleared the workspace (and
+// folded the scalar-state coefficients) and no adjoint has run since; the
+// scalar-state adjoint then skips its clearing and tags its descriptors with
+// a sweep number no solve reaches, so the sweeps' descriptors never match.
 static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                         const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
-                        size_t ws_bytes, void *stream, bool u_ready) {
+                        size_t ws_bytes, void *stream, bool u_ready, bool fresh) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, &pl);
@@ -924,11 +934,14 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
   // n = d = 1 with vector-friendly sizes takes the scalar-state adjoint
   const bool scalar = pl.path == PATH_TIME && pl.scalar_ok && al16(h) && al16(x) && al16(g) && al16(lambda) &&
                       al16(dx) && !getenv("PARARNN_NO_SCALAR");
-  if (scalar)
+  const bool keep = scalar && fresh;
+  if (keep) {
+  } else if (scalar) {
     HIPCHK(launch_zero_coef(ws, pl.zero_bytes, (const float *)w->W_x, (const float *)w->b_x, (const float *)w->W_h,
                             (const float *)w->b_h, kcell(p->cell), (float *)(ws + pl.off_coef), s));
-  else
+  } else {
     HIPCHK(launch_zero(ws, pl.zero_bytes, s));
+  }
   if (pl.path == PATH_TIME) {
     TimeArgs a{};
     a.x = (const float *)x;
@@ -944,7 +957,7 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
     a.dh0 = (float *)dh0;
     a.part = (float *)(ws + pl.off_part);
     a.B = p->B; a.T = p->T; a.d = p->d; a.n = p->n;
-    a.k = 1;
+    a.k = keep ? ADJ_TAG_SWEEP : 1;
     a.st = (SolveState *)(ws + pl.off_state);
     a.agg = (unsigned long long *)(ws + pl.off_agg);
     a.incl = (unsigned long long *)(ws + pl.off_incl);
@@ -1122,7 +1135,7 @@ int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *
   if (sa.done) return sa.rc < 0 ? sa.rc : rc;
   if (sa.rc < 0) return sa.rc;  // the speculative enqueue was rejected: the same arguments fail again
   if (rc == PR_NONFINITE) return rc;
-  const int ra = adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, true);
+  const int ra = adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, true, !sa.ran);
   return ra < 0 ? ra : rc;
 }
 
