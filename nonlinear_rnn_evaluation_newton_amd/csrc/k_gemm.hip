@@ -225,10 +225,22 @@ constexpr int WGM = PR_GEMM_WGM, WGN = PR_GEMM_WGN, FM = BT / 32 / WGM, FN = BT 
 constexpr int GT = 64 * WGM * WGN;  // threads per block
 constexpr int GQ = BT * (BK / 8) / GT;  // 16-byte staging chunks per operand per thread
 
-template <typename TO>
+// KO = true: both operands stored K-outer (A [K, lda], B [K, ldb]; the
+// products over the time rows).  Each thread loads a 4 (k) x 8 (m) block as
+// four 16-byte row pieces, transposes it with byte permutes and writes eight
+// 8-byte k-runs, so the tiles land K-contiguous as in the other layout.  Rows
+// are unpadded (64 k) and their 16-byte k-chunks XOR-swizzled by
+// sw(m) = (m ^ (m >> 3)) & 7, which spreads both these writes (one m of each
+// thread's 8 per instruction, 32 m-groups) and the fragment reads (32
+// consecutive rows, two adjacent chunks) evenly over the banks.
+__device__ inline int ko_sw(int m) { return (m ^ (m >> 3)) & 7; }
+constexpr int BKO = BK;  // row length of the K-outer layout (elements)
+
+template <typename TO, bool KO>
 __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BT * BLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BT * BLD];
+  constexpr int LDW = KO ? BKO : BLD;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BT * LDW];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BT * LDW];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   const int tiles = tiles_m * tiles_n;
@@ -243,12 +255,17 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
   const int kchunk = ((g.K + g.splits - 1) / g.splits + BK - 1) / BK * BK;
   const int kb = split * kchunk, ke = min(g.K, kb + kchunk);
 
-  const uint16_t *A = (const uint16_t *)g.A + (size_t)m0 * g.lda;
-  const uint16_t *B = (const uint16_t *)g.B + (size_t)n0 * g.ldb;
-  const GRsrc ra = g_rsrc(A, (unsigned)(min(BT, g.M - m0) * g.lda * 2));
-  const GRsrc rb = g_rsrc(B, (unsigned)(min(BT, g.N - n0) * g.ldb * 2));
+  const uint16_t *A = (const uint16_t *)g.A + (KO ? (size_t)m0 : (size_t)m0 * g.lda);
+  const uint16_t *B = (const uint16_t *)g.B + (KO ? (size_t)n0 : (size_t)n0 * g.ldb);
+  // K-outer: the resource spans the rows up to K from the block's first
+  // column; columns past M (N) and rows past the split's K range read zero
+  // through the offsets (M, N, lda, ldb are multiples of 8)
+  const GRsrc ra = g_rsrc(A, KO ? (unsigned)(((size_t)g.K * g.lda - m0) * 2) : (unsigned)(min(BT, g.M - m0) * g.lda * 2));
+  const GRsrc rb = g_rsrc(B, KO ? (unsigned)(((size_t)g.K * g.ldb - n0) * 2) : (unsigned)(min(BT, g.N - n0) * g.ldb * 2));
 
-  // staging: GQ chunks of 8 K-consecutive elements per operand per thread
+  // staging: GQ chunks of 8 elements per operand per thread; K-contiguous:
+  // 8 K-consecutive elements of one row; K-outer: 8 columns (m-group tid %
+  // 32) of K rows 4 (tid / 32) + q
   int srow[GQ], skc[GQ];
 #pragma unroll
   for (int q = 0; q < GQ; q++) {
@@ -256,22 +273,51 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
     srow[q] = e >> 3;
     skc[q] = (e & 7) * 8;
   }
+  const int ko_mg = tid & 31, ko_k = (tid >> 5) * 4;
+  const bool ko_ina = m0 + ko_mg * 8 < g.M, ko_inb = n0 + ko_mg * 8 < g.N;
   gu32x4 va[GQ], vb[GQ];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < GQ; q++) {
-      const bool in = k0 + skc[q] < ke;
-      va[q] = __builtin_amdgcn_raw_buffer_load_b128(
-          ra, in ? (unsigned)(srow[q] * g.lda + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
-      vb[q] = __builtin_amdgcn_raw_buffer_load_b128(
-          rb, in ? (unsigned)(srow[q] * g.ldb + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
+      if constexpr (KO) {
+        const int k = k0 + ko_k + q;
+        va[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, (k < ke && ko_ina) ? (unsigned)(k * g.lda + ko_mg * 8) * 2u : 0x80000000u, 0, 0);
+        vb[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (k < ke && ko_inb) ? (unsigned)(k * g.ldb + ko_mg * 8) * 2u : 0x80000000u, 0, 0);
+      } else {
+        const bool in = k0 + skc[q] < ke;
+        va[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, in ? (unsigned)(srow[q] * g.lda + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
+        vb[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, in ? (unsigned)(srow[q] * g.ldb + k0 + skc[q]) * 2u : 0x80000000u, 0, 0);
+      }
+    }
+  };
+  // K-outer: column c of the 4 x 8 block becomes the 4-element k-run of row
+  // 8 mg + c (two dwords: rows 0-1 and 2-3 of the block, low halves for even
+  // c, high halves for odd)
+  auto ko_store = [&](uint16_t *dst, const gu32x4 (&v)[GQ]) {
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      const unsigned lo = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
+      const unsigned hi = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
+      const int m = ko_mg * 8 + c;
+      const int idx = m * BKO + (((ko_k >> 3) ^ ko_sw(m)) << 3) + (ko_k & 7);
+      *reinterpret_cast<unsigned long long *>(&dst[idx]) = ((unsigned long long)hi << 32) | lo;
     }
   };
   auto lstore = [&](int buf) {
+    if constexpr (KO) {
+      ko_store(sA[buf], va);
+      ko_store(sB[buf], vb);
+    } else {
 #pragma unroll
-    for (int q = 0; q < GQ; q++) {
-      *reinterpret_cast<gu32x4 *>(&sA[buf][srow[q] * BLD + skc[q]]) = va[q];
-      *reinterpret_cast<gu32x4 *>(&sB[buf][srow[q] * BLD + skc[q]]) = vb[q];
+      for (int q = 0; q < GQ; q++) {
+        *reinterpret_cast<gu32x4 *>(&sA[buf][srow[q] * BLD + skc[q]]) = va[q];
+        *reinterpret_cast<gu32x4 *>(&sB[buf][srow[q] * BLD + skc[q]]) = vb[q];
+      }
     }
   };
 
@@ -302,10 +348,26 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
     const uint16_t *cA = sA[buf], *cB = sB[buf];
     bf16x8_t a[2][FM], b[2][FN];
     auto frag = [&](int h, int ks) {
+      if constexpr (KO) {
+        const int kc = (ks + kl) >> 3;
 #pragma unroll
-      for (int i = 0; i < FM; i++) a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
+        for (int i = 0; i < FM; i++) {
+          const int r = arow + i * 32;
+          a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + r * BKO + ((kc ^ ko_sw(r)) << 3));
+        }
 #pragma unroll
-      for (int j = 0; j < FN; j++) b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+        for (int j = 0; j < FN; j++) {
+          const int r = brow + j * 32;
+          b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + r * BKO + ((kc ^ ko_sw(r)) << 3));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+          a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + (arow + i * 32) * BLD + ks + kl);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+          b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + (brow + j * 32) * BLD + ks + kl);
+      }
     };
     frag(0, 0);
     // the global loads first, then the first slice's fragment reads
@@ -327,6 +389,13 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      } else if constexpr (KO) {  // two LDS stores after each MFMA
+#pragma unroll
+        for (int r = 0; r < 2 * GQ; r++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2 * GQ, 0);
       } else {  // one LDS store after each MFMA
 #pragma unroll
         for (int r = 0; r < 2 * GQ; r++) {
@@ -403,11 +472,17 @@ static bool big_nt(const GemmArgs &g) {
   return g.bf16 && g.a_kc && g.b_kc && g.vec_a && g.vec_b && g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
          g.M >= BT && g.N >= BT && (long long)BT * g.lda * 2 < (1LL << 31) && (long long)BT * g.ldb * 2 < (1LL << 31);
 }
+// both operands K-outer: whole 16-byte column pieces and 32-bit row offsets
+static bool big_tn(const GemmArgs &g) {
+  return g.bf16 && !g.a_kc && !g.b_kc && g.vec_a && g.vec_b && g.M % 8 == 0 && g.N % 8 == 0 && g.lda % 8 == 0 &&
+         g.ldb % 8 == 0 && g.lda >= g.M && g.ldb >= g.N && g.M >= BT && g.N >= BT &&
+         (long long)g.K * g.lda * 2 < (1LL << 31) && (long long)g.K * g.ldb * 2 < (1LL << 31);
+}
 
-template <typename TO>
+template <typename TO, bool KO = false>
 static hipError_t gemm_big_launch(const GemmArgs &g, hipStream_t s) {
   const int tm = (g.M + BT - 1) / BT, tn = (g.N + BT - 1) / BT;
-  hipLaunchKernelGGL((k_gemm_bf16_nt<TO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
+  hipLaunchKernelGGL((k_gemm_bf16_nt<TO, KO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
   if (g.splits > 1) {
     const size_t tot = (size_t)g.M * g.N;
     hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
@@ -538,6 +613,8 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   const bool bf = g.bf16;
   if (big_nt(g) && !getenv("PARARNN_SMALL_GEMM"))
     return g.out_f32 ? gemm_big_launch<float>(g, s) : gemm_big_launch<uint16_t>(g, s);
+  if (big_tn(g) && !getenv("PARARNN_SMALL_GEMM"))
+    return g.out_f32 ? gemm_big_launch<float, true>(g, s) : gemm_big_launch<uint16_t, true>(g, s);
 #define PR_G(AKC, BKC)                                                                        \
   if (g.a_kc == AKC && g.b_kc == BKC) {                                                       \
     if (bf) return g.out_f32 ? gemm_launch<uint16_t, AKC, BKC, float>(g, s)                   \

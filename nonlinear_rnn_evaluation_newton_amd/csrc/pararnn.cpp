@@ -58,7 +58,7 @@ struct Plan {
   size_t off_state = 0, off_agg = 0, off_incl = 0, off_bnd = 0, off_part = 0;
   size_t off_U = 0, off_dU = 0, off_gws = 0, off_coef = 0;
   size_t off_cb = 0;              // channel path: the projection's fp32 bias (folded recurrent biases) and column scale
-  size_t off_xt = 0, off_wt = 0;  // channel path adjoint: x^T and W_x^T (dU^T reuses U's space)
+  size_t off_wt = 0;              // channel path adjoint: W_x^T
   size_t off_red = 0;             // channel path adjoint: fp64 split sums of the weight partials
   size_t off_tn = 0;              // dense n = 64 adjoint: partials of the K-outer weight products
   // dense n = 64 path
@@ -198,7 +198,6 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_red = o; o = align256(o + (size_t)CHAN_RED_SPLITS * p->n * 11 * 8);
     const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
     pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
-    pl->off_xt = o; o = align256(o + rows * p->d * es);
     pl->off_wt = o; o = align256(o + (size_t)3 * p->n * p->d * es);
     pl->adjoint_bytes = o;
     return PR_OK;
@@ -1082,9 +1081,9 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
     const int tg = tr.begin(TR_AGEMM, s);
     if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))
       HIPCHK(launch_chan_reduce_tiles(kc, ca, (double *)(ws + pl.off_red), dW->W_h, dW->b_h, dW->peep, dW->b_x, s));
-    // Both products contract over an outer dimension of a stored operand;
-    // transposed copies (HBM-bound, a few percent of the products) put K
-    // innermost in every operand, the layout the GEMM reads fastest.
+    // dx contracts over U's columns: W_x is read through a transposed copy
+    // (small); dW_x contracts over the rows of dU and x, which the GEMM reads
+    // K-outer and transposes while staging its tiles.
     const int rows = p->B * p->T, G3 = 3 * p->n;
     if (dx) {  // dx = dU W_x: B operand W_x^T [d, 3n]
       HIPCHK(launch_transpose(w->W_x, ws + pl.off_wt, G3, p->d, (int)es, s));
@@ -1096,17 +1095,15 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
       gm.vec_b = gm.vec_a;
       HIPCHK(launch_gemm(gm, s));
     }
-    if (dW && dW->W_x) {  // dW_x = dU^T x: operands dU^T [3n, rows] (in U's space) and x^T [d, rows]
-      HIPCHK(launch_transpose(ws + pl.off_dU, ws + pl.off_U, rows, G3, (int)es, s));
-      HIPCHK(launch_transpose(x, ws + pl.off_xt, rows, p->d, (int)es, s));
+    if (dW && dW->W_x) {  // dW_x = dU^T x: dU [rows, 3n] and x [rows, d], both K-outer
       GemmArgs gm{};
-      gm.A = ws + pl.off_U; gm.B = ws + pl.off_xt; gm.C = dW->W_x; gm.bias = nullptr;
+      gm.A = ws + pl.off_dU; gm.B = x; gm.C = dW->W_x; gm.bias = nullptr;
       gm.ws = (float *)(ws + pl.off_gws);
-      gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = rows; gm.ldb = rows; gm.ldc = p->d;
+      gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d;
       gm.splits = gemm_splits(G3, p->d, rows);
-      gm.a_kc = true; gm.b_kc = true; gm.bf16 = bf; gm.out_f32 = true;
-      gm.vec_a = ((size_t)rows * es) % 16 == 0;
-      gm.vec_b = gm.vec_a;
+      gm.a_kc = false; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = true;
+      gm.vec_a = ((size_t)G3 * es) % 16 == 0;
+      gm.vec_b = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
       HIPCHK(launch_gemm(gm, s));
     }
     tr.end(TR_AGEMM, tg, s);

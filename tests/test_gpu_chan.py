@@ -191,11 +191,12 @@ def test_adjoint_bf16_reduced(cfg):
 
 
 @pytest.mark.parametrize("cell", [sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG])
-@pytest.mark.parametrize("B,T,d,n", [(3, 704, 264, 304), (1, 512, 512, 256)])
+@pytest.mark.parametrize("B,T,d,n", [(3, 704, 264, 304), (1, 512, 512, 256), (3, 701, 264, 304)])
 def test_bf16_large_products(cell, B, T, d, n):
     """Shapes that take the 256 x 256-tile bf16 products in all three places
-    (input projection with bias, dx = dU W_x, dW_x = dU^T x), with ragged
-    row, column and K tails (first case) and exact tile multiples (second)."""
+    (input projection with bias, dx = dU W_x, dW_x = dU^T x read K-outer),
+    with ragged row and column tails (first case), exact tile multiples
+    (second) and a K tail of the K-outer product (third: 2103 rows)."""
     p = sy.custom_problem(cell, B=B, T=T, d=d, n=n, seed=T + n, w_scale=0.8, h0=True, dtype=sy.DT_BF16)
     say("large-product case", p["name"], "B", B, "T", T, "d", d, "n", n)
     dp, h = check_solve(p, 0.0, 3, True)
