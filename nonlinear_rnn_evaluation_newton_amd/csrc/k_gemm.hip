@@ -228,13 +228,18 @@ constexpr int GQ = BT * (BK / 8) / GT;  // 16-byte staging chunks per operand pe
 // KO = true: both operands stored K-outer (A [K, lda], B [K, ldb]; the
 // products over the time rows).  Each thread loads a 4 (k) x 8 (m) block as
 // four 16-byte row pieces, transposes it with byte permutes and writes eight
-// 8-byte k-runs, so the tiles land K-contiguous as in the other layout.  Rows
-// are unpadded (64 k) and their 16-byte k-chunks XOR-swizzled by
-// sw(m) = (m ^ (m >> 3)) & 7, which spreads both these writes (one m of each
-// thread's 8 per instruction, 32 m-groups) and the fragment reads (32
-// consecutive rows, two adjacent chunks) evenly over the banks.
-__device__ inline int ko_sw(int m) { return (m ^ (m >> 3)) & 7; }
-constexpr int BKO = BK;  // row length of the K-outer layout (elements)
+// 8-byte k-runs, so the tiles land K-contiguous as in the other layout.  Two
+// unpadded rows (64 k each) share a 256-byte line of 16 chunks of 8 k, and
+// chunk ((m & 1) << 3 | k / 8) of line L = m / 2 sits at slot chunk ^ g(L),
+// g(L) = ((L >> 2) ^ 2 (L & 3)) & 15: each 32-lane phase of the 8-byte
+// writes (16 m-groups, both k-row parities) and each 16-lane phase of the
+// 16-byte fragment reads (16 consecutive rows) then covers all 64 banks once.
+__device__ inline int ko_slot(int m, int chunk) {
+  const int L = m >> 1;
+  return ((((m & 1) << 3) | chunk) ^ ((L >> 2) ^ ((L & 3) << 1))) & 15;
+}
+__device__ inline int ko_index(int m, int chunk) { return (m >> 1) * 128 + ko_slot(m, chunk) * 8; }
+constexpr int BKO = BK;  // elements per row of the K-outer layout
 
 template <typename TO, bool KO>
 __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int tiles_m, int tiles_n) {
@@ -273,7 +278,9 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
     srow[q] = e >> 3;
     skc[q] = (e & 7) * 8;
   }
-  const int ko_mg = tid & 31, ko_k = (tid >> 5) * 4;
+  // K-outer staging: m-group (8 columns) and first of 4 K rows; a
+  // wavefront's even lanes take one K row group, odd lanes the next
+  const int ko_mg = (tid & 63) >> 1, ko_k = ((tid >> 6) * 2 + (tid & 1)) * 4;
   const bool ko_ina = m0 + ko_mg * 8 < g.M, ko_inb = n0 + ko_mg * 8 < g.N;
   gu32x4 va[GQ], vb[GQ];
   auto gload = [&](int k0) {
@@ -303,8 +310,7 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
       const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
       const unsigned lo = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
       const unsigned hi = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
-      const int m = ko_mg * 8 + c;
-      const int idx = m * BKO + (((ko_k >> 3) ^ ko_sw(m)) << 3) + (ko_k & 7);
+      const int idx = ko_index(ko_mg * 8 + c, ko_k >> 3) + (ko_k & 7);
       *reinterpret_cast<unsigned long long *>(&dst[idx]) = ((unsigned long long)hi << 32) | lo;
     }
   };
@@ -351,15 +357,11 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
       if constexpr (KO) {
         const int kc = (ks + kl) >> 3;
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-          const int r = arow + i * 32;
-          a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + r * BKO + ((kc ^ ko_sw(r)) << 3));
-        }
+        for (int i = 0; i < FM; i++)
+          a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + ko_index(arow + i * 32, kc));
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-          const int r = brow + j * 32;
-          b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + r * BKO + ((kc ^ ko_sw(r)) << 3));
-        }
+        for (int j = 0; j < FN; j++)
+          b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + ko_index(brow + j * 32, kc));
       } else {
 #pragma unroll
         for (int i = 0; i < FM; i++)
