@@ -233,6 +233,52 @@ hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void
   return launch_gemm(g, s);
 }
 
+// Dense GRUs the n = 64 kernels run zero-padded (see padded_solve): fp32,
+// n < 64, outside the time-parallel kernels' range (n > 8 or d > 8).
+static bool pad_gru(const pr_problem *p) {
+  return p && p->cell == PR_CELL_GRU && p->dtype == PR_F32 && p->B >= 1 && p->T >= 1 && p->d >= 1 && p->n >= 1 &&
+         p->n < D64_N && !(p->n <= 8 && p->d <= DX_FUSED) &&
+         (p->jac == PR_JAC_DENSE || p->jac == PR_JAC_DIAG || p->jac == PR_JAC_ZERO) &&
+         (long long)p->B * p->T <= 2147483647LL;
+}
+struct PadLayout {
+  size_t wx = 0, bx = 0, wh = 0, bh = 0, h0 = 0, h = 0, g = 0, lam = 0, dh0 = 0, dwx = 0, dbx = 0, dwh = 0, dbh = 0;
+  size_t bytes = 0;
+};
+static PadLayout pad_layout(const pr_problem *p, bool adj) {
+  PadLayout L;
+  size_t o = 0;
+  const size_t rows = (size_t)p->B * p->T, N = D64_N, G3 = 3 * N;
+  L.wx = o; o = align256(o + G3 * p->d * 4);
+  L.bx = o; o = align256(o + G3 * 4);
+  L.wh = o; o = align256(o + G3 * N * 4);
+  L.bh = o; o = align256(o + G3 * 4);
+  L.h0 = o; o = align256(o + (size_t)p->B * N * 4);
+  L.h = o; o = align256(o + rows * N * 4);
+  if (adj) {
+    L.g = o; o = align256(o + rows * N * 4);
+    L.lam = o; o = align256(o + rows * N * 4);
+    L.dh0 = o; o = align256(o + (size_t)p->B * N * 4);
+    L.dwx = o; o = align256(o + G3 * p->d * 4);
+    L.dbx = o; o = align256(o + G3 * 4);
+    L.dwh = o; o = align256(o + G3 * N * 4);
+    L.dbh = o; o = align256(o + G3 * 4);
+  }
+  L.bytes = o;
+  return L;
+}
+static pr_problem padded(const pr_problem *p) {
+  pr_problem q = *p;
+  q.n = D64_N;
+  return q;
+}
+static int padded_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                        int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
+                        size_t ws_bytes, void *stream, const float *elk_lambda);
+static int padded_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
+                          void *stream, bool with_solve);
 int kcell(int cell) { return cell == PR_CELL_TANH_RNN ? C_TANH : cell == PR_CELL_LINEAR ? C_LINEAR : C_GRU; }
 
 bool al16(const void *q) { return q == nullptr || ((uintptr_t)q & 15) == 0; }
@@ -427,6 +473,11 @@ int pararnn_trace_read(double *sweep_ms, long long *sweep_launches, double *adjo
 
 size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint) {
   Plan pl;
+  if (pad_gru(p)) {
+    const pr_problem q = padded(p);
+    if (make_plan(&q, &pl) != PR_OK) return 0;
+    return pad_layout(p, with_adjoint != 0).bytes + (with_adjoint ? pl.adjoint_bytes : pl.solve_bytes);
+  }
   if (make_plan(p, &pl) != PR_OK) return 0;
   return with_adjoint ? pl.adjoint_bytes : pl.solve_bytes;
 }
@@ -879,12 +930,20 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
 int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol, int max_iters,
                   void *h, int *iters, float *delta_hist, int hist_cap, void *workspace, size_t ws_bytes,
                   void *stream) {
+  if (pad_gru(p))
+    return padded_solve(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
+                        nullptr);
   return solve_impl(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
                     nullptr);
 }
 
 size_t pararnn_elk_workspace_bytes(const pr_problem *p) {
   g_err.clear();
+  if (pad_gru(p)) {
+    const pr_problem q = padded(p);
+    const size_t inner = pararnn_elk_workspace_bytes(&q);
+    return inner ? pad_layout(p, true).bytes + inner : 0;
+  }
   Plan pl;
   if (make_plan(p, &pl) != PR_OK) return 0;
   ElkLayout el;
@@ -895,6 +954,9 @@ size_t pararnn_elk_workspace_bytes(const pr_problem *p) {
 int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float lambda,
                       float tol, int max_iters, void *h, int *iters, float *delta_hist, int hist_cap,
                       void *workspace, size_t ws_bytes, void *stream) {
+  if (pad_gru(p))
+    return padded_solve(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
+                        &lambda);
   return solve_impl(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, workspace, ws_bytes, stream,
                     &lambda);
 }
@@ -902,6 +964,9 @@ int pararnn_solve_elk(const pr_problem *p, const pr_weights *w, const void *x, c
 int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                     const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
                     size_t ws_bytes, void *stream) {
+  if (pad_gru(p))
+    return padded_adjoint(p, w, x, h0, 0.f, 1, (void *)h, nullptr, nullptr, 0, g, lambda, dx, dh0, dW, workspace,
+                          ws_bytes, stream, false);
   return adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, false, false);
 }
 
@@ -1112,12 +1177,10 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
   return fail(PR_EUNSUPPORTED, "no adjoint kernel for this problem");
 }
 
-extern "C" {
-
-int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
-                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
-                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
-                          void *stream) {
+static int solve_adjoint_core(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                              int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                              void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
+                              size_t ws_bytes, void *stream) {
   if (p && workspace && ws_bytes < pararnn_workspace_bytes(p, 1))
     return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, pararnn_workspace_bytes(p, 1));
   SpecAdjoint sa;
@@ -1134,6 +1197,162 @@ int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *
   if (rc == PR_NONFINITE) return rc;
   const int ra = adjoint_impl(p, w, x, h0, h, g, lambda, dx, dh0, dW, workspace, ws_bytes, stream, true, !sa.ran);
   return ra < 0 ? ra : rc;
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Dense GRUs of other widths on the n = 64 kernels.  Padded with zero
+// weights, biases and initial state, the extra channels stay exactly 0 (their
+// gates are 1/2 and their candidate tanh(0) = 0) and the Jacobian has no
+// entry between them and the real channels, so every sweep's update, the stop
+// measure, the sweep count and the adjoint of the real channels are those of
+// the unpadded problem.  The padded weights, states and gradients live at the
+// front of the workspace; the results are copied back.
+// ---------------------------------------------------------------------------
+// The padded weights (and h0) into the workspace; w64 / h0p point at them.
+static int pad_inputs(const pr_problem *p, const pr_weights *w, const void *h0, char *ws, const PadLayout &L,
+                      pr_weights *w64, const void **h0p, hipStream_t s) {
+  if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
+  const int n = p->n, d = p->d, N = D64_N;
+  *w64 = pr_weights{};
+  HIPCHK(launch_pad_gates((const float *)w->W_x, 3, n, d, (float *)(ws + L.wx), N, d, s));
+  HIPCHK(launch_pad_gates((const float *)w->W_h, 3, n, n, (float *)(ws + L.wh), N, N, s));
+  w64->W_x = ws + L.wx;
+  w64->W_h = ws + L.wh;
+  if (w->b_x) {
+    HIPCHK(launch_pad_gates((const float *)w->b_x, 3, n, 1, (float *)(ws + L.bx), N, 1, s));
+    w64->b_x = ws + L.bx;
+  }
+  if (w->b_h) {
+    HIPCHK(launch_pad_gates((const float *)w->b_h, 3, n, 1, (float *)(ws + L.bh), N, 1, s));
+    w64->b_h = ws + L.bh;
+  }
+  *h0p = nullptr;
+  if (h0) {
+    HIPCHK(launch_pad_gates((const float *)h0, 1, p->B, n, (float *)(ws + L.h0), p->B, N, s));
+    *h0p = ws + L.h0;
+  }
+  return PR_OK;
+}
+// [rows, 64] -> [rows, n]
+static hipError_t unpad_state(const void *src, long long rows, int n, void *dst, hipStream_t s) {
+  return launch_unpad_gates((const float *)src, 1, (int)rows, n, (float *)dst, (int)rows, D64_N, s);
+}
+// Workspace of the padded problem q for a solve (kind 0), an adjoint (1) or
+// an ELK solve (2); returns the plan's error code and message if q has none.
+static int padded_inner_bytes(const pr_problem *q, int kind, size_t *bytes) {
+  *bytes = 0;
+  Plan pl;
+  int rc = make_plan(q, &pl);
+  if (rc != PR_OK) return rc;
+  if (kind == 2) {
+    ElkLayout el;
+    rc = elk_layout(q, pl, &el);
+    if (rc != PR_OK) return rc;
+    *bytes = el.bytes > pl.adjoint_bytes ? el.bytes : pl.adjoint_bytes;
+  } else {
+    *bytes = kind == 1 ? pl.adjoint_bytes : pl.solve_bytes;
+  }
+  return PR_OK;
+}
+static int pad_workspace_check(const pr_problem *q, int kind, const PadLayout &L, void *workspace, size_t ws_bytes) {
+  size_t inner = 0;
+  const int rc = padded_inner_bytes(q, kind, &inner);
+  if (rc != PR_OK) return rc;
+  if (!workspace || ws_bytes < L.bytes + inner)
+    return fail(PR_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, L.bytes + inner);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PR_EINVAL, "workspace must be 256-byte aligned");
+  return PR_OK;
+}
+
+static int padded_solve(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                        int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, void *workspace,
+                        size_t ws_bytes, void *stream, const float *elk_lambda) {
+  g_err.clear();
+  if (!x || !h) return fail(PR_EINVAL, "x and h are required");
+  if (max_iters < 1) return fail(PR_EINVAL, "max_iters must be >= 1");
+  if (elk_lambda && (!(*elk_lambda >= 0.f) || *elk_lambda > 3.0e38f))
+    return fail(PR_EINVAL, "lambda must be >= 0 and finite");
+  const pr_problem q = padded(p);
+  const PadLayout L = pad_layout(p, elk_lambda != nullptr);
+  int rc = pad_workspace_check(&q, elk_lambda ? 2 : 0, L, workspace, ws_bytes);
+  if (rc != PR_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  pr_weights w64;
+  const void *h0p;
+  rc = pad_inputs(p, w, h0, ws, L, &w64, &h0p, s);
+  if (rc != PR_OK) return rc;
+  rc = solve_impl(&q, &w64, x, h0p, tol, max_iters, ws + L.h, iters, delta_hist, hist_cap, ws + L.bytes,
+                  ws_bytes - L.bytes, stream, elk_lambda);
+  if (rc < 0) return rc;
+  HIPCHK(unpad_state(ws + L.h, (long long)p->B * p->T, p->n, h, s));
+  return rc;
+}
+
+static int padded_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
+                          void *stream, bool with_solve) {
+  g_err.clear();
+  if (!x || !h || !g) return fail(PR_EINVAL, "x, h and g are required");
+  if (with_solve && max_iters < 1) return fail(PR_EINVAL, "max_iters must be >= 1");
+  const pr_problem q = padded(p);
+  const PadLayout L = pad_layout(p, true);
+  int rc = pad_workspace_check(&q, 1, L, workspace, ws_bytes);
+  if (rc != PR_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  const long long rows = (long long)p->B * p->T;
+  const int n = p->n, d = p->d, N = D64_N;
+  pr_weights w64;
+  const void *h0p;
+  rc = pad_inputs(p, w, h0, ws, L, &w64, &h0p, s);
+  if (rc != PR_OK) return rc;
+  HIPCHK(launch_pad_gates((const float *)g, 1, (int)rows, n, (float *)(ws + L.g), (int)rows, N, s));
+  pr_grads g64{};
+  if (dW) {
+    g64.W_x = dW->W_x ? (float *)(ws + L.dwx) : nullptr;
+    g64.b_x = dW->b_x ? (float *)(ws + L.dbx) : nullptr;
+    g64.W_h = dW->W_h ? (float *)(ws + L.dwh) : nullptr;
+    g64.b_h = dW->b_h ? (float *)(ws + L.dbh) : nullptr;
+  }
+  void *dh0p = dh0 ? ws + L.dh0 : nullptr;
+  if (with_solve) {
+    rc = solve_adjoint_core(&q, &w64, x, h0p, tol, max_iters, ws + L.h, iters, delta_hist, hist_cap, ws + L.g,
+                            ws + L.lam, dx, dh0p, dW ? &g64 : nullptr, ws + L.bytes, ws_bytes - L.bytes, stream);
+    if (rc < 0) return rc;
+    HIPCHK(unpad_state(ws + L.h, rows, n, h, s));
+    if (rc == PR_NONFINITE) return rc;
+  } else {
+    HIPCHK(launch_pad_gates((const float *)h, 1, (int)rows, n, (float *)(ws + L.h), (int)rows, N, s));
+    rc = adjoint_impl(&q, &w64, x, h0p, ws + L.h, ws + L.g, ws + L.lam, dx, dh0p, dW ? &g64 : nullptr, ws + L.bytes,
+                      ws_bytes - L.bytes, stream, false, false);
+    if (rc < 0) return rc;
+  }
+  if (lambda) HIPCHK(unpad_state(ws + L.lam, rows, n, lambda, s));
+  if (dh0) HIPCHK(unpad_state(ws + L.dh0, p->B, n, dh0, s));
+  if (dW && dW->W_x) HIPCHK(launch_unpad_gates((const float *)(ws + L.dwx), 3, n, d, dW->W_x, N, d, s));
+  if (dW && dW->b_x) HIPCHK(launch_unpad_gates((const float *)(ws + L.dbx), 3, n, 1, dW->b_x, N, 1, s));
+  if (dW && dW->W_h) HIPCHK(launch_unpad_gates((const float *)(ws + L.dwh), 3, n, n, dW->W_h, N, N, s));
+  if (dW && dW->b_h) HIPCHK(launch_unpad_gates((const float *)(ws + L.dbh), 3, n, 1, dW->b_h, N, 1, s));
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pararnn_solve_adjoint(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, float tol,
+                          int max_iters, void *h, int *iters, float *delta_hist, int hist_cap, const void *g,
+                          void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  if (pad_gru(p))
+    return padded_adjoint(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, g, lambda, dx, dh0, dW,
+                          workspace, ws_bytes, stream, true);
+  return solve_adjoint_core(p, w, x, h0, tol, max_iters, h, iters, delta_hist, hist_cap, g, lambda, dx, dh0, dW,
+                            workspace, ws_bytes, stream);
 }
 
 static bool lsim_sizes_ok(int B, int T, int nx, int m, int p) {

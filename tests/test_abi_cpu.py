@@ -65,7 +65,8 @@ def test_workspace_bytes_for_approximate_jacobians():
     (dict(jac=4), bd.PR_EINVAL), (dict(jac=-1), bd.PR_EINVAL),
     (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL),
     (dict(cell=sy.CELL_LSTM_CIFG_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
-    (dict(cell=sy.CELL_GRU, jac=bd.PR_JAC_DIAG, n=13), bd.PR_EUNSUPPORTED),
+    (dict(cell=sy.CELL_GRU, jac=bd.PR_JAC_DIAG, n=65), bd.PR_EUNSUPPORTED),
+    (dict(cell=sy.CELL_GRU, dtype=bd.PR_BF16, n=13), bd.PR_EUNSUPPORTED),
     (dict(cell=sy.CELL_TANH_RNN, jac=bd.PR_JAC_ZERO, n=64), bd.PR_EUNSUPPORTED),
 ])
 def test_invalid_problems_rejected_without_device(kw, code):
@@ -77,6 +78,53 @@ def test_invalid_problems_rejected_without_device(kw, code):
                          C.c_void_p(256), 1 << 30, None)
     assert rc == code, bd.last_error()
     assert bd.last_error() != ""
+
+
+@pytest.mark.parametrize("jac", [sy.JAC_DENSE, sy.JAC_DIAG, sy.JAC_ZERO])
+@pytest.mark.parametrize("n,d", [(13, 1), (63, 40), (5, 20), (1, 9)])
+def test_dense_gru_padded_to_64_workspace(n, d, jac):
+    """Dense GRUs with n < 64 outside the time-parallel kernels' range (n > 8
+    or d > 8) run on the n = 64 kernels zero-padded: their workspace is the
+    n = 64 problem's plus the padded copies of weights, states and gradients."""
+    pb = _prob(n=n, d=d, jac=jac, B=3, T=100)
+    q = _prob(n=64, d=d, jac=jac, B=3, T=100)
+    for adj in (False, True):
+        assert bd.workspace_bytes(pb, adj) > bd.workspace_bytes(q, adj) > 0
+    if jac == sy.JAC_DIAG:
+        assert bd.elk_workspace_bytes(pb) > bd.elk_workspace_bytes(q) > 0
+    else:
+        assert bd.elk_workspace_bytes(pb) == 0
+
+
+def test_padded_dense_gru_arguments_rejected_without_device():
+    L = bd.lib()
+    pb = _prob(n=20, d=3)
+    w = bd.Weights(1, None, 1, None, None)
+    v = C.c_void_p(16)
+    ws = bd.workspace_bytes(pb, False)
+    full = bd.workspace_bytes(pb, True)
+
+    def solve(n=ws, x=v, h=v, wp=w, it=8, base=256):
+        return L.pararnn_solve(C.byref(pb), C.byref(wp), x, None, 1e-6, it, h, None, None, 0, C.c_void_p(base), n,
+                               None)
+
+    assert solve(n=ws - 1) == bd.PR_EWORKSPACE and "workspace" in bd.last_error()
+    assert solve(x=None) == bd.PR_EINVAL and solve(h=None) == bd.PR_EINVAL and solve(it=0) == bd.PR_EINVAL
+    assert solve(wp=bd.Weights(None, None, 1, None, None)) == bd.PR_EINVAL
+    assert solve(base=264) == bd.PR_EINVAL  # not 256-byte aligned
+    assert L.pararnn_solve_adjoint(C.byref(pb), C.byref(w), v, None, 1e-6, 8, v, None, None, 0, v, None, None, None,
+                                   None, C.c_void_p(256), full - 1, None) == bd.PR_EWORKSPACE
+    assert L.pararnn_adjoint(C.byref(pb), C.byref(w), v, None, v, None, None, None, None, None, C.c_void_p(256), full,
+                             None) == bd.PR_EINVAL  # g is required
+    dense = _prob(n=20, d=3)
+    assert L.pararnn_solve_elk(C.byref(dense), C.byref(w), v, None, 0.5, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
+                               1 << 40, None) == bd.PR_EUNSUPPORTED
+    quasi = _prob(n=20, d=3, jac=sy.JAC_DIAG)
+    ews = bd.elk_workspace_bytes(quasi)
+    assert L.pararnn_solve_elk(C.byref(quasi), C.byref(w), v, None, -1.0, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
+                               ews, None) == bd.PR_EINVAL
+    assert L.pararnn_solve_elk(C.byref(quasi), C.byref(w), v, None, 0.5, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
+                               ews - 1, None) == bd.PR_EWORKSPACE
 
 
 def test_missing_pointers_and_workspace_rejected():

@@ -1,0 +1,187 @@
+"""GPU parity of dense GRUs narrower than 64 that run on the n = 64 kernels
+zero-padded (n in 9..63, or n <= 8 with d > 8): DEER, quasi-DEER, Jacobi,
+quasi-ELK and the adjoint against the fp64 oracle of the unpadded problem,
+and the combined solve + adjoint against the separate calls."""
+import numpy as np
+import pytest
+
+import oracle
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ATOL = 1e-4
+RTOL_W = 1e-4
+TOL_MARGIN, TOL_NOISE = 0.05, 2e-7
+APPROX = {sy.JAC_DENSE: oracle.NEWTON, sy.JAC_DIAG: oracle.QUASI, sy.JAC_ZERO: oracle.JACOBI}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def problem(n, d, B, T, seed, jac=sy.JAC_DENSE, w_scale=0.8):
+    p = sy.custom_problem(sy.CELL_GRU, B=B, T=T, d=d, n=n, seed=seed, w_scale=w_scale, h0=True)
+    return dict(p, jac=jac)
+
+
+def agree(it, ito, dlo, tol):
+    if it == ito:
+        return True
+    k = min(it, ito)
+    return abs(it - ito) == 1 and tol > 0 and abs(dlo[k - 1] - tol) <= max(TOL_MARGIN * tol, TOL_NOISE)
+
+
+def check_solve(p, tol, max_iters, lam=None):
+    say("case padded GRU n", p["n"], "d", p["d"], "B", p["B"], "T", p["T"], "jac", p["jac"], "tol", tol,
+        "max_iters", max_iters, "elk lambda", lam)
+    dp = bd.DeviceProblem(p, elk=lam is not None)
+    if lam is None:
+        st, it, dl = dp.solve(tol=tol, max_iters=max_iters, hist_cap=4096)
+        ref = lambda t, m: oracle.deer(p, tol=t, max_iters=m, approx=APPROX[p["jac"]])
+    else:
+        st, it, dl = dp.solve_elk(lam, tol=tol, max_iters=max_iters, hist_cap=4096)
+        ref = lambda t, m: oracle.elk(p, lam, tol=t, max_iters=m)
+    torch.cuda.synchronize()
+    ho, ito, sto, dlo = ref(tol, max_iters)
+    say("  gpu", it, st, dl[-3:], "| oracle", ito, sto, dlo[-3:])
+    assert agree(it, ito, dlo, tol)
+    if it != ito:
+        ho, ito, sto, dlo = ref(0.0, it)
+    else:
+        assert st == sto
+    err = np.abs(to64(dp.h) - ho).max()
+    m = min(len(dl), len(dlo))
+    say("  max abs err", err)
+    assert err <= ATOL
+    assert np.allclose(dl[:m], dlo[:m], rtol=1e-3, atol=ATOL)
+    return dp
+
+
+@pytest.mark.parametrize("n,d,B,T", [(12, 3, 2, 300), (33, 40, 3, 129), (63, 7, 2, 65), (5, 20, 2, 200),
+                                     (1, 9, 3, 64), (9, 1, 1, 1), (48, 64, 2, 1000)])
+def test_deer_converged(n, d, B, T):
+    p = problem(n, d, B, T, seed=n * 7 + d)
+    check_solve(p, 1e-6, T)
+
+
+@pytest.mark.parametrize("n,d", [(20, 5), (63, 16)])
+def test_deer_fixed_sweeps(n, d):
+    p = problem(n, d, 2, 257, seed=n + d)
+    for k in (1, 2, 3):
+        check_solve(p, 0.0, k)
+
+
+@pytest.mark.parametrize("jac", [sy.JAC_DIAG, sy.JAC_ZERO])
+@pytest.mark.parametrize("n,d,B,T", [(12, 3, 2, 300), (40, 24, 2, 129), (5, 20, 1, 100)])
+def test_quasi_and_jacobi(jac, n, d, B, T):
+    p = problem(n, d, B, T, seed=n + 3 * d, jac=jac)
+    check_solve(p, 1e-5, T)
+    check_solve(p, 0.0, 2)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3, 3.0])
+@pytest.mark.parametrize("n,d,T", [(17, 4, 200), (63, 33, 65)])
+def test_quasi_elk(lam, n, d, T):
+    p = problem(n, d, 2, T, seed=n + T, jac=sy.JAC_DIAG)
+    for k in (1, 3):
+        check_solve(p, 0.0, k, lam)
+    check_solve(p, 1e-5, T, lam)
+
+
+def adjoint_check(p, dp, a):
+    ref = oracle.adjoint(p, to64(dp.h))
+    for key in ("lam", "dx", "dh0"):
+        err = np.abs(to64(a[key]) - ref[key]).max()
+        say("  ", key, err)
+        assert err <= ATOL * max(1.0, np.abs(ref[key]).max()), key
+    for key in ("dW_x", "db_x", "dW_h", "db_h"):
+        r = np.abs(to64(a[key]) - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30)
+        say("  ", key, r)
+        assert r <= RTOL_W, key
+
+
+@pytest.mark.parametrize("n,d,B,T", [(12, 3, 2, 300), (33, 40, 3, 129), (63, 7, 1, 64), (5, 20, 2, 100)])
+def test_adjoint(n, d, B, T):
+    p = problem(n, d, B, T, seed=2 * n + d)
+    say("adjoint padded GRU n", n, "d", d, "B", B, "T", T)
+    dp = bd.DeviceProblem(p)
+    dp.solve()
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_check(p, dp, a)
+
+
+def test_solve_adjoint_matches_separate_calls():
+    p = problem(33, 10, 2, 300, seed=4)
+    say("solve_adjoint padded GRU n 33")
+    dp = bd.DeviceProblem(p)
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def outs():
+        return dict(lam=torch.full_like(dp.h, float("nan")), dx=torch.full_like(dp.x, float("nan")),
+                    dh0=torch.full((p["B"], p["S"]), float("nan"), dtype=dp.tdtype, device="cuda"),
+                    W_x=torch.full(tuple(dp.W_x.shape), float("nan"), **f32),
+                    b_x=torch.full(tuple(dp.b_x.shape), float("nan"), **f32),
+                    W_h=torch.full(tuple(dp.W_h.shape), float("nan"), **f32),
+                    b_h=torch.full(tuple(dp.b_h.shape), float("nan"), **f32))
+
+    gk = ("W_x", "b_x", "W_h", "b_h")
+    st1, it1, dl1 = dp.solve()
+    o1 = outs()
+    ra = bd.adjoint(dp.prob, dp.w, dp.x, dp.h0, dp.h, dp.g, dp.ws, o1["lam"], o1["dx"], o1["dh0"],
+                    {k: o1[k] for k in gk})
+    torch.cuda.synchronize()
+    h1 = dp.h.clone()
+    dp.h.fill_(float("nan"))
+    o2 = outs()
+    st2, it2, dl2 = bd.solve_adjoint(dp.prob, dp.w, dp.x, dp.h0, p["tol"], p["max_iters"], dp.h, dp.g, dp.ws,
+                                     o2["lam"], o2["dx"], o2["dh0"], {k: o2[k] for k in gk})
+    torch.cuda.synchronize()
+    say("  separate", st1, it1, ra, "| combined", st2, it2)
+    assert st1 == bd.PR_OK and ra == bd.PR_OK and (st2, it2) == (st1, it1)
+    assert np.array_equal(dl1, dl2)
+    assert torch.equal(dp.h, h1)
+    for k in o1:
+        assert torch.equal(o1[k], o2[k]), k
+    adjoint_check(p, dp, dict(o2, dW_x=o2["W_x"], db_x=o2["b_x"], dW_h=o2["W_h"], db_h=o2["b_h"]))
+
+
+def test_zero_padded_equals_explicit_64():
+    """The padded run is the n = 64 run on the explicitly zero-padded problem:
+    the same sweep count and deltas, and its first n channels bit for bit."""
+    n, d = 21, 6
+    p = problem(n, d, 2, 200, seed=9)
+    N = 64
+
+    def pad_rows(a, cols_p):
+        a = np.asarray(a).reshape(3, n, -1)
+        out = np.zeros((3, N, cols_p))
+        out[:, :n, :a.shape[2]] = a
+        return out.reshape(3 * N, cols_p) if cols_p > 1 else out.reshape(3 * N)
+
+    q = dict(p, n=N, S=N, W_x=pad_rows(p["W_x"], d), W_h=pad_rows(p["W_h"], N), b_x=pad_rows(p["b_x"], 1),
+             b_h=pad_rows(p["b_h"], 1), h0=np.pad(p["h0"], ((0, 0), (0, N - n))),
+             g=np.pad(p["g"], ((0, 0), (0, 0), (0, N - n))))
+    dp, dq = bd.DeviceProblem(p), bd.DeviceProblem(q)
+    sp, ip, lp = dp.solve()
+    sq, iq, lq = dq.solve()
+    torch.cuda.synchronize()
+    say("  padded", sp, ip, "| explicit 64", sq, iq)
+    assert (sp, ip) == (sq, iq) and np.array_equal(lp, lq)
+    assert torch.equal(dp.h, dq.h[:, :, :n])
+    assert torch.count_nonzero(dq.h[:, :, n:]) == 0
