@@ -466,6 +466,199 @@ __global__ __launch_bounds__(GT, 1) void k_gemm_bf16_nt(const GemmArgs g, int ti
   }
 }
 
+// Direct staging for K-contiguous operands: each 16-byte buffer load writes
+// LDS straight from memory (buffer_load ... lds: lane l of an instruction
+// fills bytes 16 l .. 16 l + 15 of a 1 KB run whose base is wavefront-
+// uniform), so operands take no registers and no LDS store instructions on
+// their way in.  Two stages of one 64-wide K step each; the loads of step
+// j + 1 are issued at the start of step j.  The layout is set by which chunk
+// each lane fetches: tile rows are 64 k (128 bytes) unpadded, and 8-element
+// chunk c of row r sits at slot c ^ ((r >> 1) & 7), which spreads each
+// 16-lane phase of the fragment reads (16 consecutive rows, one chunk) over
+// all 64 banks.  Out-of-range offsets write zeros, as the register path
+// reads them.
+//
+// Wavefront grid DWM x DWN over the 256 x 256 tile: 2 x 4 wavefronts of
+// 128 x 64, two per SIMD, so one wavefront's waits overlap the other's MFMAs
+// (2 x 2 wavefronts of 128 x 128, one per SIMD, read a third less LDS per
+// MFMA but ran 25% slower: nothing hides a lone wavefront's waits).
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ inline int dl_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// Wait until this wavefront's direct loads have landed and its LDS reads are
+// done, then meet the other wavefronts.  Empty asm statements with a memory
+// clobber keep every memory access on its side of the barrier.
+__device__ inline void dl_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+#ifndef PR_DWM
+#define PR_DWM 2
+#define PR_DWN 4
+#endif
+constexpr int DWM = PR_DWM, DWN = PR_DWN, DFM = BT / 32 / DWM, DFN = BT / 32 / DWN, DGT = 64 * DWM * DWN;
+constexpr int DQ = BT * BK / 8 / DGT;  // direct loads per operand per thread and K step
+
+template <typename TO>
+__global__ __launch_bounds__(DGT, 1) void k_gemm_bf16_dl(const GemmArgs g, int tiles_m, int tiles_n) {
+  // one array per stage (A tile, then B tile), so the compiler can tell the
+  // stage being loaded from the one being read
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BT * BK], s1[2 * BT * BK];
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / DWN, wn = wid % DWN;
+  const int tiles = tiles_m * tiles_n;
+  int id = blockIdx.x;
+  if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
+  constexpr int GM = 8;
+  const int width = GM * tiles_n, fm = (id / width) * GM;
+  const int gm = min(tiles_m - fm, GM);
+  const int tm = fm + (id % width) % gm, tn = (id % width) / gm;
+  const int m0 = tm * BT, n0 = tn * BT;
+  const int split = blockIdx.y;
+  const int kchunk = ((g.K + g.splits - 1) / g.splits + BK - 1) / BK * BK;
+  const int kb = split * kchunk, ke = min(g.K, kb + kchunk);
+
+  const uint16_t *A = (const uint16_t *)g.A + (size_t)m0 * g.lda;
+  const uint16_t *B = (const uint16_t *)g.B + (size_t)n0 * g.ldb;
+  const GRsrc ra = g_rsrc(A, (unsigned)(min(BT, g.M - m0) * g.lda * 2));
+  const GRsrc rb = g_rsrc(B, (unsigned)(min(BT, g.N - n0) * g.ldb * 2));
+  // instruction q of wavefront w fills slots 64 (DQ w + q) + lane: row
+  // r = 8 (DQ w + q) + lane / 8, physical slot lane % 8, so the chunk swizzle
+  // (r >> 1) & 7 = 4 (q & 1) + lane / 16 (DQ is even) takes two values per
+  // lane; the row's wavefront-uniform part goes in the scalar offset
+  static_assert(DQ % 2 == 0, "even number of direct loads");
+  const int rl = lane >> 3, kce = ((lane & 7) ^ (lane >> 4)) * 8, kco = ((lane & 7) ^ (4 | (lane >> 4))) * 8;
+  const unsigned va_e = (unsigned)(rl * g.lda + kce) * 2u, va_o = (unsigned)(rl * g.lda + kco) * 2u;
+  const unsigned vb_e = (unsigned)(rl * g.ldb + kce) * 2u, vb_o = (unsigned)(rl * g.ldb + kco) * 2u;
+  auto dload = [&](uint16_t *d, int k0) {
+#pragma unroll
+    for (int q = 0; q < DQ; q++) {
+      const int kc = (q & 1) ? kco : kce;
+      const bool in = k0 + kc < ke;
+      const int u = wid * DQ + q;
+      const unsigned sa = (unsigned)(u * 8 * g.lda + k0) * 2u, sb = (unsigned)(u * 8 * g.ldb + k0) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)&d[u * 512], 16,
+                                               in ? ((q & 1) ? va_o : va_e) : 0x80000000u, sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)&d[BT * BK + u * 512], 16,
+                                               in ? ((q & 1) ? vb_o : vb_e) : 0x80000000u, sb, 0, 0);
+    }
+  };
+
+  f32x16_t acc[DFN][DFM];
+#pragma unroll
+  for (int j = 0; j < DFN; j++)
+#pragma unroll
+    for (int i = 0; i < DFM; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[j][i][r] = 0.f;
+
+  if (kb < ke) dload(s0, kb);
+  dl_sync();
+  const int arow = wm * (DFM * 32) + (lane & 31), brow = wn * (DFN * 32) + (lane & 31), kl = lane >> 5;
+  // Per K step: the next step's loads go straight to the other stage (read
+  // by every wavefront before the previous barrier) and have the whole step's
+  // MFMAs to land; fragments of slice q + 1 are read while slice q's MFMAs
+  // run.  The loop is unrolled over the two stages.
+  constexpr int NQ = BK / 16;
+  auto step = [&](const uint16_t *cA, uint16_t *nx, int k0) {
+    const uint16_t *cB = cA + BT * BK;
+    if (k0 + BK < ke) dload(nx, k0 + BK);
+    bf16x8_t a[2][DFM], b[2][DFN];
+    auto frag = [&](int h, int q) {
+      const int c = 2 * q + kl;
+#pragma unroll
+      for (int i = 0; i < DFM; i++) a[h][i] = *reinterpret_cast<const bf16x8_t *>(cA + dl_off(arow + i * 32, c));
+#pragma unroll
+      for (int j = 0; j < DFN; j++) b[h][j] = *reinterpret_cast<const bf16x8_t *>(cB + dl_off(brow + j * 32, c));
+    };
+    frag(0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * DQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DFM + DFN, 0);
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+      if (q + 1 < NQ) frag((q + 1) & 1, q + 1);
+#pragma unroll
+      for (int j = 0; j < DFN; j++)
+#pragma unroll
+        for (int i = 0; i < DFM; i++)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q & 1][j], a[q & 1][i], acc[j][i], 0, 0, 0);
+      if (q + 1 < NQ) {
+#pragma unroll
+        for (int r = 0; r < DFM + DFN; r++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DFM * DFN - (DFM + DFN), 0);
+      }
+    }
+    dl_sync();
+  };
+  // whole pairs of steps, then an odd last one (no join of the accumulators
+  // inside the loop)
+  int k0 = kb;
+  for (; k0 + BK < ke; k0 += 2 * BK) {
+    step(s0, s1, k0);
+    step(s1, s0, k0 + BK);
+  }
+  if (k0 < ke) step(s0, s1, k0);
+
+  // lane holds rows m = (lane & 31) of each 32 x 32 tile and, per group of 4
+  // registers, the 4 adjacent columns 8 * (r / 4) + 4 * (lane / 32) + (0..3)
+  const bool vec_c = g.splits == 1 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0;
+#pragma unroll
+  for (int j = 0; j < DFN; j++) {
+    // the bias and scale of this lane's columns (they do not depend on the row)
+    float bias[4][4], scale[4][4];
+#pragma unroll
+    for (int rg = 0; rg < 4; rg++) {
+      const int n = n0 + wn * (DFN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        bias[rg][c] = (split != 0 || n + c >= g.N) ? 0.f
+                      : g.bias32 ? g.bias32[n + c]
+                      : g.bias ? bf2f(((const uint16_t *)g.bias)[n + c]) : 0.f;
+        scale[rg][c] = (g.scale32 && n + c < g.N) ? g.scale32[n + c] : 1.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DFM; i++) {
+      const int m = m0 + wm * (DFM * 32) + i * 32 + (lane & 31);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int rg = 0; rg < 4; rg++) {
+        const int n = n0 + wn * (DFN * 32) + j * 32 + 8 * rg + 4 * (lane >> 5);
+        if (n >= g.N) continue;
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) v[c] = fmaf(acc[j][i][4 * rg + c], scale[rg][c], bias[rg][c]);
+        if (g.splits > 1) {
+          float *w = g.ws + ((size_t)split * g.M + m) * g.N + n;
+          if (n + 4 <= g.N && (g.N % 4) == 0) *reinterpret_cast<float4 *>(w) = make_float4(v[0], v[1], v[2], v[3]);
+          else
+            for (int c = 0; c < 4 && n + c < g.N; c++) w[c] = v[c];
+          continue;
+        }
+        TO *o = (TO *)g.C + (size_t)m * g.ldc + n;
+        if (vec_c && n + 4 <= g.N) {
+          if constexpr (sizeof(TO) == 2) {
+            uint2 u;
+            u.x = (unsigned)f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16);
+            u.y = (unsigned)f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2 *>(o) = u;
+          } else {
+            *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+          for (int c = 0; c < 4 && n + c < g.N; c++) store_out<TO>(o + c, v[c]);
+        }
+      }
+    }
+  }
+}
+
 // The large-tile kernel takes bf16 products with both operands K-contiguous,
 // 16-byte rows (K, lda, ldb multiples of 8, aligned bases), both output
 // extents of at least one block tile, and 256 rows of either operand within
@@ -484,7 +677,8 @@ static bool big_tn(const GemmArgs &g) {
 template <typename TO, bool KO = false>
 static hipError_t gemm_big_launch(const GemmArgs &g, hipStream_t s) {
   const int tm = (g.M + BT - 1) / BT, tn = (g.N + BT - 1) / BT;
-  hipLaunchKernelGGL((k_gemm_bf16_nt<TO, KO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
+  if constexpr (KO) hipLaunchKernelGGL((k_gemm_bf16_nt<TO, KO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
+  else hipLaunchKernelGGL((k_gemm_bf16_dl<TO>), dim3(tm * tn, g.splits), dim3(DGT), 0, s, g, tm, tn);
   if (g.splits > 1) {
     const size_t tot = (size_t)g.M * g.N;
     hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
