@@ -23,7 +23,8 @@ int main() {
   const int jacs[] = {PR_JAC_DENSE, PR_JAC_DIAG, PR_JAC_BLOCK2, PR_JAC_ZERO, 4};
   const int sizes[][4] = {{2, 256, 2, 4},     {16, 1 << 20, 1, 1}, {8, 4096, 1024, 1024}, {4, 8192, 2048, 2048},
                           {16, 16384, 32, 64}, {1, 1, 1, 1},        {3, 77, 9, 130},       {0, 5, 1, 1},
-                          {2, -3, 1, 1},      {65536, 65536, 1, 1}, {1, 1 << 30, 1, 8},    {5, 1000, 7, 64}};
+                          {2, -3, 1, 1},      {65536, 65536, 1, 1}, {1, 1 << 30, 1, 8},    {5, 1000, 7, 64},
+                          {2, 100, 3, 20},    {2, 50, 20, 5},       {1, 1, 1, 63},         {65536, 65536, 3, 33}};
   for (int c : cells)
     for (int j : jacs)
       for (int dt = 0; dt < 3; dt++)
