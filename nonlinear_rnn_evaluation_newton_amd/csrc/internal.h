@@ -157,7 +157,9 @@ struct GemmArgs {
   int M, N, K, lda, ldb, ldc, splits;
   bool a_kc, b_kc, bf16, out_f32, vec_a, vec_b;
 };
-int gemm_splits(int M, int N, int K);
+// K splits of a long-K product; big: sized for the 256 x 256 bf16 kernel
+// (used when M and N reach a block tile)
+int gemm_splits(int M, int N, int K, bool big = false);
 // C[192,N] = A^T B and csum = column sums of A for K-outer fp32 A [K,192],
 // B [K,N] (N <= 64); C or csum may be null; ws of tn_workspace_bytes(K)
 size_t tn_workspace_bytes(int K);

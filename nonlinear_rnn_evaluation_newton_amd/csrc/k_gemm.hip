@@ -798,7 +798,28 @@ hipError_t launch_tn_products(const float *A, const float *B, int K, int N, floa
 // Split K until the grid covers the device about twice (long-K products
 // such as dW = dU^T x have few output tiles; every split writes a full fp32
 // partial of C), keeping at least 8 K tiles per split.
-int gemm_splits(int M, int N, int K) {
+int gemm_splits(int M, int N, int K, bool big) {
+  if (big && M >= BT && N >= BT) {
+    // The large-tile kernel runs one block per CU, so a grid of t tiles x s
+    // splits takes ceil(t s / 256) rounds of 1/s of the full-K block time;
+    // each split beyond one adds a fp32 partial of C written and summed.
+    // Rates (measured): a 256 x 256 block at ~3.7 TFLOP/s, partials moved at
+    // ~5 TB/s.  The split count with the smallest estimate, K chunks of at
+    // least 512.
+    const int tiles = ((M + BT - 1) / BT) * ((N + BT - 1) / BT);
+    const double full = 2.0 * BT * BT * (double)K / 3.7e12;
+    double best = 1e30;
+    int bs = 1;
+    for (int s = 1; s <= 32 && (s == 1 || K / s >= 8 * BK); s++) {
+      const double t = (double)((tiles * s + 255) / 256) * full / s +
+                       (s > 1 ? ((double)s * 8.0 + 4.0) * M * N / 5e12 : 0.0);
+      if (t < best * 0.999) {
+        best = t;
+        bs = s;
+      }
+    }
+    return bs;
+  }
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   int s = 1;
   while (tiles * s < 512 && K / (s * 2) >= 8 * GBK && s < 512) s *= 2;

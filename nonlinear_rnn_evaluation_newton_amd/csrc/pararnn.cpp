@@ -196,7 +196,8 @@ int make_plan(const pr_problem *p, Plan *pl) {
     pl->off_dU = o; o = align256(o + rows * 3 * p->n * es);
     pl->off_part = o; o = align256(o + nt * g.CH * 11 * 4);
     pl->off_red = o; o = align256(o + (size_t)CHAN_RED_SPLITS * p->n * 11 * 8);
-    const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL));
+    const int splits = gemm_splits(3 * p->n, p->d, (int)(rows < 2147483647ULL ? rows : 2147483647ULL),
+                                   p->dtype == PR_BF16);
     pl->off_gws = o; o = align256(o + (splits > 1 ? (size_t)splits * 3 * p->n * p->d * 4 : 0));
     pl->off_wt = o; o = align256(o + (size_t)3 * p->n * p->d * es);
     pl->adjoint_bytes = o;
@@ -1165,7 +1166,7 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
       gm.A = ws + pl.off_dU; gm.B = x; gm.C = dW->W_x; gm.bias = nullptr;
       gm.ws = (float *)(ws + pl.off_gws);
       gm.M = G3; gm.N = p->d; gm.K = rows; gm.lda = G3; gm.ldb = p->d; gm.ldc = p->d;
-      gm.splits = gemm_splits(G3, p->d, rows);
+      gm.splits = gemm_splits(G3, p->d, rows, bf);
       gm.a_kc = false; gm.b_kc = false; gm.bf16 = bf; gm.out_f32 = true;
       gm.vec_a = ((size_t)G3 * es) % 16 == 0;
       gm.vec_b = ((uintptr_t)x % 16 == 0) && ((size_t)p->d * es) % 16 == 0;
