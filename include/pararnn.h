@@ -147,14 +147,17 @@ size_t pararnn_workspace_bytes(const pr_problem *p, int with_adjoint);
 /*
  * Newton (or, per p->jac, quasi-Newton or Jacobi) solve of the recurrence
  * from the initial guess h = 0 everywhere.  Kernels exist for: TANH_RNN, GRU
- * and LINEAR with n <= 8 and d <= 8 (fp32, any jac); GRU with any other
- * n <= 64 (fp32; DENSE, DIAG or ZERO); GRU_DIAG and LSTM_CIFG_DIAG (fp32 or
- * bf16, any jac that suits them).  Other problems return PR_EUNSUPPORTED.
- * A GRU with n < 64 outside the first group runs on the n = 64 kernels with
- * its weights, biases and h0 padded with zeros into the front of the
- * workspace: the padded channels stay exactly 0 and couple to nothing, so
- * iterates, deltas, sweep counts and gradients are those of the n-wide
- * problem (pararnn_workspace_bytes includes the padded copies).
+ * and LINEAR with n <= 8 and d <= 8 (fp32, any jac); GRU and TANH_RNN with
+ * any other n <= 64 (fp32; DENSE, DIAG or ZERO); GRU_DIAG and LSTM_CIFG_DIAG
+ * (fp32 or bf16, any jac that suits them).  Other problems return
+ * PR_EUNSUPPORTED.  A GRU with n < 64 or a tanh RNN outside the first group
+ * runs on the n = 64 GRU kernels with its weights, biases and h0 padded with
+ * zeros into the front of the workspace (a tanh RNN's as the GRU's
+ * candidate gate, with the reset gate held at 1 and the update gate at 0 by
+ * input biases of +-1e30): the padded channels stay exactly 0 and couple to
+ * nothing, so iterates, deltas, sweep counts and gradients are those of the
+ * n-wide problem of the cell itself (pararnn_workspace_bytes includes the
+ * padded copies).
  *   x     [B, T, d]                input sequence
  *   h0    [B, S] or NULL (= 0)     state before the first step
  *   tol   stop when delta_k = max over (b, t, i) of |dh| is < tol; tol <= 0
@@ -183,8 +186,9 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
  * then h += dh.  lambda = 0 is quasi-DEER; larger lambda shortens the steps
  * (lambda ||dh||^2 <= ||r||^2).  p->jac is not used.  Kernels exist for
  * every problem pararnn_solve supports: the tanh RNN and GRU with n <= 8 and
- * d <= 8 and the dense GRU with any other n <= 64 (fp32), GRU_DIAG and
- * LSTM_CIFG_DIAG (fp32 or bf16); other problems return PR_EUNSUPPORTED.  Arguments and results as
+ * d <= 8 and the dense GRU and tanh RNN with any other n <= 64 (fp32),
+ * GRU_DIAG and LSTM_CIFG_DIAG (fp32 or bf16); other problems return
+ * PR_EUNSUPPORTED.  Arguments and results as
  * pararnn_solve, plus lambda (>= 0, finite); the workspace must hold
  * pararnn_elk_workspace_bytes (which also covers pararnn_adjoint).
  */

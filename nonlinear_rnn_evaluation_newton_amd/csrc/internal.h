@@ -171,10 +171,15 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 // Gate-blocked zero padding (fp32): src [G*n, cols] -> dst [G*np, cols_p],
 // row g*np + j = row g*n + j of src for j < n (first cols columns), zeros
-// elsewhere; unpad copies back (cols <= cols_p).  A state array [rows, n]
-// padded to [rows, np] is the case G = 1, n = np = rows, cols = n, cols_p = np.
-hipError_t launch_pad_gates(const float *src, int G, int n, int cols, float *dst, int np, int cols_p, hipStream_t s);
+// elsewhere; with only_gate >= 0, src is one gate [n, cols] placed in block
+// only_gate and the other blocks are zero.  unpad copies back (cols <=
+// cols_p).  A state array [rows, n] padded to [rows, np] is the case G = 1,
+// n = np = rows, cols = n, cols_p = np.
+hipError_t launch_pad_gates(const float *src, int G, int n, int cols, float *dst, int np, int cols_p, hipStream_t s,
+                            int only_gate = -1);
 hipError_t launch_unpad_gates(const float *src, int G, int n, int cols, float *dst, int np, int cols_p, hipStream_t s);
+// dst[j] = v0, dst[np + j] = v1 for j < n (the first two gate blocks of a bias)
+hipError_t launch_gate_consts(float *dst, int n, int np, float v0, float v1, hipStream_t s);
 // copy `bytes` (a multiple of 4) from device memory to host-coherent memory,
 // then store val to *seq with a system-scope release (one block)
 hipError_t launch_snapshot(const void *src, void *dst, size_t bytes, unsigned *seq, unsigned val, hipStream_t s);

@@ -234,11 +234,13 @@ hipError_t input_projection(const pr_problem *p, const pr_weights *w, const void
   return launch_gemm(g, s);
 }
 
-// Dense GRUs the n = 64 kernels run zero-padded (see padded_solve): fp32,
-// n < 64, outside the time-parallel kernels' range (n > 8 or d > 8).
+// Dense cells the n = 64 GRU kernels run zero-padded (see padded_solve):
+// GRUs with n < 64 and tanh RNNs (as GRUs, see pad_inputs) with n <= 64,
+// fp32, outside the time-parallel kernels' range (n > 8 or d > 8).
 static bool pad_gru(const pr_problem *p) {
-  return p && p->cell == PR_CELL_GRU && p->dtype == PR_F32 && p->B >= 1 && p->T >= 1 && p->d >= 1 && p->n >= 1 &&
-         p->n < D64_N && !(p->n <= 8 && p->d <= DX_FUSED) &&
+  return p && (p->cell == PR_CELL_GRU || p->cell == PR_CELL_TANH_RNN) && p->dtype == PR_F32 && p->B >= 1 &&
+         p->T >= 1 && p->d >= 1 && p->n >= 1 &&
+         (p->n < D64_N || (p->n == D64_N && p->cell == PR_CELL_TANH_RNN)) && !(p->n <= 8 && p->d <= DX_FUSED) &&
          (p->jac == PR_JAC_DENSE || p->jac == PR_JAC_DIAG || p->jac == PR_JAC_ZERO) &&
          (long long)p->B * p->T <= 2147483647LL;
 }
@@ -270,6 +272,7 @@ static PadLayout pad_layout(const pr_problem *p, bool adj) {
 }
 static pr_problem padded(const pr_problem *p) {
   pr_problem q = *p;
+  q.cell = PR_CELL_GRU;
   q.n = D64_N;
   return q;
 }
@@ -1211,22 +1214,34 @@ namespace {
 // the unpadded problem.  The padded weights, states and gradients live at the
 // front of the workspace; the results are copied back.
 // ---------------------------------------------------------------------------
+// A tanh RNN runs as the GRU whose reset gate is held at 1 and update gate
+// at 0: its weights fill the candidate gate (block 2), the other blocks are
+// zero, and the input biases of gates 0 and 1 are +-TANH_AS_GRU_BIAS, so the
+// sigmoids give exactly 1 and 0 (exp of the negated argument is 0 or +inf,
+// and the reciprocal of +inf is 0).  Then h' = tanh(W_x x + b_x + W_h h +
+// b_h), and every Jacobian term through r or z carries r (1 - r) = 0 or
+// z (1 - z) = 0, leaving diag(1 - c^2) W_h.
+constexpr float TANH_AS_GRU_BIAS = 1e30f;
 // The padded weights (and h0) into the workspace; w64 / h0p point at them.
 static int pad_inputs(const pr_problem *p, const pr_weights *w, const void *h0, char *ws, const PadLayout &L,
                       pr_weights *w64, const void **h0p, hipStream_t s) {
   if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
   const int n = p->n, d = p->d, N = D64_N;
+  const bool tanh = p->cell == PR_CELL_TANH_RNN;
+  const int gate = tanh ? 2 : -1;  // the source gate block (all three for a GRU)
   *w64 = pr_weights{};
-  HIPCHK(launch_pad_gates((const float *)w->W_x, 3, n, d, (float *)(ws + L.wx), N, d, s));
-  HIPCHK(launch_pad_gates((const float *)w->W_h, 3, n, n, (float *)(ws + L.wh), N, N, s));
+  HIPCHK(launch_pad_gates((const float *)w->W_x, 3, n, d, (float *)(ws + L.wx), N, d, s, gate));
+  HIPCHK(launch_pad_gates((const float *)w->W_h, 3, n, n, (float *)(ws + L.wh), N, N, s, gate));
   w64->W_x = ws + L.wx;
   w64->W_h = ws + L.wh;
-  if (w->b_x) {
-    HIPCHK(launch_pad_gates((const float *)w->b_x, 3, n, 1, (float *)(ws + L.bx), N, 1, s));
+  if (w->b_x || tanh) {
+    if (w->b_x) HIPCHK(launch_pad_gates((const float *)w->b_x, 3, n, 1, (float *)(ws + L.bx), N, 1, s, gate));
+    else HIPCHK(launch_pad_gates(nullptr, 3, 0, 1, (float *)(ws + L.bx), N, 1, s));  // zeros
+    if (tanh) HIPCHK(launch_gate_consts((float *)(ws + L.bx), n, N, TANH_AS_GRU_BIAS, -TANH_AS_GRU_BIAS, s));
     w64->b_x = ws + L.bx;
   }
   if (w->b_h) {
-    HIPCHK(launch_pad_gates((const float *)w->b_h, 3, n, 1, (float *)(ws + L.bh), N, 1, s));
+    HIPCHK(launch_pad_gates((const float *)w->b_h, 3, n, 1, (float *)(ws + L.bh), N, 1, s, gate));
     w64->b_h = ws + L.bh;
   }
   *h0p = nullptr;
@@ -1334,10 +1349,14 @@ static int padded_adjoint(const pr_problem *p, const pr_weights *w, const void *
   }
   if (lambda) HIPCHK(unpad_state(ws + L.lam, rows, n, lambda, s));
   if (dh0) HIPCHK(unpad_state(ws + L.dh0, p->B, n, dh0, s));
-  if (dW && dW->W_x) HIPCHK(launch_unpad_gates((const float *)(ws + L.dwx), 3, n, d, dW->W_x, N, d, s));
-  if (dW && dW->b_x) HIPCHK(launch_unpad_gates((const float *)(ws + L.dbx), 3, n, 1, dW->b_x, N, 1, s));
-  if (dW && dW->W_h) HIPCHK(launch_unpad_gates((const float *)(ws + L.dwh), 3, n, n, dW->W_h, N, N, s));
-  if (dW && dW->b_h) HIPCHK(launch_unpad_gates((const float *)(ws + L.dbh), 3, n, 1, dW->b_h, N, 1, s));
+  // a tanh RNN's gradients are the candidate gate's block
+  const int G = p->cell == PR_CELL_TANH_RNN ? 1 : 3, g0 = 3 - G;
+  const float *dwx = (const float *)(ws + L.dwx) + (size_t)g0 * N * d, *dbx = (const float *)(ws + L.dbx) + g0 * N;
+  const float *dwh = (const float *)(ws + L.dwh) + (size_t)g0 * N * N, *dbh = (const float *)(ws + L.dbh) + g0 * N;
+  if (dW && dW->W_x) HIPCHK(launch_unpad_gates(dwx, G, n, d, dW->W_x, N, d, s));
+  if (dW && dW->b_x) HIPCHK(launch_unpad_gates(dbx, G, n, 1, dW->b_x, N, 1, s));
+  if (dW && dW->W_h) HIPCHK(launch_unpad_gates(dwh, G, n, n, dW->W_h, N, N, s));
+  if (dW && dW->b_h) HIPCHK(launch_unpad_gates(dbh, G, n, 1, dW->b_h, N, 1, s));
   return rc;
 }
 

@@ -61,13 +61,13 @@ def test_workspace_bytes_for_approximate_jacobians():
     (dict(cell=9), bd.PR_EINVAL), (dict(jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL), (dict(dtype=7), bd.PR_EINVAL),
     (dict(B=0), bd.PR_EINVAL), (dict(T=0), bd.PR_EINVAL), (dict(d=0), bd.PR_EINVAL), (dict(n=-3), bd.PR_EINVAL),
     (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
-    (dict(cell=sy.CELL_TANH_RNN, n=13), bd.PR_EUNSUPPORTED),
+    (dict(cell=sy.CELL_LINEAR, n=13), bd.PR_EUNSUPPORTED), (dict(cell=sy.CELL_TANH_RNN, n=65), bd.PR_EUNSUPPORTED),
     (dict(jac=4), bd.PR_EINVAL), (dict(jac=-1), bd.PR_EINVAL),
     (dict(cell=sy.CELL_GRU_DIAG, jac=bd.PR_JAC_BLOCK2), bd.PR_EINVAL),
     (dict(cell=sy.CELL_LSTM_CIFG_DIAG, jac=bd.PR_JAC_DENSE), bd.PR_EINVAL),
     (dict(cell=sy.CELL_GRU, jac=bd.PR_JAC_DIAG, n=65), bd.PR_EUNSUPPORTED),
     (dict(cell=sy.CELL_GRU, dtype=bd.PR_BF16, n=13), bd.PR_EUNSUPPORTED),
-    (dict(cell=sy.CELL_TANH_RNN, jac=bd.PR_JAC_ZERO, n=64), bd.PR_EUNSUPPORTED),
+    (dict(cell=sy.CELL_LINEAR, jac=bd.PR_JAC_ZERO, n=64), bd.PR_EUNSUPPORTED),
 ])
 def test_invalid_problems_rejected_without_device(kw, code):
     L = bd.lib()
@@ -80,13 +80,15 @@ def test_invalid_problems_rejected_without_device(kw, code):
     assert bd.last_error() != ""
 
 
+@pytest.mark.parametrize("cell", [sy.CELL_GRU, sy.CELL_TANH_RNN])
 @pytest.mark.parametrize("jac", [sy.JAC_DENSE, sy.JAC_DIAG, sy.JAC_ZERO])
 @pytest.mark.parametrize("n,d", [(13, 1), (63, 40), (5, 20), (1, 9)])
-def test_dense_gru_padded_to_64_workspace(n, d, jac):
-    """Dense GRUs with n < 64 outside the time-parallel kernels' range (n > 8
-    or d > 8) run on the n = 64 kernels zero-padded: their workspace is the
-    n = 64 problem's plus the padded copies of weights, states and gradients."""
-    pb = _prob(n=n, d=d, jac=jac, B=3, T=100)
+def test_dense_gru_padded_to_64_workspace(n, d, jac, cell):
+    """Dense GRUs (n < 64) and tanh RNNs (n <= 64) outside the time-parallel
+    kernels' range (n > 8 or d > 8) run on the n = 64 GRU kernels zero-padded:
+    their workspace is the n = 64 GRU's plus the padded copies of weights,
+    states and gradients."""
+    pb = _prob(cell=cell, n=n, d=d, jac=jac, B=3, T=100)
     q = _prob(n=64, d=d, jac=jac, B=3, T=100)
     for adj in (False, True):
         assert bd.workspace_bytes(pb, adj) > bd.workspace_bytes(q, adj) > 0
@@ -173,7 +175,7 @@ def test_elk_arguments_rejected_without_device():
     assert bd.elk_workspace_bytes(good) >= bd.workspace_bytes(good, True) > 0
     small = bd.Problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 4)
     assert bd.elk_workspace_bytes(small) >= bd.workspace_bytes(small, True) > 0  # the small dense cells
-    wide = bd.Problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)  # no kernels for n = 16 at all
+    wide = bd.Problem(sy.CELL_LINEAR, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)  # no kernels for n = 16 at all
     assert bd.workspace_bytes(wide, False) == 0 and bd.elk_workspace_bytes(wide) == 0
     w = bd.Weights(1, None, 1, None, None)
     v = C.c_void_p(16)

@@ -1,7 +1,9 @@
-"""GPU parity of dense GRUs narrower than 64 that run on the n = 64 kernels
-zero-padded (n in 9..63, or n <= 8 with d > 8): DEER, quasi-DEER, Jacobi,
-quasi-ELK and the adjoint against the fp64 oracle of the unpadded problem,
-and the combined solve + adjoint against the separate calls."""
+"""GPU parity of dense GRUs narrower than 64 and of dense tanh RNNs up to 64
+wide that run on the n = 64 GRU kernels zero-padded (n in 9..64, or n <= 8
+with d > 8; a tanh RNN as the GRU with its reset gate held at 1 and update
+gate at 0): DEER, quasi-DEER, Jacobi, quasi-ELK and the adjoint against the
+fp64 oracle of the unpadded problem of the cell itself, and the combined
+solve + adjoint against the separate calls."""
 import numpy as np
 import pytest
 
@@ -33,8 +35,8 @@ def to64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def problem(n, d, B, T, seed, jac=sy.JAC_DENSE, w_scale=0.8):
-    p = sy.custom_problem(sy.CELL_GRU, B=B, T=T, d=d, n=n, seed=seed, w_scale=w_scale, h0=True)
+def problem(n, d, B, T, seed, jac=sy.JAC_DENSE, w_scale=0.8, cell=sy.CELL_GRU):
+    p = sy.custom_problem(cell, B=B, T=T, d=d, n=n, seed=seed, w_scale=w_scale, h0=True)
     return dict(p, jac=jac)
 
 
@@ -46,7 +48,7 @@ def agree(it, ito, dlo, tol):
 
 
 def check_solve(p, tol, max_iters, lam=None):
-    say("case padded GRU n", p["n"], "d", p["d"], "B", p["B"], "T", p["T"], "jac", p["jac"], "tol", tol,
+    say("case padded", p["name"], "n", p["n"], "d", p["d"], "B", p["B"], "T", p["T"], "jac", p["jac"], "tol", tol,
         "max_iters", max_iters, "elk lambda", lam)
     dp = bd.DeviceProblem(p, elk=lam is not None)
     if lam is None:
@@ -159,6 +161,41 @@ def test_solve_adjoint_matches_separate_calls():
     for k in o1:
         assert torch.equal(o1[k], o2[k]), k
     adjoint_check(p, dp, dict(o2, dW_x=o2["W_x"], db_x=o2["b_x"], dW_h=o2["W_h"], db_h=o2["b_h"]))
+
+
+@pytest.mark.parametrize("n,d,B,T", [(12, 3, 2, 300), (33, 40, 3, 129), (64, 7, 2, 65), (5, 20, 2, 200),
+                                     (1, 9, 3, 64), (9, 1, 1, 1)])
+def test_tanh_rnn_deer(n, d, B, T):
+    p = problem(n, d, B, T, seed=n * 5 + d, cell=sy.CELL_TANH_RNN)
+    check_solve(p, 1e-6, T)
+    check_solve(p, 0.0, 2)
+
+
+@pytest.mark.parametrize("jac", [sy.JAC_DIAG, sy.JAC_ZERO])
+@pytest.mark.parametrize("n,d", [(20, 4), (64, 16)])
+def test_tanh_rnn_quasi_and_jacobi(jac, n, d):
+    p = problem(n, d, 2, 200, seed=n + d, jac=jac, cell=sy.CELL_TANH_RNN)
+    check_solve(p, 1e-5, 200)
+    check_solve(p, 0.0, 3)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+def test_tanh_rnn_quasi_elk(lam):
+    p = problem(30, 6, 2, 150, seed=8, jac=sy.JAC_DIAG, cell=sy.CELL_TANH_RNN)
+    check_solve(p, 0.0, 2, lam)
+    check_solve(p, 1e-5, 150, lam)
+
+
+@pytest.mark.parametrize("n,d,B,T", [(12, 3, 2, 300), (64, 20, 2, 129), (5, 20, 1, 100)])
+def test_tanh_rnn_adjoint(n, d, B, T):
+    p = problem(n, d, B, T, seed=3 * n + d, cell=sy.CELL_TANH_RNN)
+    say("adjoint padded tanh RNN n", n, "d", d, "B", B, "T", T)
+    dp = bd.DeviceProblem(p)
+    dp.solve()
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    adjoint_check(p, dp, a)
 
 
 def test_zero_padded_equals_explicit_64():
