@@ -94,13 +94,18 @@ ChanGeomInfo chan_geom(int cell, int n);  // tiles of the standalone scan
 // one wavefront each; per sweep a carry scan then a pass that applies the
 // sweep and composes the next sweep's tile aggregates
 constexpr int CHAN2_TT = 64;
-enum { CHAN2_FIRST = 0, CHAN2_CARRY = 1, CHAN2_APPLY_NEXT = 2, CHAN2_APPLY = 3 };
+// CHAN2_APPLY_ADJ: the last pass of a fixed sweep count followed by an
+// adjoint (a.g set): it composes the adjoint's tile aggregates at the final
+// iterate; the adjoint then runs with fused = true
+enum { CHAN2_FIRST = 0, CHAN2_CARRY = 1, CHAN2_APPLY_NEXT = 2, CHAN2_APPLY = 3, CHAN2_APPLY_ADJ = 4 };
 ChanGeomInfo chan2_geom(int cell, int n);
 // apx: APX_NEWTON, APX_DIAG (LSTM) or APX_ZERO
 hipError_t launch_chan2(int cell, int apx, bool bf16, const ChanArgs &a, int what, hipStream_t s);
 // adjoint as streaming passes on the same tiles (aggregates, reverse carry
 // scan, apply); per-tile weight partials [tiles][CH][11]
-hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s);
+// fused: the tile aggregates were composed by a CHAN2_APPLY_ADJ pass (all but
+// each tile's first step) and only the carry and the applying pass run
+hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s, bool fused = false);
 // weight gradients from per-tile partials: CHAN_RED_SPLITS fp64 partial sums
 // per (channel, slot) in `red`, then their sum in order
 constexpr int CHAN_RED_SPLITS = 32;

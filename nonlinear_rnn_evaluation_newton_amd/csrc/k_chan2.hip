@@ -19,6 +19,10 @@
 //                  partial aggregate of sweep k + 1 at the new iterate.
 //
 // Before sweep 1 a pass composes the aggregates at the initial guess only.
+// When the sweep count is fixed and an adjoint follows, the last pass
+// composes the adjoint's tile aggregates instead (ADJ): the elements
+// (J_t^T, J_t^T g_t) at the final iterate, with the cell's own Jacobian,
+// which the adjoint would otherwise evaluate in a pass of its own.
 // The iterate is read once and written once per sweep, like a single-pass
 // scan, at the price of a second cell evaluation per step; no wavefront ever
 // waits for another, so there is no look-back latency and no co-residency
@@ -101,8 +105,9 @@ __device__ inline void state_before(const ChanArgs &a, int k, int t0, int b, int
   }
 }
 
-template <int CELL, typename ST, int CPL, bool APPLY, bool NEXT>
+template <int CELL, typename ST, int CPL, bool APPLY, bool NEXT, bool ADJ = false>
 __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
+  static_assert(!ADJ || (APPLY && !NEXT), "the adjoint's aggregates come with the last applying pass");
   constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1, CH = 64 * CPL, AW = SW * SW + SW, ES = (int)sizeof(ST);
   constexpr int UW = words_of<ST, CPL>(), HW = words_of<ST, CPL * SW>(), TT = CHAN2_TT;
   __shared__ int s_stop;
@@ -128,6 +133,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
     const Rsrc ru = sc_rsrc((const ST *)a.U + row0 * 3 * n, (unsigned)(nrows * 3 * n * ES));
     const Rsrc rh = sc_rsrc((APPLY && k >= 2) ? (const ST *)a.h + row0 * S : nullptr, (unsigned)(nrows * S * ES));
     const Rsrc rw = sc_rsrc((ST *)a.h + row0 * S, (unsigned)(nrows * S * ES));
+    const Rsrc rg = sc_rsrc(ADJ ? (const ST *)a.g + row0 * S : nullptr, (unsigned)(nrows * S * ES));
 
     float s_old[CPL * SW], s_new[CPL * SW], dh[CPL * SW];
     Op<SW> agg[CPL];
@@ -154,19 +160,22 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
     const unsigned lane_oob = active ? 0u : SC_OOB;
     const unsigned ulane = (unsigned)(c0 * ES) | lane_oob, hlane = (unsigned)(c0 * SW * ES) | lane_oob;
     unsigned ua[C2_P][3][UW], ha[C2_P][HW], ub[C2_P][3][UW], hb[C2_P][HW];
-    auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW]) __attribute__((always_inline)) {
+    unsigned ga[ADJ ? C2_P : 1][HW], gb[ADJ ? C2_P : 1][HW];  // ADJ: the upstream gradient g
+    auto load = [&](int g, unsigned (&u)[C2_P][3][UW], unsigned (&h)[C2_P][HW],
+                    unsigned (&gr)[ADJ ? C2_P : 1][HW]) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
         const int s = g * C2_P + q;
 #pragma unroll
         for (int gi = 0; gi < 3; gi++) bldw<CPL * ES>(ru, ulane + (unsigned)((s * 3 * n + gi * n) * ES), u[q][gi]);
         bldw<CPL * SW * ES>(rh, hlane + (unsigned)(s * S * ES), h[q]);
+        if constexpr (ADJ) bldw<CPL * SW * ES>(rg, hlane + (unsigned)(s * S * ES), gr[q]);
       }
     };
     // FULL: every lane active and every step inside [0, T) (all tiles but a
     // sequence's last one when n fills the stripe): no identity selects
-    auto steps = [&](auto full, int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW])
-                     __attribute__((always_inline)) {
+    auto steps = [&](auto full, int g, const unsigned (&u)[C2_P][3][UW], const unsigned (&h)[C2_P][HW],
+                     const unsigned (&gr)[ADJ ? C2_P : 1][HW]) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full)::value;
 #pragma unroll
       for (int q = 0; q < C2_P; q++) {
@@ -216,6 +225,28 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
               agg[c] = compose(e, agg[c]);
             }
           }
+          if constexpr (ADJ) {
+            // the adjoint's element of this step at the new iterate, with the
+            // cell's own Jacobian: mu_{t-1} = J_t^T mu_t + J_t^T g_t, composed
+            // so that later steps act first (the tile's first step is the
+            // adjoint carry kernel's)
+            if (s > 0) {
+              float f[SW], J[SW * SW];
+              chan_cell<cell_code(CELL)>(&s_new[c * SW], uc, w[c], f, J);
+              Op<SW> e;
+#pragma unroll
+              for (int r = 0; r < SW; r++) {
+                float v = 0.f;
+#pragma unroll
+                for (int q2 = 0; q2 < SW; q2++) {
+                  e.A[r * SW + q2] = valid ? J[q2 * SW + r] : (r == q2 ? 1.f : 0.f);
+                  v = fmaf(J[q2 * SW + r], unpackw<ST>(gr[q], c * SW + q2), v);
+                }
+                e.b[r] = valid ? v : 0.f;
+              }
+              agg[c] = compose(agg[c], e);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < SW; i++) s_new[c * SW + i] = hn[c * SW + i];
         }
@@ -223,12 +254,12 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
       }
     };
     auto walk = [&](auto full) __attribute__((always_inline)) {
-      load(0, ua, ha);
+      load(0, ua, ha, ga);
       for (int g = 0; g < C2_NG; g += 2) {
-        load(g + 1, ub, hb);
-        steps(full, g, ua, ha);
-        load(g + 2, ua, ha);
-        steps(full, g + 1, ub, hb);
+        load(g + 1, ub, hb, gb);
+        steps(full, g, ua, ha, ga);
+        load(g + 2, ua, ha, ga);
+        steps(full, g + 1, ub, hb, gb);
       }
     };
     const int last_c = (stripe % CG) * CH + 63 * CPL;  // first channel of lane 63
@@ -242,7 +273,7 @@ __global__ __launch_bounds__(256) void k_chan_pass(const ChanArgs a) {
           for (int i = 0; i < CPL * SW; i++) bp[i] = s_new[i];
         }
       }
-      if constexpr (NEXT) {
+      if constexpr (NEXT || ADJ) {
         float *pa = (float *)a.agg + ((size_t)L * CH + lane * CPL) * AW;
 #pragma unroll
         for (int c = 0; c < CPL; c++) {
@@ -597,17 +628,91 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
 
 // Reverse exclusive scan of the tile aggregates of one stripe (block): mu
 // entering each tile from the tile above, C2_CW wavefronts over contiguous
-// ranges of tiles (loads of C2_R tiles issued together).
-template <int SW, int CPL>
+// ranges of tiles (loads of C2_R tiles issued together).  FUSED: the last
+// sweep's pass composed each tile's steps but its first (see k_chan_pass);
+// that step's element, at the final state before the tile, is composed here
+// first and the full aggregate written back.
+template <int CELL, typename ST, int CPL, bool FUSED>
 __global__ __launch_bounds__(64 * C2_CW) void k_chan_adj_carry(const ChanArgs a) {
-  constexpr int CH = 64 * CPL, AW = SW * SW + SW, R = C2_R;
+  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1;
+  constexpr int CH = 64 * CPL, AW = SW * SW + SW, R = C2_R, TT = CHAN2_TT;
   __shared__ float s_tot[C2_CW][CH][AW];
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stripe = blockIdx.x, nt = a.tps, per = (nt + C2_CW - 1) / C2_CW;
   // wavefront wid takes the wid-th range from the top
   const int j1 = max(0, nt - wid * per), j0 = max(0, j1 - per);
-  const float *pagg = (const float *)a.agg;
   float *carry = (float *)a.incl;
+  if constexpr (FUSED) {
+    const int T = a.T, n = a.n, S = SW * n;
+    const int CG = (n + CH - 1) / CH, b = stripe / CG;
+    const int c0 = (stripe % CG) * CH + lane * CPL;
+    const bool active = c0 < n;
+    const int cc = active ? c0 : 0;
+    ChanW w[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) w[c] = load_chan_w<ST, CELL>(a, cc + c);
+    const ST *U = (const ST *)a.U, *H = (const ST *)a.h, *G = (const ST *)a.g;
+    float *pagg = (float *)a.agg;
+    for (int jc = j0; jc < j1; jc += R) {
+      // every load of the chunk is issued unconditionally (idle slots read a
+      // valid tile's data and are discarded), then used
+      float u[R][CPL][3], sb[R][CPL * SW], gv[R][CPL * SW], pg[R][CPL][AW];
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        const int jj = jc + r < j1 ? jc + r : j0, L = stripe * nt + jj, t0 = jj * TT;
+        const size_t row = (size_t)b * T + t0;
+        // the final state before step t0: h[t0 - 1], h0 or 0
+        const ST *hp = t0 > 0 ? H + (row - 1) * S + (size_t)cc * SW
+                              : (a.h0 ? (const ST *)a.h0 + (size_t)b * S + (size_t)cc * SW : H);
+#pragma unroll
+        for (int c = 0; c < CPL; c++)
+#pragma unroll
+          for (int gi = 0; gi < 3; gi++) u[r][c][gi] = ldf(U, row * 3 * n + (size_t)gi * n + cc + c);
+#pragma unroll
+        for (int i = 0; i < CPL * SW; i++) {
+          const float v = ldf(hp, i);
+          sb[r][i] = (t0 > 0 || a.h0) ? v : 0.f;
+          gv[r][i] = ldf(G, row * S + (size_t)cc * SW + i);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; c++)
+#pragma unroll
+          for (int i = 0; i < AW; i++) pg[r][c][i] = pagg[((size_t)L * CH + lane * CPL + c) * AW + i];
+      }
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        const int j = jc + r, L = stripe * nt + j;
+        if (!(active && j < j1)) continue;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+          float f[SW], J[SW * SW];
+          chan_cell<cell_code(CELL)>(&sb[r][c * SW], u[r][c], w[c], f, J);
+          Op<SW> e, p;
+#pragma unroll
+          for (int q = 0; q < SW; q++) {
+            float v = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < SW; q2++) {
+              e.A[q * SW + q2] = J[q2 * SW + q];
+              v = fmaf(J[q2 * SW + q], gv[r][c * SW + q2], v);
+            }
+            e.b[q] = v;
+          }
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) p.A[i] = pg[r][c][i];
+#pragma unroll
+          for (int i = 0; i < SW; i++) p.b[i] = pg[r][c][SW * SW + i];
+          const Op<SW> full = compose(e, p);  // the first step acts last
+          float *pa = pagg + ((size_t)L * CH + lane * CPL + c) * AW;
+#pragma unroll
+          for (int i = 0; i < SW * SW; i++) pa[i] = full.A[i];
+#pragma unroll
+          for (int i = 0; i < SW; i++) pa[SW * SW + i] = full.b[i];
+        }
+      }
+    }
+  }
+  const float *pagg = (const float *)a.agg;
   auto ld_op = [&](int j, int c) {
     Op<SW> o;
     const float *q = pagg + (((size_t)stripe * nt + j) * CH + lane * CPL + c) * AW;
@@ -683,24 +788,29 @@ __global__ __launch_bounds__(64 * C2_CW) void k_chan_adj_carry(const ChanArgs a)
 }
 
 template <int CELL, typename ST, int CPL>
-static hipError_t chan2_adj_launch(const ChanArgs &a, hipStream_t s) {
-  constexpr int SW = cell_code(CELL) == C_LSTM ? 2 : 1;
+static hipError_t chan2_adj_launch(const ChanArgs &a, bool fused, hipStream_t s) {
   const unsigned grid = (unsigned)((a.ntiles + 3) / 4);
-  hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, false>), dim3(grid), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_chan_adj_carry<SW, CPL>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
+  if (fused) {
+    hipLaunchKernelGGL((k_chan_adj_carry<CELL, ST, CPL, true>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_chan_adj_carry<CELL, ST, CPL, false>), dim3(a.stripes), dim3(64 * C2_CW), 0, s, a);
+  }
   hipLaunchKernelGGL((k_chan_adj_pass<CELL, ST, CPL, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s) {
+hipError_t launch_chan2_adjoint(int cell, bool bf16, const ChanArgs &a, hipStream_t s, bool fused) {
   const ChanGeomInfo g = chan2_geom(cell, a.n);
   if (cell == C_GRU_DIAG) {
     if (g.CPL == 2)
-      return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 2>(a, s) : chan2_adj_launch<C_GRU_DIAG, float, 2>(a, s);
-    return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 1>(a, s) : chan2_adj_launch<C_GRU_DIAG, float, 1>(a, s);
+      return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 2>(a, fused, s)
+                  : chan2_adj_launch<C_GRU_DIAG, float, 2>(a, fused, s);
+    return bf16 ? chan2_adj_launch<C_GRU_DIAG, uint16_t, 1>(a, fused, s)
+                : chan2_adj_launch<C_GRU_DIAG, float, 1>(a, fused, s);
   }
   if (cell == C_LSTM)
-    return bf16 ? chan2_adj_launch<C_LSTM, uint16_t, 1>(a, s) : chan2_adj_launch<C_LSTM, float, 1>(a, s);
+    return bf16 ? chan2_adj_launch<C_LSTM, uint16_t, 1>(a, fused, s) : chan2_adj_launch<C_LSTM, float, 1>(a, fused, s);
   return hipErrorInvalidValue;
 }
 
@@ -728,6 +838,9 @@ static hipError_t chan2_launch(const ChanArgs &a, int what, hipStream_t s) {
       break;
     case CHAN2_APPLY:
       hipLaunchKernelGGL((k_chan_pass<CELL, ST, CPL, true, false>), dim3(pass_grid), dim3(256), 0, s, a);
+      break;
+    case CHAN2_APPLY_ADJ:
+      hipLaunchKernelGGL((k_chan_pass<CELL, ST, CPL, true, false, true>), dim3(pass_grid), dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

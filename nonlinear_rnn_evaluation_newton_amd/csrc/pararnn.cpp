@@ -582,6 +582,7 @@ struct SpecAdjoint {
   const pr_grads *dW;
   bool done = false;  // out: the adjoint ran at the returned trajectory
   bool ran = false;   // out: an adjoint was enqueued (done or not)
+  bool chan_aggs = false;  // out: the last channel pass composed the adjoint's tile aggregates
   int rc = PR_OK;     // out: its status when done
 };
 // Whether the last combined call on a problem converged within its first
@@ -604,7 +605,7 @@ static SpecMemo &spec_memo() {
 
 static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                         const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
-                        size_t ws_bytes, void *stream, bool u_ready, bool fresh);
+                        size_t ws_bytes, void *stream, bool u_ready, bool fresh, bool chan_aggs = false);
 // Sweep number of the descriptors of an adjoint that follows its solve
 // without clearing: above any sweep count (the scalar-state path has T < 2^29).
 constexpr int ADJ_TAG_SWEEP = 1 << 30;
@@ -792,6 +793,14 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
                          (first >= kmax || (scalar && al16(spec->g) && al16(spec->lambda) && al16(spec->dx) &&
                                             spec_memo().same(p, tol, max_iters) && spec_memo().first_batch));
   bool spec_enqueued = false;
+  // channel cells with a fixed sweep count: the last pass composes the
+  // adjoint's tile aggregates (it evaluates the cell at the final iterate
+  // anyway), so the adjoint skips its own aggregate pass
+  const bool fuse_adj = speculate && pl.path == PATH_CHAN && tol <= 0.f && spec->g != nullptr;
+  if (fuse_adj) {
+    ca.g = spec->g;
+    spec->chan_aggs = true;
+  }
   int k = 1, out_iters = 0, out_status = PR_OK;
   // Sweep timing: the dense n = 64 path brackets every sweep (its parts are
   // timed too); the others bracket each batch of back-to-back sweeps, so the
@@ -847,8 +856,10 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
         const bool bf = p->dtype == PR_BF16;
         if (kk == 1) HIPCHK(launch_chan2(kc, pl.approx, bf, ca, CHAN2_FIRST, s));
         HIPCHK(launch_chan2(kc, pl.approx, bf, ca, CHAN2_CARRY, s));
-        // the last possible sweep composes no aggregates for a next one
-        HIPCHK(launch_chan2(kc, pl.approx, bf, ca, kk == kmax ? CHAN2_APPLY : CHAN2_APPLY_NEXT, s));
+        // the last possible sweep composes no aggregates for a next one (but
+        // the adjoint's, when it follows a fixed sweep count)
+        const int what = kk < kmax ? CHAN2_APPLY_NEXT : fuse_adj ? CHAN2_APPLY_ADJ : CHAN2_APPLY;
+        HIPCHK(launch_chan2(kc, pl.approx, bf, ca, what, s));
       }
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1) + 1], s));
     }
@@ -859,7 +870,7 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     // behind it keeps the device busy while the host decides
     if (speculate && k == 1) {
       spec->rc = adjoint_impl(p, w, x, h0, h, spec->g, spec->lambda, spec->dx, spec->dh0, spec->dW, workspace,
-                              ws_bytes, stream, true, true);
+                              ws_bytes, stream, true, true, spec->chan_aggs);
       spec_enqueued = spec->rc >= 0;
       spec->ran = spec_enqueued;
     }
@@ -986,7 +997,7 @@ int pararnn_adjoint(const pr_problem *p, const pr_weights *w, const void *x, con
 // a sweep number no solve reaches, so the sweeps' descriptors never match.
 static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x, const void *h0, const void *h,
                         const void *g, void *lambda, void *dx, void *dh0, const pr_grads *dW, void *workspace,
-                        size_t ws_bytes, void *stream, bool u_ready, bool fresh) {
+                        size_t ws_bytes, void *stream, bool u_ready, bool fresh, bool chan_aggs) {
   g_err.clear();
   Plan pl;
   int rc = make_plan(p, &pl);
@@ -1145,7 +1156,7 @@ static int adjoint_impl(const pr_problem *p, const pr_weights *w, const void *x,
     const int ta = tr.begin(TR_ADJ, s);
     ca.tps = pl.tps_2;
     ca.ntiles = pl.ntiles_2;
-    HIPCHK(launch_chan2_adjoint(kc, bf, ca, s));
+    HIPCHK(launch_chan2_adjoint(kc, bf, ca, s, chan_aggs));
     tr.end(TR_ADJ, ta, s);
     const int tg = tr.begin(TR_AGEMM, s);
     if (dW && (dW->W_h || dW->b_h || dW->peep || dW->b_x))

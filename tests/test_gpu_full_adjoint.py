@@ -169,6 +169,42 @@ def test_fp32_full_length_adjoint(cell, T):
         assert r <= RTOL_W, rk
 
 
+@pytest.mark.parametrize("cell,jac", [(sy.CELL_GRU_DIAG, sy.JAC_DIAG), (sy.CELL_LSTM_CIFG_DIAG, sy.JAC_BLOCK2),
+                                      (sy.CELL_LSTM_CIFG_DIAG, sy.JAC_DIAG), (sy.CELL_GRU_DIAG, sy.JAC_ZERO)])
+def test_fp32_full_length_fixed_sweeps_adjoint(cell, jac):
+    """A fixed sweep count, as the per-channel workloads run: the last sweep's
+    pass composes the adjoint's tile aggregates with the cell's own Jacobian
+    (whatever Jacobian the sweeps used) and the adjoint carry adds each tile's
+    first step.  Full length with a ragged last tile, h0 and biases, every
+    tensor element by element."""
+    T = 8192 + 37
+    p = dict(sy.custom_problem(cell, B=2, T=T, d=12, n=66, seed=T + 7 * cell + jac, w_scale=0.8, h0=True), jac=jac)
+    p["tol"], p["max_iters"] = 0.0, 3
+    say("fp32 full-length fixed-sweep adjoint case", p["name"], "jac", jac, "T", T)
+    dp = bd.DeviceProblem(p)
+    st, it, dl, o = solve_adjoint(dp)
+    say("  gpu sweeps", it, "status", st)
+    assert st == bd.PR_OK and it == 3
+    h = to64(dp.h)
+    approx = {sy.JAC_DIAG: oracle.QUASI, sy.JAC_ZERO: oracle.JACOBI}.get(jac, oracle.NEWTON)
+    if cell == sy.CELL_GRU_DIAG and jac == sy.JAC_DIAG:
+        approx = oracle.NEWTON  # the diagonal cell's own Jacobian is diagonal
+    ho, *_ = oracle.deer(p, tol=0.0, max_iters=3, approx=approx)
+    assert np.abs(h - ho).max() <= ATOL
+    ref = oracle.adjoint(p, h)
+    for key in ("lam", "dx", "dh0"):
+        err = np.abs(to64(o[key]) - ref[key]).max()
+        say("  ", key, "abs", err)
+        assert err <= ATOL * max(1.0, np.abs(ref[key]).max()), key
+    keys = [("W_x", "dW_x"), ("b_x", "db_x"), ("W_h", "dW_h"), ("b_h", "db_h")]
+    if cell == sy.CELL_LSTM_CIFG_DIAG:
+        keys.append(("peep", "dpeep"))
+    for k, rk in keys:
+        r = rel(to64(o[k]), ref[rk])
+        say("  ", rk, "rel", r)
+        assert r <= RTOL_W, rk
+
+
 def test_dense64_full_size_adjoint():
     """The dense n = 64 GRU workload (B = 16, T = 16384: 256 chunks of 64
     steps per sequence), every sequence, every tensor."""

@@ -97,17 +97,37 @@ def same(r1, r2):
         assert torch.equal(r1[4][k], r2[4][k]), k
 
 
-@pytest.mark.parametrize("cell,n,dtype", [(sy.CELL_LSTM_CIFG_DIAG, 40, sy.DT_BF16), (sy.CELL_GRU, 64, sy.DT_F32),
+def close(r1, r2, bf16):
+    """The solve bit for bit; the adjoint within rounding (the per-channel
+    cells' combined call composes the adjoint's tile aggregates in the last
+    sweep's pass, in the other order along time)."""
+    assert r1[0] == r2[0] and r1[1] == r2[1] and np.array_equal(r1[2], r2[2])
+    assert torch.equal(r1[3], r2[3])
+    for k in r1[4]:
+        a, b = r1[4][k].float(), r2[4][k].float()
+        scale = max(float(a.abs().max()), 1e-30)
+        err = float((a - b).abs().max()) / scale
+        print("  ", k, "rel diff", err, flush=True)
+        assert err <= (1e-2 if bf16 and k in ("lam", "dx", "dh0") else 1e-5), k
+
+
+@pytest.mark.parametrize("cell,n,dtype", [(sy.CELL_LSTM_CIFG_DIAG, 40, sy.DT_BF16), (sy.CELL_LSTM_CIFG_DIAG, 40, sy.DT_F32),
+                                          (sy.CELL_GRU_DIAG, 70, sy.DT_BF16), (sy.CELL_GRU, 64, sy.DT_F32),
                                           (sy.CELL_TANH_RNN, 4, sy.DT_F32)])
 def test_fixed_sweep_count_speculates(cell, n, dtype):
     """tol = 0 (a fixed number of sweeps): the adjoint is enqueued behind the
-    only batch of sweeps, before the poll; results as the separate calls."""
+    only batch of sweeps, before the poll; results as the separate calls (the
+    per-channel cells' adjoint within rounding, see close)."""
     p = sy.custom_problem(cell, B=2, T=257, d=5, n=n, seed=n, w_scale=0.5, h0=True, dtype=dtype)
     print("case fixed sweeps cell", cell, "n", n, "dtype", dtype, flush=True)
     dp = bd.DeviceProblem(p)
     ref = run_separate(dp, 0.0, 3)
+    chan = cell in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
     for _ in range(2):
-        same(ref, run_combined(dp, 0.0, 3))
+        if chan:
+            close(ref, run_combined(dp, 0.0, 3), dtype == sy.DT_BF16)
+        else:
+            same(ref, run_combined(dp, 0.0, 3))
 
 
 def test_scalar_speculation_hit_and_miss(monkeypatch):
