@@ -73,18 +73,19 @@ def units_of(p: dict) -> int:
     return p["B"] * p["T"]
 
 
-def sweep_bytes_per_unit(p: dict, k: int) -> float:
+def sweep_bytes_per_unit(p: dict, k: int, adjoint_aggregates: bool = False) -> float:
     """Algorithmic HBM bytes per unit of one fused Newton sweep.
 
     Dense small state (time-parallel kernel): reads x (fused projection) and,
     from sweep 2 on, the current iterate h; writes the new h.  Per-channel
-    cells: read U (3 gates), read h (sweep >= 2), write h.  Sweep 1 starts from
-    h = 0 and does not read it.
+    cells: read U (3 gates), read h (sweep >= 2), write h; the last sweep of
+    a fixed sweep count followed by the adjoint also reads g (it composes the
+    adjoint's tile aggregates).  Sweep 1 starts from h = 0 and does not read it.
     """
     es = 2 if p["dtype"] == sy.DT_BF16 else 4
     sw = 2 if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else 1
     if p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG):
-        return 3 * es + sw * es + (sw * es if k >= 2 else 0)
+        return 3 * es + sw * es + (sw * es if k >= 2 else 0) + (sw * es if adjoint_aggregates else 0)
     return p["d"] * 4 + p["n"] * 4 + (p["n"] * 4 if k >= 2 else 0)
 
 
@@ -375,14 +376,17 @@ def main() -> int:
         if gn > 0:
             extra["adjoint_products_us"] = round(gm / gn * 1e3, 2)
     elif tr is not None and tr["sweep_launches"] > 0:
-        per_solve_bytes = sum(sweep_bytes_per_unit(p, k) for k in range(1, iters + 1)) * wu
+        # per-channel cells with a fixed sweep count: the step's last sweep
+        # composes the adjoint's aggregates (pararnn_solve_adjoint)
+        fused = chan and not elk and p["tol"] <= 0
+        per_solve_bytes = sum(sweep_bytes_per_unit(p, k, fused and k == iters) for k in range(1, iters + 1)) * wu
         nsolves = tr["sweep_launches"] / iters
         avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
         achieved = per_solve_bytes * nsolves / (tr["sweep_ms"] * 1e-3) / 1e9
         kname = ((ELK_FULL_KERNELS if args.jac == "own" and not (p["cell"] == sy.CELL_GRU_DIAG or p["n"] == 1)
                   else ELK_KERNELS) if elk else
                  "k_chan_carry + k_chan_pass per sweep (carry scan; cell, Jacobian, update and the next "
-                 "sweep's tile aggregates)" if chan else
+                 "sweep's tile aggregates, or in the last sweep of a fixed count the adjoint's)" if chan else
                  ("k_pipe<SweepPol>" if scalar_path(p) and not approx else "k_time_sweep") +
                  " (fused cell + Jacobian + scan + update)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -179,14 +179,37 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     }
 }
 
+// Sums the split partials in split order (a fixed order: the result does not
+// depend on scheduling).  Four adjacent elements per thread when rows are
+// whole 16-byte groups, else one.
 template <typename TO>
 __global__ void k_gemm_splitk_sum(const GemmArgs g) {
+  const size_t MN = (size_t)g.M * g.N;
+  const bool vec = (g.N % 4) == 0 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0 && sizeof(TO) == 4;
+  if (vec) {
+    const size_t e = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (e >= MN) return;
+    float4 s = *reinterpret_cast<const float4 *>(g.ws + e);
+    for (int q = 1; q < g.splits; q++) {
+      const float4 v = *reinterpret_cast<const float4 *>(g.ws + (size_t)q * MN + e);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const size_t row = e / g.N, col = e % g.N;
+    *reinterpret_cast<float4 *>((float *)g.C + row * g.ldc + col) = s;
+    return;
+  }
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (size_t)g.M * g.N) return;
+  if (e >= MN) return;
   float s = 0.f;
-  for (int q = 0; q < g.splits; q++) s += g.ws[(size_t)q * g.M * g.N + e];
+  for (int q = 0; q < g.splits; q++) s += g.ws[(size_t)q * MN + e];
   const size_t row = e / g.N, col = e % g.N;
   store_out<TO>((TO *)g.C + row * g.ldc + col, s);
+}
+template <typename TO>
+static unsigned splitk_sum_blocks(const GemmArgs &g) {
+  const size_t tot = (size_t)g.M * g.N;
+  const bool vec = (g.N % 4) == 0 && (g.ldc % 4) == 0 && ((uintptr_t)g.C % 16) == 0 && sizeof(TO) == 4;
+  return (unsigned)(((vec ? (tot + 3) / 4 : tot) + 255) / 256);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,8 +703,7 @@ static hipError_t gemm_big_launch(const GemmArgs &g, hipStream_t s) {
   if constexpr (KO) hipLaunchKernelGGL((k_gemm_bf16_nt<TO, KO>), dim3(tm * tn, g.splits), dim3(GT), 0, s, g, tm, tn);
   else hipLaunchKernelGGL((k_gemm_bf16_dl<TO>), dim3(tm * tn, g.splits), dim3(DGT), 0, s, g, tm, tn);
   if (g.splits > 1) {
-    const size_t tot = (size_t)g.M * g.N;
-    hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3(splitk_sum_blocks<TO>(g)), dim3(256), 0, s, g);
   }
   return hipGetLastError();
 }
@@ -691,8 +713,7 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
   hipLaunchKernelGGL((k_gemm<T, AKC, BKC, TO>), dim3(tiles, g.splits), dim3(256), 0, s, g);
   if (g.splits > 1) {
-    const size_t tot = (size_t)g.M * g.N;
-    hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_splitk_sum<TO>), dim3(splitk_sum_blocks<TO>(g)), dim3(256), 0, s, g);
   }
   return hipGetLastError();
 }
