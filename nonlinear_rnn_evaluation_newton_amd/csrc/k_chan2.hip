@@ -43,9 +43,10 @@ constexpr int C2_NG = CHAN2_TT / C2_P;  // load groups per tile
 constexpr int C2_CW = 16;               // wavefronts per carry block
 constexpr int C2_R = 4;                 // tiles per carry chunk (their loads are issued together)
 
-// Store CNT values as ST (bf16: round to nearest even); out-of-range offsets
+// Store CNT values as ST (bf16: round to nearest even) with cache policy POL
+// (SC_NT for outputs nothing in the call reads back); out-of-range offsets
 // are dropped.
-template <typename ST, int CNT>
+template <typename ST, int CNT, int POL = 0>
 __device__ inline void bst(Rsrc r, unsigned off, const float *in) {
   constexpr int BYTES = CNT * (int)sizeof(ST);
   auto word = [&](int i) -> unsigned {
@@ -53,18 +54,18 @@ __device__ inline void bst(Rsrc r, unsigned off, const float *in) {
     else return __float_as_uint(in[i]);
   };
   if constexpr (BYTES == 2) {
-    st_u16(r, off, f2bf(in[0]));
+    __builtin_amdgcn_raw_buffer_store_b16(f2bf(in[0]), r, off, 0, POL);
   } else if constexpr (BYTES == 4) {
-    st_u32(r, off, word(0));
+    __builtin_amdgcn_raw_buffer_store_b32(word(0), r, off, 0, POL);
   } else if constexpr (BYTES == 8) {
     u32x2 v;
     v.x = word(0); v.y = word(1);
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, POL);
   } else {
     static_assert(BYTES == 16, "unsupported access width");
     u32x4 v;
     v.x = word(0); v.y = word(1); v.z = word(2); v.w = word(3);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POL);
   }
 }
 
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(256) void k_chan_adj_pass(const ChanArgs a) {
         }
       }
       if constexpr (APPLY) {
-        bst<ST, CPL * SW>(rl, slane + (unsigned)(s * S * ES), lo);
+        bst<ST, CPL * SW, SC_NT>(rl, slane + (unsigned)(s * S * ES), lo);
 #pragma unroll
         for (int k3 = 0; k3 < 3; k3++) bst<ST, CPL>(rd, ulane + (unsigned)((s * 3 * n + k3 * n) * ES), du[k3]);
         if (t0 + s == 0 && a.dh0 && active) {

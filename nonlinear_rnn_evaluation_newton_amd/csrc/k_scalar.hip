@@ -707,8 +707,8 @@ struct AdjPol : ScBase {
         if (e == 0) dh0 = J * l;
       }
       const unsigned off = (in && t < T) ? (unsigned)t * 4u : SC_OOB;
-      st4(rl, off, lv[0], lv[1], lv[2], lv[3]);
-      st4(rd, off, dxv[0], dxv[1], dxv[2], dxv[3]);
+      st4_nt(rl, off, lv[0], lv[1], lv[2], lv[3]);
+      st4_nt(rd, off, dxv[0], dxv[1], dxv[2], dxv[3]);
       st1(r0, t == 0 ? 0u : SC_OOB, dh0);
       c = fmaf(Tl.tA[q], c, Tl.tb[q]);
     }

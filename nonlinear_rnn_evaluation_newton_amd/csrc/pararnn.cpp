@@ -912,8 +912,11 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   }
   if (tr.on && !per_sweep_events) {
     // a batch's launches past the stop exit at once; count the ones that worked
+    // (the host has seen the snapshot written after the batch's end event, but
+    // the runtime may not report that event complete yet: wait for it)
     for (int i = 0; i < nbatch && batch_first[i] <= out_iters; i++) {
       float ms = 0.f;
+      HIPCHK(hipEventSynchronize(tr.sw[2 * (batch_last[i] - 1) + 1]));
       HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (batch_first[i] - 1)], tr.sw[2 * (batch_last[i] - 1) + 1]));
       tr.ms[TR_SWEEP] += ms;
       tr.cnt[TR_SWEEP] += (batch_last[i] < out_iters ? batch_last[i] : out_iters) - batch_first[i] + 1;
@@ -923,6 +926,7 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     const int m = out_iters < Trace::CAP ? out_iters : Trace::CAP;
     for (int kk = 1; kk <= m; kk++) {
       float ms = 0.f;
+      HIPCHK(hipEventSynchronize(tr.sw[2 * (kk - 1) + 1]));
       HIPCHK(hipEventElapsedTime(&ms, tr.sw[2 * (kk - 1)], tr.sw[2 * (kk - 1) + 1]));
       tr.ms[TR_SWEEP] += ms;
       tr.cnt[TR_SWEEP]++;

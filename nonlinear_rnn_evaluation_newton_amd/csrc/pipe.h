@@ -66,6 +66,14 @@ __device__ inline void st4(Rsrc r, unsigned off, float a, float b, float c, floa
   v.x = __float_as_uint(a); v.y = __float_as_uint(b); v.z = __float_as_uint(c); v.w = __float_as_uint(d);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
+// Non-temporal store (cache policy NT) for outputs nothing in the call reads
+// back: the lines are not kept in the caches, which are left to the inputs.
+constexpr int SC_NT = 2;
+__device__ inline void st4_nt(Rsrc r, unsigned off, float a, float b, float c, float d) {
+  u32x4 v;
+  v.x = __float_as_uint(a); v.y = __float_as_uint(b); v.z = __float_as_uint(c); v.w = __float_as_uint(d);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, SC_NT);
+}
 __device__ inline void st1(Rsrc r, unsigned off, float a) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, 0);
 }
