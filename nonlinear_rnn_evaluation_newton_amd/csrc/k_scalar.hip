@@ -498,7 +498,7 @@ struct SweepPol : ScBase {
   // block maximum of |dh| into a shard of the sweep's convergence measure
   __device__ static void finish(const TimeArgs &a, Acc &acc, ScShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const unsigned m = wave_max_u32(acc.dmax);
+    const unsigned m = wave_max_dpp(acc.dmax);
     if (lane == 0 && wid < SC_CW) sh.dmax[wid] = m;
     __syncthreads();
     if (tid == 0) {
@@ -730,7 +730,7 @@ struct AdjPol : ScBase {
     }
 #pragma unroll
     for (int i = 0; i < P; i++) {
-      const float w = wave_sum(v[i]);
+      const float w = wave_total(v[i]);
       if (lane == 0 && wid < SC_CW) sh.red[wid][i] = w;
     }
     __syncthreads();
