@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256) void k_time_adjoint(const TimeArgs a) {
   // block reduction of the weight-gradient partials
 #pragma unroll
   for (int p = 0; p < P; p++) {
-    float v = wave_sum(acc[p]);
+    float v = wave_total(acc[p]);
     if (lane == 0) s_red[wid][p] = v;
   }
   __syncthreads();

@@ -30,35 +30,6 @@ __device__ inline float rdlane(float v, int l) { return __int_as_float(__builtin
 __device__ inline float shift_in(float first, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
-// v of the lane the DPP control names (0 where there is none, or where the
-// row mask leaves the row out)
-template <int CTRL, int ROWS>
-__device__ inline unsigned dpp_or0(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
-}
-// Sum and maximum over the wavefront's 64 lanes, returned to every lane: an
-// inclusive scan by row shifts (1, 2, 4, 8) and row broadcasts (15, 31),
-// whose last lane holds the total.  A fixed order, and no LDS round trip per
-// level as a shuffle butterfly has.
-__device__ inline float wave_total(float v) {
-  v += __uint_as_float(dpp_or0<0x111, 0xf>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_or0<0x112, 0xf>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_or0<0x114, 0xf>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_or0<0x118, 0xf>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_or0<0x142, 0xa>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_or0<0x143, 0xc>(__float_as_uint(v)));
-  return rdlane(v, 63);
-}
-__device__ inline unsigned wave_max_dpp(unsigned v) {
-  v = max(v, dpp_or0<0x111, 0xf>(v));
-  v = max(v, dpp_or0<0x112, 0xf>(v));
-  v = max(v, dpp_or0<0x114, 0xf>(v));
-  v = max(v, dpp_or0<0x118, 0xf>(v));
-  v = max(v, dpp_or0<0x142, 0xa>(v));
-  v = max(v, dpp_or0<0x143, 0xc>(v));
-  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // lane l receives v of lane l + 1; lane 63 receives last
 __device__ inline float shift_out(float last, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));
