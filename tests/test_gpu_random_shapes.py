@@ -1,0 +1,160 @@
+"""GPU parity on seeded random problems across the supported-problem table:
+every cell family, Jacobian choice, storage type and kernel path (small
+dense time-parallel, scalar-state pipeline, per-channel passes, dense n = 64
+MFMA with zero padding), at random batch, length, input and state widths,
+with and without h0.  Each case runs a random fixed number of sweeps (so the
+k-th iterate is compared, whatever the stop rule would do) against the fp64
+oracle's sweep with the same Jacobian, then the adjoint at the GPU's
+trajectory against the oracle's reverse-mode adjoint.  Linear cells are
+drawn with a recurrent spectral radius of at most 0.95, so no trajectory
+leaves the fp32 range; status and sweep count must still equal the oracle's.
+
+Bars: fp32 storage max-abs 1e-4 (scaled by max(1, |ref|)) on h, lambda, dx,
+dh0 and 1e-4 norm-wise relative on the weight gradients; bf16 storage 2e-2
+norm-wise relative on every tensor."""
+import numpy as np
+import pytest
+
+import oracle
+from nonlinear_rnn_evaluation_newton_amd import binding as bd
+from nonlinear_rnn_evaluation_newton_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ATOL = 1e-4
+RTOL_BF = 2e-2
+RTOL_W = 1e-4
+NCASES = 200
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def draw(i: int) -> dict:
+    """Case i: a family by i % 5, sizes and options from a generator seeded by i."""
+    rng = np.random.default_rng(1000 + i)
+    fam = i % 5
+    ri = lambda lo, hi: int(rng.integers(lo, hi + 1))
+    h0 = bool(rng.integers(0, 2))
+    dtype = sy.DT_F32
+    if fam == 0:    # small dense cells on the time-parallel kernels
+        cell = [sy.CELL_TANH_RNN, sy.CELL_GRU, sy.CELL_LINEAR][ri(0, 2)]
+        n, d, B, T = ri(1, 8), ri(1, 8), ri(1, 4), ri(1, 2500)
+        jac = [sy.JAC_DENSE, sy.JAC_DIAG, sy.JAC_ZERO][ri(0, 2)]
+    elif fam == 1:  # scalar state: the scalar pipeline takes Newton with T % 4 == 0
+        cell = [sy.CELL_TANH_RNN, sy.CELL_GRU, sy.CELL_LINEAR][ri(0, 2)]
+        n, d, B, T = 1, 1, ri(1, 6), 4 * ri(1, 12000)
+        jac = sy.JAC_DENSE
+    elif fam == 2:  # diagonal GRU
+        cell = sy.CELL_GRU_DIAG
+        n, d, B, T = ri(1, 300), ri(1, 200), ri(1, 3), ri(1, 600)
+        jac = [sy.JAC_DIAG, sy.JAC_ZERO][ri(0, 1)]
+        dtype = [sy.DT_F32, sy.DT_BF16][ri(0, 1)]
+    elif fam == 3:  # CIFG/peephole LSTM
+        cell = sy.CELL_LSTM_CIFG_DIAG
+        n, d, B, T = ri(1, 200), ri(1, 200), ri(1, 3), ri(1, 600)
+        jac = [sy.JAC_BLOCK2, sy.JAC_DIAG, sy.JAC_ZERO][ri(0, 2)]
+        dtype = [sy.DT_F32, sy.DT_BF16][ri(0, 1)]
+    else:           # dense GRU / tanh RNN of width 9..64 on the n = 64 kernels
+        cell = [sy.CELL_GRU, sy.CELL_TANH_RNN][ri(0, 1)]
+        n, d, B, T = ri(9, 64), ri(1, 40), ri(1, 2), ri(1, 400)
+        jac = [sy.JAC_DENSE, sy.JAC_DIAG, sy.JAC_ZERO][ri(0, 2)]
+    # Newton converges in a few sweeps; the approximate Jacobians' iterates
+    # are compared after a few sweeps as well (the k-th iterate is defined)
+    k = ri(1, min(T, 6))
+    p = sy.custom_problem(cell, B=B, T=T, d=d, n=n, seed=7 * i + 1, w_scale=0.8, dtype=dtype, h0=h0)
+    p = dict(p, jac=jac, name=f"random{i}_{sy.CELL_NAMES[cell]}")
+    if cell == sy.CELL_LINEAR:
+        # a linear recurrence with spectral radius above 1 grows past the
+        # fp32 range over a long sequence: keep it at most 0.95
+        rho = float(np.abs(np.linalg.eigvals(p["W_h"])).max())
+        if rho > 0.95:
+            p["W_h"] = sy.round_storage(p["W_h"] * (0.95 / rho), dtype)
+    own = jac == sy.natural_jac(cell) or (jac == sy.JAC_DIAG and (cell == sy.CELL_GRU_DIAG or n == 1))
+    approx = oracle.NEWTON if own else oracle.JACOBI if jac == sy.JAC_ZERO else oracle.QUASI
+    return dict(p=p, k=k, approx=approx, bf16=dtype == sy.DT_BF16)
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_random_problem(i):
+    c = draw(i)
+    p, k, bf16 = c["p"], c["k"], c["bf16"]
+    say("case", i, p["name"], "jac", p["jac"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"], "sweeps", k,
+        "bf16", bf16, "h0", bool(np.any(p["h0"])))
+    dp = bd.DeviceProblem(p)
+    st, it, _ = dp.solve(tol=0.0, max_iters=k)
+    torch.cuda.synchronize()
+    h = to64(dp.h)
+    ho, ito, sto, _ = oracle.deer(p, tol=0.0, max_iters=k, approx=c["approx"])
+    say("  gpu status", st, "sweeps", it, "| oracle", sto, ito)
+    assert (st, it) == (sto, ito) == (bd.PR_OK, k)
+    if bf16:
+        r = rel(h, ho)
+        say("  h rel", r)
+        assert r <= RTOL_BF
+    else:
+        err = float(np.abs(h - ho).max())
+        say("  h abs", err)
+        assert err <= ATOL * max(1.0, float(np.abs(ho).max()))
+
+    st, a = dp.adjoint()
+    torch.cuda.synchronize()
+    assert st == bd.PR_OK
+    ref = oracle.adjoint(p, h)
+    for key in ("lam", "dx", "dh0"):
+        g = to64(a[key])
+        if bf16:
+            r = rel(g, ref[key])
+            say("  ", key, "rel", r)
+            assert r <= RTOL_BF, key
+        else:
+            err = float(np.abs(g - ref[key]).max())
+            say("  ", key, "abs", err)
+            assert err <= ATOL * max(1.0, float(np.abs(ref[key]).max())), key
+    keys = ["dW_x", "db_x", "dW_h", "db_h"] + (["dpeep"] if p["cell"] == sy.CELL_LSTM_CIFG_DIAG else [])
+    for key in keys:
+        r = rel(to64(a[key]), ref[key])
+        say("  ", key, "rel", r)
+        assert r <= (RTOL_BF if bf16 else RTOL_W), key
+
+
+@pytest.mark.parametrize("i", range(0, NCASES, 2))
+def test_random_problem_to_tolerance(i):
+    """Newton (the cell's own Jacobian) to tol 1e-5 on the fp32 cases of the
+    same draws: the sweep count must equal the oracle's unless one of the
+    oracle's measures lies within a factor 2 of tol (then fp32 rounding may
+    move the stop by one sweep), and the result must match."""
+    c = draw(i)
+    p = c["p"]
+    if c["bf16"] or c["approx"] != oracle.NEWTON:
+        pytest.skip("fp32 Newton cases only")
+    tol = 1e-5
+    say("case", i, p["name"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"])
+    dp = bd.DeviceProblem(p)
+    st, it, dl = dp.solve(tol=tol, max_iters=p["T"])
+    torch.cuda.synchronize()
+    ho, ito, sto, dlo = oracle.deer(p, tol=tol, max_iters=p["T"])
+    say("  gpu", st, it, dl, "| oracle", sto, ito, dlo)
+    assert st == sto == bd.PR_OK
+    near = bool(np.any((dlo > tol / 2) & (dlo < 2 * tol)))
+    assert it == ito or (near and abs(it - ito) <= 1)
+    err = float(np.abs(to64(dp.h) - ho).max())
+    say("  h abs", err)
+    assert err <= ATOL * max(1.0, float(np.abs(ho).max()))
