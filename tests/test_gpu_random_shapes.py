@@ -158,3 +158,87 @@ def test_random_problem_to_tolerance(i):
     err = float(np.abs(to64(dp.h) - ho).max())
     say("  h abs", err)
     assert err <= ATOL * max(1.0, float(np.abs(ho).max()))
+
+
+def draw_elk(i: int):
+    """The problem of case i for pararnn_solve_elk: ELK with the cell's own
+    Jacobian where it is built (the LSTM's 2x2 blocks, dense cells with
+    n <= 8, the diagonal GRU), else quasi-ELK; a damping from a few decades."""
+    c = draw(i)
+    p = c["p"]
+    rng = np.random.default_rng(5000 + i)
+    cell, n = p["cell"], p["n"]
+    can_full = cell in (sy.CELL_LSTM_CIFG_DIAG, sy.CELL_GRU_DIAG) or (n <= 8 and p["d"] <= 8)
+    full = can_full and bool(rng.integers(0, 2))
+    lam = [0.0, 0.05, 0.5, 2.0][int(rng.integers(0, 4))]
+    q = dict(p, jac=sy.natural_jac(cell) if full else sy.JAC_DIAG)
+    return q, c["k"], lam, full, c["bf16"]
+
+
+@pytest.mark.parametrize("i", range(1, NCASES, 2))
+def test_random_elk(i):
+    """pararnn_solve_elk on the odd draws, a fixed sweep count, against the
+    oracle's ELK (full covariances) or quasi-ELK with the same damping."""
+    p, k, lam, full, bf16 = draw_elk(i)
+    say("case", i, p["name"], "full" if full else "quasi", "lambda", lam, "B", p["B"], "T", p["T"], "d", p["d"],
+        "n", p["n"], "sweeps", k, "bf16", bf16)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, _ = dp.solve_elk(lam, tol=0.0, max_iters=k)
+    torch.cuda.synchronize()
+    ho, ito, sto, _ = (oracle.elk_full if full else oracle.elk)(p, lam, tol=0.0, max_iters=k)
+    say("  gpu status", st, "sweeps", it, "| oracle", sto, ito)
+    assert (st, it) == (sto, ito) == (bd.PR_OK, k)
+    h = to64(dp.h)
+    if bf16:
+        r = rel(h, ho)
+        say("  h rel", r)
+        assert r <= RTOL_BF
+    else:
+        err = float(np.abs(h - ho).max())
+        say("  h abs", err)
+        assert err <= ATOL * max(1.0, float(np.abs(ho).max()))
+
+
+def signed_permutations(rng, shape, q):
+    """Matrices q x q with one entry of -1, 0 or 1 per row in a random column:
+    every product of them has entries in {-1, 0, 1}, so the scan is exact in
+    fp32 for small integer offsets."""
+    A = np.zeros(shape + (q, q))
+    col = rng.integers(0, q, size=shape + (q,))
+    val = rng.integers(-1, 2, size=shape + (q,)).astype(float)
+    np.put_along_axis(A, col[..., None], val[..., None], axis=-1)
+    return A
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_random_affine_scan(i):
+    """pararnn_affine_scan on random shapes (diagonal, 2x2 blocks, dense
+    n <= 8; forward and reverse) with exactly representable data: bit-exact
+    against the oracle's sequential solve."""
+    rng = np.random.default_rng(9000 + i)
+    kind = i % 3
+    B, T, reverse = int(rng.integers(1, 5)), int(rng.integers(1, 5000)), bool(rng.integers(0, 2))
+    if kind == 0:
+        n = int(rng.integers(1, 400))
+        jac, ok = bd.PR_JAC_DIAG, oracle.DIAG
+        A = rng.integers(-1, 2, size=(B, T, n)).astype(float)
+        b = rng.integers(-4, 5, size=(B, T, n)).astype(float)
+    elif kind == 1:
+        n = int(rng.integers(1, 300))
+        jac, ok = bd.PR_JAC_BLOCK2, oracle.BLOCK2
+        A = signed_permutations(rng, (B, T, n), 2)
+        b = rng.integers(-4, 5, size=(B, T, n, 2)).astype(float)
+    else:
+        n = int(rng.integers(1, 9))
+        jac, ok = bd.PR_JAC_DENSE, oracle.DENSE
+        A = signed_permutations(rng, (B, T), n)
+        b = rng.integers(-4, 5, size=(B, T, n)).astype(float)
+    say("scan case", i, "jac", jac, "B", B, "T", T, "n", n, "reverse", reverse)
+    y_ref = oracle.affine_solve(ok, A, b, reverse=reverse)
+    At = torch.tensor(A, dtype=torch.float32, device="cuda")
+    bt = torch.tensor(b, dtype=torch.float32, device="cuda")
+    yt = torch.empty_like(bt)
+    ws = torch.empty(bd.scan_workspace_bytes(jac, B, T, n), dtype=torch.uint8, device="cuda")
+    bd.affine_scan(jac, At, bt, yt, ws, reverse=reverse)
+    torch.cuda.synchronize()
+    assert np.array_equal(yt.cpu().numpy().astype(np.float64), y_ref)
