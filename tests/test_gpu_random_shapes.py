@@ -242,3 +242,63 @@ def test_random_affine_scan(i):
     bd.affine_scan(jac, At, bt, yt, ws, reverse=reverse)
     torch.cuda.synchronize()
     assert np.array_equal(yt.cpu().numpy().astype(np.float64), y_ref)
+
+
+def adjoint_buffers(dp):
+    p = dp.p
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = dict(lam=torch.full_like(dp.h, float("nan")), dx=torch.full_like(dp.x, float("nan")),
+             dh0=torch.full((p["B"], p["S"]), float("nan"), dtype=dp.tdtype, device="cuda"),
+             W_x=torch.full(tuple(dp.W_x.shape), float("nan"), **f32),
+             b_x=torch.full(tuple(dp.b_x.shape), float("nan"), **f32),
+             W_h=torch.full(tuple(dp.W_h.shape), float("nan"), **f32),
+             b_h=torch.full(tuple(dp.b_h.shape), float("nan"), **f32))
+    if dp.peep is not None:
+        o["peep"] = torch.full(tuple(dp.peep.shape), float("nan"), **f32)
+    return o
+
+
+@pytest.mark.parametrize("i", range(0, NCASES, 4))
+def test_random_solve_adjoint(i):
+    """pararnn_solve_adjoint (the benchmark's call) on every fourth draw with
+    the cell's own Jacobian, called twice in a row so that the second call
+    speculates where the path allows it: the per-channel cells with their
+    fixed sweep count (the last sweep composes the adjoint's aggregates),
+    the others to tol 1e-5.  Each call's h against the oracle's sweeps, its
+    adjoint against the oracle's at the GPU's h."""
+    c = draw(i)
+    p = dict(c["p"], jac=sy.natural_jac(c["p"]["cell"]))
+    bf16 = c["bf16"]
+    chan = p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
+    tol, mi = (0.0, c["k"]) if chan else (1e-5, p["T"])
+    say("case", i, p["name"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"], "tol", tol, "max_iters", mi,
+        "bf16", bf16)
+    dp = bd.DeviceProblem(p)
+    ho, ito, sto, dlo = oracle.deer(p, tol=tol, max_iters=mi)
+    for call in range(2):
+        o = adjoint_buffers(dp)
+        st, it, _ = bd.solve_adjoint(dp.prob, dp.w, dp.x, dp.h0, tol, mi, dp.h, dp.g, dp.ws, o["lam"], o["dx"],
+                                     o["dh0"], {k: o[k] for k in ("W_x", "b_x", "W_h", "b_h", "peep") if k in o})
+        torch.cuda.synchronize()
+        say("  call", call, "status", st, "sweeps", it, "| oracle", sto, ito)
+        assert st == sto == bd.PR_OK
+        near = bool(np.any((dlo > tol / 2) & (dlo < 2 * tol)))
+        assert it == ito or (near and abs(it - ito) <= 1)
+        h = to64(dp.h)
+        hr = ho if it == ito else oracle.deer(p, tol=0.0, max_iters=it)[0]
+        if bf16:
+            assert rel(h, hr) <= RTOL_BF
+        else:
+            assert float(np.abs(h - hr).max()) <= ATOL * max(1.0, float(np.abs(hr).max()))
+        ref = oracle.adjoint(p, h)
+        for key in ("lam", "dx", "dh0"):
+            g = to64(o[key])
+            if bf16:
+                assert rel(g, ref[key]) <= RTOL_BF, key
+            else:
+                assert float(np.abs(g - ref[key]).max()) <= ATOL * max(1.0, float(np.abs(ref[key]).max())), key
+        for key, rk in (("W_x", "dW_x"), ("b_x", "db_x"), ("W_h", "dW_h"), ("b_h", "db_h"), ("peep", "dpeep")):
+            if key in o:
+                r = rel(to64(o[key]), ref[rk])
+                say("   ", key, "rel", r)
+                assert r <= (RTOL_BF if bf16 else RTOL_W), key
