@@ -302,3 +302,33 @@ def test_random_solve_adjoint(i):
                 r = rel(to64(o[key]), ref[rk])
                 say("   ", key, "rel", r)
                 assert r <= (RTOL_BF if bf16 else RTOL_W), key
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_lsim(i):
+    """pararnn_lsim on random batch, length, state, input and output widths
+    (up to 8) and sample times, with and without an initial state and a
+    state output, against the oracle's zero-order-hold recurrence; max-abs
+    1e-4 relative to max(1, |ref|) of each tensor."""
+    rng = np.random.default_rng(12000 + i)
+    B, T = int(rng.integers(1, 5)), int(rng.integers(1, 6000))
+    nx, m, pp = (int(rng.integers(1, 9)) for _ in range(3))
+    dt = float(np.float32(10.0 ** rng.uniform(-3, -1)))
+    with_x0, want_x = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    q = sy.make_lsim(B=B, T=T, nx=nx, m=m, p=pp, dt=dt, seed=13 * i + 5, x0=with_x0)
+    say("lsim case", i, "B", B, "T", T, "nx", nx, "m", m, "p", pp, "dt", dt, "x0", with_x0, "x out", want_x)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    ws = torch.empty(bd.lsim_workspace_bytes(B, T, nx, m, pp), dtype=torch.uint8, device="cuda")
+    x = torch.full((B, T, nx), float("nan"), dtype=torch.float32, device="cuda") if want_x else None
+    y = torch.full((B, T, pp), float("nan"), dtype=torch.float32, device="cuda")
+    bd.lsim(dev(q["A"]), dev(q["Bm"]), dev(q["Cm"]), dev(q["Dm"]), q["dt"], dev(q["U"]), dev(q["x0"]), x, y, ws)
+    torch.cuda.synchronize()
+    yo, xo = oracle.lsim(q["A"], q["Bm"], q["Cm"], q["Dm"], q["U"], np.arange(T) * q["dt"], x0=q["x0"])
+    e = lambda a, r: float(np.abs(a - r).max() / max(1.0, np.abs(r).max()))
+    ey = e(y.double().cpu().numpy(), yo)
+    say("  err y", ey)
+    assert ey <= 1e-4
+    if want_x:
+        ex = e(x.double().cpu().numpy(), xo)
+        say("  err x", ex)
+        assert ex <= 1e-4
