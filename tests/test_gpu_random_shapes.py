@@ -135,16 +135,18 @@ def test_random_problem(i):
         assert r <= (RTOL_BF if bf16 else RTOL_W), key
 
 
-@pytest.mark.parametrize("i", range(0, NCASES, 2))
+def _fp32_newton(i: int) -> bool:
+    c = draw(i)
+    return not c["bf16"] and c["approx"] == oracle.NEWTON
+
+
+@pytest.mark.parametrize("i", [i for i in range(0, NCASES, 2) if _fp32_newton(i)])
 def test_random_problem_to_tolerance(i):
     """Newton (the cell's own Jacobian) to tol 1e-5 on the fp32 cases of the
     same draws: the sweep count must equal the oracle's unless one of the
     oracle's measures lies within a factor 2 of tol (then fp32 rounding may
     move the stop by one sweep), and the result must match."""
-    c = draw(i)
-    p = c["p"]
-    if c["bf16"] or c["approx"] != oracle.NEWTON:
-        pytest.skip("fp32 Newton cases only")
+    p = draw(i)["p"]
     tol = 1e-5
     say("case", i, p["name"], "B", p["B"], "T", p["T"], "d", p["d"], "n", p["n"])
     dp = bd.DeviceProblem(p)
