@@ -35,6 +35,10 @@ ELK_KERNELS = ("quasi-ELK sweep: per-channel cells k_elkc_filter + k_elkc_filter
 ELK_FULL_KERNELS = ("ELK sweep (the cell's own Jacobian, full covariances): producer of J | r (k_elkf_jr_lstm or "
                     "k_elkf_jr_dense), then k_elkf_elem (chunk filtering elements), k_elkf_fcarry, k_elkf_gains "
                     "(in-chunk filter and smoother gains), k_elkf_scarry, k_elkf_apply")
+ELK64_KERNELS = ("ELK sweep with the full 64x64 Jacobian: k_d64_gates (the Jacobian's factors and the residual), "
+                 "k_elk64_rows (the damped step's normal equations, one 64x64 block row per step), per level of "
+                 "the block cyclic reduction k_elk64_elim and k_elk64_keep, k_elk64_root, per level k_elk64_back, "
+                 "k_elk64_apply")
 FP32_MFMA_PEAK_TFS = 157.3
 
 
@@ -364,7 +368,18 @@ def main() -> int:
     wu = units_of(p)
     chan = p["cell"] in (sy.CELL_GRU_DIAG, sy.CELL_LSTM_CIFG_DIAG)
     dense64 = p["cell"] == sy.CELL_GRU and p["n"] == 64
-    if tr is not None and tr["sweep_launches"] > 0 and dense64 and approx:
+    if tr is not None and tr["sweep_launches"] > 0 and dense64 and elk and args.jac == "own":
+        # ELK with the full 64 x 64 Jacobian: per step the sweep runs six
+        # 64 x 64 products on fp32 MFMA (J^T J for the normal equations'
+        # diagonal block; at the step's elimination W A, W A^T and A^T P; at
+        # its row's updates A P and A Q) and one 64 x 64 inverse (VALU)
+        flops = 6 * 2.0 * 64 ** 3
+        avg_ms = tr["sweep_ms"] / tr["sweep_launches"]
+        tfs = flops * B * T / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                    "frac": round(tfs / FP32_MFMA_PEAK_TFS, 4), "traffic": None, "kernel": ELK64_KERNELS,
+                    "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": flops * B * T}
+    elif tr is not None and tr["sweep_launches"] > 0 and dense64 and approx:
         # diagonal (or zero) Jacobian, n = 64: the sweep is the gates GEMM,
         # a per-channel scan and the update.  Algorithmic bytes per step: read
         # U (192 floats) and, from sweep 2 on, h (64); write h (64)

@@ -175,20 +175,24 @@ int pararnn_solve(const pr_problem *p, const pr_weights *w, const void *x, const
                   size_t ws_bytes, void *stream);
 
 /*
- * Quasi-ELK solve (Gonzalez et al. abstract: ELK stabilises DEER through the
- * connection between Levenberg-Marquardt and Kalman smoothing; Para-Seq
- * README, Main features: ELK and quasi-ELK solvers).  Each sweep takes the
- * damped step
- *   dh = argmin sum_t ||dh_t - d_t dh_{t-1} - r_t||^2 + lambda ||dh||^2
- * with d_t the diagonal of J_t (the LSTM: dc'/dc and dh'/dh), computed per
- * state entry as the Kalman filter / Rauch-Tung-Striebel smoother mean of
- * dh_t = d_t dh_{t-1} + r_t + N(0, 1) observed as 0 with variance 1/lambda,
- * then h += dh.  lambda = 0 is quasi-DEER; larger lambda shortens the steps
- * (lambda ||dh||^2 <= ||r||^2).  p->jac is not used.  Kernels exist for
- * every problem pararnn_solve supports: the tanh RNN and GRU with n <= 8 and
- * d <= 8 and the dense GRU and tanh RNN with any other n <= 64 (fp32),
- * GRU_DIAG and LSTM_CIFG_DIAG (fp32 or bf16); other problems return
- * PR_EUNSUPPORTED.  Arguments and results as
+ * ELK and quasi-ELK solves (Gonzalez et al. abstract: ELK stabilises DEER
+ * through the connection between Levenberg-Marquardt and Kalman smoothing;
+ * Para-Seq README, Main features: ELK and quasi-ELK solvers).  Each sweep
+ * takes the damped step
+ *   dh = argmin sum_t ||dh_t - M_t dh_{t-1} - r_t||^2 + lambda ||dh||^2,
+ * the Kalman filter / Rauch-Tung-Striebel smoother mean of
+ * dh_t = M_t dh_{t-1} + r_t + N(0, I) observed as 0 with covariance I/lambda,
+ * then h += dh.  p->jac chooses M_t: the cell's own Jacobian (ELK: the LSTM's
+ * 2x2 blocks with PR_JAC_BLOCK2, the dense cells' full n x n Jacobian with
+ * PR_JAC_DENSE) or its diagonal (quasi-ELK, PR_JAC_DIAG; the LSTM's dc'/dc
+ * and dh'/dh); PR_JAC_ZERO is refused with PR_EINVAL.  lambda = 0 is Newton's
+ * (quasi-DEER's) step; larger lambda shortens the steps
+ * (lambda ||dh||^2 <= ||r||^2).  Kernels exist for every problem
+ * pararnn_solve supports: the tanh RNN, GRU and linear cell with n <= 8 and
+ * d <= 8, the dense GRU and tanh RNN with any other n <= 64 (fp32; ELK there
+ * holds three 64 x 64 fp32 blocks per step in the workspace), GRU_DIAG and
+ * LSTM_CIFG_DIAG (fp32 or bf16); other problems return PR_EUNSUPPORTED.
+ * Arguments and results as
  * pararnn_solve, plus lambda (>= 0, finite); the workspace must hold
  * pararnn_elk_workspace_bytes (which also covers pararnn_adjoint).
  */

@@ -257,6 +257,20 @@ struct ElkFullArgs {
   int max_iters;
   SolveState *st;
 };
+// ELK with the full 64 x 64 Jacobian of the dense GRU: the damped step's
+// normal equations eliminated by block cyclic reduction (k_elk64.hip).
+struct Elk64Args {
+  const float *gates;      // [B*T, 5, 64] from the gates kernel: z, alpha, beta, gamma, res
+  const float *Wh;         // [192, 64]
+  float *A, *D, *S;        // [B*T, 64, 64] block rows (A, D become P, Q at elimination)
+  float *f, *g, *v, *x;    // [B*T, 64]
+  float *h;                // [B*T, 64] iterate
+  int B, T;
+  float lam;
+  int k;
+  SolveState *st;
+};
+hipError_t launch_elk64_passes(const Elk64Args &a, hipStream_t s);
 int elk_full_chunk_len(int T);
 hipError_t launch_elk_full_lstm(bool bf16, const ElkFullArgs &a, hipStream_t s);
 hipError_t launch_elk_full_dense(int cell, int Nv, const TimeArgs &ta, const ElkFullArgs &a, hipStream_t s);

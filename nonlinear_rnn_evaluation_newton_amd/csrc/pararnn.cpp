@@ -495,6 +495,7 @@ struct ElkLayout {
   size_t off_jr = 0, off_ge = 0, off_r1 = 0, off_pc = 0, off_mc = 0, off_r3 = 0, off_msc = 0;
   size_t off_fagg = 0, off_fcar = 0, off_fsub = 0, off_dr = 0, off_hb = 0;
   size_t off_elem = 0, off_fin = 0, off_rev = 0, off_msin = 0;
+  size_t off_A = 0, off_D = 0, off_S = 0, off_f = 0, off_g = 0, off_v = 0, off_x = 0;  // n = 64 ELK
   size_t bytes = 0;
   int cps = 0, nch = 0, cpf = 0, nchf = 0;
   bool full = false;           // the cell's own Jacobian (else its diagonal: quasi-ELK)
@@ -509,10 +510,6 @@ static int elk_kind(const pr_problem *p, const Plan &pl, bool *full) {
   if (p->jac == PR_JAC_ZERO) return fail(PR_EINVAL, "ELK needs a Jacobian: jac must be the cell's own or PR_JAC_DIAG");
   const bool own = (p->cell == PR_CELL_LSTM_CIFG_DIAG && p->jac == PR_JAC_BLOCK2) ||
                    (pl.path != PATH_CHAN && p->jac == PR_JAC_DENSE && p->n > 1);
-  if (own && pl.path == PATH_D64)
-    return fail(PR_EUNSUPPORTED,
-                "ELK with the full 64 x 64 Jacobian is not built (its covariance updates cost O(n^3) per step); "
-                "jac = PR_JAC_DIAG runs quasi-ELK");
   *full = own;
   return PR_OK;
 }
@@ -521,6 +518,19 @@ static int elk_layout(const pr_problem *p, const Plan &pl, ElkLayout *el) {
     return fail(PR_EUNSUPPORTED, "no quasi-ELK kernels for this problem");
   int rc = elk_kind(p, pl, &el->full);
   if (rc != PR_OK) return rc;
+  if (el->full && pl.path == PATH_D64) {  // block rows of the normal equations, 64 x 64 each
+    const size_t rows = (size_t)p->B * p->T;
+    size_t o = pl.solve_bytes;
+    el->off_A = o; o = align256(o + rows * 4096 * 4);
+    el->off_D = o; o = align256(o + rows * 4096 * 4);
+    el->off_S = o; o = align256(o + rows * 4096 * 4);
+    el->off_f = o; o = align256(o + rows * 64 * 4);
+    el->off_g = o; o = align256(o + rows * 64 * 4);
+    el->off_v = o; o = align256(o + rows * 64 * 4);
+    el->off_x = o; o = align256(o + rows * 64 * 4);
+    el->bytes = o;
+    return PR_OK;
+  }
   if (el->full) {
     const int N = pl.path == PATH_CHAN ? 2 : pl.N;
     el->Nf = N;
@@ -622,7 +632,9 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
     if (!(*elk_lambda >= 0.f) || *elk_lambda > 3.0e38f) return fail(PR_EINVAL, "lambda must be >= 0 and finite");
     rc = elk_layout(p, pl, &el);
     if (rc != PR_OK) return rc;
-    pl.approx = APX_DIAG;  // the quasi-ELK producers evaluate the Jacobian's diagonal
+    // the quasi-ELK producers evaluate the Jacobian's diagonal; ELK on the
+    // 64 x 64 GRU takes the gates kernel's factors of the whole Jacobian
+    pl.approx = el.full && pl.path == PATH_D64 ? APX_NEWTON : APX_DIAG;
     pl.solve_bytes = el.bytes;
   }
   if (!w || !w->W_x || !w->W_h) return fail(PR_EINVAL, "W_x and W_h are required");
@@ -723,7 +735,22 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
   ElkArgs ea{};
   ElkChanArgs eca{};
   ElkFullArgs fa{};
-  if (elk_lambda && el.full) {
+  Elk64Args e64{};
+  if (elk_lambda && el.full && pl.path == PATH_D64) {
+    e64.gates = da.gates;
+    e64.Wh = da.Wh;
+    e64.A = (float *)(ws + el.off_A);
+    e64.D = (float *)(ws + el.off_D);
+    e64.S = (float *)(ws + el.off_S);
+    e64.f = (float *)(ws + el.off_f);
+    e64.g = (float *)(ws + el.off_g);
+    e64.v = (float *)(ws + el.off_v);
+    e64.x = (float *)(ws + el.off_x);
+    e64.h = (float *)h;
+    e64.B = p->B; e64.T = p->T;
+    e64.lam = *elk_lambda;
+    e64.st = (SolveState *)(ws + pl.off_state);
+  } else if (elk_lambda && el.full) {
     fa.jr = (float *)(ws + el.off_jr);
     fa.ge = (float *)(ws + el.off_ge);
     fa.elem = (float *)(ws + el.off_elem);
@@ -822,7 +849,12 @@ static int solve_impl(const pr_problem *p, const pr_weights *w, const void *x, c
       a.k = kk;
       const bool ev = tr.on && per_sweep_events && kk <= Trace::CAP;
       if (ev) HIPCHK(hipEventRecord(tr.sw[2 * (kk - 1)], s));
-      if (elk_lambda && el.full) {  // the damped step with the cell's own Jacobian
+      if (elk_lambda && el.full && pl.path == PATH_D64) {  // the gates, then the normal equations
+        da.k = kk;
+        HIPCHK(launch_d64_sweep_part(da, 0, s));
+        e64.k = kk;
+        HIPCHK(launch_elk64_passes(e64, s));
+      } else if (elk_lambda && el.full) {  // the damped step with the cell's own Jacobian
         fa.k = kk;
         if (pl.path == PATH_CHAN) HIPCHK(launch_elk_full_lstm(p->dtype == PR_BF16, fa, s));
         else HIPCHK(launch_elk_full_dense(kc, pl.N, a, fa, s));

@@ -92,10 +92,10 @@ def test_dense_gru_padded_to_64_workspace(n, d, jac, cell):
     q = _prob(n=64, d=d, jac=jac, B=3, T=100)
     for adj in (False, True):
         assert bd.workspace_bytes(pb, adj) > bd.workspace_bytes(q, adj) > 0
-    if jac == sy.JAC_DIAG:
-        assert bd.elk_workspace_bytes(pb) > bd.elk_workspace_bytes(q) > 0
-    else:
+    if jac == sy.JAC_ZERO:  # ELK needs a Jacobian
         assert bd.elk_workspace_bytes(pb) == 0
+    else:  # quasi-ELK, or ELK with the full 64 x 64 Jacobian
+        assert bd.elk_workspace_bytes(pb) > bd.elk_workspace_bytes(q) > 0
 
 
 def test_padded_dense_gru_arguments_rejected_without_device():
@@ -118,15 +118,13 @@ def test_padded_dense_gru_arguments_rejected_without_device():
                                    None, C.c_void_p(256), full - 1, None) == bd.PR_EWORKSPACE
     assert L.pararnn_adjoint(C.byref(pb), C.byref(w), v, None, v, None, None, None, None, None, C.c_void_p(256), full,
                              None) == bd.PR_EINVAL  # g is required
-    dense = _prob(n=20, d=3)
-    assert L.pararnn_solve_elk(C.byref(dense), C.byref(w), v, None, 0.5, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
-                               1 << 40, None) == bd.PR_EUNSUPPORTED
-    quasi = _prob(n=20, d=3, jac=sy.JAC_DIAG)
-    ews = bd.elk_workspace_bytes(quasi)
-    assert L.pararnn_solve_elk(C.byref(quasi), C.byref(w), v, None, -1.0, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
-                               ews, None) == bd.PR_EINVAL
-    assert L.pararnn_solve_elk(C.byref(quasi), C.byref(w), v, None, 0.5, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
-                               ews - 1, None) == bd.PR_EWORKSPACE
+    for jac in (sy.JAC_DENSE, sy.JAC_DIAG):  # ELK with the full 64 x 64 Jacobian, quasi-ELK
+        q = _prob(n=20, d=3, jac=jac)
+        ews = bd.elk_workspace_bytes(q)
+        assert L.pararnn_solve_elk(C.byref(q), C.byref(w), v, None, -1.0, 1e-6, 8, v, None, None, 0,
+                                   C.c_void_p(256), ews, None) == bd.PR_EINVAL
+        assert L.pararnn_solve_elk(C.byref(q), C.byref(w), v, None, 0.5, 1e-6, 8, v, None, None, 0, C.c_void_p(256),
+                                   ews - 1, None) == bd.PR_EWORKSPACE
 
 
 def test_missing_pointers_and_workspace_rejected():
@@ -246,8 +244,8 @@ def test_noalloc_scan_rejects_without_device():
 
 def test_elk_workspace_follows_the_jacobian():
     """pararnn_solve_elk takes the cell's own Jacobian (ELK) or its diagonal
-    (quasi-ELK); ELK on the 64 x 64 GRU and ELK without a Jacobian are
-    refused before any HIP call."""
+    (quasi-ELK); ELK without a Jacobian is refused before any HIP call.  ELK
+    on the 64 x 64 GRU holds three 64 x 64 block rows per step."""
     L = bd.lib()
     P = bd.make_problem
     lstm_full = bd.elk_workspace_bytes(P(sy.CELL_LSTM_CIFG_DIAG, sy.JAC_BLOCK2, bd.PR_BF16, 4, 8192, 2048, 2048))
@@ -255,8 +253,9 @@ def test_elk_workspace_follows_the_jacobian():
     assert lstm_full > lstm_quasi > 0
     assert bd.elk_workspace_bytes(P(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 256, 2, 4)) > 0
     assert bd.elk_workspace_bytes(P(sy.CELL_GRU, sy.JAC_DIAG, bd.PR_F32, 16, 16384, 32, 64)) > 0
-    for pb, code in ((P(sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 16, 16384, 32, 64), bd.PR_EUNSUPPORTED),
-                     (P(sy.CELL_GRU, sy.JAC_ZERO, bd.PR_F32, 2, 64, 3, 4), bd.PR_EINVAL)):
+    dense_full = bd.elk_workspace_bytes(P(sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 16, 16384, 32, 64))
+    assert dense_full >= 16 * 16384 * 3 * 4096 * 4
+    for pb, code in ((P(sy.CELL_GRU, sy.JAC_ZERO, bd.PR_F32, 2, 64, 3, 4), bd.PR_EINVAL),):
         assert bd.elk_workspace_bytes(pb) == 0
         w = bd.Weights(1, None, 1, None, None)
         rc = L.pararnn_solve_elk(C.byref(pb), C.byref(w), C.c_void_p(16), None, 0.1, 1e-6, 8, C.c_void_p(16), None,

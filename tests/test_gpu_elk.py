@@ -209,10 +209,9 @@ def test_small_dense_full_size_scalar_gru():
 
 
 def test_unsupported_and_invalid():
-    prob = bd.make_problem(sy.CELL_TANH_RNN, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)
-    assert bd.elk_workspace_bytes(prob) == 0  # no kernels for n = 16 at all
-    # ELK with the full 64 x 64 Jacobian is not built; without a Jacobian ELK is undefined
-    assert bd.elk_workspace_bytes(bd.make_problem(sy.CELL_GRU, sy.JAC_DENSE, bd.PR_F32, 1, 64, 32, 64)) == 0
+    prob = bd.make_problem(sy.CELL_LINEAR, sy.JAC_DENSE, bd.PR_F32, 2, 100, 2, 16)
+    assert bd.elk_workspace_bytes(prob) == 0  # no kernels for a linear cell with n = 16 at all
+    # without a Jacobian ELK is undefined
     assert bd.elk_workspace_bytes(bd.make_problem(sy.CELL_GRU, sy.JAC_ZERO, bd.PR_F32, 1, 64, 3, 4)) == 0
     q = quasi(sy.make_problem(5, B=1, T=64))
     dp = bd.DeviceProblem(q, elk=True)
@@ -300,6 +299,49 @@ def test_full_elk_lstm_full_size_sampled():
     r = float(np.abs(hg - hq).max() / max(np.abs(hq).max(), 1e-30))
     say("  sampled channels", ch, "rel err", r)
     assert r <= RTOL_BF
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.1, 2.0])
+@pytest.mark.parametrize("B,T", [(2, 1), (2, 2), (1, 3), (2, 5), (2, 33), (1, 100), (2, 257)])
+def test_full_elk_dense64(lam, B, T):
+    """ELK with the full 64 x 64 Jacobian of the dense GRU (the damped step's
+    normal equations by block cyclic reduction) against the oracle's Kalman
+    filter and smoother: one sweep, then three; lengths with one row, odd
+    and power-of-two-plus-one row counts."""
+    p = sy.make_problem(5, B=B, T=T)
+    check(p, lam, 0.0, 1, full=True)
+    check(p, lam, 0.0, 3, full=True)
+
+
+def test_full_elk_dense64_to_tolerance():
+    p = sy.make_problem(5, B=2, T=300)
+    check(p, 0.1, p["tol"], p["max_iters"], full=True)
+
+
+def test_full_elk_dense64_full_size():
+    """The full dense GRU workload (B=16, T=16384, d=32, n=64) with ELK
+    (lambda 0.1) to the workload's tolerance: the damped steps reach the
+    sequential rollout, the fixed point every sweep variant shares (the
+    oracle's Kalman smoother at this size would take hours on the host)."""
+    lam = 0.1
+    p = sy.make_problem(5, with_g=False)
+    say("full-size case", p["name"], "ELK lambda", lam)
+    dp = bd.DeviceProblem(p, elk=True)
+    st, it, dl = dp.solve_elk(lam, hist_cap=4096)
+    torch.cuda.synchronize()
+    say("  sweeps", it, "status", st, "deltas", dl)
+    assert st == bd.PR_OK and it < 100
+    err = float(np.abs(to64(dp.h) - oracle.rollout(p)).max())
+    say("  max abs err against the rollout", err)
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("cell,n,d", [(sy.CELL_GRU, 20, 3), (sy.CELL_TANH_RNN, 40, 6), (sy.CELL_GRU, 63, 33)])
+def test_full_elk_padded_dense(cell, n, d):
+    """Dense GRUs below 64 and tanh RNNs above 8 on the n = 64 kernels
+    (zero-padded), with h0 and biases."""
+    p = sy.custom_problem(cell, B=2, T=90, d=d, n=n, seed=n + d, w_scale=0.8, h0=True)
+    check(p, 0.3, 0.0, 3, full=True)
 
 
 def test_full_elk_damping_keeps_steps_bounded():

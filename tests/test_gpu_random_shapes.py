@@ -164,13 +164,14 @@ def test_random_problem_to_tolerance(i):
 
 def draw_elk(i: int):
     """The problem of case i for pararnn_solve_elk: ELK with the cell's own
-    Jacobian where it is built (the LSTM's 2x2 blocks, dense cells with
-    n <= 8, the diagonal GRU), else quasi-ELK; a damping from a few decades."""
+    Jacobian (the LSTM's 2x2 blocks, the dense cells' n x n on the small
+    kernels or 64 x 64 on the padded ones, the diagonal GRU) or quasi-ELK,
+    drawn at random; a damping from a few decades."""
     c = draw(i)
     p = c["p"]
     rng = np.random.default_rng(5000 + i)
     cell, n = p["cell"], p["n"]
-    can_full = cell in (sy.CELL_LSTM_CIFG_DIAG, sy.CELL_GRU_DIAG) or (n <= 8 and p["d"] <= 8)
+    can_full = cell != sy.CELL_LINEAR or n <= 8
     full = can_full and bool(rng.integers(0, 2))
     lam = [0.0, 0.05, 0.5, 2.0][int(rng.integers(0, 4))]
     q = dict(p, jac=sy.natural_jac(cell) if full else sy.JAC_DIAG)

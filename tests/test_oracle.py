@@ -798,6 +798,18 @@ def test_full_elk_step_solves_the_damped_least_squares(cell, lam):
             np.testing.assert_allclose(h_next[b] - h_prev[b], _damped_lsq_blocks(J[b], r[b], lam), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("lam", [0.1, 2.0])
+def test_full_elk_step_on_the_64_wide_gru(lam):
+    # the same check at the state width of the dense GRU workload (one 64 x 64
+    # block per step): the normal equations of a 6-step sequence
+    p = sy.make_problem(5, B=1, T=6)
+    h1, _, _, _ = oracle.elk_full(p, lam, tol=0.0, max_iters=1)
+    h2, _, _, _ = oracle.elk_full(p, lam, tol=0.0, max_iters=2)
+    for h_prev, h_next in ((np.zeros_like(h1), h1), (h1, h2)):
+        J, r = _full_jacobian_and_residual(p, h_prev)
+        np.testing.assert_allclose(h_next[0] - h_prev[0], _damped_lsq_blocks(J[0], r[0], lam), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("cell", FULL_ELK_CELLS)
 def test_full_elk_without_damping_is_newton(cell):
     p = small_problem(cell, T=30)
