@@ -97,36 +97,45 @@ __device__ inline void e64_put(float *L, const f32x16_e &v) {
   for (int r = 0; r < 16; r++) L[e64_row(r) * E64_LS + c] = v[r];
 }
 
+// v of lane c of each quad of lanes, in every lane of the quad (c is a
+// constant once the caller's loop is unrolled)
+__device__ inline float e64_quad_bcast(float v, int c) {
+  int x = __float_as_int(v);
+  switch (c) {
+    case 0: x = __builtin_amdgcn_mov_dpp(x, 0x00, 0xf, 0xf, false); break;
+    case 1: x = __builtin_amdgcn_mov_dpp(x, 0x55, 0xf, 0xf, false); break;
+    case 2: x = __builtin_amdgcn_mov_dpp(x, 0xaa, 0xf, 0xf, false); break;
+    default: x = __builtin_amdgcn_mov_dpp(x, 0xff, 0xf, 0xf, false); break;
+  }
+  return __int_as_float(x);
+}
+
 // In-place inverse of an SPD 64 x 64 matrix by Gauss-Jordan elimination
 // without pivoting (every pivot of an SPD matrix is positive).  Thread t
-// holds row t / 4, columns 16 (t % 4) .. + 15 in m[16]; sRow / sCol are
-// 2 x 64 floats of LDS each (the pivot row and column, double-buffered).
-__device__ inline void e64_inverse(float (&m)[16], float *sRow, float *sCol) {
-  const int t = threadIdx.x, row = t >> 2, c0 = (t & 3) * 16;
+// holds row t / 4, columns 16 (t % 4) .. + 15 in m[16], so the four threads
+// of a row are a quad of lanes: the pivot column's entry of a row comes from
+// its owner by a quad broadcast, and only the normalised pivot row goes
+// through LDS (sRow: 2 x 64 floats, double-buffered), one barrier per pivot.
+__device__ inline void e64_inverse(float (&m)[16], float *sRow) {
+  const int t = threadIdx.x, row = t >> 2, cq = t & 3, c0 = cq * 16;
+#pragma unroll
   for (int k = 0; k < 64; k++) {
-    float *R = sRow + (k & 1) * 64, *Cc = sCol + (k & 1) * 64;
-    if (row == k) {
+    float *R = sRow + (k & 1) * 64;
+    const int kq = k >> 4, kr = k & 15;
+    const float f = e64_quad_bcast(m[kr], kq);  // this row's entry in column k
+    if (row == k) {  // the pivot row, divided by the pivot; 1 / pivot in column k
+      const float rp = 1.f / f;
 #pragma unroll
-      for (int q = 0; q < 16; q++) R[c0 + q] = m[q];
-    }
-    if ((k >> 4) == (t & 3)) {
-#pragma unroll
-      for (int q = 0; q < 16; q++)
-        if (q == (k & 15)) Cc[row] = m[q];
+      for (int q = 0; q < 16; q++) R[c0 + q] = (q == kr && cq == kq) ? rp : m[q] * rp;
     }
     __syncthreads();
-    const float rp = 1.f / R[k];
     if (row == k) {
 #pragma unroll
-      for (int q = 0; q < 16; q++) m[q] = (c0 + q == k ? 1.f : m[q]) * rp;
+      for (int q = 0; q < 16; q++) m[q] = R[c0 + q];
     } else {
-      const float f = Cc[row];
+      if (cq == kq) m[kr] = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; q++) {
-        const int j = c0 + q;
-        const float rk = (j == k ? 1.f : R[j]) * rp;
-        m[q] = fmaf(-f, rk, j == k ? 0.f : m[q]);
-      }
+      for (int q = 0; q < 16; q++) m[q] = fmaf(-f, R[c0 + q], m[q]);
     }
   }
   __syncthreads();
@@ -156,8 +165,9 @@ constexpr int E64_RUN = 16;
 __global__ __launch_bounds__(256) void k_elk64_rows(const Elk64Args a) {
   __shared__ int s_stop;
   __shared__ float sW[3 * E64_MAT];  // W_hr, W_hz, W_hn
-  __shared__ float sJ[2][E64_MAT];
-  __shared__ float sR[2][64];
+  __shared__ float sJ[E64_MAT];      // J_{t+1}, then J_t
+  __shared__ float sG[256];          // z, alpha, beta, gamma of the step being built
+  __shared__ float sR[2][64];        // r_{t+1} and r_t
   if (e64_stopped(a, &s_stop)) return;
   const int T = a.T, runs = (T + E64_RUN - 1) / E64_RUN;
   const int b = blockIdx.x / runs, t0 = (blockIdx.x % runs) * E64_RUN, t1 = min(T, t0 + E64_RUN);
@@ -168,50 +178,55 @@ __global__ __launch_bounds__(256) void k_elk64_rows(const Elk64Args a) {
     float *d = sW + (row >> 6) * E64_MAT + (row & 63) * E64_LS + c4;
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
-  __syncthreads();
-  // J_t and r_t of step t into buffer q
-  auto build = [&](int t, int q) {
-    const float *G = a.gates + ((size_t)b * T + t) * 320;
+  // J_t into sJ (and, with store, A_t = -J_t into the workspace) and r_t
+  // into sR[q]; every thread calls it (it holds a barrier)
+  auto build = [&](int t, int q, bool store) {
+    const size_t rowi = (size_t)b * T + t;
+    const float *G = a.gates + rowi * 320;
+    for (int e = threadIdx.x; e < 320; e += 256) {
+      if (e < 256) sG[e] = G[e];
+      else sR[q][e - 256] = G[e];
+    }
+    __syncthreads();
+    float *A = a.A + rowi * E64_NN;
     for (int e = threadIdx.x; e < 4096; e += 256) {
       const int i = e >> 6, k = e & 63;
-      float v = G[64 + i] * sW[E64_MAT + i * E64_LS + k];           // alpha W_hz
-      v = fmaf(G[128 + i], sW[2 * E64_MAT + i * E64_LS + k], v);    // beta W_hn
-      v = fmaf(G[192 + i], sW[i * E64_LS + k], v);                  // gamma W_hr
-      sJ[q][i * E64_LS + k] = i == k ? v + G[i] : v;                // + diag(z)
+      float v = sG[64 + i] * sW[E64_MAT + i * E64_LS + k];           // alpha W_hz
+      v = fmaf(sG[128 + i], sW[2 * E64_MAT + i * E64_LS + k], v);    // beta W_hn
+      v = fmaf(sG[192 + i], sW[i * E64_LS + k], v);                  // gamma W_hr
+      v = i == k ? v + sG[i] : v;                                     // + diag(z)
+      sJ[i * E64_LS + k] = v;
+      if (store) A[e] = -v;
     }
-    if (threadIdx.x < 64) sR[q][threadIdx.x] = G[256 + threadIdx.x];
   };
-  int cur = 0;  // buffer of J_{t+1}
-  const bool has_next = t1 < T;
-  if (has_next) build(t1, cur);
+  int q = 0;  // sR buffer of r_{t+1}
+  __syncthreads();  // W_h is staged
+  if (t1 < T) build(t1, q, false);
   for (int t = t1 - 1; t >= t0; t--) {
     const bool nx = t + 1 < T;
-    build(t, cur ^ 1);
-    __syncthreads();
+    __syncthreads();  // J_{t+1} and r_{t+1} are complete
     const size_t rowi = (size_t)b * T + t;
-    float *A = a.A + rowi * E64_NN, *D = a.D + rowi * E64_NN;
-    // A_t = -J_t
-    for (int e = threadIdx.x; e < 4096; e += 256) A[e] = -sJ[cur ^ 1][(e >> 6) * E64_LS + (e & 63)];
+    float *D = a.D + rowi * E64_NN;
+    float fpart = 0.f;  // -(J_{t+1}^T r_{t+1})_k in thread k < 64
     if (nx) {
-      const f32x16_e jj = e64_mm<true, false>(sJ[cur], sJ[cur]);
+      const f32x16_e jj = e64_mm<true, false>(sJ, sJ);
       const int c = e64_col();
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int i = e64_row(r);
         D[i * 64 + c] = jj[r] + (i == c ? 1.f + a.lam : 0.f);
       }
-      if (threadIdx.x < 64) {  // f_t = r_t - J_{t+1}^T r_{t+1}
+      if (threadIdx.x < 64) {
         const int k = threadIdx.x;
-        float s = sR[cur ^ 1][k];
-        for (int i = 0; i < 64; i++) s = fmaf(-sJ[cur][i * E64_LS + k], sR[cur][i], s);
-        a.f[rowi * 64 + k] = s;
+        for (int i = 0; i < 64; i++) fpart = fmaf(-sJ[i * E64_LS + k], sR[q][i], fpart);
       }
     } else {
       for (int e = threadIdx.x; e < 4096; e += 256) D[e] = (e >> 6) == (e & 63) ? 1.f + a.lam : 0.f;
-      if (threadIdx.x < 64) a.f[rowi * 64 + threadIdx.x] = sR[cur ^ 1][threadIdx.x];
     }
-    __syncthreads();  // buffer cur is rebuilt two steps on
-    cur ^= 1;
+    __syncthreads();  // every read of J_{t+1} is done
+    build(t, q ^ 1, true);
+    if (threadIdx.x < 64) a.f[rowi * 64 + threadIdx.x] = sR[q ^ 1][threadIdx.x] + fpart;  // f_t = r_t - J^T r
+    q ^= 1;
   }
 }
 
@@ -220,8 +235,8 @@ __global__ __launch_bounds__(256) void k_elk64_rows(const Elk64Args a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_elk64_elim(const Elk64Args a, int s) {
   __shared__ int s_stop;
-  __shared__ float sM[3][E64_MAT];  // W, A_j, A_{j+s} (then P_j)
-  __shared__ float sRow[128], sCol[128], sV[2][64];
+  __shared__ float sM[2][E64_MAT];  // W (then P), A_{j+s} (then A_j)
+  __shared__ float sRow[128], sV[2][64];
   if (e64_stopped(a, &s_stop)) return;
   const int T = a.T, per = (T - s + 2 * s - 1) / (2 * s);  // eliminated rows per sequence
   const int b = blockIdx.x / per, m = blockIdx.x % per, j = s * (2 * m + 1);
@@ -229,19 +244,21 @@ __global__ __launch_bounds__(256) void k_elk64_elim(const Elk64Args a, int s) {
   const int t = threadIdx.x, row = t >> 2, c0 = (t & 3) * 16;
   const size_t rj = (size_t)b * T + j;
   const bool right = j + s < T;
-  float w[16];
+  // D_j and A_j into registers (A_j goes to LDS once A_{j+s} is done with)
+  float w[16], aj[16];
   {
-    const float4 *src = reinterpret_cast<const float4 *>(a.D + rj * E64_NN + row * 64 + c0);
+    const float4 *srcD = reinterpret_cast<const float4 *>(a.D + rj * E64_NN + row * 64 + c0);
+    const float4 *srcA = reinterpret_cast<const float4 *>(a.A + rj * E64_NN + row * 64 + c0);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const float4 v = src[q];
+      const float4 v = srcD[q], u = srcA[q];
       w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      aj[4 * q] = u.x; aj[4 * q + 1] = u.y; aj[4 * q + 2] = u.z; aj[4 * q + 3] = u.w;
     }
   }
-  e64_load(sM[1], a.A + rj * E64_NN);
-  if (right) e64_load(sM[2], a.A + (rj + s) * E64_NN);
+  if (right) e64_load(sM[1], a.A + (rj + s) * E64_NN);
   if (t < 64) sV[0][t] = a.f[rj * 64 + t];
-  e64_inverse(w, sRow, sCol);  // ends with a barrier: sM[1], sM[2], sV[0] are in
+  e64_inverse(w, sRow);  // ends with a barrier: sM[1] and sV[0] are in
 #pragma unroll
   for (int q = 0; q < 16; q++) sM[0][row * E64_LS + c0 + q] = w[q];
   const float gv = e64_mv_regs(w, sV[0]);  // g_j = W f_j
@@ -250,17 +267,21 @@ __global__ __launch_bounds__(256) void k_elk64_elim(const Elk64Args a, int s) {
     a.g[rj * 64 + row] = gv;
   }
   __syncthreads();
+  const f32x16_e Q = right ? e64_mm<false, true>(sM[0], sM[1]) : f32x16_e{};  // W A_{j+s}^T
+  __syncthreads();  // every read of A_{j+s} is done
+#pragma unroll
+  for (int q = 0; q < 16; q++) sM[1][row * E64_LS + c0 + q] = aj[q];
+  __syncthreads();
   const f32x16_e P = e64_mm<false, false>(sM[0], sM[1]);  // W A_j
-  const f32x16_e Q = right ? e64_mm<false, true>(sM[0], sM[2]) : f32x16_e{};  // W A_{j+s}^T
   if (t < 64) {  // v_j = A_j^T g_j
     float sacc = 0.f;
     for (int i = 0; i < 64; i++) sacc = fmaf(sM[1][i * E64_LS + t], sV[1][i], sacc);
     a.v[rj * 64 + t] = sacc;
   }
-  __syncthreads();  // every read of sM[2] is done
-  e64_put(sM[2], P);
+  __syncthreads();  // every read of W is done
+  e64_put(sM[0], P);
   __syncthreads();
-  const f32x16_e S = e64_mm<true, false>(sM[1], sM[2]);  // A_j^T P_j
+  const f32x16_e S = e64_mm<true, false>(sM[1], sM[0]);  // A_j^T P_j
   e64_store(a.S + rj * E64_NN, S);
   e64_store(a.A + rj * E64_NN, P);  // P_j in place of A_j
   e64_store(a.D + rj * E64_NN, Q);  // Q_j in place of D_j (zero without a right neighbour)
@@ -271,38 +292,52 @@ __global__ __launch_bounds__(256) void k_elk64_elim(const Elk64Args a, int s) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_elk64_keep(const Elk64Args a, int s) {
   __shared__ int s_stop;
-  __shared__ float sM[3][E64_MAT];  // A_i, P_{i-s}, Q_{i-s}
+  __shared__ float sM[2][E64_MAT];  // A_i, P_{i-s} (then Q_{i-s})
   __shared__ float sV[64];
   if (e64_stopped(a, &s_stop)) return;
   const int T = a.T, per = (T + 2 * s - 1) / (2 * s);
   const int b = blockIdx.x / per, i = 2 * s * (blockIdx.x % per);
   if (b >= a.B || i >= T) return;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, row = t >> 2, c0 = (t & 3) * 16, c = e64_col();
   const size_t ri = (size_t)b * T + i;
   const bool left = i >= s, right = i + s < T;
+  float *D = a.D + ri * E64_NN, *A = a.A + ri * E64_NN;
+  // this thread's share of D_i and S_{i+s} (the product's quadrant layout)
+  // and of Q_{i-s} (rows of 16), loaded ahead of the products
+  float dq[16], sq[16], qq[16];
+  const float *Sr = a.S + (ri + (right ? s : 0)) * E64_NN;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    dq[r] = D[e64_row(r) * 64 + c];
+    sq[r] = right ? Sr[e64_row(r) * 64 + c] : 0.f;
+  }
   f32x16_e AP{}, AQ{};
   float fl = 0.f;
   if (left) {
+    const float4 *srcQ = reinterpret_cast<const float4 *>(a.D + (ri - s) * E64_NN + row * 64 + c0);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 v = srcQ[q];
+      qq[4 * q] = v.x; qq[4 * q + 1] = v.y; qq[4 * q + 2] = v.z; qq[4 * q + 3] = v.w;
+    }
     e64_load(sM[0], a.A + ri * E64_NN);
     e64_load(sM[1], a.A + (ri - s) * E64_NN);  // P_{i-s}
-    e64_load(sM[2], a.D + (ri - s) * E64_NN);  // Q_{i-s}
     if (t < 64) sV[t] = a.g[(ri - s) * 64 + t];
     __syncthreads();
     AP = e64_mm<false, false>(sM[0], sM[1]);
-    AQ = e64_mm<false, false>(sM[0], sM[2]);
     if (t < 64) {
       for (int k = 0; k < 64; k++) fl = fmaf(sM[0][t * E64_LS + k], sV[k], fl);
     }
+    __syncthreads();  // every read of P is done
+#pragma unroll
+    for (int q = 0; q < 16; q++) sM[1][row * E64_LS + c0 + q] = qq[q];
+    __syncthreads();
+    AQ = e64_mm<false, false>(sM[0], sM[1]);
   }
-  const int c = e64_col();
-  float *D = a.D + ri * E64_NN, *A = a.A + ri * E64_NN;
-  const float *Sr = right ? a.S + (ri + s) * E64_NN : nullptr;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int rr = e64_row(r);
-    float d = D[rr * 64 + c] - AQ[r];
-    if (right) d -= Sr[rr * 64 + c];
-    D[rr * 64 + c] = d;
+    D[rr * 64 + c] = dq[r] - AQ[r] - sq[r];
     A[rr * 64 + c] = left ? -AP[r] : 0.f;
   }
   if (t < 64) a.f[ri * 64 + t] -= fl + (right ? a.v[(ri + s) * 64 + t] : 0.f);
@@ -313,7 +348,7 @@ __global__ __launch_bounds__(256) void k_elk64_keep(const Elk64Args a, int s) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_elk64_root(const Elk64Args a) {
   __shared__ int s_stop;
-  __shared__ float sRow[128], sCol[128], sV[64];
+  __shared__ float sRow[128], sV[64];
   if (e64_stopped(a, &s_stop)) return;
   const int b = blockIdx.x, t = threadIdx.x, row = t >> 2, c0 = (t & 3) * 16;
   const size_t r0 = (size_t)b * a.T;
@@ -322,7 +357,7 @@ __global__ __launch_bounds__(256) void k_elk64_root(const Elk64Args a) {
 #pragma unroll
   for (int q = 0; q < 16; q++) w[q] = src[q];
   if (t < 64) sV[t] = a.f[r0 * 64 + t];
-  e64_inverse(w, sRow, sCol);
+  e64_inverse(w, sRow);
   const float xv = e64_mv_regs(w, sV);
   if ((t & 3) == 0) a.x[r0 * 64 + row] = xv;
 }
