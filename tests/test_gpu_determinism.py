@@ -98,3 +98,16 @@ def test_lookback_paths_repeat_within_rounding(make):
             worst = max(worst, float((o[k] - ref[3][k]).abs().max()))
     print("  sweeps", ref[1], "largest run-to-run difference", worst, flush=True)
     assert worst <= 1e-6
+
+
+def test_elk_64_wide_is_bitwise_reproducible():
+    """ELK with the full 64 x 64 Jacobian (block cyclic reduction: every
+    product and sum in a fixed order) repeats bit for bit."""
+    p = sy.make_problem(5, B=2, T=700)
+    dp = bd.DeviceProblem(p, elk=True)
+    dp.solve_elk(0.1)
+    h0 = dp.h.clone()
+    for _ in range(3):
+        dp.solve_elk(0.1)
+        torch.cuda.synchronize()
+        assert torch.equal(dp.h, h0)
