@@ -124,11 +124,11 @@ __device__ inline void e64_inverse(float (&m)[16], float *sRow) {
     const int kq = k >> 4, kr = k & 15;
     const float f = e64_quad_bcast(m[kr], kq);  // this row's entry in column k
     if (row == k) {  // the pivot row, divided by the pivot; 1 / pivot in column k
-      const float rp = 1.f / f;
+      const float rp = __builtin_amdgcn_rcpf(f);  // pivots of an SPD matrix: well inside the range
 #pragma unroll
       for (int q = 0; q < 16; q++) R[c0 + q] = (q == kr && cq == kq) ? rp : m[q] * rp;
     }
-    __syncthreads();
+    lds_barrier();  // orders LDS only: loads issued before the inverse stay in flight
     if (row == k) {
 #pragma unroll
       for (int q = 0; q < 16; q++) m[q] = R[c0 + q];
