@@ -313,6 +313,14 @@ def test_full_elk_dense64(lam, B, T):
     check(p, lam, 0.0, 3, full=True)
 
 
+@pytest.mark.parametrize("T,lam", [(150, 0.5), (1500, 0.05)])
+def test_full_elk_dense64_h0_biases(T, lam):
+    """n = 64 exactly (no padding) with h0, biases and an input width off the
+    workload's; T = 1500 takes eleven levels of the reduction."""
+    p = sy.custom_problem(sy.CELL_GRU, B=1 if T > 1000 else 2, T=T, d=7, n=64, seed=T, w_scale=0.8, h0=True)
+    check(p, lam, 0.0, 2, full=True)
+
+
 def test_full_elk_dense64_to_tolerance():
     p = sy.make_problem(5, B=2, T=300)
     check(p, 0.1, p["tol"], p["max_iters"], full=True)
